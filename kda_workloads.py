@@ -1,0 +1,141 @@
+"""Seeded synthetic inputs for the KDA hot path (shared by tests, smoke and bench).
+
+This module holds no arithmetic of the method itself: it only draws random
+tensors with the shapes and value distributions of the five workloads below and
+returns them as CPU torch tensors.  Both the HIP path and the fp64 oracle are
+fed from it.
+
+Random stream: one torch CPU generator per workload, seeded, drawing in the
+fixed order q, k, v, g_raw, beta_raw, state, slots, accepted lengths.
+
+Distributions (per workload description):
+  q, k, v ~ N(0, 1)                       (tiny fp32 case: q and k L2-normalised per head)
+  g       = -0.1 * softplus(N(0, 1))      per key channel, fp32, always <= 0
+  beta    = sigmoid(N(0, 1))              per (token, head), fp32
+  state   ~ N(0, 0.05^2)                  fp32 pool slots (0.05 read as the standard deviation)
+"""
+import torch
+import torch.nn.functional as F
+
+# The five workloads: tiny recurrent fp32, decode over a state pool, speculative
+# verify + replay commit, chunked prefill, long-context varlen prefill (one GPU's
+# head share).
+TINY = dict(name="tiny_fp32_T64_H2_d64", T=64, H=2, dk=64, dv=64)
+DECODE = dict(name="decode_pool512_N64_H32_d128", num_slots=512, N=64, T=1, H=32, dk=128, dv=128)
+VERIFY = dict(name="verify_replay_N32_T8_H32_d128", num_slots=512, N=32, T=8, H=32, dk=128, dv=128)
+PREFILL = dict(name="prefill_T8192_H32_d128", T=8192, H=32, dk=128, dv=128)
+VARLEN = dict(name="varlen_prefill_4seq_128076tok_H16_d128", seqlens=(100000, 16384, 8192, 3500),
+              num_slots=512, H=16, dk=128, dv=128)
+
+
+def _gen(seed):
+    g = torch.Generator(device="cpu")
+    g.manual_seed(int(seed))
+    return g
+
+
+def _normal(gen, shape, std=1.0):
+    x = torch.randn(*shape, generator=gen, dtype=torch.float32)
+    return x * std if std != 1.0 else x
+
+
+def _gate(gen, shape):
+    return -0.1 * F.softplus(_normal(gen, shape))
+
+
+def _beta(gen, shape):
+    return torch.sigmoid(_normal(gen, shape))
+
+
+def _distinct_slots(gen, num_slots, n):
+    return torch.randperm(num_slots, generator=gen)[:n].to(torch.int32)
+
+
+def tiny(seed=0, T=None, H=None, dk=None, dv=None):
+    """Tiny fp32 case: one sequence, zero initial state.
+
+    Returns dict(q, k, v [T, H, d] fp32, g [T, H, dk], beta [T, H]).  q and k are
+    L2-normalised per head with torch.nn.functional.normalize.
+    """
+    T = T or TINY["T"]; H = H or TINY["H"]; dk = dk or TINY["dk"]; dv = dv or TINY["dv"]
+    gen = _gen(seed)
+    q = F.normalize(_normal(gen, (T, H, dk)), dim=-1)
+    k = F.normalize(_normal(gen, (T, H, dk)), dim=-1)
+    v = _normal(gen, (T, H, dv))
+    g = _gate(gen, (T, H, dk))
+    beta = _beta(gen, (T, H))
+    return dict(q=q, k=k, v=v, g=g, beta=beta)
+
+
+def decode(seed=0, N=None, T=None, H=None, dk=None, dv=None, num_slots=None,
+           dtype=torch.bfloat16, with_accepted=False):
+    """Decode / MTP / verify over a state pool.
+
+    Returns dict(q, k [N, T, H, dk] dtype, v [N, T, H, dv] dtype, g [N, T, H, dk] fp32,
+    beta [N, T, H] fp32, pool [num_slots, H, dk, dv] fp32, slot_idx [N] int32 (distinct),
+    and, with with_accepted, accepted [N] int32 uniform in 1..T).
+    """
+    N = N or DECODE["N"]; T = T or DECODE["T"]; H = H or DECODE["H"]
+    dk = dk or DECODE["dk"]; dv = dv or DECODE["dv"]; num_slots = num_slots or DECODE["num_slots"]
+    if N > num_slots:
+        raise ValueError("need N <= num_slots for distinct slots")
+    gen = _gen(seed)
+    q = _normal(gen, (N, T, H, dk)).to(dtype)
+    k = _normal(gen, (N, T, H, dk)).to(dtype)
+    v = _normal(gen, (N, T, H, dv)).to(dtype)
+    g = _gate(gen, (N, T, H, dk))
+    beta = _beta(gen, (N, T, H))
+    pool = _normal(gen, (num_slots, H, dk, dv), std=0.05)
+    slot_idx = _distinct_slots(gen, num_slots, N)
+    out = dict(q=q, k=k, v=v, g=g, beta=beta, pool=pool, slot_idx=slot_idx)
+    if with_accepted:
+        out["accepted"] = torch.randint(1, T + 1, (N,), generator=gen, dtype=torch.int32)
+    return out
+
+
+def verify(seed=0, **kw):
+    """Speculative verify + replay: decode() at N=32, T=8 with accepted lengths."""
+    args = dict(N=VERIFY["N"], T=VERIFY["T"], H=VERIFY["H"], dk=VERIFY["dk"], dv=VERIFY["dv"],
+                num_slots=VERIFY["num_slots"], with_accepted=True)
+    args.update(kw)
+    return decode(seed, **args)
+
+
+def prefill(seed=0, seqlens=(8192,), H=None, dk=None, dv=None, num_slots=None, h0_std=None,
+            dtype=torch.bfloat16):
+    """Varlen chunked prefill inputs.
+
+    Returns dict(q, k [T_total, H, dk] dtype, v [T_total, H, dv] dtype, g [T_total, H, dk] fp32,
+    beta [T_total, H] fp32, cu_seqlens [num_seqs + 1] int32, pool [num_slots, H, dk, dv] fp32,
+    slot_idx [num_seqs] int32 distinct).  With h0_std None the pool is zero (zero initial
+    state); otherwise it is drawn ~ N(0, h0_std^2).
+    """
+    H = H or PREFILL["H"]; dk = dk or PREFILL["dk"]; dv = dv or PREFILL["dv"]
+    seqlens = tuple(int(s) for s in seqlens)
+    ns = len(seqlens)
+    num_slots = num_slots or ns
+    T = sum(seqlens)
+    gen = _gen(seed)
+    q = _normal(gen, (T, H, dk)).to(dtype)
+    k = _normal(gen, (T, H, dk)).to(dtype)
+    v = _normal(gen, (T, H, dv)).to(dtype)
+    g = _gate(gen, (T, H, dk))
+    beta = _beta(gen, (T, H))
+    if h0_std is None:
+        pool = torch.zeros(num_slots, H, dk, dv, dtype=torch.float32)
+    else:
+        pool = _normal(gen, (num_slots, H, dk, dv), std=h0_std)
+    slot_idx = _distinct_slots(gen, num_slots, ns)
+    cu = torch.zeros(ns + 1, dtype=torch.int32)
+    cu[1:] = torch.cumsum(torch.tensor(seqlens, dtype=torch.int64), 0).to(torch.int32)
+    return dict(q=q, k=k, v=v, g=g, beta=beta, cu_seqlens=cu, pool=pool, slot_idx=slot_idx)
+
+
+def prefill_long(seed=0, **kw):
+    """Long-context varlen prefill: 4 sequences (100000, 16384, 8192, 3500), H=16,
+    initial states from 4 distinct slots of a 512-slot pool ~ N(0, 0.05^2)."""
+    args = dict(seqlens=VARLEN["seqlens"], H=VARLEN["H"], dk=VARLEN["dk"], dv=VARLEN["dv"],
+                num_slots=VARLEN["num_slots"], h0_std=0.05)
+    args.update(kw)
+    return prefill(seed, **args)
+
