@@ -1,0 +1,150 @@
+/*
+ * kda.h -- C ABI of the MI355X (gfx950) Kimi Delta Attention hot path.
+ *
+ * The method (gated delta rule, one sequence, one head, state S of dk x dv,
+ * row c = key channel, dv contiguous), per token, in the order the decode
+ * kernel description lists the steps (page "Kimi K3 ... 昇腾 day-0 adaptation",
+ * section "融合算子加速：KDA Prefill与Decode双路径"):
+ *
+ *   qh = q / sqrt(|q|^2 + 1e-6),  kh = k / sqrt(|k|^2 + 1e-6)    Q/K L2 norm
+ *   alpha = exp(g)                       per key channel          gate
+ *   S' = diag(alpha) S                                            state decay
+ *   u  = beta * (v - S'^T kh)                                     delta rule, beta
+ *   S  = S' + kh u^T                                              outer-product update
+ *   o  = scale * S^T qh                                           output (updated state)
+ *   S written back to its state-pool slot                         in-place write-back
+ *
+ * Conventions shared by every entry point:
+ *  - Ownership: the caller owns every buffer.  No entry point allocates or frees
+ *    memory or keeps state between calls; calls are thread-safe.
+ *  - All pointers are device pointers to contiguous row-major arrays, 16-byte
+ *    aligned.  Index arrays (slot_idx, accepted_len, cu_seqlens) live on the device
+ *    and are read by the kernels, not by the host.
+ *  - Supported head dims: dk, dv in {64, 128}.  Other values: KDA_ERR_UNSUPPORTED.
+ *    kda_chunk_prefill with fp32 q/k/v additionally needs dk = 64 (its fp32 MFMA
+ *    operand tiles for dk = 128 do not fit the 160 KiB LDS of a CU).
+ *  - Every argument check runs on the host before any HIP call; on failure nothing
+ *    is launched and the error code is returned.  Device-resident indices are not
+ *    checked: a slot index >= num_slots, duplicate slots within one call, or
+ *    cu_seqlens that do not match total_tokens are undefined behaviour.
+ *  - Calls are asynchronous on `stream` (NULL = the null stream).  A launch failure
+ *    returns KDA_ERR_HIP.
+ *  - dtype KDA_BF16: q, k, v and o are bfloat16 (o rounded to nearest even); with
+ *    KDA_F32 they are fp32.  g, beta, the state pool and records are always fp32.
+ */
+#ifndef KDA_H
+#define KDA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    KDA_OK = 0,
+    KDA_ERR_INVALID_ARG = -1, /* null/misaligned pointer, bad size or dtype      */
+    KDA_ERR_UNSUPPORTED = -2, /* dk or dv outside {64, 128}; fp32 prefill, dk 128 */
+    KDA_ERR_WORKSPACE = -3,   /* prefill workspace null or too small             */
+    KDA_ERR_HIP = -4          /* a HIP launch failed                             */
+} kda_status;
+
+typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
+
+/*
+ * kda_decode_step -- fused decode / MTP step over state-pool slots.
+ *
+ * Follows the decode path of section "KDA Prefill与Decode双路径" (one fused kernel:
+ * L2 norm, gate and beta, decay, delta rule, outer-product update, output, in-place
+ * final-state write-back; work split by sequence x value head) and, with records,
+ * the verification half of ReplaySSM (page "2.8倍性能提升！基于CANN实现Kimi K3高性能推理",
+ * section 04: verification stores only the per-token update records).
+ *
+ *   q, k        [N, T, H, dk]   dtype
+ *   v           [N, T, H, dv]   dtype
+ *   g           [N, T, H, dk]   fp32, log of the per-key-channel decay (g <= 0 expected)
+ *   beta        [N, T, H]       fp32
+ *   state_pool  [num_slots, H, dk, dv] fp32
+ *   slot_idx    [N] int32: sequence n uses slot slot_idx[n]; a negative index skips the
+ *               sequence (no state read or write, its o is written as zeros, its records
+ *               are not written).  Slots must be distinct within a call.
+ *   o           [N, T, H, dv]   dtype (output)
+ *   records     NULL: commit mode -- the T tokens are applied in order and the final
+ *               state is written back to the slot in place.
+ *               non-NULL: verify mode -- the slot is left untouched; fp32 records
+ *               [N, T, H, 2*dk + dv] = {kh (dk) | alpha (dk) | u (dv)} are written for
+ *               every token, and o is the output the token would have if committed.
+ *   T >= 1 tokens per sequence (T = 1 decode, T > 1 MTP / speculative verify).
+ *   scale       output scale (1/sqrt(dk) is the usual choice).
+ *   use_qk_l2norm  1: normalise q and k as above; 0: use them as given.
+ */
+int kda_decode_step(const void* q, const void* k, const void* v, int dtype, const float* g,
+                    const float* beta, float* state_pool, int64_t num_slots,
+                    const int32_t* slot_idx, int N, int T, int H, int dk, int dv, float scale,
+                    int use_qk_l2norm, void* o, float* records, hipStream_t stream);
+
+/*
+ * kda_replay_commit -- ReplaySSM commit (section 04 of the CANN inference page: once
+ * the accepted length is known, the records of the accepted tokens are applied in
+ * order starting from the committed state).
+ *
+ * For each sequence n with slot_idx[n] >= 0 and each head, starting from the slot's
+ * committed state, applies records[n, t, h] for t = 0 .. accepted_len[n]-1:
+ *     S <- diag(alpha) S + kh u^T
+ * and writes the state back to the slot.  records are those written by
+ * kda_decode_step in verify mode ([N, T, H, 2*dk + dv] fp32).  accepted_len [N] int32
+ * on the device, each in 0..T (0 leaves the slot untouched; values outside 0..T are
+ * undefined behaviour).  The fp32 arithmetic matches commit-mode kda_decode_step, so
+ * replaying a prefix reproduces the state that committing the same tokens gives.
+ */
+int kda_replay_commit(float* state_pool, int64_t num_slots, const int32_t* slot_idx,
+                      const float* records, const int32_t* accepted_len, int N, int T, int H,
+                      int dk, int dv, hipStream_t stream);
+
+/*
+ * kda_chunk_prefill_workspace_size -- bytes of device workspace kda_chunk_prefill
+ * needs for these sizes (an upper bound that depends only on the arguments).
+ */
+size_t kda_chunk_prefill_workspace_size(int num_seqs, int64_t total_tokens, int H, int dk,
+                                        int dv, int dtype);
+
+/*
+ * kda_chunk_prefill -- varlen chunked prefill (section "KDA Prefill与Decode双路径":
+ * 64-token chunks, with Q/K normalisation, gate cumulation and the chunk recurrence
+ * done as batched work).  The result equals running the token recurrence over each
+ * sequence.
+ *
+ *   q, k        [total_tokens, H, dk]   dtype
+ *   v           [total_tokens, H, dv]   dtype
+ *   g           [total_tokens, H, dk]   fp32
+ *   beta        [total_tokens, H]       fp32
+ *   cu_seqlens  [num_seqs + 1] int32 on the device: sequence i is tokens
+ *               cu_seqlens[i] .. cu_seqlens[i+1]-1; cu_seqlens[0] = 0,
+ *               non-decreasing, cu_seqlens[num_seqs] = total_tokens.  Empty
+ *               sequences are allowed (the state passes through).
+ *   state_pool  [num_slots, H, dk, dv] fp32; slot_idx [num_seqs] int32 (distinct,
+ *               >= 0).  h0_from_pool = 1: the initial state of sequence i is read from
+ *               slot slot_idx[i]; 0: it is zero.  The final state is always written
+ *               to slot slot_idx[i].
+ *   o           [total_tokens, H, dv] dtype (output)
+ *   workspace   device buffer of at least kda_chunk_prefill_workspace_size(...) bytes;
+ *               its contents on entry do not matter.
+ */
+int kda_chunk_prefill(const void* q, const void* k, const void* v, int dtype, const float* g,
+                      const float* beta, const int32_t* cu_seqlens, int num_seqs,
+                      int64_t total_tokens, float* state_pool, int64_t num_slots,
+                      const int32_t* slot_idx, int h0_from_pool, int H, int dk, int dv,
+                      float scale, int use_qk_l2norm, void* o, void* workspace,
+                      size_t workspace_bytes, hipStream_t stream);
+
+/* Human-readable name of a kda_status value (static string, never NULL). */
+const char* kda_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H */

@@ -1,0 +1,17 @@
+"""Kimi Delta Attention (KDA) gated delta-rule hot path for AMD MI355X (gfx950).
+
+Python front end of the C ABI in include/kda.h.  Tensors are torch tensors on
+the GPU; they provide device memory and the stream, nothing else:
+
+  decode_step    fused decode / MTP step over state-pool slots (commit or verify)
+  replay_commit  ReplaySSM commit of accepted update records
+  chunk_prefill  varlen 64-token chunked prefill with initial / final states
+
+All arithmetic runs in the HIP kernels of libkda.so.
+"""
+from ._lib import KdaError, load, status_string  # noqa: F401
+from .ops import (chunk_prefill, chunk_prefill_workspace_size, decode_step,  # noqa: F401
+                  replay_commit)
+
+__all__ = ["decode_step", "replay_commit", "chunk_prefill", "chunk_prefill_workspace_size",
+           "KdaError", "load", "status_string"]

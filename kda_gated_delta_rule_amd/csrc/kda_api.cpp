@@ -1,0 +1,129 @@
+// kda_api.cpp -- the extern "C" entry points declared in include/kda.h.
+//
+// Every argument check runs here, on the host, before any HIP call: an invalid
+// call returns its error code without touching the device.  The launchers in
+// the kernel translation units only see validated arguments.
+#include "kda.h"
+
+#include <math.h>
+
+#include "kda_internal.hpp"
+
+#define KDA_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool supported_dim(int d) { return d == 64 || d == 128; }
+bool valid_dtype(int dt) { return dt == KDA_F32 || dt == KDA_BF16; }
+
+// Total element count of a product of non-negative sizes, or -1 on int64 overflow.
+int64_t checked_mul(int64_t a, int64_t b) {
+    if (a < 0 || b < 0) return -1;
+    if (a != 0 && b > INT64_MAX / a) return -1;
+    return a * b;
+}
+
+int to_status(hipError_t e) { return e == hipSuccess ? KDA_OK : KDA_ERR_HIP; }
+
+}  // namespace
+
+KDA_EXPORT int kda_decode_step(const void* q, const void* k, const void* v, int dtype,
+                               const float* g, const float* beta, float* state_pool,
+                               int64_t num_slots, const int32_t* slot_idx, int N, int T, int H,
+                               int dk, int dv, float scale, int use_qk_l2norm, void* o,
+                               float* records, hipStream_t stream) {
+    if (!valid_dtype(dtype)) return KDA_ERR_INVALID_ARG;
+    if (N < 0 || T < 1 || H < 1 || num_slots < 1) return KDA_ERR_INVALID_ARG;
+    if (!isfinite(scale)) return KDA_ERR_INVALID_ARG;
+    if (use_qk_l2norm != 0 && use_qk_l2norm != 1) return KDA_ERR_INVALID_ARG;
+    if (!supported_dim(dk) || !supported_dim(dv)) return KDA_ERR_UNSUPPORTED;
+    const void* ptrs[] = {q, k, v, g, beta, state_pool, slot_idx, o};
+    for (const void* p : ptrs)
+        if (!p || !aligned16(p)) return KDA_ERR_INVALID_ARG;
+    if (records && !aligned16(records)) return KDA_ERR_INVALID_ARG;
+    const int64_t tokens = checked_mul(checked_mul(N, T), H);
+    if (tokens < 0 || checked_mul(tokens, 2 * dk + dv) < 0) return KDA_ERR_INVALID_ARG;
+    if (checked_mul(checked_mul(num_slots, H), static_cast<int64_t>(dk) * dv) < 0)
+        return KDA_ERR_INVALID_ARG;
+    if (checked_mul(N, H) > (1ll << 30)) return KDA_ERR_INVALID_ARG;  // grid size
+    if (N == 0) return KDA_OK;
+
+    kda::DecodeArgs a{q, k, v, g, beta, state_pool, slot_idx, o, records,
+                      N, T, H, scale, use_qk_l2norm};
+    return to_status(kda::launch_decode(a, dtype == KDA_BF16, dk, dv, stream));
+}
+
+KDA_EXPORT int kda_replay_commit(float* state_pool, int64_t num_slots, const int32_t* slot_idx,
+                                 const float* records, const int32_t* accepted_len, int N, int T,
+                                 int H, int dk, int dv, hipStream_t stream) {
+    if (N < 0 || T < 1 || H < 1 || num_slots < 1) return KDA_ERR_INVALID_ARG;
+    if (!supported_dim(dk) || !supported_dim(dv)) return KDA_ERR_UNSUPPORTED;
+    const void* ptrs[] = {state_pool, slot_idx, records, accepted_len};
+    for (const void* p : ptrs)
+        if (!p || !aligned16(p)) return KDA_ERR_INVALID_ARG;
+    const int64_t tokens = checked_mul(checked_mul(N, T), H);
+    if (tokens < 0 || checked_mul(tokens, 2 * dk + dv) < 0) return KDA_ERR_INVALID_ARG;
+    if (checked_mul(checked_mul(num_slots, H), static_cast<int64_t>(dk) * dv) < 0)
+        return KDA_ERR_INVALID_ARG;
+    if (checked_mul(N, H) > (1ll << 30)) return KDA_ERR_INVALID_ARG;
+    if (N == 0) return KDA_OK;
+
+    kda::ReplayArgs a{state_pool, slot_idx, records, accepted_len, N, T, H};
+    return to_status(kda::launch_replay(a, dk, dv, stream));
+}
+
+KDA_EXPORT size_t kda_chunk_prefill_workspace_size(int num_seqs, int64_t total_tokens, int H,
+                                                   int dk, int dv, int dtype) {
+    if (num_seqs < 0 || total_tokens < 0 || H < 1 || !supported_dim(dk) || !supported_dim(dv) ||
+        !valid_dtype(dtype))
+        return 0;
+    return kda::prefill_workspace_bytes(num_seqs, total_tokens, H, dk, dv, dtype == KDA_BF16);
+}
+
+KDA_EXPORT int kda_chunk_prefill(const void* q, const void* k, const void* v, int dtype,
+                                 const float* g, const float* beta, const int32_t* cu_seqlens,
+                                 int num_seqs, int64_t total_tokens, float* state_pool,
+                                 int64_t num_slots, const int32_t* slot_idx, int h0_from_pool,
+                                 int H, int dk, int dv, float scale, int use_qk_l2norm, void* o,
+                                 void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (!valid_dtype(dtype)) return KDA_ERR_INVALID_ARG;
+    if (num_seqs < 0 || total_tokens < 0 || H < 1 || num_slots < 1) return KDA_ERR_INVALID_ARG;
+    if (num_seqs == 0 && total_tokens != 0) return KDA_ERR_INVALID_ARG;
+    if (!isfinite(scale)) return KDA_ERR_INVALID_ARG;
+    if (use_qk_l2norm != 0 && use_qk_l2norm != 1) return KDA_ERR_INVALID_ARG;
+    if (h0_from_pool != 0 && h0_from_pool != 1) return KDA_ERR_INVALID_ARG;
+    if (!supported_dim(dk) || !supported_dim(dv)) return KDA_ERR_UNSUPPORTED;
+    if (!kda::prefill_supported(dtype == KDA_BF16, dk, dv)) return KDA_ERR_UNSUPPORTED;
+    if (total_tokens > (1ll << 31) - 1) return KDA_ERR_INVALID_ARG;  // int32 cu_seqlens
+    if (checked_mul(checked_mul(total_tokens, H), 2 * dk + dv) < 0) return KDA_ERR_INVALID_ARG;
+    if (checked_mul(checked_mul(num_slots, H), static_cast<int64_t>(dk) * dv) < 0)
+        return KDA_ERR_INVALID_ARG;
+    if (num_seqs == 0) return KDA_OK;
+    const void* ptrs[] = {cu_seqlens, state_pool, slot_idx};
+    for (const void* p : ptrs)
+        if (!p || !aligned16(p)) return KDA_ERR_INVALID_ARG;
+    if (total_tokens > 0) {
+        const void* tp[] = {q, k, v, g, beta, o};
+        for (const void* p : tp)
+            if (!p || !aligned16(p)) return KDA_ERR_INVALID_ARG;
+    }
+    const size_t need =
+        kda::prefill_workspace_bytes(num_seqs, total_tokens, H, dk, dv, dtype == KDA_BF16);
+    if (!workspace || !aligned16(workspace) || workspace_bytes < need) return KDA_ERR_WORKSPACE;
+
+    kda::PrefillArgs a{q, k, v, g, beta, cu_seqlens, num_seqs, total_tokens, state_pool,
+                       slot_idx, h0_from_pool, H, scale, use_qk_l2norm, o, workspace};
+    return to_status(kda::launch_prefill(a, dtype == KDA_BF16, dk, dv, stream));
+}
+
+KDA_EXPORT const char* kda_status_string(int status) {
+    switch (status) {
+        case KDA_OK: return "KDA_OK";
+        case KDA_ERR_INVALID_ARG: return "KDA_ERR_INVALID_ARG: invalid argument";
+        case KDA_ERR_UNSUPPORTED: return "KDA_ERR_UNSUPPORTED: dk and dv must be 64 or 128 (fp32 prefill: dk = 64)";
+        case KDA_ERR_WORKSPACE: return "KDA_ERR_WORKSPACE: prefill workspace missing or too small";
+        case KDA_ERR_HIP: return "KDA_ERR_HIP: a HIP launch failed";
+        default: return "unknown kda_status";
+    }
+}

@@ -1,0 +1,176 @@
+// kda_device.hpp -- small device helpers shared by the gfx950 KDA kernels:
+// bf16 <-> fp32 conversion, typed vector loads/stores, wave64 reductions and
+// the MFMA tile primitives used by the chunked prefill.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kda {
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------------------
+// bf16: stored as uint16_t.  Widening is exact; narrowing is the hardware
+// round-to-nearest-even conversion (v_cvt_pk_bf16_f32 on gfx950), the same
+// rounding torch applies on a cast.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+    return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    return static_cast<uint32_t>(f32_to_bf16(a)) | (static_cast<uint32_t>(f32_to_bf16(b)) << 16);
+}
+
+// Element type tags for the q/k/v/o tensors.
+struct F32 {
+    using storage = float;
+    static constexpr int bytes = 4;
+};
+struct BF16 {
+    using storage = uint16_t;
+    static constexpr int bytes = 2;
+};
+
+// Loads element i as fp32.
+template <class T>
+__device__ __forceinline__ float load1(const void* p, int64_t i);
+template <>
+__device__ __forceinline__ float load1<F32>(const void* p, int64_t i) {
+    return static_cast<const float*>(p)[i];
+}
+template <>
+__device__ __forceinline__ float load1<BF16>(const void* p, int64_t i) {
+    return bf16_to_f32(static_cast<const uint16_t*>(p)[i]);
+}
+
+// Loads 2 consecutive elements (index i, i+1) as fp32.
+template <class T>
+__device__ __forceinline__ float2 load2(const void* p, int64_t i);
+template <>
+__device__ __forceinline__ float2 load2<F32>(const void* p, int64_t i) {
+    return *reinterpret_cast<const float2*>(static_cast<const float*>(p) + i);
+}
+template <>
+__device__ __forceinline__ float2 load2<BF16>(const void* p, int64_t i) {
+    uint32_t w = *reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(p) + i);
+    return make_float2(__uint_as_float(w << 16), __uint_as_float(w & 0xffff0000u));
+}
+
+// Loads 4 consecutive elements as fp32.
+template <class T>
+__device__ __forceinline__ float4 load4(const void* p, int64_t i);
+template <>
+__device__ __forceinline__ float4 load4<F32>(const void* p, int64_t i) {
+    return *reinterpret_cast<const float4*>(static_cast<const float*>(p) + i);
+}
+template <>
+__device__ __forceinline__ float4 load4<BF16>(const void* p, int64_t i) {
+    uint2 w = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(p) + i);
+    return make_float4(__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u),
+                       __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xffff0000u));
+}
+
+// Stores 4 consecutive elements (fp32 in, rounded for bf16).
+template <class T>
+__device__ __forceinline__ void store4(void* p, int64_t i, float4 x);
+template <>
+__device__ __forceinline__ void store4<F32>(void* p, int64_t i, float4 x) {
+    *reinterpret_cast<float4*>(static_cast<float*>(p) + i) = x;
+}
+template <>
+__device__ __forceinline__ void store4<BF16>(void* p, int64_t i, float4 x) {
+    uint2 w = make_uint2(pack_bf16x2(x.x, x.y), pack_bf16x2(x.z, x.w));
+    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p) + i) = w;
+}
+
+// ---------------------------------------------------------------------------
+// wave64 reductions (butterfly; every lane ends with the total).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m, kWave);
+    return x;
+}
+
+__device__ __forceinline__ float4 f4_fma(float4 a, float4 b, float4 c) {
+    return make_float4(fmaf(a.x, b.x, c.x), fmaf(a.y, b.y, c.y), fmaf(a.z, b.z, c.z),
+                       fmaf(a.w, b.w, c.w));
+}
+__device__ __forceinline__ float4 f4_scale_fma(float a, float4 b, float4 c) {
+    return make_float4(fmaf(a, b.x, c.x), fmaf(a, b.y, c.y), fmaf(a, b.z, c.z),
+                       fmaf(a, b.w, c.w));
+}
+__device__ __forceinline__ float4 f4_mul(float4 a, float s) {
+    return make_float4(a.x * s, a.y * s, a.z * s, a.w * s);
+}
+__device__ __forceinline__ float4 f4_add(float4 a, float4 b) {
+    return make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w);
+}
+__device__ __forceinline__ float4 f4_sub(float4 a, float4 b) {
+    return make_float4(a.x - b.x, a.y - b.y, a.z - b.z, a.w - b.w);
+}
+__device__ __forceinline__ float4 f4_shfl_xor(float4 a, int m) {
+    return make_float4(__shfl_xor(a.x, m, kWave), __shfl_xor(a.y, m, kWave),
+                       __shfl_xor(a.z, m, kWave), __shfl_xor(a.w, m, kWave));
+}
+
+// ---------------------------------------------------------------------------
+// MFMA 16x16 output tiles, "NT" form:  C[m][n] += sum_k A[m][k] * B[n][k],
+// with A stored row-major [16 rows][lda] and B stored row-major [16 rows][ldb]
+// (both K-contiguous), typically in LDS.
+//   bf16: v_mfma_f32_16x16x32_bf16, lane l supplies A[l%16][k0 + 8(l/16) .. +7]
+//         and B[l%16][k0 + 8(l/16) .. +7].
+//   fp32: v_mfma_f32_16x16x4_f32, lane l supplies A[l%16][k0 + l/16] and
+//         B[l%16][k0 + l/16].
+// Accumulator layout (both): lane l holds C[4(l/16) + r][l%16], r = 0..3.
+// ---------------------------------------------------------------------------
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+template <class T>
+struct Mma;
+
+template <>
+struct Mma<BF16> {
+    using elem = uint16_t;
+    static constexpr int KS = 32;
+    __device__ static __forceinline__ f32x4 step(const elem* A, int lda, const elem* B, int ldb,
+                                                 int k0, f32x4 c, int lane) {
+        const int r = lane & 15, kk = k0 + 8 * (lane >> 4);
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(A + r * lda + kk);
+        const bf16x8 b = *reinterpret_cast<const bf16x8*>(B + r * ldb + kk);
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+    }
+    __device__ static __forceinline__ elem from_f32(float x) { return f32_to_bf16(x); }
+    __device__ static __forceinline__ float to_f32(elem x) { return bf16_to_f32(x); }
+};
+
+template <>
+struct Mma<F32> {
+    using elem = float;
+    static constexpr int KS = 4;
+    __device__ static __forceinline__ f32x4 step(const elem* A, int lda, const elem* B, int ldb,
+                                                 int k0, f32x4 c, int lane) {
+        const int r = lane & 15, kk = k0 + (lane >> 4);
+        return __builtin_amdgcn_mfma_f32_16x16x4f32(A[r * lda + kk], B[r * ldb + kk], c, 0, 0, 0);
+    }
+    __device__ static __forceinline__ elem from_f32(float x) { return x; }
+    __device__ static __forceinline__ float to_f32(elem x) { return x; }
+};
+
+// C += A[16 x K] * B[16 x K]^T over k in [k_begin, k_end), both multiples of Mma::KS.
+template <class T>
+__device__ __forceinline__ f32x4 mma_nt(const typename Mma<T>::elem* A, int lda,
+                                        const typename Mma<T>::elem* B, int ldb, int k_begin,
+                                        int k_end, f32x4 c, int lane) {
+    for (int k0 = k_begin; k0 < k_end; k0 += Mma<T>::KS) c = Mma<T>::step(A, lda, B, ldb, k0, c, lane);
+    return c;
+}
+
+}  // namespace kda

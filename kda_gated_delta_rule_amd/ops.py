@@ -1,0 +1,115 @@
+"""Thin wrappers: torch tensors -> C ABI calls of libkda.so (marshalling only)."""
+import torch
+
+from . import _lib
+
+_DTYPES = {torch.float32: _lib.KDA_F32, torch.bfloat16: _lib.KDA_BF16}
+
+
+def _stream(t):
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _need(cond, msg):
+    if not cond:
+        raise ValueError(msg)
+
+
+def _contig(*ts):
+    for t in ts:
+        if t is not None:
+            _need(t.is_contiguous(), "tensors must be contiguous")
+
+
+def decode_step(q, k, v, g, beta, state_pool, slot_idx, *, o=None, records=None, scale=None,
+                use_qk_l2norm=True):
+    """Decode / MTP step (kda_decode_step).
+
+    q, k [N, T, H, dk], v [N, T, H, dv] (bf16 or fp32); g [N, T, H, dk] fp32; beta [N, T, H]
+    fp32; state_pool [num_slots, H, dk, dv] fp32 (updated in place unless records is given);
+    slot_idx [N] int32.  records: None (commit) or an fp32 [N, T, H, 2dk + dv] tensor to fill
+    (verify: the pool is left untouched).  Returns o [N, T, H, dv] in the dtype of q.
+    """
+    N, T, H, dk = q.shape
+    dv = v.shape[-1]
+    _need(q.dtype in _DTYPES and k.dtype == q.dtype and v.dtype == q.dtype, "q/k/v dtype")
+    _need(g.dtype == torch.float32 and beta.dtype == torch.float32, "g and beta must be fp32")
+    _need(state_pool.dtype == torch.float32 and slot_idx.dtype == torch.int32, "pool/slot dtype")
+    _need(k.shape == q.shape and g.shape == q.shape and v.shape == (N, T, H, dv), "q/k/v/g shape")
+    _need(beta.shape == (N, T, H) and slot_idx.shape == (N,), "beta/slot_idx shape")
+    _need(state_pool.dim() == 4 and state_pool.shape[1:] == (H, dk, dv), "state_pool shape")
+    if o is None:
+        o = torch.empty(N, T, H, dv, dtype=q.dtype, device=q.device)
+    _need(o.shape == (N, T, H, dv) and o.dtype == q.dtype, "o shape/dtype")
+    if records is not None:
+        _need(records.shape == (N, T, H, 2 * dk + dv) and records.dtype == torch.float32,
+              "records shape/dtype")
+    _contig(q, k, v, g, beta, state_pool, slot_idx, o, records)
+    if scale is None:
+        scale = dk ** -0.5
+    st = _lib.load().kda_decode_step(
+        _ptr(q), _ptr(k), _ptr(v), _DTYPES[q.dtype], _ptr(g), _ptr(beta), _ptr(state_pool),
+        state_pool.shape[0], _ptr(slot_idx), N, T, H, dk, dv, float(scale), int(bool(use_qk_l2norm)),
+        _ptr(o), _ptr(records), _stream(q))
+    _lib.check("kda_decode_step", st)
+    return o
+
+
+def replay_commit(state_pool, slot_idx, records, accepted_len):
+    """ReplaySSM commit (kda_replay_commit): applies records[n, :accepted_len[n]] to the slots."""
+    N, T, H, R = records.shape
+    dk = state_pool.shape[2]
+    dv = state_pool.shape[3]
+    _need(R == 2 * dk + dv and state_pool.shape[1] == H, "records/state_pool shape")
+    _need(slot_idx.shape == (N,) and accepted_len.shape == (N,), "slot_idx/accepted_len shape")
+    _need(accepted_len.dtype == torch.int32 and slot_idx.dtype == torch.int32, "index dtype")
+    _contig(state_pool, slot_idx, records, accepted_len)
+    st = _lib.load().kda_replay_commit(_ptr(state_pool), state_pool.shape[0], _ptr(slot_idx),
+                                       _ptr(records), _ptr(accepted_len), N, T, H, dk, dv,
+                                       _stream(state_pool))
+    _lib.check("kda_replay_commit", st)
+
+
+def chunk_prefill_workspace_size(num_seqs, total_tokens, H, dk, dv, dtype=torch.bfloat16):
+    return int(_lib.load().kda_chunk_prefill_workspace_size(num_seqs, total_tokens, H, dk, dv,
+                                                            _DTYPES[dtype]))
+
+
+def chunk_prefill(q, k, v, g, beta, cu_seqlens, state_pool, slot_idx, *, h0_from_pool=True,
+                  o=None, workspace=None, scale=None, use_qk_l2norm=True):
+    """Varlen chunked prefill (kda_chunk_prefill).
+
+    q, k [T_total, H, dk], v [T_total, H, dv] (bf16 or fp32); g [T_total, H, dk] fp32;
+    beta [T_total, H] fp32; cu_seqlens [num_seqs + 1] int32; state_pool [num_slots, H, dk, dv]
+    fp32 (final states written to slot_idx [num_seqs] int32).  workspace: a uint8 tensor of at
+    least chunk_prefill_workspace_size(...) bytes, or None to allocate one.  Returns o.
+    """
+    Tt, H, dk = q.shape
+    dv = v.shape[-1]
+    ns = cu_seqlens.shape[0] - 1
+    _need(q.dtype in _DTYPES and k.dtype == q.dtype and v.dtype == q.dtype, "q/k/v dtype")
+    _need(g.dtype == torch.float32 and beta.dtype == torch.float32, "g and beta must be fp32")
+    _need(k.shape == q.shape and g.shape == q.shape and v.shape == (Tt, H, dv), "q/k/v/g shape")
+    _need(beta.shape == (Tt, H), "beta shape")
+    _need(cu_seqlens.dtype == torch.int32 and slot_idx.dtype == torch.int32, "index dtype")
+    _need(slot_idx.shape == (ns,), "slot_idx shape")
+    _need(state_pool.dim() == 4 and state_pool.shape[1:] == (H, dk, dv), "state_pool shape")
+    if o is None:
+        o = torch.empty(Tt, H, dv, dtype=q.dtype, device=q.device)
+    need = chunk_prefill_workspace_size(ns, Tt, H, dk, dv, q.dtype)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _contig(q, k, v, g, beta, cu_seqlens, state_pool, slot_idx, o, workspace)
+    if scale is None:
+        scale = dk ** -0.5
+    st = _lib.load().kda_chunk_prefill(
+        _ptr(q), _ptr(k), _ptr(v), _DTYPES[q.dtype], _ptr(g), _ptr(beta), _ptr(cu_seqlens), ns,
+        Tt, _ptr(state_pool), state_pool.shape[0], _ptr(slot_idx), int(bool(h0_from_pool)), H, dk,
+        dv, float(scale), int(bool(use_qk_l2norm)), _ptr(o), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(q))
+    _lib.check("kda_chunk_prefill", st)
+    return o

@@ -1,0 +1,138 @@
+"""CPU checks of the C ABI: the library loads, exports every function include/kda.h
+declares, and rejects invalid arguments on the host before any HIP call (so these
+run without a GPU).  Pointers here are fake, never dereferenced: every call below
+fails validation or returns early before a launch.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from kda_gated_delta_rule_amd import _build, _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_build.LIB):
+        _build.build(force=True)
+    return _lib.load()
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "kda.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(kda_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert set(names) == set(_lib.SIGNATURES), names
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    for code in (0, -1, -2, -3, -4):
+        s = _lib.status_string(code)
+        assert s.startswith("KDA_")
+    assert "unknown" in _lib.status_string(7)
+
+
+A = 0x10000  # a 16-byte aligned fake address
+
+
+def decode_args(**over):
+    args = dict(q=A, k=A, v=A, dtype=1, g=A, beta=A, pool=A, num_slots=8, slot=A, N=4, T=1, H=2,
+                dk=128, dv=128, scale=0.1, l2=1, o=A, rec=None, stream=None)
+    args.update(over)
+    return list(args.values())
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(q=None), _lib.KDA_ERR_INVALID_ARG),
+    (dict(o=None), _lib.KDA_ERR_INVALID_ARG),
+    (dict(slot=None), _lib.KDA_ERR_INVALID_ARG),
+    (dict(q=A + 4), _lib.KDA_ERR_INVALID_ARG),
+    (dict(rec=A + 8), _lib.KDA_ERR_INVALID_ARG),
+    (dict(dtype=2), _lib.KDA_ERR_INVALID_ARG),
+    (dict(T=0), _lib.KDA_ERR_INVALID_ARG),
+    (dict(H=0), _lib.KDA_ERR_INVALID_ARG),
+    (dict(N=-1), _lib.KDA_ERR_INVALID_ARG),
+    (dict(num_slots=0), _lib.KDA_ERR_INVALID_ARG),
+    (dict(l2=2), _lib.KDA_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), _lib.KDA_ERR_INVALID_ARG),
+    (dict(dk=96), _lib.KDA_ERR_UNSUPPORTED),
+    (dict(dv=256), _lib.KDA_ERR_UNSUPPORTED),
+    (dict(N=0), _lib.KDA_OK),  # nothing to do: returns before any launch
+])
+def test_decode_validation(lib, over, code):
+    assert lib.kda_decode_step(*decode_args(**over)) == code
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(pool=None), _lib.KDA_ERR_INVALID_ARG),
+    (dict(rec=None), _lib.KDA_ERR_INVALID_ARG),
+    (dict(acc=None), _lib.KDA_ERR_INVALID_ARG),
+    (dict(acc=A + 4), _lib.KDA_ERR_INVALID_ARG),
+    (dict(T=0), _lib.KDA_ERR_INVALID_ARG),
+    (dict(dk=32), _lib.KDA_ERR_UNSUPPORTED),
+    (dict(N=0), _lib.KDA_OK),
+])
+def test_replay_validation(lib, over, code):
+    args = dict(pool=A, num_slots=8, slot=A, rec=A, acc=A, N=2, T=8, H=2, dk=128, dv=128,
+                stream=None)
+    args.update(over)
+    assert lib.kda_replay_commit(*args.values()) == code
+
+
+def prefill_args(**over):
+    args = dict(q=A, k=A, v=A, dtype=1, g=A, beta=A, cu=A, ns=2, T=200, pool=A, num_slots=4,
+                slot=A, h0=1, H=2, dk=128, dv=128, scale=0.1, l2=1, o=A, ws=A, ws_bytes=0,
+                stream=None)
+    args.update(over)
+    return args
+
+
+def test_prefill_workspace_size(lib):
+    f = lib.kda_chunk_prefill_workspace_size
+    small = f(1, 64, 1, 128, 128, 1)
+    assert small > 0
+    assert f(1, 128, 1, 128, 128, 1) > small
+    assert f(1, 64, 2, 128, 128, 1) > small
+    assert f(1, 64, 1, 128, 128, 0) > small  # fp32 operands are wider
+    assert f(1, 64, 1, 96, 128, 1) == 0      # unsupported dim
+    assert f(-1, 64, 1, 128, 128, 1) == 0
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(q=None), _lib.KDA_ERR_INVALID_ARG),
+    (dict(cu=None), _lib.KDA_ERR_INVALID_ARG),
+    (dict(g=A + 4), _lib.KDA_ERR_INVALID_ARG),
+    (dict(h0=3), _lib.KDA_ERR_INVALID_ARG),
+    (dict(ns=0), _lib.KDA_ERR_INVALID_ARG),  # tokens without sequences
+    (dict(ns=0, T=0), _lib.KDA_OK),
+    (dict(T=-5), _lib.KDA_ERR_INVALID_ARG),
+    (dict(dk=100), _lib.KDA_ERR_UNSUPPORTED),
+    (dict(dtype=0, dk=128), _lib.KDA_ERR_UNSUPPORTED),  # fp32 prefill needs dk = 64
+    (dict(ws=None), _lib.KDA_ERR_WORKSPACE),
+    (dict(ws_bytes=1024), _lib.KDA_ERR_WORKSPACE),
+])
+def test_prefill_validation(lib, over, code):
+    # ws_bytes stays too small, so a case that passes every other check stops at the
+    # workspace check, before any launch
+    assert lib.kda_chunk_prefill(*prefill_args(**over).values()) == code
+
+
+def test_prefill_valid_arguments_reach_workspace_check(lib):
+    # all arguments valid except the workspace size: the call must stop at that check
+    assert lib.kda_chunk_prefill(*prefill_args().values()) == _lib.KDA_ERR_WORKSPACE
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(_lib, "_LIB", None)
+    monkeypatch.setattr(_lib, "lib_path", lambda: str(tmp_path / "missing.so"))
+    with pytest.raises(ImportError):
+        _lib.load()

@@ -1,0 +1,217 @@
+"""GPU parity of the decode / MTP / verify kernel and the ReplaySSM commit kernel
+against the fp64 oracle, through the C ABI (python binding -> libkda.so).
+
+Tolerances (relative L2 over the whole tensor): 1e-4 for fp32 q/k/v, 1e-2 for bf16
+q/k/v with an fp32 state.  Slot mapping, untouched slots and the bf16 output
+rounding are checked bit for bit.
+"""
+import numpy as np
+import pytest
+import torch
+
+import kda_gated_delta_rule_amd as kda
+import kda_workloads as W
+from oracle import kda_oracle as O
+from tests._util import announce, f64, need_gpu, rel_l2, worst_rel_l2
+
+pytestmark = pytest.mark.gpu
+
+NAMES = ("q", "k", "v", "g", "beta")
+
+
+def run_decode(x, dev, records=False, **kw):
+    pool = x["pool"].to(dev)
+    args = [x[n].to(dev) for n in NAMES]
+    rec = None
+    if records:
+        N, T, H, dk = x["q"].shape
+        dv = x["v"].shape[-1]
+        rec = torch.full((N, T, H, 2 * dk + dv), float("nan"), device=dev)
+    o = kda.decode_step(*args, pool, x["slot_idx"].to(dev), records=rec, **kw)
+    torch.cuda.synchronize()
+    return o, pool, rec
+
+
+def oracle_decode(x, want_records=False, **kw):
+    sl = x["slot_idx"].long()
+    return O.decode(*(f64(x[n]) for n in NAMES), f64(x["pool"][sl]), want_records=want_records, **kw)
+
+
+def test_tiny_fp32_through_decode():
+    """Tiny fp32 recurrent case (1 sequence, T = 64, H = 2, d = 64) run as one 64-token MTP call."""
+    dev = need_gpu()
+    announce("decode tiny fp32 T=64 H=2 d=64")
+    t = W.tiny(seed=0)
+    x = {n: t[n][None] for n in NAMES}
+    x["pool"] = torch.zeros(1, 2, 64, 64)
+    x["slot_idx"] = torch.zeros(1, dtype=torch.int32)
+    o, pool, _ = run_decode(x, dev, scale=64 ** -0.5)
+    o_ref, h_ref, _ = oracle_decode(x, scale=64 ** -0.5)
+    assert rel_l2(f64(o), o_ref) <= 1e-4
+    assert rel_l2(f64(pool.cpu()), h_ref) <= 1e-4
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_decode_pool_full_size(seed):
+    """Decode step over a state pool: 512 slots [H=32, 128, 128], 64 sequences, bf16 q/k/v."""
+    dev = need_gpu()
+    announce("decode pool512 N64 H32 d128 bf16 seed=%d" % seed)
+    x = W.decode(seed=seed)
+    o, pool, _ = run_decode(x, dev)
+    o_ref, h_ref, _ = oracle_decode(x)
+    sl = x["slot_idx"].long()
+    got = pool.cpu()
+    assert rel_l2(f64(o), o_ref) <= 1e-2
+    assert rel_l2(f64(got[sl]), h_ref) <= 1e-2
+    assert worst_rel_l2(f64(o)[:, 0], o_ref[:, 0], axis=1) <= 2e-2
+    untouched = torch.ones(x["pool"].shape[0], dtype=torch.bool)
+    untouched[sl] = False
+    assert torch.equal(got[untouched], x["pool"][untouched])
+
+
+@pytest.mark.parametrize("dk,dv", [(64, 64), (64, 128), (128, 64)])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_decode_head_dims(dk, dv, dtype):
+    dev = need_gpu()
+    announce("decode dims dk=%d dv=%d %s" % (dk, dv, dtype))
+    x = W.decode(seed=3, N=5, T=3, H=3, dk=dk, dv=dv, num_slots=9, dtype=dtype)
+    o, pool, _ = run_decode(x, dev)
+    o_ref, h_ref, _ = oracle_decode(x)
+    tol = 1e-4 if dtype == torch.float32 else 1e-2
+    assert rel_l2(f64(o), o_ref) <= tol
+    assert rel_l2(f64(pool.cpu()[x["slot_idx"].long()]), h_ref) <= tol
+
+
+@pytest.mark.parametrize("T", [2, 8, 9, 20])
+def test_mtp_multi_token(T):
+    """T > 1 (MTP): tokens are applied in order with the state kept on chip; crosses the
+    8-token LDS blocks."""
+    dev = need_gpu()
+    announce("decode MTP T=%d" % T)
+    x = W.decode(seed=4, N=6, T=T, H=4, dk=128, dv=128, num_slots=16, dtype=torch.float32)
+    o, pool, _ = run_decode(x, dev)
+    o_ref, h_ref, _ = oracle_decode(x)
+    assert rel_l2(f64(o), o_ref) <= 1e-4
+    assert rel_l2(f64(pool.cpu()[x["slot_idx"].long()]), h_ref) <= 1e-4
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_slot_mapping_bit_exact(dtype):
+    """beta = 0, g = 0, no norm, scale = 1, q = e_i: o[n, h] = S[slot_n, h, i, :] exactly
+    (rounded by the hardware bf16 conversion in bf16 mode, which must equal torch's cast),
+    and every slot of the pool is byte-identical afterwards."""
+    dev = need_gpu()
+    announce("decode slot mapping %s" % dtype)
+    N, H, d, num_slots = 24, 4, 128, 64
+    gen = torch.Generator().manual_seed(7)
+    pool = torch.randn(num_slots, H, d, d, generator=gen) * 3.0
+    slots = torch.randperm(num_slots, generator=gen)[:N].to(torch.int32)
+    rows = torch.randint(0, d, (N, H), generator=gen)
+    q = torch.zeros(N, 1, H, d)
+    q[torch.arange(N)[:, None], 0, torch.arange(H)[None, :], rows] = 1.0
+    x = dict(q=q.to(dtype), k=torch.randn(N, 1, H, d, generator=gen).to(dtype),
+             v=torch.randn(N, 1, H, d, generator=gen).to(dtype), g=torch.zeros(N, 1, H, d),
+             beta=torch.zeros(N, 1, H), pool=pool, slot_idx=slots)
+    o, pool_after, _ = run_decode(x, dev, scale=1.0, use_qk_l2norm=False)
+    expect = pool[slots.long()[:, None], torch.arange(H)[None, :], rows]  # [N, H, d]
+    assert torch.equal(o.cpu()[:, 0], expect.to(dtype))
+    assert torch.equal(pool_after.cpu(), pool)
+
+
+def test_skipped_slot():
+    """A negative slot index skips the sequence: zero output, pool untouched."""
+    dev = need_gpu()
+    announce("decode skipped slot")
+    x = W.decode(seed=5, N=4, T=2, H=2, dk=128, dv=128, num_slots=8)
+    x["slot_idx"][2] = -1
+    o, pool, _ = run_decode(x, dev)
+    assert torch.count_nonzero(o[2]).item() == 0
+    keep = [0, 1, 3]
+    y = {n: x[n][keep] for n in NAMES}
+    y["pool"], y["slot_idx"] = x["pool"], x["slot_idx"][keep]
+    o_ref, h_ref, _ = oracle_decode(y)
+    assert rel_l2(f64(o[keep]), o_ref) <= 1e-2
+    got = pool.cpu()
+    assert rel_l2(f64(got[y["slot_idx"].long()]), h_ref) <= 1e-2
+    others = torch.ones(8, dtype=torch.bool)
+    others[y["slot_idx"].long()] = False
+    assert torch.equal(got[others], x["pool"][others])
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_verify_and_replay_full_size(seed):
+    """Speculative verify (32 sequences x 8 tokens, H = 32, d = 128) then ReplaySSM commit of
+    accepted lengths drawn from 1..8, against direct recurrence over the accepted tokens."""
+    dev = need_gpu()
+    announce("verify+replay N32 T8 H32 d128 seed=%d" % seed)
+    x = W.verify(seed=seed)
+    o, pool, rec = run_decode(x, dev, records=True)
+    got = pool.cpu()
+    assert torch.equal(got, x["pool"]), "verify must not touch the pool"
+    o_ref, _, rec_ref = oracle_decode(x, want_records=True)
+    assert rel_l2(f64(o), o_ref) <= 1e-2
+    assert rel_l2(f64(rec), rec_ref) <= 1e-2
+    acc = x["accepted"]
+    kda.replay_commit(pool, x["slot_idx"].to(dev), rec, acc.to(dev))
+    torch.cuda.synchronize()
+    got = pool.cpu()
+    sl = x["slot_idx"].long()
+    for n in range(x["q"].shape[0]):
+        a = int(acc[n])
+        _, h_n, _ = O.decode(*(f64(x[nm][n:n + 1, :a]) for nm in NAMES), f64(x["pool"][sl[n:n + 1]]))
+        assert rel_l2(f64(got[sl[n]]), h_n[0]) <= 1e-2, n
+    others = torch.ones(x["pool"].shape[0], dtype=torch.bool)
+    others[sl] = False
+    assert torch.equal(got[others], x["pool"][others])
+
+
+def test_replay_bit_exact_with_commit():
+    """Replaying a prefix of verify records reproduces, bit for bit, the state that committing
+    the same tokens with the decode kernel gives (same fp32 operations)."""
+    dev = need_gpu()
+    announce("replay vs commit bit-exact")
+    x = W.verify(seed=3, N=12, H=4, num_slots=32)
+    _, pool_v, rec = run_decode(x, dev, records=True)
+    acc = x["accepted"]
+    kda.replay_commit(pool_v, x["slot_idx"].to(dev), rec, acc.to(dev))
+    pool_c = x["pool"].to(dev)
+    for a in sorted(set(int(v) for v in acc)):
+        idx = (acc == a).nonzero().flatten()
+        args = [x[n][idx, :a].contiguous().to(dev) for n in NAMES]
+        kda.decode_step(*args, pool_c, x["slot_idx"][idx].contiguous().to(dev))
+    torch.cuda.synchronize()
+    assert torch.equal(pool_v.cpu(), pool_c.cpu())
+
+
+def test_replay_accept_zero_and_skip():
+    dev = need_gpu()
+    announce("replay accepted=0 and skipped slot")
+    x = W.verify(seed=6, N=4, H=2, num_slots=8)
+    _, pool, rec = run_decode(x, dev, records=True)
+    acc = torch.tensor([0, 8, 3, 5], dtype=torch.int32)
+    slots = x["slot_idx"].clone()
+    slots[3] = -1
+    kda.replay_commit(pool, slots.to(dev), rec, acc.to(dev))
+    torch.cuda.synchronize()
+    got = pool.cpu()
+    sl = x["slot_idx"].long()
+    assert torch.equal(got[sl[0]], x["pool"][sl[0]])
+    assert torch.equal(got[sl[3]], x["pool"][sl[3]])
+    for n in (1, 2):
+        a = int(acc[n])
+        _, h_n, _ = O.decode(*(f64(x[nm][n:n + 1, :a]) for nm in NAMES), f64(x["pool"][sl[n:n + 1]]))
+        assert rel_l2(f64(got[sl[n]]), h_n[0]) <= 1e-2
+
+
+def test_invariant_beta1_unit_key_on_gpu():
+    """beta = 1 with a unit key (fp32): after the step S^T k = v up to fp32 rounding."""
+    dev = need_gpu()
+    announce("decode invariant beta=1 unit key")
+    x = W.decode(seed=8, N=8, T=1, H=4, dk=128, dv=128, num_slots=8, dtype=torch.float32)
+    x["beta"] = torch.ones_like(x["beta"])
+    x["k"] = torch.nn.functional.normalize(x["k"], dim=-1)
+    _, pool, _ = run_decode(x, dev, use_qk_l2norm=False)
+    S = f64(pool.cpu()[x["slot_idx"].long()])
+    k = f64(x["k"])[:, 0]
+    got = np.einsum("nhcj,nhc->nhj", S, k)
+    assert np.abs(got - f64(x["v"])[:, 0]).max() <= 1e-5 * max(1.0, np.abs(S).max())

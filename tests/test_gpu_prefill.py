@@ -1,0 +1,163 @@
+"""GPU parity of the chunked prefill against the fp64 token recurrence (oracle),
+through the C ABI.  Small varlen cases are compared element-wise in full; the two
+full-size workloads (T = 8192 x H = 32, and the 4-sequence 128,076-token H = 16
+batch) are compared on sampled heads, whose oracle chains are computed in full.
+"""
+import numpy as np
+import pytest
+import torch
+
+import kda_gated_delta_rule_amd as kda
+import kda_workloads as W
+from oracle import kda_oracle as O
+from tests._util import announce, f64, need_gpu, rel_l2, worst_rel_l2
+
+pytestmark = pytest.mark.gpu
+
+NAMES = ("q", "k", "v", "g", "beta")
+
+
+def run_prefill(y, dev, h0_from_pool=True, **kw):
+    pool = y["pool"].to(dev)
+    o = kda.chunk_prefill(*(y[n].to(dev) for n in NAMES), y["cu_seqlens"].to(dev), pool,
+                          y["slot_idx"].to(dev), h0_from_pool=h0_from_pool, **kw)
+    torch.cuda.synchronize()
+    return o, pool
+
+
+def oracle_prefill(y, h0_from_pool=True, heads=None, **kw):
+    sl = y["slot_idx"].long()
+    pick = (lambda t: t) if heads is None else (lambda t: t[:, heads])
+    h0 = f64(y["pool"][sl]) if h0_from_pool else None
+    if h0 is not None and heads is not None:
+        h0 = h0[:, heads]
+    return O.recurrent(*(f64(pick(y[n])) for n in NAMES), y["cu_seqlens"].numpy(), h0=h0, **kw)
+
+
+def test_tiny_fp32_through_prefill():
+    """Tiny fp32 case (T = 64, H = 2, d = 64): exactly one 64-token chunk; rel-L2 <= 1e-4."""
+    dev = need_gpu()
+    announce("prefill tiny fp32 one chunk")
+    t = W.tiny(seed=0)
+    y = dict(t)
+    y["cu_seqlens"] = torch.tensor([0, 64], dtype=torch.int32)
+    y["pool"] = torch.full((1, 2, 64, 64), 7.0)  # h0_from_pool = 0: contents must not matter
+    y["slot_idx"] = torch.zeros(1, dtype=torch.int32)
+    o, pool = run_prefill(y, dev, h0_from_pool=False, scale=64 ** -0.5)
+    o_ref, h_ref, _ = oracle_prefill(y, h0_from_pool=False, scale=64 ** -0.5)
+    assert rel_l2(f64(o), o_ref) <= 1e-4
+    assert rel_l2(f64(pool.cpu()), h_ref) <= 1e-4
+
+
+@pytest.mark.parametrize("dv", [64, 128])
+def test_fp32_varlen_ragged(dv):
+    """fp32 (dk = 64): ragged varlen batch with tails, an empty sequence and h0 from slots."""
+    dev = need_gpu()
+    announce("prefill fp32 varlen dk=64 dv=%d" % dv)
+    y = W.prefill(seed=1, seqlens=(1, 63, 64, 65, 0, 200, 130), H=3, dk=64, dv=dv, num_slots=10,
+                  h0_std=0.05, dtype=torch.float32)
+    o, pool = run_prefill(y, dev)
+    o_ref, h_ref, _ = oracle_prefill(y)
+    assert rel_l2(f64(o), o_ref) <= 1e-4
+    assert rel_l2(f64(pool.cpu()[y["slot_idx"].long()]), h_ref) <= 1e-4
+
+
+@pytest.mark.parametrize("dk,dv", [(128, 128), (64, 64), (128, 64), (64, 128)])
+def test_bf16_varlen_ragged(dk, dv):
+    dev = need_gpu()
+    announce("prefill bf16 varlen dk=%d dv=%d" % (dk, dv))
+    y = W.prefill(seed=2, seqlens=(1, 63, 64, 65, 0, 200, 777), H=4, dk=dk, dv=dv, num_slots=12,
+                  h0_std=0.05)
+    o, pool = run_prefill(y, dev)
+    o_ref, h_ref, _ = oracle_prefill(y)
+    assert rel_l2(f64(o), o_ref) <= 1e-2
+    got = pool.cpu()
+    sl = y["slot_idx"].long()
+    assert rel_l2(f64(got[sl]), h_ref) <= 1e-2
+    others = torch.ones(12, dtype=torch.bool)
+    others[sl] = False
+    assert torch.equal(got[others], y["pool"][others])
+
+
+def test_zero_initial_state_ignores_pool_contents():
+    dev = need_gpu()
+    announce("prefill h0 zero")
+    y = W.prefill(seed=3, seqlens=(150, 20), H=2, dk=128, dv=128, num_slots=2, h0_std=1.0)
+    o, pool = run_prefill(y, dev, h0_from_pool=False)
+    o_ref, h_ref, _ = oracle_prefill(y, h0_from_pool=False)
+    assert rel_l2(f64(o), o_ref) <= 1e-2
+    assert rel_l2(f64(pool.cpu()[y["slot_idx"].long()]), h_ref) <= 1e-2
+
+
+def test_fp32_prefill_with_dk128_is_rejected():
+    dev = need_gpu()
+    y = W.prefill(seed=6, seqlens=(10,), H=1, dk=128, dv=128, num_slots=1, dtype=torch.float32)
+    with pytest.raises(kda.KdaError) as e:
+        run_prefill(y, dev)
+    assert e.value.status == -2
+
+
+def test_empty_sequence_passes_state_through():
+    dev = need_gpu()
+    announce("prefill empty sequence")
+    y = W.prefill(seed=4, seqlens=(0, 70, 0), H=2, dk=128, dv=128, num_slots=3, h0_std=0.05)
+    _, pool = run_prefill(y, dev)
+    got = pool.cpu()
+    sl = y["slot_idx"].long()
+    assert torch.equal(got[sl[0]], y["pool"][sl[0]])
+    assert torch.equal(got[sl[2]], y["pool"][sl[2]])
+
+
+@pytest.mark.parametrize("dtype,d,tol", [(torch.float32, 64, 1e-4), (torch.bfloat16, 128, 1e-2)])
+def test_prefill_then_decode_equals_longer_prefill(dtype, d, tol):
+    """Checkpoint / resume through the pool: prefill(x[:a]) then decode(x[a:]) equals the
+    recurrence over x (state handed over in the slot)."""
+    dev = need_gpu()
+    announce("prefill then decode handover %s d=%d" % (dtype, d))
+    y = W.prefill(seed=5, seqlens=(131,), H=4, dk=d, dv=d, num_slots=1, h0_std=0.05, dtype=dtype)
+    a = 128
+    head = {n: y[n][:a] for n in NAMES}
+    head.update(cu_seqlens=torch.tensor([0, a], dtype=torch.int32), pool=y["pool"],
+                slot_idx=y["slot_idx"])
+    _, pool = run_prefill(head, dev)
+    tail = [y[n][a:][None].contiguous().to(dev) for n in NAMES]
+    o_tail = kda.decode_step(*tail, pool, y["slot_idx"].to(dev))
+    torch.cuda.synchronize()
+    o_ref, h_ref, _ = oracle_prefill(y)
+    assert rel_l2(f64(o_tail[0]), o_ref[a:]) <= tol
+    assert rel_l2(f64(pool.cpu()[0]), h_ref[0]) <= tol
+
+
+def test_prefill_full_size_T8192_H32():
+    """Chunked prefill workload: T = 8192, H = 32, dk = dv = 128, bf16, zero initial state.
+    Oracle on 3 sampled heads (full 8192-token chains); every output must be finite."""
+    dev = need_gpu()
+    announce("prefill T8192 H32 d128")
+    y = W.prefill(seed=0, seqlens=(8192,), H=32, dk=128, dv=128, num_slots=1)
+    o, pool = run_prefill(y, dev, h0_from_pool=False)
+    assert torch.isfinite(o).all()
+    heads = [0, 13, 31]
+    o_ref, h_ref, _ = oracle_prefill(y, h0_from_pool=False, heads=heads)
+    assert rel_l2(f64(o[:, heads]), o_ref) <= 1e-2
+    assert worst_rel_l2(f64(o[:, heads]), o_ref, axis=1) <= 1e-2
+    assert rel_l2(f64(pool.cpu()[0, heads]), h_ref[0]) <= 1e-2
+
+
+def test_prefill_full_size_varlen_long_context():
+    """Long-context varlen workload: 4 sequences (100000, 16384, 8192, 3500) packed with
+    cu_seqlens, H = 16, initial states from 4 pool slots.  Oracle on 2 sampled heads over
+    all four sequences (the 100,000-token chain included)."""
+    dev = need_gpu()
+    announce("prefill varlen 128076 tokens H16")
+    y = W.prefill_long(seed=0)
+    o, pool = run_prefill(y, dev)
+    assert torch.isfinite(o).all()
+    heads = [2, 11]
+    o_ref, h_ref, _ = oracle_prefill(y, heads=heads)
+    assert rel_l2(f64(o[:, heads]), o_ref) <= 1e-2
+    sl = y["slot_idx"].long()
+    assert rel_l2(f64(pool.cpu()[sl][:, heads]), h_ref) <= 1e-2
+    # per-sequence outputs
+    cu = y["cu_seqlens"].tolist()
+    for i in range(4):
+        assert rel_l2(f64(o[cu[i]:cu[i + 1], heads]), o_ref[cu[i]:cu[i + 1]]) <= 1e-2, i
