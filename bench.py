@@ -1,0 +1,344 @@
+#!/usr/bin/env python3
+"""Benchmark of the KDA hot path on one MI355X.
+
+Timed step (the headline metric): one fused decode step over the state pool of
+the decode workload -- 512 fp32 slots of [H=32, 128, 128], 64 active sequences,
+1 token each, bf16 q/k/v, state updated in place.  Successive steps cycle through
+8 disjoint sets of 64 slots (the whole 1 GiB pool), so state reads come from HBM
+rather than the 256 MB Infinity Cache.
+
+value = state updates per second = (sequences x heads) x steps / elapsed.
+
+Also measured in the same run (reported under "extra", not part of the timed
+step): chunked prefill (T = 8192, H = 32) and the long-context varlen prefill
+(4 sequences, 128,076 tokens, H = 16) as tokens/s with their MFMA and HBM
+fractions; speculative verify + ReplaySSM commit (32 x 8 tokens, H = 32); a
+device copy of 1 GiB as a bandwidth reference; and the fp64 CPU oracle on a
+bounded sample of the decode workload (cpu_baseline).
+
+Prints ONE JSON line.
+"""
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, vendor figure
+METRIC = ("KDA decode state-updates/s (HBM GB/s % peak); "
+          "chunked-prefill tokens/s (MFMA %)")
+
+
+def decode_bytes_per_update(dk, dv, io_bytes):
+    """Algorithmic HBM bytes of one (token, head) decode update: the fp32 state read and
+    written once, q, k, v and o in the io dtype, g (fp32 per key channel) and beta."""
+    return 2 * dk * dv * 4 + (2 * dk + dv) * io_bytes + dk * 4 + 4 + dv * io_bytes
+
+
+def prefill_bytes_per_token_head(dk, dv, io_bytes):
+    """q, k, v read + o written (io dtype), g (fp32) and beta read, once each."""
+    return (2 * dk + dv) * io_bytes + dk * 4 + 4 + dv * io_bytes
+
+
+def prefill_flops_per_token_head(dk, dv, C=64):
+    """Algorithmic flops per (token, head) of the 64-token chunk form, counting every
+    intra-chunk product as a dense C x C tile: A and P (2 C^2 dk each), the W and Ut
+    triangular solves (2 C^2 dk and 2 C^2 dv), Q' = QG - P W and Ot = P Ut (2 C^2 dk and
+    2 C^2 dv) -- together 2 C^2 (3 dk + 2 dv) -- plus the three state products W S, Q' S and
+    Kt U (2 C dk dv each); divided by the C tokens of a chunk."""
+    per_chunk = 2 * C * C * (3 * dk + 2 * dv) + 3 * 2 * C * dk * dv
+    return per_chunk / C
+
+
+def counted_traffic(path):
+    """HBM bytes per launch measured by the rocprofv3 FETCH_SIZE / WRITE_SIZE runs recorded in
+    `path` (scaled by a copy kernel of known size), or None when the kernel sources have changed
+    since those counters were taken."""
+    import hashlib
+
+    try:
+        rec = json.load(open(path))
+        src = b"".join(open(os.path.join(ROOT, f), "rb").read() for f in rec["sources"])
+    except (OSError, ValueError, KeyError):
+        return None
+    if hashlib.sha256(src).hexdigest() != rec.get("source_sha256"):
+        return None
+    return rec["traffic_bytes_per_launch"]
+
+
+def time_loop(fn, steps, sync):
+    """Runs fn(i) for i in range(steps) with HIP events around every call on the current
+    stream; returns (total elapsed seconds, mean per-call seconds)."""
+    import torch
+
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    sync()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        starts[i].record()
+        fn(i)
+        ends[i].record()
+    sync()
+    total = time.perf_counter() - t0
+    per = sum(s.elapsed_time(e) for s, e in zip(starts, ends)) / steps / 1e3
+    return total, per
+
+
+def bench_decode(args, dev, log):
+    import torch
+
+    import kda_gated_delta_rule_amd as kda
+    import kda_workloads as W
+
+    cfg = W.DECODE
+    x = W.decode(seed=0)
+    N, H, dk, dv, ns = cfg["N"], cfg["H"], cfg["dk"], cfg["dv"], cfg["num_slots"]
+    pool = x["pool"].to(dev)
+    q, k, v, g, beta = (x[n].to(dev) for n in ("q", "k", "v", "g", "beta"))
+    o = torch.empty_like(q)
+    # 8 disjoint 64-slot sets covering the pool; set 0 is the workload's own slot set
+    rest = [s for s in torch.randperm(ns, generator=torch.Generator().manual_seed(1)).tolist()
+            if s not in set(x["slot_idx"].tolist())]
+    sets = [x["slot_idx"]] + [torch.tensor(rest[i * N:(i + 1) * N], dtype=torch.int32)
+                              for i in range(ns // N - 1)]
+    sets = [s.to(dev) for s in sets]
+
+    def step(i):
+        kda.decode_step(q, k, v, g, beta, pool, sets[i % len(sets)], o=o)
+
+    # Decode runs as a captured HIP graph (as serving engines run it): the warmup graph
+    # holds exactly `warmup` steps, the timed graph exactly `steps` steps.
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step(0)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graphs = []
+    for n in (args.warmup, args.steps):
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr):
+            for i in range(n):
+                step(i)
+        graphs.append(gr)
+    if args.warmup:
+        graphs[0].replay()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record()
+    graphs[1].replay()
+    ev1.record()
+    torch.cuda.synchronize()
+    total = time.perf_counter() - t0
+    per = ev0.elapsed_time(ev1) / 1e3 / args.steps  # HIP-event time per launch
+    updates = N * H
+    bpu = decode_bytes_per_update(dk, dv, 2)
+    achieved = updates * bpu / per / 1e9
+    log("decode (graph): %.2f us/step wall, %.2f us/launch (events), %.3f GB/s algorithmic"
+        % (total / args.steps * 1e6, per * 1e6, achieved))
+    return dict(total=total, per=per, updates=updates, bytes_per_update=bpu, achieved=achieved,
+                inputs=x)
+
+
+def bench_verify_replay(args, dev, log):
+    import torch
+
+    import kda_gated_delta_rule_amd as kda
+    import kda_workloads as W
+
+    x = W.verify(seed=0)
+    N, T, H, dk, dv = x["q"].shape[0], x["q"].shape[1], x["q"].shape[2], 128, 128
+    pool = x["pool"].to(dev)
+    q, k, v, g, beta = (x[n].to(dev) for n in ("q", "k", "v", "g", "beta"))
+    slots, acc = x["slot_idx"].to(dev), x["accepted"].to(dev)
+    rec = torch.empty(N, T, H, 2 * dk + dv, device=dev)
+    o = torch.empty_like(q)
+    pool_bytes = dk * dv * 4
+
+    def step(i):
+        kda.decode_step(q, k, v, g, beta, pool, slots, o=o, records=rec)
+        kda.replay_commit(pool, slots, rec, acc)
+
+    iters = max(10, args.steps // 4)
+    for i in range(3):
+        step(i)
+    total, per = time_loop(step, iters, torch.cuda.synchronize)
+    acc_sum = int(x["accepted"].sum())
+    verify_bytes = N * H * (pool_bytes + T * ((2 * dk + dv) * 2 + dk * 4 + 4 + dv * 2 +
+                                               (2 * dk + dv) * 4))
+    commit_bytes = N * H * 2 * pool_bytes + acc_sum * H * (2 * dk + dv) * 4
+    gbs = (verify_bytes + commit_bytes) / per / 1e9
+    log("verify+replay: %.2f us/step, %.1f GB/s" % (per * 1e6, gbs))
+    return {"workload": W.VERIFY["name"], "us_per_step": per * 1e6,
+            "sequence_tokens_per_s": N * T / per, "accepted_tokens": acc_sum,
+            "algorithmic_bytes": verify_bytes + commit_bytes, "achieved_GBs": gbs,
+            "hbm_frac": gbs / HBM_PEAK_GBS}
+
+
+def bench_prefill(args, dev, log, which):
+    import torch
+
+    import kda_gated_delta_rule_amd as kda
+    import kda_workloads as W
+
+    if which == "prefill":
+        y, name, h0 = W.prefill(seed=0), W.PREFILL["name"], False
+    else:
+        y, name, h0 = W.prefill_long(seed=0), W.VARLEN["name"], True
+    Tt, H, dk = y["q"].shape
+    dv = y["v"].shape[-1]
+    ns = y["cu_seqlens"].shape[0] - 1
+    q, k, v, g, beta, cu = (y[n].to(dev) for n in ("q", "k", "v", "g", "beta", "cu_seqlens"))
+    pool, slots = y["pool"].to(dev), y["slot_idx"].to(dev)
+    o = torch.empty_like(v)
+    ws = torch.empty(kda.chunk_prefill_workspace_size(ns, Tt, H, dk, dv), dtype=torch.uint8,
+                     device=dev)
+
+    def step(i):
+        kda.chunk_prefill(q, k, v, g, beta, cu, pool, slots, h0_from_pool=h0, o=o, workspace=ws)
+
+    iters = max(5, args.steps // 10)
+    for i in range(2):
+        step(i)
+    total, per = time_loop(step, iters, torch.cuda.synchronize)
+    th = Tt * H
+    flops = th * prefill_flops_per_token_head(dk, dv)
+    byts = th * prefill_bytes_per_token_head(dk, dv, 2)
+    tflops = flops / per / 1e12
+    gbs = byts / per / 1e9
+    log("%s: %.1f us/call, %.3g tokens/s, %.1f TFLOP/s (%.1f%% MFMA), %.0f GB/s (%.1f%% HBM)"
+        % (name, per * 1e6, Tt / per, tflops, 100 * tflops / BF16_PEAK_TFLOPS, gbs,
+           100 * gbs / HBM_PEAK_GBS))
+    return {"workload": name, "us_per_call": per * 1e6, "tokens_per_s": Tt / per,
+            "token_heads_per_s": th / per, "algorithmic_flops": flops, "algorithmic_bytes": byts,
+            "achieved_TFLOPs": tflops, "mfma_frac": tflops / BF16_PEAK_TFLOPS,
+            "achieved_GBs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS,
+            "binding_roofline_frac": max(tflops / BF16_PEAK_TFLOPS, gbs / HBM_PEAK_GBS)}
+
+
+def bench_copy(dev, log):
+    """Reference device copy of 1 GiB (fp32), also the known-size kernel that scales the
+    FETCH_SIZE / WRITE_SIZE counters."""
+    import torch
+
+    n = 1 << 28
+    src = torch.ones(n, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    total, per = time_loop(lambda i: dst.copy_(src), 10, torch.cuda.synchronize)
+    gbs = 2 * n * 4 / per / 1e9
+    log("copy 1 GiB: %.1f us, %.0f GB/s (read + write)" % (per * 1e6, gbs))
+    del src, dst
+    return {"bytes_read": n * 4, "bytes_written": n * 4, "us": per * 1e6, "GBs": gbs}
+
+
+def cpu_baseline(x, log, budget_s=10.0):
+    """fp64 oracle on the decode workload's step (all 64 x 32 (sequence, head) updates),
+    repeated until about budget_s seconds of wall time."""
+    import numpy as np
+
+    from oracle import kda_oracle as O
+
+    f = lambda t: t.float().numpy().astype(np.float64)
+    sl = x["slot_idx"].long()
+    ins = [f(x[n]) for n in ("q", "k", "v", "g", "beta")]
+    h0 = f(x["pool"][sl])
+    threads = O.default_threads()
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        O.decode(*ins, h0, nthreads=threads)
+        reps += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    el = time.perf_counter() - t0
+    n_upd = x["q"].shape[0] * x["q"].shape[2] * reps
+    log("cpu oracle: %d decode steps in %.1f s on %d threads" % (reps, el, threads))
+    return {"value": n_upd / el, "unit": "state-updates/s", "cores": threads, "kind": "oracle",
+            "sample": "%d full decode steps of the workload (64 sequences x 32 heads, 1 token, "
+                      "dk = dv = 128), fp64, %.1f s" % (reps, el),
+            "cpu": platform.processor() or platform.machine()}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--decode-only", action="store_true",
+                    help="measure only the decode step and the copy reference (for counter runs)")
+    ap.add_argument("--quiet", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build measures one GPU only (--gpus 1); the KDA kernels shard "
+              "by head and sequence with no exchange, and no multi-GPU run is provided.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import kda_gated_delta_rule_amd as kda
+
+    log = (lambda m: None) if args.quiet else (lambda m: print("[bench] " + m, file=sys.stderr,
+                                                               flush=True))
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(2)
+    kda.load()
+    dev = torch.device("cuda:0")
+    log("device: %s" % torch.cuda.get_device_name(0))
+
+    dec = bench_decode(args, dev, log)
+    value = dec["updates"] * args.steps / dec["total"]
+    extra = {"copy_reference": bench_copy(dev, log)}
+    if not args.decode_only:
+        extra["verify_replay"] = bench_verify_replay(args, dev, log)
+        extra["prefill"] = bench_prefill(args, dev, log, "prefill")
+        extra["prefill_varlen"] = bench_prefill(args, dev, log, "varlen")
+    cpu = None if args.decode_only else cpu_baseline(dec["inputs"], log)
+
+    import kda_workloads as W
+
+    line = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "state-updates/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": dec["total"] / args.steps * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp32",
+        "data": "synthetic",
+        "config": {"workload": W.DECODE["name"], "num_slots": 512, "sequences": 64, "tokens": 1,
+                   "heads": 32, "dk": 128, "dv": 128, "io_dtype": "bf16", "state_dtype": "fp32",
+                   "slot_rotation": "8 disjoint sets of 64 slots (1 GiB pool)",
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": dec["achieved"], "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": dec["achieved"] / HBM_PEAK_GBS,
+                     "traffic": counted_traffic(os.path.join(
+                         ROOT, "profiles", "decode_pool512_N64_H32_d128_traffic.json")),
+                     "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, "
+                                     "scaled by a 1 GiB copy)",
+                     "kernel": "decode_kernel<dk=128,dv=128,BV=64,T=1,bf16,commit>",
+                     "bytes_per_update": dec["bytes_per_update"],
+                     "updates_per_launch": dec["updates"],
+                     "avg_launch_us": dec["per"] * 1e6},
+        "cpu_baseline": cpu,
+        "extra": extra,
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

@@ -89,6 +89,18 @@ __device__ __forceinline__ void store4<BF16>(void* p, int64_t i, float4 x) {
     *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p) + i) = w;
 }
 
+// Streaming (non-temporal) 16-byte state access: every state byte is read once and
+// written once per call, so it is not kept in the caches on the way.
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ float4 load_stream4(const float* p) {
+    const f32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(p));
+    return make_float4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void store_stream4(float* p, float4 x) {
+    const f32x4_t v = {x.x, x.y, x.z, x.w};
+    __builtin_nontemporal_store(v, reinterpret_cast<f32x4_t*>(p));
+}
+
 // ---------------------------------------------------------------------------
 // wave64 reductions (butterfly; every lane ends with the total).
 // ---------------------------------------------------------------------------

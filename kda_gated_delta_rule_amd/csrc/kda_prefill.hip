@@ -322,25 +322,31 @@ __global__ __launch_bounds__(kThreads) void chunk_intra_kernel(PrefillArgs a) {
 #pragma unroll
                 for (int t = 0; t < kChunk; ++t) x[t] = sBeta[t] * M::to_f32(sKG[t * P::LDK + j]);
             } else {
+                // unconditional loads (rows past the chunk end re-read its last row and
+                // are zeroed by beta = 0), so all 64 are in flight together
                 const int jv = j - DK;
 #pragma unroll
-                for (int t = 0; t < kChunk; ++t)
-                    x[t] = t < L ? sBeta[t] * load1<TIn>(a.v, ((static_cast<int64_t>(t0) + t) * H + h) * DV + jv)
-                                 : 0.f;
+                for (int t = 0; t < kChunk; ++t) {
+                    const int tc = t < L ? t : L - 1;
+                    x[t] = load1<TIn>(a.v, ((static_cast<int64_t>(t0) + tc) * H + h) * DV + jv);
+                }
+#pragma unroll
+                for (int t = 0; t < kChunk; ++t) x[t] *= sBeta[t];
             }
+            // row t: x_t -= sum_{s<t} A_ts x_s, with 4 independent partial sums
 #pragma unroll
             for (int t = 1; t < kChunk; ++t) {
                 const float* Arow = sA + t * P::LDA;
-                float acc = x[t];
+                float acc[4] = {x[t], 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int s4 = 0; s4 < t; s4 += 4) {
                     const float4 av = *reinterpret_cast<const float4*>(Arow + s4);
-                    acc = fmaf(-av.x, x[s4], acc);
-                    if (s4 + 1 < t) acc = fmaf(-av.y, x[s4 + 1], acc);
-                    if (s4 + 2 < t) acc = fmaf(-av.z, x[s4 + 2], acc);
-                    if (s4 + 3 < t) acc = fmaf(-av.w, x[s4 + 3], acc);
+                    acc[0] = fmaf(-av.x, x[s4], acc[0]);
+                    if (s4 + 1 < t) acc[1] = fmaf(-av.y, x[s4 + 1], acc[1]);
+                    if (s4 + 2 < t) acc[2] = fmaf(-av.z, x[s4 + 2], acc[2]);
+                    if (s4 + 3 < t) acc[3] = fmaf(-av.w, x[s4 + 3], acc[3]);
                 }
-                x[t] = acc;
+                x[t] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
             }
             elem* dst = j < DK ? sWt + j * P::LDT : sUt + (j - DK) * P::LDT;
 #pragma unroll
