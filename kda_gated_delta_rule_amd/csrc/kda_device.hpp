@@ -101,6 +101,16 @@ __device__ __forceinline__ void store_stream4(float* p, float4 x) {
     __builtin_nontemporal_store(v, reinterpret_cast<f32x4_t*>(p));
 }
 
+// Workgroup barrier for LDS traffic only: waits for this wave's LDS operations
+// (lgkmcnt) and not for outstanding global loads/stores (vmcnt), unlike
+// __syncthreads(), whose workgroup fence waits for every global access.  Used where
+// a barrier orders LDS reads/writes between waves, so prefetched global loads and
+// output stores stay in flight across it.  The "memory" clobber keeps the compiler
+// from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // ---------------------------------------------------------------------------
 // wave64 reductions (butterfly; every lane ends with the total).
 // ---------------------------------------------------------------------------

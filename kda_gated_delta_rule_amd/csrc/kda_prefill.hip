@@ -59,7 +59,7 @@ __host__ __device__ constexpr size_t align_up(size_t x, size_t a) { return (x + 
 //   chunk_off  int32 [num_seqs + 1]     first chunk of each sequence; [num_seqs] = count
 //   table      int4  [max_chunks]       {sequence, first token, length, 0}
 //   records    [max_chunks * H] of     W [64][DK] | Q' [64][DK] | Kt [DK][64] |
-//                                       Ut [64][DV] | Ot [64][DV]  (element e bytes)
+//                                       Ut^T [DV][64] | Ot^T [DV][64]  (element e bytes)
 //                                       | exp(G_L) [DK] fp32
 // ---------------------------------------------------------------------------
 struct WsLayout {
@@ -128,58 +128,88 @@ __global__ __launch_bounds__(kThreads) void chunk_map_kernel(const int32_t* __re
 }
 
 // ---------------------------------------------------------------------------
-// 2. chunk_intra: LDS plan (bytes), per instantiation
+// 2. chunk_intra: one workgroup per (chunk, head)
+//
+// LDS regions are reused by phase (row-major tiles [64][LDK], transposed tiles
+// [D][LDT], fp32 tiles [64][LDA]):
+//   X1: G (fp32)            | KG, KI          | T (fp32)        | W^T, Ut^T
+//   X2: QG
+//   X3: KG^T                                   | Q' staging
+//   X4: V^T                                    | Ot^T staging
+//   X5: Kt^T (write-out)    | A (fp32)        | T' = T diag(beta)
+//   X6: P
+//   X7: beta, G_L, cumsum part totals, per-wave 16x16 fp32 scratch
 // ---------------------------------------------------------------------------
 template <int DK, int DV, class TIn>
 struct IntraPlan {
     using M = Mma<TIn>;
     using elem = typename M::elem;
     static constexpr int E = sizeof(elem);
-    static constexpr int PAD = E == 2 ? 8 : 4;  // row pad: 16-byte rows stay bank-spread
-    static constexpr int LDK = DK + PAD;        // [64][DK] tiles
-    static constexpr int LDV = DV + PAD;        // [64][DV] tiles
-    static constexpr int LDT = kChunk + PAD;    // transposed [D][64] tiles
-    static constexpr int LDG = DK + 4;          // fp32 G
-    static constexpr int LDA = kChunk + 4;      // fp32 A
+    static constexpr int PAD = E == 2 ? 8 : 4;  // rows stay 16-byte aligned and bank-spread
+    static constexpr int LDK = DK + PAD;
+    static constexpr int LDT = kChunk + PAD;
+    static constexpr int LDG = DK + 4;
+    static constexpr int LDA = kChunk + 4;
     static constexpr size_t cmax(size_t a, size_t b) { return a > b ? a : b; }
-    // regions
-    static constexpr size_t R_G = align_up(cmax(64ull * LDG * 4, 64ull * LDA * 4), 16);  // G, then A
-    static constexpr size_t R_KG = align_up(cmax(64ull * LDK * E, 64ull * LDK * E), 16);   // KG, then Q'
-    static constexpr size_t R_KI = align_up(cmax(64ull * LDK * E, 64ull * LDV * E), 16);   // KI, then Ot
-    static constexpr size_t R_QG = align_up(64ull * LDK * E, 16);
-    static constexpr size_t R_KT = align_up(cmax(64ull * LDK * E, 1ull * DK * LDT * E), 16);  // Kt rows, then W^T
-    static constexpr size_t R_UT = align_up(1ull * DV * LDT * E, 16);
-    static constexpr size_t R_PM = align_up(64ull * LDT * E, 16);
-    static constexpr size_t R_SM = align_up(4ull * (64 + DK + DK + 4 * DK), 16);  // beta, GL, eGL, totals
-    static constexpr size_t O_G = 0, O_KG = O_G + R_G, O_KI = O_KG + R_KG, O_QG = O_KI + R_KI;
-    static constexpr size_t O_KT = O_QG + R_QG, O_UT = O_KT + R_KT, O_PM = O_UT + R_UT;
-    static constexpr size_t O_SM = O_PM + R_PM;
-    static constexpr size_t BYTES = O_SM + R_SM;
+    static constexpr size_t X1 = align_up(cmax(cmax(64ull * LDG * 4, 2ull * 64 * LDK * E),
+                                               cmax(64ull * LDA * 4, 1ull * (DK + DV) * LDT * E)), 16);
+    static constexpr size_t X2 = align_up(64ull * LDK * E, 16);
+    static constexpr size_t X3 = align_up(cmax(1ull * DK * LDT * E, 64ull * LDK * E), 16);
+    static constexpr size_t X4 = align_up(1ull * DV * LDT * E, 16);
+    static constexpr size_t X5 = align_up(cmax(cmax(1ull * DK * LDT * E, 64ull * LDA * 4), 64ull * LDT * E), 16);
+    static constexpr size_t X6 = align_up(64ull * LDT * E, 16);
+    static constexpr size_t X7 = align_up(4ull * (64 + DK + 4 * DK) + 4ull * 4 * 16 * 16, 16);
+    static constexpr size_t O1 = 0, O2 = O1 + X1, O3 = O2 + X2, O4 = O3 + X3, O5 = O4 + X4;
+    static constexpr size_t O6 = O5 + X5, O7 = O6 + X6;
+    static constexpr size_t BYTES = O7 + X7;
     static constexpr bool fits = BYTES <= 160 * 1024;
 };
+
+// fp32 16x16 block product with both operands row-major:
+// C[m][n] += sum_{k < 16} A[m][k] * B[k][n] (v_mfma_f32_16x16x4_f32, 4 steps).
+__device__ __forceinline__ f32x4 mma16_nn_f32(const float* A, int lda, const float* B, int ldb,
+                                              f32x4 c, int lane) {
+    const int r = lane & 15, kq = lane >> 4;
+#pragma unroll
+    for (int k0 = 0; k0 < 16; k0 += 4)
+        c = __builtin_amdgcn_mfma_f32_16x16x4f32(A[r * lda + k0 + kq], B[(k0 + kq) * ldb + r], c, 0, 0, 0);
+    return c;
+}
+
+// Stores a 16x16 accumulator tile (times s) row-major into fp32 LDS.
+__device__ __forceinline__ void store16_f32(float* D, int ld, f32x4 c, float s, int lane) {
+    const int col = lane & 15, row = 4 * (lane >> 4);
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) D[(row + rr) * ld + col] = s * c[rr];
+}
 
 template <int DK, int DV, class TIn>
 __global__ __launch_bounds__(kThreads) void chunk_intra_kernel(PrefillArgs a) {
     using P = IntraPlan<DK, DV, TIn>;
     using M = typename P::M;
     using elem = typename P::elem;
-    constexpr int E = P::E;
+    constexpr int E = P::E, LDK = P::LDK, LDT = P::LDT, LDG = P::LDG, LDA = P::LDA;
     static_assert(P::fits, "LDS plan exceeds 160 KiB");
     __shared__ __attribute__((aligned(16))) char smem[P::BYTES];
-    float* sG = reinterpret_cast<float*>(smem + P::O_G);    // [64][LDG]
-    float* sA = reinterpret_cast<float*>(smem + P::O_G);    // [64][LDA] (after G is dead)
-    elem* sKG = reinterpret_cast<elem*>(smem + P::O_KG);    // [64][LDK]  kh exp(G)
-    elem* sQo = reinterpret_cast<elem*>(smem + P::O_KG);    // [64][LDK]  Q' staging
-    elem* sKI = reinterpret_cast<elem*>(smem + P::O_KI);    // [64][LDK]  kh exp(-G)
-    elem* sOo = reinterpret_cast<elem*>(smem + P::O_KI);    // [64][LDV]  Ot staging
-    elem* sQG = reinterpret_cast<elem*>(smem + P::O_QG);    // [64][LDK]  qh exp(G)
-    elem* sKt = reinterpret_cast<elem*>(smem + P::O_KT);    // [64][LDK]  kh exp(G_L - G)
-    elem* sWt = reinterpret_cast<elem*>(smem + P::O_KT);    // [DK][LDT]  W^T
-    elem* sUt = reinterpret_cast<elem*>(smem + P::O_UT);    // [DV][LDT]  Ut^T
-    elem* sPm = reinterpret_cast<elem*>(smem + P::O_PM);    // [64][LDT]  P
-    float* sBeta = reinterpret_cast<float*>(smem + P::O_SM);  // [64]
-    float* sGL = sBeta + 64;                                   // [DK] G_L
-    float* sTot = sGL + DK;                                    // [4][DK] cumsum part totals
+    float* sG = reinterpret_cast<float*>(smem + P::O1);
+    elem* sKG = reinterpret_cast<elem*>(smem + P::O1);
+    elem* sKI = reinterpret_cast<elem*>(smem + P::O1 + 64 * LDK * E);
+    float* sT = reinterpret_cast<float*>(smem + P::O1);
+    elem* sWt = reinterpret_cast<elem*>(smem + P::O1);
+    elem* sUt = reinterpret_cast<elem*>(smem + P::O1 + DK * LDT * E);
+    elem* sQG = reinterpret_cast<elem*>(smem + P::O2);
+    elem* sKGt = reinterpret_cast<elem*>(smem + P::O3);
+    elem* sQo = reinterpret_cast<elem*>(smem + P::O3);
+    elem* sVt = reinterpret_cast<elem*>(smem + P::O4);
+    elem* sOt = reinterpret_cast<elem*>(smem + P::O4);
+    elem* sKtt = reinterpret_cast<elem*>(smem + P::O5);
+    float* sA = reinterpret_cast<float*>(smem + P::O5);
+    elem* sTp = reinterpret_cast<elem*>(smem + P::O5);
+    elem* sPm = reinterpret_cast<elem*>(smem + P::O6);
+    float* sBeta = reinterpret_cast<float*>(smem + P::O7);
+    float* sGL = sBeta + 64;
+    float* sTot = sGL + DK;
+    float* sScr = sTot + 4 * DK;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int chunk = blockIdx.x, h = blockIdx.y, H = a.H;
@@ -192,25 +222,34 @@ __global__ __launch_bounds__(kThreads) void chunk_intra_kernel(PrefillArgs a) {
     char* rec = static_cast<char*>(a.workspace) + ws.off_rec +
                 ws.rec_bytes * (static_cast<size_t>(chunk) * H + h);
 
-    // ---- 1. rows: load q, k, g; L2 norm; beta --------------------------------
-    constexpr int NCH = DK / 4;  // channels per thread (4 threads per row)
-    const int r = tid >> 2, sg = tid & 3, c0 = sg * NCH;
+    // ---- 1. rows (4 threads per token row): q, k, g, v loads; L2 norm; beta ----------
+    constexpr int NCH = DK / 4, NCV = DV / 4;
+    const int r = tid >> 2, sg = tid & 3, c0 = sg * NCH, j0 = sg * NCV;
     const bool valid = r < L;
     const int64_t tok = static_cast<int64_t>(t0) + r;
     float qv[NCH], kv[NCH];
     {
-        const int64_t base = (tok * H + h) * DK + c0;
+        const int64_t bk = (tok * H + h) * DK + c0, bv = (tok * H + h) * DV + j0;
 #pragma unroll
         for (int i = 0; i < NCH; i += 4) {
             float4 x = make_float4(0.f, 0.f, 0.f, 0.f), y = x, z = x;
             if (valid) {
-                x = load4<TIn>(a.q, base + i);
-                y = load4<TIn>(a.k, base + i);
-                z = *reinterpret_cast<const float4*>(a.g + base + i);
+                x = load4<TIn>(a.q, bk + i);
+                y = load4<TIn>(a.k, bk + i);
+                z = *reinterpret_cast<const float4*>(a.g + bk + i);
             }
             qv[i] = x.x; qv[i + 1] = x.y; qv[i + 2] = x.z; qv[i + 3] = x.w;
             kv[i] = y.x; kv[i + 1] = y.y; kv[i + 2] = y.z; kv[i + 3] = y.w;
-            *reinterpret_cast<float4*>(&sG[r * P::LDG + c0 + i]) = z;
+            *reinterpret_cast<float4*>(&sG[r * LDG + c0 + i]) = z;
+        }
+#pragma unroll
+        for (int i = 0; i < NCV; i += 4) {
+            float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (valid) x = load4<TIn>(a.v, bv + i);
+            sVt[(j0 + i) * LDT + r] = M::from_f32(x.x);
+            sVt[(j0 + i + 1) * LDT + r] = M::from_f32(x.y);
+            sVt[(j0 + i + 2) * LDT + r] = M::from_f32(x.z);
+            sVt[(j0 + i + 3) * LDT + r] = M::from_f32(x.w);
         }
     }
     if (a.use_l2) {
@@ -232,158 +271,194 @@ __global__ __launch_bounds__(kThreads) void chunk_intra_kernel(PrefillArgs a) {
         }
     }
     if (sg == 0) sBeta[r] = valid ? a.beta[tok * H + h] : 0.f;
-    // P's strictly-upper tiles that the k-loops of step 5 touch must be zero
+    // P's strictly-upper 16x16 blocks are read by the k-loops of phase 7: zero them
     for (int idx = tid; idx < 64 * kChunk; idx += kThreads) {
         const int t = idx / kChunk, s = idx % kChunk;
-        if ((s >> 4) > (t >> 4)) sPm[t * P::LDT + s] = M::from_f32(0.f);
+        if ((s >> 4) > (t >> 4)) sPm[t * LDT + s] = M::from_f32(0.f);
     }
-    __syncthreads();
+    lds_barrier();
 
-    // ---- 2. gate cumsum over the chunk's tokens, per key channel --------------
+    // ---- 2. gate cumsum over the chunk's tokens, per key channel ----------------------
     {
-        constexpr int NP = kThreads / DK;  // parts per column
-        constexpr int RP = 64 / NP;        // rows per part
+        constexpr int NP = kThreads / DK, RP = 64 / NP;
         const int c = tid % DK, part = tid / DK;
         float x[RP];
         float run = 0.f;
 #pragma unroll
         for (int i = 0; i < RP; ++i) {
-            run += sG[(part * RP + i) * P::LDG + c];
+            run += sG[(part * RP + i) * LDG + c];
             x[i] = run;
         }
         sTot[part * DK + c] = run;
-        __syncthreads();
+        lds_barrier();
         float off = 0.f;
         for (int p = 0; p < part; ++p) off += sTot[p * DK + c];
 #pragma unroll
-        for (int i = 0; i < RP; ++i) sG[(part * RP + i) * P::LDG + c] = x[i] + off;
-        if (part == NP - 1) sGL[c] = x[RP - 1] + off;  // G at the last row (= G_{L-1}: padded rows add 0)
+        for (int i = 0; i < RP; ++i) sG[(part * RP + i) * LDG + c] = x[i] + off;
+        if (part == NP - 1) sGL[c] = x[RP - 1] + off;  // G at row 63 = G_{L-1} (padded rows add 0)
     }
-    __syncthreads();
+    lds_barrier();
 
-    // ---- 3. operands: kh exp(G), kh exp(-G), qh exp(G), kh exp(G_L - G) --------
-#pragma unroll
-    for (int i = 0; i < NCH; ++i) {
-        const int c = c0 + i;
-        const float G = sG[r * P::LDG + c];
-        const float eg = __expf(G), ei = __expf(-G), et = __expf(sGL[c] - G);
-        sKG[r * P::LDK + c] = M::from_f32(kv[i] * eg);
-        sKI[r * P::LDK + c] = M::from_f32(kv[i] * ei);
-        sQG[r * P::LDK + c] = M::from_f32(qv[i] * eg);
-        sKt[r * P::LDK + c] = M::from_f32(kv[i] * et);
-    }
-    __syncthreads();
-
-    // ---- 4a. Kt = (kh exp(G_L - G))^T to the workspace; exp(G_L) -------------------
+    // ---- 3. operands: KG = kh e^G, KI = kh e^-G, QG = qh e^G, Kt = kh e^(G_L - G) ------
     {
-        elem* gKt = reinterpret_cast<elem*>(rec + ws.o_kt);
-        constexpr int VE = 16 / E;                 // elements per 16-byte vector
-        constexpr int NV = DK * kChunk / VE;       // vectors in the tile
-        for (int v = tid; v < NV; v += kThreads) {
-            const int c = v / (kChunk / VE), t = (v % (kChunk / VE)) * VE;
-            elem tmp[VE];
+        float gr[NCH];
 #pragma unroll
-            for (int e = 0; e < VE; ++e) tmp[e] = sKt[(t + e) * P::LDK + c];
-            *reinterpret_cast<uint4*>(gKt + c * kChunk + t) = *reinterpret_cast<const uint4*>(tmp);
+        for (int i = 0; i < NCH; i += 4) {
+            const float4 z = *reinterpret_cast<const float4*>(&sG[r * LDG + c0 + i]);
+            gr[i] = z.x; gr[i + 1] = z.y; gr[i + 2] = z.z; gr[i + 3] = z.w;
+        }
+        lds_barrier();  // G (X1) is dead from here: KG and KI take its place
+#pragma unroll
+        for (int i = 0; i < NCH; ++i) {
+            const int c = c0 + i;
+            const float eg = __expf(gr[i]), ei = __expf(-gr[i]), et = __expf(sGL[c] - gr[i]);
+            const elem kg = M::from_f32(kv[i] * eg);
+            sKG[r * LDK + c] = kg;
+            sKGt[c * LDT + r] = kg;
+            sKI[r * LDK + c] = M::from_f32(kv[i] * ei);
+            sQG[r * LDK + c] = M::from_f32(qv[i] * eg);
+            sKtt[c * LDT + r] = M::from_f32(kv[i] * et);
+        }
+    }
+    lds_barrier();
+
+    // ---- 4. Kt^T and exp(G_L) to the workspace; A and P on MFMA -------------------------
+    {
+        constexpr int VE = 16 / E;
+        elem* gKt = reinterpret_cast<elem*>(rec + ws.o_kt);
+        for (int v = tid; v < DK * kChunk / VE; v += kThreads) {
+            const int c = v / (kChunk / VE), t = (v % (kChunk / VE)) * VE;
+            *reinterpret_cast<u32x4*>(gKt + c * kChunk + t) =
+                *reinterpret_cast<const u32x4*>(sKtt + c * LDT + t);
         }
         float* gGL = reinterpret_cast<float*>(rec + ws.o_gl);
         for (int c = tid; c < DK; c += kThreads) gGL[c] = __expf(sGL[c]);
     }
-    // ---- 4b. A = beta (KG KI^T) strictly lower, P = QG KI^T lower, on MFMA ----------
     {
-        // 10 lower-triangular 16x16 tiles for each of A and P: 20 tile jobs, 5 per wave
-        for (int job = wave; job < 20; job += 4) {
-            const int which = job / 10, tix = job % 10;  // 0: A, 1: P
-            int ti = 0, tj = tix;
-            while (tj > ti) { tj -= ti + 1; ++ti; }      // tix -> (ti, tj), tj <= ti
-            const elem* Aop = (which == 0 ? sKG : sQG) + ti * 16 * P::LDK;
-            const elem* Bop = sKI + tj * 16 * P::LDK;
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            acc = mma_nt<TIn>(Aop, P::LDK, Bop, P::LDK, 0, DK, acc, lane);
+        // 10 lower-triangular 16x16 tiles for each of A and P: 20 jobs, 5 per wave
+        // lower-triangular tile index -> (row block, column block), as bit fields: no
+        // data-dependent control flow between the MFMAs and the reads of their results
+        f32x4 acc[5];
+#pragma unroll
+        for (int n = 0; n < 5; ++n) {
+            const int job = wave + 4 * n;
+            const int which = job / 10, tix = job % 10;
+            const int ti = static_cast<int>((0x3333222110ull >> (4 * tix)) & 15);
+            const int tj = static_cast<int>((0x3210210100ull >> (4 * tix)) & 15);
+            const elem* Aop = (which == 0 ? sKG : sQG) + ti * 16 * LDK;
+            acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+            acc[n] = mma_nt<TIn>(Aop, LDK, sKI + tj * 16 * LDK, LDK, 0, DK, acc[n], lane);
+        }
+        lds_barrier();  // Kt^T (X5) has been copied out: A takes its place
+#pragma unroll
+        for (int n = 0; n < 5; ++n) {
+            const int job = wave + 4 * n;
+            const int which = job / 10, tix = job % 10;
+            const int ti = static_cast<int>((0x3333222110ull >> (4 * tix)) & 15);
+            const int tj = static_cast<int>((0x3210210100ull >> (4 * tix)) & 15);
             const int s = tj * 16 + (lane & 15);
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) {
                 const int t = ti * 16 + 4 * (lane >> 4) + rr;
                 if (which == 0)
-                    sA[t * P::LDA + s] = s < t ? sBeta[t] * acc[rr] : 0.f;
+                    sA[t * LDA + s] = s < t ? sBeta[t] * acc[n][rr] : 0.f;
                 else
-                    sPm[t * P::LDT + s] = M::from_f32(s <= t ? acc[rr] : 0.f);
+                    sPm[t * LDT + s] = M::from_f32(s <= t ? acc[n][rr] : 0.f);
             }
         }
     }
-    __syncthreads();
+    lds_barrier();
 
-    // ---- 5. forward substitution: (I + A) X = [beta KG | beta V], one column per thread
-    {
-        const int j = tid;
-        if (j < DK + DV) {
-            float x[kChunk];
-            if (j < DK) {
+    // ---- 5. T = (I + A)^-1 (unit lower triangular) in fp32, by 16x16 blocks ------------
+    // 5a. diagonal blocks by forward substitution (one thread per block column); the
+    //     strictly-upper blocks of T are zero.
+    if (wave == 0) {
+        const int bi = lane >> 4, col = lane & 15;
+        const float* Ab = sA + (16 * bi) * LDA + 16 * bi;
+        float x[16];
 #pragma unroll
-                for (int t = 0; t < kChunk; ++t) x[t] = sBeta[t] * M::to_f32(sKG[t * P::LDK + j]);
+        for (int rr = 0; rr < 16; ++rr) {
+            float acc = rr == col ? 1.f : 0.f;
+#pragma unroll
+            for (int s = 0; s < rr; ++s) acc = fmaf(-Ab[rr * LDA + s], x[s], acc);
+            x[rr] = rr < col ? 0.f : acc;
+        }
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) sT[(16 * bi + rr) * LDA + 16 * bi + col] = x[rr];
+    } else {
+        for (int idx = tid - 64; idx < 64 * 64; idx += kThreads - 64) {
+            const int t = idx / 64, s = idx % 64;
+            if ((s >> 4) > (t >> 4)) sT[t * LDA + s] = 0.f;
+        }
+    }
+    lds_barrier();
+    // 5b-d. off-diagonal blocks, one diagonal of blocks at a time:
+    //   T_ij = -T_ii * sum_{k=j}^{i-1} A_ik T_kj
+    for (int d = 1; d < 4; ++d) {
+        if (wave < 4 - d) {
+            const int i = wave + d, j = wave;
+            f32x4 y = {0.f, 0.f, 0.f, 0.f};
+            for (int k = j; k < i; ++k)
+                y = mma16_nn_f32(sA + (16 * i) * LDA + 16 * k, LDA, sT + (16 * k) * LDA + 16 * j, LDA, y, lane);
+            float* scr = sScr + wave * 256;
+            store16_f32(scr, 16, y, 1.f, lane);
+            f32x4 z = {0.f, 0.f, 0.f, 0.f};
+            z = mma16_nn_f32(sT + (16 * i) * LDA + 16 * i, LDA, scr, 16, z, lane);
+            store16_f32(sT + (16 * i) * LDA + 16 * j, LDA, z, -1.f, lane);
+        }
+        lds_barrier();
+    }
+    // 5e. T' = T diag(beta) in the MFMA operand type (A, in X5, is dead)
+    for (int idx = tid; idx < 64 * 64; idx += kThreads) {
+        const int t = idx / 64, s = idx % 64;
+        sTp[t * LDT + s] = M::from_f32(sT[t * LDA + s] * sBeta[s]);
+    }
+    lds_barrier();
+
+    // ---- 6. W = T' KG and Ut = T' V on MFMA -> W^T, Ut^T (T is dead: X1 reused) ----------
+    {
+        constexpr int NCB = (DK + DV) / 16;
+        for (int job = wave; job < 4 * NCB; job += 4) {
+            const int ti = job & 3, cb = job >> 2;
+            const int kend = 32 * (ti / 2 + 1);  // T' is lower triangular
+            const bool isw = cb < DK / 16;
+            const elem* Bop = isw ? sKGt + cb * 16 * LDT : sVt + (cb - DK / 16) * 16 * LDT;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            acc = mma_nt<TIn>(sTp + ti * 16 * LDT, LDT, Bop, LDT, 0, kend, acc, lane);
+            elem* D = isw ? sWt + cb * 16 * LDT : sUt + (cb - DK / 16) * 16 * LDT;
+            const int col = lane & 15, t = ti * 16 + 4 * (lane >> 4);
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) D[col * LDT + t + rr] = M::from_f32(acc[rr]);
+        }
+    }
+    lds_barrier();
+
+    // ---- 7. Q' = QG - P W -> row-major staging; Ot = P Ut -> Ot^T staging -------------
+    {
+        constexpr int NCB = (DK + DV) / 16;
+        for (int job = wave; job < 4 * NCB; job += 4) {
+            const int ti = job & 3, cb = job >> 2;
+            const int kend = 32 * (ti / 2 + 1);
+            const bool isq = cb < DK / 16;
+            const elem* Bop = isq ? sWt + cb * 16 * LDT : sUt + (cb - DK / 16) * 16 * LDT;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            acc = mma_nt<TIn>(sPm + ti * 16 * LDT, LDT, Bop, LDT, 0, kend, acc, lane);
+            const int col = lane & 15, t = ti * 16 + 4 * (lane >> 4);
+            if (isq) {
+                const int c = cb * 16 + col;
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr)
+                    sQo[(t + rr) * LDK + c] = M::from_f32(M::to_f32(sQG[(t + rr) * LDK + c]) - acc[rr]);
             } else {
-                // unconditional loads (rows past the chunk end re-read its last row and
-                // are zeroed by beta = 0), so all 64 are in flight together
-                const int jv = j - DK;
+                const int j = (cb - DK / 16) * 16 + col;
 #pragma unroll
-                for (int t = 0; t < kChunk; ++t) {
-                    const int tc = t < L ? t : L - 1;
-                    x[t] = load1<TIn>(a.v, ((static_cast<int64_t>(t0) + tc) * H + h) * DV + jv);
-                }
-#pragma unroll
-                for (int t = 0; t < kChunk; ++t) x[t] *= sBeta[t];
-            }
-            // row t: x_t -= sum_{s<t} A_ts x_s, with 4 independent partial sums
-#pragma unroll
-            for (int t = 1; t < kChunk; ++t) {
-                const float* Arow = sA + t * P::LDA;
-                float acc[4] = {x[t], 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int s4 = 0; s4 < t; s4 += 4) {
-                    const float4 av = *reinterpret_cast<const float4*>(Arow + s4);
-                    acc[0] = fmaf(-av.x, x[s4], acc[0]);
-                    if (s4 + 1 < t) acc[1] = fmaf(-av.y, x[s4 + 1], acc[1]);
-                    if (s4 + 2 < t) acc[2] = fmaf(-av.z, x[s4 + 2], acc[2]);
-                    if (s4 + 3 < t) acc[3] = fmaf(-av.w, x[s4 + 3], acc[3]);
-                }
-                x[t] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
-            }
-            elem* dst = j < DK ? sWt + j * P::LDT : sUt + (j - DK) * P::LDT;
-#pragma unroll
-            for (int t = 0; t < kChunk; ++t) dst[t] = M::from_f32(x[t]);
-        }
-    }
-    __syncthreads();
-
-    // ---- 6. Q' = QG - P W and Ot = P Ut on MFMA (row block = wave) -------------------
-    {
-        const int ti = wave;                 // token rows 16 ti .. 16 ti + 15
-        const int kend = 32 * (ti / 2 + 1);  // P is lower triangular: s <= t
-        const elem* Aop = sPm + ti * 16 * P::LDT;
-        for (int cb = 0; cb < DK / 16; ++cb) {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            acc = mma_nt<TIn>(Aop, P::LDT, sWt + cb * 16 * P::LDT, P::LDT, 0, kend, acc, lane);
-            const int c = cb * 16 + (lane & 15);
-#pragma unroll
-            for (int rr = 0; rr < 4; ++rr) {
-                const int t = ti * 16 + 4 * (lane >> 4) + rr;
-                sQo[t * P::LDK + c] = M::from_f32(M::to_f32(sQG[t * P::LDK + c]) - acc[rr]);
-            }
-        }
-        for (int cb = 0; cb < DV / 16; ++cb) {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            acc = mma_nt<TIn>(Aop, P::LDT, sUt + cb * 16 * P::LDT, P::LDT, 0, kend, acc, lane);
-            const int c = cb * 16 + (lane & 15);
-#pragma unroll
-            for (int rr = 0; rr < 4; ++rr) {
-                const int t = ti * 16 + 4 * (lane >> 4) + rr;
-                sOo[t * P::LDV + c] = M::from_f32(acc[rr]);
+                for (int rr = 0; rr < 4; ++rr) sOt[j * LDT + t + rr] = M::from_f32(acc[rr]);
             }
         }
     }
-    __syncthreads();
+    lds_barrier();
 
-    // ---- 7. write W, Q', Ut, Ot (row-major) to the workspace with 16-byte stores ---------
+    // ---- 8. W, Q' (row-major) and Ut^T, Ot^T to the workspace, 16-byte stores ----------
     {
         constexpr int VE = 16 / E;
         elem* gW = reinterpret_cast<elem*>(rec + ws.o_w);
@@ -394,19 +469,14 @@ __global__ __launch_bounds__(kThreads) void chunk_intra_kernel(PrefillArgs a) {
             const int t = v / (DK / VE), c = (v % (DK / VE)) * VE;
             elem tmp[VE];
 #pragma unroll
-            for (int e = 0; e < VE; ++e) tmp[e] = sWt[(c + e) * P::LDT + t];
-            *reinterpret_cast<uint4*>(gW + t * DK + c) = *reinterpret_cast<const uint4*>(tmp);
-            *reinterpret_cast<uint4*>(gQ + t * DK + c) =
-                *reinterpret_cast<const uint4*>(sQo + t * P::LDK + c);
+            for (int e = 0; e < VE; ++e) tmp[e] = sWt[(c + e) * LDT + t];
+            *reinterpret_cast<u32x4*>(gW + t * DK + c) = *reinterpret_cast<const u32x4*>(tmp);
+            *reinterpret_cast<u32x4*>(gQ + t * DK + c) = *reinterpret_cast<const u32x4*>(sQo + t * LDK + c);
         }
-        for (int v = tid; v < kChunk * DV / VE; v += kThreads) {
-            const int t = v / (DV / VE), c = (v % (DV / VE)) * VE;
-            elem tmp[VE];
-#pragma unroll
-            for (int e = 0; e < VE; ++e) tmp[e] = sUt[(c + e) * P::LDT + t];
-            *reinterpret_cast<uint4*>(gU + t * DV + c) = *reinterpret_cast<const uint4*>(tmp);
-            *reinterpret_cast<uint4*>(gO + t * DV + c) =
-                *reinterpret_cast<const uint4*>(sOo + t * P::LDV + c);
+        for (int v = tid; v < DV * kChunk / VE; v += kThreads) {
+            const int j = v / (kChunk / VE), t = (v % (kChunk / VE)) * VE;
+            *reinterpret_cast<u32x4*>(gU + j * kChunk + t) = *reinterpret_cast<const u32x4*>(sUt + j * LDT + t);
+            *reinterpret_cast<u32x4*>(gO + j * kChunk + t) = *reinterpret_cast<const u32x4*>(sOt + j * LDT + t);
         }
     }
 }
@@ -423,10 +493,9 @@ struct CarryPlan {
     static constexpr int PAD = E == 2 ? 8 : 4;
     static constexpr int LDK = DK + PAD;      // W, Q' [64][LDK]; S^T [BV][LDK]
     static constexpr int LDT = kChunk + PAD;  // Kt [DK][LDT]; U^T [BV][LDT]
-    static constexpr int LDB = BV + PAD;      // Ut, Ot tiles [64][LDB]
-    // one operand buffer (per chunk)
+    // one operand buffer (per chunk); Ut^T, Ot^T tiles are [BV][LDT]
     static constexpr size_t B_W = 64ull * LDK * E, B_Q = B_W, B_KT = 1ull * DK * LDT * E;
-    static constexpr size_t B_U = 64ull * LDB * E, B_O = B_U, B_GL = 4ull * DK;
+    static constexpr size_t B_U = 1ull * BV * LDT * E, B_O = B_U, B_GL = 4ull * DK;
     static constexpr size_t O_W = 0, O_Q = O_W + B_W, O_KT = O_Q + B_Q, O_U = O_KT + B_KT;
     static constexpr size_t O_O = O_U + B_U, O_GL = O_O + B_O;
     static constexpr size_t BUF = align_up(O_GL + B_GL, 16);
@@ -436,7 +505,7 @@ struct CarryPlan {
     // 16-byte vectors per chunk to stage, per operand (each a multiple of kThreads
     // except exp(G_L))
     static constexpr int VE = 16 / E;
-    static constexpr int NV_W = 64 * DK / VE, NV_KT = DK * 64 / VE, NV_U = 64 * BV / VE;
+    static constexpr int NV_W = 64 * DK / VE, NV_KT = DK * 64 / VE, NV_U = BV * 64 / VE;
     static constexpr int NV_GL = DK / 4;
     static constexpr int PT_W = NV_W / kThreads, PT_KT = NV_KT / kThreads, PT_U = NV_U / kThreads;
     static_assert(NV_W % kThreads == 0 && NV_KT % kThreads == 0 && NV_U % kThreads == 0, "");
@@ -463,11 +532,11 @@ __device__ __forceinline__ void carry_fetch(CarryRegs<CP>& R, const char* rec, c
     }
 #pragma unroll
     for (int i = 0; i < CP::PT_KT; ++i) R.kt[i] = gk[tid + i * kThreads];
+    // the tile's rows of Ut^T / Ot^T are contiguous
+    const size_t toff = static_cast<size_t>(tile) * CP::BV * kChunk * CP::E;
 #pragma unroll
     for (int i = 0; i < CP::PT_U; ++i) {
-        const int w = tid + i * kThreads;
-        const int t = w / (CP::BV / CP::VE), c = (w % (CP::BV / CP::VE)) * CP::VE;
-        const size_t off = (static_cast<size_t>(t) * DV + tile * CP::BV + c) * CP::E;
+        const size_t off = toff + static_cast<size_t>(tid + i * kThreads) * 16;
         R.u[i] = *reinterpret_cast<const u32x4*>(rec + ws.o_u + off);
         R.o[i] = *reinterpret_cast<const u32x4*>(rec + ws.o_o + off);
     }
@@ -494,8 +563,8 @@ __device__ __forceinline__ void carry_stage(const CarryRegs<CP>& R, char* buf, i
 #pragma unroll
     for (int i = 0; i < CP::PT_U; ++i) {
         const int v = tid + i * kThreads;
-        const int t = v / (CP::BV / CP::VE), c = (v % (CP::BV / CP::VE)) * CP::VE;
-        const size_t off = (static_cast<size_t>(t) * CP::LDB + c) * CP::E;
+        const int j = v / (kChunk / CP::VE), t = (v % (kChunk / CP::VE)) * CP::VE;
+        const size_t off = (static_cast<size_t>(j) * CP::LDT + t) * CP::E;
         *reinterpret_cast<u32x4*>(buf + CP::O_U + off) = R.u[i];
         *reinterpret_cast<u32x4*>(buf + CP::O_O + off) = R.o[i];
     }
@@ -552,7 +621,7 @@ __global__ __launch_bounds__(kThreads) void chunk_carry_kernel(PrefillArgs a) {
                         tid, DV);
         carry_stage<CP>(regs, smem, tid);
     }
-    __syncthreads();
+    lds_barrier();
 
     for (int c = c_begin; c < c_end; ++c) {
         char* buf = smem + ((c - c_begin) & 1) * CP::BUF;
@@ -562,11 +631,13 @@ __global__ __launch_bounds__(kThreads) void chunk_carry_kernel(PrefillArgs a) {
         const elem* bU = reinterpret_cast<const elem*>(buf + CP::O_U);
         const elem* bO = reinterpret_cast<const elem*>(buf + CP::O_O);
         const float* bGL = reinterpret_cast<const float*>(buf + CP::O_GL);
+        // this chunk's token range first: vmcnt retires in order, so a load issued after
+        // the prefetch below would make its first use wait for the whole prefetch
+        const int4 info = table[c];
+        const int t0 = info.y, L = info.z;
         // next chunk's operands (the last iteration re-fetches its own chunk, unused)
         const int cn = c + 1 < c_end ? c + 1 : c;
         carry_fetch<CP>(regs, recs + ws.rec_bytes * (static_cast<size_t>(cn) * H + h), ws, tile, tid, DV);
-        const int4 info = table[c];
-        const int t0 = info.y, L = info.z;
 
         // (1) S (fp32 registers) -> S^T operand in LDS
 #pragma unroll
@@ -578,7 +649,7 @@ __global__ __launch_bounds__(kThreads) void chunk_carry_kernel(PrefillArgs a) {
 #pragma unroll
                 for (int rr = 0; rr < 4; ++rr) sSt[col * CP::LDK + row + rr] = M::from_f32(S[i][cb][rr]);
             }
-        __syncthreads();
+        lds_barrier();
 
         // (2) U = Ut - W S and O = scale (Q' S + Ot): token rows 16 wave .. +15
 #pragma unroll
@@ -592,8 +663,8 @@ __global__ __launch_bounds__(kThreads) void chunk_carry_kernel(PrefillArgs a) {
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) {
                 const int t = trow + rr;
-                uv[rr] = M::to_f32(bU[t * CP::LDB + col]) - u[rr];
-                const float ov = a.scale * (o[rr] + M::to_f32(bO[t * CP::LDB + col]));
+                uv[rr] = M::to_f32(bU[col * CP::LDT + t]) - u[rr];
+                const float ov = a.scale * (o[rr] + M::to_f32(bO[col * CP::LDT + t]));
                 if (t < L) {
                     const int64_t oi = ((static_cast<int64_t>(t0) + t) * H + h) * DV + tile * BV + col;
                     if constexpr (CP::E == 2)
@@ -605,7 +676,7 @@ __global__ __launch_bounds__(kThreads) void chunk_carry_kernel(PrefillArgs a) {
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) sUt[col * CP::LDT + trow + rr] = M::from_f32(uv[rr]);
         }
-        __syncthreads();
+        lds_barrier();
 
         // (3) S = exp(G_L) S + Kt U
 #pragma unroll
@@ -621,7 +692,7 @@ __global__ __launch_bounds__(kThreads) void chunk_carry_kernel(PrefillArgs a) {
             }
         }
         carry_stage<CP>(regs, smem + ((c + 1 - c_begin) & 1) * CP::BUF, tid);
-        __syncthreads();
+        lds_barrier();
     }
 
     // final state back to the slot

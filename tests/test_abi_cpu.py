@@ -136,3 +136,13 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(_lib, "lib_path", lambda: str(tmp_path / "missing.so"))
     with pytest.raises(ImportError):
         _lib.load()
+
+
+def test_isa_has_no_mfma_result_read_through_short_branch_path():
+    """Compiles the kernels to gfx950 assembly and checks that no MFMA accumulator is
+    read through a forward branch with fewer than 10 wait states (a stale-result hazard
+    the compiler left uncovered once, behind a data-dependent loop)."""
+    from kda_gated_delta_rule_amd import isa_lint
+
+    findings = isa_lint.lint()
+    assert not findings, findings[:3]
