@@ -9,7 +9,7 @@
 //
 //   A_ts = beta_t sum_c kh_tc kh_sc exp(G_tc - G_sc)   (s < t)     "KK^T" with decay
 //   P_ts =        sum_c qh_tc kh_sc exp(G_tc - G_sc)   (s <= t)    "QK^T" with decay
-//   (I + A) W  = beta kh exp(G)          (I + A) Ut = beta V      (UT transform, WY factor)
+//   T = (I + A)^-1,  W = T diag(beta) kh exp(G),  Ut = T diag(beta) V   (UT transform)
 //   U  = Ut - W S0
 //   O  = scale ((qh exp(G) - P W) S0 + P Ut)  =  scale (Q' S0 + Ot)
 //   S  = diag(exp(G_L)) S0 + (kh exp(G_L - G))^T U
@@ -18,17 +18,25 @@
 //   1. chunk_map    cu_seqlens -> per-sequence chunk offsets and a chunk table
 //                   (sequence, first token, length); chunks restart at every
 //                   sequence start, the last one may be short.
-//   2. chunk_intra  one workgroup per (chunk, head), all chunks in parallel:
-//                   Q/K norm, gate cumsum, A and P on MFMA, forward substitution
-//                   for W and Ut in fp32, Q' = qh exp(G) - P W and Ot = P Ut on
-//                   MFMA; writes W, Q', Kt = (kh exp(G_L - G))^T, Ut, Ot and
-//                   exp(G_L) to the workspace.
+//   2. chunk_intra  persistent workgroups walking the (chunk, head) items, the next
+//                   item's inputs loaded into registers while the current one is
+//                   computed: Q/K norm, gate cumsum (DPP scan), A and P on MFMA,
+//                   T by blocked substitution in fp32, W, Ut, Q' and Ot on MFMA;
+//                   writes W, Q', Kt = (kh exp(G_L - G))^T, Ut, Ot and exp(G_L)
+//                   to a per-(chunk, head) workspace record.
 //   3. chunk_carry  one workgroup per (sequence, head, 32-column dv tile),
 //                   sequential over the sequence's chunks: U = Ut - W S,
-//                   O = scale (Q' S + Ot), S = exp(G_L) S + Kt U, all on MFMA
-//                   from LDS with the next chunk's operands prefetched; the
-//                   fp32 state stays in registers and is written to its slot
+//                   O = scale (Q' S + Ot), S = exp(G_L) S + Kt U, all on MFMA;
+//                   the fp32 state stays in registers and is written to its slot
 //                   at the end.
+//
+// The record is stored in the carry's MFMA fragment order ("granules": the 16
+// bytes one lane feeds one MFMA k-step, 64 lanes contiguous), so every carry
+// load is a contiguous 1 KiB per wave, and the chunk_intra kernel produces most
+// granules straight from its MFMA accumulators: a 16x16 accumulator tile holds
+// four consecutive rows of one column per lane, which is the operand layout of
+// the next product over that dimension when the k index of both operands is
+// permuted the same way (two tiles per bf16 granule, one per fp32 granule).
 //
 // The exp(G_t - G_s) factor is split as exp(G_t) * exp(-G_s) (chunk-start
 // reference) so A and P are plain MFMA products.  exp(-G_s) grows along the
@@ -48,24 +56,136 @@ namespace {
 constexpr int kChunk = 64;
 constexpr int kThreads = 256;
 constexpr int kCarryBV = 32;  // dv columns per carry workgroup
+constexpr int kCarryNB = 2;   // chunks whose operands the carry has in flight
 constexpr int kNumXcd = 8;    // MI355X: 8 XCDs, workgroups dispatched round-robin
 constexpr float kNormEps = 1e-6f;
+constexpr int kBufFlags = 0x00020000;  // raw buffer resource word 3 (gfx9 family)
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 __host__ __device__ constexpr size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+__host__ __device__ constexpr size_t cmax(size_t a, size_t b) { return a > b ? a : b; }
+
+// ---------------------------------------------------------------------------
+// Fragment geometry per operand type.  A granule is 16 bytes: 8 bf16 (one
+// v_mfma_f32_16x16x32_bf16 k-step) or 4 fp32 (four v_mfma_f32_16x16x4_f32 k-steps).
+// In accumulator terms a granule spans CT 16x16 tiles along k.
+// ---------------------------------------------------------------------------
+template <class TIn>
+struct Geo;
+template <>
+struct Geo<BF16> {
+    using elem = uint16_t;
+    static constexpr int E = 2;
+    static constexpr int GW = 8;  // elements per granule
+    static constexpr int CT = 2;  // accumulator tiles per granule
+};
+template <>
+struct Geo<F32> {
+    using elem = float;
+    static constexpr int E = 4;
+    static constexpr int GW = 4;
+    static constexpr int CT = 1;
+};
+
+// C += A B over one granule (both operands list their k values in the same order).
+__device__ __forceinline__ f32x4 gmma(u32x4 a, u32x4 b, f32x4 c, BF16) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
+                                                   c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 gmma(u32x4 a, u32x4 b, f32x4 c, F32) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+        c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[e]), __uint_as_float(b[e]), c, 0, 0, 0);
+    return c;
+}
+
+// Accumulator tiles -> granule: bf16 packs 4 values of each of two tiles, fp32
+// takes one tile.
+__device__ __forceinline__ u32x4 tiles_to_gran(f32x4 t0, f32x4 t1, BF16) {
+    return u32x4{pack_bf16x2(t0[0], t0[1]), pack_bf16x2(t0[2], t0[3]), pack_bf16x2(t1[0], t1[1]),
+                 pack_bf16x2(t1[2], t1[3])};
+}
+__device__ __forceinline__ u32x4 tiles_to_gran(f32x4 t0, f32x4, F32) {
+    return u32x4{__float_as_uint(t0[0]), __float_as_uint(t0[1]), __float_as_uint(t0[2]), __float_as_uint(t0[3])};
+}
+
+// Granule <-> GW fp32 values.
+__device__ __forceinline__ void gran_to_f32(u32x4 g, float* x, BF16) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        x[2 * i] = __uint_as_float(g[i] << 16);
+        x[2 * i + 1] = __uint_as_float(g[i] & 0xffff0000u);
+    }
+}
+__device__ __forceinline__ void gran_to_f32(u32x4 g, float* x, F32) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[i] = __uint_as_float(g[i]);
+}
+__device__ __forceinline__ u32x4 f32_to_gran(const float* x, BF16) {
+    return u32x4{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(x[4], x[5]), pack_bf16x2(x[6], x[7])};
+}
+__device__ __forceinline__ u32x4 f32_to_gran(const float* x, F32) {
+    return u32x4{__float_as_uint(x[0]), __float_as_uint(x[1]), __float_as_uint(x[2]), __float_as_uint(x[3])};
+}
+
+// Four consecutive elements to LDS: 8 bytes (bf16) or 16 bytes (fp32).
+__device__ __forceinline__ void lds_store4(uint16_t* p, float x0, float x1, float x2, float x3) {
+    *reinterpret_cast<u32x2*>(p) = u32x2{pack_bf16x2(x0, x1), pack_bf16x2(x2, x3)};
+}
+__device__ __forceinline__ void lds_store4(float* p, float x0, float x1, float x2, float x3) {
+    *reinterpret_cast<f32x4*>(p) = f32x4{x0, x1, x2, x3};
+}
+// Four consecutive LDS elements as fp32.
+__device__ __forceinline__ f32x4 lds_load4(const uint16_t* p) {
+    const u32x2 w = *reinterpret_cast<const u32x2*>(p);
+    return f32x4{__uint_as_float(w[0] << 16), __uint_as_float(w[0] & 0xffff0000u), __uint_as_float(w[1] << 16),
+                 __uint_as_float(w[1] & 0xffff0000u)};
+}
+__device__ __forceinline__ f32x4 lds_load4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
+
+// One MFMA k-step with both operands read from LDS in the natural order
+// (row r = lane % 16, k contiguous): bf16 16 bytes per lane, fp32 4 bytes.
+__device__ __forceinline__ f32x4 lmma(const uint16_t* A, const uint16_t* B, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(*reinterpret_cast<const bf16x8*>(A),
+                                                   *reinterpret_cast<const bf16x8*>(B), c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 lmma(const float* A, const float* B, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(*A, *B, c, 0, 0, 0);
+}
+
+// Value of the neighbouring lane (lane ^ 1, same 16-lane row).
+__device__ __forceinline__ float swap_adjacent(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xf, 0xf, false));
+}
+// Inclusive prefix sum over the 16 lanes of each row (DPP row_shr 1, 2, 4, 8; lanes
+// shifted in from outside the row contribute 0).
+__device__ __forceinline__ float row_scan16(float x) {
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x111, 0xf, 0xf, false));
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x112, 0xf, 0xf, false));
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x114, 0xf, 0xf, false));
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x118, 0xf, 0xf, false));
+    return x;
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, int64_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes), kBufFlags);
+}
 
 // ---------------------------------------------------------------------------
 // Workspace layout (all offsets 256-byte aligned):
 //   chunk_off  int32 [num_seqs + 1]     first chunk of each sequence; [num_seqs] = count
 //   table      int4  [max_chunks]       {sequence, first token, length, 0}
-//   records    [max_chunks * H] of     W [64][DK] | Q' [64][DK] | Kt [DK][64] |
-//                                       Ut^T [DV][64] | Ot^T [DV][64]  (element e bytes)
-//                                       | exp(G_L) [DK] fp32
+//   records    [max_chunks * H]         one per (chunk, head), granule order:
+//     W, Q'  [token block 4][dk granule GK][lane 64] x 16 B     rows t, k over dk
+//     Kt     [dk block DK/16][token granule GT][lane 64] x 16 B rows c, k over tokens
+//     Ut, Ot [dv tile NT][token block 4][part 2][lane 64] x UB  accumulator layout
+//     exp(G_L) [DK] fp32
 // ---------------------------------------------------------------------------
 struct WsLayout {
     int64_t max_chunks;
     size_t off_table, off_rec, rec_bytes, total;
-    size_t o_w, o_q, o_kt, o_u, o_o, o_gl;
+    size_t o_w, o_q, o_kt, o_uo, o_gl;
     __host__ __device__ WsLayout(int num_seqs, int64_t total_tokens, int H, int dk, int dv, int e) {
         max_chunks = total_tokens / kChunk + num_seqs;
         off_table = align_up(sizeof(int32_t) * (num_seqs + 1), 256);
@@ -73,12 +193,22 @@ struct WsLayout {
         o_w = 0;
         o_q = o_w + static_cast<size_t>(kChunk) * dk * e;
         o_kt = o_q + static_cast<size_t>(kChunk) * dk * e;
-        o_u = o_kt + static_cast<size_t>(dk) * kChunk * e;
-        o_o = o_u + static_cast<size_t>(kChunk) * dv * e;
-        o_gl = o_o + static_cast<size_t>(kChunk) * dv * e;
+        o_uo = o_kt + static_cast<size_t>(dk) * kChunk * e;
+        o_gl = o_uo + 2ull * kChunk * dv * e;
         rec_bytes = align_up(o_gl + sizeof(float) * dk, 256);
         total = off_rec + rec_bytes * static_cast<size_t>(max_chunks) * H;
     }
+};
+
+// Granule counts of the record, shared by its producer and its consumer.
+template <int DK, int DV, class TIn>
+struct RecGeo {
+    static constexpr int CT = Geo<TIn>::CT, E = Geo<TIn>::E;
+    static constexpr int GK = DK / (16 * CT);      // granules along dk
+    static constexpr int GT = kChunk / (16 * CT);  // granules along the chunk's tokens
+    static constexpr int BV = kCarryBV, NT = DV / BV, NCB = BV / 16;
+    static constexpr int UB = NCB * 4 * E;         // bytes of one U/O part per lane
+    static_assert(DV % BV == 0 && DK % 64 == 0 && UB % 16 == 0, "record geometry");
 };
 
 // ---------------------------------------------------------------------------
@@ -128,459 +258,645 @@ __global__ __launch_bounds__(kThreads) void chunk_map_kernel(const int32_t* __re
 }
 
 // ---------------------------------------------------------------------------
-// 2. chunk_intra: one workgroup per (chunk, head)
+// 2. chunk_intra
 //
-// LDS regions are reused by phase (row-major tiles [64][LDK], transposed tiles
-// [D][LDT], fp32 tiles [64][LDA]):
-//   X1: G (fp32)            | KG, KI          | T (fp32)        | W^T, Ut^T
-//   X2: QG
-//   X3: KG^T                                   | Q' staging
-//   X4: V^T                                    | Ot^T staging
-//   X5: Kt^T (write-out)    | A (fp32)        | T' = T diag(beta)
-//   X6: P
-//   X7: beta, G_L, cumsum part totals, per-wave 16x16 fp32 scratch
+// Wave w owns tokens 16w .. 16w+15 of the chunk; lane (r = lane % 16, q = lane / 16)
+// holds token 16w + r and, of every row vector, the granules j of channels
+// GW (4j + q) .. + GW - 1.  LDS regions (reused by phase):
+//   R1  KI [64][LDK]            | T fp32 [64][LDA]
+//   R2  KG^T [DK][LDT]          | W^T [DK][LDT]
+//   R3  V^T [DV][LDT]           | Ut^T [DV][LDT]
+//   R4  Kt^T [DK][LDT]          | A fp32 [64][LDA]
+//   RT  T' = T diag(beta) [64][LDT]
+//   RP  P [64][LDT]
+//   RQ  QG [64][LDK]
+//   RM  beta [64], wave gate totals [4][DK]
 // ---------------------------------------------------------------------------
 template <int DK, int DV, class TIn>
 struct IntraPlan {
-    using M = Mma<TIn>;
-    using elem = typename M::elem;
-    static constexpr int E = sizeof(elem);
+    using G = Geo<TIn>;
+    using elem = typename G::elem;
+    static constexpr int E = G::E, GW = G::GW;
     static constexpr int PAD = E == 2 ? 8 : 4;  // rows stay 16-byte aligned and bank-spread
     static constexpr int LDK = DK + PAD;
     static constexpr int LDT = kChunk + PAD;
-    static constexpr int LDG = DK + 4;
     static constexpr int LDA = kChunk + 4;
-    static constexpr size_t cmax(size_t a, size_t b) { return a > b ? a : b; }
-    static constexpr size_t X1 = align_up(cmax(cmax(64ull * LDG * 4, 2ull * 64 * LDK * E),
-                                               cmax(64ull * LDA * 4, 1ull * (DK + DV) * LDT * E)), 16);
-    static constexpr size_t X2 = align_up(64ull * LDK * E, 16);
-    static constexpr size_t X3 = align_up(cmax(1ull * DK * LDT * E, 64ull * LDK * E), 16);
-    static constexpr size_t X4 = align_up(1ull * DV * LDT * E, 16);
-    static constexpr size_t X5 = align_up(cmax(cmax(1ull * DK * LDT * E, 64ull * LDA * 4), 64ull * LDT * E), 16);
-    static constexpr size_t X6 = align_up(64ull * LDT * E, 16);
-    static constexpr size_t X7 = align_up(4ull * (64 + DK + 4 * DK) + 4ull * 4 * 16 * 16, 16);
-    static constexpr size_t O1 = 0, O2 = O1 + X1, O3 = O2 + X2, O4 = O3 + X3, O5 = O4 + X4;
-    static constexpr size_t O6 = O5 + X5, O7 = O6 + X6;
-    static constexpr size_t BYTES = O7 + X7;
+    static constexpr int NGK = DK / (4 * GW), NGV = DV / (4 * GW);  // granules per lane
+    static constexpr size_t R1 = align_up(cmax(64ull * LDK * E, 64ull * LDA * 4), 16);
+    static constexpr size_t R2 = align_up(1ull * DK * LDT * E, 16);
+    static constexpr size_t R3 = align_up(1ull * DV * LDT * E, 16);
+    static constexpr size_t R4 = align_up(cmax(1ull * DK * LDT * E, 64ull * LDA * 4), 16);
+    static constexpr size_t RT = align_up(64ull * LDT * E, 16);
+    static constexpr size_t RP = RT;
+    static constexpr size_t RQ = align_up(64ull * LDK * E, 16);
+    static constexpr size_t RM = align_up(4ull * (64 + 4 * DK), 16);
+    static constexpr size_t O1 = 0, O2 = O1 + R1, O3 = O2 + R2, O4 = O3 + R3, OT = O4 + R4;
+    static constexpr size_t OP = OT + RT, OQ = OP + RP, OM = OQ + RQ;
+    static constexpr size_t BYTES = OM + RM;
     static constexpr bool fits = BYTES <= 160 * 1024;
 };
 
-// fp32 16x16 block product with both operands row-major:
-// C[m][n] += sum_{k < 16} A[m][k] * B[k][n] (v_mfma_f32_16x16x4_f32, 4 steps).
-__device__ __forceinline__ f32x4 mma16_nn_f32(const float* A, int lda, const float* B, int ldb,
-                                              f32x4 c, int lane) {
-    const int r = lane & 15, kq = lane >> 4;
-#pragma unroll
-    for (int k0 = 0; k0 < 16; k0 += 4)
-        c = __builtin_amdgcn_mfma_f32_16x16x4f32(A[r * lda + k0 + kq], B[(k0 + kq) * ldb + r], c, 0, 0, 0);
-    return c;
-}
+// One item's inputs, as loaded (granules of q, k, v; fp32 gate; beta).
+template <int DK, int DV, class TIn>
+struct IntraIn {
+    using P = IntraPlan<DK, DV, TIn>;
+    u32x4 q[P::NGK], k[P::NGK], v[P::NGV];
+    f32x4 g[P::NGK][P::GW / 4];
+    float beta;
+};
 
-// Stores a 16x16 accumulator tile (times s) row-major into fp32 LDS.
-__device__ __forceinline__ void store16_f32(float* D, int ld, f32x4 c, float s, int lane) {
-    const int col = lane & 15, row = 4 * (lane >> 4);
+// Loads item (chunk, head)'s rows through buffer resources bounded at the chunk's
+// last token, so rows past it read as zero (neutral padding).
+template <int DK, int DV, class TIn>
+__device__ __forceinline__ void intra_fetch(IntraIn<DK, DV, TIn>& X, const PrefillArgs& a, int t0, int L, int h,
+                                            int wave, int lane) {
+    using P = IntraPlan<DK, DV, TIn>;
+    constexpr int E = P::E, GW = P::GW;
+    const int H = a.H, r = lane & 15, q = lane >> 4, t = 16 * wave + r;
+    const int64_t tok = static_cast<int64_t>(t0) * H + h;
+    const int rows = (L - 1) * H + 1;
+    const auto rq = buf_rsrc(static_cast<const char*>(a.q) + tok * DK * E, static_cast<int64_t>(rows) * DK * E);
+    const auto rk = buf_rsrc(static_cast<const char*>(a.k) + tok * DK * E, static_cast<int64_t>(rows) * DK * E);
+    const auto rv = buf_rsrc(static_cast<const char*>(a.v) + tok * DV * E, static_cast<int64_t>(rows) * DV * E);
+    const auto rg = buf_rsrc(a.g + tok * DK, static_cast<int64_t>(rows) * DK * 4);
+    const auto rb = buf_rsrc(a.beta + tok, static_cast<int64_t>(rows) * 4);
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) D[(row + rr) * ld + col] = s * c[rr];
+    for (int j = 0; j < P::NGK; ++j) {
+        const int off = (t * H * DK + GW * (4 * j + q)) * E;
+        X.q[j] = __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0);
+        X.k[j] = __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < P::NGV; ++j)
+        X.v[j] = __builtin_amdgcn_raw_buffer_load_b128(rv, (t * H * DV + GW * (4 * j + q)) * E, 0, 0);
+#pragma unroll
+    for (int j = 0; j < P::NGK; ++j)
+#pragma unroll
+        for (int m = 0; m < GW / 4; ++m)
+            X.g[j][m] = __builtin_bit_cast(
+                f32x4, __builtin_amdgcn_raw_buffer_load_b128(rg, (t * H * DK + GW * (4 * j + q) + 4 * m) * 4, 0, 0));
+    X.beta = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rb, t * H * 4, 0, 0));
 }
 
 template <int DK, int DV, class TIn>
-__global__ __launch_bounds__(kThreads) void chunk_intra_kernel(PrefillArgs a) {
+__device__ __forceinline__ void intra_compute(const IntraIn<DK, DV, TIn>& X, char* smem, const PrefillArgs& a,
+                                              char* rec, const WsLayout& ws, int wave, int lane, int tid) {
     using P = IntraPlan<DK, DV, TIn>;
-    using M = typename P::M;
+    using RG = RecGeo<DK, DV, TIn>;
     using elem = typename P::elem;
-    constexpr int E = P::E, LDK = P::LDK, LDT = P::LDT, LDG = P::LDG, LDA = P::LDA;
-    static_assert(P::fits, "LDS plan exceeds 160 KiB");
-    __shared__ __attribute__((aligned(16))) char smem[P::BYTES];
-    float* sG = reinterpret_cast<float*>(smem + P::O1);
-    elem* sKG = reinterpret_cast<elem*>(smem + P::O1);
-    elem* sKI = reinterpret_cast<elem*>(smem + P::O1 + 64 * LDK * E);
+    constexpr int E = P::E, GW = P::GW, NGK = P::NGK, NGV = P::NGV;
+    constexpr int LDK = P::LDK, LDT = P::LDT, LDA = P::LDA;
+    constexpr int KS = Mma<TIn>::KS, KST = kChunk / KS;  // natural k-steps over tokens
+    constexpr TIn tag{};
+    elem* sKI = reinterpret_cast<elem*>(smem + P::O1);
     float* sT = reinterpret_cast<float*>(smem + P::O1);
-    elem* sWt = reinterpret_cast<elem*>(smem + P::O1);
-    elem* sUt = reinterpret_cast<elem*>(smem + P::O1 + DK * LDT * E);
-    elem* sQG = reinterpret_cast<elem*>(smem + P::O2);
-    elem* sKGt = reinterpret_cast<elem*>(smem + P::O3);
-    elem* sQo = reinterpret_cast<elem*>(smem + P::O3);
-    elem* sVt = reinterpret_cast<elem*>(smem + P::O4);
-    elem* sOt = reinterpret_cast<elem*>(smem + P::O4);
-    elem* sKtt = reinterpret_cast<elem*>(smem + P::O5);
-    float* sA = reinterpret_cast<float*>(smem + P::O5);
-    elem* sTp = reinterpret_cast<elem*>(smem + P::O5);
-    elem* sPm = reinterpret_cast<elem*>(smem + P::O6);
-    float* sBeta = reinterpret_cast<float*>(smem + P::O7);
-    float* sGL = sBeta + 64;
-    float* sTot = sGL + DK;
-    float* sScr = sTot + 4 * DK;
+    elem* sKGt = reinterpret_cast<elem*>(smem + P::O2);
+    elem* sWt = sKGt;
+    elem* sVt = reinterpret_cast<elem*>(smem + P::O3);
+    elem* sUt = sVt;
+    elem* sKTt = reinterpret_cast<elem*>(smem + P::O4);
+    float* sA = reinterpret_cast<float*>(smem + P::O4);
+    elem* sTp = reinterpret_cast<elem*>(smem + P::OT);
+    elem* sP = reinterpret_cast<elem*>(smem + P::OP);
+    elem* sQG = reinterpret_cast<elem*>(smem + P::OQ);
+    float* sBeta = reinterpret_cast<float*>(smem + P::OM);
+    float* sTot = sBeta + 64;
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int chunk = blockIdx.x, h = blockIdx.y, H = a.H;
-    const WsLayout ws(a.num_seqs, a.total_tokens, H, DK, DV, E);
-    const int32_t* chunk_off = static_cast<const int32_t*>(a.workspace);
-    if (chunk >= chunk_off[a.num_seqs]) return;
-    const int4 info = reinterpret_cast<const int4*>(static_cast<const char*>(a.workspace) +
-                                                    ws.off_table)[chunk];
-    const int t0 = info.y, L = info.z;
-    char* rec = static_cast<char*>(a.workspace) + ws.off_rec +
-                ws.rec_bytes * (static_cast<size_t>(chunk) * H + h);
+    const int r = lane & 15, q = lane >> 4, t = 16 * wave + r;
 
-    // ---- 1. rows (4 threads per token row): q, k, g, v loads; L2 norm; beta ----------
-    constexpr int NCH = DK / 4, NCV = DV / 4;
-    const int r = tid >> 2, sg = tid & 3, c0 = sg * NCH, j0 = sg * NCV;
-    const bool valid = r < L;
-    const int64_t tok = static_cast<int64_t>(t0) + r;
-    float qv[NCH], kv[NCH];
-    {
-        const int64_t bk = (tok * H + h) * DK + c0, bv = (tok * H + h) * DV + j0;
+    // ---- 1. norms, gate cumsum inside the wave, wave totals -------------------------
+    float qf[NGK][GW], kf[NGK][GW], gf[NGK][GW];
 #pragma unroll
-        for (int i = 0; i < NCH; i += 4) {
-            float4 x = make_float4(0.f, 0.f, 0.f, 0.f), y = x, z = x;
-            if (valid) {
-                x = load4<TIn>(a.q, bk + i);
-                y = load4<TIn>(a.k, bk + i);
-                z = *reinterpret_cast<const float4*>(a.g + bk + i);
-            }
-            qv[i] = x.x; qv[i + 1] = x.y; qv[i + 2] = x.z; qv[i + 3] = x.w;
-            kv[i] = y.x; kv[i + 1] = y.y; kv[i + 2] = y.z; kv[i + 3] = y.w;
-            *reinterpret_cast<float4*>(&sG[r * LDG + c0 + i]) = z;
-        }
+    for (int j = 0; j < NGK; ++j) {
+        gran_to_f32(X.q[j], qf[j], tag);
+        gran_to_f32(X.k[j], kf[j], tag);
 #pragma unroll
-        for (int i = 0; i < NCV; i += 4) {
-            float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (valid) x = load4<TIn>(a.v, bv + i);
-            sVt[(j0 + i) * LDT + r] = M::from_f32(x.x);
-            sVt[(j0 + i + 1) * LDT + r] = M::from_f32(x.y);
-            sVt[(j0 + i + 2) * LDT + r] = M::from_f32(x.z);
-            sVt[(j0 + i + 3) * LDT + r] = M::from_f32(x.w);
-        }
+        for (int m = 0; m < GW / 4; ++m)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) gf[j][4 * m + e] = X.g[j][m][e];
     }
     if (a.use_l2) {
         float sq = 0.f, sk = 0.f;
 #pragma unroll
-        for (int i = 0; i < NCH; ++i) {
-            sq = fmaf(qv[i], qv[i], sq);
-            sk = fmaf(kv[i], kv[i], sk);
-        }
-        sq += __shfl_xor(sq, 1, 64);
-        sk += __shfl_xor(sk, 1, 64);
-        sq += __shfl_xor(sq, 2, 64);
-        sk += __shfl_xor(sk, 2, 64);
+        for (int j = 0; j < NGK; ++j)
+#pragma unroll
+            for (int e = 0; e < GW; ++e) {
+                sq = fmaf(qf[j][e], qf[j][e], sq);
+                sk = fmaf(kf[j][e], kf[j][e], sk);
+            }
+        sq += __shfl_xor(sq, 16, 64);
+        sk += __shfl_xor(sk, 16, 64);
+        sq += __shfl_xor(sq, 32, 64);
+        sk += __shfl_xor(sk, 32, 64);
         const float iq = 1.f / sqrtf(sq + kNormEps), ik = 1.f / sqrtf(sk + kNormEps);
 #pragma unroll
-        for (int i = 0; i < NCH; ++i) {
-            qv[i] *= iq;
-            kv[i] *= ik;
-        }
+        for (int j = 0; j < NGK; ++j)
+#pragma unroll
+            for (int e = 0; e < GW; ++e) {
+                qf[j][e] *= iq;
+                kf[j][e] *= ik;
+            }
     }
-    if (sg == 0) sBeta[r] = valid ? a.beta[tok * H + h] : 0.f;
-    // P's strictly-upper 16x16 blocks are read by the k-loops of phase 7: zero them
-    for (int idx = tid; idx < 64 * kChunk; idx += kThreads) {
-        const int t = idx / kChunk, s = idx % kChunk;
-        if ((s >> 4) > (t >> 4)) sPm[t * LDT + s] = M::from_f32(0.f);
+#pragma unroll
+    for (int j = 0; j < NGK; ++j)
+#pragma unroll
+        for (int e = 0; e < GW; ++e) gf[j][e] = row_scan16(gf[j][e]);
+    if (r == 15) {
+#pragma unroll
+        for (int j = 0; j < NGK; ++j)
+#pragma unroll
+            for (int m = 0; m < GW / 4; ++m)
+                *reinterpret_cast<f32x4*>(sTot + wave * DK + GW * (4 * j + q) + 4 * m) =
+                    f32x4{gf[j][4 * m], gf[j][4 * m + 1], gf[j][4 * m + 2], gf[j][4 * m + 3]};
     }
+    if (q == 0) sBeta[t] = X.beta;
     lds_barrier();
 
-    // ---- 2. gate cumsum over the chunk's tokens, per key channel ----------------------
+    // ---- 2. G, exp factors, operands --------------------------------------------------
+    u32x4 KG[NGK], QG[NGK];
     {
-        constexpr int NP = kThreads / DK, RP = 64 / NP;
-        const int c = tid % DK, part = tid / DK;
-        float x[RP];
-        float run = 0.f;
+        float* gl_out = reinterpret_cast<float*>(rec + ws.o_gl);
 #pragma unroll
-        for (int i = 0; i < RP; ++i) {
-            run += sG[(part * RP + i) * LDG + c];
-            x[i] = run;
+        for (int j = 0; j < NGK; ++j) {
+            float kg[GW], ki[GW], qg[GW], kt[GW];
+#pragma unroll
+            for (int m = 0; m < GW / 4; ++m) {
+                const int c = GW * (4 * j + q) + 4 * m;
+                f32x4 pre = {0.f, 0.f, 0.f, 0.f}, tot = pre;
+#pragma unroll
+                for (int w2 = 0; w2 < 4; ++w2) {
+                    const f32x4 x = *reinterpret_cast<const f32x4*>(sTot + w2 * DK + c);
+                    if (w2 < wave) pre += x;
+                    tot += x;
+                }
+                f32x4 egl;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int i = 4 * m + e;
+                    const float G = gf[j][i] + pre[e];
+                    const float eg = __expf(G), ei = __expf(-G);
+                    egl[e] = __expf(tot[e]);
+                    kg[i] = kf[j][i] * eg;
+                    ki[i] = kf[j][i] * ei;
+                    qg[i] = qf[j][i] * eg;
+                    kt[i] = kf[j][i] * __expf(tot[e] - G);
+                }
+                if (wave == 0 && r == 0) *reinterpret_cast<f32x4*>(gl_out + c) = egl;
+            }
+            KG[j] = f32_to_gran(kg, tag);
+            QG[j] = f32_to_gran(qg, tag);
+            *reinterpret_cast<u32x4*>(sKI + t * LDK + GW * (4 * j + q)) = f32_to_gran(ki, tag);
+            *reinterpret_cast<u32x4*>(sQG + t * LDK + GW * (4 * j + q)) = QG[j];
+            // transposed copies [channel][token]
+            if constexpr (E == 2) {
+                // pair adjacent tokens: even lanes write channel e, odd lanes channel e + 1
+                float kgr[GW], ktr[GW];
+                gran_to_f32(KG[j], kgr, tag);
+                gran_to_f32(f32_to_gran(kt, tag), ktr, tag);
+                const bool odd = r & 1;
+                const int te = t & ~1;
+#pragma unroll
+                for (int e = 0; e < GW; e += 2) {
+                    const int c = GW * (4 * j + q) + e + (odd ? 1 : 0);
+                    const float s1 = swap_adjacent(odd ? kgr[e] : kgr[e + 1]);
+                    const float s2 = swap_adjacent(odd ? ktr[e] : ktr[e + 1]);
+                    const uint32_t w1 = odd ? pack_bf16x2(s1, kgr[e + 1]) : pack_bf16x2(kgr[e], s1);
+                    const uint32_t w2 = odd ? pack_bf16x2(s2, ktr[e + 1]) : pack_bf16x2(ktr[e], s2);
+                    *reinterpret_cast<uint32_t*>(sKGt + c * LDT + te) = w1;
+                    *reinterpret_cast<uint32_t*>(sKTt + c * LDT + te) = w2;
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < GW; ++e) {
+                    const int c = GW * (4 * j + q) + e;
+                    sKGt[c * LDT + t] = kg[e];
+                    sKTt[c * LDT + t] = kt[e];
+                }
+            }
         }
-        sTot[part * DK + c] = run;
-        lds_barrier();
-        float off = 0.f;
-        for (int p = 0; p < part; ++p) off += sTot[p * DK + c];
 #pragma unroll
-        for (int i = 0; i < RP; ++i) sG[(part * RP + i) * LDG + c] = x[i] + off;
-        if (part == NP - 1) sGL[c] = x[RP - 1] + off;  // G at row 63 = G_{L-1} (padded rows add 0)
-    }
-    lds_barrier();
-
-    // ---- 3. operands: KG = kh e^G, KI = kh e^-G, QG = qh e^G, Kt = kh e^(G_L - G) ------
-    {
-        float gr[NCH];
+        for (int j = 0; j < NGV; ++j) {
+            float vf[GW];
+            gran_to_f32(X.v[j], vf, tag);
+            if constexpr (E == 2) {
+                const bool odd = r & 1;
+                const int te = t & ~1;
 #pragma unroll
-        for (int i = 0; i < NCH; i += 4) {
-            const float4 z = *reinterpret_cast<const float4*>(&sG[r * LDG + c0 + i]);
-            gr[i] = z.x; gr[i + 1] = z.y; gr[i + 2] = z.z; gr[i + 3] = z.w;
-        }
-        lds_barrier();  // G (X1) is dead from here: KG and KI take its place
+                for (int e = 0; e < GW; e += 2) {
+                    const int c = GW * (4 * j + q) + e + (odd ? 1 : 0);
+                    const float s1 = swap_adjacent(odd ? vf[e] : vf[e + 1]);
+                    *reinterpret_cast<uint32_t*>(sVt + c * LDT + te) =
+                        odd ? pack_bf16x2(s1, vf[e + 1]) : pack_bf16x2(vf[e], s1);
+                }
+            } else {
 #pragma unroll
-        for (int i = 0; i < NCH; ++i) {
-            const int c = c0 + i;
-            const float eg = __expf(gr[i]), ei = __expf(-gr[i]), et = __expf(sGL[c] - gr[i]);
-            const elem kg = M::from_f32(kv[i] * eg);
-            sKG[r * LDK + c] = kg;
-            sKGt[c * LDT + r] = kg;
-            sKI[r * LDK + c] = M::from_f32(kv[i] * ei);
-            sQG[r * LDK + c] = M::from_f32(qv[i] * eg);
-            sKtt[c * LDT + r] = M::from_f32(kv[i] * et);
-        }
-    }
-    lds_barrier();
-
-    // ---- 4. Kt^T and exp(G_L) to the workspace; A and P on MFMA -------------------------
-    {
-        constexpr int VE = 16 / E;
-        elem* gKt = reinterpret_cast<elem*>(rec + ws.o_kt);
-        for (int v = tid; v < DK * kChunk / VE; v += kThreads) {
-            const int c = v / (kChunk / VE), t = (v % (kChunk / VE)) * VE;
-            *reinterpret_cast<u32x4*>(gKt + c * kChunk + t) =
-                *reinterpret_cast<const u32x4*>(sKtt + c * LDT + t);
-        }
-        float* gGL = reinterpret_cast<float*>(rec + ws.o_gl);
-        for (int c = tid; c < DK; c += kThreads) gGL[c] = __expf(sGL[c]);
-    }
-    {
-        // 10 lower-triangular 16x16 tiles for each of A and P: 20 jobs, 5 per wave
-        // lower-triangular tile index -> (row block, column block), as bit fields: no
-        // data-dependent control flow between the MFMAs and the reads of their results
-        f32x4 acc[5];
-#pragma unroll
-        for (int n = 0; n < 5; ++n) {
-            const int job = wave + 4 * n;
-            const int which = job / 10, tix = job % 10;
-            const int ti = static_cast<int>((0x3333222110ull >> (4 * tix)) & 15);
-            const int tj = static_cast<int>((0x3210210100ull >> (4 * tix)) & 15);
-            const elem* Aop = (which == 0 ? sKG : sQG) + ti * 16 * LDK;
-            acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
-            acc[n] = mma_nt<TIn>(Aop, LDK, sKI + tj * 16 * LDK, LDK, 0, DK, acc[n], lane);
-        }
-        lds_barrier();  // Kt^T (X5) has been copied out: A takes its place
-#pragma unroll
-        for (int n = 0; n < 5; ++n) {
-            const int job = wave + 4 * n;
-            const int which = job / 10, tix = job % 10;
-            const int ti = static_cast<int>((0x3333222110ull >> (4 * tix)) & 15);
-            const int tj = static_cast<int>((0x3210210100ull >> (4 * tix)) & 15);
-            const int s = tj * 16 + (lane & 15);
-#pragma unroll
-            for (int rr = 0; rr < 4; ++rr) {
-                const int t = ti * 16 + 4 * (lane >> 4) + rr;
-                if (which == 0)
-                    sA[t * LDA + s] = s < t ? sBeta[t] * acc[n][rr] : 0.f;
-                else
-                    sPm[t * LDT + s] = M::from_f32(s <= t ? acc[n][rr] : 0.f);
+                for (int e = 0; e < GW; ++e) sVt[(GW * (4 * j + q) + e) * LDT + t] = vf[e];
             }
         }
     }
     lds_barrier();
 
-    // ---- 5. T = (I + A)^-1 (unit lower triangular) in fp32, by 16x16 blocks ------------
-    // 5a. diagonal blocks by forward substitution (one thread per block column); the
-    //     strictly-upper blocks of T are zero.
-    if (wave == 0) {
-        const int bi = lane >> 4, col = lane & 15;
-        const float* Ab = sA + (16 * bi) * LDA + 16 * bi;
+    // ---- 3. Kt record; A^T and P^T tiles (all four column blocks, straight-line) -----
+    {
+        constexpr int NKT = DK / 16 * RG::GT * 64;  // granules of Kt
+        static_assert(NKT % kThreads == 0, "");
+#pragma unroll
+        for (int n = 0; n < NKT / kThreads; ++n) {
+            const int gi = tid + kThreads * n, ln = gi & 63, blk = gi >> 6;
+            const int c = 16 * (blk / RG::GT) + (ln & 15), g = blk % RG::GT, q2 = ln >> 4;
+            u32x4 val;
+            if constexpr (E == 2) {
+                const u32x2 lo = *reinterpret_cast<const u32x2*>(sKTt + c * LDT + 32 * g + 4 * q2);
+                const u32x2 hi = *reinterpret_cast<const u32x2*>(sKTt + c * LDT + 32 * g + 16 + 4 * q2);
+                val = u32x4{lo[0], lo[1], hi[0], hi[1]};
+            } else {
+                val = *reinterpret_cast<const u32x4*>(sKTt + c * LDT + 16 * g + 4 * q2);
+            }
+            *reinterpret_cast<u32x4*>(rec + ws.o_kt + static_cast<size_t>(gi) * 16) = val;
+        }
+    }
+    f32x4 Areg[4];
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+        f32x4 accA = {0.f, 0.f, 0.f, 0.f}, accP = accA;
+#pragma unroll
+        for (int j = 0; j < NGK; ++j) {
+            const u32x4 b = *reinterpret_cast<const u32x4*>(sKI + (16 * jj + r) * LDK + GW * (4 * j + q));
+            accA = gmma(b, KG[j], accA, tag);
+            accP = gmma(b, QG[j], accP, tag);
+        }
+        // lane holds (s = 16 jj + 4q + rr, t): A_ts = beta_t (KG_t . KI_s) for s < t
+        float p4[4];
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+            const int s = 16 * jj + 4 * q + rr;
+            Areg[jj][rr] = s < t ? X.beta * accA[rr] : 0.f;
+            p4[rr] = s <= t ? accP[rr] : 0.f;
+        }
+        lds_store4(sP + t * LDT + 16 * jj + 4 * q, p4[0], p4[1], p4[2], p4[3]);
+    }
+    lds_barrier();
+
+    // ---- 4. A to LDS (Kt^T is dead); zero the upper blocks of T' ----------------------
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) *reinterpret_cast<f32x4*>(sA + t * LDA + 16 * jj + 4 * q) = Areg[jj];
+    for (int jj = wave + 1; jj < 4; ++jj) lds_store4(sTp + t * LDT + 16 * jj + 4 * q, 0.f, 0.f, 0.f, 0.f);
+    lds_barrier();
+
+    // ---- 5. T = (I + A)^-1 by 16x16 blocks ----------------------------------------------
+    // 5a. diagonal block of this wave by forward substitution, one lane per column
+    {
+        const int col = r;
+        const float* Ab = sA + (16 * wave) * LDA + 16 * wave;
         float x[16];
 #pragma unroll
         for (int rr = 0; rr < 16; ++rr) {
+            f32x4 row[4];
+#pragma unroll
+            for (int m = 0; m < 4; ++m) row[m] = *reinterpret_cast<const f32x4*>(Ab + rr * LDA + 4 * m);
             float acc = rr == col ? 1.f : 0.f;
 #pragma unroll
-            for (int s = 0; s < rr; ++s) acc = fmaf(-Ab[rr * LDA + s], x[s], acc);
-            x[rr] = rr < col ? 0.f : acc;
+            for (int s = 0; s < rr; ++s) acc = fmaf(-row[s >> 2][s & 3], x[s], acc);
+            x[rr] = acc;
         }
+        if (q == 0) {
+            const float bc = sBeta[16 * wave + col];
 #pragma unroll
-        for (int rr = 0; rr < 16; ++rr) sT[(16 * bi + rr) * LDA + 16 * bi + col] = x[rr];
-    } else {
-        for (int idx = tid - 64; idx < 64 * 64; idx += kThreads - 64) {
-            const int t = idx / 64, s = idx % 64;
-            if ((s >> 4) > (t >> 4)) sT[t * LDA + s] = 0.f;
-        }
-    }
-    lds_barrier();
-    // 5b-d. off-diagonal blocks, one diagonal of blocks at a time:
-    //   T_ij = -T_ii * sum_{k=j}^{i-1} A_ik T_kj
-    for (int d = 1; d < 4; ++d) {
-        if (wave < 4 - d) {
-            const int i = wave + d, j = wave;
-            f32x4 y = {0.f, 0.f, 0.f, 0.f};
-            for (int k = j; k < i; ++k)
-                y = mma16_nn_f32(sA + (16 * i) * LDA + 16 * k, LDA, sT + (16 * k) * LDA + 16 * j, LDA, y, lane);
-            float* scr = sScr + wave * 256;
-            store16_f32(scr, 16, y, 1.f, lane);
-            f32x4 z = {0.f, 0.f, 0.f, 0.f};
-            z = mma16_nn_f32(sT + (16 * i) * LDA + 16 * i, LDA, scr, 16, z, lane);
-            store16_f32(sT + (16 * i) * LDA + 16 * j, LDA, z, -1.f, lane);
-        }
-        lds_barrier();
-    }
-    // 5e. T' = T diag(beta) in the MFMA operand type (A, in X5, is dead)
-    for (int idx = tid; idx < 64 * 64; idx += kThreads) {
-        const int t = idx / 64, s = idx % 64;
-        sTp[t * LDT + s] = M::from_f32(sT[t * LDA + s] * sBeta[s]);
-    }
-    lds_barrier();
-
-    // ---- 6. W = T' KG and Ut = T' V on MFMA -> W^T, Ut^T (T is dead: X1 reused) ----------
-    {
-        constexpr int NCB = (DK + DV) / 16;
-        for (int job = wave; job < 4 * NCB; job += 4) {
-            const int ti = job & 3, cb = job >> 2;
-            const int kend = 32 * (ti / 2 + 1);  // T' is lower triangular
-            const bool isw = cb < DK / 16;
-            const elem* Bop = isw ? sKGt + cb * 16 * LDT : sVt + (cb - DK / 16) * 16 * LDT;
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            acc = mma_nt<TIn>(sTp + ti * 16 * LDT, LDT, Bop, LDT, 0, kend, acc, lane);
-            elem* D = isw ? sWt + cb * 16 * LDT : sUt + (cb - DK / 16) * 16 * LDT;
-            const int col = lane & 15, t = ti * 16 + 4 * (lane >> 4);
-#pragma unroll
-            for (int rr = 0; rr < 4; ++rr) D[col * LDT + t + rr] = M::from_f32(acc[rr]);
-        }
-    }
-    lds_barrier();
-
-    // ---- 7. Q' = QG - P W -> row-major staging; Ot = P Ut -> Ot^T staging -------------
-    {
-        constexpr int NCB = (DK + DV) / 16;
-        for (int job = wave; job < 4 * NCB; job += 4) {
-            const int ti = job & 3, cb = job >> 2;
-            const int kend = 32 * (ti / 2 + 1);
-            const bool isq = cb < DK / 16;
-            const elem* Bop = isq ? sWt + cb * 16 * LDT : sUt + (cb - DK / 16) * 16 * LDT;
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            acc = mma_nt<TIn>(sPm + ti * 16 * LDT, LDT, Bop, LDT, 0, kend, acc, lane);
-            const int col = lane & 15, t = ti * 16 + 4 * (lane >> 4);
-            if (isq) {
-                const int c = cb * 16 + col;
-#pragma unroll
-                for (int rr = 0; rr < 4; ++rr)
-                    sQo[(t + rr) * LDK + c] = M::from_f32(M::to_f32(sQG[(t + rr) * LDK + c]) - acc[rr]);
-            } else {
-                const int j = (cb - DK / 16) * 16 + col;
-#pragma unroll
-                for (int rr = 0; rr < 4; ++rr) sOt[j * LDT + t + rr] = M::from_f32(acc[rr]);
+            for (int rr = 0; rr < 16; ++rr) {
+                sT[(16 * wave + rr) * LDA + 16 * wave + col] = x[rr];
+                sTp[(16 * wave + rr) * LDT + 16 * wave + col] = Mma<TIn>::from_f32(x[rr] * bc);
             }
         }
     }
     lds_barrier();
-
-    // ---- 8. W, Q' (row-major) and Ut^T, Ot^T to the workspace, 16-byte stores ----------
-    {
-        constexpr int VE = 16 / E;
-        elem* gW = reinterpret_cast<elem*>(rec + ws.o_w);
-        elem* gQ = reinterpret_cast<elem*>(rec + ws.o_q);
-        elem* gU = reinterpret_cast<elem*>(rec + ws.o_u);
-        elem* gO = reinterpret_cast<elem*>(rec + ws.o_o);
-        for (int v = tid; v < kChunk * DK / VE; v += kThreads) {
-            const int t = v / (DK / VE), c = (v % (DK / VE)) * VE;
-            elem tmp[VE];
+    // 5b. T_{w, w-d} = -T_ww sum_{k = w-d}^{w-1} A_wk T_{k, w-d}, one block diagonal at a time
 #pragma unroll
-            for (int e = 0; e < VE; ++e) tmp[e] = sWt[(c + e) * LDT + t];
-            *reinterpret_cast<u32x4*>(gW + t * DK + c) = *reinterpret_cast<const u32x4*>(tmp);
-            *reinterpret_cast<u32x4*>(gQ + t * DK + c) = *reinterpret_cast<const u32x4*>(sQo + t * LDK + c);
+    for (int d = 1; d < 4; ++d) {
+        if (wave >= d) {
+            const int jb = wave - d;
+            f32x4 y = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < d; ++kk) {
+                const int kb = jb + kk;
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks)
+                    y = __builtin_amdgcn_mfma_f32_16x16x4f32(sA[(16 * wave + r) * LDA + 16 * kb + 4 * ks + q],
+                                                             sT[(16 * kb + 4 * ks + q) * LDA + 16 * jb + r], y, 0,
+                                                             0, 0);
+            }
+            // z = T_ww y; lane (r, q) supplies k = 4q + ks of both operands
+            f32x4 z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks)
+                z = __builtin_amdgcn_mfma_f32_16x16x4f32(sT[(16 * wave + r) * LDA + 16 * wave + 4 * q + ks], y[ks], z,
+                                                         0, 0, 0);
+            const float bc = sBeta[16 * jb + r];
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+                const int row = 16 * wave + 4 * q + rr;
+                sT[row * LDA + 16 * jb + r] = -z[rr];
+                sTp[row * LDT + 16 * jb + r] = Mma<TIn>::from_f32(-z[rr] * bc);
+            }
         }
-        for (int v = tid; v < DV * kChunk / VE; v += kThreads) {
-            const int j = v / (kChunk / VE), t = (v % (kChunk / VE)) * VE;
-            *reinterpret_cast<u32x4*>(gU + j * kChunk + t) = *reinterpret_cast<const u32x4*>(sUt + j * LDT + t);
-            *reinterpret_cast<u32x4*>(gO + j * kChunk + t) = *reinterpret_cast<const u32x4*>(sOt + j * LDT + t);
+        lds_barrier();
+    }
+
+    // ---- 6. W = T' KG, Ut = T' V (tiles rows t) and W^T (record) ------------------------
+    constexpr int NCK = DK / 16, NCV = DV / 16;
+    uint32_t wpk[NCK][E], upk[NCV][E];  // packed 4-element columns for W^T / Ut^T in LDS
+    {
+        const elem* Tr = sTp + (16 * wave + r) * LDT + (KS / 4) * q;
+        f32x4 wt[NCK];
+#pragma unroll
+        for (int cb = 0; cb < NCK; ++cb) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acc2 = acc;
+            const elem* Kr = sKGt + (16 * cb + r) * LDT + (KS / 4) * q;
+#pragma unroll
+            for (int ks = 0; ks < KST; ++ks) {
+                acc = lmma(Tr + KS * ks, Kr + KS * ks, acc);   // W tile (t, c)
+                acc2 = lmma(Kr + KS * ks, Tr + KS * ks, acc2);  // W^T tile (c, t)
+            }
+            wt[cb] = acc2;
+            if constexpr (E == 2) {
+                wpk[cb][0] = pack_bf16x2(acc[0], acc[1]);
+                wpk[cb][1] = pack_bf16x2(acc[2], acc[3]);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) wpk[cb][e] = __float_as_uint(acc[e]);
+            }
+        }
+#pragma unroll
+        for (int g = 0; g < RG::GK; ++g)
+            *reinterpret_cast<u32x4*>(rec + ws.o_w + ((static_cast<size_t>(wave) * RG::GK + g) * 64 + lane) * 16) =
+                tiles_to_gran(wt[RG::CT * g], wt[RG::CT * g + RG::CT - 1], tag);
+#pragma unroll
+        for (int jb = 0; jb < NCV; ++jb) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            const elem* Vr = sVt + (16 * jb + r) * LDT + (KS / 4) * q;
+#pragma unroll
+            for (int ks = 0; ks < KST; ++ks) acc = lmma(Tr + KS * ks, Vr + KS * ks, acc);
+            if constexpr (E == 2) {
+                upk[jb][0] = pack_bf16x2(acc[0], acc[1]);
+                upk[jb][1] = pack_bf16x2(acc[2], acc[3]);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) upk[jb][e] = __float_as_uint(acc[e]);
+            }
+        }
+        // Ut record: per dv tile, the NCB column blocks' 4 values each
+#pragma unroll
+        for (int tile = 0; tile < RG::NT; ++tile) {
+            char* dst = rec + ws.o_uo + ((static_cast<size_t>(tile * 4 + wave) * 2 + 0) * 64 + lane) * RG::UB;
+#pragma unroll
+            for (int n = 0; n < RG::UB / 16; ++n) {
+                u32x4 val;
+                if constexpr (E == 2)
+                    val = u32x4{upk[RG::NCB * tile + 2 * n][0], upk[RG::NCB * tile + 2 * n][1],
+                                upk[RG::NCB * tile + 2 * n + 1][0], upk[RG::NCB * tile + 2 * n + 1][1]};
+                else
+                    val = u32x4{upk[RG::NCB * tile + n][0], upk[RG::NCB * tile + n][1], upk[RG::NCB * tile + n][2],
+                                upk[RG::NCB * tile + n][3]};
+                *reinterpret_cast<u32x4*>(dst + 16 * n) = val;
+            }
+        }
+    }
+    lds_barrier();  // every wave is done reading KG^T and V^T
+#pragma unroll
+    for (int cb = 0; cb < NCK; ++cb) {
+        elem* d = sWt + (16 * cb + r) * LDT + 16 * wave + 4 * q;
+        if constexpr (E == 2)
+            *reinterpret_cast<u32x2*>(d) = u32x2{wpk[cb][0], wpk[cb][1]};
+        else
+            *reinterpret_cast<u32x4*>(d) = u32x4{wpk[cb][0], wpk[cb][1], wpk[cb][2], wpk[cb][3]};
+    }
+#pragma unroll
+    for (int jb = 0; jb < NCV; ++jb) {
+        elem* d = sUt + (16 * jb + r) * LDT + 16 * wave + 4 * q;
+        if constexpr (E == 2)
+            *reinterpret_cast<u32x2*>(d) = u32x2{upk[jb][0], upk[jb][1]};
+        else
+            *reinterpret_cast<u32x4*>(d) = u32x4{upk[jb][0], upk[jb][1], upk[jb][2], upk[jb][3]};
+    }
+    lds_barrier();
+
+    // ---- 7. Q'^T = QG^T - W^T P^T and Ot = P Ut (records) ------------------------------
+    {
+        const elem* Pr = sP + (16 * wave + r) * LDT + (KS / 4) * q;
+        f32x4 qt[NCK];
+#pragma unroll
+        for (int cb = 0; cb < NCK; ++cb) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            const elem* Wr = sWt + (16 * cb + r) * LDT + (KS / 4) * q;
+#pragma unroll
+            for (int ks = 0; ks < KST; ++ks) acc = lmma(Wr + KS * ks, Pr + KS * ks, acc);
+            // lane holds (c = 16 cb + 4q + rr, t): Q'_tc = QG_tc - (P W)_tc
+            qt[cb] = lds_load4(sQG + t * LDK + 16 * cb + 4 * q) - acc;
+        }
+#pragma unroll
+        for (int g = 0; g < RG::GK; ++g)
+            *reinterpret_cast<u32x4*>(rec + ws.o_q + ((static_cast<size_t>(wave) * RG::GK + g) * 64 + lane) * 16) =
+                tiles_to_gran(qt[RG::CT * g], qt[RG::CT * g + RG::CT - 1], tag);
+        f32x4 ot[NCV];
+#pragma unroll
+        for (int jb = 0; jb < NCV; ++jb) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            const elem* Ur = sUt + (16 * jb + r) * LDT + (KS / 4) * q;
+#pragma unroll
+            for (int ks = 0; ks < KST; ++ks) acc = lmma(Pr + KS * ks, Ur + KS * ks, acc);
+            ot[jb] = acc;
+        }
+#pragma unroll
+        for (int tile = 0; tile < RG::NT; ++tile) {
+            char* dst = rec + ws.o_uo + ((static_cast<size_t>(tile * 4 + wave) * 2 + 1) * 64 + lane) * RG::UB;
+#pragma unroll
+            for (int n = 0; n < RG::UB / 16; ++n) {
+                const int jb = RG::NCB * tile + (E == 2 ? 2 * n : n);
+                *reinterpret_cast<u32x4*>(dst + 16 * n) = tiles_to_gran(ot[jb], ot[E == 2 ? jb + 1 : jb], tag);
+            }
         }
     }
 }
 
+// Persistent: workgroup b takes items b, b + grid, ... (item = chunk * H + head); the
+// next item's inputs are requested before the current one is computed.
+template <int DK, int DV, class TIn>
+__global__ __launch_bounds__(kThreads) void chunk_intra_kernel(PrefillArgs a) {
+    using P = IntraPlan<DK, DV, TIn>;
+    static_assert(P::fits, "LDS plan exceeds 160 KiB");
+    __shared__ __attribute__((aligned(16))) char smem[P::BYTES];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int H = a.H;
+    const WsLayout ws(a.num_seqs, a.total_tokens, H, DK, DV, P::E);
+    const int32_t* chunk_off = static_cast<const int32_t*>(a.workspace);
+    const int4* table = reinterpret_cast<const int4*>(static_cast<const char*>(a.workspace) + ws.off_table);
+    char* recs = static_cast<char*>(a.workspace) + ws.off_rec;
+    const int total = chunk_off[a.num_seqs] * H;
+    const int stride = gridDim.x;
+    int item = blockIdx.x;
+    if (item >= total) return;
+
+    IntraIn<DK, DV, TIn> X;
+    {
+        const int4 info = table[item / H];
+        intra_fetch(X, a, info.y, info.z, item % H, wave, lane);
+    }
+    for (; item < total; item += stride) {
+        const IntraIn<DK, DV, TIn> Y = X;
+        const int nxt = item + stride < total ? item + stride : item;  // the last fetch is a harmless repeat
+        {
+            const int4 info = table[nxt / H];
+            intra_fetch(X, a, info.y, info.z, nxt % H, wave, lane);
+        }
+        char* rec = recs + ws.rec_bytes * static_cast<size_t>(item);
+        intra_compute(Y, smem, a, rec, ws, wave, lane, tid);
+    }
+}
+
 // ---------------------------------------------------------------------------
-// 3. chunk_carry
+// 3. chunk_carry: one workgroup (4 waves) per (sequence, head, BV-column dv tile),
+//    sequential over the sequence's chunks.  Wave w owns token rows 16w .. 16w+15 of
+//    U and O and key rows 16 RB w .. 16 RB (w+1) - 1 of S.  Its granules of W, Q',
+//    Kt, Ut, Ot and exp(G_L) go from the workspace into registers NB chunks ahead of
+//    their use; every fetch is issued unconditionally (clamped to the last chunk) and
+//    the ragged output rows are dropped by the buffer range check, so the loop has
+//    no data-dependent memory operations and the loads stay in flight across steps.
+//    S and U cross between waves through LDS as whole granules.
 // ---------------------------------------------------------------------------
 template <int DK, int DV, class TIn>
 struct CarryPlan {
-    using M = Mma<TIn>;
-    using elem = typename M::elem;
-    static constexpr int E = sizeof(elem);
-    static constexpr int BV = kCarryBV;
-    static constexpr int PAD = E == 2 ? 8 : 4;
-    static constexpr int LDK = DK + PAD;      // W, Q' [64][LDK]; S^T [BV][LDK]
-    static constexpr int LDT = kChunk + PAD;  // Kt [DK][LDT]; U^T [BV][LDT]
-    // one operand buffer (per chunk); Ut^T, Ot^T tiles are [BV][LDT]
-    static constexpr size_t B_W = 64ull * LDK * E, B_Q = B_W, B_KT = 1ull * DK * LDT * E;
-    static constexpr size_t B_U = 1ull * BV * LDT * E, B_O = B_U, B_GL = 4ull * DK;
-    static constexpr size_t O_W = 0, O_Q = O_W + B_W, O_KT = O_Q + B_Q, O_U = O_KT + B_KT;
-    static constexpr size_t O_O = O_U + B_U, O_GL = O_O + B_O;
-    static constexpr size_t BUF = align_up(O_GL + B_GL, 16);
-    static constexpr size_t O_ST = 2 * BUF, O_UT = O_ST + align_up(1ull * BV * LDK * E, 16);
-    static constexpr size_t BYTES = O_UT + align_up(1ull * BV * LDT * E, 16);
-    static constexpr bool fits = BYTES <= 160 * 1024;
-    // 16-byte vectors per chunk to stage, per operand (each a multiple of kThreads
-    // except exp(G_L))
-    static constexpr int VE = 16 / E;
-    static constexpr int NV_W = 64 * DK / VE, NV_KT = DK * 64 / VE, NV_U = BV * 64 / VE;
-    static constexpr int NV_GL = DK / 4;
-    static constexpr int PT_W = NV_W / kThreads, PT_KT = NV_KT / kThreads, PT_U = NV_U / kThreads;
-    static_assert(NV_W % kThreads == 0 && NV_KT % kThreads == 0 && NV_U % kThreads == 0, "");
-    static_assert(NV_GL <= kThreads, "");
+    using RG = RecGeo<DK, DV, TIn>;
+    static constexpr int E = RG::E, CT = RG::CT, GK = RG::GK, GT = RG::GT;
+    static constexpr int BV = RG::BV, NCB = RG::NCB, NT = RG::NT;
+    static constexpr int RB = DK / 64;  // 16-row blocks of S per wave
+    static constexpr int NUB = RG::UB / 16;
+    static constexpr size_t O_SX = 0, O_UX = 1ull * GK * NCB * 64 * 16;
+    static constexpr size_t BYTES = O_UX + 1ull * GT * NCB * 64 * 16;
 };
-
-// One chunk's operands in flight: fetched from the workspace into registers while
-// the previous chunk computes, then stored to an LDS buffer.
-template <class CP>
-struct CarryRegs {
-    u32x4 w[CP::PT_W], q[CP::PT_W], kt[CP::PT_KT], u[CP::PT_U], o[CP::PT_U], gl;
-};
-
-template <class CP>
-__device__ __forceinline__ void carry_fetch(CarryRegs<CP>& R, const char* rec, const WsLayout& ws,
-                                            int tile, int tid, int DV) {
-    const u32x4* gw = reinterpret_cast<const u32x4*>(rec + ws.o_w);
-    const u32x4* gq = reinterpret_cast<const u32x4*>(rec + ws.o_q);
-    const u32x4* gk = reinterpret_cast<const u32x4*>(rec + ws.o_kt);
-#pragma unroll
-    for (int i = 0; i < CP::PT_W; ++i) {
-        R.w[i] = gw[tid + i * kThreads];
-        R.q[i] = gq[tid + i * kThreads];
-    }
-#pragma unroll
-    for (int i = 0; i < CP::PT_KT; ++i) R.kt[i] = gk[tid + i * kThreads];
-    // the tile's rows of Ut^T / Ot^T are contiguous
-    const size_t toff = static_cast<size_t>(tile) * CP::BV * kChunk * CP::E;
-#pragma unroll
-    for (int i = 0; i < CP::PT_U; ++i) {
-        const size_t off = toff + static_cast<size_t>(tid + i * kThreads) * 16;
-        R.u[i] = *reinterpret_cast<const u32x4*>(rec + ws.o_u + off);
-        R.o[i] = *reinterpret_cast<const u32x4*>(rec + ws.o_o + off);
-    }
-    if (tid < CP::NV_GL) R.gl = reinterpret_cast<const u32x4*>(rec + ws.o_gl)[tid];
-}
-
-template <class CP>
-__device__ __forceinline__ void carry_stage(const CarryRegs<CP>& R, char* buf, int tid) {
-    constexpr int DK = CP::LDK - CP::PAD;
-#pragma unroll
-    for (int i = 0; i < CP::PT_W; ++i) {
-        const int v = tid + i * kThreads;
-        const int t = v / (DK / CP::VE), c = (v % (DK / CP::VE)) * CP::VE;
-        const size_t off = (static_cast<size_t>(t) * CP::LDK + c) * CP::E;
-        *reinterpret_cast<u32x4*>(buf + CP::O_W + off) = R.w[i];
-        *reinterpret_cast<u32x4*>(buf + CP::O_Q + off) = R.q[i];
-    }
-#pragma unroll
-    for (int i = 0; i < CP::PT_KT; ++i) {
-        const int v = tid + i * kThreads;
-        const int c = v / (kChunk / CP::VE), t = (v % (kChunk / CP::VE)) * CP::VE;
-        *reinterpret_cast<u32x4*>(buf + CP::O_KT + (static_cast<size_t>(c) * CP::LDT + t) * CP::E) = R.kt[i];
-    }
-#pragma unroll
-    for (int i = 0; i < CP::PT_U; ++i) {
-        const int v = tid + i * kThreads;
-        const int j = v / (kChunk / CP::VE), t = (v % (kChunk / CP::VE)) * CP::VE;
-        const size_t off = (static_cast<size_t>(j) * CP::LDT + t) * CP::E;
-        *reinterpret_cast<u32x4*>(buf + CP::O_U + off) = R.u[i];
-        *reinterpret_cast<u32x4*>(buf + CP::O_O + off) = R.o[i];
-    }
-    if (tid < CP::NV_GL) reinterpret_cast<u32x4*>(buf + CP::O_GL)[tid] = R.gl;
-}
 
 template <int DK, int DV, class TIn>
+struct CarryOps {
+    using CP = CarryPlan<DK, DV, TIn>;
+    u32x4 w[CP::GK], q[CP::GK], kt[CP::RB][CP::GT], u[CP::NUB], o[CP::NUB];
+    f32x4 gl[CP::RB];
+};
+
+template <int DK, int DV, class TIn>
+__device__ __forceinline__ void carry_fetch(CarryOps<DK, DV, TIn>& F, const char* rec, const WsLayout& ws,
+                                            int tile, int wave, int lane) {
+    using CP = CarryPlan<DK, DV, TIn>;
+#pragma unroll
+    for (int g = 0; g < CP::GK; ++g) {
+        const size_t off = ((static_cast<size_t>(wave) * CP::GK + g) * 64 + lane) * 16;
+        F.w[g] = *reinterpret_cast<const u32x4*>(rec + ws.o_w + off);
+        F.q[g] = *reinterpret_cast<const u32x4*>(rec + ws.o_q + off);
+    }
+#pragma unroll
+    for (int i = 0; i < CP::RB; ++i)
+#pragma unroll
+        for (int g = 0; g < CP::GT; ++g)
+            F.kt[i][g] = *reinterpret_cast<const u32x4*>(
+                rec + ws.o_kt + ((static_cast<size_t>(CP::RB * wave + i) * CP::GT + g) * 64 + lane) * 16);
+    const char* uo = rec + ws.o_uo + (static_cast<size_t>(tile * 4 + wave) * 2 * 64 + lane) * (CP::NUB * 16);
+#pragma unroll
+    for (int n = 0; n < CP::NUB; ++n) {
+        F.u[n] = *reinterpret_cast<const u32x4*>(uo + 16 * n);
+        F.o[n] = *reinterpret_cast<const u32x4*>(uo + 64 * CP::NUB * 16 + 16 * n);
+    }
+#pragma unroll
+    for (int i = 0; i < CP::RB; ++i)
+        F.gl[i] = *reinterpret_cast<const f32x4*>(rec + ws.o_gl + (16 * (CP::RB * wave + i) + 4 * (lane >> 4)) * 4);
+}
+
+// Value (column block cb, row rr) of a U/O part held as granules.
+__device__ __forceinline__ float uo_val(const u32x4* p, int cb, int rr, BF16) {
+    const uint32_t w = p[(cb * 4 + rr) >> 3][((cb * 4 + rr) >> 1) & 3];
+    return __uint_as_float((rr & 1) ? (w & 0xffff0000u) : (w << 16));
+}
+__device__ __forceinline__ float uo_val(const u32x4* p, int cb, int rr, F32) { return __uint_as_float(p[cb][rr]); }
+
+__device__ __forceinline__ void store_out(__amdgpu_buffer_rsrc_t r, int off_elems, float x, BF16) {
+    __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(x), r, off_elems * 2, 0, 0);
+}
+__device__ __forceinline__ void store_out(__amdgpu_buffer_rsrc_t r, int off_elems, float x, F32) {
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), r, off_elems * 4, 0, 0);
+}
+
+// Accumulator tile (4 values) into its granule slot in LDS: the 8-byte half of a
+// bf16 granule, or a whole fp32 granule.
+__device__ __forceinline__ void lds_tile_to_gran(char* base, int gran_idx, int half, f32x4 v, BF16) {
+    *reinterpret_cast<u32x2*>(base + gran_idx * 16 + half * 8) =
+        u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+}
+__device__ __forceinline__ void lds_tile_to_gran(char* base, int gran_idx, int, f32x4 v, F32) {
+    *reinterpret_cast<f32x4*>(base + gran_idx * 16) = v;
+}
+
+// One chunk: U = Ut - W S, O = scale (Q' S + Ot) (rows >= L dropped by the buffer range),
+// S = diag(exp(G_L)) S + Kt U.
+template <int DK, int DV, class TIn>
+__device__ __forceinline__ void carry_step(const CarryOps<DK, DV, TIn>& F, f32x4 (&S)[DK / 64][kCarryBV / 16],
+                                           char* sx, char* ux, __amdgpu_buffer_rsrc_t orsrc, int orow, int ocol,
+                                           float scale, int wave, int lane) {
+    using CP = CarryPlan<DK, DV, TIn>;
+    constexpr TIn tag{};
+    const int r = lane & 15, q4 = 4 * (lane >> 4);
+
+    // (1) this wave's S tiles -> S granules (k over dk) in LDS
+#pragma unroll
+    for (int i = 0; i < CP::RB; ++i) {
+        const int cb = CP::RB * wave + i;
+#pragma unroll
+        for (int jb = 0; jb < CP::NCB; ++jb)
+            lds_tile_to_gran(sx, ((cb / CP::CT) * CP::NCB + jb) * 64 + lane, cb % CP::CT, S[i][jb], tag);
+    }
+    lds_barrier();
+
+    // (2) U and O for token rows 16 wave .. +15
+    const int trow = 16 * wave + q4;
+#pragma unroll
+    for (int jb = 0; jb < CP::NCB; ++jb) {
+        f32x4 u = {0.f, 0.f, 0.f, 0.f}, o = u;
+#pragma unroll
+        for (int g = 0; g < CP::GK; ++g) {
+            const u32x4 b = *reinterpret_cast<const u32x4*>(sx + ((g * CP::NCB + jb) * 64 + lane) * 16);
+            u = gmma(F.w[g], b, u, tag);
+            o = gmma(F.q[g], b, o, tag);
+        }
+        f32x4 uv;
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+            uv[rr] = uo_val(F.u, jb, rr, tag) - u[rr];
+            store_out(orsrc, (trow + rr) * orow + ocol + 16 * jb + r, scale * (o[rr] + uo_val(F.o, jb, rr, tag)),
+                      tag);
+        }
+        lds_tile_to_gran(ux, ((wave / CP::CT) * CP::NCB + jb) * 64 + lane, wave % CP::CT, uv, tag);
+    }
+    lds_barrier();
+
+    // (3) S = exp(G_L) S + Kt U
+#pragma unroll
+    for (int jb = 0; jb < CP::NCB; ++jb) {
+        u32x4 bu[CP::GT];
+#pragma unroll
+        for (int g = 0; g < CP::GT; ++g)
+            bu[g] = *reinterpret_cast<const u32x4*>(ux + ((g * CP::NCB + jb) * 64 + lane) * 16);
+#pragma unroll
+        for (int i = 0; i < CP::RB; ++i) {
+            f32x4 acc = S[i][jb] * F.gl[i];
+#pragma unroll
+            for (int g = 0; g < CP::GT; ++g) acc = gmma(F.kt[i][g], bu[g], acc, tag);
+            S[i][jb] = acc;
+        }
+    }
+}
+
+template <int DK, int DV, class TIn, int NB>
 __global__ __launch_bounds__(kThreads) void chunk_carry_kernel(PrefillArgs a) {
     using CP = CarryPlan<DK, DV, TIn>;
-    using M = typename CP::M;
-    using elem = typename CP::elem;
-    constexpr int BV = CP::BV, NT = DV / BV;
-    static_assert(CP::fits, "LDS plan exceeds 160 KiB");
+    constexpr int BV = CP::BV, NT = CP::NT, E = CP::E;
     __shared__ __attribute__((aligned(16))) char smem[CP::BYTES];
-    elem* sSt = reinterpret_cast<elem*>(smem + CP::O_ST);  // S^T [BV][LDK]
-    elem* sUt = reinterpret_cast<elem*>(smem + CP::O_UT);  // U^T [BV][LDT]
+    char* sx = smem + CP::O_SX;
+    char* ux = smem + CP::O_UX;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int H = a.H;
@@ -591,142 +907,96 @@ __global__ __launch_bounds__(kThreads) void chunk_carry_kernel(PrefillArgs a) {
     if (group >= groups) return;
     const int seq = group / H, h = group % H;
 
-    const WsLayout ws(a.num_seqs, a.total_tokens, H, DK, DV, CP::E);
+    const WsLayout ws(a.num_seqs, a.total_tokens, H, DK, DV, E);
     const int32_t* chunk_off = static_cast<const int32_t*>(a.workspace);
-    const int4* table = reinterpret_cast<const int4*>(static_cast<const char*>(a.workspace) + ws.off_table);
     const char* recs = static_cast<const char*>(a.workspace) + ws.off_rec;
     const int c_begin = chunk_off[seq], c_end = chunk_off[seq + 1];
+    const int bos = a.cu_seqlens[seq], eos = a.cu_seqlens[seq + 1];
     const int slot = a.slot_idx[seq];
     float* Sg = a.pool + (static_cast<int64_t>(slot) * H + h) * (DK * DV) + tile * BV;
 
-    // state tiles owned by this wave: dk row blocks 2 wave, 2 wave + 1 (x DK/128) and both
-    // 16-column blocks of the dv tile.  S[rb][cb] holds rows 16 rb + 4 (lane/16) + r.
-    constexpr int RB = DK / 16 / 4;  // row blocks per wave (2 for DK = 128, 1 for 64)
-    f32x4 S[RB][2];
+    // S[i][jb] holds rows 16 (RB wave + i) + 4 (lane/16) + rr of columns 16 jb + lane%16
+    f32x4 S[CP::RB][CP::NCB];
 #pragma unroll
-    for (int i = 0; i < RB; ++i)
+    for (int i = 0; i < CP::RB; ++i)
 #pragma unroll
-        for (int cb = 0; cb < 2; ++cb) {
-            const int col = cb * 16 + (lane & 15);
+        for (int jb = 0; jb < CP::NCB; ++jb) S[i][jb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (a.h0_from_pool) {
 #pragma unroll
-            for (int rr = 0; rr < 4; ++rr) {
-                const int row = (wave * RB + i) * 16 + 4 * (lane >> 4) + rr;
-                S[i][cb][rr] = a.h0_from_pool ? Sg[row * DV + col] : 0.f;
-            }
-        }
-
-    CarryRegs<CP> regs;
-    if (c_begin < c_end) {
-        carry_fetch<CP>(regs, recs + ws.rec_bytes * (static_cast<size_t>(c_begin) * H + h), ws, tile,
-                        tid, DV);
-        carry_stage<CP>(regs, smem, tid);
+        for (int i = 0; i < CP::RB; ++i)
+#pragma unroll
+            for (int jb = 0; jb < CP::NCB; ++jb)
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr)
+                    S[i][jb][rr] = Sg[(16 * (wave * CP::RB + i) + 4 * (lane >> 4) + rr) * DV + 16 * jb + (lane & 15)];
     }
-    lds_barrier();
 
-    for (int c = c_begin; c < c_end; ++c) {
-        char* buf = smem + ((c - c_begin) & 1) * CP::BUF;
-        const elem* bW = reinterpret_cast<const elem*>(buf + CP::O_W);
-        const elem* bQ = reinterpret_cast<const elem*>(buf + CP::O_Q);
-        const elem* bKt = reinterpret_cast<const elem*>(buf + CP::O_KT);
-        const elem* bU = reinterpret_cast<const elem*>(buf + CP::O_U);
-        const elem* bO = reinterpret_cast<const elem*>(buf + CP::O_O);
-        const float* bGL = reinterpret_cast<const float*>(buf + CP::O_GL);
-        // this chunk's token range first: vmcnt retires in order, so a load issued after
-        // the prefetch below would make its first use wait for the whole prefetch
-        const int4 info = table[c];
-        const int t0 = info.y, L = info.z;
-        // next chunk's operands (the last iteration re-fetches its own chunk, unused)
-        const int cn = c + 1 < c_end ? c + 1 : c;
-        carry_fetch<CP>(regs, recs + ws.rec_bytes * (static_cast<size_t>(cn) * H + h), ws, tile, tid, DV);
-
-        // (1) S (fp32 registers) -> S^T operand in LDS
+    if (c_begin < c_end) {
+        const int last = c_end - 1;
+        auto rec_of = [&](int c) { return recs + ws.rec_bytes * (static_cast<size_t>(c) * H + h); };
+        const int orow = H * DV, ocol = h * DV + tile * BV;
+        CarryOps<DK, DV, TIn> F[NB];
 #pragma unroll
-        for (int i = 0; i < RB; ++i)
+        for (int k = 0; k < NB; ++k) carry_fetch(F[k], rec_of(min(c_begin + k, last)), ws, tile, wave, lane);
+        for (int c = c_begin; c < c_end; c += NB) {
 #pragma unroll
-            for (int cb = 0; cb < 2; ++cb) {
-                const int col = cb * 16 + (lane & 15);
-                const int row = (wave * RB + i) * 16 + 4 * (lane >> 4);
-#pragma unroll
-                for (int rr = 0; rr < 4; ++rr) sSt[col * CP::LDK + row + rr] = M::from_f32(S[i][cb][rr]);
-            }
-        lds_barrier();
-
-        // (2) U = Ut - W S and O = scale (Q' S + Ot): token rows 16 wave .. +15
-#pragma unroll
-        for (int cb = 0; cb < 2; ++cb) {
-            f32x4 u = {0.f, 0.f, 0.f, 0.f}, o = u;
-            u = mma_nt<TIn>(bW + wave * 16 * CP::LDK, CP::LDK, sSt + cb * 16 * CP::LDK, CP::LDK, 0, DK, u, lane);
-            o = mma_nt<TIn>(bQ + wave * 16 * CP::LDK, CP::LDK, sSt + cb * 16 * CP::LDK, CP::LDK, 0, DK, o, lane);
-            const int col = cb * 16 + (lane & 15);
-            const int trow = wave * 16 + 4 * (lane >> 4);
-            float uv[4];
-#pragma unroll
-            for (int rr = 0; rr < 4; ++rr) {
-                const int t = trow + rr;
-                uv[rr] = M::to_f32(bU[col * CP::LDT + t]) - u[rr];
-                const float ov = a.scale * (o[rr] + M::to_f32(bO[col * CP::LDT + t]));
-                if (t < L) {
-                    const int64_t oi = ((static_cast<int64_t>(t0) + t) * H + h) * DV + tile * BV + col;
-                    if constexpr (CP::E == 2)
-                        static_cast<uint16_t*>(a.o)[oi] = f32_to_bf16(ov);
-                    else
-                        static_cast<float*>(a.o)[oi] = ov;
+            for (int k = 0; k < NB; ++k) {
+                const int cc = c + k;
+                if (cc < c_end) {
+                    const int t0 = bos + kChunk * (cc - c_begin), L = min(kChunk, eos - t0);
+                    const __amdgpu_buffer_rsrc_t orsrc =
+                        buf_rsrc(static_cast<char*>(a.o) + static_cast<int64_t>(t0) * orow * E,
+                                 static_cast<int64_t>(L) * orow * E);
+                    carry_step<DK, DV, TIn>(F[k], S, sx, ux, orsrc, orow, ocol, a.scale, wave, lane);
                 }
-            }
-#pragma unroll
-            for (int rr = 0; rr < 4; ++rr) sUt[col * CP::LDT + trow + rr] = M::from_f32(uv[rr]);
-        }
-        lds_barrier();
-
-        // (3) S = exp(G_L) S + Kt U
-#pragma unroll
-        for (int i = 0; i < RB; ++i) {
-            const int rb = wave * RB + i;
-#pragma unroll
-            for (int cb = 0; cb < 2; ++cb) {
-                f32x4 acc;
-#pragma unroll
-                for (int rr = 0; rr < 4; ++rr) acc[rr] = S[i][cb][rr] * bGL[rb * 16 + 4 * (lane >> 4) + rr];
-                S[i][cb] = mma_nt<TIn>(bKt + rb * 16 * CP::LDT, CP::LDT, sUt + cb * 16 * CP::LDT, CP::LDT, 0,
-                                       kChunk, acc, lane);
+                carry_fetch(F[k], rec_of(min(cc + NB, last)), ws, tile, wave, lane);
             }
         }
-        carry_stage<CP>(regs, smem + ((c + 1 - c_begin) & 1) * CP::BUF, tid);
-        lds_barrier();
     }
 
     // final state back to the slot
 #pragma unroll
-    for (int i = 0; i < RB; ++i)
+    for (int i = 0; i < CP::RB; ++i)
 #pragma unroll
-        for (int cb = 0; cb < 2; ++cb) {
-            const int col = cb * 16 + (lane & 15);
+        for (int jb = 0; jb < CP::NCB; ++jb)
 #pragma unroll
-            for (int rr = 0; rr < 4; ++rr) {
-                const int row = (wave * RB + i) * 16 + 4 * (lane >> 4) + rr;
-                Sg[row * DV + col] = S[i][cb][rr];
-            }
-        }
+            for (int rr = 0; rr < 4; ++rr)
+                Sg[(16 * (wave * CP::RB + i) + 4 * (lane >> 4) + rr) * DV + 16 * jb + (lane & 15)] = S[i][jb][rr];
+}
+
+// Compute units of the current device (cached per device).
+int device_cu_count() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cached[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
 }
 
 template <int DK, int DV, class TIn>
 hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t stream) {
-    if constexpr (!IntraPlan<DK, DV, TIn>::fits || !CarryPlan<DK, DV, TIn>::fits) {
+    if constexpr (!IntraPlan<DK, DV, TIn>::fits) {
         return hipErrorInvalidConfiguration;
     } else {
-        constexpr int E = sizeof(typename Mma<TIn>::elem);
+        constexpr int E = Geo<TIn>::E;
         const WsLayout ws(a.num_seqs, a.total_tokens, a.H, DK, DV, E);
         int32_t* chunk_off = static_cast<int32_t*>(a.workspace);
         int4* table = reinterpret_cast<int4*>(static_cast<char*>(a.workspace) + ws.off_table);
-        hipLaunchKernelGGL(chunk_map_kernel, dim3(1), dim3(kThreads), 0, stream, a.cu_seqlens,
-                           a.num_seqs, chunk_off, table);
-        if (ws.max_chunks > 0)
-            hipLaunchKernelGGL((chunk_intra_kernel<DK, DV, TIn>),
-                               dim3(static_cast<unsigned>(ws.max_chunks), a.H), dim3(kThreads), 0,
-                               stream, a);
+        hipLaunchKernelGGL(chunk_map_kernel, dim3(1), dim3(kThreads), 0, stream, a.cu_seqlens, a.num_seqs, chunk_off,
+                           table);
+        const int64_t items = ws.max_chunks * a.H;
+        if (items > 0) {
+            const int cus = device_cu_count();
+            const int grid = static_cast<int>(items < cus ? items : cus);
+            hipLaunchKernelGGL((chunk_intra_kernel<DK, DV, TIn>), dim3(grid), dim3(kThreads), 0, stream, a);
+        }
         const int groups = a.num_seqs * a.H;
         const int grid = (groups + kNumXcd - 1) / kNumXcd * kNumXcd * (DV / kCarryBV);
-        hipLaunchKernelGGL((chunk_carry_kernel<DK, DV, TIn>), dim3(grid), dim3(kThreads), 0, stream, a);
+        hipLaunchKernelGGL((chunk_carry_kernel<DK, DV, TIn, kCarryNB>), dim3(grid), dim3(kThreads), 0, stream, a);
         return hipGetLastError();
     }
 }
@@ -748,10 +1018,10 @@ size_t prefill_workspace_bytes(int num_seqs, int64_t total_tokens, int H, int dk
 
 bool prefill_supported(int bf16, int dk, int dv) {
     if (bf16) return true;
-    if (dk == 64 && dv == 64) return IntraPlan<64, 64, F32>::fits && CarryPlan<64, 64, F32>::fits;
-    if (dk == 64 && dv == 128) return IntraPlan<64, 128, F32>::fits && CarryPlan<64, 128, F32>::fits;
-    if (dk == 128 && dv == 64) return IntraPlan<128, 64, F32>::fits && CarryPlan<128, 64, F32>::fits;
-    return IntraPlan<128, 128, F32>::fits && CarryPlan<128, 128, F32>::fits;
+    if (dk == 64 && dv == 64) return IntraPlan<64, 64, F32>::fits;
+    if (dk == 64 && dv == 128) return IntraPlan<64, 128, F32>::fits;
+    if (dk == 128 && dv == 64) return IntraPlan<128, 64, F32>::fits;
+    return IntraPlan<128, 128, F32>::fits;
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, int bf16, int dk, int dv, hipStream_t stream) {
