@@ -365,6 +365,9 @@ __device__ __forceinline__ void intra_compute(const IntraIn<DK, DV, TIn>& X, cha
     const int r = lane & 15, q = lane >> 4, t = 16 * wave + r;
 
     // ---- 1. norms, gate cumsum inside the wave, wave totals -------------------------
+    // The gates are scaled by log2(e) before the scan, so each exponential below is a
+    // single exp2.
+    constexpr float kLog2e = 1.4426950408889634f;
     float qf[NGK][GW], kf[NGK][GW], gf[NGK][GW];
 #pragma unroll
     for (int j = 0; j < NGK; ++j) {
@@ -373,7 +376,7 @@ __device__ __forceinline__ void intra_compute(const IntraIn<DK, DV, TIn>& X, cha
 #pragma unroll
         for (int m = 0; m < GW / 4; ++m)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) gf[j][4 * m + e] = X.g[j][m][e];
+            for (int e = 0; e < 4; ++e) gf[j][4 * m + e] = X.g[j][m][e] * kLog2e;
     }
     if (a.use_l2) {
         float sq = 0.f, sk = 0.f;
@@ -412,7 +415,25 @@ __device__ __forceinline__ void intra_compute(const IntraIn<DK, DV, TIn>& X, cha
     if (q == 0) sBeta[t] = X.beta;
     lds_barrier();
 
-    // ---- 2. G, exp factors, operands --------------------------------------------------
+    // ---- 2. G, exponentials, operands -------------------------------------------------
+    // G = in-wave scan + earlier waves' totals (t0 + t1 + ... in a fixed order; the
+    // wave-uniform 0/1 multipliers select the prefix without per-lane selects), G_L =
+    // all four totals.
+    const float m1 = wave > 0 ? 1.f : 0.f, m2 = wave > 1 ? 1.f : 0.f, m3 = wave > 2 ? 1.f : 0.f;
+    const bool odd = r & 1;
+    const int te = t & ~1;
+    // v_perm_b32 selectors for the adjacent-token pairs of the transposed copies: even
+    // lanes write (own, neighbour) low halves, odd lanes (neighbour, own) high halves
+    const uint32_t psel = odd ? 0x03020706u : 0x05040100u;
+    auto pair_store = [&](elem* dstT, u32x4 wv, int j) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t nbr = static_cast<uint32_t>(
+                __builtin_amdgcn_update_dpp(0, static_cast<int>(wv[i]), 0xB1, 0xf, 0xf, false));
+            const int c = GW * (4 * j + q) + 2 * i + (odd ? 1 : 0);
+            *reinterpret_cast<uint32_t*>(dstT + c * LDT + te) = __builtin_amdgcn_perm(nbr, wv[i], psel);
+        }
+    };
     u32x4 KG[NGK], QG[NGK];
     {
         float* gl_out = reinterpret_cast<float*>(rec + ws.o_gl);
@@ -422,26 +443,27 @@ __device__ __forceinline__ void intra_compute(const IntraIn<DK, DV, TIn>& X, cha
 #pragma unroll
             for (int m = 0; m < GW / 4; ++m) {
                 const int c = GW * (4 * j + q) + 4 * m;
-                f32x4 pre = {0.f, 0.f, 0.f, 0.f}, tot = pre;
-#pragma unroll
-                for (int w2 = 0; w2 < 4; ++w2) {
-                    const f32x4 x = *reinterpret_cast<const f32x4*>(sTot + w2 * DK + c);
-                    if (w2 < wave) pre += x;
-                    tot += x;
-                }
-                f32x4 egl;
+                const f32x4 t0 = *reinterpret_cast<const f32x4*>(sTot + c);
+                const f32x4 t1 = *reinterpret_cast<const f32x4*>(sTot + DK + c);
+                const f32x4 t2 = *reinterpret_cast<const f32x4*>(sTot + 2 * DK + c);
+                const f32x4 t3 = *reinterpret_cast<const f32x4*>(sTot + 3 * DK + c);
+                f32x4 tot;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int i = 4 * m + e;
-                    const float G = gf[j][i] + pre[e];
-                    const float eg = __expf(G), ei = __expf(-G);
-                    egl[e] = __expf(tot[e]);
+                    const float pre = fmaf(t2[e], m3, fmaf(t1[e], m2, t0[e] * m1));
+                    tot[e] = (t0[e] + t1[e]) + t2[e] + t3[e];
+                    const float G = gf[j][i] + pre;
+                    const float eg = __builtin_amdgcn_exp2f(G), ei = __builtin_amdgcn_exp2f(-G);
                     kg[i] = kf[j][i] * eg;
                     ki[i] = kf[j][i] * ei;
                     qg[i] = qf[j][i] * eg;
-                    kt[i] = kf[j][i] * __expf(tot[e] - G);
+                    kt[i] = kf[j][i] * __builtin_amdgcn_exp2f(tot[e] - G);
                 }
-                if (wave == 0 && r == 0) *reinterpret_cast<f32x4*>(gl_out + c) = egl;
+                if (wave == 0 && r == 0)
+                    *reinterpret_cast<f32x4*>(gl_out + c) =
+                        f32x4{__builtin_amdgcn_exp2f(tot[0]), __builtin_amdgcn_exp2f(tot[1]),
+                              __builtin_amdgcn_exp2f(tot[2]), __builtin_amdgcn_exp2f(tot[3])};
             }
             KG[j] = f32_to_gran(kg, tag);
             QG[j] = f32_to_gran(qg, tag);
@@ -449,22 +471,8 @@ __device__ __forceinline__ void intra_compute(const IntraIn<DK, DV, TIn>& X, cha
             *reinterpret_cast<u32x4*>(sQG + t * LDK + GW * (4 * j + q)) = QG[j];
             // transposed copies [channel][token]
             if constexpr (E == 2) {
-                // pair adjacent tokens: even lanes write channel e, odd lanes channel e + 1
-                float kgr[GW], ktr[GW];
-                gran_to_f32(KG[j], kgr, tag);
-                gran_to_f32(f32_to_gran(kt, tag), ktr, tag);
-                const bool odd = r & 1;
-                const int te = t & ~1;
-#pragma unroll
-                for (int e = 0; e < GW; e += 2) {
-                    const int c = GW * (4 * j + q) + e + (odd ? 1 : 0);
-                    const float s1 = swap_adjacent(odd ? kgr[e] : kgr[e + 1]);
-                    const float s2 = swap_adjacent(odd ? ktr[e] : ktr[e + 1]);
-                    const uint32_t w1 = odd ? pack_bf16x2(s1, kgr[e + 1]) : pack_bf16x2(kgr[e], s1);
-                    const uint32_t w2 = odd ? pack_bf16x2(s2, ktr[e + 1]) : pack_bf16x2(ktr[e], s2);
-                    *reinterpret_cast<uint32_t*>(sKGt + c * LDT + te) = w1;
-                    *reinterpret_cast<uint32_t*>(sKTt + c * LDT + te) = w2;
-                }
+                pair_store(sKGt, KG[j], j);
+                pair_store(sKTt, f32_to_gran(kt, tag), j);
             } else {
 #pragma unroll
                 for (int e = 0; e < GW; ++e) {
@@ -476,26 +484,15 @@ __device__ __forceinline__ void intra_compute(const IntraIn<DK, DV, TIn>& X, cha
         }
 #pragma unroll
         for (int j = 0; j < NGV; ++j) {
-            float vf[GW];
-            gran_to_f32(X.v[j], vf, tag);
             if constexpr (E == 2) {
-                const bool odd = r & 1;
-                const int te = t & ~1;
-#pragma unroll
-                for (int e = 0; e < GW; e += 2) {
-                    const int c = GW * (4 * j + q) + e + (odd ? 1 : 0);
-                    const float s1 = swap_adjacent(odd ? vf[e] : vf[e + 1]);
-                    *reinterpret_cast<uint32_t*>(sVt + c * LDT + te) =
-                        odd ? pack_bf16x2(s1, vf[e + 1]) : pack_bf16x2(vf[e], s1);
-                }
+                pair_store(sVt, X.v[j], j);
             } else {
 #pragma unroll
-                for (int e = 0; e < GW; ++e) sVt[(GW * (4 * j + q) + e) * LDT + t] = vf[e];
+                for (int e = 0; e < GW; ++e) sVt[(GW * (4 * j + q) + e) * LDT + t] = __uint_as_float(X.v[j][e]);
             }
         }
     }
     lds_barrier();
-
     // ---- 3. Kt record; A^T and P^T tiles (all four column blocks, straight-line) -----
     {
         constexpr int NKT = DK / 16 * RG::GT * 64;  // granules of Kt
@@ -724,7 +721,7 @@ __global__ __launch_bounds__(kThreads) void chunk_intra_kernel(PrefillArgs a) {
     using P = IntraPlan<DK, DV, TIn>;
     static_assert(P::fits, "LDS plan exceeds 160 KiB");
     __shared__ __attribute__((aligned(16))) char smem[P::BYTES];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int H = a.H;
     const WsLayout ws(a.num_seqs, a.total_tokens, H, DK, DV, P::E);
     const int32_t* chunk_off = static_cast<const int32_t*>(a.workspace);
@@ -740,15 +737,19 @@ __global__ __launch_bounds__(kThreads) void chunk_intra_kernel(PrefillArgs a) {
         const int4 info = table[item / H];
         intra_fetch(X, a, info.y, info.z, item % H, wave, lane);
     }
+    // the table entry of the item after next is read one iteration ahead of its use;
+    // fetches past the last item repeat a valid one and are never used
+    int nxt = item + stride < total ? item + stride : item;
+    int4 nxt_info = table[nxt / H];
     for (; item < total; item += stride) {
         const IntraIn<DK, DV, TIn> Y = X;
-        const int nxt = item + stride < total ? item + stride : item;  // the last fetch is a harmless repeat
-        {
-            const int4 info = table[nxt / H];
-            intra_fetch(X, a, info.y, info.z, nxt % H, wave, lane);
-        }
+        intra_fetch(X, a, nxt_info.y, nxt_info.z, nxt % H, wave, lane);
+        const int nn = nxt + stride < total ? nxt + stride : nxt;
+        const int4 nn_info = table[nn / H];
         char* rec = recs + ws.rec_bytes * static_cast<size_t>(item);
         intra_compute(Y, smem, a, rec, ws, wave, lane, tid);
+        nxt = nn;
+        nxt_info = nn_info;
     }
 }
 
@@ -862,12 +863,28 @@ __device__ __forceinline__ void carry_step(const CarryOps<DK, DV, TIn>& F, f32x4
             u = gmma(F.w[g], b, u, tag);
             o = gmma(F.q[g], b, o, tag);
         }
-        f32x4 uv;
+        f32x4 uv, ov;
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
             uv[rr] = uo_val(F.u, jb, rr, tag) - u[rr];
-            store_out(orsrc, (trow + rr) * orow + ocol + 16 * jb + r, scale * (o[rr] + uo_val(F.o, jb, rr, tag)),
-                      tag);
+            ov[rr] = scale * (o[rr] + uo_val(F.o, jb, rr, tag));
+        }
+        if constexpr (CP::E == 2) {
+            // lanes r, r ^ 1 hold adjacent columns: the even lane stores rows 0, 1 and the
+            // odd lane rows 2, 3 as column pairs (one dword each)
+            const bool odd = r & 1;
+            const uint32_t p01 = pack_bf16x2(ov[0], ov[1]), p23 = pack_bf16x2(ov[2], ov[3]);
+            const uint32_t own = odd ? p23 : p01;
+            const uint32_t nbr = static_cast<uint32_t>(
+                __builtin_amdgcn_update_dpp(0, static_cast<int>(odd ? p01 : p23), 0xB1, 0xf, 0xf, false));
+            const int row = trow + (odd ? 2 : 0), col = ocol + 16 * jb + (r & ~1);
+            const uint32_t d0 = __builtin_amdgcn_perm(nbr, own, odd ? 0x01000504u : 0x05040100u);
+            const uint32_t d1 = __builtin_amdgcn_perm(nbr, own, odd ? 0x03020706u : 0x07060302u);
+            __builtin_amdgcn_raw_buffer_store_b32(d0, orsrc, (row * orow + col) * 2, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b32(d1, orsrc, ((row + 1) * orow + col) * 2, 0, 0);
+        } else {
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) store_out(orsrc, (trow + rr) * orow + ocol + 16 * jb + r, ov[rr], tag);
         }
         lds_tile_to_gran(ux, ((wave / CP::CT) * CP::NCB + jb) * 64 + lane, wave % CP::CT, uv, tag);
     }
@@ -898,7 +915,7 @@ __global__ __launch_bounds__(kThreads) void chunk_carry_kernel(PrefillArgs a) {
     char* sx = smem + CP::O_SX;
     char* ux = smem + CP::O_UX;
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int H = a.H;
     // XCD-aware mapping: the NT dv tiles of one (sequence, head) share an XCD (and its L2)
     const int groups = a.num_seqs * H;
