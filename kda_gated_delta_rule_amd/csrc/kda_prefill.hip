@@ -175,28 +175,57 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, int
 // ---------------------------------------------------------------------------
 // Workspace layout (all offsets 256-byte aligned):
 //   chunk_off  int32 [num_seqs + 1]     first chunk of each sequence; [num_seqs] = count
+//   seg_off    int32 [num_seqs + 1]     first segment of each sequence; [num_seqs] = count
 //   table      int4  [max_chunks]       {sequence, first token, length, 0}
+//   segtab     int4  [max_segs]         {sequence, first chunk, chunks, 2 k + last}
 //   records    [max_chunks * H]         one per (chunk, head), granule order:
-//     W, Q'  [token block 4][dk granule GK][lane 64] x 16 B     rows t, k over dk
+//     W, QG  [token block 4][dk granule GK][lane 64] x 16 B     rows t, k over dk
 //     Kt     [dk block DK/16][token granule GT][lane 64] x 16 B rows c, k over tokens
-//     Ut, Ot [dv tile NT][token block 4][part 2][lane 64] x UB  accumulator layout
+//     Ut     [dv tile NT][token block 4][lane 64] x UB          accumulator layout
+//     P      [token block 4][token granule GT][lane 64] x 16 B  rows t, k over tokens
 //     exp(G_L) [DK] fp32
+//   segment blocks [max_segs * H], fp32 row-major:
+//     S_loc [DK][DV]   state after the segment from a zero state
+//     Phi   [DK][DK]   the segment's transition (S_end = Phi S_start + S_loc)
+//     S_start [DK][DV] state entering the segment
+// A segment is up to seg_chunks consecutive chunks of one sequence: 16, doubled
+// (up to 64) while the batch would give more than 1024 (segment, head) pairs, so
+// small batches still spread over every compute unit and long ones keep the
+// sequential scan short.
 // ---------------------------------------------------------------------------
+__host__ __device__ inline int seg_chunks_for(int64_t total_tokens, int H) {
+    int seg = 16;
+    while (seg < 64 && total_tokens / kChunk / seg * H > 1024) seg *= 2;
+    return seg;
+}
+
 struct WsLayout {
-    int64_t max_chunks;
-    size_t off_table, off_rec, rec_bytes, total;
-    size_t o_w, o_q, o_kt, o_uo, o_gl;
+    int64_t max_chunks, max_segs;
+    int seg_chunks;
+    size_t off_segoff, off_table, off_segtab, off_rec, rec_bytes, off_seg, seg_bytes, total;
+    size_t o_w, o_q, o_kt, o_u, o_p, o_gl;
+    size_t s_loc, s_phi, s_start;
     __host__ __device__ WsLayout(int num_seqs, int64_t total_tokens, int H, int dk, int dv, int e) {
         max_chunks = total_tokens / kChunk + num_seqs;
-        off_table = align_up(sizeof(int32_t) * (num_seqs + 1), 256);
-        off_rec = off_table + align_up(sizeof(int32_t) * 4 * max_chunks, 256);
+        seg_chunks = seg_chunks_for(total_tokens, H);
+        max_segs = max_chunks / seg_chunks + num_seqs;
+        off_segoff = align_up(sizeof(int32_t) * (num_seqs + 1), 256);
+        off_table = off_segoff + align_up(sizeof(int32_t) * (num_seqs + 1), 256);
+        off_segtab = off_table + align_up(sizeof(int32_t) * 4 * max_chunks, 256);
+        off_rec = off_segtab + align_up(sizeof(int32_t) * 4 * max_segs, 256);
         o_w = 0;
         o_q = o_w + static_cast<size_t>(kChunk) * dk * e;
         o_kt = o_q + static_cast<size_t>(kChunk) * dk * e;
-        o_uo = o_kt + static_cast<size_t>(dk) * kChunk * e;
-        o_gl = o_uo + 2ull * kChunk * dv * e;
+        o_u = o_kt + static_cast<size_t>(dk) * kChunk * e;
+        o_p = o_u + static_cast<size_t>(kChunk) * dv * e;
+        o_gl = o_p + static_cast<size_t>(kChunk) * kChunk * e;
         rec_bytes = align_up(o_gl + sizeof(float) * dk, 256);
-        total = off_rec + rec_bytes * static_cast<size_t>(max_chunks) * H;
+        off_seg = off_rec + rec_bytes * static_cast<size_t>(max_chunks) * H;
+        s_loc = 0;
+        s_phi = s_loc + sizeof(float) * dk * dv;
+        s_start = s_phi + sizeof(float) * dk * dk;
+        seg_bytes = align_up(s_start + sizeof(float) * dk * dv, 256);
+        total = off_seg + seg_bytes * static_cast<size_t>(max_segs) * H;
     }
 };
 
@@ -207,30 +236,24 @@ struct RecGeo {
     static constexpr int GK = DK / (16 * CT);      // granules along dk
     static constexpr int GT = kChunk / (16 * CT);  // granules along the chunk's tokens
     static constexpr int BV = kCarryBV, NT = DV / BV, NCB = BV / 16;
-    static constexpr int UB = NCB * 4 * E;         // bytes of one U/O part per lane
+    static constexpr int UB = NCB * 4 * E;         // bytes of one Ut tile per lane
     static_assert(DV % BV == 0 && DK % 64 == 0 && UB % 16 == 0, "record geometry");
 };
 
 // ---------------------------------------------------------------------------
-// 1. chunk map (single workgroup)
+// 1. chunk map (single workgroup): chunk and segment offsets per sequence and the
+//    chunk and segment tables.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kThreads) void chunk_map_kernel(const int32_t* __restrict__ cu,
-                                                             int num_seqs, int32_t* chunk_off,
-                                                             int4* table) {
-    __shared__ int32_t part[kThreads];
-    __shared__ int32_t carry;
+// Exclusive scan of f(i) over i < n in blocks of kThreads; out[n] = total.
+template <class F>
+__device__ void block_exclusive_scan(int n, F f, int32_t* out, int32_t* part, int32_t* carry) {
     const int tid = threadIdx.x;
-    if (tid == 0) carry = 0;
+    if (tid == 0) *carry = 0;
     __syncthreads();
-    // exclusive scan of ceil(len / 64) over sequences, in blocks of kThreads
-    for (int base = 0; base < num_seqs; base += kThreads) {
+    for (int base = 0; base < n; base += kThreads) {
         const int i = base + tid;
-        int nch = 0;
-        if (i < num_seqs) {
-            const int len = cu[i + 1] - cu[i];
-            nch = len > 0 ? (len + kChunk - 1) / kChunk : 0;
-        }
-        part[tid] = nch;
+        const int x0 = i < n ? f(i) : 0;
+        part[tid] = x0;
         __syncthreads();
         for (int off = 1; off < kThreads; off <<= 1) {  // Hillis-Steele inclusive scan
             const int x = tid >= off ? part[tid - off] : 0;
@@ -238,22 +261,39 @@ __global__ __launch_bounds__(kThreads) void chunk_map_kernel(const int32_t* __re
             part[tid] += x;
             __syncthreads();
         }
-        if (i < num_seqs) chunk_off[i] = carry + part[tid] - nch;
+        if (i < n) out[i] = *carry + part[tid] - x0;
         __syncthreads();
-        if (tid == kThreads - 1) carry += part[kThreads - 1];
+        if (tid == kThreads - 1) *carry += part[kThreads - 1];
         __syncthreads();
     }
-    if (tid == 0) chunk_off[num_seqs] = carry;
+    if (tid == 0) out[n] = *carry;
     __syncthreads();
-    // chunk table
+}
+
+__global__ __launch_bounds__(kThreads) void chunk_map_kernel(const int32_t* __restrict__ cu, int num_seqs,
+                                                             int seg_chunks, int32_t* chunk_off, int32_t* seg_off,
+                                                             int4* table, int4* segtab) {
+    __shared__ int32_t part[kThreads];
+    __shared__ int32_t carry;
+    auto nchunks = [&](int i) {
+        const int len = cu[i + 1] - cu[i];
+        return len > 0 ? (len + kChunk - 1) / kChunk : 0;
+    };
+    block_exclusive_scan(num_seqs, nchunks, chunk_off, part, &carry);
+    block_exclusive_scan(num_seqs, [&](int i) { return (nchunks(i) + seg_chunks - 1) / seg_chunks; }, seg_off, part,
+                         &carry);
+    const int tid = threadIdx.x;
     for (int i = 0; i < num_seqs; ++i) {
         const int bos = cu[i], eos = cu[i + 1];
-        const int first = chunk_off[i];
-        const int nch = eos > bos ? (eos - bos + kChunk - 1) / kChunk : 0;
+        const int first = chunk_off[i], nch = chunk_off[i + 1] - first;
         for (int c = tid; c < nch; c += kThreads) {
             const int t0 = bos + c * kChunk;
             table[first + c] = make_int4(i, t0, min(kChunk, eos - t0), 0);
         }
+        const int s0 = seg_off[i], ns = seg_off[i + 1] - s0;
+        for (int k = tid; k < ns; k += kThreads)
+            segtab[s0 + k] = make_int4(i, first + k * seg_chunks, min(seg_chunks, nch - k * seg_chunks),
+                                       2 * k + (k == ns - 1 ? 1 : 0));
     }
 }
 
@@ -264,11 +304,10 @@ __global__ __launch_bounds__(kThreads) void chunk_map_kernel(const int32_t* __re
 // holds token 16w + r and, of every row vector, the granules j of channels
 // GW (4j + q) .. + GW - 1.  LDS regions (reused by phase):
 //   R1  KI [64][LDK]            | T fp32 [64][LDA]
-//   R2  KG^T [DK][LDT]          | W^T [DK][LDT]
-//   R3  V^T [DV][LDT]           | Ut^T [DV][LDT]
+//   R2  KG^T [DK][LDT]
+//   R3  V^T [DV][LDT]
 //   R4  Kt^T [DK][LDT]          | A fp32 [64][LDA]
 //   RT  T' = T diag(beta) [64][LDT]
-//   RP  P [64][LDT]
 //   RQ  QG [64][LDK]
 //   RM  beta [64], wave gate totals [4][DK]
 // ---------------------------------------------------------------------------
@@ -287,11 +326,10 @@ struct IntraPlan {
     static constexpr size_t R3 = align_up(1ull * DV * LDT * E, 16);
     static constexpr size_t R4 = align_up(cmax(1ull * DK * LDT * E, 64ull * LDA * 4), 16);
     static constexpr size_t RT = align_up(64ull * LDT * E, 16);
-    static constexpr size_t RP = RT;
     static constexpr size_t RQ = align_up(64ull * LDK * E, 16);
     static constexpr size_t RM = align_up(4ull * (64 + 4 * DK), 16);
     static constexpr size_t O1 = 0, O2 = O1 + R1, O3 = O2 + R2, O4 = O3 + R3, OT = O4 + R4;
-    static constexpr size_t OP = OT + RT, OQ = OP + RP, OM = OQ + RQ;
+    static constexpr size_t OQ = OT + RT, OM = OQ + RQ;
     static constexpr size_t BYTES = OM + RM;
     static constexpr bool fits = BYTES <= 160 * 1024;
 };
@@ -351,13 +389,10 @@ __device__ __forceinline__ void intra_compute(const IntraIn<DK, DV, TIn>& X, cha
     elem* sKI = reinterpret_cast<elem*>(smem + P::O1);
     float* sT = reinterpret_cast<float*>(smem + P::O1);
     elem* sKGt = reinterpret_cast<elem*>(smem + P::O2);
-    elem* sWt = sKGt;
     elem* sVt = reinterpret_cast<elem*>(smem + P::O3);
-    elem* sUt = sVt;
     elem* sKTt = reinterpret_cast<elem*>(smem + P::O4);
     float* sA = reinterpret_cast<float*>(smem + P::O4);
     elem* sTp = reinterpret_cast<elem*>(smem + P::OT);
-    elem* sP = reinterpret_cast<elem*>(smem + P::OP);
     elem* sQG = reinterpret_cast<elem*>(smem + P::OQ);
     float* sBeta = reinterpret_cast<float*>(smem + P::OM);
     float* sTot = sBeta + 64;
@@ -512,7 +547,7 @@ __device__ __forceinline__ void intra_compute(const IntraIn<DK, DV, TIn>& X, cha
             *reinterpret_cast<u32x4*>(rec + ws.o_kt + static_cast<size_t>(gi) * 16) = val;
         }
     }
-    f32x4 Areg[4];
+    f32x4 Areg[4], Preg[4];
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
         f32x4 accA = {0.f, 0.f, 0.f, 0.f}, accP = accA;
@@ -530,7 +565,25 @@ __device__ __forceinline__ void intra_compute(const IntraIn<DK, DV, TIn>& X, cha
             Areg[jj][rr] = s < t ? X.beta * accA[rr] : 0.f;
             p4[rr] = s <= t ? accP[rr] : 0.f;
         }
-        lds_store4(sP + t * LDT + 16 * jj + 4 * q, p4[0], p4[1], p4[2], p4[3]);
+        Preg[jj] = f32x4{p4[0], p4[1], p4[2], p4[3]};
+    }
+    // P granules (rows t of this token block, k over tokens) and QG granules (rows t, k
+    // over dk, the order of the W granules) to the record
+#pragma unroll
+    for (int g = 0; g < RG::GT; ++g)
+        *reinterpret_cast<u32x4*>(rec + ws.o_p + ((static_cast<size_t>(wave) * RG::GT + g) * 64 + lane) * 16) =
+            tiles_to_gran(Preg[RG::CT * g], Preg[RG::CT * g + RG::CT - 1], tag);
+#pragma unroll
+    for (int g = 0; g < RG::GK; ++g) {
+        u32x4 val;
+        if constexpr (E == 2) {
+            const u32x2 lo = *reinterpret_cast<const u32x2*>(sQG + t * LDK + 32 * g + 4 * q);
+            const u32x2 hi = *reinterpret_cast<const u32x2*>(sQG + t * LDK + 32 * g + 16 + 4 * q);
+            val = u32x4{lo[0], lo[1], hi[0], hi[1]};
+        } else {
+            val = *reinterpret_cast<const u32x4*>(sQG + t * LDK + 16 * g + 4 * q);
+        }
+        *reinterpret_cast<u32x4*>(rec + ws.o_q + ((static_cast<size_t>(wave) * RG::GK + g) * 64 + lane) * 16) = val;
     }
     lds_barrier();
 
@@ -598,117 +651,40 @@ __device__ __forceinline__ void intra_compute(const IntraIn<DK, DV, TIn>& X, cha
         lds_barrier();
     }
 
-    // ---- 6. W = T' KG, Ut = T' V (tiles rows t) and W^T (record) ------------------------
+    // ---- 6. W^T = KG^T T'^T and Ut = T' V, straight to the record ---------------------
     constexpr int NCK = DK / 16, NCV = DV / 16;
-    uint32_t wpk[NCK][E], upk[NCV][E];  // packed 4-element columns for W^T / Ut^T in LDS
     {
         const elem* Tr = sTp + (16 * wave + r) * LDT + (KS / 4) * q;
         f32x4 wt[NCK];
 #pragma unroll
         for (int cb = 0; cb < NCK; ++cb) {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acc2 = acc;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
             const elem* Kr = sKGt + (16 * cb + r) * LDT + (KS / 4) * q;
 #pragma unroll
-            for (int ks = 0; ks < KST; ++ks) {
-                acc = lmma(Tr + KS * ks, Kr + KS * ks, acc);   // W tile (t, c)
-                acc2 = lmma(Kr + KS * ks, Tr + KS * ks, acc2);  // W^T tile (c, t)
-            }
-            wt[cb] = acc2;
-            if constexpr (E == 2) {
-                wpk[cb][0] = pack_bf16x2(acc[0], acc[1]);
-                wpk[cb][1] = pack_bf16x2(acc[2], acc[3]);
-            } else {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) wpk[cb][e] = __float_as_uint(acc[e]);
-            }
+            for (int ks = 0; ks < KST; ++ks) acc = lmma(Kr + KS * ks, Tr + KS * ks, acc);  // tile (c, t)
+            wt[cb] = acc;
         }
 #pragma unroll
         for (int g = 0; g < RG::GK; ++g)
             *reinterpret_cast<u32x4*>(rec + ws.o_w + ((static_cast<size_t>(wave) * RG::GK + g) * 64 + lane) * 16) =
                 tiles_to_gran(wt[RG::CT * g], wt[RG::CT * g + RG::CT - 1], tag);
+        f32x4 ut[NCV];
 #pragma unroll
         for (int jb = 0; jb < NCV; ++jb) {
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
             const elem* Vr = sVt + (16 * jb + r) * LDT + (KS / 4) * q;
 #pragma unroll
-            for (int ks = 0; ks < KST; ++ks) acc = lmma(Tr + KS * ks, Vr + KS * ks, acc);
-            if constexpr (E == 2) {
-                upk[jb][0] = pack_bf16x2(acc[0], acc[1]);
-                upk[jb][1] = pack_bf16x2(acc[2], acc[3]);
-            } else {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) upk[jb][e] = __float_as_uint(acc[e]);
-            }
+            for (int ks = 0; ks < KST; ++ks) acc = lmma(Tr + KS * ks, Vr + KS * ks, acc);  // tile (t, j)
+            ut[jb] = acc;
         }
-        // Ut record: per dv tile, the NCB column blocks' 4 values each
+        // per dv tile, its NCB column blocks' 4 values each
 #pragma unroll
         for (int tile = 0; tile < RG::NT; ++tile) {
-            char* dst = rec + ws.o_uo + ((static_cast<size_t>(tile * 4 + wave) * 2 + 0) * 64 + lane) * RG::UB;
-#pragma unroll
-            for (int n = 0; n < RG::UB / 16; ++n) {
-                u32x4 val;
-                if constexpr (E == 2)
-                    val = u32x4{upk[RG::NCB * tile + 2 * n][0], upk[RG::NCB * tile + 2 * n][1],
-                                upk[RG::NCB * tile + 2 * n + 1][0], upk[RG::NCB * tile + 2 * n + 1][1]};
-                else
-                    val = u32x4{upk[RG::NCB * tile + n][0], upk[RG::NCB * tile + n][1], upk[RG::NCB * tile + n][2],
-                                upk[RG::NCB * tile + n][3]};
-                *reinterpret_cast<u32x4*>(dst + 16 * n) = val;
-            }
-        }
-    }
-    lds_barrier();  // every wave is done reading KG^T and V^T
-#pragma unroll
-    for (int cb = 0; cb < NCK; ++cb) {
-        elem* d = sWt + (16 * cb + r) * LDT + 16 * wave + 4 * q;
-        if constexpr (E == 2)
-            *reinterpret_cast<u32x2*>(d) = u32x2{wpk[cb][0], wpk[cb][1]};
-        else
-            *reinterpret_cast<u32x4*>(d) = u32x4{wpk[cb][0], wpk[cb][1], wpk[cb][2], wpk[cb][3]};
-    }
-#pragma unroll
-    for (int jb = 0; jb < NCV; ++jb) {
-        elem* d = sUt + (16 * jb + r) * LDT + 16 * wave + 4 * q;
-        if constexpr (E == 2)
-            *reinterpret_cast<u32x2*>(d) = u32x2{upk[jb][0], upk[jb][1]};
-        else
-            *reinterpret_cast<u32x4*>(d) = u32x4{upk[jb][0], upk[jb][1], upk[jb][2], upk[jb][3]};
-    }
-    lds_barrier();
-
-    // ---- 7. Q'^T = QG^T - W^T P^T and Ot = P Ut (records) ------------------------------
-    {
-        const elem* Pr = sP + (16 * wave + r) * LDT + (KS / 4) * q;
-        f32x4 qt[NCK];
-#pragma unroll
-        for (int cb = 0; cb < NCK; ++cb) {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            const elem* Wr = sWt + (16 * cb + r) * LDT + (KS / 4) * q;
-#pragma unroll
-            for (int ks = 0; ks < KST; ++ks) acc = lmma(Wr + KS * ks, Pr + KS * ks, acc);
-            // lane holds (c = 16 cb + 4q + rr, t): Q'_tc = QG_tc - (P W)_tc
-            qt[cb] = lds_load4(sQG + t * LDK + 16 * cb + 4 * q) - acc;
-        }
-#pragma unroll
-        for (int g = 0; g < RG::GK; ++g)
-            *reinterpret_cast<u32x4*>(rec + ws.o_q + ((static_cast<size_t>(wave) * RG::GK + g) * 64 + lane) * 16) =
-                tiles_to_gran(qt[RG::CT * g], qt[RG::CT * g + RG::CT - 1], tag);
-        f32x4 ot[NCV];
-#pragma unroll
-        for (int jb = 0; jb < NCV; ++jb) {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            const elem* Ur = sUt + (16 * jb + r) * LDT + (KS / 4) * q;
-#pragma unroll
-            for (int ks = 0; ks < KST; ++ks) acc = lmma(Pr + KS * ks, Ur + KS * ks, acc);
-            ot[jb] = acc;
-        }
-#pragma unroll
-        for (int tile = 0; tile < RG::NT; ++tile) {
-            char* dst = rec + ws.o_uo + ((static_cast<size_t>(tile * 4 + wave) * 2 + 1) * 64 + lane) * RG::UB;
+            char* dst = rec + ws.o_u + (static_cast<size_t>(tile * 4 + wave) * 64 + lane) * RG::UB;
 #pragma unroll
             for (int n = 0; n < RG::UB / 16; ++n) {
                 const int jb = RG::NCB * tile + (E == 2 ? 2 * n : n);
-                *reinterpret_cast<u32x4*>(dst + 16 * n) = tiles_to_gran(ot[jb], ot[E == 2 ? jb + 1 : jb], tag);
+                *reinterpret_cast<u32x4*>(dst + 16 * n) = tiles_to_gran(ut[jb], ut[E == 2 ? jb + 1 : jb], tag);
             }
         }
     }
@@ -754,70 +730,89 @@ __global__ __launch_bounds__(kThreads) void chunk_intra_kernel(PrefillArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// 3. chunk_carry: one workgroup (4 waves) per (sequence, head, BV-column dv tile),
-//    sequential over the sequence's chunks.  Wave w owns token rows 16w .. 16w+15 of
-//    U and O and key rows 16 RB w .. 16 RB (w+1) - 1 of S.  Its granules of W, Q',
-//    Kt, Ut, Ot and exp(G_L) go from the workspace into registers NB chunks ahead of
-//    their use; every fetch is issued unconditionally (clamped to the last chunk) and
-//    the ragged output rows are dropped by the buffer range check, so the loop has
-//    no data-dependent memory operations and the loads stay in flight across steps.
-//    S and U cross between waves through LDS as whole granules.
+// 3. Segment carries.  The chunk recurrence S_{c+1} = M_c S_c + B_c (M_c =
+//    diag(exp(G_L)) - Kt W, B_c = Kt Ut) is affine in S, so a segment of chunks maps
+//    its entering state to S_end = Phi S_start + S_loc.  Three launches:
+//      seg_carry<LOCAL>  per (segment, head), every segment but a sequence's last:
+//                        runs the chunk steps on [S | Phi] from [0 | I] and stores
+//                        S_loc and Phi;
+//      seg_scan          per (sequence, head, 16-column tile): S_start of segment 0
+//                        is the initial state, S_start(k+1) = Phi_k S_start(k) +
+//                        S_loc(k) in fp32;
+//      seg_carry<OUT>    per (segment, head): runs the chunk steps from S_start,
+//                        writes O, and the sequence's last segment writes the
+//                        final state to its slot.
+//    A seg_carry workgroup has 8 waves and owns all state columns: wave w computes
+//    token block w & 3 of U (w < 4) or of O [OUT] / of the Phi columns' U [LOCAL]
+//    (w >= 4), and the state rows of dk block w % (DK/16) for its column blocks.  Its
+//    record granules go from the workspace into registers NB chunks ahead of their
+//    use (issued unconditionally, clamped to the segment's last chunk); ragged output
+//    rows are dropped by the buffer range check.  S and U cross between waves
+//    through LDS as whole granules.
 // ---------------------------------------------------------------------------
-template <int DK, int DV, class TIn>
-struct CarryPlan {
+constexpr int kSegThreads = 512;
+constexpr int kLocal = 0, kOut = 1;
+
+template <int DK, int DV, class TIn, int MODE>
+struct SegPlan {
     using RG = RecGeo<DK, DV, TIn>;
-    static constexpr int E = RG::E, CT = RG::CT, GK = RG::GK, GT = RG::GT;
-    static constexpr int BV = RG::BV, NCB = RG::NCB, NT = RG::NT;
-    static constexpr int RB = DK / 64;  // 16-row blocks of S per wave
+    static constexpr int E = RG::E, CT = RG::CT, GK = RG::GK, GT = RG::GT, NT = RG::NT, TB = RG::NCB;
     static constexpr int NUB = RG::UB / 16;
-    static constexpr size_t O_SX = 0, O_UX = 1ull * GK * NCB * 64 * 16;
-    static constexpr size_t BYTES = O_UX + 1ull * GT * NCB * 64 * 16;
+    static constexpr int VB = DV / 16, KB = DK / 16;
+    static constexpr int NCB = MODE == kOut ? VB : VB + KB;  // 16-column blocks of the state
+    static constexpr int WPC = 8 / KB;                       // waves per dk block (1 or 2)
+    static constexpr int SJB = NCB / WPC;                    // state column blocks per wave
+    static constexpr size_t O_SX = 0, O_UX = 16ull * GK * NCB * 64;
+    static constexpr size_t BYTES = O_UX + 16ull * GT * NCB * 64;
+    static_assert(8 % KB == 0 && NCB % WPC == 0, "segment plan");
 };
 
-template <int DK, int DV, class TIn>
-struct CarryOps {
-    using CP = CarryPlan<DK, DV, TIn>;
-    u32x4 w[CP::GK], q[CP::GK], kt[CP::RB][CP::GT], u[CP::NUB], o[CP::NUB];
-    f32x4 gl[CP::RB];
+// One chunk's operands for one wave.
+template <class SP>
+struct SegOps {
+    u32x4 a[SP::GK];             // W (U task) or QG (O task) granules of the token block
+    u32x4 uo[SP::NT][SP::NUB];   // Ut of the token block, every dv tile (U task)
+    u32x4 p[SP::GT];             // P granules of the token block (O task)
+    u32x4 kt[SP::GT];            // Kt granules of the wave's dk block
+    f32x4 gl;                    // exp(G_L) of the wave's rows
 };
 
-template <int DK, int DV, class TIn>
-__device__ __forceinline__ void carry_fetch(CarryOps<DK, DV, TIn>& F, const char* rec, const WsLayout& ws,
-                                            int tile, int wave, int lane) {
-    using CP = CarryPlan<DK, DV, TIn>;
+template <class SP>
+__device__ __forceinline__ void seg_fetch(SegOps<SP>& F, const char* rec, const WsLayout& ws, int tb, int task,
+                                          int cb, int lane) {
+    // task (wave-uniform): 0 = U (W, Ut), 1 = O (QG, P), 2 = none
+    if (task < 2) {
+        const char* ab = rec + (task ? ws.o_q : ws.o_w);
 #pragma unroll
-    for (int g = 0; g < CP::GK; ++g) {
-        const size_t off = ((static_cast<size_t>(wave) * CP::GK + g) * 64 + lane) * 16;
-        F.w[g] = *reinterpret_cast<const u32x4*>(rec + ws.o_w + off);
-        F.q[g] = *reinterpret_cast<const u32x4*>(rec + ws.o_q + off);
+        for (int g = 0; g < SP::GK; ++g)
+            F.a[g] = *reinterpret_cast<const u32x4*>(ab + ((static_cast<size_t>(tb) * SP::GK + g) * 64 + lane) * 16);
+    }
+    if (task == 0) {
+#pragma unroll
+        for (int t = 0; t < SP::NT; ++t)
+#pragma unroll
+            for (int n = 0; n < SP::NUB; ++n)
+                F.uo[t][n] = *reinterpret_cast<const u32x4*>(
+                    rec + ws.o_u + (static_cast<size_t>(t * 4 + tb) * 64 + lane) * (SP::NUB * 16) + 16 * n);
+    } else if (task == 1) {
+#pragma unroll
+        for (int g = 0; g < SP::GT; ++g)
+            F.p[g] = *reinterpret_cast<const u32x4*>(rec + ws.o_p + ((static_cast<size_t>(tb) * SP::GT + g) * 64 + lane) * 16);
     }
 #pragma unroll
-    for (int i = 0; i < CP::RB; ++i)
-#pragma unroll
-        for (int g = 0; g < CP::GT; ++g)
-            F.kt[i][g] = *reinterpret_cast<const u32x4*>(
-                rec + ws.o_kt + ((static_cast<size_t>(CP::RB * wave + i) * CP::GT + g) * 64 + lane) * 16);
-    const char* uo = rec + ws.o_uo + (static_cast<size_t>(tile * 4 + wave) * 2 * 64 + lane) * (CP::NUB * 16);
-#pragma unroll
-    for (int n = 0; n < CP::NUB; ++n) {
-        F.u[n] = *reinterpret_cast<const u32x4*>(uo + 16 * n);
-        F.o[n] = *reinterpret_cast<const u32x4*>(uo + 64 * CP::NUB * 16 + 16 * n);
-    }
-#pragma unroll
-    for (int i = 0; i < CP::RB; ++i)
-        F.gl[i] = *reinterpret_cast<const f32x4*>(rec + ws.o_gl + (16 * (CP::RB * wave + i) + 4 * (lane >> 4)) * 4);
+    for (int g = 0; g < SP::GT; ++g)
+        F.kt[g] = *reinterpret_cast<const u32x4*>(rec + ws.o_kt + ((static_cast<size_t>(cb) * SP::GT + g) * 64 + lane) * 16);
+    F.gl = *reinterpret_cast<const f32x4*>(rec + ws.o_gl + (16 * cb + 4 * (lane >> 4)) * 4);
 }
 
-// Value (column block cb, row rr) of a U/O part held as granules.
+// Value (column block jb, row rr) of a U/O part held as granules, one tile of
+// kCarryBV columns per granule set.
 __device__ __forceinline__ float uo_val(const u32x4* p, int cb, int rr, BF16) {
     const uint32_t w = p[(cb * 4 + rr) >> 3][((cb * 4 + rr) >> 1) & 3];
     return __uint_as_float((rr & 1) ? (w & 0xffff0000u) : (w << 16));
 }
 __device__ __forceinline__ float uo_val(const u32x4* p, int cb, int rr, F32) { return __uint_as_float(p[cb][rr]); }
 
-__device__ __forceinline__ void store_out(__amdgpu_buffer_rsrc_t r, int off_elems, float x, BF16) {
-    __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(x), r, off_elems * 2, 0, 0);
-}
 __device__ __forceinline__ void store_out(__amdgpu_buffer_rsrc_t r, int off_elems, float x, F32) {
     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), r, off_elems * 4, 0, 0);
 }
@@ -832,153 +827,261 @@ __device__ __forceinline__ void lds_tile_to_gran(char* base, int gran_idx, int, 
     *reinterpret_cast<f32x4*>(base + gran_idx * 16) = v;
 }
 
-// One chunk: U = Ut - W S, O = scale (Q' S + Ot) (rows >= L dropped by the buffer range),
-// S = diag(exp(G_L)) S + Kt U.
-template <int DK, int DV, class TIn>
-__device__ __forceinline__ void carry_step(const CarryOps<DK, DV, TIn>& F, f32x4 (&S)[DK / 64][kCarryBV / 16],
-                                           char* sx, char* ux, __amdgpu_buffer_rsrc_t orsrc, int orow, int ocol,
-                                           float scale, int wave, int lane) {
-    using CP = CarryPlan<DK, DV, TIn>;
+// O rows 4 (lane/16) + rr of column 16 jb + lane%16 (bf16: lanes r, r ^ 1 store column
+// pairs, the even lane rows 0, 1 and the odd lane rows 2, 3, one dword each).
+__device__ __forceinline__ void store_o4(__amdgpu_buffer_rsrc_t orsrc, int trow, int orow, int col, f32x4 ov, int r,
+                                         BF16) {
+    const bool odd = r & 1;
+    const uint32_t p01 = pack_bf16x2(ov[0], ov[1]), p23 = pack_bf16x2(ov[2], ov[3]);
+    const uint32_t own = odd ? p23 : p01;
+    const uint32_t nbr = static_cast<uint32_t>(
+        __builtin_amdgcn_update_dpp(0, static_cast<int>(odd ? p01 : p23), 0xB1, 0xf, 0xf, false));
+    const int row = trow + (odd ? 2 : 0), c = col - (r & 1);
+    const uint32_t d0 = __builtin_amdgcn_perm(nbr, own, odd ? 0x01000504u : 0x05040100u);
+    const uint32_t d1 = __builtin_amdgcn_perm(nbr, own, odd ? 0x03020706u : 0x07060302u);
+    __builtin_amdgcn_raw_buffer_store_b32(d0, orsrc, (row * orow + c) * 2, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b32(d1, orsrc, ((row + 1) * orow + c) * 2, 0, 0);
+}
+__device__ __forceinline__ void store_o4(__amdgpu_buffer_rsrc_t orsrc, int trow, int orow, int col, f32x4 ov, int,
+                                         F32) {
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) store_out(orsrc, (trow + rr) * orow + col, ov[rr], F32{});
+}
+
+// One chunk on the segment state.
+template <int DK, int DV, class TIn, int MODE>
+__device__ __forceinline__ void seg_step(const SegOps<SegPlan<DK, DV, TIn, MODE>>& F,
+                                         f32x4 (&S)[SegPlan<DK, DV, TIn, MODE>::SJB], char* sx, char* ux,
+                                         __amdgpu_buffer_rsrc_t orsrc, int orow, int ocol, float scale, int tb,
+                                         int part, int cb, int jb0, int lane) {
+    using SP = SegPlan<DK, DV, TIn, MODE>;
     constexpr TIn tag{};
     const int r = lane & 15, q4 = 4 * (lane >> 4);
 
-    // (1) this wave's S tiles -> S granules (k over dk) in LDS
+    // (1) this wave's state tiles -> S granules (k over dk) in LDS
 #pragma unroll
-    for (int i = 0; i < CP::RB; ++i) {
-        const int cb = CP::RB * wave + i;
+    for (int j = 0; j < SP::SJB; ++j)
+        lds_tile_to_gran(sx, ((cb / SP::CT) * SP::NCB + jb0 + j) * 64 + lane, cb % SP::CT, S[j], tag);
+    lds_barrier();
+
+    // (2) the token block's U (part 0), O [OUT] or Phi-column U [LOCAL] (part 1)
+    auto prod = [&](int jb) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int jb = 0; jb < CP::NCB; ++jb)
-            lds_tile_to_gran(sx, ((cb / CP::CT) * CP::NCB + jb) * 64 + lane, cb % CP::CT, S[i][jb], tag);
+        for (int g = 0; g < SP::GK; ++g)
+            acc = gmma(F.a[g], *reinterpret_cast<const u32x4*>(sx + ((g * SP::NCB + jb) * 64 + lane) * 16), acc, tag);
+        return acc;
+    };
+    const int ug = ((tb / SP::CT) * SP::NCB) * 64 + lane, uh = tb % SP::CT;
+    if (part == 0) {
+#pragma unroll
+        for (int jb = 0; jb < SP::VB; ++jb) {
+            const f32x4 acc = prod(jb);
+            f32x4 uv;
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) uv[rr] = uo_val(F.uo[jb / SP::TB], jb % SP::TB, rr, tag) - acc[rr];
+            lds_tile_to_gran(ux, ug + jb * 64, uh, uv, tag);
+        }
+        if constexpr (MODE == kLocal) {
+            // the Phi columns' U (no Ut term) by the same wave, so W is loaded once
+#pragma unroll
+            for (int jb = SP::VB; jb < SP::NCB; ++jb) lds_tile_to_gran(ux, ug + jb * 64, uh, -prod(jb), tag);
+        }
+    }
+    // O task, first half: QG S (the P U half needs this chunk's U)
+    f32x4 oacc[MODE == kOut ? SP::VB : 1];
+    if constexpr (MODE == kOut) {
+        if (part == 1) {
+#pragma unroll
+            for (int jb = 0; jb < SP::VB; ++jb) oacc[jb] = prod(jb);
+        }
     }
     lds_barrier();
 
-    // (2) U and O for token rows 16 wave .. +15
-    const int trow = 16 * wave + q4;
+    // (3) S = exp(G_L) S + Kt U; O = scale (QG S + P U)
 #pragma unroll
-    for (int jb = 0; jb < CP::NCB; ++jb) {
-        f32x4 u = {0.f, 0.f, 0.f, 0.f}, o = u;
+    for (int j = 0; j < SP::SJB; ++j) {
+        f32x4 acc = S[j] * F.gl;
 #pragma unroll
-        for (int g = 0; g < CP::GK; ++g) {
-            const u32x4 b = *reinterpret_cast<const u32x4*>(sx + ((g * CP::NCB + jb) * 64 + lane) * 16);
-            u = gmma(F.w[g], b, u, tag);
-            o = gmma(F.q[g], b, o, tag);
-        }
-        f32x4 uv, ov;
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-            uv[rr] = uo_val(F.u, jb, rr, tag) - u[rr];
-            ov[rr] = scale * (o[rr] + uo_val(F.o, jb, rr, tag));
-        }
-        if constexpr (CP::E == 2) {
-            // lanes r, r ^ 1 hold adjacent columns: the even lane stores rows 0, 1 and the
-            // odd lane rows 2, 3 as column pairs (one dword each)
-            const bool odd = r & 1;
-            const uint32_t p01 = pack_bf16x2(ov[0], ov[1]), p23 = pack_bf16x2(ov[2], ov[3]);
-            const uint32_t own = odd ? p23 : p01;
-            const uint32_t nbr = static_cast<uint32_t>(
-                __builtin_amdgcn_update_dpp(0, static_cast<int>(odd ? p01 : p23), 0xB1, 0xf, 0xf, false));
-            const int row = trow + (odd ? 2 : 0), col = ocol + 16 * jb + (r & ~1);
-            const uint32_t d0 = __builtin_amdgcn_perm(nbr, own, odd ? 0x01000504u : 0x05040100u);
-            const uint32_t d1 = __builtin_amdgcn_perm(nbr, own, odd ? 0x03020706u : 0x07060302u);
-            __builtin_amdgcn_raw_buffer_store_b32(d0, orsrc, (row * orow + col) * 2, 0, 0);
-            __builtin_amdgcn_raw_buffer_store_b32(d1, orsrc, ((row + 1) * orow + col) * 2, 0, 0);
-        } else {
-#pragma unroll
-            for (int rr = 0; rr < 4; ++rr) store_out(orsrc, (trow + rr) * orow + ocol + 16 * jb + r, ov[rr], tag);
-        }
-        lds_tile_to_gran(ux, ((wave / CP::CT) * CP::NCB + jb) * 64 + lane, wave % CP::CT, uv, tag);
+        for (int g = 0; g < SP::GT; ++g)
+            acc = gmma(F.kt[g], *reinterpret_cast<const u32x4*>(ux + ((g * SP::NCB + jb0 + j) * 64 + lane) * 16),
+                       acc, tag);
+        S[j] = acc;
     }
-    lds_barrier();
-
-    // (3) S = exp(G_L) S + Kt U
+    if constexpr (MODE == kOut) {
+        if (part == 1) {
+            const int trow = 16 * tb + q4;
 #pragma unroll
-    for (int jb = 0; jb < CP::NCB; ++jb) {
-        u32x4 bu[CP::GT];
+            for (int jb = 0; jb < SP::VB; ++jb) {
+                f32x4 acc = oacc[jb];
 #pragma unroll
-        for (int g = 0; g < CP::GT; ++g)
-            bu[g] = *reinterpret_cast<const u32x4*>(ux + ((g * CP::NCB + jb) * 64 + lane) * 16);
-#pragma unroll
-        for (int i = 0; i < CP::RB; ++i) {
-            f32x4 acc = S[i][jb] * F.gl[i];
-#pragma unroll
-            for (int g = 0; g < CP::GT; ++g) acc = gmma(F.kt[i][g], bu[g], acc, tag);
-            S[i][jb] = acc;
+                for (int g = 0; g < SP::GT; ++g)
+                    acc = gmma(F.p[g], *reinterpret_cast<const u32x4*>(ux + ((g * SP::NCB + jb) * 64 + lane) * 16),
+                               acc, tag);
+                store_o4(orsrc, trow, orow, ocol + 16 * jb + r, acc * scale, r, tag);
+            }
         }
     }
 }
 
-template <int DK, int DV, class TIn, int NB>
-__global__ __launch_bounds__(kThreads) void chunk_carry_kernel(PrefillArgs a) {
-    using CP = CarryPlan<DK, DV, TIn>;
-    constexpr int BV = CP::BV, NT = CP::NT, E = CP::E;
-    __shared__ __attribute__((aligned(16))) char smem[CP::BYTES];
-    char* sx = smem + CP::O_SX;
-    char* ux = smem + CP::O_UX;
+template <int DK, int DV, class TIn, int MODE, int NB>
+__global__ __launch_bounds__(kSegThreads) void seg_carry_kernel(PrefillArgs a) {
+    using SP = SegPlan<DK, DV, TIn, MODE>;
+    constexpr int E = SP::E;
+    __shared__ __attribute__((aligned(16))) char smem[SP::BYTES];
+    char* sx = smem + SP::O_SX;
+    char* ux = smem + SP::O_UX;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int H = a.H;
-    // XCD-aware mapping: the NT dv tiles of one (sequence, head) share an XCD (and its L2)
-    const int groups = a.num_seqs * H;
-    const int b = blockIdx.x, xcd = b % kNumXcd, local = b / kNumXcd;
-    const int group = (local / NT) * kNumXcd + xcd, tile = local % NT;
-    if (group >= groups) return;
-    const int seq = group / H, h = group % H;
-
+    const int tb = wave & 3, part = wave >> 2;
+    const int cb = wave % SP::KB, jb0 = (wave / SP::KB) * SP::SJB;
+    const int H = a.H, s = blockIdx.x / H, h = blockIdx.x % H;
     const WsLayout ws(a.num_seqs, a.total_tokens, H, DK, DV, E);
-    const int32_t* chunk_off = static_cast<const int32_t*>(a.workspace);
-    const char* recs = static_cast<const char*>(a.workspace) + ws.off_rec;
-    const int c_begin = chunk_off[seq], c_end = chunk_off[seq + 1];
-    const int bos = a.cu_seqlens[seq], eos = a.cu_seqlens[seq + 1];
-    const int slot = a.slot_idx[seq];
-    float* Sg = a.pool + (static_cast<int64_t>(slot) * H + h) * (DK * DV) + tile * BV;
+    const char* base = static_cast<const char*>(a.workspace);
+    const int32_t* chunk_off = reinterpret_cast<const int32_t*>(base);
+    const int32_t* seg_off = reinterpret_cast<const int32_t*>(base + ws.off_segoff);
+    if (s >= seg_off[a.num_seqs]) return;
+    const int4 sg = reinterpret_cast<const int4*>(base + ws.off_segtab)[s];
+    const int seq = sg.x, c_first = sg.y, nc = sg.z, last = sg.w & 1;
+    if (MODE == kLocal && last) return;  // the last segment's transition is never used
+    char* blk = const_cast<char*>(base) + ws.off_seg + ws.seg_bytes * (static_cast<size_t>(s) * H + h);
+    const int r = lane & 15, q4 = 4 * (lane >> 4);
 
-    // S[i][jb] holds rows 16 (RB wave + i) + 4 (lane/16) + rr of columns 16 jb + lane%16
-    f32x4 S[CP::RB][CP::NCB];
+    // state tiles: S[j] holds rows 16 cb + q4 + rr of columns 16 (jb0 + j) + r
+    f32x4 S[SP::SJB];
+    if constexpr (MODE == kOut) {
+        const float* Ss = reinterpret_cast<const float*>(blk + ws.s_start);
 #pragma unroll
-    for (int i = 0; i < CP::RB; ++i)
+        for (int j = 0; j < SP::SJB; ++j)
 #pragma unroll
-        for (int jb = 0; jb < CP::NCB; ++jb) S[i][jb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (a.h0_from_pool) {
+            for (int rr = 0; rr < 4; ++rr) S[j][rr] = Ss[(16 * cb + q4 + rr) * DV + 16 * (jb0 + j) + r];
+    } else {
 #pragma unroll
-        for (int i = 0; i < CP::RB; ++i)
+        for (int j = 0; j < SP::SJB; ++j)
 #pragma unroll
-            for (int jb = 0; jb < CP::NCB; ++jb)
-#pragma unroll
-                for (int rr = 0; rr < 4; ++rr)
-                    S[i][jb][rr] = Sg[(16 * (wave * CP::RB + i) + 4 * (lane >> 4) + rr) * DV + 16 * jb + (lane & 15)];
+            for (int rr = 0; rr < 4; ++rr)
+                S[j][rr] = (jb0 + j >= SP::VB && 16 * cb + q4 + rr == 16 * (jb0 + j - SP::VB) + r) ? 1.f : 0.f;
     }
 
-    if (c_begin < c_end) {
-        const int last = c_end - 1;
-        auto rec_of = [&](int c) { return recs + ws.rec_bytes * (static_cast<size_t>(c) * H + h); };
-        const int orow = H * DV, ocol = h * DV + tile * BV;
-        CarryOps<DK, DV, TIn> F[NB];
+    const char* recs = base + ws.off_rec;
+    auto rec_of = [&](int c) { return recs + ws.rec_bytes * (static_cast<size_t>(c) * H + h); };
+    const int task = part == 0 ? 0 : (MODE == kOut ? 1 : 2);
+    const int c_last = c_first + nc - 1;
+    const int bos = a.cu_seqlens[seq], eos = a.cu_seqlens[seq + 1], cs0 = chunk_off[seq];
+    const int orow = H * DV, ocol = h * DV;
+    SegOps<SP> F[NB];
 #pragma unroll
-        for (int k = 0; k < NB; ++k) carry_fetch(F[k], rec_of(min(c_begin + k, last)), ws, tile, wave, lane);
-        for (int c = c_begin; c < c_end; c += NB) {
+    for (int k = 0; k < NB; ++k)
+        seg_fetch(F[k], rec_of(min(c_first + k, c_last)), ws, tb, task, cb, lane);
+    for (int c = c_first; c <= c_last; c += NB) {
 #pragma unroll
-            for (int k = 0; k < NB; ++k) {
-                const int cc = c + k;
-                if (cc < c_end) {
-                    const int t0 = bos + kChunk * (cc - c_begin), L = min(kChunk, eos - t0);
-                    const __amdgpu_buffer_rsrc_t orsrc =
-                        buf_rsrc(static_cast<char*>(a.o) + static_cast<int64_t>(t0) * orow * E,
-                                 static_cast<int64_t>(L) * orow * E);
-                    carry_step<DK, DV, TIn>(F[k], S, sx, ux, orsrc, orow, ocol, a.scale, wave, lane);
-                }
-                carry_fetch(F[k], rec_of(min(cc + NB, last)), ws, tile, wave, lane);
+        for (int k = 0; k < NB; ++k) {
+            const int cc = c + k;
+            if (cc <= c_last) {
+                // output rows of this chunk (an empty range in LOCAL mode, which stores nothing)
+                const int t0 = bos + kChunk * (cc - cs0), L = min(kChunk, eos - t0);
+                const __amdgpu_buffer_rsrc_t orsrc =
+                    buf_rsrc(static_cast<char*>(a.o) + static_cast<int64_t>(t0) * orow * E,
+                             MODE == kOut ? static_cast<int64_t>(L) * orow * E : 0);
+                seg_step<DK, DV, TIn, MODE>(F[k], S, sx, ux, orsrc, orow, ocol, a.scale, tb, part, cb, jb0, lane);
             }
+            seg_fetch(F[k], rec_of(min(cc + NB, c_last)), ws, tb, task, cb, lane);
         }
     }
 
-    // final state back to the slot
+    // results
+    if constexpr (MODE == kOut) {
+        if (last) {
+            float* Sg = a.pool + (static_cast<int64_t>(a.slot_idx[seq]) * H + h) * (DK * DV);
 #pragma unroll
-    for (int i = 0; i < CP::RB; ++i)
+            for (int j = 0; j < SP::SJB; ++j)
 #pragma unroll
-        for (int jb = 0; jb < CP::NCB; ++jb)
+                for (int rr = 0; rr < 4; ++rr) Sg[(16 * cb + q4 + rr) * DV + 16 * (jb0 + j) + r] = S[j][rr];
+        }
+    } else {
+        float* Sl = reinterpret_cast<float*>(blk + ws.s_loc);
+        float* Ph = reinterpret_cast<float*>(blk + ws.s_phi);
 #pragma unroll
-            for (int rr = 0; rr < 4; ++rr)
-                Sg[(16 * (wave * CP::RB + i) + 4 * (lane >> 4) + rr) * DV + 16 * jb + (lane & 15)] = S[i][jb][rr];
+        for (int j = 0; j < SP::SJB; ++j) {
+            const int jb = jb0 + j;
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+                const int row = 16 * cb + q4 + rr;
+                if (jb < SP::VB)
+                    Sl[row * DV + 16 * jb + r] = S[j][rr];
+                else
+                    Ph[row * DK + 16 * (jb - SP::VB) + r] = S[j][rr];
+            }
+        }
+    }
+}
+
+// seg_scan: one workgroup (4 waves) per (sequence, head, 16-column tile).  Wave w owns
+// the tile's rows 16 (RW w + i) .. + 15.  X (fp32) -> S_start of each segment; X =
+// Phi X + S_loc on fp32 MFMA, X crossing the waves through LDS transposed.
+template <int DK, int DV, int E>
+__global__ __launch_bounds__(kThreads) void seg_scan_kernel(PrefillArgs a) {
+    constexpr int NTS = DV / 16, KB = DK / 16, RW = KB / 4, LDX = DK + 4;
+    __shared__ __attribute__((aligned(16))) float xs[16 * LDX];  // X^T [16 columns][DK]
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int r = lane & 15, q4 = 4 * (lane >> 4);
+    const int H = a.H, b = blockIdx.x, tile = b % NTS, group = b / NTS;
+    if (group >= a.num_seqs * H) return;
+    const int seq = group / H, h = group % H;
+    const WsLayout ws(a.num_seqs, a.total_tokens, H, DK, DV, E);
+    const char* base = static_cast<const char*>(a.workspace);
+    const int32_t* seg_off = reinterpret_cast<const int32_t*>(base + ws.off_segoff);
+    const int s0 = seg_off[seq], nseg = seg_off[seq + 1] - s0;
+    float* Sg = a.pool + (static_cast<int64_t>(a.slot_idx[seq]) * H + h) * (DK * DV) + 16 * tile;
+    const int col = 16 * tile + r;
+
+    f32x4 X[RW];
+#pragma unroll
+    for (int i = 0; i < RW; ++i)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr)
+            X[i][rr] = a.h0_from_pool ? Sg[(16 * (RW * wave + i) + q4 + rr) * DV + r] : 0.f;
+    if (nseg == 0) {
+        // no tokens: the final state is the initial state (zero unless read from the slot)
+        if (!a.h0_from_pool)
+#pragma unroll
+            for (int i = 0; i < RW; ++i)
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr) Sg[(16 * (RW * wave + i) + q4 + rr) * DV + r] = 0.f;
+        return;
+    }
+    for (int k = 0; k < nseg; ++k) {
+        char* blk = const_cast<char*>(base) + ws.off_seg + ws.seg_bytes * (static_cast<size_t>(s0 + k) * H + h);
+        float* Ss = reinterpret_cast<float*>(blk + ws.s_start);
+#pragma unroll
+        for (int i = 0; i < RW; ++i)
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) Ss[(16 * (RW * wave + i) + q4 + rr) * DV + col] = X[i][rr];
+        if (k == nseg - 1) break;
+        const float* Sl = reinterpret_cast<const float*>(blk + ws.s_loc);
+        const float* Ph = reinterpret_cast<const float*>(blk + ws.s_phi);
+#pragma unroll
+        for (int i = 0; i < RW; ++i)
+            *reinterpret_cast<f32x4*>(xs + r * LDX + 16 * (RW * wave + i) + q4) = X[i];
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < RW; ++i) {
+            const int rb = RW * wave + i;
+            f32x4 acc;
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) acc[rr] = Sl[(16 * rb + q4 + rr) * DV + col];
+            // lane (r, q) supplies k = 16 kb + 4q + ks of Phi row 16 rb + r and of X column r
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+                const f32x4 pa = *reinterpret_cast<const f32x4*>(Ph + (16 * rb + r) * DK + 16 * kb + q4);
+                const f32x4 pb = *reinterpret_cast<const f32x4*>(xs + r * LDX + 16 * kb + q4);
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(pa[ks], pb[ks], acc, 0, 0, 0);
+            }
+            X[i] = acc;
+        }
+        __syncthreads();
+    }
 }
 
 // Compute units of the current device (cached per device).
@@ -1001,19 +1104,24 @@ hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t stream) {
     } else {
         constexpr int E = Geo<TIn>::E;
         const WsLayout ws(a.num_seqs, a.total_tokens, a.H, DK, DV, E);
-        int32_t* chunk_off = static_cast<int32_t*>(a.workspace);
-        int4* table = reinterpret_cast<int4*>(static_cast<char*>(a.workspace) + ws.off_table);
-        hipLaunchKernelGGL(chunk_map_kernel, dim3(1), dim3(kThreads), 0, stream, a.cu_seqlens, a.num_seqs, chunk_off,
-                           table);
+        char* base = static_cast<char*>(a.workspace);
+        hipLaunchKernelGGL(chunk_map_kernel, dim3(1), dim3(kThreads), 0, stream, a.cu_seqlens, a.num_seqs,
+                           ws.seg_chunks, reinterpret_cast<int32_t*>(base), reinterpret_cast<int32_t*>(base + ws.off_segoff),
+                           reinterpret_cast<int4*>(base + ws.off_table), reinterpret_cast<int4*>(base + ws.off_segtab));
         const int64_t items = ws.max_chunks * a.H;
         if (items > 0) {
             const int cus = device_cu_count();
             const int grid = static_cast<int>(items < cus ? items : cus);
             hipLaunchKernelGGL((chunk_intra_kernel<DK, DV, TIn>), dim3(grid), dim3(kThreads), 0, stream, a);
+            const dim3 sgrid(static_cast<unsigned>(ws.max_segs * a.H));
+            hipLaunchKernelGGL((seg_carry_kernel<DK, DV, TIn, kLocal, kCarryNB>), sgrid, dim3(kSegThreads), 0,
+                               stream, a);
         }
-        const int groups = a.num_seqs * a.H;
-        const int grid = (groups + kNumXcd - 1) / kNumXcd * kNumXcd * (DV / kCarryBV);
-        hipLaunchKernelGGL((chunk_carry_kernel<DK, DV, TIn, kCarryNB>), dim3(grid), dim3(kThreads), 0, stream, a);
+        hipLaunchKernelGGL((seg_scan_kernel<DK, DV, E>), dim3(a.num_seqs * a.H * (DV / 16)), dim3(kThreads), 0, stream,
+                           a);
+        if (items > 0)
+            hipLaunchKernelGGL((seg_carry_kernel<DK, DV, TIn, kOut, kCarryNB>),
+                               dim3(static_cast<unsigned>(ws.max_segs * a.H)), dim3(kSegThreads), 0, stream, a);
         return hipGetLastError();
     }
 }

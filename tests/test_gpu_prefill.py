@@ -79,6 +79,38 @@ def test_bf16_varlen_ragged(dk, dv):
     assert torch.equal(got[others], y["pool"][others])
 
 
+# Sequences longer than one 32-chunk segment go through the segment scan: a local pass
+# from [0 | I], the fp32 scan of segment start states, and the output pass.  Lengths
+# cover 1-chunk tail segments, exact multiples of the segment and of the chunk.
+MULTI_SEG = (4200, 2049, 64, 0, 4097, 2048)
+
+
+@pytest.mark.parametrize("dv", [64, 128])
+def test_fp32_multi_segment(dv):
+    """fp32 (dk = 64) through several segments per sequence with h0 from slots; <= 1e-4."""
+    dev = need_gpu()
+    announce("prefill fp32 multi-segment dk=64 dv=%d" % dv)
+    y = W.prefill(seed=7, seqlens=MULTI_SEG, H=2, dk=64, dv=dv, num_slots=8, h0_std=0.05,
+                  dtype=torch.float32)
+    o, pool = run_prefill(y, dev)
+    o_ref, h_ref, _ = oracle_prefill(y)
+    assert rel_l2(f64(o), o_ref) <= 1e-4
+    assert rel_l2(f64(pool.cpu()[y["slot_idx"].long()]), h_ref) <= 1e-4
+
+
+@pytest.mark.parametrize("h0", [True, False])
+def test_bf16_multi_segment(h0):
+    """bf16 dk = dv = 128 through several segments per sequence; rel-L2 <= 1e-2."""
+    dev = need_gpu()
+    announce("prefill bf16 multi-segment h0_from_pool=%d" % h0)
+    y = W.prefill(seed=8, seqlens=MULTI_SEG, H=3, dk=128, dv=128, num_slots=8, h0_std=0.05)
+    o, pool = run_prefill(y, dev, h0_from_pool=h0)
+    o_ref, h_ref, _ = oracle_prefill(y, h0_from_pool=h0)
+    assert rel_l2(f64(o), o_ref) <= 1e-2
+    assert worst_rel_l2(f64(o), o_ref, 1) <= 2e-2  # per head
+    assert rel_l2(f64(pool.cpu()[y["slot_idx"].long()]), h_ref) <= 1e-2
+
+
 def test_zero_initial_state_ignores_pool_contents():
     dev = need_gpu()
     announce("prefill h0 zero")
