@@ -1050,37 +1050,57 @@ __global__ __launch_bounds__(kThreads) void seg_scan_kernel(PrefillArgs a) {
                 for (int rr = 0; rr < 4; ++rr) Sg[(16 * (RW * wave + i) + q4 + rr) * DV + r] = 0.f;
         return;
     }
+    // Phi_k and S_loc(k) rows of this wave, loaded one segment ahead of their use
+    struct Ops {
+        f32x4 ph[RW][KB], sl[RW];
+    };
+    auto blk_of = [&](int k) {
+        return const_cast<char*>(base) + ws.off_seg + ws.seg_bytes * (static_cast<size_t>(s0 + k) * H + h);
+    };
+    auto load = [&](Ops& o, int k) {
+        const char* blk = blk_of(k);
+        const float* Sl = reinterpret_cast<const float*>(blk + ws.s_loc);
+        const float* Ph = reinterpret_cast<const float*>(blk + ws.s_phi);
+#pragma unroll
+        for (int i = 0; i < RW; ++i) {
+            const int rb = RW * wave + i;
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+                o.ph[i][kb] = *reinterpret_cast<const f32x4*>(Ph + (16 * rb + r) * DK + 16 * kb + q4);
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) o.sl[i][rr] = Sl[(16 * rb + q4 + rr) * DV + col];
+        }
+    };
+    Ops cur;
+    if (nseg > 1) load(cur, 0);
     for (int k = 0; k < nseg; ++k) {
-        char* blk = const_cast<char*>(base) + ws.off_seg + ws.seg_bytes * (static_cast<size_t>(s0 + k) * H + h);
-        float* Ss = reinterpret_cast<float*>(blk + ws.s_start);
+        float* Ss = reinterpret_cast<float*>(blk_of(k) + ws.s_start);
 #pragma unroll
         for (int i = 0; i < RW; ++i)
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) Ss[(16 * (RW * wave + i) + q4 + rr) * DV + col] = X[i][rr];
         if (k == nseg - 1) break;
-        const float* Sl = reinterpret_cast<const float*>(blk + ws.s_loc);
-        const float* Ph = reinterpret_cast<const float*>(blk + ws.s_phi);
+        Ops nxt;
+        load(nxt, min(k + 1, nseg - 2));  // the last segment has no transition; repeat a valid one
 #pragma unroll
         for (int i = 0; i < RW; ++i)
             *reinterpret_cast<f32x4*>(xs + r * LDX + 16 * (RW * wave + i) + q4) = X[i];
-        __syncthreads();
+        lds_barrier();
+        // lane (r, q) supplies k = 16 kb + 4q + ks of Phi row 16 rb + r and of X column r
 #pragma unroll
         for (int i = 0; i < RW; ++i) {
-            const int rb = RW * wave + i;
-            f32x4 acc;
-#pragma unroll
-            for (int rr = 0; rr < 4; ++rr) acc[rr] = Sl[(16 * rb + q4 + rr) * DV + col];
-            // lane (r, q) supplies k = 16 kb + 4q + ks of Phi row 16 rb + r and of X column r
+            f32x4 acc = cur.sl[i];
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb) {
-                const f32x4 pa = *reinterpret_cast<const f32x4*>(Ph + (16 * rb + r) * DK + 16 * kb + q4);
                 const f32x4 pb = *reinterpret_cast<const f32x4*>(xs + r * LDX + 16 * kb + q4);
 #pragma unroll
-                for (int ks = 0; ks < 4; ++ks) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(pa[ks], pb[ks], acc, 0, 0, 0);
+                for (int ks = 0; ks < 4; ++ks)
+                    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(cur.ph[i][kb][ks], pb[ks], acc, 0, 0, 0);
             }
             X[i] = acc;
         }
-        __syncthreads();
+        lds_barrier();
+        cur = nxt;
     }
 }
 
