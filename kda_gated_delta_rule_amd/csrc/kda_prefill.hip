@@ -306,10 +306,12 @@ __global__ __launch_bounds__(kThreads) void chunk_map_kernel(const int32_t* __re
 //   R1  KI [64][LDK]            | T fp32 [64][LDA]
 //   R2  KG^T [DK][LDT]
 //   R3  V^T [DV][LDT]
-//   R4  Kt^T [DK][LDT]          | A fp32 [64][LDA]
+//   RD  the diagonal 16x16 blocks of A, fp32 [4][16][LDD]
 //   RT  T' = T diag(beta) [64][LDT]
-//   RQ  QG [64][LDK]
 //   RM  beta [64], wave gate totals [4][DK]
+// (bf16, dk = dv = 128: 68.5 KiB, so two workgroups share a CU.)  The rest of A stays in
+// the registers of the wave that owns its rows; the QG and Kt record granules are built
+// in registers by MFMA products with a 0/1 selector (exact), without an LDS transpose.
 // ---------------------------------------------------------------------------
 template <int DK, int DV, class TIn>
 struct IntraPlan {
@@ -324,12 +326,12 @@ struct IntraPlan {
     static constexpr size_t R1 = align_up(cmax(64ull * LDK * E, 64ull * LDA * 4), 16);
     static constexpr size_t R2 = align_up(1ull * DK * LDT * E, 16);
     static constexpr size_t R3 = align_up(1ull * DV * LDT * E, 16);
-    static constexpr size_t R4 = align_up(cmax(1ull * DK * LDT * E, 64ull * LDA * 4), 16);
+    static constexpr int LDD = 20;  // fp32 diagonal-block rows (16 + 4, 16-byte aligned)
+    static constexpr size_t RD = align_up(4ull * 16 * LDD * 4, 16);
     static constexpr size_t RT = align_up(64ull * LDT * E, 16);
-    static constexpr size_t RQ = align_up(64ull * LDK * E, 16);
     static constexpr size_t RM = align_up(4ull * (64 + 4 * DK), 16);
-    static constexpr size_t O1 = 0, O2 = O1 + R1, O3 = O2 + R2, O4 = O3 + R3, OT = O4 + R4;
-    static constexpr size_t OQ = OT + RT, OM = OQ + RQ;
+    static constexpr size_t O1 = 0, O2 = O1 + R1, O3 = O2 + R2, OD = O3 + R3, OT = OD + RD;
+    static constexpr size_t OM = OT + RT;
     static constexpr size_t BYTES = OM + RM;
     static constexpr bool fits = BYTES <= 160 * 1024;
 };
@@ -390,10 +392,8 @@ __device__ __forceinline__ void intra_compute(const IntraIn<DK, DV, TIn>& X, cha
     float* sT = reinterpret_cast<float*>(smem + P::O1);
     elem* sKGt = reinterpret_cast<elem*>(smem + P::O2);
     elem* sVt = reinterpret_cast<elem*>(smem + P::O3);
-    elem* sKTt = reinterpret_cast<elem*>(smem + P::O4);
-    float* sA = reinterpret_cast<float*>(smem + P::O4);
+    float* sD = reinterpret_cast<float*>(smem + P::OD);
     elem* sTp = reinterpret_cast<elem*>(smem + P::OT);
-    elem* sQG = reinterpret_cast<elem*>(smem + P::OQ);
     float* sBeta = reinterpret_cast<float*>(smem + P::OM);
     float* sTot = sBeta + 64;
 
@@ -403,37 +403,34 @@ __device__ __forceinline__ void intra_compute(const IntraIn<DK, DV, TIn>& X, cha
     // The gates are scaled by log2(e) before the scan, so each exponential below is a
     // single exp2.
     constexpr float kLog2e = 1.4426950408889634f;
-    float qf[NGK][GW], kf[NGK][GW], gf[NGK][GW];
+    // q and k stay packed (unpacked again where used); only the norms' scale factors live on
+    float gf[NGK][GW];
 #pragma unroll
-    for (int j = 0; j < NGK; ++j) {
-        gran_to_f32(X.q[j], qf[j], tag);
-        gran_to_f32(X.k[j], kf[j], tag);
+    for (int j = 0; j < NGK; ++j)
 #pragma unroll
         for (int m = 0; m < GW / 4; ++m)
 #pragma unroll
             for (int e = 0; e < 4; ++e) gf[j][4 * m + e] = X.g[j][m][e] * kLog2e;
-    }
+    float iq = 1.f, ik = 1.f;
     if (a.use_l2) {
         float sq = 0.f, sk = 0.f;
 #pragma unroll
-        for (int j = 0; j < NGK; ++j)
+        for (int j = 0; j < NGK; ++j) {
+            float qv[GW], kv[GW];
+            gran_to_f32(X.q[j], qv, tag);
+            gran_to_f32(X.k[j], kv, tag);
 #pragma unroll
             for (int e = 0; e < GW; ++e) {
-                sq = fmaf(qf[j][e], qf[j][e], sq);
-                sk = fmaf(kf[j][e], kf[j][e], sk);
+                sq = fmaf(qv[e], qv[e], sq);
+                sk = fmaf(kv[e], kv[e], sk);
             }
+        }
         sq += __shfl_xor(sq, 16, 64);
         sk += __shfl_xor(sk, 16, 64);
         sq += __shfl_xor(sq, 32, 64);
         sk += __shfl_xor(sk, 32, 64);
-        const float iq = 1.f / sqrtf(sq + kNormEps), ik = 1.f / sqrtf(sk + kNormEps);
-#pragma unroll
-        for (int j = 0; j < NGK; ++j)
-#pragma unroll
-            for (int e = 0; e < GW; ++e) {
-                qf[j][e] *= iq;
-                kf[j][e] *= ik;
-            }
+        iq = 1.f / sqrtf(sq + kNormEps);
+        ik = 1.f / sqrtf(sk + kNormEps);
     }
 #pragma unroll
     for (int j = 0; j < NGK; ++j)
@@ -470,11 +467,35 @@ __device__ __forceinline__ void intra_compute(const IntraIn<DK, DV, TIn>& X, cha
         }
     };
     u32x4 KG[NGK], QG[NGK];
+    // V^T first, so the V registers are free for the rest of the phase
+#pragma unroll
+    for (int j = 0; j < NGV; ++j) {
+        if constexpr (E == 2) {
+            pair_store(sVt, X.v[j], j);
+        } else {
+#pragma unroll
+            for (int e = 0; e < GW; ++e) sVt[(GW * (4 * j + q) + e) * LDT + t] = __uint_as_float(X.v[j][e]);
+        }
+    }
+    // sel[h]: the 0/1 granule whose row n picks channel 16 h + n of a 32-channel bf16
+    // granule (fp32: channel n of a 16-channel granule, one 0/1 value per k-step).  A
+    // product with it copies values exactly and leaves them in accumulator layout, which
+    // gives the Kt and QG record granules without an LDS transpose.
+    u32x4 sel[RG::CT];
+#pragma unroll
+    for (int h = 0; h < RG::CT; ++h) {
+        float x[GW];
+#pragma unroll
+        for (int e = 0; e < GW; ++e) x[e] = (E == 2 ? (8 * q + e == 16 * h + r) : (4 * q + e == r)) ? 1.f : 0.f;
+        sel[h] = f32_to_gran(x, tag);
+    }
     {
         float* gl_out = reinterpret_cast<float*>(rec + ws.o_gl);
 #pragma unroll
         for (int j = 0; j < NGK; ++j) {
-            float kg[GW], ki[GW], qg[GW], kt[GW];
+            float kg[GW], ki[GW], qg[GW], kt[GW], qv[GW], kv[GW];
+            gran_to_f32(X.q[j], qv, tag);
+            gran_to_f32(X.k[j], kv, tag);
 #pragma unroll
             for (int m = 0; m < GW / 4; ++m) {
                 const int c = GW * (4 * j + q) + 4 * m;
@@ -490,10 +511,11 @@ __device__ __forceinline__ void intra_compute(const IntraIn<DK, DV, TIn>& X, cha
                     tot[e] = (t0[e] + t1[e]) + t2[e] + t3[e];
                     const float G = gf[j][i] + pre;
                     const float eg = __builtin_amdgcn_exp2f(G), ei = __builtin_amdgcn_exp2f(-G);
-                    kg[i] = kf[j][i] * eg;
-                    ki[i] = kf[j][i] * ei;
-                    qg[i] = qf[j][i] * eg;
-                    kt[i] = kf[j][i] * __builtin_amdgcn_exp2f(tot[e] - G);
+                    const float kh = kv[i] * ik;
+                    kg[i] = kh * eg;
+                    ki[i] = kh * ei;
+                    qg[i] = qv[i] * iq * eg;
+                    kt[i] = kh * __builtin_amdgcn_exp2f(tot[e] - G);
                 }
                 if (wave == 0 && r == 0)
                     *reinterpret_cast<f32x4*>(gl_out + c) =
@@ -503,50 +525,37 @@ __device__ __forceinline__ void intra_compute(const IntraIn<DK, DV, TIn>& X, cha
             KG[j] = f32_to_gran(kg, tag);
             QG[j] = f32_to_gran(qg, tag);
             *reinterpret_cast<u32x4*>(sKI + t * LDK + GW * (4 * j + q)) = f32_to_gran(ki, tag);
-            *reinterpret_cast<u32x4*>(sQG + t * LDK + GW * (4 * j + q)) = QG[j];
-            // transposed copies [channel][token]
+            // transposed copy [channel][token]
             if constexpr (E == 2) {
                 pair_store(sKGt, KG[j], j);
-                pair_store(sKTt, f32_to_gran(kt, tag), j);
             } else {
 #pragma unroll
-                for (int e = 0; e < GW; ++e) {
-                    const int c = GW * (4 * j + q) + e;
-                    sKGt[c * LDT + t] = kg[e];
-                    sKTt[c * LDT + t] = kt[e];
-                }
+                for (int e = 0; e < GW; ++e) sKGt[(GW * (4 * j + q) + e) * LDT + t] = kg[e];
             }
-        }
+            // records: granule j spans the dk blocks CT j .. CT j + CT - 1
+            const u32x4 ktg = f32_to_gran(kt, tag);
+            f32x4 qt[RG::CT];
 #pragma unroll
-        for (int j = 0; j < NGV; ++j) {
-            if constexpr (E == 2) {
-                pair_store(sVt, X.v[j], j);
-            } else {
-#pragma unroll
-                for (int e = 0; e < GW; ++e) sVt[(GW * (4 * j + q) + e) * LDT + t] = __uint_as_float(X.v[j][e]);
+            for (int h = 0; h < RG::CT; ++h) {
+                const int cb = RG::CT * j + h;
+                // Kt tile (rows t of this token block, columns c): lane holds tokens
+                // 16 wave + 4q + rr of channel 16 cb + r -> its half of the Kt granule
+                const f32x4 kt4 = gmma(ktg, sel[h], f32x4{0.f, 0.f, 0.f, 0.f}, tag);
+                char* dk = rec + ws.o_kt + ((static_cast<size_t>(cb) * RG::GT + wave / RG::CT) * 64 + lane) * 16;
+                if constexpr (E == 2)
+                    *reinterpret_cast<u32x2*>(dk + (wave % RG::CT) * 8) =
+                        u32x2{pack_bf16x2(kt4[0], kt4[1]), pack_bf16x2(kt4[2], kt4[3])};
+                else
+                    *reinterpret_cast<f32x4*>(dk) = kt4;
+                // QG^T tile (rows c, columns t): lane holds channels 16 cb + 4q + rr of token t
+                qt[h] = gmma(sel[h], QG[j], f32x4{0.f, 0.f, 0.f, 0.f}, tag);
             }
+            *reinterpret_cast<u32x4*>(rec + ws.o_q + ((static_cast<size_t>(wave) * RG::GK + j) * 64 + lane) * 16) =
+                tiles_to_gran(qt[0], qt[RG::CT - 1], tag);
         }
     }
     lds_barrier();
-    // ---- 3. Kt record; A^T and P^T tiles (all four column blocks, straight-line) -----
-    {
-        constexpr int NKT = DK / 16 * RG::GT * 64;  // granules of Kt
-        static_assert(NKT % kThreads == 0, "");
-#pragma unroll
-        for (int n = 0; n < NKT / kThreads; ++n) {
-            const int gi = tid + kThreads * n, ln = gi & 63, blk = gi >> 6;
-            const int c = 16 * (blk / RG::GT) + (ln & 15), g = blk % RG::GT, q2 = ln >> 4;
-            u32x4 val;
-            if constexpr (E == 2) {
-                const u32x2 lo = *reinterpret_cast<const u32x2*>(sKTt + c * LDT + 32 * g + 4 * q2);
-                const u32x2 hi = *reinterpret_cast<const u32x2*>(sKTt + c * LDT + 32 * g + 16 + 4 * q2);
-                val = u32x4{lo[0], lo[1], hi[0], hi[1]};
-            } else {
-                val = *reinterpret_cast<const u32x4*>(sKTt + c * LDT + 16 * g + 4 * q2);
-            }
-            *reinterpret_cast<u32x4*>(rec + ws.o_kt + static_cast<size_t>(gi) * 16) = val;
-        }
-    }
+    // ---- 3. A^T and P^T tiles (all four column blocks, straight-line); P record -------
     f32x4 Areg[4], Preg[4];
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
@@ -573,37 +582,30 @@ __device__ __forceinline__ void intra_compute(const IntraIn<DK, DV, TIn>& X, cha
     for (int g = 0; g < RG::GT; ++g)
         *reinterpret_cast<u32x4*>(rec + ws.o_p + ((static_cast<size_t>(wave) * RG::GT + g) * 64 + lane) * 16) =
             tiles_to_gran(Preg[RG::CT * g], Preg[RG::CT * g + RG::CT - 1], tag);
-#pragma unroll
-    for (int g = 0; g < RG::GK; ++g) {
-        u32x4 val;
-        if constexpr (E == 2) {
-            const u32x2 lo = *reinterpret_cast<const u32x2*>(sQG + t * LDK + 32 * g + 4 * q);
-            const u32x2 hi = *reinterpret_cast<const u32x2*>(sQG + t * LDK + 32 * g + 16 + 4 * q);
-            val = u32x4{lo[0], lo[1], hi[0], hi[1]};
-        } else {
-            val = *reinterpret_cast<const u32x4*>(sQG + t * LDK + 16 * g + 4 * q);
-        }
-        *reinterpret_cast<u32x4*>(rec + ws.o_q + ((static_cast<size_t>(wave) * RG::GK + g) * 64 + lane) * 16) = val;
-    }
     lds_barrier();
 
-    // ---- 4. A to LDS (Kt^T is dead); zero the upper blocks of T' ----------------------
+    // ---- 4. this wave's diagonal block of A to LDS; zero the upper blocks of its T' rows
+    //      (both read only by this wave until the next barrier)
+    {
+        f32x4 dg = Areg[0];
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) *reinterpret_cast<f32x4*>(sA + t * LDA + 16 * jj + 4 * q) = Areg[jj];
+        for (int jj = 1; jj < 4; ++jj)
+            if (jj == wave) dg = Areg[jj];
+        *reinterpret_cast<f32x4*>(sD + (16 * wave + r) * P::LDD + 4 * q) = dg;
+    }
     for (int jj = wave + 1; jj < 4; ++jj) lds_store4(sTp + t * LDT + 16 * jj + 4 * q, 0.f, 0.f, 0.f, 0.f);
-    lds_barrier();
 
     // ---- 5. T = (I + A)^-1 by 16x16 blocks ----------------------------------------------
     // 5a. diagonal block of this wave by forward substitution, one lane per column
     {
         const int col = r;
-        const float* Ab = sA + (16 * wave) * LDA + 16 * wave;
+        const float* Ab = sD + (16 * wave) * P::LDD;
         float x[16];
 #pragma unroll
         for (int rr = 0; rr < 16; ++rr) {
             f32x4 row[4];
 #pragma unroll
-            for (int m = 0; m < 4; ++m) row[m] = *reinterpret_cast<const f32x4*>(Ab + rr * LDA + 4 * m);
+            for (int m = 0; m < 4; ++m) row[m] = *reinterpret_cast<const f32x4*>(Ab + rr * P::LDD + 4 * m);
             float acc = rr == col ? 1.f : 0.f;
 #pragma unroll
             for (int s = 0; s < rr; ++s) acc = fmaf(-row[s >> 2][s & 3], x[s], acc);
@@ -624,15 +626,19 @@ __device__ __forceinline__ void intra_compute(const IntraIn<DK, DV, TIn>& X, cha
     for (int d = 1; d < 4; ++d) {
         if (wave >= d) {
             const int jb = wave - d;
+            // y = sum over k blocks jb .. wave - 1 of A_{wave,kb} T_{kb,jb}; A comes from the
+            // registers (lane (r, q) supplies k = 4q + ks: A[16 wave + r][16 kb + 4q + ks]);
+            // blocks outside the range are masked to zero in both operands
             f32x4 y = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int kk = 0; kk < d; ++kk) {
-                const int kb = jb + kk;
+            for (int kb = 0; kb < 3; ++kb) {
+                const bool in = kb >= jb && kb < wave;
 #pragma unroll
-                for (int ks = 0; ks < 4; ++ks)
-                    y = __builtin_amdgcn_mfma_f32_16x16x4f32(sA[(16 * wave + r) * LDA + 16 * kb + 4 * ks + q],
-                                                             sT[(16 * kb + 4 * ks + q) * LDA + 16 * jb + r], y, 0,
-                                                             0, 0);
+                for (int ks = 0; ks < 4; ++ks) {
+                    const float av = in ? Areg[kb][ks] : 0.f;
+                    const float tv = in ? sT[(16 * kb + 4 * q + ks) * LDA + 16 * jb + r] : 0.f;
+                    y = __builtin_amdgcn_mfma_f32_16x16x4f32(av, tv, y, 0, 0, 0);
+                }
             }
             // z = T_ww y; lane (r, q) supplies k = 4q + ks of both operands
             f32x4 z = {0.f, 0.f, 0.f, 0.f};
@@ -651,49 +657,52 @@ __device__ __forceinline__ void intra_compute(const IntraIn<DK, DV, TIn>& X, cha
         lds_barrier();
     }
 
-    // ---- 6. W^T = KG^T T'^T and Ut = T' V, straight to the record ---------------------
-    constexpr int NCK = DK / 16, NCV = DV / 16;
+    // ---- 6. W^T = KG^T T'^T and Ut = T' V, straight to the record (each granule stored as
+    //      soon as its tiles are done) -------------------------------------------------
     {
         const elem* Tr = sTp + (16 * wave + r) * LDT + (KS / 4) * q;
-        f32x4 wt[NCK];
 #pragma unroll
-        for (int cb = 0; cb < NCK; ++cb) {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            const elem* Kr = sKGt + (16 * cb + r) * LDT + (KS / 4) * q;
+        for (int g = 0; g < RG::GK; ++g) {
+            f32x4 wt[RG::CT];
 #pragma unroll
-            for (int ks = 0; ks < KST; ++ks) acc = lmma(Kr + KS * ks, Tr + KS * ks, acc);  // tile (c, t)
-            wt[cb] = acc;
-        }
+            for (int h = 0; h < RG::CT; ++h) {
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+                const elem* Kr = sKGt + (16 * (RG::CT * g + h) + r) * LDT + (KS / 4) * q;
 #pragma unroll
-        for (int g = 0; g < RG::GK; ++g)
+                for (int ks = 0; ks < KST; ++ks) acc = lmma(Kr + KS * ks, Tr + KS * ks, acc);  // tile (c, t)
+                wt[h] = acc;
+            }
             *reinterpret_cast<u32x4*>(rec + ws.o_w + ((static_cast<size_t>(wave) * RG::GK + g) * 64 + lane) * 16) =
-                tiles_to_gran(wt[RG::CT * g], wt[RG::CT * g + RG::CT - 1], tag);
-        f32x4 ut[NCV];
-#pragma unroll
-        for (int jb = 0; jb < NCV; ++jb) {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            const elem* Vr = sVt + (16 * jb + r) * LDT + (KS / 4) * q;
-#pragma unroll
-            for (int ks = 0; ks < KST; ++ks) acc = lmma(Tr + KS * ks, Vr + KS * ks, acc);  // tile (t, j)
-            ut[jb] = acc;
+                tiles_to_gran(wt[0], wt[RG::CT - 1], tag);
         }
-        // per dv tile, its NCB column blocks' 4 values each
+        // Ut: per dv tile, its NCB column blocks' 4 values each
 #pragma unroll
         for (int tile = 0; tile < RG::NT; ++tile) {
             char* dst = rec + ws.o_u + (static_cast<size_t>(tile * 4 + wave) * 64 + lane) * RG::UB;
 #pragma unroll
             for (int n = 0; n < RG::UB / 16; ++n) {
-                const int jb = RG::NCB * tile + (E == 2 ? 2 * n : n);
-                *reinterpret_cast<u32x4*>(dst + 16 * n) = tiles_to_gran(ut[jb], ut[E == 2 ? jb + 1 : jb], tag);
+                f32x4 ut[RG::CT];
+#pragma unroll
+                for (int h = 0; h < RG::CT; ++h) {
+                    const int jb = RG::NCB * tile + RG::CT * n + h;
+                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+                    const elem* Vr = sVt + (16 * jb + r) * LDT + (KS / 4) * q;
+#pragma unroll
+                    for (int ks = 0; ks < KST; ++ks) acc = lmma(Tr + KS * ks, Vr + KS * ks, acc);  // tile (t, j)
+                    ut[h] = acc;
+                }
+                *reinterpret_cast<u32x4*>(dst + 16 * n) = tiles_to_gran(ut[0], ut[RG::CT - 1], tag);
             }
         }
     }
 }
 
-// Persistent: workgroup b takes items b, b + grid, ... (item = chunk * H + head); the
-// next item's inputs are requested before the current one is computed.
+// Persistent: workgroup b takes items b, b + grid, ... (item = chunk * H + head); two
+// workgroups share a CU (bf16), so one computes while the other waits for its inputs.
+// The table entry of the next item is read with a vector load one item ahead, so the
+// LDS barriers (which wait for scalar loads) never wait for it.
 template <int DK, int DV, class TIn>
-__global__ __launch_bounds__(kThreads) void chunk_intra_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(kThreads, 2) void chunk_intra_kernel(PrefillArgs a) {
     using P = IntraPlan<DK, DV, TIn>;
     static_assert(P::fits, "LDS plan exceeds 160 KiB");
     __shared__ __attribute__((aligned(16))) char smem[P::BYTES];
@@ -705,27 +714,17 @@ __global__ __launch_bounds__(kThreads) void chunk_intra_kernel(PrefillArgs a) {
     char* recs = static_cast<char*>(a.workspace) + ws.off_rec;
     const int total = chunk_off[a.num_seqs] * H;
     const int stride = gridDim.x;
+    const auto rtab = buf_rsrc(table, static_cast<int64_t>(ws.max_chunks) * 16);
     int item = blockIdx.x;
     if (item >= total) return;
-
-    IntraIn<DK, DV, TIn> X;
-    {
-        const int4 info = table[item / H];
-        intra_fetch(X, a, info.y, info.z, item % H, wave, lane);
-    }
-    // the table entry of the item after next is read one iteration ahead of its use;
-    // fetches past the last item repeat a valid one and are never used
-    int nxt = item + stride < total ? item + stride : item;
-    int4 nxt_info = table[nxt / H];
+    u32x4 info = __builtin_amdgcn_raw_buffer_load_b128(rtab, (item / H) * 16, 0, 0);
     for (; item < total; item += stride) {
-        const IntraIn<DK, DV, TIn> Y = X;
-        intra_fetch(X, a, nxt_info.y, nxt_info.z, nxt % H, wave, lane);
-        const int nn = nxt + stride < total ? nxt + stride : nxt;
-        const int4 nn_info = table[nn / H];
-        char* rec = recs + ws.rec_bytes * static_cast<size_t>(item);
-        intra_compute(Y, smem, a, rec, ws, wave, lane, tid);
-        nxt = nn;
-        nxt_info = nn_info;
+        IntraIn<DK, DV, TIn> X;
+        intra_fetch(X, a, __builtin_amdgcn_readfirstlane(info[1]), __builtin_amdgcn_readfirstlane(info[2]), item % H,
+                    wave, lane);
+        const int nxt = item + stride < total ? item + stride : item;
+        info = __builtin_amdgcn_raw_buffer_load_b128(rtab, (nxt / H) * 16, 0, 0);
+        intra_compute(X, smem, a, recs + ws.rec_bytes * static_cast<size_t>(item), ws, wave, lane, tid);
     }
 }
 
@@ -764,8 +763,15 @@ struct SegPlan {
     static constexpr int SJB = NCB / WPC;                    // state column blocks per wave
     static constexpr size_t O_SX = 0, O_UX = 16ull * GK * NCB * 64;
     static constexpr size_t BYTES = O_UX + 16ull * GT * NCB * 64;
+    static constexpr bool fits = BYTES <= 160 * 1024;
     static_assert(8 % KB == 0 && NCB % WPC == 0, "segment plan");
 };
+
+// The prefill supports a shape when every kernel's LDS plan fits a CU (fp32 inputs: dk = 64).
+template <int DK, int DV, class TIn>
+constexpr bool prefill_fits() {
+    return IntraPlan<DK, DV, TIn>::fits && SegPlan<DK, DV, TIn, kLocal>::fits && SegPlan<DK, DV, TIn, kOut>::fits;
+}
 
 // One chunk's operands for one wave.
 template <class SP>
@@ -1119,7 +1125,7 @@ int device_cu_count() {
 
 template <int DK, int DV, class TIn>
 hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t stream) {
-    if constexpr (!IntraPlan<DK, DV, TIn>::fits) {
+    if constexpr (!prefill_fits<DK, DV, TIn>()) {
         return hipErrorInvalidConfiguration;
     } else {
         constexpr int E = Geo<TIn>::E;
@@ -1130,8 +1136,8 @@ hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t stream) {
                            reinterpret_cast<int4*>(base + ws.off_table), reinterpret_cast<int4*>(base + ws.off_segtab));
         const int64_t items = ws.max_chunks * a.H;
         if (items > 0) {
-            const int cus = device_cu_count();
-            const int grid = static_cast<int>(items < cus ? items : cus);
+            const int slots = 2 * device_cu_count();
+            const int grid = static_cast<int>(items < slots ? items : slots);
             hipLaunchKernelGGL((chunk_intra_kernel<DK, DV, TIn>), dim3(grid), dim3(kThreads), 0, stream, a);
             const dim3 sgrid(static_cast<unsigned>(ws.max_segs * a.H));
             hipLaunchKernelGGL((seg_carry_kernel<DK, DV, TIn, kLocal, kCarryNB>), sgrid, dim3(kSegThreads), 0,
@@ -1163,10 +1169,10 @@ size_t prefill_workspace_bytes(int num_seqs, int64_t total_tokens, int H, int dk
 
 bool prefill_supported(int bf16, int dk, int dv) {
     if (bf16) return true;
-    if (dk == 64 && dv == 64) return IntraPlan<64, 64, F32>::fits;
-    if (dk == 64 && dv == 128) return IntraPlan<64, 128, F32>::fits;
-    if (dk == 128 && dv == 64) return IntraPlan<128, 64, F32>::fits;
-    return IntraPlan<128, 128, F32>::fits;
+    if (dk == 64 && dv == 64) return prefill_fits<64, 64, F32>();
+    if (dk == 64 && dv == 128) return prefill_fits<64, 128, F32>();
+    if (dk == 128 && dv == 64) return prefill_fits<128, 64, F32>();
+    return prefill_fits<128, 128, F32>();
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, int bf16, int dk, int dv, hipStream_t stream) {
