@@ -132,8 +132,8 @@ size_t kda_chunk_prefill_workspace_size(int num_seqs, int64_t total_tokens, int 
  *   o           [total_tokens, H, dv] dtype (output)
  *   workspace   device buffer of at least kda_chunk_prefill_workspace_size(...) bytes;
  *               its contents on entry do not matter.
- * Limits: H <= 65535 and (total_tokens / 64 + num_seqs) * H < 2^31, else
- * KDA_ERR_INVALID_ARG.
+ * Limits: H <= 65535 and (total_tokens / 64 + num_seqs) * H <= 2^22, else
+ * KDA_ERR_INVALID_ARG (2^22 items take 176 GB of workspace or more).
  */
 int kda_chunk_prefill(const void* q, const void* k, const void* v, int dtype, const float* g,
                       const float* beta, const int32_t* cu_seqlens, int num_seqs,

@@ -96,9 +96,11 @@ KDA_EXPORT int kda_chunk_prefill(const void* q, const void* k, const void* v, in
     if (!supported_dim(dk) || !supported_dim(dv)) return KDA_ERR_UNSUPPORTED;
     if (!kda::prefill_supported(dtype == KDA_BF16, dk, dv)) return KDA_ERR_UNSUPPORTED;
     if (total_tokens > (1ll << 31) - 1) return KDA_ERR_INVALID_ARG;  // int32 cu_seqlens
-    // 32-bit per-chunk buffer offsets and (chunk, head) item counts
+    // (chunk, head) items: 32-bit counts and offsets, and every launch's work-item count
+    // within 32 bits (the segment kernels run one 512-thread block per (segment, head));
+    // 2^22 items already take 176 GB of workspace or more
     if (H > 65535) return KDA_ERR_INVALID_ARG;
-    if (checked_mul(total_tokens / 64 + num_seqs, H) > (1ll << 31) - 1) return KDA_ERR_INVALID_ARG;
+    if (checked_mul(total_tokens / 64 + num_seqs, H) > (1ll << 22)) return KDA_ERR_INVALID_ARG;
     if (checked_mul(checked_mul(total_tokens, H), 2 * dk + dv) < 0) return KDA_ERR_INVALID_ARG;
     if (checked_mul(checked_mul(num_slots, H), static_cast<int64_t>(dk) * dv) < 0)
         return KDA_ERR_INVALID_ARG;

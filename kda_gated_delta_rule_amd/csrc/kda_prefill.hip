@@ -786,9 +786,9 @@ struct SegOps {
 template <class SP>
 __device__ __forceinline__ void seg_fetch(SegOps<SP>& F, const char* rec, const WsLayout& ws, int tb, int task,
                                           int cb, int lane) {
-    // task (wave-uniform): 0 = U (W, Ut), 1 = O (QG, P), 2 = none
-    if (task < 2) {
-        const char* ab = rec + (task ? ws.o_q : ws.o_w);
+    // task (wave-uniform): 0 = U (W, Ut), 1 = O (QG, P), 2 = W alone (the Phi columns' U)
+    {
+        const char* ab = rec + (task == 1 ? ws.o_q : ws.o_w);
 #pragma unroll
         for (int g = 0; g < SP::GK; ++g)
             F.a[g] = *reinterpret_cast<const u32x4*>(ab + ((static_cast<size_t>(tb) * SP::GK + g) * 64 + lane) * 16);
@@ -870,7 +870,7 @@ __device__ __forceinline__ void seg_step(const SegOps<SegPlan<DK, DV, TIn, MODE>
         lds_tile_to_gran(sx, ((cb / SP::CT) * SP::NCB + jb0 + j) * 64 + lane, cb % SP::CT, S[j], tag);
     lds_barrier();
 
-    // (2) the token block's U (part 0), O [OUT] or Phi-column U [LOCAL] (part 1)
+    // (2) the token block's U (part 0), and QG S [OUT] or the Phi columns' U [LOCAL] (part 1)
     auto prod = [&](int jb) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -888,8 +888,10 @@ __device__ __forceinline__ void seg_step(const SegOps<SegPlan<DK, DV, TIn, MODE>
             for (int rr = 0; rr < 4; ++rr) uv[rr] = uo_val(F.uo[jb / SP::TB], jb % SP::TB, rr, tag) - acc[rr];
             lds_tile_to_gran(ux, ug + jb * 64, uh, uv, tag);
         }
-        if constexpr (MODE == kLocal) {
-            // the Phi columns' U (no Ut term) by the same wave, so W is loaded once
+    }
+    if constexpr (MODE == kLocal) {
+        // the Phi columns' U (no Ut term)
+        if (part == 1) {
 #pragma unroll
             for (int jb = SP::VB; jb < SP::NCB; ++jb) lds_tile_to_gran(ux, ug + jb * 64, uh, -prod(jb), tag);
         }
@@ -1025,14 +1027,13 @@ __global__ __launch_bounds__(kSegThreads) void seg_carry_kernel(PrefillArgs a) {
 // seg_scan: one workgroup (4 waves) per (sequence, head, 16-column tile).  Wave w owns
 // the tile's rows 16 (RW w + i) .. + 15.  X (fp32) -> S_start of each segment; X =
 // Phi X + S_loc on fp32 MFMA, X crossing the waves through LDS transposed.
+// One column tile of the segment scan of one (sequence, head): walks the segments in
+// order, storing S_start(k) and forming S_start(k+1) = Phi_k S_start(k) + S_loc(k).
 template <int DK, int DV, int E>
-__global__ __launch_bounds__(kThreads) void seg_scan_kernel(PrefillArgs a) {
-    constexpr int NTS = DV / 16, KB = DK / 16, RW = KB / 4, LDX = DK + 4;
-    __shared__ __attribute__((aligned(16))) float xs[16 * LDX];  // X^T [16 columns][DK]
-    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+__device__ __forceinline__ void scan_group(const PrefillArgs& a, int group, int tile, float* xs, int lane, int wave) {
+    constexpr int KB = DK / 16, RW = KB / 4, LDX = DK + 4;
+    const int H = a.H;
     const int r = lane & 15, q4 = 4 * (lane >> 4);
-    const int H = a.H, b = blockIdx.x, tile = b % NTS, group = b / NTS;
-    if (group >= a.num_seqs * H) return;
     const int seq = group / H, h = group % H;
     const WsLayout ws(a.num_seqs, a.total_tokens, H, DK, DV, E);
     const char* base = static_cast<const char*>(a.workspace);
@@ -1077,8 +1078,12 @@ __global__ __launch_bounds__(kThreads) void seg_scan_kernel(PrefillArgs a) {
             for (int rr = 0; rr < 4; ++rr) o.sl[i][rr] = Sl[(16 * rb + q4 + rr) * DV + col];
         }
     };
-    Ops cur;
-    if (nseg > 1) load(cur, 0);
+    // two segments in flight: the loads of step k + 2 are issued before step k's products
+    Ops cur, nx1;
+    if (nseg > 1) {
+        load(cur, 0);
+        load(nx1, min(1, nseg - 2));
+    }
     for (int k = 0; k < nseg; ++k) {
         float* Ss = reinterpret_cast<float*>(blk_of(k) + ws.s_start);
 #pragma unroll
@@ -1086,8 +1091,8 @@ __global__ __launch_bounds__(kThreads) void seg_scan_kernel(PrefillArgs a) {
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) Ss[(16 * (RW * wave + i) + q4 + rr) * DV + col] = X[i][rr];
         if (k == nseg - 1) break;
-        Ops nxt;
-        load(nxt, min(k + 1, nseg - 2));  // the last segment has no transition; repeat a valid one
+        Ops nx2;
+        load(nx2, min(k + 2, nseg - 2));  // the last segment has no transition; repeat a valid one
 #pragma unroll
         for (int i = 0; i < RW; ++i)
             *reinterpret_cast<f32x4*>(xs + r * LDX + 16 * (RW * wave + i) + q4) = X[i];
@@ -1106,7 +1111,24 @@ __global__ __launch_bounds__(kThreads) void seg_scan_kernel(PrefillArgs a) {
             X[i] = acc;
         }
         lds_barrier();
-        cur = nxt;
+        cur = nx1;
+        nx1 = nx2;
+    }
+}
+
+template <int DK, int DV, int E>
+__global__ __launch_bounds__(kThreads) void seg_scan_kernel(PrefillArgs a) {
+    constexpr int NTS = DV / 16, LDX = DK + 4;
+    __shared__ __attribute__((aligned(16))) float xs[16 * LDX];  // X^T [16 columns][DK]
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    // The NTS column tiles of one (sequence, head) all read the same Phi blocks: they get
+    // virtual block ids congruent mod kNumXcd, so they run on one XCD and share its L2
+    // (the grid is a multiple of kNumXcd, so the grid stride keeps the congruence).
+    const int H = a.H, NG = a.num_seqs * H;
+    const int nvb = (NG + kNumXcd - 1) / kNumXcd * kNumXcd * NTS;
+    for (int vb = blockIdx.x; vb < nvb; vb += gridDim.x) {
+        const int j = vb / kNumXcd, tile = j % NTS, group = (j / NTS) * kNumXcd + vb % kNumXcd;
+        if (group < NG) scan_group<DK, DV, E>(a, group, tile, xs, lane, wave);
     }
 }
 
@@ -1143,8 +1165,11 @@ hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t stream) {
             hipLaunchKernelGGL((seg_carry_kernel<DK, DV, TIn, kLocal, kCarryNB>), sgrid, dim3(kSegThreads), 0,
                                stream, a);
         }
-        hipLaunchKernelGGL((seg_scan_kernel<DK, DV, E>), dim3(a.num_seqs * a.H * (DV / 16)), dim3(kThreads), 0, stream,
-                           a);
+        // one block per (sequence, head, 16-column tile), padded to whole XCD groups;
+        // beyond 4096 such groups the blocks loop
+        const int groups = (a.num_seqs * a.H + kNumXcd - 1) / kNumXcd;
+        const int sblocks = (groups < 4096 ? groups : 4096) * kNumXcd * (DV / 16);
+        hipLaunchKernelGGL((seg_scan_kernel<DK, DV, E>), dim3(sblocks), dim3(kThreads), 0, stream, a);
         if (items > 0)
             hipLaunchKernelGGL((seg_carry_kernel<DK, DV, TIn, kOut, kCarryNB>),
                                dim3(static_cast<unsigned>(ws.max_segs * a.H)), dim3(kSegThreads), 0, stream, a);
