@@ -274,6 +274,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--decode-only", action="store_true",
                     help="measure only the decode step and the copy reference (for counter runs)")
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="measure only the copy reference and the two prefill workloads (for counter "
+                         "runs); prints their figures without the headline metric")
     ap.add_argument("--quiet", action="store_true")
     args = ap.parse_args()
 
@@ -295,6 +298,13 @@ def main():
     kda.load()
     dev = torch.device("cuda:0")
     log("device: %s" % torch.cuda.get_device_name(0))
+
+    if args.prefill_only:
+        extra = {"copy_reference": bench_copy(dev, log),
+                 "prefill": bench_prefill(args, dev, log, "prefill"),
+                 "prefill_varlen": bench_prefill(args, dev, log, "varlen")}
+        print(json.dumps({"mode": "prefill-only", "extra": extra}))
+        return
 
     dec = bench_decode(args, dev, log)
     value = dec["updates"] * args.steps / dec["total"]
