@@ -69,12 +69,15 @@ def test_decode_pool_full_size(seed):
     assert torch.equal(got[untouched], x["pool"][untouched])
 
 
+@pytest.mark.parametrize("T", [1, 3])
 @pytest.mark.parametrize("dk,dv", [(64, 64), (64, 128), (128, 64)])
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
-def test_decode_head_dims(dk, dv, dtype):
+def test_decode_head_dims(dk, dv, dtype, T):
+    """Both decode kernels (T = 1: four-wave tiles; T > 1: one-wave tiles) at every head
+    shape."""
     dev = need_gpu()
-    announce("decode dims dk=%d dv=%d %s" % (dk, dv, dtype))
-    x = W.decode(seed=3, N=5, T=3, H=3, dk=dk, dv=dv, num_slots=9, dtype=dtype)
+    announce("decode dims dk=%d dv=%d %s T=%d" % (dk, dv, dtype, T))
+    x = W.decode(seed=3, N=5, T=T, H=3, dk=dk, dv=dv, num_slots=9, dtype=dtype)
     o, pool, _ = run_decode(x, dev)
     o_ref, h_ref, _ = oracle_decode(x)
     tol = 1e-4 if dtype == torch.float32 else 1e-2
@@ -118,11 +121,12 @@ def test_slot_mapping_bit_exact(dtype):
     assert torch.equal(pool_after.cpu(), pool)
 
 
-def test_skipped_slot():
+@pytest.mark.parametrize("T", [1, 2])
+def test_skipped_slot(T):
     """A negative slot index skips the sequence: zero output, pool untouched."""
     dev = need_gpu()
-    announce("decode skipped slot")
-    x = W.decode(seed=5, N=4, T=2, H=2, dk=128, dv=128, num_slots=8)
+    announce("decode skipped slot T=%d" % T)
+    x = W.decode(seed=5, N=4, T=T, H=2, dk=128, dv=128, num_slots=8)
     x["slot_idx"][2] = -1
     o, pool, _ = run_decode(x, dev)
     assert torch.count_nonzero(o[2]).item() == 0
@@ -165,12 +169,16 @@ def test_verify_and_replay_full_size(seed):
     assert torch.equal(got[others], x["pool"][others])
 
 
-def test_replay_bit_exact_with_commit():
+@pytest.mark.parametrize("dk,dv", [(128, 128), (64, 64), (128, 64)])
+def test_replay_bit_exact_with_commit(dk, dv):
     """Replaying a prefix of verify records reproduces, bit for bit, the state that committing
-    the same tokens with the decode kernel gives (same fp32 operations)."""
+    the same tokens with the decode kernels gives (same fp32 operations; accepted lengths of
+    1 commit through the T = 1 kernel, longer ones through the T > 1 kernel, both against
+    records written by the T > 1 kernel)."""
     dev = need_gpu()
-    announce("replay vs commit bit-exact")
-    x = W.verify(seed=3, N=12, H=4, num_slots=32)
+    announce("replay vs commit bit-exact dk=%d dv=%d" % (dk, dv))
+    x = W.verify(seed=3, N=12, H=4, dk=dk, dv=dv, num_slots=32)
+    x["accepted"][0], x["accepted"][1] = 1, 8  # both kernels on the commit side
     _, pool_v, rec = run_decode(x, dev, records=True)
     acc = x["accepted"]
     kda.replay_commit(pool_v, x["slot_idx"].to(dev), rec, acc.to(dev))
