@@ -282,16 +282,18 @@ __global__ __launch_bounds__(kThreads) void chunk_map_kernel(const int32_t* __re
     block_exclusive_scan(num_seqs, nchunks, chunk_off, part, &carry);
     block_exclusive_scan(num_seqs, [&](int i) { return (nchunks(i) + seg_chunks - 1) / seg_chunks; }, seg_off, part,
                          &carry);
-    const int tid = threadIdx.x;
-    for (int i = 0; i < num_seqs; ++i) {
+    // one wave per sequence (its lanes over the sequence's chunks and segments), so the
+    // sequences' offset loads overlap instead of forming one chain
+    const int lane = threadIdx.x % kWave;
+    for (int i = threadIdx.x / kWave; i < num_seqs; i += kThreads / kWave) {
         const int bos = cu[i], eos = cu[i + 1];
         const int first = chunk_off[i], nch = chunk_off[i + 1] - first;
-        for (int c = tid; c < nch; c += kThreads) {
+        const int s0 = seg_off[i], ns = seg_off[i + 1] - s0;
+        for (int c = lane; c < nch; c += kWave) {
             const int t0 = bos + c * kChunk;
             table[first + c] = make_int4(i, t0, min(kChunk, eos - t0), 0);
         }
-        const int s0 = seg_off[i], ns = seg_off[i + 1] - s0;
-        for (int k = tid; k < ns; k += kThreads)
+        for (int k = lane; k < ns; k += kWave)
             segtab[s0 + k] = make_int4(i, first + k * seg_chunks, min(seg_chunks, nch - k * seg_chunks),
                                        2 * k + (k == ns - 1 ? 1 : 0));
     }
