@@ -111,6 +111,22 @@ def test_bf16_multi_segment(h0):
     assert rel_l2(f64(pool.cpu()[y["slot_idx"].long()]), h_ref) <= 1e-2
 
 
+def test_many_short_sequences_scan_grid_loops():
+    """520 sequences x 64 heads = 33,280 (sequence, head) scan groups, more than the scan
+    launch covers at once (4,096 groups of 8), so its blocks loop; lengths 0..70 (empty,
+    single-token, one- and two-chunk sequences), h0 from slots, bf16 dk = dv = 64."""
+    dev = need_gpu()
+    announce("prefill 520 short sequences x 64 heads")
+    gen = np.random.default_rng(11)
+    lens = gen.choice([0, 1, 2, 3, 5, 17, 63, 64, 65, 70], size=520).tolist()
+    y = W.prefill(seed=9, seqlens=tuple(lens), H=64, dk=64, dv=64, num_slots=520, h0_std=0.05)
+    assert 520 * 64 > 4096 * 8
+    o, pool = run_prefill(y, dev)
+    o_ref, h_ref, _ = oracle_prefill(y)
+    assert rel_l2(f64(o), o_ref) <= 1e-2
+    assert rel_l2(f64(pool.cpu()[y["slot_idx"].long()]), h_ref) <= 1e-2
+
+
 def test_zero_initial_state_ignores_pool_contents():
     dev = need_gpu()
     announce("prefill h0 zero")
