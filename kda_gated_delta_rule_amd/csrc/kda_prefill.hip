@@ -189,13 +189,14 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, int
 //     Phi   [DK][DK]   the segment's transition (S_end = Phi S_start + S_loc)
 //     S_start [DK][DV] state entering the segment
 // A segment is up to seg_chunks consecutive chunks of one sequence: 16, doubled
-// (up to 64) while the batch would give more than 1024 (segment, head) pairs, so
-// small batches still spread over every compute unit and long ones keep the
-// sequential scan short.
+// (up to 128) while the batch would give more than 256 (segment, head) pairs, i.e.
+// about one segment workgroup per compute unit.  Small batches still spread over
+// every CU; long ones get fewer, longer segments: a shorter sequential scan, and
+// more of the work in each sequence's last segment, which the local pass skips.
 // ---------------------------------------------------------------------------
 __host__ __device__ inline int seg_chunks_for(int64_t total_tokens, int H) {
     int seg = 16;
-    while (seg < 64 && total_tokens / kChunk / seg * H > 1024) seg *= 2;
+    while (seg < 128 && total_tokens / kChunk / seg * H > 256) seg *= 2;
     return seg;
 }
 

@@ -79,9 +79,10 @@ def test_bf16_varlen_ragged(dk, dv):
     assert torch.equal(got[others], y["pool"][others])
 
 
-# Sequences longer than one 32-chunk segment go through the segment scan: a local pass
-# from [0 | I], the fp32 scan of segment start states, and the output pass.  Lengths
-# cover 1-chunk tail segments, exact multiples of the segment and of the chunk.
+# Sequences longer than one segment (16 chunks at these sizes) go through the segment
+# scan: a local pass from [0 | I], the fp32 scan of segment start states, and the output
+# pass.  Lengths cover 1-chunk tail segments, exact multiples of the segment and of the
+# chunk.
 MULTI_SEG = (4200, 2049, 64, 0, 4097, 2048)
 
 
