@@ -1027,14 +1027,15 @@ __global__ __launch_bounds__(kSegThreads) void seg_carry_kernel(PrefillArgs a) {
     }
 }
 
-// seg_scan: one workgroup (4 waves) per (sequence, head, 16-column tile).  Wave w owns
-// the tile's rows 16 (RW w + i) .. + 15.  X (fp32) -> S_start of each segment; X =
-// Phi X + S_loc on fp32 MFMA, X crossing the waves through LDS transposed.
+// seg_scan: one workgroup of DK / 16 waves per (sequence, head, 16-column tile); wave w
+// owns the tile's rows 16 w .. 16 w + 15 (one row block, so each wave's chain of
+// dependent fp32 MFMAs per segment step is DK / 4 long).  X (fp32) -> S_start of each
+// segment; X = Phi X + S_loc on fp32 MFMA, X crossing the waves through LDS transposed.
 // One column tile of the segment scan of one (sequence, head): walks the segments in
 // order, storing S_start(k) and forming S_start(k+1) = Phi_k S_start(k) + S_loc(k).
 template <int DK, int DV, int E>
 __device__ __forceinline__ void scan_group(const PrefillArgs& a, int group, int tile, float* xs, int lane, int wave) {
-    constexpr int KB = DK / 16, RW = KB / 4, LDX = DK + 4;
+    constexpr int KB = DK / 16, RW = 1, LDX = DK + 4;  // one row block per wave
     const int H = a.H;
     const int r = lane & 15, q4 = 4 * (lane >> 4);
     const int seq = group / H, h = group % H;
@@ -1081,21 +1082,17 @@ __device__ __forceinline__ void scan_group(const PrefillArgs& a, int group, int 
             for (int rr = 0; rr < 4; ++rr) o.sl[i][rr] = Sl[(16 * rb + q4 + rr) * DV + col];
         }
     };
-    // two segments in flight: the loads of step k + 2 are issued before step k's products
-    Ops cur, nx1;
-    if (nseg > 1) {
-        load(cur, 0);
-        load(nx1, min(1, nseg - 2));
-    }
-    for (int k = 0; k < nseg; ++k) {
+    // Two segments in flight: step k uses the operands loaded two steps earlier and issues
+    // the loads of step k + 2.  The three operand sets rotate by name (the loop is unrolled
+    // three times), so no register copy forces a wait for loads still in flight.
+    auto step = [&](int k, const Ops& cur, Ops& fill) {
         float* Ss = reinterpret_cast<float*>(blk_of(k) + ws.s_start);
 #pragma unroll
         for (int i = 0; i < RW; ++i)
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) Ss[(16 * (RW * wave + i) + q4 + rr) * DV + col] = X[i][rr];
-        if (k == nseg - 1) break;
-        Ops nx2;
-        load(nx2, min(k + 2, nseg - 2));  // the last segment has no transition; repeat a valid one
+        if (k == nseg - 1) return false;
+        load(fill, min(k + 2, nseg - 2));  // the last segment has no transition; repeat a valid one
 #pragma unroll
         for (int i = 0; i < RW; ++i)
             *reinterpret_cast<f32x4*>(xs + r * LDX + 16 * (RW * wave + i) + q4) = X[i];
@@ -1114,13 +1111,22 @@ __device__ __forceinline__ void scan_group(const PrefillArgs& a, int group, int 
             X[i] = acc;
         }
         lds_barrier();
-        cur = nx1;
-        nx1 = nx2;
+        return true;
+    };
+    Ops o0, o1, o2;
+    if (nseg > 1) {
+        load(o0, 0);
+        load(o1, min(1, nseg - 2));
+    }
+    for (int k = 0;; k += 3) {
+        if (!step(k, o0, o2)) break;
+        if (!step(k + 1, o1, o0)) break;
+        if (!step(k + 2, o2, o1)) break;
     }
 }
 
 template <int DK, int DV, int E>
-__global__ __launch_bounds__(kThreads) void seg_scan_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(64 * (DK / 16)) void seg_scan_kernel(PrefillArgs a) {
     constexpr int NTS = DV / 16, LDX = DK + 4;
     __shared__ __attribute__((aligned(16))) float xs[16 * LDX];  // X^T [16 columns][DK]
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1172,7 +1178,7 @@ hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t stream) {
         // beyond 4096 such groups the blocks loop
         const int groups = (a.num_seqs * a.H + kNumXcd - 1) / kNumXcd;
         const int sblocks = (groups < 4096 ? groups : 4096) * kNumXcd * (DV / 16);
-        hipLaunchKernelGGL((seg_scan_kernel<DK, DV, E>), dim3(sblocks), dim3(kThreads), 0, stream, a);
+        hipLaunchKernelGGL((seg_scan_kernel<DK, DV, E>), dim3(sblocks), dim3(64 * (DK / 16)), 0, stream, a);
         if (items > 0)
             hipLaunchKernelGGL((seg_carry_kernel<DK, DV, TIn, kOut, kCarryNB>),
                                dim3(static_cast<unsigned>(ws.max_segs * a.H)), dim3(kSegThreads), 0, stream, a);
