@@ -80,6 +80,8 @@ typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
  *   T >= 1 tokens per sequence (T = 1 decode, T > 1 MTP / speculative verify).
  *   scale       output scale (1/sqrt(dk) is the usual choice).
  *   use_qk_l2norm  1: normalise q and k as above; 0: use them as given.
+ * Limit: N * H <= 2^22 (a launch's work-item count stays within 32 bits; 2^22 (sequence,
+ * head) states are 256 GiB at dk = dv = 128), else KDA_ERR_INVALID_ARG.
  */
 int kda_decode_step(const void* q, const void* k, const void* v, int dtype, const float* g,
                     const float* beta, float* state_pool, int64_t num_slots,
@@ -99,6 +101,7 @@ int kda_decode_step(const void* q, const void* k, const void* v, int dtype, cons
  * on the device, each in 0..T (0 leaves the slot untouched; values outside 0..T are
  * undefined behaviour).  The fp32 arithmetic matches commit-mode kda_decode_step, so
  * replaying a prefix reproduces the state that committing the same tokens gives.
+ * Limit: N * H <= 2^22, as for kda_decode_step.
  */
 int kda_replay_commit(float* state_pool, int64_t num_slots, const int32_t* slot_idx,
                       const float* records, const int32_t* accepted_len, int N, int T, int H,

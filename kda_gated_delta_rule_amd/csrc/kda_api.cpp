@@ -46,7 +46,8 @@ KDA_EXPORT int kda_decode_step(const void* q, const void* k, const void* v, int 
     if (tokens < 0 || checked_mul(tokens, 2 * dk + dv) < 0) return KDA_ERR_INVALID_ARG;
     if (checked_mul(checked_mul(num_slots, H), static_cast<int64_t>(dk) * dv) < 0)
         return KDA_ERR_INVALID_ARG;
-    if (checked_mul(N, H) > (1ll << 30)) return KDA_ERR_INVALID_ARG;  // grid size
+    // launch size: up to 2 dv tiles per head, 256 threads each, within 32-bit work-items
+    if (checked_mul(N, H) > (1ll << 22)) return KDA_ERR_INVALID_ARG;
     if (N == 0) return KDA_OK;
 
     kda::DecodeArgs a{q, k, v, g, beta, state_pool, slot_idx, o, records,
@@ -66,7 +67,7 @@ KDA_EXPORT int kda_replay_commit(float* state_pool, int64_t num_slots, const int
     if (tokens < 0 || checked_mul(tokens, 2 * dk + dv) < 0) return KDA_ERR_INVALID_ARG;
     if (checked_mul(checked_mul(num_slots, H), static_cast<int64_t>(dk) * dv) < 0)
         return KDA_ERR_INVALID_ARG;
-    if (checked_mul(N, H) > (1ll << 30)) return KDA_ERR_INVALID_ARG;
+    if (checked_mul(N, H) > (1ll << 22)) return KDA_ERR_INVALID_ARG;  // as for decode
     if (N == 0) return KDA_OK;
 
     kda::ReplayArgs a{state_pool, slot_idx, records, accepted_len, N, T, H};

@@ -61,6 +61,7 @@ def decode_args(**over):
     (dict(T=0), _lib.KDA_ERR_INVALID_ARG),
     (dict(H=0), _lib.KDA_ERR_INVALID_ARG),
     (dict(N=-1), _lib.KDA_ERR_INVALID_ARG),
+    (dict(N=(1 << 21) + 1), _lib.KDA_ERR_INVALID_ARG),  # N * H above 2^22 (H = 2)
     (dict(num_slots=0), _lib.KDA_ERR_INVALID_ARG),
     (dict(l2=2), _lib.KDA_ERR_INVALID_ARG),
     (dict(scale=float("nan")), _lib.KDA_ERR_INVALID_ARG),
@@ -79,6 +80,7 @@ def test_decode_validation(lib, over, code):
     (dict(acc=A + 4), _lib.KDA_ERR_INVALID_ARG),
     (dict(T=0), _lib.KDA_ERR_INVALID_ARG),
     (dict(dk=32), _lib.KDA_ERR_UNSUPPORTED),
+    (dict(N=(1 << 21) + 1), _lib.KDA_ERR_INVALID_ARG),  # N * H above 2^22 (H = 2)
     (dict(N=0), _lib.KDA_OK),
 ])
 def test_replay_validation(lib, over, code):
