@@ -148,6 +148,45 @@ def test_beta0_g0_keeps_the_state_exactly(dtype, d):
     assert rel_l2(f64(o), o_ref) <= (1e-4 if dtype == torch.float32 else 1e-2)
 
 
+@pytest.mark.parametrize("h0", [True, False])
+def test_all_sequences_empty(h0):
+    """Every sequence empty (no chunks: only the scan's pass-through runs): the final state
+    is the initial one (h0 from the slot) or zero; other slots are untouched."""
+    dev = need_gpu()
+    announce("prefill all sequences empty h0_from_pool=%d" % h0)
+    y = W.prefill(seed=12, seqlens=(0, 0, 0), H=2, dk=128, dv=128, num_slots=5, h0_std=0.3)
+    o, pool = run_prefill(y, dev, h0_from_pool=h0)
+    assert o.shape[0] == 0
+    got, sl = pool.cpu(), y["slot_idx"].long()
+    if h0:
+        assert torch.equal(got[sl], y["pool"][sl])
+    else:
+        assert torch.count_nonzero(got[sl]).item() == 0
+    others = torch.ones(5, dtype=torch.bool)
+    others[sl] = False
+    assert torch.equal(got[others], y["pool"][others])
+
+
+def test_workspace_reused_across_calls():
+    """One workspace buffer (filled with garbage first) serves two calls of different shapes
+    in a row; its contents on entry do not matter."""
+    dev = need_gpu()
+    announce("prefill workspace reuse")
+    ya = W.prefill(seed=13, seqlens=(300, 1500), H=2, dk=128, dv=128, num_slots=2, h0_std=0.05)
+    yb = W.prefill(seed=14, seqlens=(70, 5, 64), H=2, dk=128, dv=128, num_slots=3, h0_std=0.05)
+    need = max(kda.chunk_prefill_workspace_size(2, 1800, 2, 128, 128),
+               kda.chunk_prefill_workspace_size(3, 139, 2, 128, 128))
+    ws = torch.full((need,), 0xAB, dtype=torch.uint8, device=dev)
+    for y in (ya, yb):
+        pool = y["pool"].to(dev)
+        o = kda.chunk_prefill(*(y[n].to(dev) for n in NAMES), y["cu_seqlens"].to(dev), pool,
+                              y["slot_idx"].to(dev), workspace=ws)
+        torch.cuda.synchronize()
+        o_ref, h_ref, _ = oracle_prefill(y)
+        assert rel_l2(f64(o), o_ref) <= 1e-2
+        assert rel_l2(f64(pool.cpu()[y["slot_idx"].long()]), h_ref) <= 1e-2
+
+
 def test_zero_initial_state_ignores_pool_contents():
     dev = need_gpu()
     announce("prefill h0 zero")
