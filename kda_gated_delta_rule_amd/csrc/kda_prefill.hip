@@ -11,26 +11,28 @@
 //   P_ts =        sum_c qh_tc kh_sc exp(G_tc - G_sc)   (s <= t)    "QK^T" with decay
 //   T = (I + A)^-1,  W = T diag(beta) kh exp(G),  Ut = T diag(beta) V   (UT transform)
 //   U  = Ut - W S0
-//   O  = scale ((qh exp(G) - P W) S0 + P Ut)  =  scale (Q' S0 + Ot)
+//   O  = scale (QG S0 + P U),   QG = qh exp(G)
 //   S  = diag(exp(G_L)) S0 + (kh exp(G_L - G))^T U
 //
-// Three kernels:
-//   1. chunk_map    cu_seqlens -> per-sequence chunk offsets and a chunk table
-//                   (sequence, first token, length); chunks restart at every
-//                   sequence start, the last one may be short.
-//   2. chunk_intra  persistent workgroups walking the (chunk, head) items, the next
-//                   item's inputs loaded into registers while the current one is
-//                   computed: Q/K norm, gate cumsum (DPP scan), A and P on MFMA,
-//                   T by blocked substitution in fp32, W, Ut, Q' and Ot on MFMA;
-//                   writes W, Q', Kt = (kh exp(G_L - G))^T, Ut, Ot and exp(G_L)
-//                   to a per-(chunk, head) workspace record.
-//   3. chunk_carry  one workgroup per (sequence, head, 32-column dv tile),
-//                   sequential over the sequence's chunks: U = Ut - W S,
-//                   O = scale (Q' S + Ot), S = exp(G_L) S + Kt U, all on MFMA;
-//                   the fp32 state stays in registers and is written to its slot
-//                   at the end.
+// Five launches on the caller's stream:
+//   1. chunk_map    cu_seqlens -> per-sequence chunk and segment offsets, the chunk
+//                   table (sequence, first token, length; chunks restart at every
+//                   sequence start, the last one may be short) and the segment table.
+//   2. chunk_intra  persistent, two workgroups per CU walking the (chunk, head) items:
+//                   Q/K norm, gate cumsum (DPP scan), A and P on MFMA, T by blocked
+//                   substitution in fp32, W and Ut on MFMA; writes W, QG, Kt =
+//                   (kh exp(G_L - G))^T, Ut, P and exp(G_L) to a per-(chunk, head)
+//                   workspace record.
+//   3. seg_carry<LOCAL>  the chunk map is affine in S, so a segment of chunks maps its
+//                   entering state to Phi S_start + S_loc: per (segment, head), the chunk
+//                   steps on [S | Phi] from [0 | I] (section 3 below).
+//   4. seg_scan     per (sequence, head, 16-column tile): S_start(k + 1) = Phi_k
+//                   S_start(k) + S_loc(k) in fp32, from the initial state.
+//   5. seg_carry<OUT>  per (segment, head): the chunk steps from S_start, writing O and,
+//                   for a sequence's last segment, the final state to its slot.
+// Every product of the carries is on MFMA with the fp32 state in registers.
 //
-// The record is stored in the carry's MFMA fragment order ("granules": the 16
+// The record is stored in the carries' MFMA fragment order ("granules": the 16
 // bytes one lane feeds one MFMA k-step, 64 lanes contiguous), so every carry
 // load is a contiguous 1 KiB per wave, and the chunk_intra kernel produces most
 // granules straight from its MFMA accumulators: a 16x16 accumulator tile holds
@@ -55,7 +57,7 @@ namespace {
 
 constexpr int kChunk = 64;
 constexpr int kThreads = 256;
-constexpr int kCarryBV = 32;  // dv columns per carry workgroup
+constexpr int kCarryBV = 32;  // dv columns per Ut record tile
 constexpr int kCarryNB = 2;   // chunks whose operands the carry has in flight
 constexpr int kNumXcd = 8;    // MI355X: 8 XCDs, workgroups dispatched round-robin
 constexpr float kNormEps = 1e-6f;
