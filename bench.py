@@ -223,6 +223,44 @@ def bench_prefill(args, dev, log, which):
             "binding_roofline_frac": max(tflops / BF16_PEAK_TFLOPS, gbs / HBM_PEAK_GBS)}
 
 
+def bench_prefill_snapshots(args, dev, log, plain_us):
+    """The T = 8192 x H = 32 prefill with prefix-cache snapshots every 1,024 tokens (8 states
+    per head written to extra pool slots); reports the time per call and the cost over the
+    plain call."""
+    import torch
+
+    import kda_gated_delta_rule_amd as kda
+    import kda_workloads as W
+
+    y = W.prefill(seed=0)
+    Tt, H, dk = y["q"].shape
+    dv = y["v"].shape[-1]
+    every = 1024
+    nsnap = Tt // every
+    q, k, v, g, beta, cu = (y[n].to(dev) for n in ("q", "k", "v", "g", "beta", "cu_seqlens"))
+    pool = torch.zeros(1 + nsnap, H, dk, dv, device=dev)
+    slots = torch.zeros(1, dtype=torch.int32, device=dev)
+    snap = torch.arange(1, 1 + nsnap, dtype=torch.int32, device=dev).reshape(1, nsnap)
+    o = torch.empty_like(v)
+    ws = torch.empty(kda.chunk_prefill_workspace_size(1, Tt, H, dk, dv), dtype=torch.uint8,
+                     device=dev)
+
+    def step(i):
+        kda.chunk_prefill(q, k, v, g, beta, cu, pool, slots, h0_from_pool=False, o=o, workspace=ws,
+                          snapshot_every=every, snapshot_slots=snap)
+
+    iters = max(5, args.steps // 10)
+    for i in range(2):
+        step(i)
+    total, per = time_loop(step, iters, torch.cuda.synchronize)
+    log("%s with %d snapshots per head: %.1f us/call (plain %.1f us)"
+        % (W.PREFILL["name"], nsnap, per * 1e6, plain_us))
+    return {"workload": W.PREFILL["name"] + "_snapshots_every1024", "snapshot_every": every,
+            "snapshots_per_head": nsnap, "snapshot_bytes": nsnap * H * dk * dv * 4,
+            "us_per_call": per * 1e6, "plain_us_per_call": plain_us,
+            "overhead": per * 1e6 / plain_us - 1.0}
+
+
 def bench_copy(dev, log):
     """Reference device copy of 1 GiB (fp32), also the known-size kernel that scales the
     FETCH_SIZE / WRITE_SIZE counters."""
@@ -313,6 +351,8 @@ def main():
         extra["verify_replay"] = bench_verify_replay(args, dev, log)
         extra["prefill"] = bench_prefill(args, dev, log, "prefill")
         extra["prefill_varlen"] = bench_prefill(args, dev, log, "varlen")
+        extra["prefill_snapshots"] = bench_prefill_snapshots(args, dev, log,
+                                                             extra["prefill"]["us_per_call"])
     cpu = None if args.decode_only else cpu_baseline(dec["inputs"], log)
 
     import kda_workloads as W

@@ -145,6 +145,38 @@ int kda_chunk_prefill(const void* q, const void* k, const void* v, int dtype, co
                       float scale, int use_qk_l2norm, void* o, void* workspace,
                       size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * kda_chunk_prefill_snapshots -- kda_chunk_prefill that also keeps prefix states, for a
+ * KDA prefix cache (the Kimi K3 day-0 adaptation page, section "Kimi K3——面向长程智能体的
+ * 开源旗舰大模型", infrastructure item: KDA Prefix-Cache reuses KDA states across shared
+ * prefixes).  The page names the feature only; here it is read as states stored at
+ * chunk-aligned positions, so a later request sharing the prefix resumes from the stored
+ * state instead of recomputing it.
+ *
+ * Every argument of kda_chunk_prefill, plus:
+ *   snap_every  snapshot interval in tokens, a positive multiple of 64 (chunk aligned)
+ *   snap_slots  [num_seqs, max_snaps] int32 on the device: the state of sequence i after
+ *               (j + 1) * snap_every tokens is written to pool slot snap_slots[i][j],
+ *               for every j < max_snaps with (j + 1) * snap_every <= the sequence's
+ *               length (at the full length it equals the final state); a negative entry
+ *               skips that snapshot.  Snapshot slots must be distinct from each other
+ *               and from the call's slot_idx (not checked: undefined behaviour).
+ *   max_snaps   >= 1, the row length of snap_slots
+ * The snapshot is the carried fp32 state at that chunk boundary (the same value the
+ * following chunk starts from), so resuming a prefill or decode from the slot continues
+ * the sequence exactly as the longer call would.
+ * Errors: as kda_chunk_prefill; snap_every not a positive multiple of 64, max_snaps < 1,
+ * a null or misaligned snap_slots, or num_seqs * max_snaps >= 2^31 give
+ * KDA_ERR_INVALID_ARG.
+ */
+int kda_chunk_prefill_snapshots(const void* q, const void* k, const void* v, int dtype,
+                                const float* g, const float* beta, const int32_t* cu_seqlens,
+                                int num_seqs, int64_t total_tokens, float* state_pool,
+                                int64_t num_slots, const int32_t* slot_idx, int h0_from_pool,
+                                int H, int dk, int dv, float scale, int use_qk_l2norm, void* o,
+                                void* workspace, size_t workspace_bytes, int snap_every,
+                                const int32_t* snap_slots, int max_snaps, hipStream_t stream);
+
 /* Human-readable name of a kda_status value (static string, never NULL). */
 const char* kda_status_string(int status);
 

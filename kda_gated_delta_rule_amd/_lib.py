@@ -34,6 +34,9 @@ SIGNATURES = {
     "kda_chunk_prefill": (_c_i, [_c_p, _c_p, _c_p, _c_i, _c_p, _c_p, _c_p, _c_i, _c_i64, _c_p,
                                  _c_i64, _c_p, _c_i, _c_i, _c_i, _c_i, _c_f, _c_i, _c_p, _c_p, _c_sz,
                                  _c_p]),
+    "kda_chunk_prefill_snapshots": (_c_i, [_c_p, _c_p, _c_p, _c_i, _c_p, _c_p, _c_p, _c_i, _c_i64,
+                                           _c_p, _c_i64, _c_p, _c_i, _c_i, _c_i, _c_i, _c_f, _c_i,
+                                           _c_p, _c_p, _c_sz, _c_i, _c_p, _c_i, _c_p]),
     "kda_status_string": (ctypes.c_char_p, [_c_i]),
 }
 

@@ -82,12 +82,15 @@ KDA_EXPORT size_t kda_chunk_prefill_workspace_size(int num_seqs, int64_t total_t
     return kda::prefill_workspace_bytes(num_seqs, total_tokens, H, dk, dv, dtype == KDA_BF16);
 }
 
-KDA_EXPORT int kda_chunk_prefill(const void* q, const void* k, const void* v, int dtype,
-                                 const float* g, const float* beta, const int32_t* cu_seqlens,
-                                 int num_seqs, int64_t total_tokens, float* state_pool,
-                                 int64_t num_slots, const int32_t* slot_idx, int h0_from_pool,
-                                 int H, int dk, int dv, float scale, int use_qk_l2norm, void* o,
-                                 void* workspace, size_t workspace_bytes, hipStream_t stream) {
+namespace {
+
+int chunk_prefill_impl(const void* q, const void* k, const void* v, int dtype, const float* g,
+                       const float* beta, const int32_t* cu_seqlens, int num_seqs,
+                       int64_t total_tokens, float* state_pool, int64_t num_slots,
+                       const int32_t* slot_idx, int h0_from_pool, int H, int dk, int dv,
+                       float scale, int use_qk_l2norm, void* o, void* workspace,
+                       size_t workspace_bytes, int snap_every, const int32_t* snap_slots,
+                       int max_snaps, hipStream_t stream) {
     if (!valid_dtype(dtype)) return KDA_ERR_INVALID_ARG;
     if (num_seqs < 0 || total_tokens < 0 || H < 1 || num_slots < 1) return KDA_ERR_INVALID_ARG;
     if (num_seqs == 0 && total_tokens != 0) return KDA_ERR_INVALID_ARG;
@@ -119,8 +122,38 @@ KDA_EXPORT int kda_chunk_prefill(const void* q, const void* k, const void* v, in
     if (!workspace || !aligned16(workspace) || workspace_bytes < need) return KDA_ERR_WORKSPACE;
 
     kda::PrefillArgs a{q, k, v, g, beta, cu_seqlens, num_seqs, total_tokens, state_pool,
-                       slot_idx, h0_from_pool, H, scale, use_qk_l2norm, o, workspace};
+                       slot_idx, h0_from_pool, H, scale, use_qk_l2norm, o, workspace,
+                       snap_every, snap_slots, max_snaps};
     return to_status(kda::launch_prefill(a, dtype == KDA_BF16, dk, dv, stream));
+}
+
+}  // namespace
+
+
+KDA_EXPORT int kda_chunk_prefill(const void* q, const void* k, const void* v, int dtype,
+                                 const float* g, const float* beta, const int32_t* cu_seqlens,
+                                 int num_seqs, int64_t total_tokens, float* state_pool,
+                                 int64_t num_slots, const int32_t* slot_idx, int h0_from_pool,
+                                 int H, int dk, int dv, float scale, int use_qk_l2norm, void* o,
+                                 void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    return chunk_prefill_impl(q, k, v, dtype, g, beta, cu_seqlens, num_seqs, total_tokens,
+                              state_pool, num_slots, slot_idx, h0_from_pool, H, dk, dv, scale,
+                              use_qk_l2norm, o, workspace, workspace_bytes, 0, nullptr, 0, stream);
+}
+
+KDA_EXPORT int kda_chunk_prefill_snapshots(
+    const void* q, const void* k, const void* v, int dtype, const float* g, const float* beta,
+    const int32_t* cu_seqlens, int num_seqs, int64_t total_tokens, float* state_pool,
+    int64_t num_slots, const int32_t* slot_idx, int h0_from_pool, int H, int dk, int dv,
+    float scale, int use_qk_l2norm, void* o, void* workspace, size_t workspace_bytes,
+    int snap_every, const int32_t* snap_slots, int max_snaps, hipStream_t stream) {
+    if (snap_every < 64 || snap_every % 64 != 0 || max_snaps < 1) return KDA_ERR_INVALID_ARG;
+    if (!snap_slots || !aligned16(snap_slots)) return KDA_ERR_INVALID_ARG;
+    if (checked_mul(num_seqs, max_snaps) > (1ll << 31) - 1) return KDA_ERR_INVALID_ARG;
+    return chunk_prefill_impl(q, k, v, dtype, g, beta, cu_seqlens, num_seqs, total_tokens,
+                              state_pool, num_slots, slot_idx, h0_from_pool, H, dk, dv, scale,
+                              use_qk_l2norm, o, workspace, workspace_bytes, snap_every,
+                              snap_slots, max_snaps, stream);
 }
 
 KDA_EXPORT const char* kda_status_string(int status) {

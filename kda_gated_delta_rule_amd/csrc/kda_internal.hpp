@@ -48,6 +48,11 @@ struct PrefillArgs {
     int use_l2;
     void* o;
     void* workspace;
+    // prefix snapshots (0 / nullptr / 0: none): the state after (j + 1) * snap_every tokens of
+    // sequence i goes to slot snap_slots[i * max_snaps + j] (negative: skipped)
+    int snap_every = 0;
+    const int32_t* snap_slots = nullptr;
+    int max_snaps = 0;
 };
 
 // Each launcher returns hipSuccess or the launch error.

@@ -982,6 +982,20 @@ __global__ __launch_bounds__(kSegThreads) void seg_carry_kernel(PrefillArgs a) {
     const int c_last = c_first + nc - 1;
     const int bos = a.cu_seqlens[seq], eos = a.cu_seqlens[seq + 1], cs0 = chunk_off[seq];
     const int orow = H * DV, ocol = h * DV;
+    // Prefix snapshot [OUT]: the state after p tokens of the sequence (p > 0, a multiple of
+    // snap_every) goes to its snapshot slot, if one is given.  p is wave-uniform.
+    auto snapshot = [&](int p) {
+        if (p <= 0 || p % a.snap_every != 0) return;
+        const int j = p / a.snap_every - 1;
+        if (j >= a.max_snaps) return;
+        const int slot = a.snap_slots[static_cast<int64_t>(seq) * a.max_snaps + j];
+        if (slot < 0) return;
+        float* Sn = a.pool + (static_cast<int64_t>(slot) * H + h) * (DK * DV);
+#pragma unroll
+        for (int j2 = 0; j2 < SP::SJB; ++j2)
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) Sn[(16 * cb + q4 + rr) * DV + 16 * (jb0 + j2) + r] = S[j2][rr];
+    };
     SegOps<SP> F[NB];
 #pragma unroll
     for (int k = 0; k < NB; ++k)
@@ -996,6 +1010,7 @@ __global__ __launch_bounds__(kSegThreads) void seg_carry_kernel(PrefillArgs a) {
                 const __amdgpu_buffer_rsrc_t orsrc =
                     buf_rsrc(static_cast<char*>(a.o) + static_cast<int64_t>(t0) * orow * E,
                              MODE == kOut ? static_cast<int64_t>(L) * orow * E : 0);
+                if (MODE == kOut && a.snap_every > 0) snapshot(t0 - bos);  // S = state before this chunk
                 seg_step<DK, DV, TIn, MODE>(F[k], S, sx, ux, orsrc, orow, ocol, a.scale, tb, part, cb, jb0, lane);
             }
             seg_fetch(F[k], rec_of(min(cc + NB, c_last)), ws, tb, task, cb, lane);
@@ -1010,6 +1025,7 @@ __global__ __launch_bounds__(kSegThreads) void seg_carry_kernel(PrefillArgs a) {
             for (int j = 0; j < SP::SJB; ++j)
 #pragma unroll
                 for (int rr = 0; rr < 4; ++rr) Sg[(16 * cb + q4 + rr) * DV + 16 * (jb0 + j) + r] = S[j][rr];
+            if (a.snap_every > 0) snapshot(eos - bos);  // a snapshot at the full length
         }
     } else {
         float* Sl = reinterpret_cast<float*>(blk + ws.s_loc);

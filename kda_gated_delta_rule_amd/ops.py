@@ -80,13 +80,18 @@ def chunk_prefill_workspace_size(num_seqs, total_tokens, H, dk, dv, dtype=torch.
 
 
 def chunk_prefill(q, k, v, g, beta, cu_seqlens, state_pool, slot_idx, *, h0_from_pool=True,
-                  o=None, workspace=None, scale=None, use_qk_l2norm=True):
-    """Varlen chunked prefill (kda_chunk_prefill).
+                  o=None, workspace=None, scale=None, use_qk_l2norm=True, snapshot_every=None,
+                  snapshot_slots=None):
+    """Varlen chunked prefill (kda_chunk_prefill, or kda_chunk_prefill_snapshots when
+    snapshot_every is given).
 
     q, k [T_total, H, dk], v [T_total, H, dv] (bf16 or fp32); g [T_total, H, dk] fp32;
     beta [T_total, H] fp32; cu_seqlens [num_seqs + 1] int32; state_pool [num_slots, H, dk, dv]
     fp32 (final states written to slot_idx [num_seqs] int32).  workspace: a uint8 tensor of at
-    least chunk_prefill_workspace_size(...) bytes, or None to allocate one.  Returns o.
+    least chunk_prefill_workspace_size(...) bytes, or None to allocate one.  snapshot_every (a
+    multiple of 64) with snapshot_slots [num_seqs, max_snaps] int32: the state of sequence i
+    after (j + 1) * snapshot_every tokens is also written to slot snapshot_slots[i, j] (negative
+    entries skipped).  Returns o.
     """
     Tt, H, dk = q.shape
     dv = v.shape[-1]
@@ -106,10 +111,19 @@ def chunk_prefill(q, k, v, g, beta, cu_seqlens, state_pool, slot_idx, *, h0_from
     _contig(q, k, v, g, beta, cu_seqlens, state_pool, slot_idx, o, workspace)
     if scale is None:
         scale = dk ** -0.5
-    st = _lib.load().kda_chunk_prefill(
-        _ptr(q), _ptr(k), _ptr(v), _DTYPES[q.dtype], _ptr(g), _ptr(beta), _ptr(cu_seqlens), ns,
-        Tt, _ptr(state_pool), state_pool.shape[0], _ptr(slot_idx), int(bool(h0_from_pool)), H, dk,
-        dv, float(scale), int(bool(use_qk_l2norm)), _ptr(o), _ptr(workspace),
-        workspace.numel() * workspace.element_size(), _stream(q))
-    _lib.check("kda_chunk_prefill", st)
+    args = (_ptr(q), _ptr(k), _ptr(v), _DTYPES[q.dtype], _ptr(g), _ptr(beta), _ptr(cu_seqlens),
+            ns, Tt, _ptr(state_pool), state_pool.shape[0], _ptr(slot_idx), int(bool(h0_from_pool)),
+            H, dk, dv, float(scale), int(bool(use_qk_l2norm)), _ptr(o), _ptr(workspace),
+            workspace.numel() * workspace.element_size())
+    if snapshot_every is None:
+        _need(snapshot_slots is None, "snapshot_slots needs snapshot_every")
+        st = _lib.load().kda_chunk_prefill(*args, _stream(q))
+        _lib.check("kda_chunk_prefill", st)
+    else:
+        _need(snapshot_slots is not None and snapshot_slots.dtype == torch.int32
+              and snapshot_slots.dim() == 2 and snapshot_slots.shape[0] == ns, "snapshot_slots")
+        _contig(snapshot_slots)
+        st = _lib.load().kda_chunk_prefill_snapshots(*args, int(snapshot_every), _ptr(snapshot_slots),
+                                                     snapshot_slots.shape[1], _stream(q))
+        _lib.check("kda_chunk_prefill_snapshots", st)
     return o

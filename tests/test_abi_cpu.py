@@ -128,6 +128,21 @@ def test_prefill_validation(lib, over, code):
     assert lib.kda_chunk_prefill(*prefill_args(**over).values()) == code
 
 
+@pytest.mark.parametrize("every,slots,max_snaps,code", [
+    (0, A, 4, _lib.KDA_ERR_INVALID_ARG),
+    (32, A, 4, _lib.KDA_ERR_INVALID_ARG),     # not chunk aligned
+    (100, A, 4, _lib.KDA_ERR_INVALID_ARG),
+    (256, A, 0, _lib.KDA_ERR_INVALID_ARG),    # no snapshot row
+    (256, None, 4, _lib.KDA_ERR_INVALID_ARG),
+    (256, A + 4, 4, _lib.KDA_ERR_INVALID_ARG),
+    (256, A, 4, _lib.KDA_ERR_WORKSPACE),      # valid: stops at the workspace check
+])
+def test_prefill_snapshot_validation(lib, every, slots, max_snaps, code):
+    args = list(prefill_args().values())
+    args = args[:-1] + [every, slots, max_snaps, None]
+    assert lib.kda_chunk_prefill_snapshots(*args) == code
+
+
 def test_prefill_valid_arguments_reach_workspace_check(lib):
     # all arguments valid except the workspace size: the call must stop at that check
     assert lib.kda_chunk_prefill(*prefill_args().values()) == _lib.KDA_ERR_WORKSPACE

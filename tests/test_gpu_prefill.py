@@ -187,6 +187,92 @@ def test_workspace_reused_across_calls():
         assert rel_l2(f64(pool.cpu()[y["slot_idx"].long()]), h_ref) <= 1e-2
 
 
+def prefix_states(y, requests, h0_from_pool=True):
+    """Oracle states after the first p tokens of sequence i, for each (i, p) in requests: one
+    fp64 recurrence call over a batch whose sequences are those prefixes."""
+    cu = y["cu_seqlens"].tolist()
+    parts = {n: [] for n in NAMES}
+    lens, h0 = [], []
+    for i, p in requests:
+        for n in NAMES:
+            parts[n].append(y[n][cu[i]:cu[i] + p])
+        lens.append(p)
+        h0.append(f64(y["pool"][int(y["slot_idx"][i])]) if h0_from_pool
+                  else np.zeros(y["pool"].shape[1:]))
+    cat = {n: torch.cat(parts[n]) for n in NAMES}
+    cu_p = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    _, ht, _ = O.recurrent(*(f64(cat[n]) for n in NAMES), cu_p, h0=np.stack(h0))
+    return ht
+
+
+@pytest.mark.parametrize("dtype,d,tol", [(torch.bfloat16, 128, 1e-2), (torch.float32, 64, 1e-4)])
+def test_prefix_snapshots(dtype, d, tol):
+    """kda_chunk_prefill_snapshots: the state after every 256 tokens of each sequence lands in
+    its snapshot slot and equals the recurrence's state at that position (one at a segment
+    start, one at a full length); skipped (-1) and out-of-range entries leave slots untouched;
+    o and the final states are those of the plain call."""
+    dev = need_gpu()
+    announce("prefill prefix snapshots %s d=%d" % (dtype, d))
+    seqlens, every, max_snaps = (1500, 512, 200, 0, 2049), 256, 9
+    ns = len(seqlens)
+    num_slots = ns + ns * max_snaps
+    y = W.prefill(seed=15, seqlens=seqlens, H=2, dk=d, dv=d, num_slots=num_slots, h0_std=0.05,
+                  dtype=dtype)
+    taken = set(y["slot_idx"].tolist())
+    free = [s for s in range(num_slots) if s not in taken]
+    snap = torch.tensor(free[:ns * max_snaps], dtype=torch.int32).reshape(ns, max_snaps)
+    snap[0, 1] = -1  # skipped
+    pool = y["pool"].to(dev)
+    o = kda.chunk_prefill(*(y[n].to(dev) for n in NAMES), y["cu_seqlens"].to(dev), pool,
+                          y["slot_idx"].to(dev), snapshot_every=every,
+                          snapshot_slots=snap.to(dev))
+    torch.cuda.synchronize()
+    got = pool.cpu()
+    o_ref, h_ref, _ = oracle_prefill(y)
+    assert rel_l2(f64(o), o_ref) <= tol
+    assert rel_l2(f64(got[y["slot_idx"].long()]), h_ref) <= tol
+    requests, slots = [], []
+    untouched = set(range(num_slots)) - taken
+    for i, L in enumerate(seqlens):
+        for j in range(max_snaps):
+            p = (j + 1) * every
+            if p <= L and snap[i, j] >= 0:
+                requests.append((i, p))
+                slots.append(int(snap[i, j]))
+                untouched.discard(int(snap[i, j]))
+    assert (4, 2048) in requests and (1, 512) in requests  # a segment start, a full length
+    ref = prefix_states(y, requests)
+    for n, (req, sl) in enumerate(zip(requests, slots)):
+        assert rel_l2(f64(got[sl]), ref[n]) <= tol, req
+    for sl in sorted(untouched):
+        assert torch.equal(got[sl], y["pool"][sl]), sl
+
+
+def test_resume_from_snapshot_matches_the_longer_call():
+    """Prefix-cache use: a 2,500-token prefill keeps a snapshot after 1,024 tokens; a second
+    prefill of tokens 1,024.. that starts from the snapshot slot gives the outputs and final
+    state of the longer call."""
+    dev = need_gpu()
+    announce("prefill resume from snapshot")
+    y = W.prefill(seed=16, seqlens=(2500,), H=3, dk=128, dv=128, num_slots=3, h0_std=0.05)
+    pool = y["pool"].to(dev)
+    fin = int(y["slot_idx"][0])
+    ss = [s for s in range(3) if s != fin][0]  # snapshot slot
+    snap = torch.tensor([[ss, -1]], dtype=torch.int32, device=dev)  # after 1024 tokens
+    full = kda.chunk_prefill(*(y[n].to(dev) for n in NAMES), y["cu_seqlens"].to(dev), pool,
+                             y["slot_idx"].to(dev), snapshot_every=1024, snapshot_slots=snap)
+    a = 1024
+    tail = [y[n][a:].contiguous().to(dev) for n in NAMES]
+    pool2 = pool.clone()
+    rest = kda.chunk_prefill(*tail, torch.tensor([0, 2500 - a], dtype=torch.int32, device=dev),
+                             pool2, torch.tensor([ss], dtype=torch.int32, device=dev))
+    torch.cuda.synchronize()
+    assert rel_l2(f64(rest), f64(full[a:])) <= 1e-2
+    assert rel_l2(f64(pool2.cpu()[ss]), f64(pool.cpu()[fin])) <= 1e-2
+    o_ref, _, _ = oracle_prefill(y)
+    assert rel_l2(f64(rest), o_ref[a:]) <= 1e-2
+
+
 def test_zero_initial_state_ignores_pool_contents():
     dev = need_gpu()
     announce("prefill h0 zero")
