@@ -273,20 +273,11 @@ __device__ void block_exclusive_scan(int n, F f, int32_t* out, int32_t* part, in
     __syncthreads();
 }
 
-__global__ __launch_bounds__(kThreads) void chunk_map_kernel(const int32_t* __restrict__ cu, int num_seqs,
-                                                             int seg_chunks, int32_t* chunk_off, int32_t* seg_off,
-                                                             int4* table, int4* segtab) {
-    __shared__ int32_t part[kThreads];
-    __shared__ int32_t carry;
-    auto nchunks = [&](int i) {
-        const int len = cu[i + 1] - cu[i];
-        return len > 0 ? (len + kChunk - 1) / kChunk : 0;
-    };
-    block_exclusive_scan(num_seqs, nchunks, chunk_off, part, &carry);
-    block_exclusive_scan(num_seqs, [&](int i) { return (nchunks(i) + seg_chunks - 1) / seg_chunks; }, seg_off, part,
-                         &carry);
-    // one wave per sequence (its lanes over the sequence's chunks and segments), so the
-    // sequences' offset loads overlap instead of forming one chain
+// The chunk table (sequence, first token, length) and the segment table (sequence, first
+// chunk, chunks, 2 k + last) from the chunk and segment offsets: one wave per sequence (its
+// lanes over the sequence's chunks and segments), so the sequences' loads overlap.
+__device__ void write_chunk_tables(const int32_t* cu, int num_seqs, int seg_chunks, const int32_t* chunk_off,
+                                   const int32_t* seg_off, int4* table, int4* segtab) {
     const int lane = threadIdx.x % kWave;
     for (int i = threadIdx.x / kWave; i < num_seqs; i += kThreads / kWave) {
         const int bos = cu[i], eos = cu[i + 1];
@@ -300,6 +291,25 @@ __global__ __launch_bounds__(kThreads) void chunk_map_kernel(const int32_t* __re
             segtab[s0 + k] = make_int4(i, first + k * seg_chunks, min(seg_chunks, nch - k * seg_chunks),
                                        2 * k + (k == ns - 1 ? 1 : 0));
     }
+}
+
+// Batches of at most kThreads sequences need no chunk_map launch: every intra-chunk
+// workgroup scans the chunk counts itself, and workgroup 0 writes the tables above.
+__host__ __device__ inline bool map_inline(int num_seqs) { return num_seqs <= kThreads; }
+
+__global__ __launch_bounds__(kThreads) void chunk_map_kernel(const int32_t* __restrict__ cu, int num_seqs,
+                                                             int seg_chunks, int32_t* chunk_off, int32_t* seg_off,
+                                                             int4* table, int4* segtab) {
+    __shared__ int32_t part[kThreads];
+    __shared__ int32_t carry;
+    auto nchunks = [&](int i) {
+        const int len = cu[i + 1] - cu[i];
+        return len > 0 ? (len + kChunk - 1) / kChunk : 0;
+    };
+    block_exclusive_scan(num_seqs, nchunks, chunk_off, part, &carry);
+    block_exclusive_scan(num_seqs, [&](int i) { return (nchunks(i) + seg_chunks - 1) / seg_chunks; }, seg_off, part,
+                         &carry);
+    write_chunk_tables(cu, num_seqs, seg_chunks, chunk_off, seg_off, table, segtab);
 }
 
 // ---------------------------------------------------------------------------
@@ -712,23 +722,63 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_intra_kernel(PrefillArgs a)
     static_assert(P::fits, "LDS plan exceeds 160 KiB");
     __shared__ __attribute__((aligned(16))) char smem[P::BYTES];
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int H = a.H;
-    const WsLayout ws(a.num_seqs, a.total_tokens, H, DK, DV, P::E);
-    const int32_t* chunk_off = static_cast<const int32_t*>(a.workspace);
-    const int4* table = reinterpret_cast<const int4*>(static_cast<const char*>(a.workspace) + ws.off_table);
+    const int H = a.H, ns = a.num_seqs;
+    const WsLayout ws(ns, a.total_tokens, H, DK, DV, P::E);
+    int32_t* chunk_off = static_cast<int32_t*>(a.workspace);
+    int4* table = reinterpret_cast<int4*>(static_cast<char*>(a.workspace) + ws.off_table);
     char* recs = static_cast<char*>(a.workspace) + ws.off_rec;
-    const int total = chunk_off[a.num_seqs] * H;
     const int stride = gridDim.x;
-    const auto rtab = buf_rsrc(table, static_cast<int64_t>(ws.max_chunks) * 16);
-    int item = blockIdx.x;
-    if (item >= total) return;
-    u32x4 info = __builtin_amdgcn_raw_buffer_load_b128(rtab, (item / H) * 16, 0, 0);
-    for (; item < total; item += stride) {
+
+    // Batches of up to kThreads sequences: the chunk offsets are scanned into LDS here (from
+    // cu_seqlens, copied once), and workgroup 0 also writes the workspace tables the segment
+    // kernels read.  Larger batches: chunk_map_kernel ran first and each item reads its entry
+    // of the chunk table.
+    __shared__ int32_t m_cu[kThreads + 1], m_coff[kThreads + 1], m_soff[kThreads + 1], m_part[kThreads];
+    __shared__ int32_t m_carry;
+    const bool inl = map_inline(ns);
+    if (inl) {
+        for (int i = tid; i <= ns; i += kThreads) m_cu[i] = a.cu_seqlens[i];
+        __syncthreads();
+        auto nchunks = [&](int i) {
+            const int len = m_cu[i + 1] - m_cu[i];
+            return len > 0 ? (len + kChunk - 1) / kChunk : 0;
+        };
+        block_exclusive_scan(ns, nchunks, m_coff, m_part, &m_carry);
+        if (blockIdx.x == 0) {
+            const int seg = ws.seg_chunks;
+            block_exclusive_scan(ns, [&](int i) { return (nchunks(i) + seg - 1) / seg; }, m_soff, m_part, &m_carry);
+            int32_t* seg_off = reinterpret_cast<int32_t*>(static_cast<char*>(a.workspace) + ws.off_segoff);
+            for (int i = tid; i <= ns; i += kThreads) {
+                chunk_off[i] = m_coff[i];
+                seg_off[i] = m_soff[i];
+            }
+            write_chunk_tables(m_cu, ns, seg, m_coff, m_soff, table,
+                               reinterpret_cast<int4*>(static_cast<char*>(a.workspace) + ws.off_segtab));
+        }
+    }
+    const int total = (inl ? m_coff[ns] : chunk_off[ns]) * H;
+    for (int item = blockIdx.x; item < total; item += stride) {
+        const int c = item / H;
+        int t0, L;
+        if (inl) {
+            // the sequence lo with m_coff[lo] <= c < m_coff[lo + 1] (it has chunks)
+            int lo = 0, hi = ns;
+            while (hi - lo > 1) {
+                const int mid = (lo + hi) >> 1;
+                if (m_coff[mid] <= c)
+                    lo = mid;
+                else
+                    hi = mid;
+            }
+            t0 = __builtin_amdgcn_readfirstlane(m_cu[lo] + kChunk * (c - m_coff[lo]));
+            L = __builtin_amdgcn_readfirstlane(min(kChunk, m_cu[lo + 1] - t0));
+        } else {
+            const int4 e = table[c];
+            t0 = e.y;
+            L = e.z;
+        }
         IntraIn<DK, DV, TIn> X;
-        intra_fetch(X, a, __builtin_amdgcn_readfirstlane(info[1]), __builtin_amdgcn_readfirstlane(info[2]), item % H,
-                    wave, lane);
-        const int nxt = item + stride < total ? item + stride : item;
-        info = __builtin_amdgcn_raw_buffer_load_b128(rtab, (nxt / H) * 16, 0, 0);
+        intra_fetch(X, a, t0, L, item % H, wave, lane);
         intra_compute(X, smem, a, recs + ws.rec_bytes * static_cast<size_t>(item), ws, wave, lane, tid);
     }
 }
@@ -1180,10 +1230,11 @@ hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t stream) {
         constexpr int E = Geo<TIn>::E;
         const WsLayout ws(a.num_seqs, a.total_tokens, a.H, DK, DV, E);
         char* base = static_cast<char*>(a.workspace);
-        hipLaunchKernelGGL(chunk_map_kernel, dim3(1), dim3(kThreads), 0, stream, a.cu_seqlens, a.num_seqs,
+        const int64_t items = ws.max_chunks * a.H;
+        if (!map_inline(a.num_seqs) || items == 0)
+            hipLaunchKernelGGL(chunk_map_kernel, dim3(1), dim3(kThreads), 0, stream, a.cu_seqlens, a.num_seqs,
                            ws.seg_chunks, reinterpret_cast<int32_t*>(base), reinterpret_cast<int32_t*>(base + ws.off_segoff),
                            reinterpret_cast<int4*>(base + ws.off_table), reinterpret_cast<int4*>(base + ws.off_segtab));
-        const int64_t items = ws.max_chunks * a.H;
         if (items > 0) {
             const int slots = 2 * device_cu_count();
             const int grid = static_cast<int>(items < slots ? items : slots);
