@@ -71,6 +71,29 @@ def counted_traffic(path):
     return rec["traffic_bytes_per_launch"]
 
 
+def counted_mfma(path, workload, us_per_call):
+    """MFMA evidence of one prefill call from the rocprofv3 counter record in `path` (per kernel:
+    MFMA busy %, executed MFMA flops; see profiles/): the executed MFMA flops per call, their rate
+    over the measured call time as a fraction of the bf16 peak, and the MFMA busy % weighted by
+    each kernel's traced duration.  None when the kernel sources have changed since."""
+    import hashlib
+
+    try:
+        rec = json.load(open(path))
+        src = b"".join(open(os.path.join(ROOT, f), "rb").read() for f in rec["sources"])
+        ks = rec["workloads"][workload]
+    except (OSError, ValueError, KeyError):
+        return None
+    if hashlib.sha256(src).hexdigest() != rec.get("source_sha256"):
+        return None
+    flops = sum(k["mfma_flops_bf16"] + k["mfma_flops_f32"] for k in ks.values())
+    t = sum(k["us"] for k in ks.values())
+    return {"executed_mfma_flops": flops,
+            "executed_mfma_frac": flops / (us_per_call * 1e-6) / (BF16_PEAK_TFLOPS * 1e12),
+            "mfma_busy_frac": sum(k["us"] * k["mfma_busy_pct"] for k in ks.values()) / t / 100.0,
+            "per_kernel_mfma_busy_pct": {n: k["mfma_busy_pct"] for n, k in ks.items()}}
+
+
 def time_loop(fn, steps, sync):
     """Runs fn(i) for i in range(steps) with HIP events around every call on the current
     stream; returns (total elapsed seconds, mean per-call seconds)."""
@@ -220,7 +243,9 @@ def bench_prefill(args, dev, log, which):
             "token_heads_per_s": th / per, "algorithmic_flops": flops, "algorithmic_bytes": byts,
             "achieved_TFLOPs": tflops, "mfma_frac": tflops / BF16_PEAK_TFLOPS,
             "achieved_GBs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS,
-            "binding_roofline_frac": max(tflops / BF16_PEAK_TFLOPS, gbs / HBM_PEAK_GBS)}
+            "binding_roofline_frac": max(tflops / BF16_PEAK_TFLOPS, gbs / HBM_PEAK_GBS),
+            "mfma_counters": counted_mfma(os.path.join(ROOT, "profiles", "prefill_mfma_counters.json"),
+                                          name, per * 1e6)}
 
 
 def bench_prefill_snapshots(args, dev, log, plain_us):
