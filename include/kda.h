@@ -99,8 +99,9 @@ int kda_decode_step(const void* q, const void* k, const void* v, int dtype, cons
  * and writes the state back to the slot.  records are those written by
  * kda_decode_step in verify mode ([N, T, H, 2*dk + dv] fp32).  accepted_len [N] int32
  * on the device, each in 0..T (0 leaves the slot untouched; values outside 0..T are
- * undefined behaviour).  The fp32 arithmetic matches commit-mode kda_decode_step, so
- * replaying a prefix reproduces the state that committing the same tokens gives.
+ * undefined behaviour).  The fp32 arithmetic matches commit-mode kda_decode_step with
+ * T >= 2, so replaying a prefix of two or more tokens reproduces, bit for bit, the state
+ * that committing the same tokens gives (a one-token commit agrees up to fp32 rounding).
  * Limit: N * H <= 2^22, as for kda_decode_step.
  */
 int kda_replay_commit(float* state_pool, int64_t num_slots, const int32_t* slot_idx,

@@ -11,30 +11,27 @@
 //  * The fp32 state tile (dk x BV, BV = 64 columns) of a (sequence, head, dv tile) is
 //    streamed once from HBM into VGPRs with 16-byte non-temporal loads (each wave load
 //    instruction covers whole 256-byte tile rows), kept there for all T tokens, and
-//    written back once with non-temporal stores.  The step is about 0.9 flop per byte,
-//    so nothing goes through MFMA.
-//  * Both reductions over dk (S'^T k and S'^T q) come from one pass over the decayed
-//    state, using o = scale * (S'^T q + (k.q) u): the output needs no second pass.
-//  * The rows of a tile form 16 row groups (group g = rows g, g + 16, ...), group 4w + rq
-//    at lane position rq (0..3) of slice w (0..3).  Each group's sum runs down its rows
-//    in order; the four groups of a lane position are added in order w = 0..3; the four
-//    lane positions are then combined pairwise ((r0 + r1) + (r2 + r3)) with the gfx950
-//    row-swap instructions (v_permlane16_swap, v_permlane32_swap).  Both kernels below
-//    follow exactly this order, so the u a verify call records is bit-identical to the u
-//    a commit computes, and replaying records reproduces a commit exactly.
-//  * T = 1 (decode_kernel, HBM-bound): 256 threads (4 waves) per tile; thread (w, rq, c4)
-//    owns columns 4 c4 .. 4 c4 + 3 of row group 4w + rq; the slices meet through one LDS
-//    exchange (one barrier per token).  Per-token vectors (qh, kh, alpha, v, beta, k.q)
-//    are prepared by one wave per token into LDS, row-permuted for 16-byte LDS loads.
-//  * T > 1 (decode_multi_kernel, MTP / verify): the token steps are VALU-bound (fp32 at
-//    one wave64 instruction per 4 cycles), so one wave holds the whole tile (128
-//    registers) and lane (rq, c4) owns columns 4 c4 .. 4 c4 + 3 of row groups 4w + rq
-//    for all w: no LDS exchange and no barrier per token, and the 2,048-tile
-//    verify workload fits the GPU in one round (two waves per SIMD).  The state loads
-//    go out first; token inputs are loaded two tokens at a time while they stream.
+//    written back once with non-temporal stores.  A one-token step is about 0.9 flop
+//    per byte and runs on the VALU; only the multi-token blocks use MFMA.
+//  * T = 1 (decode_kernel, HBM-bound): both reductions over dk (S'^T k and S'^T q) come
+//    from one pass over the decayed state, using o = scale * (S'^T q + (k.q) u): the
+//    output needs no second pass.  256 threads (4 waves) per tile; thread (w, rq, c4) owns
+//    columns 4 c4 .. 4 c4 + 3 of row group 4w + rq (group g = rows g, g + 16, ...); each
+//    group's sum runs down its rows, the four waves' sums meet through one LDS exchange
+//    (one barrier per token), and the four lane positions are combined pairwise with the
+//    gfx950 row-swap instructions (v_permlane16_swap, v_permlane32_swap).  Per-token
+//    vectors (qh, kh, alpha, v, beta, k.q) are prepared by one wave per token into LDS.
+//  * T > 1 (wy_multi_kernel, MTP / verify): the WY form of 8-token blocks (see the
+//    kernel): one fp32 MFMA pass over the register-resident tile gives the 16 products
+//    with the entering state, a per-column 8x8 triangular solve gives u and o, and the
+//    state is updated only when it is kept (commit, or between blocks) -- with the
+//    replay kernel's fp32 operations, so replaying verify records reproduces a commit of
+//    two or more tokens exactly.
 //  * Replay: 256-thread workgroups per (sequence, head), elementwise (no reductions).
 #include "kda_device.hpp"
 #include "kda_internal.hpp"
+
+#include <type_traits>
 
 namespace kda {
 
@@ -272,107 +269,57 @@ __global__ __launch_bounds__(kThreads, 5) void decode_kernel(DecodeArgs a) {
     }
 }
 
-// Tile of decode_multi_kernel (one wave): see the file header for the lane mapping.
-template <int DK, int DV, int BV>
-struct DecTile {
-    static constexpr int NC4 = BV / 4;                    // float4 column groups
-    static constexpr int RQ = kWave / NC4;                // lanes per column group
-    static constexpr int NRG = 16;                        // row groups of the dk reductions
-    static constexpr int NW = NRG / RQ;                   // row groups per lane
-    static constexpr int RPT = DK / NRG;                  // rows per row group
-    static constexpr int NT = DV / BV;                    // tiles per head
-    static constexpr int EPL = DK / kWave;                // key channels per lane in the prep
-    static constexpr int VPL = (BV + kWave - 1) / kWave;  // v columns per lane in the prep
-    static_assert(NC4 == 16 && RQ == 4 && RPT % 4 == 0 && DV % BV == 0, "decode tile");
-    static_assert(EPL >= 1, "dk is 64 or 128");
-    // LDS slot of key channel c: the rows of one row group are contiguous.
-    __device__ static constexpr int pos(int c) { return (c % NRG) * RPT + c / NRG; }
+// ---------------------------------------------------------------------------
+// T > 1 (MTP, verify): the WY form of a block of up to 8 tokens on one state tile.  For
+// the tokens t of a block entering with state S0, G_t = g_1 + ... + g_t per key channel:
+//   S'_t^T kh_t = S0^T (kh_t e^{G_t}) + sum_{s<t} (kh_s . e^{G_t - G_s} kh_t) u_s
+// so with R = S0^T [kh_t e^{G_t} | qh_t e^{G_t}] (16 vectors of dk, one fp32 MFMA pass
+// over the tile) and, per column,
+//   u_t = beta_t (v_t - RK_t - sum_{s<t} kk_ts u_s),  kk_ts = sum_c kh_tc kh_sc e^{G_tc - G_sc}
+//   o_t = scale (RQ_t + sum_{s<=t} qk_ts u_s),        qk_ts = sum_c qh_tc kh_sc e^{G_tc - G_sc}
+// (the token recurrence rearranged, exact in exact arithmetic).  A verify call never
+// updates the state.  A commit (and a call of more than 8 tokens, between blocks) then
+// applies S <- diag(alpha_t) S + kh_t u_t^T in token order with the replay kernel's fp32
+// operations, so replaying a verify call's records gives, bit for bit, the state a commit
+// of the same tokens gives.
+//
+// One wave per (sequence, head, 64-column tile).  The state tile is loaded with 16-byte
+// loads, lane l holding rows 4 s + l / 16 (s = 0 .. dk/4 - 1), columns 4 (l % 16) .. + 3:
+// component e of the k-step-s register is exactly the A operand of a 16x16x4 fp32 MFMA
+// (row m = l % 16 <-> tile column 4 m + e, k = l / 16), so the product needs no
+// re-layout.  The 64 dot products kk and qk of a block are reduced over the wave with a
+// shuffle reduce-scatter (lane l ends with value l).
+// ---------------------------------------------------------------------------
+constexpr int kWyTB = 8;  // tokens per block
+constexpr int kWyRt = 20; // R^T row stride (floats): 16 vectors, rows 16-byte aligned
+
+template <int DK>
+struct WyLds {
+    static constexpr int KS = DK / 4;  // fp32 MFMA k-steps over dk
+    union {
+        float xp[16][4][KS];   // X[4 s + q][n] at [n][q][s]: n < 8 kh_n e^G_n, n >= 8 qh e^G
+        float rt[64][kWyRt];   // R^T: tile column j, vector n
+    };
+    float kr[kWyTB][4][KS];    // kh_t of row 4 s + q at [t][q][s]
+    float ar[kWyTB][4][KS];    // alpha_t likewise
+    float ut[kWyTB][64];       // u_t of the tile's columns
+    float pq[64];              // kk and qk of the block (index: see wy_pair)
 };
 
+// Dot-product index of the pair (a, b), a > b: kk_ab at wy_pair(a, b), qk_ab at 32 + that;
+// the diagonal qk_aa at 28 + a (a < 4) and 56 + a (a >= 4).
+__host__ __device__ constexpr int wy_pair(int a, int b) { return a * (a - 1) / 2 + b; }
+__host__ __device__ constexpr int wy_diag(int a) { return a < 4 ? 28 + a : 56 + a; }
 
-// One token's inputs as this lane loads them (key channels EPL lane .. EPL lane + EPL - 1,
-// v column lane of the tile).
-template <int DK, int DV, int BV>
-struct PrepIn {
-    float q[DecTile<DK, DV, BV>::EPL], k[DecTile<DK, DV, BV>::EPL], g[DecTile<DK, DV, BV>::EPL];
-    float v[DecTile<DK, DV, BV>::VPL];
-    float b;
-};
-
-template <int DK, int DV, int BV, class TIn>
-__device__ __forceinline__ PrepIn<DK, DV, BV> prep_load(const DecodeArgs& a, int n, int t, int h, int tile,
-                                                        int lane) {
-    using C = DecTile<DK, DV, BV>;
-    PrepIn<DK, DV, BV> x;
-    const int64_t tok = (static_cast<int64_t>(n) * a.T + t) * a.H + h;
-    const int64_t rowk = tok * DK;
-    if constexpr (C::EPL == 2) {
-        const int c = lane * 2;
-        const float2 qq = load2<TIn>(a.q, rowk + c);
-        const float2 kk = load2<TIn>(a.k, rowk + c);
-        const float2 gg = *reinterpret_cast<const float2*>(a.g + rowk + c);
-        x.q[0] = qq.x; x.q[1] = qq.y;
-        x.k[0] = kk.x; x.k[1] = kk.y;
-        x.g[0] = gg.x; x.g[1] = gg.y;
-    } else {
-        x.q[0] = load1<TIn>(a.q, rowk + lane);
-        x.k[0] = load1<TIn>(a.k, rowk + lane);
-        x.g[0] = a.g[rowk + lane];
-    }
-#pragma unroll
-    for (int e = 0; e < C::VPL; ++e) {
-        const int col = lane + e * kWave;
-        x.v[e] = col < BV ? load1<TIn>(a.v, tok * DV + tile * BV + col) : 0.f;
-    }
-    x.b = a.beta[tok];
-    return x;
+template <class TIn>
+__device__ __forceinline__ void store1(void* p, int64_t i, float x);
+template <>
+__device__ __forceinline__ void store1<F32>(void* p, int64_t i, float x) {
+    static_cast<float*>(p)[i] = x;
 }
-
-// Token t (local slot j): L2 norms, alpha = exp(g), k.q into LDS (and the k, alpha
-// records of a verify call, written by tile 0).
-template <int DK, int DV, int BV, int TB, bool VERIFY>
-__device__ __forceinline__ void prep_store(const DecodeArgs& a, TokenLds<DK, BV, TB>& L, int j, int n, int t,
-                                           int h, int tile, int lane, const PrepIn<DK, DV, BV>& x) {
-    using C = DecTile<DK, DV, BV>;
-    const int64_t tok = (static_cast<int64_t>(n) * a.T + t) * a.H + h;
-    float iq = 1.f, ik = 1.f;
-    if (a.use_l2) {
-        float sq = 0.f, sk = 0.f;
-#pragma unroll
-        for (int e = 0; e < C::EPL; ++e) {
-            sq = fmaf(x.q[e], x.q[e], sq);
-            sk = fmaf(x.k[e], x.k[e], sk);
-        }
-        sq = wave_sum(sq);
-        sk = wave_sum(sk);
-        iq = 1.f / sqrtf(sq + kNormEps);
-        ik = 1.f / sqrtf(sk + kNormEps);
-    }
-    float kq = 0.f;
-    float* rec = VERIFY ? a.records + tok * (2 * DK + DV) : nullptr;
-#pragma unroll
-    for (int e = 0; e < C::EPL; ++e) {
-        const int c = lane * C::EPL + e;
-        const float qh = x.q[e] * iq, kh = x.k[e] * ik, al = expf(x.g[e]);
-        kq = fmaf(qh, kh, kq);
-        L.q[j][C::pos(c)] = qh;
-        L.k[j][C::pos(c)] = kh;
-        L.a[j][C::pos(c)] = al;
-        if (VERIFY && tile == 0) {
-            rec[c] = kh;
-            rec[DK + c] = al;
-        }
-    }
-    kq = wave_sum(kq);
-#pragma unroll
-    for (int e = 0; e < C::VPL; ++e) {
-        const int col = lane + e * kWave;
-        if (col < BV) L.v[j][col] = x.v[e];
-    }
-    if (lane == 0) {
-        L.beta[j] = x.b;
-        L.kq[j] = kq;
-    }
+template <>
+__device__ __forceinline__ void store1<BF16>(void* p, int64_t i, float x) {
+    static_cast<uint16_t*>(p)[i] = f32_to_bf16(x);
 }
 
 // Orders this wave's LDS accesses in the compiler's schedule (the hardware completes one
@@ -382,123 +329,243 @@ __device__ __forceinline__ void wave_lds_order() {
     asm volatile("" ::: "memory");
 }
 
-template <int DK, int DV, int BV, int TB, class TIn, bool VERIFY>
-__global__ __launch_bounds__(kWave, 2) void decode_multi_kernel(DecodeArgs a) {
-    using C = DecTile<DK, DV, BV>;
-    __shared__ TokenLds<DK, BV, TB> L;
+// One reduce-scatter step over lane bit M: 2N values per lane -> N, the lane keeping the
+// upper half when its bit M is set.
+template <int N, int M>
+__device__ __forceinline__ void rs_step(const float (&v)[2 * N], float (&w)[N], int lane) {
+    const bool hi = (lane & M) != 0;
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        const float keep = hi ? v[i + N] : v[i];
+        const float send = hi ? v[i] : v[i + N];
+        w[i] = keep + __shfl_xor(send, M, kWave);
+    }
+}
+
+template <int DK, int DV, class TIn, bool VERIFY>
+__global__ __launch_bounds__(kWave, 2) void wy_multi_kernel(DecodeArgs a) {
+    constexpr int BV = 64, NT = DV / BV, EPL = DK / kWave;
+    using LD = WyLds<DK>;
+    constexpr int KS = LD::KS;
+    __shared__ LD L;
 
     const int lane = threadIdx.x;
-    const int tile = blockIdx.x % C::NT;
-    const int nh = blockIdx.x / C::NT;
+    const int tile = blockIdx.x % NT;
+    const int nh = blockIdx.x / NT;
     const int h = nh % a.H, n = nh / a.H;
-    const int c4 = lane % C::NC4, rq = lane / C::NC4;
-    const int col0 = tile * BV + 4 * c4;
     const int slot = a.slot_idx[n];
+    const int64_t tok0 = static_cast<int64_t>(n) * a.T * a.H + h;  // token t: tok0 + t * H
 
     if (slot < 0) {  // skipped sequence: zero outputs, no state access
-        for (int idx = lane; idx < a.T * C::NC4; idx += kWave) {
-            const int t = idx / C::NC4, c = idx % C::NC4;
-            const int64_t tok = (static_cast<int64_t>(n) * a.T + t) * a.H + h;
-            store4<TIn>(a.o, tok * DV + tile * BV + 4 * c, make_float4(0.f, 0.f, 0.f, 0.f));
-        }
+        for (int t = 0; t < a.T; ++t) store1<TIn>(a.o, (tok0 + static_cast<int64_t>(t) * a.H) * DV + tile * BV + lane, 0.f);
         return;
     }
     float* S = a.pool + (static_cast<int64_t>(slot) * a.H + h) * (DK * DV);
     const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(S, 0, DK * DV * 4, kBufFlags);
-    const int voff = (rq * DV + col0) * 4;
+    const int lq = lane >> 4, lm = lane & 15;
+    const int voff = (lq * DV + tile * BV + 4 * lm) * 4;
 
-    // The state tile's loads go out first and stream while the tokens are prepared, PG
-    // tokens at a time (their input loads all issued before any is used).
-    constexpr int PG = TB < 2 ? TB : 2;  // tokens whose input loads are in flight together
-    auto prep_block = [&](int tb, int nb) {
-        for (int j0 = 0; j0 < nb; j0 += PG) {
-            PrepIn<DK, DV, BV> pin[PG];
+    float4 sv[KS];
+    // one block of tokens; the first one (FIRST, a compile-time flag, so its loads stay in
+    // straight-line code) also issues the state tile's loads
+    auto block = [&](int tb, auto first) {
+        constexpr bool FIRST = decltype(first)::value;
+        const int nb = min(kWyTB, a.T - tb);
+        // (1) token inputs of the block: lane l owns key channels EPL l .. EPL l + EPL - 1
+        float kh[kWyTB][EPL], qh[kWyTB][EPL], G[kWyTB][EPL], vt[kWyTB], bt[kWyTB];
+        // branch-free: tokens past the block's end load the last token's inputs (a valid
+        // address) and are zeroed afterwards, so every load is in flight before the first wait
 #pragma unroll
-            for (int j = 0; j < PG; ++j)
-                if (j0 + j < nb) pin[j] = prep_load<DK, DV, BV, TIn>(a, n, tb + j0 + j, h, tile, lane);
-#pragma unroll
-            for (int j = 0; j < PG; ++j)
-                if (j0 + j < nb) prep_store<DK, DV, BV, TB, VERIFY>(a, L, j0 + j, n, tb + j0 + j, h, tile, lane, pin[j]);
+        for (int t = 0; t < kWyTB; ++t) {
+            const int64_t tok = tok0 + static_cast<int64_t>(tb + min(t, nb - 1)) * a.H;
+            const int64_t rowk = tok * DK + EPL * lane;
+            if constexpr (EPL == 2) {
+                const float2 qq = load2<TIn>(a.q, rowk), kk = load2<TIn>(a.k, rowk);
+                const float2 gg = *reinterpret_cast<const float2*>(a.g + rowk);
+                qh[t][0] = qq.x; qh[t][1] = qq.y;
+                kh[t][0] = kk.x; kh[t][1] = kk.y;
+                G[t][0] = gg.x; G[t][1] = gg.y;
+            } else {
+                qh[t][0] = load1<TIn>(a.q, rowk);
+                kh[t][0] = load1<TIn>(a.k, rowk);
+                G[t][0] = a.g[rowk];
+            }
+            vt[t] = load1<TIn>(a.v, tok * DV + tile * BV + lane);
+            bt[t] = a.beta[tok];
         }
-    };
-    float4 s[C::NW][C::RPT];
-    auto load_state = [&]() {
+        asm volatile("" ::: "memory");  // keeps every load above in flight before any use
+        // the state tile's loads go out after the first block's token loads: loads complete
+        // in issue order, so the token preparation below overlaps the tile's arrival
+        if constexpr (FIRST) {
 #pragma unroll
-        for (int w = 0; w < C::NW; ++w)
+            for (int st = 0; st < KS; ++st) sv[st] = state_load4(srs, voff, 4 * st * DV * 4);
+            asm volatile("" ::: "memory");  // ... issued here, before the preparation
+        }
+        // L2 norms, alpha, in-block gate cumsum; X, kh and alpha rows into LDS (branch-free,
+        // so the loads' wait counts stay exact; tokens past the block's end become zeros)
 #pragma unroll
-            for (int i = 0; i < C::RPT; ++i) s[w][i] = state_load4(srs, voff, (4 * w + C::NRG * i) * DV * 4);
-    };
-    load_state();
-
-    for (int tb = 0; tb < a.T; tb += TB) {
-        const int nb = min(TB, a.T - tb);
-        prep_block(tb, nb);
-        wave_lds_order();
-
-        for (int j = 0; j < nb; ++j) {
-            const int t = tb + j;
-            float4 tk, tq;
+        for (int t = 0; t < kWyTB; ++t) {
+            const bool live = t < nb;
+            float sq = 0.f, sk = 0.f;
 #pragma unroll
-            for (int w = 0; w < C::NW; ++w) {
-                const int g0 = (4 * w + rq) * C::RPT;
-                const float4* a4 = reinterpret_cast<const float4*>(&L.a[j][g0]);
-                const float4* k4 = reinterpret_cast<const float4*>(&L.k[j][g0]);
-                const float4* q4 = reinterpret_cast<const float4*>(&L.q[j][g0]);
-                float4 pk = make_float4(0.f, 0.f, 0.f, 0.f), pq = pk;
+            for (int e = 0; e < EPL; ++e) {
+                sq = fmaf(qh[t][e], qh[t][e], sq);
+                sk = fmaf(kh[t][e], kh[t][e], sk);
+            }
+            sq = wave_sum(sq);
+            sk = wave_sum(sk);
+            const float iq = a.use_l2 ? 1.f / sqrtf(sq + kNormEps) : 1.f;
+            const float ik = a.use_l2 ? 1.f / sqrtf(sk + kNormEps) : 1.f;
+            vt[t] = live ? vt[t] : 0.f;
+            bt[t] = live ? bt[t] : 0.f;
 #pragma unroll
-                for (int i4 = 0; i4 < C::RPT / 4; ++i4) {
-                    const float4 av = a4[i4], kv = k4[i4], qv = q4[i4];
-                    const float al[4] = {av.x, av.y, av.z, av.w};
-                    const float kk[4] = {kv.x, kv.y, kv.z, kv.w};
-                    const float qq[4] = {qv.x, qv.y, qv.z, qv.w};
+            for (int e = 0; e < EPL; ++e) {
+                const int c = EPL * lane + e;
+                const float g = live ? G[t][e] : 0.f;
+                const float al = expf(g);
+                G[t][e] = t == 0 ? g : G[t - 1][e] + g;
+                kh[t][e] = live ? kh[t][e] * ik : 0.f;
+                qh[t][e] = live ? qh[t][e] * iq : 0.f;
+                const float eg = expf(G[t][e]);
+                L.xp[t][c & 3][c >> 2] = kh[t][e] * eg;
+                L.xp[8 + t][c & 3][c >> 2] = qh[t][e] * eg;
+                L.kr[t][c & 3][c >> 2] = kh[t][e];
+                L.ar[t][c & 3][c >> 2] = al;
+            }
+        }
+        if (VERIFY && tile == 0) {  // the kh and alpha parts of the records, from LDS
+            wave_lds_order();
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        float4& x = s[w][4 * i4 + r];
-                        x = f4_mul(x, al[r]);            // decay
-                        pk = f4_scale_fma(kk[r], x, pk);  // S'^T k
-                        pq = f4_scale_fma(qq[r], x, pq);  // S'^T q
+            for (int t = 0; t < kWyTB; ++t) {
+                if (t < nb) {
+                    float* rec = a.records + (tok0 + static_cast<int64_t>(tb + t) * a.H) * (2 * DK + DV);
+#pragma unroll
+                    for (int e = 0; e < EPL; ++e) {
+                        const int c = EPL * lane + e;
+                        rec[c] = L.kr[t][c & 3][c >> 2];
+                        rec[DK + c] = L.ar[t][c & 3][c >> 2];
                     }
                 }
-                // row groups 4w + rq in order w = 0..3
-                if (w == 0) {
-                    tk = pk;
-                    tq = pq;
-                } else {
-                    tk = f4_add(tk, pk);
-                    tq = f4_add(tq, pq);
-                }
-            }
-            tk = quad_sum(tk);  // then the four lane positions rq pairwise
-            tq = quad_sum(tq);
-            const float4 vv = *reinterpret_cast<const float4*>(&L.v[j][4 * c4]);
-            const float b = L.beta[j], kq = L.kq[j];
-            const float4 u = f4_mul(f4_sub(vv, tk), b);                 // beta * delta
-            const float4 ov = f4_mul(f4_scale_fma(kq, u, tq), a.scale);  // scale S^T q
-#pragma unroll
-            for (int w = 0; w < C::NW; ++w) {
-                const float4* k4 = reinterpret_cast<const float4*>(&L.k[j][(4 * w + rq) * C::RPT]);
-#pragma unroll
-                for (int i4 = 0; i4 < C::RPT / 4; ++i4) {
-                    const float4 kv = k4[i4];
-                    const float kk[4] = {kv.x, kv.y, kv.z, kv.w};
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) s[w][4 * i4 + r] = f4_scale_fma(kk[r], u, s[w][4 * i4 + r]);
-                }
-            }
-            if (rq == 0) {
-                const int64_t tok = (static_cast<int64_t>(n) * a.T + t) * a.H + h;
-                store4<TIn>(a.o, tok * DV + col0, ov);
-                if (VERIFY)
-                    *reinterpret_cast<float4*>(a.records + tok * (2 * DK + DV) + 2 * DK + col0) = u;
             }
         }
-        if (tb + TB < a.T) wave_lds_order();  // the next block's vectors overwrite L
-    }
+        // (2) the block's 64 dot products: partial sums over this lane's channels, values i
+        // and i + 32 together, then the reduce-scatter (lane l keeps value l)
+        float r32[32];
+        {
+            const bool up = (lane & 32) != 0;
+            // the first step (lane bit 32) as each pair is formed: value i (kk) and i + 32 (qk)
+            auto first = [&](int i, float lo, float hi) {
+                const float keep = up ? hi : lo, send = up ? lo : hi;
+                r32[i] = keep + __shfl_xor(send, 32, kWave);
+            };
+#pragma unroll
+            for (int ta = 1; ta < kWyTB; ++ta)
+#pragma unroll
+                for (int sb = 0; sb < ta; ++sb) {
+                    float kk = 0.f, qk = 0.f;
+#pragma unroll
+                    for (int e = 0; e < EPL; ++e) {
+                        const float w = kh[sb][e] * expf(G[ta][e] - G[sb][e]);
+                        kk = fmaf(kh[ta][e], w, kk);
+                        qk = fmaf(qh[ta][e], w, qk);
+                    }
+                    first(wy_pair(ta, sb), kk, qk);
+                }
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {  // the diagonal qk_tt (t < 4) and qk_{t+4, t+4}
+                float d0 = 0.f, d1 = 0.f;
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) {
+                    d0 = fmaf(qh[t][e], kh[t][e], d0);
+                    d1 = fmaf(qh[t + 4][e], kh[t + 4][e], d1);
+                }
+                first(wy_diag(t), d0, d1);
+            }
+        }
+        float r16[16], r8[8], r4[4], r2[2], r1[1];
+        rs_step<16, 16>(r32, r16, lane);
+        rs_step<8, 8>(r16, r8, lane);
+        rs_step<4, 4>(r8, r4, lane);
+        rs_step<2, 2>(r4, r2, lane);
+        rs_step<1, 1>(r2, r1, lane);
+        L.pq[lane] = r1[0];
+        wave_lds_order();
+
+        // (3) R = S0^T X on fp32 MFMA: acc[e] holds R rows (tile columns) 16 lq + 4 i + e,
+        // i = 0..3, of vector lm
+        f32x4 acc[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[e] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < KS / 4; ++i) {
+            const f32x4 bx = *reinterpret_cast<const f32x4*>(&L.xp[lm][lq][4 * i]);
+#pragma unroll
+            for (int k4 = 0; k4 < 4; ++k4) {
+                const float4 x = sv[4 * i + k4];
+                acc[0] = __builtin_amdgcn_mfma_f32_16x16x4f32(x.x, bx[k4], acc[0], 0, 0, 0);
+                acc[1] = __builtin_amdgcn_mfma_f32_16x16x4f32(x.y, bx[k4], acc[1], 0, 0, 0);
+                acc[2] = __builtin_amdgcn_mfma_f32_16x16x4f32(x.z, bx[k4], acc[2], 0, 0, 0);
+                acc[3] = __builtin_amdgcn_mfma_f32_16x16x4f32(x.w, bx[k4], acc[3], 0, 0, 0);
+            }
+        }
+        wave_lds_order();  // the X reads above precede the R^T writes into the same LDS
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) L.rt[16 * lq + 4 * i + e][lm] = acc[e][i];
+        wave_lds_order();
+
+        // (4) per column j = lane: u and o of the block's tokens
+        float rk[16];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const f32x4 x = *reinterpret_cast<const f32x4*>(&L.rt[lane][4 * i]);
+            rk[4 * i] = x[0]; rk[4 * i + 1] = x[1]; rk[4 * i + 2] = x[2]; rk[4 * i + 3] = x[3];
+        }
+        float u[kWyTB];
+#pragma unroll
+        for (int t = 0; t < kWyTB; ++t) {
+            u[t] = 0.f;
+            if (t < nb) {
+                float d = vt[t] - rk[t];
+#pragma unroll
+                for (int sb = 0; sb < t; ++sb) d = fmaf(-L.pq[wy_pair(t, sb)], u[sb], d);
+                u[t] = bt[t] * d;
+                float o = rk[8 + t];
+#pragma unroll
+                for (int sb = 0; sb < t; ++sb) o = fmaf(L.pq[32 + wy_pair(t, sb)], u[sb], o);
+                o = fmaf(L.pq[wy_diag(t)], u[t], o);
+                const int64_t tok = tok0 + static_cast<int64_t>(tb + t) * a.H;
+                store1<TIn>(a.o, tok * DV + tile * BV + lane, o * a.scale);
+                if (VERIFY) a.records[tok * (2 * DK + DV) + 2 * DK + tile * BV + lane] = u[t];
+                L.ut[t][lane] = u[t];
+            }
+        }
+
+        // (5) the state update, in token order with the replay kernel's operations
+        if (!VERIFY || tb + kWyTB < a.T) {
+            wave_lds_order();
+            for (int t = 0; t < nb; ++t) {
+                const float4 uu = *reinterpret_cast<const float4*>(&L.ut[t][4 * lm]);
+#pragma unroll
+                for (int i = 0; i < KS / 4; ++i) {
+                    const f32x4 al = *reinterpret_cast<const f32x4*>(&L.ar[t][lq][4 * i]);
+                    const f32x4 kv = *reinterpret_cast<const f32x4*>(&L.kr[t][lq][4 * i]);
+#pragma unroll
+                    for (int k4 = 0; k4 < 4; ++k4) {
+                        float4& x = sv[4 * i + k4];
+                        x = f4_scale_fma(kv[k4], uu, f4_mul(x, al[k4]));
+                    }
+                }
+            }
+        }
+        wave_lds_order();  // the next block's writes follow every read of this one
+    };
+    block(0, std::true_type{});
+    for (int tb = kWyTB; tb < a.T; tb += kWyTB) block(tb, std::false_type{});
     if (!VERIFY) {
 #pragma unroll
-        for (int w = 0; w < C::NW; ++w)
-#pragma unroll
-            for (int i = 0; i < C::RPT; ++i) state_store4(srs, voff, (4 * w + C::NRG * i) * DV * 4, s[w][i]);
+        for (int st = 0; st < KS; ++st) state_store4(srs, voff, 4 * st * DV * 4, sv[st]);
     }
 }
 
@@ -562,34 +629,24 @@ __global__ __launch_bounds__(kThreads) void replay_kernel(ReplayArgs a) {
     for (int i = 0; i < C::RPT; ++i) store_stream4(S + (rg + C::RG * i) * DV + col0, s[i]);
 }
 
-// T = 1: four-wave workgroups (HBM-bound); T > 1: one wave per tile (the token steps
-// are VALU-bound, and a wave-local reduction needs no barrier).  Both reduce over dk in the
-// same order, so their results are bit-identical.
-template <int DK, int DV, int BV, int TB, class TIn>
-hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
-    const dim3 grid(static_cast<unsigned>(a.N) * a.H * (DV / BV));
-    if constexpr (TB == 1) {
-        if (a.records)
-            hipLaunchKernelGGL((decode_kernel<DK, DV, BV, TB, TIn, true>), grid, dim3(kThreads), 0, stream, a);
-        else
-            hipLaunchKernelGGL((decode_kernel<DK, DV, BV, TB, TIn, false>), grid, dim3(kThreads), 0, stream, a);
-    } else {
-        if (a.records)
-            hipLaunchKernelGGL((decode_multi_kernel<DK, DV, BV, TB, TIn, true>), grid, dim3(kWave), 0, stream, a);
-        else
-            hipLaunchKernelGGL((decode_multi_kernel<DK, DV, BV, TB, TIn, false>), grid, dim3(kWave), 0, stream, a);
-    }
-    return hipGetLastError();
-}
-
-// dv tiles of 64 columns, one wave each.  The tile fixes the order of the dk reductions, so
-// every T uses the same one: the u a verify call records is then bit-identical to the u a
-// commit call computes, and replaying records reproduces a commit exactly.
+// T = 1: four-wave workgroups per 64-column tile (HBM-bound, decode_kernel).  T > 1: one
+// wave per 64-column tile, the WY form of 8-token blocks (wy_multi_kernel).
 template <int DK, int DV, class TIn>
 hipError_t launch_decode_d(const DecodeArgs& a, hipStream_t stream) {
     constexpr int BV = DV < 64 ? DV : 64;
-    if (a.T == 1) return launch_decode_t<DK, DV, BV, 1, TIn>(a, stream);
-    return launch_decode_t<DK, DV, BV, 8, TIn>(a, stream);
+    const dim3 grid(static_cast<unsigned>(a.N) * a.H * (DV / BV));
+    if (a.T == 1) {
+        if (a.records)
+            hipLaunchKernelGGL((decode_kernel<DK, DV, BV, 1, TIn, true>), grid, dim3(kThreads), 0, stream, a);
+        else
+            hipLaunchKernelGGL((decode_kernel<DK, DV, BV, 1, TIn, false>), grid, dim3(kThreads), 0, stream, a);
+    } else {
+        if (a.records)
+            hipLaunchKernelGGL((wy_multi_kernel<DK, DV, TIn, true>), grid, dim3(kWave), 0, stream, a);
+        else
+            hipLaunchKernelGGL((wy_multi_kernel<DK, DV, TIn, false>), grid, dim3(kWave), 0, stream, a);
+    }
+    return hipGetLastError();
 }
 
 template <class TIn>
