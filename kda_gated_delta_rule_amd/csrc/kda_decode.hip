@@ -292,6 +292,7 @@ __global__ __launch_bounds__(kThreads, 5) void decode_kernel(DecodeArgs a) {
 // ---------------------------------------------------------------------------
 constexpr int kWyTB = 8;  // tokens per block
 constexpr int kWyRt = 20; // R^T row stride (floats): 16 vectors, rows 16-byte aligned
+constexpr float kLog2e = 1.4426950408889634f;
 
 template <int DK>
 struct WyLds {
@@ -373,60 +374,106 @@ __global__ __launch_bounds__(kWave, 2) void wy_multi_kernel(DecodeArgs a) {
         const int nb = min(kWyTB, a.T - tb);
         // (1) token inputs of the block: lane l owns key channels EPL l .. EPL l + EPL - 1
         float kh[kWyTB][EPL], qh[kWyTB][EPL], G[kWyTB][EPL], vt[kWyTB], bt[kWyTB];
+        // bf16 inputs arrive as raw words (a dword holds a lane's two channels) and are
+        // widened only after the state loads are issued
+        constexpr bool kBf = std::is_same<TIn, BF16>::value;
+        uint32_t qw[kWyTB], kw[kWyTB], vw[kWyTB];
         // branch-free: tokens past the block's end load the last token's inputs (a valid
         // address) and are zeroed afterwards, so every load is in flight before the first wait
 #pragma unroll
         for (int t = 0; t < kWyTB; ++t) {
             const int64_t tok = tok0 + static_cast<int64_t>(tb + min(t, nb - 1)) * a.H;
             const int64_t rowk = tok * DK + EPL * lane;
-            if constexpr (EPL == 2) {
-                const float2 qq = load2<TIn>(a.q, rowk), kk = load2<TIn>(a.k, rowk);
-                const float2 gg = *reinterpret_cast<const float2*>(a.g + rowk);
-                qh[t][0] = qq.x; qh[t][1] = qq.y;
-                kh[t][0] = kk.x; kh[t][1] = kk.y;
-                G[t][0] = gg.x; G[t][1] = gg.y;
+            const int64_t iv = tok * DV + tile * BV + lane;
+            if constexpr (kBf) {
+                const uint16_t* q16 = static_cast<const uint16_t*>(a.q);
+                const uint16_t* k16 = static_cast<const uint16_t*>(a.k);
+                if constexpr (EPL == 2) {
+                    qw[t] = *reinterpret_cast<const uint32_t*>(q16 + rowk);
+                    kw[t] = *reinterpret_cast<const uint32_t*>(k16 + rowk);
+                } else {
+                    qw[t] = q16[rowk];
+                    kw[t] = k16[rowk];
+                }
+                vw[t] = static_cast<const uint16_t*>(a.v)[iv];
             } else {
-                qh[t][0] = load1<TIn>(a.q, rowk);
-                kh[t][0] = load1<TIn>(a.k, rowk);
-                G[t][0] = a.g[rowk];
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) {
+                    qh[t][e] = static_cast<const float*>(a.q)[rowk + e];
+                    kh[t][e] = static_cast<const float*>(a.k)[rowk + e];
+                }
+                vt[t] = static_cast<const float*>(a.v)[iv];
             }
-            vt[t] = load1<TIn>(a.v, tok * DV + tile * BV + lane);
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) G[t][e] = a.g[rowk + e];
             bt[t] = a.beta[tok];
         }
-        asm volatile("" ::: "memory");  // keeps every load above in flight before any use
+        __builtin_amdgcn_sched_barrier(0);  // every load above is in flight before any use
         // the state tile's loads go out after the first block's token loads: loads complete
         // in issue order, so the token preparation below overlaps the tile's arrival
         if constexpr (FIRST) {
 #pragma unroll
             for (int st = 0; st < KS; ++st) sv[st] = state_load4(srs, voff, 4 * st * DV * 4);
-            asm volatile("" ::: "memory");  // ... issued here, before the preparation
+            // ... issued here, before the preparation: nothing is scheduled across this point
+            // (widening the token words above the state loads would make them wait for the
+            // token loads)
+            __builtin_amdgcn_sched_barrier(0);
         }
-        // L2 norms, alpha, in-block gate cumsum; X, kh and alpha rows into LDS (branch-free,
-        // so the loads' wait counts stay exact; tokens past the block's end become zeros)
+        if constexpr (kBf) {
+#pragma unroll
+            for (int t = 0; t < kWyTB; ++t) {
+                qh[t][0] = __uint_as_float(qw[t] << 16);
+                kh[t][0] = __uint_as_float(kw[t] << 16);
+                if constexpr (EPL == 2) {
+                    qh[t][1] = __uint_as_float(qw[t] & 0xffff0000u);
+                    kh[t][1] = __uint_as_float(kw[t] & 0xffff0000u);
+                }
+                vt[t] = __uint_as_float(vw[t] << 16);
+            }
+        }
+        // L2 norms: the 16 sums of squares (q and k of 8 tokens) in one reduce-scatter over the
+        // wave (lane l ends with sum (l >> 2)), then broadcast through scalar registers
+        float nrm[2 * kWyTB];
 #pragma unroll
         for (int t = 0; t < kWyTB; ++t) {
-            const bool live = t < nb;
             float sq = 0.f, sk = 0.f;
 #pragma unroll
             for (int e = 0; e < EPL; ++e) {
                 sq = fmaf(qh[t][e], qh[t][e], sq);
                 sk = fmaf(kh[t][e], kh[t][e], sk);
             }
-            sq = wave_sum(sq);
-            sk = wave_sum(sk);
-            const float iq = a.use_l2 ? 1.f / sqrtf(sq + kNormEps) : 1.f;
-            const float ik = a.use_l2 ? 1.f / sqrtf(sk + kNormEps) : 1.f;
-            vt[t] = live ? vt[t] : 0.f;
+            nrm[t] = sq;
+            nrm[kWyTB + t] = sk;
+        }
+        float n8[8], n4[4], n2[2], n1[1];
+        rs_step<8, 32>(nrm, n8, lane);
+        rs_step<4, 16>(n8, n4, lane);
+        rs_step<2, 8>(n4, n2, lane);
+        rs_step<1, 4>(n2, n1, lane);
+        float tot = n1[0];
+        tot += __shfl_xor(tot, 2, kWave);
+        tot += __shfl_xor(tot, 1, kWave);
+        // alpha = 2^(g log2 e), the in-block gate cumsum in log2 units, X, kh and alpha rows
+        // into LDS (branch-free, so the loads' wait counts stay exact; tokens past the block's
+        // end become zeros)
+#pragma unroll
+        for (int t = 0; t < kWyTB; ++t) {
+            const bool live = t < nb;
+            const float sq = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(tot), 4 * t));
+            const float sk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(tot), 4 * (kWyTB + t)));
+            const float iq = a.use_l2 ? __builtin_amdgcn_rsqf(sq + kNormEps) : 1.f;
+            const float ik = a.use_l2 ? __builtin_amdgcn_rsqf(sk + kNormEps) : 1.f;
+            L.ut[t][lane] = live ? vt[t] : 0.f;  // v waits in this lane's u slot until the solve
             bt[t] = live ? bt[t] : 0.f;
 #pragma unroll
             for (int e = 0; e < EPL; ++e) {
                 const int c = EPL * lane + e;
-                const float g = live ? G[t][e] : 0.f;
-                const float al = expf(g);
-                G[t][e] = t == 0 ? g : G[t - 1][e] + g;
+                const float g2 = live ? G[t][e] * kLog2e : 0.f;
+                const float al = __builtin_amdgcn_exp2f(g2);
+                G[t][e] = t == 0 ? g2 : G[t - 1][e] + g2;
                 kh[t][e] = live ? kh[t][e] * ik : 0.f;
                 qh[t][e] = live ? qh[t][e] * iq : 0.f;
-                const float eg = expf(G[t][e]);
+                const float eg = __builtin_amdgcn_exp2f(G[t][e]);
                 L.xp[t][c & 3][c >> 2] = kh[t][e] * eg;
                 L.xp[8 + t][c & 3][c >> 2] = qh[t][e] * eg;
                 L.kr[t][c & 3][c >> 2] = kh[t][e];
@@ -465,7 +512,7 @@ __global__ __launch_bounds__(kWave, 2) void wy_multi_kernel(DecodeArgs a) {
                     float kk = 0.f, qk = 0.f;
 #pragma unroll
                     for (int e = 0; e < EPL; ++e) {
-                        const float w = kh[sb][e] * expf(G[ta][e] - G[sb][e]);
+                        const float w = kh[sb][e] * __builtin_amdgcn_exp2f(G[ta][e] - G[sb][e]);
                         kk = fmaf(kh[ta][e], w, kk);
                         qk = fmaf(qh[ta][e], w, qk);
                     }
@@ -527,7 +574,7 @@ __global__ __launch_bounds__(kWave, 2) void wy_multi_kernel(DecodeArgs a) {
         for (int t = 0; t < kWyTB; ++t) {
             u[t] = 0.f;
             if (t < nb) {
-                float d = vt[t] - rk[t];
+                float d = L.ut[t][lane] - rk[t];
 #pragma unroll
                 for (int sb = 0; sb < t; ++sb) d = fmaf(-L.pq[wy_pair(t, sb)], u[sb], d);
                 u[t] = bt[t] * d;
