@@ -22,7 +22,8 @@
 //    gfx950 row-swap instructions (v_permlane16_swap, v_permlane32_swap).  Per-token
 //    vectors (qh, kh, alpha, v, beta, k.q) are prepared by one wave per token into LDS.
 //  * T > 1 (wy_multi_kernel, MTP / verify): the WY form of 8-token blocks (see the
-//    kernel): one fp32 MFMA pass over the register-resident tile gives the 16 products
+//    kernel), one workgroup per head with a wave per 64-column tile (the waves split the
+//    block's preparation): one fp32 MFMA pass over the register-resident tile gives the 16 products
 //    with the entering state, a per-column 8x8 triangular solve gives u and o, and the
 //    state is updated only when it is kept (commit, or between blocks) -- with the
 //    replay kernel's fp32 operations, so replaying verify records reproduces a commit of
@@ -283,7 +284,7 @@ __global__ __launch_bounds__(kThreads, 5) void decode_kernel(DecodeArgs a) {
 // operations, so replaying a verify call's records gives, bit for bit, the state a commit
 // of the same tokens gives.
 //
-// One wave per (sequence, head, 64-column tile).  The state tile is loaded with 16-byte
+// A wave per (sequence, head, 64-column tile).  The state tile is loaded with 16-byte
 // loads, lane l holding rows 4 s + l / 16 (s = 0 .. dk/4 - 1), columns 4 (l % 16) .. + 3:
 // component e of the k-step-s register is exactly the A operand of a 16x16x4 fp32 MFMA
 // (row m = l % 16 <-> tile column 4 m + e, k = l / 16), so the product needs no
@@ -294,17 +295,21 @@ constexpr int kWyTB = 8;  // tokens per block
 constexpr int kWyRt = 20; // R^T row stride (floats): 16 vectors, rows 16-byte aligned
 constexpr float kLog2e = 1.4426950408889634f;
 
-template <int DK>
+// LDS of one head: the block's operands (shared by the head's waves) and each wave's R^T and
+// u areas.
+template <int DK, int NW>
 struct WyLds {
     static constexpr int KS = DK / 4;  // fp32 MFMA k-steps over dk
-    union {
-        float xp[16][4][KS];   // X[4 s + q][n] at [n][q][s]: n < 8 kh_n e^G_n, n >= 8 qh e^G
-        float rt[64][kWyRt];   // R^T: tile column j, vector n
+    struct Wave {
+        float rt[64][kWyRt];           // R^T: tile column j, vector n
+        float ut[kWyTB][64];           // v, then u, of the tile's columns
     };
-    float kr[kWyTB][4][KS];    // kh_t of row 4 s + q at [t][q][s]
-    float ar[kWyTB][4][KS];    // alpha_t likewise
-    float ut[kWyTB][64];       // u_t of the tile's columns
-    float pq[64];              // kk and qk of the block (index: see wy_pair)
+    float xp[16][4][KS];               // X[4 s + q][n] at [n][q][s]: n < 8 kh_n e^G_n, n >= 8 qh e^G
+    float kr[kWyTB][4][KS];            // kh_t of row 4 s + q at [t][q][s]
+    float ar[kWyTB][4][KS];            // alpha_t likewise
+    float pq[64];                      // dot products of the raw q and k (index: see wy_pair)
+    float nf[2 * kWyTB];               // norm factors: 1/|q_t| at t, 1/|k_t| at 8 + t
+    Wave w[NW];
 };
 
 // Dot-product index of the pair (a, b), a > b: kk_ab at wy_pair(a, b), qk_ab at 32 + that;
@@ -343,21 +348,26 @@ __device__ __forceinline__ void rs_step(const float (&v)[2 * N], float (&w)[N], 
     }
 }
 
+// One workgroup per (sequence, head): wave w holds the 64-column tile w.  The block's
+// preparation is split between the waves: wave 0 forms the norms and the X, kh and alpha
+// rows, wave 1 the 64 dot products of the raw q and k (scaled by the norms in the solve);
+// with a single tile (dv = 64) one wave does both.
 template <int DK, int DV, class TIn, bool VERIFY>
-__global__ __launch_bounds__(kWave, 2) void wy_multi_kernel(DecodeArgs a) {
-    constexpr int BV = 64, NT = DV / BV, EPL = DK / kWave;
-    using LD = WyLds<DK>;
+__global__ __launch_bounds__(kWave * (DV / 64), 2) void wy_multi_kernel(DecodeArgs a) {
+    constexpr int BV = 64, NW = DV / BV, EPL = DK / kWave;
+    using LD = WyLds<DK, NW>;
     constexpr int KS = LD::KS;
     __shared__ LD L;
 
-    const int lane = threadIdx.x;
-    const int tile = blockIdx.x % NT;
-    const int nh = blockIdx.x / NT;
-    const int h = nh % a.H, n = nh / a.H;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int tile = NW == 1 ? 0 : __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
+    const bool norm_role = NW == 1 || tile == 0, dot_role = NW == 1 || tile == 1;
+    const int h = blockIdx.x % a.H, n = blockIdx.x / a.H;
     const int slot = a.slot_idx[n];
     const int64_t tok0 = static_cast<int64_t>(n) * a.T * a.H + h;  // token t: tok0 + t * H
+    auto& Wv = L.w[tile];
 
-    if (slot < 0) {  // skipped sequence: zero outputs, no state access
+    if (slot < 0) {  // skipped sequence (the whole workgroup): zero outputs, no state access
         for (int t = 0; t < a.T; ++t) store1<TIn>(a.o, (tok0 + static_cast<int64_t>(t) * a.H) * DV + tile * BV + lane, 0.f);
         return;
     }
@@ -365,6 +375,11 @@ __global__ __launch_bounds__(kWave, 2) void wy_multi_kernel(DecodeArgs a) {
     const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(S, 0, DK * DV * 4, kBufFlags);
     const int lq = lane >> 4, lm = lane & 15;
     const int voff = (lq * DV + tile * BV + 4 * lm) * 4;
+    // orders the head's LDS exchanges: a workgroup barrier with two waves, program order with one
+    auto sync = [&]() {
+        if constexpr (NW > 1) lds_barrier();
+        else wave_lds_order();
+    };
 
     float4 sv[KS];
     // one block of tokens; the first one (FIRST, a compile-time flag, so its loads stay in
@@ -431,77 +446,30 @@ __global__ __launch_bounds__(kWave, 2) void wy_multi_kernel(DecodeArgs a) {
                 vt[t] = __uint_as_float(vw[t] << 16);
             }
         }
-        // L2 norms: the 16 sums of squares (q and k of 8 tokens) in one reduce-scatter over the
-        // wave (lane l ends with sum (l >> 2)), then broadcast through scalar registers
-        float nrm[2 * kWyTB];
-#pragma unroll
-        for (int t = 0; t < kWyTB; ++t) {
-            float sq = 0.f, sk = 0.f;
-#pragma unroll
-            for (int e = 0; e < EPL; ++e) {
-                sq = fmaf(qh[t][e], qh[t][e], sq);
-                sk = fmaf(kh[t][e], kh[t][e], sk);
-            }
-            nrm[t] = sq;
-            nrm[kWyTB + t] = sk;
-        }
-        float n8[8], n4[4], n2[2], n1[1];
-        rs_step<8, 32>(nrm, n8, lane);
-        rs_step<4, 16>(n8, n4, lane);
-        rs_step<2, 8>(n4, n2, lane);
-        rs_step<1, 4>(n2, n1, lane);
-        float tot = n1[0];
-        tot += __shfl_xor(tot, 2, kWave);
-        tot += __shfl_xor(tot, 1, kWave);
-        // alpha = 2^(g log2 e), the in-block gate cumsum in log2 units, X, kh and alpha rows
-        // into LDS (branch-free, so the loads' wait counts stay exact; tokens past the block's
-        // end become zeros)
+        // tokens past the block's end become zeros; the gates go to log2 units and their
+        // in-block cumsum; v waits in this wave's u slots until the solve
 #pragma unroll
         for (int t = 0; t < kWyTB; ++t) {
             const bool live = t < nb;
-            const float sq = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(tot), 4 * t));
-            const float sk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(tot), 4 * (kWyTB + t)));
-            const float iq = a.use_l2 ? __builtin_amdgcn_rsqf(sq + kNormEps) : 1.f;
-            const float ik = a.use_l2 ? __builtin_amdgcn_rsqf(sk + kNormEps) : 1.f;
-            L.ut[t][lane] = live ? vt[t] : 0.f;  // v waits in this lane's u slot until the solve
+            Wv.ut[t][lane] = live ? vt[t] : 0.f;
             bt[t] = live ? bt[t] : 0.f;
 #pragma unroll
             for (int e = 0; e < EPL; ++e) {
                 const int c = EPL * lane + e;
                 const float g2 = live ? G[t][e] * kLog2e : 0.f;
-                const float al = __builtin_amdgcn_exp2f(g2);
+                if (norm_role) L.ar[t][c & 3][c >> 2] = __builtin_amdgcn_exp2f(g2);  // alpha
                 G[t][e] = t == 0 ? g2 : G[t - 1][e] + g2;
-                kh[t][e] = live ? kh[t][e] * ik : 0.f;
-                qh[t][e] = live ? qh[t][e] * iq : 0.f;
-                const float eg = __builtin_amdgcn_exp2f(G[t][e]);
-                L.xp[t][c & 3][c >> 2] = kh[t][e] * eg;
-                L.xp[8 + t][c & 3][c >> 2] = qh[t][e] * eg;
-                L.kr[t][c & 3][c >> 2] = kh[t][e];
-                L.ar[t][c & 3][c >> 2] = al;
+                kh[t][e] = live ? kh[t][e] : 0.f;
+                qh[t][e] = live ? qh[t][e] : 0.f;
             }
         }
-        if (VERIFY && tile == 0) {  // the kh and alpha parts of the records, from LDS
-            wave_lds_order();
-#pragma unroll
-            for (int t = 0; t < kWyTB; ++t) {
-                if (t < nb) {
-                    float* rec = a.records + (tok0 + static_cast<int64_t>(tb + t) * a.H) * (2 * DK + DV);
-#pragma unroll
-                    for (int e = 0; e < EPL; ++e) {
-                        const int c = EPL * lane + e;
-                        rec[c] = L.kr[t][c & 3][c >> 2];
-                        rec[DK + c] = L.ar[t][c & 3][c >> 2];
-                    }
-                }
-            }
-        }
-        // (2) the block's 64 dot products: partial sums over this lane's channels, values i
-        // and i + 32 together, then the reduce-scatter (lane l keeps value l)
-        float r32[32];
-        {
+
+        // (2a) the 64 dot products of the raw q and k: partial sums over this lane's channels,
+        // values i and i + 32 together, then the reduce-scatter (lane l keeps value l)
+        if (dot_role) {
+            float r32[32];
             const bool up = (lane & 32) != 0;
-            // the first step (lane bit 32) as each pair is formed: value i (kk) and i + 32 (qk)
-            auto first = [&](int i, float lo, float hi) {
+            auto first_step = [&](int i, float lo, float hi) {
                 const float keep = up ? hi : lo, send = up ? lo : hi;
                 r32[i] = keep + __shfl_xor(send, 32, kWave);
             };
@@ -516,7 +484,7 @@ __global__ __launch_bounds__(kWave, 2) void wy_multi_kernel(DecodeArgs a) {
                         kk = fmaf(kh[ta][e], w, kk);
                         qk = fmaf(qh[ta][e], w, qk);
                     }
-                    first(wy_pair(ta, sb), kk, qk);
+                    first_step(wy_pair(ta, sb), kk, qk);
                 }
 #pragma unroll
             for (int t = 0; t < 4; ++t) {  // the diagonal qk_tt (t < 4) and qk_{t+4, t+4}
@@ -526,17 +494,71 @@ __global__ __launch_bounds__(kWave, 2) void wy_multi_kernel(DecodeArgs a) {
                     d0 = fmaf(qh[t][e], kh[t][e], d0);
                     d1 = fmaf(qh[t + 4][e], kh[t + 4][e], d1);
                 }
-                first(wy_diag(t), d0, d1);
+                first_step(wy_diag(t), d0, d1);
+            }
+            float r16[16], r8[8], r4[4], r2[2], r1[1];
+            rs_step<16, 16>(r32, r16, lane);
+            rs_step<8, 8>(r16, r8, lane);
+            rs_step<4, 4>(r8, r4, lane);
+            rs_step<2, 2>(r4, r2, lane);
+            rs_step<1, 1>(r2, r1, lane);
+            L.pq[lane] = r1[0];
+        }
+        // (2b) the norms (16 sums of squares in one reduce-scatter: lane l ends with sum l >> 2),
+        // then kh and X = [kh e^G | qh e^G] rows into LDS (alpha went there above)
+        if (norm_role) {
+            float nrm[2 * kWyTB];
+#pragma unroll
+            for (int t = 0; t < kWyTB; ++t) {
+                float sq = 0.f, sk = 0.f;
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) {
+                    sq = fmaf(qh[t][e], qh[t][e], sq);
+                    sk = fmaf(kh[t][e], kh[t][e], sk);
+                }
+                nrm[t] = sq;
+                nrm[kWyTB + t] = sk;
+            }
+            float n8[8], n4[4], n2[2], n1[1];
+            rs_step<8, 32>(nrm, n8, lane);
+            rs_step<4, 16>(n8, n4, lane);
+            rs_step<2, 8>(n4, n2, lane);
+            rs_step<1, 4>(n2, n1, lane);
+            float tot = n1[0];
+            tot += __shfl_xor(tot, 2, kWave);
+            tot += __shfl_xor(tot, 1, kWave);
+            const float f = a.use_l2 ? __builtin_amdgcn_rsqf(tot + kNormEps) : 1.f;
+            if ((lane & 3) == 0) L.nf[lane >> 2] = f;
+#pragma unroll
+            for (int t = 0; t < kWyTB; ++t) {
+                const float iq = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(f), 4 * t));
+                const float ik = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(f), 4 * (kWyTB + t)));
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) {
+                    const int c = EPL * lane + e;
+                    const float k1 = kh[t][e] * ik, q1 = qh[t][e] * iq;
+                    const float eg = __builtin_amdgcn_exp2f(G[t][e]);
+                    L.xp[t][c & 3][c >> 2] = k1 * eg;
+                    L.xp[8 + t][c & 3][c >> 2] = q1 * eg;
+                    L.kr[t][c & 3][c >> 2] = k1;
+                }
             }
         }
-        float r16[16], r8[8], r4[4], r2[2], r1[1];
-        rs_step<16, 16>(r32, r16, lane);
-        rs_step<8, 8>(r16, r8, lane);
-        rs_step<4, 4>(r8, r4, lane);
-        rs_step<2, 2>(r4, r2, lane);
-        rs_step<1, 1>(r2, r1, lane);
-        L.pq[lane] = r1[0];
-        wave_lds_order();
+        sync();
+        if (VERIFY && tile == 0) {  // the kh and alpha parts of the records, from LDS
+#pragma unroll
+            for (int t = 0; t < kWyTB; ++t) {
+                if (t < nb) {
+                    float* rec = a.records + (tok0 + static_cast<int64_t>(tb + t) * a.H) * (2 * DK + DV);
+#pragma unroll
+                    for (int e = 0; e < EPL; ++e) {
+                        const int c = EPL * lane + e;
+                        rec[c] = L.kr[t][c & 3][c >> 2];
+                        rec[DK + c] = L.ar[t][c & 3][c >> 2];
+                    }
+                }
+            }
+        }
 
         // (3) R = S0^T X on fp32 MFMA: acc[e] holds R rows (tile columns) 16 lq + 4 i + e,
         // i = 0..3, of vector lm
@@ -555,18 +577,18 @@ __global__ __launch_bounds__(kWave, 2) void wy_multi_kernel(DecodeArgs a) {
                 acc[3] = __builtin_amdgcn_mfma_f32_16x16x4f32(x.w, bx[k4], acc[3], 0, 0, 0);
             }
         }
-        wave_lds_order();  // the X reads above precede the R^T writes into the same LDS
 #pragma unroll
         for (int e = 0; e < 4; ++e)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) L.rt[16 * lq + 4 * i + e][lm] = acc[e][i];
+            for (int i = 0; i < 4; ++i) Wv.rt[16 * lq + 4 * i + e][lm] = acc[e][i];
         wave_lds_order();
 
-        // (4) per column j = lane: u and o of the block's tokens
+        // (4) per column j = lane: u and o of the block's tokens, the dot products scaled by
+        // the norm factors (kk_ts = ik_t ik_s kk_raw, qk_ts = iq_t ik_s qk_raw)
         float rk[16];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const f32x4 x = *reinterpret_cast<const f32x4*>(&L.rt[lane][4 * i]);
+            const f32x4 x = *reinterpret_cast<const f32x4*>(&Wv.rt[lane][4 * i]);
             rk[4 * i] = x[0]; rk[4 * i + 1] = x[1]; rk[4 * i + 2] = x[2]; rk[4 * i + 3] = x[3];
         }
         float u[kWyTB];
@@ -574,18 +596,21 @@ __global__ __launch_bounds__(kWave, 2) void wy_multi_kernel(DecodeArgs a) {
         for (int t = 0; t < kWyTB; ++t) {
             u[t] = 0.f;
             if (t < nb) {
-                float d = L.ut[t][lane] - rk[t];
+                const float iq = L.nf[t], ik = L.nf[kWyTB + t];
+                float d = Wv.ut[t][lane] - rk[t];
 #pragma unroll
-                for (int sb = 0; sb < t; ++sb) d = fmaf(-L.pq[wy_pair(t, sb)], u[sb], d);
+                for (int sb = 0; sb < t; ++sb)
+                    d = fmaf(-(L.pq[wy_pair(t, sb)] * ik * L.nf[kWyTB + sb]), u[sb], d);
                 u[t] = bt[t] * d;
                 float o = rk[8 + t];
 #pragma unroll
-                for (int sb = 0; sb < t; ++sb) o = fmaf(L.pq[32 + wy_pair(t, sb)], u[sb], o);
-                o = fmaf(L.pq[wy_diag(t)], u[t], o);
+                for (int sb = 0; sb < t; ++sb)
+                    o = fmaf(L.pq[32 + wy_pair(t, sb)] * iq * L.nf[kWyTB + sb], u[sb], o);
+                o = fmaf(L.pq[wy_diag(t)] * iq * ik, u[t], o);
                 const int64_t tok = tok0 + static_cast<int64_t>(tb + t) * a.H;
                 store1<TIn>(a.o, tok * DV + tile * BV + lane, o * a.scale);
                 if (VERIFY) a.records[tok * (2 * DK + DV) + 2 * DK + tile * BV + lane] = u[t];
-                L.ut[t][lane] = u[t];
+                Wv.ut[t][lane] = u[t];
             }
         }
 
@@ -593,20 +618,20 @@ __global__ __launch_bounds__(kWave, 2) void wy_multi_kernel(DecodeArgs a) {
         if (!VERIFY || tb + kWyTB < a.T) {
             wave_lds_order();
             for (int t = 0; t < nb; ++t) {
-                const float4 uu = *reinterpret_cast<const float4*>(&L.ut[t][4 * lm]);
+                const float4 uu = *reinterpret_cast<const float4*>(&Wv.ut[t][4 * lm]);
 #pragma unroll
                 for (int i = 0; i < KS / 4; ++i) {
-                    const f32x4 al = *reinterpret_cast<const f32x4*>(&L.ar[t][lq][4 * i]);
+                    const f32x4 alv = *reinterpret_cast<const f32x4*>(&L.ar[t][lq][4 * i]);
                     const f32x4 kv = *reinterpret_cast<const f32x4*>(&L.kr[t][lq][4 * i]);
 #pragma unroll
                     for (int k4 = 0; k4 < 4; ++k4) {
                         float4& x = sv[4 * i + k4];
-                        x = f4_scale_fma(kv[k4], uu, f4_mul(x, al[k4]));
+                        x = f4_scale_fma(kv[k4], uu, f4_mul(x, alv[k4]));
                     }
                 }
             }
         }
-        wave_lds_order();  // the next block's writes follow every read of this one
+        sync();  // the next block's writes follow every read of this one, in both waves
     };
     block(0, std::true_type{});
     for (int tb = kWyTB; tb < a.T; tb += kWyTB) block(tb, std::false_type{});
@@ -677,7 +702,8 @@ __global__ __launch_bounds__(kThreads) void replay_kernel(ReplayArgs a) {
 }
 
 // T = 1: four-wave workgroups per 64-column tile (HBM-bound, decode_kernel).  T > 1: one
-// wave per 64-column tile, the WY form of 8-token blocks (wy_multi_kernel).
+// workgroup per head, a wave per 64-column tile, the WY form of 8-token blocks
+// (wy_multi_kernel).
 template <int DK, int DV, class TIn>
 hipError_t launch_decode_d(const DecodeArgs& a, hipStream_t stream) {
     constexpr int BV = DV < 64 ? DV : 64;
@@ -688,10 +714,11 @@ hipError_t launch_decode_d(const DecodeArgs& a, hipStream_t stream) {
         else
             hipLaunchKernelGGL((decode_kernel<DK, DV, BV, 1, TIn, false>), grid, dim3(kThreads), 0, stream, a);
     } else {
+        const dim3 hgrid(static_cast<unsigned>(a.N) * a.H), hblock(kWave * (DV / 64));
         if (a.records)
-            hipLaunchKernelGGL((wy_multi_kernel<DK, DV, TIn, true>), grid, dim3(kWave), 0, stream, a);
+            hipLaunchKernelGGL((wy_multi_kernel<DK, DV, TIn, true>), hgrid, hblock, 0, stream, a);
         else
-            hipLaunchKernelGGL((wy_multi_kernel<DK, DV, TIn, false>), grid, dim3(kWave), 0, stream, a);
+            hipLaunchKernelGGL((wy_multi_kernel<DK, DV, TIn, false>), hgrid, hblock, 0, stream, a);
     }
     return hipGetLastError();
 }
