@@ -98,27 +98,47 @@ def test_mtp_multi_token(T):
     assert rel_l2(f64(pool.cpu()[x["slot_idx"].long()]), h_ref) <= 1e-4
 
 
+@pytest.mark.parametrize("T", [1, 3])
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
-def test_slot_mapping_bit_exact(dtype):
-    """beta = 0, g = 0, no norm, scale = 1, q = e_i: o[n, h] = S[slot_n, h, i, :] exactly
-    (rounded by the hardware bf16 conversion in bf16 mode, which must equal torch's cast),
-    and every slot of the pool is byte-identical afterwards."""
+def test_slot_mapping_bit_exact(dtype, T):
+    """beta = 0, g = 0, no norm, scale = 1, q = e_i for every token: o[n, t, h] = S[slot_n, h,
+    i, :] exactly (rounded by the hardware bf16 conversion in bf16 mode, which must equal
+    torch's cast), and every slot of the pool is byte-identical afterwards.  T = 1 runs the
+    one-token kernel, T = 3 the multi-token one (its fp32 MFMA sums S0 entries times 1 and
+    0, which is exact)."""
     dev = need_gpu()
-    announce("decode slot mapping %s" % dtype)
+    announce("decode slot mapping %s T=%d" % (dtype, T))
     N, H, d, num_slots = 24, 4, 128, 64
     gen = torch.Generator().manual_seed(7)
     pool = torch.randn(num_slots, H, d, d, generator=gen) * 3.0
     slots = torch.randperm(num_slots, generator=gen)[:N].to(torch.int32)
     rows = torch.randint(0, d, (N, H), generator=gen)
-    q = torch.zeros(N, 1, H, d)
-    q[torch.arange(N)[:, None], 0, torch.arange(H)[None, :], rows] = 1.0
-    x = dict(q=q.to(dtype), k=torch.randn(N, 1, H, d, generator=gen).to(dtype),
-             v=torch.randn(N, 1, H, d, generator=gen).to(dtype), g=torch.zeros(N, 1, H, d),
-             beta=torch.zeros(N, 1, H), pool=pool, slot_idx=slots)
+    q = torch.zeros(N, T, H, d)
+    q[torch.arange(N)[:, None, None], torch.arange(T)[None, :, None], torch.arange(H)[None, None, :],
+      rows[:, None, :]] = 1.0
+    x = dict(q=q.to(dtype), k=torch.randn(N, T, H, d, generator=gen).to(dtype),
+             v=torch.randn(N, T, H, d, generator=gen).to(dtype), g=torch.zeros(N, T, H, d),
+             beta=torch.zeros(N, T, H), pool=pool, slot_idx=slots)
     o, pool_after, _ = run_decode(x, dev, scale=1.0, use_qk_l2norm=False)
     expect = pool[slots.long()[:, None], torch.arange(H)[None, :], rows]  # [N, H, d]
-    assert torch.equal(o.cpu()[:, 0], expect.to(dtype))
+    for t in range(T):
+        assert torch.equal(o.cpu()[:, t], expect.to(dtype)), t
     assert torch.equal(pool_after.cpu(), pool)
+
+
+@pytest.mark.parametrize("T", [5, 11])
+def test_mtp_without_l2norm(T):
+    """use_qk_l2norm = 0 on the multi-token kernel (its norm factors are then 1): fp32
+    parity of outputs and states, within and across 8-token blocks."""
+    dev = need_gpu()
+    announce("MTP without l2 norm T=%d" % T)
+    x = W.decode(seed=10, N=4, T=T, H=2, dk=128, dv=128, num_slots=8, dtype=torch.float32)
+    x["q"] = x["q"] * 0.1
+    x["k"] = torch.nn.functional.normalize(x["k"], dim=-1)
+    o, pool, _ = run_decode(x, dev, use_qk_l2norm=False)
+    o_ref, h_ref, _ = oracle_decode(x, use_qk_l2norm=False)
+    assert rel_l2(f64(o), o_ref) <= 1e-4
+    assert rel_l2(f64(pool.cpu()[x["slot_idx"].long()]), h_ref) <= 1e-4
 
 
 @pytest.mark.parametrize("T", [1, 2])
