@@ -73,8 +73,8 @@ def test_decode_pool_full_size(seed):
 @pytest.mark.parametrize("dk,dv", [(64, 64), (64, 128), (128, 64)])
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
 def test_decode_head_dims(dk, dv, dtype, T):
-    """Both decode kernels (T = 1: four-wave tiles; T > 1: one-wave tiles) at every head
-    shape."""
+    """Both decode kernels (T = 1: four-wave tiles; T > 1: the multi-token kernel, one wave
+    per 64-column tile) at every head shape."""
     dev = need_gpu()
     announce("decode dims dk=%d dv=%d %s T=%d" % (dk, dv, dtype, T))
     x = W.decode(seed=3, N=5, T=T, H=3, dk=dk, dv=dv, num_slots=9, dtype=dtype)
