@@ -178,28 +178,58 @@ def bench_verify_replay(args, dev, log):
 
     x = W.verify(seed=0)
     N, T, H, dk, dv = x["q"].shape[0], x["q"].shape[1], x["q"].shape[2], 128, 128
+    ns = x["pool"].shape[0]
     pool = x["pool"].to(dev)
     q, k, v, g, beta = (x[n].to(dev) for n in ("q", "k", "v", "g", "beta"))
-    slots, acc = x["slot_idx"].to(dev), x["accepted"].to(dev)
+    acc = x["accepted"].to(dev)
+    # disjoint N-slot sets covering the pool (1 GiB, more than the 256 MB Infinity Cache), one
+    # per step in turn, so the state is read from HBM; set 0 is the workload's own slot set
+    rest = [s for s in torch.randperm(ns, generator=torch.Generator().manual_seed(2)).tolist()
+            if s not in set(x["slot_idx"].tolist())]
+    sets = [x["slot_idx"]] + [torch.tensor(rest[i * N:(i + 1) * N], dtype=torch.int32)
+                              for i in range(ns // N - 1)]
+    sets = [st.to(dev) for st in sets]
     rec = torch.empty(N, T, H, 2 * dk + dv, device=dev)
     o = torch.empty_like(q)
     pool_bytes = dk * dv * 4
 
     def step(i):
-        kda.decode_step(q, k, v, g, beta, pool, slots, o=o, records=rec)
-        kda.replay_commit(pool, slots, rec, acc)
+        sl = sets[i % len(sets)]
+        kda.decode_step(q, k, v, g, beta, pool, sl, o=o, records=rec)
+        kda.replay_commit(pool, sl, rec, acc)
 
-    iters = max(10, args.steps // 4)
+    iters = max(len(sets), args.steps // 4)
     for i in range(3):
         step(i)
-    total, per = time_loop(step, iters, torch.cuda.synchronize)
+    _, per_eager = time_loop(step, iters, torch.cuda.synchronize)
+    # replayed from one captured HIP graph, as the decode step
+    gr = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step(0)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(gr):
+        for i in range(iters):
+            step(i)
+    gr.replay()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record()
+    gr.replay()
+    ev1.record()
+    torch.cuda.synchronize()
+    per = ev0.elapsed_time(ev1) / 1e3 / iters
     acc_sum = int(x["accepted"].sum())
     verify_bytes = N * H * (pool_bytes + T * ((2 * dk + dv) * 2 + dk * 4 + 4 + dv * 2 +
                                                (2 * dk + dv) * 4))
     commit_bytes = N * H * 2 * pool_bytes + acc_sum * H * (2 * dk + dv) * 4
     gbs = (verify_bytes + commit_bytes) / per / 1e9
-    log("verify+replay: %.2f us/step, %.1f GB/s" % (per * 1e6, gbs))
+    log("verify+replay: %.2f us/step (graph; %.2f us eager), %.1f GB/s" % (per * 1e6, per_eager * 1e6, gbs))
     return {"workload": W.VERIFY["name"], "us_per_step": per * 1e6,
+            "timing": "graph replay of %d steps, %d disjoint slot sets in turn" % (iters, len(sets)),
+            "us_per_step_eager": per_eager * 1e6,
             "sequence_tokens_per_s": N * T / per, "accepted_tokens": acc_sum,
             "algorithmic_bytes": verify_bytes + commit_bytes, "achieved_GBs": gbs,
             "hbm_frac": gbs / HBM_PEAK_GBS}
@@ -230,16 +260,37 @@ def bench_prefill(args, dev, log, which):
     iters = max(5, args.steps // 10)
     for i in range(2):
         step(i)
-    total, per = time_loop(step, iters, torch.cuda.synchronize)
+    _, per_eager = time_loop(step, iters, torch.cuda.synchronize)
+    # As decode: the calls replayed from one captured HIP graph (as serving engines run the
+    # prefill), HIP-event time per call.
+    gr = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step(0)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(gr):
+        for i in range(iters):
+            step(i)
+    gr.replay()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record()
+    gr.replay()
+    ev1.record()
+    torch.cuda.synchronize()
+    per = ev0.elapsed_time(ev1) / 1e3 / iters
     th = Tt * H
     flops = th * prefill_flops_per_token_head(dk, dv)
     byts = th * prefill_bytes_per_token_head(dk, dv, 2)
     tflops = flops / per / 1e12
     gbs = byts / per / 1e9
-    log("%s: %.1f us/call, %.3g tokens/s, %.1f TFLOP/s (%.1f%% MFMA), %.0f GB/s (%.1f%% HBM)"
-        % (name, per * 1e6, Tt / per, tflops, 100 * tflops / BF16_PEAK_TFLOPS, gbs,
-           100 * gbs / HBM_PEAK_GBS))
-    return {"workload": name, "us_per_call": per * 1e6, "tokens_per_s": Tt / per,
+    log("%s: %.1f us/call (graph; %.1f us eager), %.3g tokens/s, %.1f TFLOP/s (%.1f%% MFMA), "
+        "%.0f GB/s (%.1f%% HBM)" % (name, per * 1e6, per_eager * 1e6, Tt / per, tflops,
+                                    100 * tflops / BF16_PEAK_TFLOPS, gbs, 100 * gbs / HBM_PEAK_GBS))
+    return {"workload": name, "us_per_call": per * 1e6, "timing": "graph replay of %d calls" % iters,
+            "us_per_call_eager": per_eager * 1e6, "tokens_per_s": Tt / per,
             "token_heads_per_s": th / per, "algorithmic_flops": flops, "algorithmic_bytes": byts,
             "achieved_TFLOPs": tflops, "mfma_frac": tflops / BF16_PEAK_TFLOPS,
             "achieved_GBs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS,
@@ -250,8 +301,8 @@ def bench_prefill(args, dev, log, which):
 
 def bench_prefill_snapshots(args, dev, log, plain_us):
     """The T = 8192 x H = 32 prefill with prefix-cache snapshots every 1,024 tokens (8 states
-    per head written to extra pool slots); reports the time per call and the cost over the
-    plain call."""
+    per head written to extra pool slots); reports the eager time per call and the cost over
+    the plain call timed the same way."""
     import torch
 
     import kda_gated_delta_rule_amd as kda
@@ -278,7 +329,7 @@ def bench_prefill_snapshots(args, dev, log, plain_us):
     for i in range(2):
         step(i)
     total, per = time_loop(step, iters, torch.cuda.synchronize)
-    log("%s with %d snapshots per head: %.1f us/call (plain %.1f us)"
+    log("%s with %d snapshots per head: %.1f us/call eager (plain %.1f us eager)"
         % (W.PREFILL["name"], nsnap, per * 1e6, plain_us))
     return {"workload": W.PREFILL["name"] + "_snapshots_every1024", "snapshot_every": every,
             "snapshots_per_head": nsnap, "snapshot_bytes": nsnap * H * dk * dv * 4,
@@ -377,7 +428,7 @@ def main():
         extra["prefill"] = bench_prefill(args, dev, log, "prefill")
         extra["prefill_varlen"] = bench_prefill(args, dev, log, "varlen")
         extra["prefill_snapshots"] = bench_prefill_snapshots(args, dev, log,
-                                                             extra["prefill"]["us_per_call"])
+                                                             extra["prefill"]["us_per_call_eager"])
     cpu = None if args.decode_only else cpu_baseline(dec["inputs"], log)
 
     import kda_workloads as W
