@@ -352,7 +352,9 @@ __device__ __forceinline__ void rs_step(const float (&v)[2 * N], float (&w)[N], 
 // preparation is split between the waves: wave 0 forms the norms and the X, kh and alpha
 // rows, wave 1 the 64 dot products of the raw q and k (scaled by the norms in the solve);
 // with a single tile (dv = 64) one wave does both.
-template <int DK, int DV, class TIn, bool VERIFY>
+// ONEBLK: a verify call of at most 8 tokens (one block, no state update), where the state
+// registers are free after the MFMA pass.
+template <int DK, int DV, class TIn, bool VERIFY, bool ONEBLK>
 __global__ __launch_bounds__(kWave * (DV / 64), 2) void wy_multi_kernel(DecodeArgs a) {
     constexpr int BV = 64, NW = DV / BV, EPL = DK / kWave;
     using LD = WyLds<DK, NW>;
@@ -591,11 +593,14 @@ __global__ __launch_bounds__(kWave * (DV / 64), 2) void wy_multi_kernel(DecodeAr
             const f32x4 x = *reinterpret_cast<const f32x4*>(&Wv.rt[lane][4 * i]);
             rk[4 * i] = x[0]; rk[4 * i + 1] = x[1]; rk[4 * i + 2] = x[2]; rk[4 * i + 3] = x[3];
         }
-        float u[kWyTB];
+        if constexpr (ONEBLK) {
+            // branch-free over the 8 tokens, so the coefficient reads of later tokens overlap
+            // the chain of earlier ones (the registers allow it once the state is dead): tokens
+            // past the block's end have beta = 0 and zero operands, so their u is 0, and their o
+            // is never stored.  Live tokens take the same operations as the branch below.
+            float u[kWyTB], ov[kWyTB];
 #pragma unroll
-        for (int t = 0; t < kWyTB; ++t) {
-            u[t] = 0.f;
-            if (t < nb) {
+            for (int t = 0; t < kWyTB; ++t) {
                 const float iq = L.nf[t], ik = L.nf[kWyTB + t];
                 float d = Wv.ut[t][lane] - rk[t];
 #pragma unroll
@@ -606,16 +611,45 @@ __global__ __launch_bounds__(kWave * (DV / 64), 2) void wy_multi_kernel(DecodeAr
 #pragma unroll
                 for (int sb = 0; sb < t; ++sb)
                     o = fmaf(L.pq[32 + wy_pair(t, sb)] * iq * L.nf[kWyTB + sb], u[sb], o);
-                o = fmaf(L.pq[wy_diag(t)] * iq * ik, u[t], o);
-                const int64_t tok = tok0 + static_cast<int64_t>(tb + t) * a.H;
-                store1<TIn>(a.o, tok * DV + tile * BV + lane, o * a.scale);
-                if (VERIFY) a.records[tok * (2 * DK + DV) + 2 * DK + tile * BV + lane] = u[t];
+                ov[t] = fmaf(L.pq[wy_diag(t)] * iq * ik, u[t], o) * a.scale;
+            }
+            wave_lds_order();  // the v reads above precede the u writes into the same slots
+#pragma unroll
+            for (int t = 0; t < kWyTB; ++t) {
                 Wv.ut[t][lane] = u[t];
+                if (t < nb) {
+                    const int64_t tok = tok0 + static_cast<int64_t>(tb + t) * a.H;
+                    store1<TIn>(a.o, tok * DV + tile * BV + lane, ov[t]);
+                    if (VERIFY) a.records[tok * (2 * DK + DV) + 2 * DK + tile * BV + lane] = u[t];
+                }
+            }
+        } else {
+            float u[kWyTB];
+#pragma unroll
+            for (int t = 0; t < kWyTB; ++t) {
+                u[t] = 0.f;
+                if (t < nb) {
+                    const float iq = L.nf[t], ik = L.nf[kWyTB + t];
+                    float d = Wv.ut[t][lane] - rk[t];
+#pragma unroll
+                    for (int sb = 0; sb < t; ++sb)
+                        d = fmaf(-(L.pq[wy_pair(t, sb)] * ik * L.nf[kWyTB + sb]), u[sb], d);
+                    u[t] = bt[t] * d;
+                    float o = rk[8 + t];
+#pragma unroll
+                    for (int sb = 0; sb < t; ++sb)
+                        o = fmaf(L.pq[32 + wy_pair(t, sb)] * iq * L.nf[kWyTB + sb], u[sb], o);
+                    o = fmaf(L.pq[wy_diag(t)] * iq * ik, u[t], o);
+                    const int64_t tok = tok0 + static_cast<int64_t>(tb + t) * a.H;
+                    store1<TIn>(a.o, tok * DV + tile * BV + lane, o * a.scale);
+                    if (VERIFY) a.records[tok * (2 * DK + DV) + 2 * DK + tile * BV + lane] = u[t];
+                    Wv.ut[t][lane] = u[t];
+                }
             }
         }
 
         // (5) the state update, in token order with the replay kernel's operations
-        if (!VERIFY || tb + kWyTB < a.T) {
+        if (!VERIFY || (!ONEBLK && tb + kWyTB < a.T)) {
             wave_lds_order();
             for (int t = 0; t < nb; ++t) {
                 const float4 uu = *reinterpret_cast<const float4*>(&Wv.ut[t][4 * lm]);
@@ -634,7 +668,8 @@ __global__ __launch_bounds__(kWave * (DV / 64), 2) void wy_multi_kernel(DecodeAr
         sync();  // the next block's writes follow every read of this one, in both waves
     };
     block(0, std::true_type{});
-    for (int tb = kWyTB; tb < a.T; tb += kWyTB) block(tb, std::false_type{});
+    if constexpr (!ONEBLK)
+        for (int tb = kWyTB; tb < a.T; tb += kWyTB) block(tb, std::false_type{});
     if (!VERIFY) {
 #pragma unroll
         for (int st = 0; st < KS; ++st) state_store4(srs, voff, 4 * st * DV * 4, sv[st]);
@@ -715,10 +750,12 @@ hipError_t launch_decode_d(const DecodeArgs& a, hipStream_t stream) {
             hipLaunchKernelGGL((decode_kernel<DK, DV, BV, 1, TIn, false>), grid, dim3(kThreads), 0, stream, a);
     } else {
         const dim3 hgrid(static_cast<unsigned>(a.N) * a.H), hblock(kWave * (DV / 64));
-        if (a.records)
-            hipLaunchKernelGGL((wy_multi_kernel<DK, DV, TIn, true>), hgrid, hblock, 0, stream, a);
+        if (a.records && a.T <= kWyTB)
+            hipLaunchKernelGGL((wy_multi_kernel<DK, DV, TIn, true, true>), hgrid, hblock, 0, stream, a);
+        else if (a.records)
+            hipLaunchKernelGGL((wy_multi_kernel<DK, DV, TIn, true, false>), hgrid, hblock, 0, stream, a);
         else
-            hipLaunchKernelGGL((wy_multi_kernel<DK, DV, TIn, false>), hgrid, hblock, 0, stream, a);
+            hipLaunchKernelGGL((wy_multi_kernel<DK, DV, TIn, false, false>), hgrid, hblock, 0, stream, a);
     }
     return hipGetLastError();
 }
