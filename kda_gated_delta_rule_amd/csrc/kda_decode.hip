@@ -279,10 +279,10 @@ __global__ __launch_bounds__(kThreads, 5) void decode_kernel(DecodeArgs a) {
 //   u_t = beta_t (v_t - RK_t - sum_{s<t} kk_ts u_s),  kk_ts = sum_c kh_tc kh_sc e^{G_tc - G_sc}
 //   o_t = scale (RQ_t + sum_{s<=t} qk_ts u_s),        qk_ts = sum_c qh_tc kh_sc e^{G_tc - G_sc}
 // (the token recurrence rearranged, exact in exact arithmetic).  A verify call never
-// updates the state.  A commit (and a call of more than 8 tokens, between blocks) then
-// applies S <- diag(alpha_t) S + kh_t u_t^T in token order with the replay kernel's fp32
-// operations, so replaying a verify call's records gives, bit for bit, the state a commit
-// of the same tokens gives.
+// writes the pool.  A commit, and any call of more than 8 tokens between its blocks (on the
+// register copy), applies S <- diag(alpha_t) S + kh_t u_t^T in token order with the replay
+// kernel's fp32 operations, so replaying a verify call's records gives, bit for bit, the
+// state a commit of the same two or more tokens gives.
 //
 // A wave per (sequence, head, 64-column tile).  The state tile is loaded with 16-byte
 // loads, lane l holding rows 4 s + l / 16 (s = 0 .. dk/4 - 1), columns 4 (l % 16) .. + 3:
