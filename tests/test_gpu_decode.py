@@ -241,6 +241,32 @@ def test_mtp_strong_decay(verify):
             assert rel_l2(f64(pool.cpu()[x["slot_idx"].long()]), h_ref) <= 1e-4
 
 
+@pytest.mark.parametrize("T", [3, 5])
+def test_verify_short_block(T):
+    """Verify calls of fewer than 8 tokens (the one-block kernel, whose solve also runs over
+    the absent tokens of the block): fp32 parity of outputs and records, the pool untouched,
+    and replaying every prefix of two or more tokens equals committing it bit for bit."""
+    dev = need_gpu()
+    announce("verify short block T=%d" % T)
+    x = W.decode(seed=11, N=6, T=T, H=3, dk=128, dv=128, num_slots=12, dtype=torch.float32,
+                 with_accepted=True)
+    x["accepted"] = torch.tensor([T, 2, T, 2, T, 2][:6], dtype=torch.int32)
+    o, pool_v, rec = run_decode(x, dev, records=True)
+    o_ref, _, rec_ref = oracle_decode(x, want_records=True)
+    assert rel_l2(f64(o), o_ref) <= 1e-4
+    assert rel_l2(f64(rec), rec_ref) <= 1e-4
+    assert torch.equal(pool_v.cpu(), x["pool"])
+    acc = x["accepted"]
+    kda.replay_commit(pool_v, x["slot_idx"].to(dev), rec, acc.to(dev))
+    pool_c = x["pool"].to(dev)
+    for a in sorted(set(int(v) for v in acc)):
+        idx = (acc == a).nonzero().flatten()
+        args = [x[n][idx, :a].contiguous().to(dev) for n in NAMES]
+        kda.decode_step(*args, pool_c, x["slot_idx"][idx].contiguous().to(dev))
+    torch.cuda.synchronize()
+    assert torch.equal(pool_v.cpu(), pool_c.cpu())
+
+
 def test_replay_accept_zero_and_skip():
     dev = need_gpu()
     announce("replay accepted=0 and skipped slot")
