@@ -299,3 +299,55 @@ def test_invariant_beta1_unit_key_on_gpu():
     k = f64(x["k"])[:, 0]
     got = np.einsum("nhcj,nhc->nhj", S, k)
     assert np.abs(got - f64(x["v"])[:, 0]).max() <= 1e-5 * max(1.0, np.abs(S).max())
+
+
+def test_pool_offsets_beyond_32_bits():
+    """Slots whose state lies beyond 2^31 elements (9 GB into a 9.2 GB pool of 140,100 slots of
+    [1, 128, 128] fp32): the one-token and multi-token kernels, verify + replay, and the prefill
+    (initial and final state in such slots) match the oracle, and the neighbouring slots keep
+    their sentinel values."""
+    dev = need_gpu()
+    announce("pool offsets beyond 32 bits")
+    S, d = 140_100, 128
+    big = torch.empty(S, 1, d, d, device=dev)
+    far = torch.tensor([140_050, 70_001, 139_998], dtype=torch.int32)
+    sentinels = torch.cat([far.long() - 1, far.long() + 1])
+    for T in (1, 3):
+        x = W.decode(seed=12 + T, N=3, T=T, H=1, dk=d, dv=d, num_slots=3, dtype=torch.float32)
+        sl = x["slot_idx"].long()
+        big[far.long()] = x["pool"][sl].to(dev)
+        big[sentinels] = 7.0
+        args = [x[n].to(dev) for n in NAMES]
+        o = kda.decode_step(*args, big, far.to(dev))
+        torch.cuda.synchronize()
+        o_ref, h_ref, _ = oracle_decode(x)
+        assert rel_l2(f64(o), o_ref) <= 1e-4, T
+        assert rel_l2(f64(big[far.long()].cpu()), h_ref) <= 1e-4, T
+        assert bool((big[sentinels] == 7.0).all()), T
+    # verify + replay through the same far slots
+    x = W.decode(seed=20, N=3, T=4, H=1, dk=d, dv=d, num_slots=3, dtype=torch.float32, with_accepted=True)
+    sl = x["slot_idx"].long()
+    big[far.long()] = x["pool"][sl].to(dev)
+    rec = torch.empty(3, 4, 1, 3 * d, device=dev)
+    kda.decode_step(*(x[n].to(dev) for n in NAMES), big, far.to(dev), records=rec)
+    assert torch.equal(big[far.long()].cpu(), x["pool"][sl])
+    kda.replay_commit(big, far.to(dev), rec, x["accepted"].to(dev))
+    torch.cuda.synchronize()
+    for n in range(3):
+        a = int(x["accepted"][n])
+        _, h_n, _ = O.decode(*(f64(x[nm][n:n + 1, :a]) for nm in NAMES), f64(x["pool"][sl[n:n + 1]]))
+        assert rel_l2(f64(big[far.long()[n]].cpu()), h_n[0]) <= 1e-4, n
+    assert bool((big[sentinels] == 7.0).all())
+    # prefill: initial states read from, final states written to far slots
+    y = W.prefill(seed=21, seqlens=(100, 37), H=1, dk=d, dv=d, num_slots=2, h0_std=0.05)
+    far2 = torch.tensor([140_020, 90_000], dtype=torch.int32)
+    big[far2.long()] = y["pool"][y["slot_idx"].long()].to(dev)
+    o = kda.chunk_prefill(*(y[n].to(dev) for n in ("q", "k", "v", "g", "beta", "cu_seqlens")), big,
+                          far2.to(dev), h0_from_pool=True)
+    torch.cuda.synchronize()
+    o_ref, h_ref, _ = O.recurrent(f64(y["q"]), f64(y["k"]), f64(y["v"]), f64(y["g"]), f64(y["beta"]),
+                                  y["cu_seqlens"].numpy(), h0=f64(y["pool"][y["slot_idx"].long()]))
+    assert rel_l2(f64(o), o_ref) <= 1e-2
+    assert rel_l2(f64(big[far2.long()].cpu()), h_ref) <= 1e-2
+    del big
+    torch.cuda.empty_cache()
