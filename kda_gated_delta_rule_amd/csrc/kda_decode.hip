@@ -176,7 +176,7 @@ __device__ __forceinline__ void prep_token(const DecodeArgs& a, TokenLds<DK, BV,
 template <int DK, int DV, int BV, int TB, class TIn, bool VERIFY>
 __global__ __launch_bounds__(kThreads, 5) void decode_kernel(DecodeArgs a) {
     using C = Tile<DK, DV, BV>;
-    __shared__ TokenLds<DK, BV, TB> L;
+    __shared__ __attribute__((aligned(16))) TokenLds<DK, BV, TB> L;  // read as float4
     __shared__ float4 red[2][kWaves][kWave][2];
 
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
@@ -359,7 +359,7 @@ __global__ __launch_bounds__(kWave * (DV / 64), 2) void wy_multi_kernel(DecodeAr
     constexpr int BV = 64, NW = DV / BV, EPL = DK / kWave;
     using LD = WyLds<DK, NW>;
     constexpr int KS = LD::KS;
-    __shared__ LD L;
+    __shared__ __attribute__((aligned(16))) LD L;  // read as f32x4
 
     const int lane = threadIdx.x & (kWave - 1);
     const int tile = NW == 1 ? 0 : __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
@@ -681,9 +681,9 @@ __global__ __launch_bounds__(kWave * (DV / 64), 2) void wy_multi_kernel(DecodeAr
 template <int DK, int DV, int BV, int TB>
 __global__ __launch_bounds__(kThreads) void replay_kernel(ReplayArgs a) {
     using C = Tile<DK, DV, BV>;
-    __shared__ float Lk[TB][DK];
-    __shared__ float La[TB][DK];
-    __shared__ float Lu[TB][BV];
+    __shared__ __attribute__((aligned(16))) float Lk[TB][DK];  // read as float4
+    __shared__ __attribute__((aligned(16))) float La[TB][DK];
+    __shared__ __attribute__((aligned(16))) float Lu[TB][BV];
 
     const int tid = threadIdx.x;
     const int tile = blockIdx.x % C::NT;
