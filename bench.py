@@ -391,6 +391,9 @@ def main():
     ap.add_argument("--prefill-only", action="store_true",
                     help="measure only the copy reference and the two prefill workloads (for counter "
                          "runs); prints their figures without the headline metric")
+    ap.add_argument("--verify-only", action="store_true",
+                    help="measure only the copy reference and verify + replay (for counter runs); "
+                         "prints their figures without the headline metric")
     ap.add_argument("--quiet", action="store_true")
     args = ap.parse_args()
 
@@ -418,6 +421,12 @@ def main():
                  "prefill": bench_prefill(args, dev, log, "prefill"),
                  "prefill_varlen": bench_prefill(args, dev, log, "varlen")}
         print(json.dumps({"mode": "prefill-only", "extra": extra}))
+        return
+
+    if args.verify_only:
+        extra = {"copy_reference": bench_copy(dev, log),
+                 "verify_replay": bench_verify_replay(args, dev, log)}
+        print(json.dumps({"mode": "verify-only", "extra": extra}))
         return
 
     dec = bench_decode(args, dev, log)
