@@ -366,6 +366,17 @@ def bench_copy(dev, log):
     return {"bytes_read": n * 4, "bytes_written": n * 4, "us": per * 1e6, "GBs": gbs}
 
 
+def cpu_model():
+    """The host CPU's model name from /proc/cpuinfo, or None where it is not readable."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(x, log, budget_s=10.0):
     """fp64 oracle on the decode workload's step (all 64 x 32 (sequence, head) updates),
     repeated until about budget_s seconds of wall time."""
@@ -390,7 +401,7 @@ def cpu_baseline(x, log, budget_s=10.0):
     return {"value": n_upd / el, "unit": "state-updates/s", "cores": threads, "kind": "oracle",
             "sample": "%d full decode steps of the workload (64 sequences x 32 heads, 1 token, "
                       "dk = dv = 128), fp64, %.1f s" % (reps, el),
-            "cpu": platform.processor() or platform.machine()}
+            "cpu": cpu_model() or platform.processor() or platform.machine()}
 
 
 def main():

@@ -59,3 +59,8 @@ def test_more_than_one_gpu_is_refused():
                          capture_output=True, text=True, timeout=120)
     assert res.returncode == 2
     assert "one GPU" in res.stderr
+
+
+def test_cpu_model_is_a_name_or_none():
+    m = bench.cpu_model()
+    assert m is None or (isinstance(m, str) and m and "\n" not in m)
