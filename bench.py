@@ -437,7 +437,11 @@ def main():
         sys.exit(2)
     kda.load()
     dev = torch.device("cuda:0")
-    log("device: %s" % torch.cuda.get_device_name(0))
+    props = torch.cuda.get_device_properties(0)
+    device = {"name": props.name, "arch": getattr(props, "gcnArchName", None),
+              "compute_units": props.multi_processor_count,
+              "memory_bytes": props.total_memory}
+    log("device: %s (%s, %d CUs)" % (props.name, device["arch"], props.multi_processor_count))
 
     if args.prefill_only:
         extra = {"copy_reference": bench_copy(dev, log),
@@ -478,6 +482,7 @@ def main():
         "vs_baseline": None,
         "dtype": "fp32",
         "data": "synthetic",
+        "device": device,
         "config": {"workload": W.DECODE["name"], "num_slots": 512, "sequences": 64, "tokens": 1,
                    "heads": 32, "dk": 128, "dv": 128, "io_dtype": "bf16", "state_dtype": "fp32",
                    "slot_rotation": "8 disjoint sets of 64 slots (1 GiB pool)",
