@@ -377,7 +377,7 @@ def cpu_model():
     return None
 
 
-def cpu_baseline(x, log, budget_s=10.0):
+def cpu_baseline(x, log, budget_s=10.0, prefill_budget_s=5.0):
     """fp64 oracle on the decode workload's step (all 64 x 32 (sequence, head) updates),
     repeated until about budget_s seconds of wall time."""
     import numpy as np
@@ -401,7 +401,35 @@ def cpu_baseline(x, log, budget_s=10.0):
     return {"value": n_upd / el, "unit": "state-updates/s", "cores": threads, "kind": "oracle",
             "sample": "%d full decode steps of the workload (64 sequences x 32 heads, 1 token, "
                       "dk = dv = 128), fp64, %.1f s" % (reps, el),
-            "cpu": cpu_model() or platform.processor() or platform.machine()}
+            "cpu": cpu_model() or platform.processor() or platform.machine(),
+            "prefill": cpu_prefill_baseline(log, threads, prefill_budget_s)}
+
+
+def cpu_prefill_baseline(log, threads, budget_s):
+    """fp64 oracle (the token recurrence, its plain definition) on whole calls of the
+    T = 8192 x H = 32 prefill workload, repeated until about budget_s seconds."""
+    import numpy as np
+
+    import kda_workloads as W
+    from oracle import kda_oracle as O
+
+    y = W.prefill(seed=0)
+    f = lambda t: t.float().numpy().astype(np.float64)
+    ins = [f(y[n]) for n in ("q", "k", "v", "g", "beta")]
+    cu = y["cu_seqlens"].numpy().astype(np.int64)
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        O.recurrent(*ins, cu, nthreads=threads)
+        reps += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    el = time.perf_counter() - t0
+    tokens = int(cu[-1]) * reps
+    log("cpu oracle: %d prefill calls (%s) in %.1f s on %d threads" % (reps, W.PREFILL["name"], el,
+                                                                       threads))
+    return {"value": tokens / el, "unit": "tokens/s", "workload": W.PREFILL["name"],
+            "sample": "%d full calls of the workload through the token recurrence, fp64, %.1f s"
+                      % (reps, el)}
 
 
 def main():
