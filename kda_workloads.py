@@ -139,3 +139,65 @@ def prefill_long(seed=0, **kw):
     args.update(kw)
     return prefill(seed, **args)
 
+
+
+# ---------------------------------------------------------------------------
+# Random cases for the parity sweep: one seed gives one decode / MTP / verify case (even seeds) or
+# one varlen prefill case (odd seeds), with random head shape, dtype, lengths, slot map, accepted
+# lengths, gate strength and L2-norm switch.  Gate strength is kept within the prefill's
+# documented range (within-chunk gate sum above about -80: the x10 gates sum to ~-52 per chunk).
+_SWEEP_DIMS = ((64, 64), (64, 128), (128, 64), (128, 128))
+
+
+def sweep_case(seed):
+    """Returns dict(kind='decode'|'prefill', desc, and the inputs of that kind):
+    decode: q, k, v [N, T, H, d], g, beta, pool, slot_idx (distinct; -1 = skipped), accepted,
+            verify (bool), use_l2, dtype;
+    prefill: q, k, v [T_total, H, d], g, beta, cu_seqlens, pool, slot_idx, h0_from_pool, use_l2,
+             dtype."""
+    gen = _gen(seed)
+    pick = lambda n: int(torch.randint(n, (1,), generator=gen))
+    uni = lambda: float(torch.rand(1, generator=gen))
+    use_l2 = uni() < 0.8
+    strong = uni() < 0.15
+    sc = 1.0 if use_l2 else 0.25  # without the norm, smaller keys keep the state bounded
+    if seed % 2 == 0:
+        dk, dv = _SWEEP_DIMS[pick(4)]
+        dtype = torch.float32 if uni() < 0.4 else torch.bfloat16
+        N = 1 + pick(40)
+        T = (1, 1, 2, 3, 5, 7, 8, 9, 12, 16, 20)[pick(11)]
+        H = 1 + pick(8)
+        num_slots = N + pick(20)
+        lead = (N, T)
+    else:
+        dtype = torch.float32 if uni() < 0.3 else torch.bfloat16
+        dk, dv = _SWEEP_DIMS[pick(4)] if dtype == torch.bfloat16 else (64, (64, 128)[pick(2)])
+        ns = 1 + pick(6)
+        choices = (0, 1, 2, 31, 63, 64, 65, 127, 128, 129, 200, 500, 1000, 1025)
+        seqlens = [choices[pick(len(choices))] if uni() < 0.9 else 1 + pick(2000) for _ in range(ns)]
+        H = 1 + pick(4)
+        num_slots = ns + pick(8)
+        lead = (sum(seqlens),)
+    q = (_normal(gen, lead + (H, dk)) * sc).to(dtype)
+    k = (_normal(gen, lead + (H, dk)) * sc).to(dtype)
+    v = _normal(gen, lead + (H, dv)).to(dtype)
+    g = _gate(gen, lead + (H, dk)) * ((20.0 if seed % 2 == 0 else 10.0) if strong else 1.0)
+    beta = _beta(gen, lead + (H,))
+    pool = _normal(gen, (num_slots, H, dk, dv), std=0.05)
+    if seed % 2 == 0:
+        slot_idx = _distinct_slots(gen, num_slots, N)
+        slot_idx[torch.rand(N, generator=gen) < 0.1] = -1
+        accepted = torch.randint(0, T + 1, (N,), generator=gen, dtype=torch.int32)
+        verify = uni() < 0.5
+        desc = "decode N%d T%d H%d dk%d dv%d %s l2=%d strong=%d verify=%d" % (
+            N, T, H, dk, dv, str(dtype).split(".")[-1], use_l2, strong, verify)
+        return dict(kind="decode", desc=desc, q=q, k=k, v=v, g=g, beta=beta, pool=pool,
+                    slot_idx=slot_idx, accepted=accepted, verify=verify, use_l2=use_l2, dtype=dtype)
+    slot_idx = _distinct_slots(gen, num_slots, ns)
+    h0_from_pool = uni() < 0.6
+    cu = torch.zeros(ns + 1, dtype=torch.int32)
+    cu[1:] = torch.cumsum(torch.tensor(seqlens, dtype=torch.int64), 0).to(torch.int32)
+    desc = "prefill lens %s H%d dk%d dv%d %s l2=%d strong=%d h0pool=%d" % (
+        seqlens, H, dk, dv, str(dtype).split(".")[-1], use_l2, strong, h0_from_pool)
+    return dict(kind="prefill", desc=desc, q=q, k=k, v=v, g=g, beta=beta, cu_seqlens=cu, pool=pool,
+                slot_idx=slot_idx, h0_from_pool=h0_from_pool, use_l2=use_l2, dtype=dtype)
