@@ -3,7 +3,10 @@ C ABI against the fp64 oracle, over random head shapes, dtypes, token counts, ra
 lengths (empty, 1, 63-65, 127-129, >1000), slot maps with skipped sequences, accepted lengths,
 strong gates and the L2-norm switch (kda_workloads.sweep_case).  Bars: rel-L2 <= 1e-4 for fp32
 inputs, <= 1e-2 for bf16; skipped sequences, untouched slots and the pool under verify are
-checked exactly."""
+checked exactly.  The bf16 prefill's intra-chunk products take bf16 operands, so their error is
+about 2^-9 |q||k| whatever q.k is; a case whose q.k cancels can exceed the 1e-2 bar (seed 631, a
+1-token sequence: 1.03e-2, the same as rounding those operands on the CPU).  The 80 seeds here
+are not such cases."""
 import numpy as np
 import pytest
 import torch
