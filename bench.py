@@ -40,6 +40,12 @@ def decode_bytes_per_update(dk, dv, io_bytes):
     return 2 * dk * dv * 4 + (2 * dk + dv) * io_bytes + dk * 4 + 4 + dv * io_bytes
 
 
+def mtp_bytes_per_head(dk, dv, T, io_bytes):
+    """Algorithmic HBM bytes of one (sequence, head) multi-token commit of T tokens: the fp32
+    state read and written once, and each token's q, k, v, o (io dtype), g (fp32) and beta."""
+    return 2 * dk * dv * 4 + T * prefill_bytes_per_token_head(dk, dv, io_bytes)
+
+
 def prefill_bytes_per_token_head(dk, dv, io_bytes):
     """q, k, v read + o written (io dtype), g (fp32) and beta read, once each."""
     return (2 * dk + dv) * io_bytes + dk * 4 + 4 + dv * io_bytes
@@ -168,6 +174,59 @@ def bench_decode(args, dev, log):
         % (total / args.steps * 1e6, per * 1e6, achieved))
     return dict(total=total, per=per, updates=updates, bytes_per_update=bpu, achieved=achieved,
                 inputs=x)
+
+
+def bench_mtp(args, dev, log, T):
+    """Multi-token commit (MTP decode: T tokens per sequence, state updated in place) on the
+    decode workload's pool and sequences, the 8 disjoint slot sets in turn, replayed from a
+    captured HIP graph."""
+    import torch
+
+    import kda_gated_delta_rule_amd as kda
+    import kda_workloads as W
+
+    cfg = W.DECODE
+    x = W.decode(seed=0, T=T)
+    N, H, dk, dv, ns = cfg["N"], cfg["H"], cfg["dk"], cfg["dv"], cfg["num_slots"]
+    pool = x["pool"].to(dev)
+    q, k, v, g, beta = (x[n].to(dev) for n in ("q", "k", "v", "g", "beta"))
+    o = torch.empty_like(q)
+    rest = [s for s in torch.randperm(ns, generator=torch.Generator().manual_seed(1)).tolist()
+            if s not in set(x["slot_idx"].tolist())]
+    sets = [x["slot_idx"]] + [torch.tensor(rest[i * N:(i + 1) * N], dtype=torch.int32)
+                              for i in range(ns // N - 1)]
+    sets = [st.to(dev) for st in sets]
+
+    def step(i):
+        kda.decode_step(q, k, v, g, beta, pool, sets[i % len(sets)], o=o)
+
+    iters = max(len(sets), args.steps // 4)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step(0)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    gr = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gr):
+        for i in range(iters):
+            step(i)
+    gr.replay()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record()
+    gr.replay()
+    ev1.record()
+    torch.cuda.synchronize()
+    per = ev0.elapsed_time(ev1) / 1e3 / iters
+    byts = N * H * mtp_bytes_per_head(dk, dv, T, 2)
+    gbs = byts / per / 1e9
+    log("MTP commit T = %d: %.2f us/call (graph), %.3g sequence-tokens/s, %.1f GB/s (%.1f%% HBM)"
+        % (T, per * 1e6, N * T / per, gbs, 100 * gbs / HBM_PEAK_GBS))
+    return {"workload": "mtp_commit_N%d_T%d_H%d_d%d" % (N, T, H, dk), "us_per_call": per * 1e6,
+            "timing": "graph replay of %d calls, %d disjoint slot sets in turn" % (iters, len(sets)),
+            "sequence_tokens_per_s": N * T / per, "algorithmic_bytes": byts, "achieved_GBs": gbs,
+            "hbm_frac": gbs / HBM_PEAK_GBS}
 
 
 def bench_verify_replay(args, dev, log):
@@ -489,6 +548,8 @@ def main():
     extra = {"copy_reference": bench_copy(dev, log)}
     if not args.decode_only:
         extra["verify_replay"] = bench_verify_replay(args, dev, log)
+        extra["mtp_commit_T2"] = bench_mtp(args, dev, log, 2)
+        extra["mtp_commit_T4"] = bench_mtp(args, dev, log, 4)
         extra["prefill"] = bench_prefill(args, dev, log, "prefill")
         extra["prefill_varlen"] = bench_prefill(args, dev, log, "varlen")
         extra["prefill_snapshots"] = bench_prefill_snapshots(args, dev, log,

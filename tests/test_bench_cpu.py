@@ -64,3 +64,8 @@ def test_more_than_one_gpu_is_refused():
 def test_cpu_model_is_a_name_or_none():
     m = bench.cpu_model()
     assert m is None or (isinstance(m, str) and m and "\n" not in m)
+
+
+def test_mtp_bytes_reduce_to_the_decode_count_at_one_token():
+    assert bench.mtp_bytes_per_head(128, 128, 1, 2) == bench.decode_bytes_per_update(128, 128, 2)
+    assert bench.mtp_bytes_per_head(128, 128, 4, 2) == 131072 + 4 * 1540
