@@ -138,6 +138,10 @@ size_t kda_chunk_prefill_workspace_size(int num_seqs, int64_t total_tokens, int 
  *               its contents on entry do not matter.
  * Limits: H <= 65535 and (total_tokens / 64 + num_seqs) * H <= 2^22, else
  * KDA_ERR_INVALID_ARG (2^22 items take 176 GB of workspace or more).
+ * Numerical range: the intra-chunk products factor exp(G_t - G_s) from the chunk start, so
+ * the sum of g over the tokens of one 64-token chunk must stay above about -80 per key
+ * channel (not checked; beyond it the results overflow).  With bf16 inputs the intra-chunk
+ * products take bf16 operands: their error is about 2^-9 |q||k| whatever q.k is.
  */
 int kda_chunk_prefill(const void* q, const void* k, const void* v, int dtype, const float* g,
                       const float* beta, const int32_t* cu_seqlens, int num_seqs,

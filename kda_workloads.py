@@ -145,7 +145,8 @@ def prefill_long(seed=0, **kw):
 # Random cases for the parity sweep: one seed gives one decode / MTP / verify case (even seeds) or
 # one varlen prefill case (odd seeds), with random head shape, dtype, lengths, slot map, accepted
 # lengths, gate strength and L2-norm switch.  Gate strength is kept within the prefill's
-# documented range (within-chunk gate sum above about -80: the x10 gates sum to ~-52 per chunk).
+# stated range (kda_chunk_prefill: the within-chunk gate sum above about -80; the x10 gates sum
+# to ~-52 per chunk).
 _SWEEP_DIMS = ((64, 64), (64, 128), (128, 64), (128, 128))
 
 
