@@ -100,6 +100,28 @@ def counted_mfma(path, workload, us_per_call):
             "per_kernel_mfma_busy_pct": {n: k["mfma_busy_pct"] for n, k in ks.items()}}
 
 
+def counted_prefill_traffic(path, workload, us_per_call, algorithmic_bytes):
+    """HBM bytes of one prefill call from the rocprofv3 FETCH_SIZE / WRITE_SIZE record in `path`
+    (per kernel, scaled by a copy kernel of known size): bytes per call, their ratio to the
+    algorithmic bytes and their rate over the measured call time.  None when the kernel sources
+    have changed since the counters were taken."""
+    import hashlib
+
+    try:
+        rec = json.load(open(path))
+        src = b"".join(open(os.path.join(ROOT, f), "rb").read() for f in rec["sources"])
+        wl = rec["workloads"][workload]
+    except (OSError, ValueError, KeyError):
+        return None
+    if hashlib.sha256(src).hexdigest() != rec.get("source_sha256"):
+        return None
+    b = wl["bytes_per_call"]
+    return {"bytes_per_call": b, "ratio_to_algorithmic": b / algorithmic_bytes,
+            "GBs_at_call_time": b / (us_per_call * 1e-6) / 1e9,
+            "per_kernel_bytes": {n: k["fetch_bytes"] + k["write_bytes"]
+                                 for n, k in wl["per_kernel"].items()}}
+
+
 def time_loop(fn, steps, sync):
     """Runs fn(i) for i in range(steps) with HIP events around every call on the current
     stream; returns (total elapsed seconds, mean per-call seconds)."""
@@ -365,7 +387,9 @@ def bench_prefill(args, dev, log, which):
             "achieved_GBs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS,
             "binding_roofline_frac": max(tflops / BF16_PEAK_TFLOPS, gbs / HBM_PEAK_GBS),
             "mfma_counters": counted_mfma(os.path.join(ROOT, "profiles", "prefill_mfma_counters.json"),
-                                          name, per * 1e6)}
+                                          name, per * 1e6),
+            "traffic": counted_prefill_traffic(os.path.join(ROOT, "profiles", "prefill_traffic.json"),
+                                               name, per * 1e6, byts)}
 
 
 def bench_prefill_snapshots(args, dev, log, plain_us):

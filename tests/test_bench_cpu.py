@@ -69,3 +69,16 @@ def test_cpu_model_is_a_name_or_none():
 def test_mtp_bytes_reduce_to_the_decode_count_at_one_token():
     assert bench.mtp_bytes_per_head(128, 128, 1, 2) == bench.decode_bytes_per_update(128, 128, 2)
     assert bench.mtp_bytes_per_head(128, 128, 4, 2) == 131072 + 4 * 1540
+
+
+def test_counted_prefill_traffic_follows_the_source_hash(tmp_path):
+    wl = {"bytes_per_call": 3e8, "per_kernel": {"intra": {"fetch_bytes": 2e8, "write_bytes": 1e8}}}
+    path, src = _record(tmp_path, {"workloads": {"w": wl}})
+    got = bench.counted_prefill_traffic(str(path), "w", 100.0, 1e8)
+    assert got["bytes_per_call"] == 3e8 and got["ratio_to_algorithmic"] == 3.0
+    assert got["GBs_at_call_time"] == pytest.approx(3e8 / 100e-6 / 1e9)
+    assert got["per_kernel_bytes"] == {"intra": 3e8}
+    assert bench.counted_prefill_traffic(str(path), "other", 100.0, 1e8) is None
+    src.write_text("// changed\n")
+    assert bench.counted_prefill_traffic(str(path), "w", 100.0, 1e8) is None
+
