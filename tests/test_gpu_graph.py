@@ -1,5 +1,6 @@
 """The entry points inside a captured HIP graph (as the benchmark and serving loops run them):
-every replay equals the same calls made eagerly, bit for bit.
+every replay equals the same calls made eagerly, bit for bit; and on concurrent streams, where
+they equal the same calls made one after another.
 
 Each case keeps two copies of the pool, one driven eagerly and one by the graph, replays the graph
 three times with eager work and a synchronisation between replays, and compares outputs, records
@@ -113,3 +114,52 @@ def test_prefill_in_a_graph():
         assert torch.equal(o_g, o_e), rep
         assert torch.equal(pool_g, pool_e), rep
         (pool_e.sum() + 1.0).item()
+
+
+def test_concurrent_streams_match_sequential_calls():
+    """Decode, verify + replay and prefill on three streams at once (disjoint slots of one pool)
+    equal the same calls made one after another: each entry point runs on the stream it is
+    given and touches only its own slots."""
+    dev = need_gpu()
+    announce("streams: decode | verify + replay | prefill concurrently on one pool")
+    H = 8
+    xd = W.decode(seed=21, N=12, T=1, H=H, num_slots=64)
+    xv = W.verify(seed=22, N=12, H=H, num_slots=64)
+    y = W.prefill(seed=23, seqlens=(500, 130), H=H, num_slots=64, h0_std=0.05)
+    pool0 = xd["pool"].to(dev)
+    # disjoint slot sets: 0-11 decode, 12-23 verify, 24-25 prefill
+    sd = torch.arange(0, 12, dtype=torch.int32, device=dev)
+    sv = torch.arange(12, 24, dtype=torch.int32, device=dev)
+    sp = torch.arange(24, 26, dtype=torch.int32, device=dev)
+    d_in = [xd[n].to(dev) for n in ("q", "k", "v", "g", "beta")]
+    v_in = [xv[n].to(dev) for n in ("q", "k", "v", "g", "beta")]
+    acc = xv["accepted"].to(dev)
+    p_in = [y[n].to(dev) for n in ("q", "k", "v", "g", "beta", "cu_seqlens")]
+    N, T, _, dk = v_in[0].shape
+    dv = v_in[2].shape[-1]
+    Tt = p_in[0].shape[0]
+
+    def run(pool, streams):
+        od, ov, op = torch.empty_like(d_in[0]), torch.empty_like(v_in[0]), torch.empty_like(p_in[2])
+        rec = torch.empty(N, T, H, 2 * dk + dv, device=dev)
+        ws = torch.empty(kda.chunk_prefill_workspace_size(2, Tt, H, dk, dv), dtype=torch.uint8,
+                         device=dev)
+        torch.cuda.synchronize()
+        with torch.cuda.stream(streams[0]):
+            kda.decode_step(*d_in, pool, sd, o=od)
+        with torch.cuda.stream(streams[1]):
+            kda.decode_step(*v_in, pool, sv, o=ov, records=rec)
+            kda.replay_commit(pool, sv, rec, acc)
+        with torch.cuda.stream(streams[2]):
+            kda.chunk_prefill(*p_in, pool, sp, h0_from_pool=True, o=op, workspace=ws)
+        torch.cuda.synchronize()
+        return od, ov, rec, op
+
+    cur = torch.cuda.current_stream()
+    pool_seq, pool_par = pool0.clone(), pool0.clone()
+    seq = run(pool_seq, [cur, cur, cur])
+    par = run(pool_par, [torch.cuda.Stream() for _ in range(3)])
+    for a, b in zip(seq, par):
+        assert torch.equal(a, b)
+    assert torch.equal(pool_seq, pool_par)
+    assert torch.equal(pool_par[26:], pool0[26:])  # slots outside the calls untouched
