@@ -163,3 +163,34 @@ def test_concurrent_streams_match_sequential_calls():
         assert torch.equal(a, b)
     assert torch.equal(pool_seq, pool_par)
     assert torch.equal(pool_par[26:], pool0[26:])  # slots outside the calls untouched
+
+
+def test_prefill_snapshots_in_a_graph():
+    dev = need_gpu()
+    announce("graph: prefill with prefix-cache snapshots every 128 tokens")
+    y = W.prefill(seed=14, seqlens=(600, 200), H=4, num_slots=16, h0_std=0.05)
+    q, k, v, g, beta, cu = (y[n].to(dev) for n in ("q", "k", "v", "g", "beta", "cu_seqlens"))
+    Tt, H, dk = q.shape
+    dv = v.shape[-1]
+    sl = torch.tensor([0, 1], dtype=torch.int32, device=dev)
+    # snapshot slots 2.. (sequence 0: 4 snapshots at 128..512; sequence 1: 1 at 128, rest skipped)
+    snap = torch.tensor([[2, 3, 4, 5], [6, -1, -1, -1]], dtype=torch.int32, device=dev)
+    ws_g = torch.empty(kda.chunk_prefill_workspace_size(2, Tt, H, dk, dv), dtype=torch.uint8, device=dev)
+    pool0 = y["pool"].to(dev)
+    pool_g = pool0.clone()
+    o_g = torch.empty_like(v)
+    graph = _capture(lambda: kda.chunk_prefill(q, k, v, g, beta, cu, pool_g, sl, h0_from_pool=False,
+                                               o=o_g, workspace=ws_g, snapshot_every=128,
+                                               snapshot_slots=snap))
+    pool_g.copy_(pool0)
+    pool_e = pool0.clone()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        o_e = kda.chunk_prefill(q, k, v, g, beta, cu, pool_e, sl, h0_from_pool=False,
+                                snapshot_every=128, snapshot_slots=snap)
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o_g, o_e), rep
+        assert torch.equal(pool_g, pool_e), rep
+        assert torch.equal(pool_g[7:], pool0[7:]), rep  # slots outside the call untouched
+        (pool_e.sum() + 1.0).item()
