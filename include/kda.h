@@ -61,7 +61,7 @@ typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
  * L2 norm, gate and beta, decay, delta rule, outer-product update, output, in-place
  * final-state write-back; work split by sequence x value head) and, with records,
  * the verification half of ReplaySSM (page "2.8倍性能提升！基于CANN实现Kimi K3高性能推理",
- * section 04: verification stores only the per-token update records).
+ * section 04): per token a record {kh | alpha | u} is written in place of a state.
  *
  *   q, k        [N, T, H, dk]   dtype
  *   v           [N, T, H, dv]   dtype
@@ -89,9 +89,9 @@ int kda_decode_step(const void* q, const void* k, const void* v, int dtype, cons
                     int use_qk_l2norm, void* o, float* records, hipStream_t stream);
 
 /*
- * kda_replay_commit -- ReplaySSM commit (section 04 of the CANN inference page: once
- * the accepted length is known, the records of the accepted tokens are applied in
- * order starting from the committed state).
+ * kda_replay_commit -- the commit half of ReplaySSM (page "2.8倍性能提升！基于CANN实现
+ * Kimi K3高性能推理", section 04): the records of a sequence's accepted prefix update its
+ * committed slot state in token order.
  *
  * For each sequence n with slot_idx[n] >= 0 and each head, starting from the slot's
  * committed state, applies records[n, t, h] for t = 0 .. accepted_len[n]-1:
@@ -138,10 +138,14 @@ size_t kda_chunk_prefill_workspace_size(int num_seqs, int64_t total_tokens, int 
  *               its contents on entry do not matter.
  * Limits: H <= 65535 and (total_tokens / 64 + num_seqs) * H <= 2^22, else
  * KDA_ERR_INVALID_ARG (2^22 items take 176 GB of workspace or more).
- * Numerical range: the intra-chunk products factor exp(G_t - G_s) from the chunk start, so
- * the sum of g over the tokens of one 64-token chunk must stay above about -80 per key
- * channel (not checked; beyond it the results overflow).  With bf16 inputs the intra-chunk
- * products take bf16 operands: their error is about 2^-9 |q||k| whatever q.k is.
+ * Numerical range: the intra-chunk products split exp(G_t - G_s) (G the in-chunk cumulative
+ * gate) at a reference between t and s; the one limit left is that, per key channel, the sum
+ * of g over any 8 consecutive tokens of a 16-token block stays above about -85 (not checked;
+ * beyond it exp overflows inside the product and the results are not finite).
+ * Precision with bf16 inputs: the intra-chunk q.k and k.k products carry each operand as a
+ * high and a low bf16 part (about 16 bits); the record operands of the chunk carry (W, U,
+ * QG, Kt, P) and the carried state as an operand of the inter-chunk products are rounded to
+ * bf16 (the state itself is kept in fp32).  fp32 inputs use fp32 operands throughout.
  */
 int kda_chunk_prefill(const void* q, const void* k, const void* v, int dtype, const float* g,
                       const float* beta, const int32_t* cu_seqlens, int num_seqs,

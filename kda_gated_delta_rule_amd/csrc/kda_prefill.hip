@@ -40,14 +40,19 @@
 // the next product over that dimension when the k index of both operands is
 // permuted the same way (two tiles per bf16 granule, one per fp32 granule).
 //
-// The exp(G_t - G_s) factor is split as exp(G_t) * exp(-G_s) (chunk-start
-// reference) so A and P are plain MFMA products.  exp(-G_s) grows along the
-// chunk; this is exact up to rounding as long as the within-chunk gate sum stays
-// above about -80 (fp32/bf16 exponent range), far outside the gates these
-// kernels are fed (a 64-token gate sum of a few units).
+// A and P are MFMA products of 16x16 tiles whose exp(G_t - G_s) factor is split
+// at a reference inside the tile's span, so both factors stay bounded: an
+// off-diagonal tile (t and s in different 16-token blocks) splits at the end of
+// the block before t's, where both factors are at most 1; a diagonal tile at its
+// block's 8th token, so each factor covers at most 8 tokens' gates.  The only
+// range limit left: per key channel, 8 consecutive tokens' gates must sum to more
+// than about -85 (else exp2 overflows inside the diagonal tile).  W, QG, Kt and
+// exp(G_L) only use factors at most 1.
 //
-// MFMA operands are bf16 for bf16 inputs and fp32 for fp32 inputs; every
-// accumulation, the cumsum and the triangular solve are fp32.
+// MFMA operands are bf16 for bf16 inputs and fp32 for fp32 inputs; with bf16
+// inputs the A and P operands are each carried as a high and a low bf16 part
+// (three MFMAs per product), so every A and P entry is accurate to about 2^-16 of
+// its terms.  Every accumulation, the cumsum and the triangular solve are fp32.
 #include "kda_device.hpp"
 #include "kda_internal.hpp"
 
@@ -100,6 +105,33 @@ __device__ __forceinline__ f32x4 gmma(u32x4 a, u32x4 b, f32x4 c, F32) {
     for (int e = 0; e < 4; ++e)
         c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[e]), __uint_as_float(b[e]), c, 0, 0, 0);
     return c;
+}
+
+// x = hi + lo, both bf16 granules (hi = x rounded to bf16, lo = the remainder rounded),
+// so hi*hi + hi*lo + lo*hi carries about 16 bits of each product; fp32 keeps x in hi.
+__device__ __forceinline__ u32x4 f32_to_gran(const float* x, BF16);
+__device__ __forceinline__ u32x4 f32_to_gran(const float* x, F32);
+__device__ __forceinline__ void gran_to_f32(u32x4 g, float* x, BF16);
+__device__ __forceinline__ void split_gran(const float* x, u32x4& hi, u32x4& lo, BF16 tag) {
+    hi = f32_to_gran(x, tag);
+    float h[8];
+    gran_to_f32(hi, h, tag);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) h[e] = x[e] - h[e];
+    lo = f32_to_gran(h, tag);
+}
+__device__ __forceinline__ void split_gran(const float* x, u32x4& hi, u32x4& lo, F32 tag) {
+    hi = f32_to_gran(x, tag);
+    lo = hi;
+}
+// C += A B with both operands as (hi, lo) pairs: three bf16 MFMAs, one fp32 granule product.
+__device__ __forceinline__ f32x4 smma(u32x4 ah, u32x4 al, u32x4 bh, u32x4 bl, f32x4 c, BF16 tag) {
+    c = gmma(ah, bh, c, tag);
+    c = gmma(ah, bl, c, tag);
+    return gmma(al, bh, c, tag);
+}
+__device__ __forceinline__ f32x4 smma(u32x4 ah, u32x4, u32x4 bh, u32x4, f32x4 c, F32 tag) {
+    return gmma(ah, bh, c, tag);
 }
 
 // Accumulator tiles -> granule: bf16 packs 4 values of each of two tiles, fp32
@@ -318,13 +350,17 @@ __global__ __launch_bounds__(kThreads) void chunk_map_kernel(const int32_t* __re
 // Wave w owns tokens 16w .. 16w+15 of the chunk; lane (r = lane % 16, q = lane / 16)
 // holds token 16w + r and, of every row vector, the granules j of channels
 // GW (4j + q) .. + GW - 1.  LDS regions (reused by phase):
-//   R1  KI [64][LDK]            | T fp32 [64][LDA]
-//   R2  KG^T [DK][LDT]
+//   phases 2-3: s-operand copies [96][DK] (copy i = rows 0 .. 16 i - 1 for the
+//          off-diagonal tiles of token block i, from row 8 i (i - 1)); bf16: their low
+//          parts in the next [96][DK]; over R1 .. R2.  From phase 4:
+//     R1  T fp32 [64][LDA]
+//     RD  the diagonal 16x16 blocks of A, fp32 [4][16][LDD]
+//     RT  T' = T diag(beta) [64][LDT]
+//     R2  KG^T [DK][LDT]
 //   R3  V^T [DV][LDT]
-//   RD  the diagonal 16x16 blocks of A, fp32 [4][16][LDD]
-//   RT  T' = T diag(beta) [64][LDT]
-//   RM  beta [64], wave gate totals [4][DK]
-// (bf16, dk = dv = 128: 68.5 KiB, so two workgroups share a CU.)  The rest of A stays in
+//   RM  beta [64], key norm factors [64], per-wave gate totals, in-wave gate cumsums at
+//       token 7, and 2^totals [4][DK] each
+// (bf16, dk = dv = 128: 72.5 KiB, so two workgroups share a CU.)  The rest of A stays in
 // the registers of the wave that owns its rows; the QG and Kt record granules are built
 // in registers by MFMA products with a 0/1 selector (exact), without an LDS transpose.
 // ---------------------------------------------------------------------------
@@ -344,11 +380,15 @@ struct IntraPlan {
     static constexpr int LDD = 20;  // fp32 diagonal-block rows (16 + 4, 16-byte aligned)
     static constexpr size_t RD = align_up(4ull * 16 * LDD * 4, 16);
     static constexpr size_t RT = align_up(64ull * LDT * E, 16);
-    static constexpr size_t RM = align_up(4ull * (64 + 4 * DK), 16);
-    static constexpr size_t O1 = 0, O2 = O1 + R1, O3 = O2 + R2, OD = O3 + R3, OT = OD + RD;
-    static constexpr size_t OM = OT + RT;
+    static constexpr size_t RM = align_up(4ull * (2 * 64 + 13 * DK), 16);
+    static constexpr size_t O1 = 0, OD = O1 + R1, OT = OD + RD, O2 = OT + RT, O3 = O2 + R2;
+    static constexpr size_t OM = O3 + R3;
     static constexpr size_t BYTES = OM + RM;
     static constexpr bool fits = BYTES <= 160 * 1024;
+    // the s-operand copies of phases 2-3 (96 rows; bf16: high and low parts) overlay R1,
+    // RD, RT and R2 (first written in phase 4)
+    static_assert(96ull * DK * E * (E == 2 ? 2 : 1) <= O3, "s-operand copies exceed R1 .. R2");
+    static_assert(DK / GW >= 8, "copy swizzle needs 8 granules per row");
 };
 
 // One item's inputs, as loaded (granules of q, k, v; fp32 gate; beta).
@@ -403,18 +443,25 @@ __device__ __forceinline__ void intra_compute(const IntraIn<DK, DV, TIn>& X, cha
     constexpr int LDK = P::LDK, LDT = P::LDT, LDA = P::LDA;
     constexpr int KS = Mma<TIn>::KS, KST = kChunk / KS;  // natural k-steps over tokens
     constexpr TIn tag{};
-    elem* sKI = reinterpret_cast<elem*>(smem + P::O1);
+    // phases 2-3: s-operand copies, rows of DK elements without padding; the 16-byte
+    // granule index is XORed with the row's low 3 bits, so the 16 rows one MFMA operand
+    // read touches spread over the LDS banks
+    elem* sKS = reinterpret_cast<elem*>(smem + P::O1);
+    auto ks_at = [](int row, int gran) { return row * DK + GW * (gran ^ (row & 7)); };
     float* sT = reinterpret_cast<float*>(smem + P::O1);
     elem* sKGt = reinterpret_cast<elem*>(smem + P::O2);
     elem* sVt = reinterpret_cast<elem*>(smem + P::O3);
     float* sD = reinterpret_cast<float*>(smem + P::OD);
     elem* sTp = reinterpret_cast<elem*>(smem + P::OT);
     float* sBeta = reinterpret_cast<float*>(smem + P::OM);
-    float* sTot = sBeta + 64;
+    float* sIk = sBeta + 64;      // key norm factors per token
+    float* sTot = sIk + 64;       // [wave][DK] the wave's gate total (log2 units)
+    float* sMid = sTot + 4 * DK;  // [wave][DK] the in-wave gate cumsum at the wave's token 7
+    float* sT2 = sMid + 4 * DK;   // [1 + wave][DK] 2^(the wave's gate total); row 0 = 1
 
     const int r = lane & 15, q = lane >> 4, t = 16 * wave + r;
 
-    // ---- 1. norms, gate cumsum inside the wave, wave totals -------------------------
+    // ---- 1. norms, gate cumsum inside the wave, per-wave gate tables ------------------
     // The gates are scaled by log2(e) before the scan, so each exponential below is a
     // single exp2.
     constexpr float kLog2e = 1.4426950408889634f;
@@ -451,22 +498,43 @@ __device__ __forceinline__ void intra_compute(const IntraIn<DK, DV, TIn>& X, cha
     for (int j = 0; j < NGK; ++j)
 #pragma unroll
         for (int e = 0; e < GW; ++e) gf[j][e] = row_scan16(gf[j][e]);
-    if (r == 15) {
+    if (r == 15 || r == 7) {
+        float* dst = r == 15 ? sTot : sMid;
 #pragma unroll
         for (int j = 0; j < NGK; ++j)
 #pragma unroll
-            for (int m = 0; m < GW / 4; ++m)
-                *reinterpret_cast<f32x4*>(sTot + wave * DK + GW * (4 * j + q) + 4 * m) =
-                    f32x4{gf[j][4 * m], gf[j][4 * m + 1], gf[j][4 * m + 2], gf[j][4 * m + 3]};
+            for (int m = 0; m < GW / 4; ++m) {
+                const int c = wave * DK + GW * (4 * j + q) + 4 * m;
+                const f32x4 x = {gf[j][4 * m], gf[j][4 * m + 1], gf[j][4 * m + 2], gf[j][4 * m + 3]};
+                *reinterpret_cast<f32x4*>(dst + c) = x;
+                if (r == 15)
+                    *reinterpret_cast<f32x4*>(sT2 + DK + c) =
+                        f32x4{__builtin_amdgcn_exp2f(x[0]), __builtin_amdgcn_exp2f(x[1]),
+                              __builtin_amdgcn_exp2f(x[2]), __builtin_amdgcn_exp2f(x[3])};
+            }
     }
-    if (q == 0) sBeta[t] = X.beta;
+    if (q == 0) {
+        sBeta[t] = X.beta;
+        sIk[t] = ik;
+    }
+    if (tid < DK) sT2[tid] = 1.f;
     lds_barrier();
 
-    // ---- 2. G, exponentials, operands -------------------------------------------------
-    // G = in-wave scan + earlier waves' totals (t0 + t1 + ... in a fixed order; the
-    // wave-uniform 0/1 multipliers select the prefix without per-lane selects), G_L =
-    // all four totals.
-    const float m1 = wave > 0 ? 1.f : 0.f, m2 = wave > 1 ? 1.f : 0.f, m3 = wave > 2 ? 1.f : 0.f;
+    // ---- 2. exponentials, operands, records, the diagonal tiles -----------------------
+    // exp(G_t - G_s) is never formed as a product of one large and one small factor:
+    //  - record operands and W use the chunk start as reference: 2^G_t <= 1 (QG, KG) and
+    //    2^(G_L - G_t) <= 1 (Kt);
+    //  - an off-diagonal tile (t in block i, s in block j < i) splits at the end of block
+    //    i - 1: t side 2^(G_t - G_end(i-1)) = 2^gf_t <= 1 (KB, QB), s side
+    //    2^(G_end(i-1) - G_s) <= 1, stored by the wave owning s once per later block i
+    //    (row s of copy i = 2^(G_end(j) - G_s) times the gate factors of blocks j+1..i-1);
+    //  - a diagonal tile (t, s in one block) splits at the block's token 7, so each factor
+    //    spans at most 8 tokens' gates.
+    // The operands are the raw q and k (exact for bf16 inputs wherever the factor is 1);
+    // the norm factors scale the finished tiles.  With bf16 inputs every A and P operand is
+    // carried as a high and a low bf16 part (products hi*hi + hi*lo + lo*hi, three MFMAs),
+    // so an entry's error is about 2^-16 of its terms, and an entry whose terms cancel
+    // (q.k near 0) keeps its own size's accuracy instead of 2^-8 of |q||k|.
     const bool odd = r & 1;
     const int te = t & ~1;
     // v_perm_b32 selectors for the adjacent-token pairs of the transposed copies: even
@@ -481,7 +549,6 @@ __device__ __forceinline__ void intra_compute(const IntraIn<DK, DV, TIn>& X, cha
             *reinterpret_cast<uint32_t*>(dstT + c * LDT + te) = __builtin_amdgcn_perm(nbr, wv[i], psel);
         }
     };
-    u32x4 KG[NGK], QG[NGK];
     // V^T first, so the V registers are free for the rest of the phase
 #pragma unroll
     for (int j = 0; j < NGV; ++j) {
@@ -504,51 +571,84 @@ __device__ __forceinline__ void intra_compute(const IntraIn<DK, DV, TIn>& X, cha
         for (int e = 0; e < GW; ++e) x[e] = (E == 2 ? (8 * q + e == 16 * h + r) : (4 * q + e == r)) ? 1.f : 0.f;
         sel[h] = f32_to_gran(x, tag);
     }
+    // gate-table rows (wave-uniform): 2^(total of block w) is row w + 1, a block outside
+    // the chunk reads the row of ones; the blocks before this one give the chunk-start
+    // reference, the blocks after it Kt and the s-operand copies
+    auto trow = [&](int w) { return (w >= 0 && w < 4 ? w + 1 : 0) * DK; };
+    const int p1 = trow(wave - 1), p2 = trow(wave - 2), p3 = trow(wave - 3);
+    const int n1 = trow(wave + 1), n2 = trow(wave + 2), n3 = trow(wave + 3);
+    // s-operand copy rows of this wave's token for copies wave + 1, wave + 2, wave + 3
+    const int c1 = 8 * (wave + 1) * wave + t, c2 = 8 * (wave + 2) * (wave + 1) + t, c3 = 48 + t;
+    u32x4 KBh[NGK], KBl[NGK], QBh[NGK], QBl[NGK];
+    f32x4 Adg = {0.f, 0.f, 0.f, 0.f}, Pdg = Adg;
     {
         float* gl_out = reinterpret_cast<float*>(rec + ws.o_gl);
 #pragma unroll
         for (int j = 0; j < NGK; ++j) {
-            float kg[GW], ki[GW], qg[GW], kt[GW], qv[GW], kv[GW];
+            float qv[GW], kv[GW], ks0[GW], ks1[GW], ks2[GW], kb[GW], qb[GW], qg[GW], kt[GW];
+            float sd[GW], kd[GW], qd[GW];
             gran_to_f32(X.q[j], qv, tag);
             gran_to_f32(X.k[j], kv, tag);
 #pragma unroll
             for (int m = 0; m < GW / 4; ++m) {
                 const int c = GW * (4 * j + q) + 4 * m;
-                const f32x4 t0 = *reinterpret_cast<const f32x4*>(sTot + c);
-                const f32x4 t1 = *reinterpret_cast<const f32x4*>(sTot + DK + c);
-                const f32x4 t2 = *reinterpret_cast<const f32x4*>(sTot + 2 * DK + c);
-                const f32x4 t3 = *reinterpret_cast<const f32x4*>(sTot + 3 * DK + c);
-                f32x4 tot;
+                const f32x4 P1 = *reinterpret_cast<const f32x4*>(sT2 + p1 + c);
+                const f32x4 P2 = *reinterpret_cast<const f32x4*>(sT2 + p2 + c);
+                const f32x4 P3 = *reinterpret_cast<const f32x4*>(sT2 + p3 + c);
+                const f32x4 N1 = *reinterpret_cast<const f32x4*>(sT2 + n1 + c);
+                const f32x4 N2 = *reinterpret_cast<const f32x4*>(sT2 + n2 + c);
+                const f32x4 N3 = *reinterpret_cast<const f32x4*>(sT2 + n3 + c);
+                const f32x4 tw = *reinterpret_cast<const f32x4*>(sTot + wave * DK + c);
+                const f32x4 md = *reinterpret_cast<const f32x4*>(sMid + wave * DK + c);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int i = 4 * m + e;
-                    const float pre = fmaf(t2[e], m3, fmaf(t1[e], m2, t0[e] * m1));
-                    tot[e] = (t0[e] + t1[e]) + t2[e] + t3[e];
-                    const float G = gf[j][i] + pre;
-                    const float eg = __builtin_amdgcn_exp2f(G), ei = __builtin_amdgcn_exp2f(-G);
-                    const float kh = kv[i] * ik;
-                    kg[i] = kh * eg;
-                    ki[i] = kh * ei;
-                    qg[i] = qv[i] * iq * eg;
-                    kt[i] = kh * __builtin_amdgcn_exp2f(tot[e] - G);
+                    const float G = gf[j][i];
+                    // 2^(G_t - chunk start) and 2^(G_L - G_t) from the block factors
+                    const float pw = P1[e] * P2[e] * P3[e];
+                    const float kw = N1[e] * N2[e] * N3[e];
+                    const float et = __builtin_amdgcn_exp2f(G);           // 2^(G_t - G_end(i-1))
+                    const float kif = __builtin_amdgcn_exp2f(tw[e] - G);  // 2^(G_end(i) - G_t)
+                    const float e1 = __builtin_amdgcn_exp2f(G - md[e]);   // diagonal tile, t side
+                    const float e2 = __builtin_amdgcn_exp2f(md[e] - G);   // diagonal tile, s side
+                    kb[i] = kv[i] * et;
+                    qb[i] = qv[i] * et;
+                    qg[i] = qb[i] * (iq * pw);
+                    ks0[i] = kv[i] * kif;
+                    kt[i] = ks0[i] * (ik * kw);
+                    ks1[i] = ks0[i] * N1[e];
+                    ks2[i] = ks1[i] * N2[e];
+                    sd[i] = kv[i] * e2;
+                    kd[i] = kv[i] * e1;
+                    qd[i] = qv[i] * e1;
                 }
-                if (wave == 0 && r == 0)
-                    *reinterpret_cast<f32x4*>(gl_out + c) =
-                        f32x4{__builtin_amdgcn_exp2f(tot[0]), __builtin_amdgcn_exp2f(tot[1]),
-                              __builtin_amdgcn_exp2f(tot[2]), __builtin_amdgcn_exp2f(tot[3])};
-            }
-            KG[j] = f32_to_gran(kg, tag);
-            QG[j] = f32_to_gran(qg, tag);
-            *reinterpret_cast<u32x4*>(sKI + t * LDK + GW * (4 * j + q)) = f32_to_gran(ki, tag);
-            // transposed copy [channel][token]
-            if constexpr (E == 2) {
-                pair_store(sKGt, KG[j], j);
-            } else {
+                if (wave == 0 && r == 0) {
+                    const f32x4 t0 = *reinterpret_cast<const f32x4*>(sTot + c);
+                    const f32x4 t1 = *reinterpret_cast<const f32x4*>(sTot + DK + c);
+                    const f32x4 t2 = *reinterpret_cast<const f32x4*>(sTot + 2 * DK + c);
+                    const f32x4 t3 = *reinterpret_cast<const f32x4*>(sTot + 3 * DK + c);
+                    f32x4 gl;
 #pragma unroll
-                for (int e = 0; e < GW; ++e) sKGt[(GW * (4 * j + q) + e) * LDT + t] = kg[e];
+                    for (int e = 0; e < 4; ++e) gl[e] = __builtin_amdgcn_exp2f(((t0[e] + t1[e]) + t2[e]) + t3[e]);
+                    *reinterpret_cast<f32x4*>(gl_out + c) = gl;
+                }
             }
+            split_gran(kb, KBh[j], KBl[j], tag);
+            split_gran(qb, QBh[j], QBl[j], tag);
+            // s-operand copies of this wave's rows for every later block i (copy i holds
+            // rows 0 .. 16 i - 1 from KS row 8 i (i - 1); the low parts 96 rows further)
+            auto put = [&](int row, const float* x) {
+                u32x4 h, l;
+                split_gran(x, h, l, tag);
+                *reinterpret_cast<u32x4*>(sKS + ks_at(row, 4 * j + q)) = h;
+                if constexpr (E == 2) *reinterpret_cast<u32x4*>(sKS + ks_at(96 + row, 4 * j + q)) = l;
+            };
+            if (wave < 3) put(c1, ks0);
+            if (wave < 2) put(c2, ks1);
+            if (wave < 1) put(c3, ks2);
             // records: granule j spans the dk blocks CT j .. CT j + CT - 1
             const u32x4 ktg = f32_to_gran(kt, tag);
+            const u32x4 qgg = f32_to_gran(qg, tag);
             f32x4 qt[RG::CT];
 #pragma unroll
             for (int h = 0; h < RG::CT; ++h) {
@@ -563,44 +663,94 @@ __device__ __forceinline__ void intra_compute(const IntraIn<DK, DV, TIn>& X, cha
                 else
                     *reinterpret_cast<f32x4*>(dk) = kt4;
                 // QG^T tile (rows c, columns t): lane holds channels 16 cb + 4q + rr of token t
-                qt[h] = gmma(sel[h], QG[j], f32x4{0.f, 0.f, 0.f, 0.f}, tag);
+                qt[h] = gmma(sel[h], qgg, f32x4{0.f, 0.f, 0.f, 0.f}, tag);
             }
             *reinterpret_cast<u32x4*>(rec + ws.o_q + ((static_cast<size_t>(wave) * RG::GK + j) * 64 + lane) * 16) =
                 tiles_to_gran(qt[0], qt[RG::CT - 1], tag);
+            // the diagonal tiles from this lane's own rows (s and t both in this block)
+            u32x4 SDh, SDl, KDh, KDl, QDh, QDl;
+            split_gran(sd, SDh, SDl, tag);
+            split_gran(kd, KDh, KDl, tag);
+            split_gran(qd, QDh, QDl, tag);
+            Adg = smma(SDh, SDl, KDh, KDl, Adg, tag);
+            Pdg = smma(SDh, SDl, QDh, QDl, Pdg, tag);
+            // one granule at a time: interleaving the unrolled iterations runs out of registers
+            __builtin_amdgcn_sched_barrier(0);
         }
     }
     lds_barrier();
-    // ---- 3. A^T and P^T tiles (all four column blocks, straight-line); P record -------
+    // ---- 3. A^T and P^T tiles of this wave's rows t over the four s blocks; P record.
+    //      The off-diagonal tiles read this block's s-operand copy; the tile of this block
+    //      is the diagonal one; later blocks are zero.
     f32x4 Areg[4], Preg[4];
+    {
+        const int kbase = 8 * wave * (wave - 1);  // this block's copy (rows 0 .. 16 wave - 1)
+        const float ab = X.beta * ik;             // A_ts = beta_t ik_t ik_s (raw product)
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-        f32x4 accA = {0.f, 0.f, 0.f, 0.f}, accP = accA;
+        for (int jj = 0; jj < 4; ++jj) {
+            f32x4 accA = {0.f, 0.f, 0.f, 0.f}, accP = accA;
+            if (jj < 3 && jj < wave) {
+                const int row = kbase + 16 * jj + r;
 #pragma unroll
-        for (int j = 0; j < NGK; ++j) {
-            const u32x4 b = *reinterpret_cast<const u32x4*>(sKI + (16 * jj + r) * LDK + GW * (4 * j + q));
-            accA = gmma(b, KG[j], accA, tag);
-            accP = gmma(b, QG[j], accP, tag);
+                for (int j = 0; j < NGK; ++j) {
+                    const u32x4 bh = *reinterpret_cast<const u32x4*>(sKS + ks_at(row, 4 * j + q));
+                    const u32x4 bl =
+                        E == 2 ? *reinterpret_cast<const u32x4*>(sKS + ks_at(96 + row, 4 * j + q)) : bh;
+                    accA = smma(bh, bl, KBh[j], KBl[j], accA, tag);
+                    accP = smma(bh, bl, QBh[j], QBl[j], accP, tag);
+                }
+            }
+            const f32x4 iks = *reinterpret_cast<const f32x4*>(sIk + 16 * jj + 4 * q);
+            // lane holds (s = 16 jj + 4q + rr, t)
+            float a4[4], p4[4];
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+                const int s = 16 * jj + 4 * q + rr;
+                const float xa = jj == wave ? Adg[rr] : accA[rr];
+                const float xp = jj == wave ? Pdg[rr] : accP[rr];
+                a4[rr] = s < t ? ab * iks[rr] * xa : 0.f;
+                p4[rr] = s <= t ? iq * iks[rr] * xp : 0.f;
+            }
+            Areg[jj] = f32x4{a4[0], a4[1], a4[2], a4[3]};
+            Preg[jj] = f32x4{p4[0], p4[1], p4[2], p4[3]};
         }
-        // lane holds (s = 16 jj + 4q + rr, t): A_ts = beta_t (KG_t . KI_s) for s < t
-        float p4[4];
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-            const int s = 16 * jj + 4 * q + rr;
-            Areg[jj][rr] = s < t ? X.beta * accA[rr] : 0.f;
-            p4[rr] = s <= t ? accP[rr] : 0.f;
-        }
-        Preg[jj] = f32x4{p4[0], p4[1], p4[2], p4[3]};
     }
-    // P granules (rows t of this token block, k over tokens) and QG granules (rows t, k
-    // over dk, the order of the W granules) to the record
+    // P granules (rows t of this token block, k over tokens) to the record
 #pragma unroll
     for (int g = 0; g < RG::GT; ++g)
         *reinterpret_cast<u32x4*>(rec + ws.o_p + ((static_cast<size_t>(wave) * RG::GT + g) * 64 + lane) * 16) =
             tiles_to_gran(Preg[RG::CT * g], Preg[RG::CT * g + RG::CT - 1], tag);
     lds_barrier();
 
-    // ---- 4. this wave's diagonal block of A to LDS; zero the upper blocks of its T' rows
-    //      (both read only by this wave until the next barrier)
+    // ---- 4. (the s-operand copies are dead) KG^T for phase 6, KG = 2^G kh from KB =
+    //      2^gf k (its high and low parts); this wave's diagonal block of A to LDS and the
+    //      upper blocks of its T' rows zeroed (both read only by this wave until the next
+    //      barrier)
+#pragma unroll
+    for (int j = 0; j < NGK; ++j) {
+        float kg[GW], lo[GW];
+        gran_to_f32(KBh[j], kg, tag);
+        gran_to_f32(KBl[j], lo, tag);
+#pragma unroll
+        for (int m = 0; m < GW / 4; ++m) {
+            const int c = GW * (4 * j + q) + 4 * m;
+            const f32x4 P1 = *reinterpret_cast<const f32x4*>(sT2 + p1 + c);
+            const f32x4 P2 = *reinterpret_cast<const f32x4*>(sT2 + p2 + c);
+            const f32x4 P3 = *reinterpret_cast<const f32x4*>(sT2 + p3 + c);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int i = 4 * m + e;
+                kg[i] = (E == 2 ? kg[i] + lo[i] : kg[i]) * (ik * (P1[e] * P2[e] * P3[e]));
+            }
+        }
+        const u32x4 KG = f32_to_gran(kg, tag);
+        if constexpr (E == 2) {
+            pair_store(sKGt, KG, j);
+        } else {
+#pragma unroll
+            for (int e = 0; e < GW; ++e) sKGt[(GW * (4 * j + q) + e) * LDT + t] = kg[e];
+        }
+    }
     {
         f32x4 dg = Areg[0];
 #pragma unroll
@@ -777,9 +927,15 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_intra_kernel(PrefillArgs a)
             t0 = e.y;
             L = e.z;
         }
+        // Lane-derived offsets and masks are formed again for every item: opaque copies of
+        // the lane and wave indices keep the compiler from hoisting them out of the item
+        // loop, where they would stay live across all phases (and spill).
+        int ln = lane, wv = wave;
+        asm volatile("" : "+v"(ln));
+        asm volatile("" : "+s"(wv));
         IntraIn<DK, DV, TIn> X;
-        intra_fetch(X, a, t0, L, item % H, wave, lane);
-        intra_compute(X, smem, a, recs + ws.rec_bytes * static_cast<size_t>(item), ws, wave, lane, tid);
+        intra_fetch(X, a, t0, L, item % H, wv, ln);
+        intra_compute(X, smem, a, recs + ws.rec_bytes * static_cast<size_t>(item), ws, wv, ln, tid);
     }
 }
 

@@ -141,12 +141,56 @@ def prefill_long(seed=0, **kw):
 
 
 
+def cancellation(seed=0, seqlens=(64,), H=4, dk=128, dv=128, gate="channel", dtype=torch.bfloat16,
+                 num_slots=None):
+    """Prefill inputs whose q.k products cancel (for use without the L2 norm).
+
+    Keys k ~ 0.25 N(0, 1).  Each query starts as 0.25 N(0, 1) and has its least-squares
+    projection on the keys of its own sequence up to and including its own token removed, so
+    q_t . k_s = 0 for s <= t before q and k are rounded to dtype (after rounding the products
+    are small but not zero).  Sequences need at most dk tokens.  gate: 'channel' (per key
+    channel, -0.1 softplus(N(0, 1)) as in the other workloads), 'scalar' (one such value per
+    token and head, the same on every channel) or 'zero'.  v ~ N(0, 1), beta = sigmoid(N(0, 1)),
+    zero pool (initial state).  Returns the dict of prefill().
+    """
+    seqlens = tuple(int(s) for s in seqlens)
+    if max(seqlens) > dk:
+        raise ValueError("cancellation needs sequences of at most dk tokens")
+    ns = len(seqlens)
+    T = sum(seqlens)
+    gen = _gen(seed)
+    k = (_normal(gen, (T, H, dk)) * 0.25).to(dtype).double()
+    r = _normal(gen, (T, H, dk)).double() * 0.25
+    q = torch.empty(T, H, dk, dtype=torch.float64)
+    t0 = 0
+    for L in seqlens:
+        for t in range(L):
+            for h in range(H):
+                K = k[t0:t0 + t + 1, h]                                   # [t + 1, dk]
+                coef = torch.linalg.lstsq(K.T, r[t0 + t, h].unsqueeze(1)).solution
+                q[t0 + t, h] = r[t0 + t, h] - (K.T @ coef).squeeze(1)
+        t0 += L
+    v = _normal(gen, (T, H, dv)).to(dtype)
+    if gate == "channel":
+        g = _gate(gen, (T, H, dk))
+    elif gate == "scalar":
+        g = _gate(gen, (T, H, 1)).expand(T, H, dk).contiguous()
+    elif gate == "zero":
+        g = torch.zeros(T, H, dk)
+    else:
+        raise ValueError("gate must be 'channel', 'scalar' or 'zero'")
+    beta = _beta(gen, (T, H))
+    num_slots = num_slots or ns
+    cu = torch.zeros(ns + 1, dtype=torch.int32)
+    cu[1:] = torch.cumsum(torch.tensor(seqlens, dtype=torch.int64), 0).to(torch.int32)
+    return dict(q=q.to(dtype), k=k.to(dtype), v=v, g=g, beta=beta, cu_seqlens=cu,
+                pool=torch.zeros(num_slots, H, dk, dv), slot_idx=_distinct_slots(gen, num_slots, ns))
+
+
 # ---------------------------------------------------------------------------
 # Random cases for the parity sweep: one seed gives one decode / MTP / verify case (even seeds) or
 # one varlen prefill case (odd seeds), with random head shape, dtype, lengths, slot map, accepted
-# lengths, gate strength and L2-norm switch.  Gate strength is kept within the prefill's
-# stated range (kda_chunk_prefill: the within-chunk gate sum above about -80; the x10 gates sum
-# to ~-52 per chunk).
+# lengths, gate strength (15% of the cases x20) and L2-norm switch.
 _SWEEP_DIMS = ((64, 64), (64, 128), (128, 64), (128, 128))
 
 
@@ -182,7 +226,7 @@ def sweep_case(seed):
     q = (_normal(gen, lead + (H, dk)) * sc).to(dtype)
     k = (_normal(gen, lead + (H, dk)) * sc).to(dtype)
     v = _normal(gen, lead + (H, dv)).to(dtype)
-    g = _gate(gen, lead + (H, dk)) * ((20.0 if seed % 2 == 0 else 10.0) if strong else 1.0)
+    g = _gate(gen, lead + (H, dk)) * (20.0 if strong else 1.0)
     beta = _beta(gen, lead + (H,))
     pool = _normal(gen, (num_slots, H, dk, dv), std=0.05)
     if seed % 2 == 0:

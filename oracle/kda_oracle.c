@@ -9,14 +9,13 @@
  *
  * Sources (cited by page title and section):
  *  - "Kimi K3 ... 昇腾 day-0 adaptation" (hwcomputing.csdn.net), section
- *    "融合算子加速：KDA Prefill与Decode双路径": the decode step is, in order,
- *    Q/K L2 norm, gate and beta processing, state decay, delta rule, outer-product
- *    update, output computation, and in-place write-back of the final state to the
- *    state pool; prefill works on 64-token chunks with gate cumulation.
- *  - "2.8倍性能提升！基于CANN实现Kimi K3高性能推理", section 04 ReplaySSM:
- *    verification keeps only the per-token update records; once the accepted
- *    length is known, the records of the accepted tokens are applied in order,
- *    starting from the committed state.
+ *    "融合算子加速：KDA Prefill与Decode双路径": the order of the steps below (norms,
+ *    gate, decay, delta rule, update, output, state back to its pool slot) and the
+ *    64-token chunks of the prefill (kda_oracle_chunked).
+ *  - "2.8倍性能提升！基于CANN实现Kimi K3高性能推理", section 04 ReplaySSM: the record
+ *    {kh | alpha | u} kept per token by a verify pass, and the commit that applies a
+ *    sequence's accepted prefix of records, in token order, to its committed state
+ *    (kda_oracle_replay).
  *
  * The pages give the step list but no formula.  The formula used here, for one
  * sequence and one head, with state S (dk x dv, row c = key channel):

@@ -1,7 +1,7 @@
 """GPU parity of the chunked prefill against the fp64 token recurrence (oracle),
-through the C ABI.  Small varlen cases are compared element-wise in full; the two
-full-size workloads (T = 8192 x H = 32, and the 4-sequence 128,076-token H = 16
-batch) are compared on sampled heads, whose oracle chains are computed in full.
+through the C ABI.  Every case is compared element-wise in full, the two full-size
+workloads (T = 8192 x H = 32, and the 4-sequence 128,076-token H = 16 batch) included;
+besides the whole-tensor relative L2, the worst (sequence, head) value is checked.
 """
 import numpy as np
 import pytest
@@ -10,7 +10,8 @@ import torch
 import kda_gated_delta_rule_amd as kda
 import kda_workloads as W
 from oracle import kda_oracle as O
-from tests._util import announce, f64, need_gpu, rel_l2, worst_rel_l2
+from tests._util import (announce, check_prefill_parity, f64, need_gpu, rel_l2, worst_chunk_head,
+                         worst_rel_l2, worst_seq_head, worst_state)
 
 pytestmark = pytest.mark.gpu
 
@@ -45,8 +46,7 @@ def test_tiny_fp32_through_prefill():
     y["slot_idx"] = torch.zeros(1, dtype=torch.int32)
     o, pool = run_prefill(y, dev, h0_from_pool=False, scale=64 ** -0.5)
     o_ref, h_ref, _ = oracle_prefill(y, h0_from_pool=False, scale=64 ** -0.5)
-    assert rel_l2(f64(o), o_ref) <= 1e-4
-    assert rel_l2(f64(pool.cpu()), h_ref) <= 1e-4
+    check_prefill_parity(f64(o), o_ref, f64(pool.cpu()), h_ref, y["cu_seqlens"], 1e-4, "tiny fp32")
 
 
 @pytest.mark.parametrize("dv", [64, 128])
@@ -58,8 +58,8 @@ def test_fp32_varlen_ragged(dv):
                   h0_std=0.05, dtype=torch.float32)
     o, pool = run_prefill(y, dev)
     o_ref, h_ref, _ = oracle_prefill(y)
-    assert rel_l2(f64(o), o_ref) <= 1e-4
-    assert rel_l2(f64(pool.cpu()[y["slot_idx"].long()]), h_ref) <= 1e-4
+    check_prefill_parity(f64(o), o_ref, f64(pool.cpu()[y["slot_idx"].long()]), h_ref, y["cu_seqlens"],
+                         1e-4, "fp32")
 
 
 @pytest.mark.parametrize("dk,dv", [(128, 128), (64, 64), (128, 64), (64, 128)])
@@ -70,10 +70,9 @@ def test_bf16_varlen_ragged(dk, dv):
                   h0_std=0.05)
     o, pool = run_prefill(y, dev)
     o_ref, h_ref, _ = oracle_prefill(y)
-    assert rel_l2(f64(o), o_ref) <= 1e-2
     got = pool.cpu()
     sl = y["slot_idx"].long()
-    assert rel_l2(f64(got[sl]), h_ref) <= 1e-2
+    check_prefill_parity(f64(o), o_ref, f64(got[sl]), h_ref, y["cu_seqlens"], 1e-2, "bf16 ragged")
     others = torch.ones(12, dtype=torch.bool)
     others[sl] = False
     assert torch.equal(got[others], y["pool"][others])
@@ -95,8 +94,8 @@ def test_fp32_multi_segment(dv):
                   dtype=torch.float32)
     o, pool = run_prefill(y, dev)
     o_ref, h_ref, _ = oracle_prefill(y)
-    assert rel_l2(f64(o), o_ref) <= 1e-4
-    assert rel_l2(f64(pool.cpu()[y["slot_idx"].long()]), h_ref) <= 1e-4
+    check_prefill_parity(f64(o), o_ref, f64(pool.cpu()[y["slot_idx"].long()]), h_ref, y["cu_seqlens"],
+                         1e-4, "fp32")
 
 
 @pytest.mark.parametrize("h0", [True, False])
@@ -107,9 +106,8 @@ def test_bf16_multi_segment(h0):
     y = W.prefill(seed=8, seqlens=MULTI_SEG, H=3, dk=128, dv=128, num_slots=8, h0_std=0.05)
     o, pool = run_prefill(y, dev, h0_from_pool=h0)
     o_ref, h_ref, _ = oracle_prefill(y, h0_from_pool=h0)
-    assert rel_l2(f64(o), o_ref) <= 1e-2
-    assert worst_rel_l2(f64(o), o_ref, 1) <= 2e-2  # per head
-    assert rel_l2(f64(pool.cpu()[y["slot_idx"].long()]), h_ref) <= 1e-2
+    check_prefill_parity(f64(o), o_ref, f64(pool.cpu()[y["slot_idx"].long()]), h_ref, y["cu_seqlens"],
+                         1e-2, "bf16 multi-segment")
 
 
 def test_many_short_sequences_scan_grid_loops():
@@ -124,8 +122,8 @@ def test_many_short_sequences_scan_grid_loops():
     assert 520 * 64 > 4096 * 8
     o, pool = run_prefill(y, dev)
     o_ref, h_ref, _ = oracle_prefill(y)
-    assert rel_l2(f64(o), o_ref) <= 1e-2
-    assert rel_l2(f64(pool.cpu()[y["slot_idx"].long()]), h_ref) <= 1e-2
+    check_prefill_parity(f64(o), o_ref, f64(pool.cpu()[y["slot_idx"].long()]), h_ref, y["cu_seqlens"],
+                         1e-2, "520 short sequences")
 
 
 @pytest.mark.parametrize("dtype,d", [(torch.bfloat16, 128), (torch.float32, 64)])
@@ -183,8 +181,8 @@ def test_workspace_reused_across_calls():
                               y["slot_idx"].to(dev), workspace=ws)
         torch.cuda.synchronize()
         o_ref, h_ref, _ = oracle_prefill(y)
-        assert rel_l2(f64(o), o_ref) <= 1e-2
-        assert rel_l2(f64(pool.cpu()[y["slot_idx"].long()]), h_ref) <= 1e-2
+        check_prefill_parity(f64(o), o_ref, f64(pool.cpu()[y["slot_idx"].long()]), h_ref,
+                             y["cu_seqlens"], 1e-2, "workspace reuse")
 
 
 def prefix_states(y, requests, h0_from_pool=True):
@@ -229,8 +227,8 @@ def test_prefix_snapshots(dtype, d, tol):
     torch.cuda.synchronize()
     got = pool.cpu()
     o_ref, h_ref, _ = oracle_prefill(y)
-    assert rel_l2(f64(o), o_ref) <= tol
-    assert rel_l2(f64(got[y["slot_idx"].long()]), h_ref) <= tol
+    check_prefill_parity(f64(o), o_ref, f64(got[y["slot_idx"].long()]), h_ref, y["cu_seqlens"], tol,
+                         "snapshots")
     requests, slots = [], []
     untouched = set(range(num_slots)) - taken
     for i, L in enumerate(seqlens):
@@ -279,8 +277,8 @@ def test_zero_initial_state_ignores_pool_contents():
     y = W.prefill(seed=3, seqlens=(150, 20), H=2, dk=128, dv=128, num_slots=2, h0_std=1.0)
     o, pool = run_prefill(y, dev, h0_from_pool=False)
     o_ref, h_ref, _ = oracle_prefill(y, h0_from_pool=False)
-    assert rel_l2(f64(o), o_ref) <= 1e-2
-    assert rel_l2(f64(pool.cpu()[y["slot_idx"].long()]), h_ref) <= 1e-2
+    check_prefill_parity(f64(o), o_ref, f64(pool.cpu()[y["slot_idx"].long()]), h_ref, y["cu_seqlens"],
+                         1e-2, "h0 zero")
 
 
 def test_fp32_prefill_with_dk128_is_rejected():
@@ -324,34 +322,32 @@ def test_prefill_then_decode_equals_longer_prefill(dtype, d, tol):
 
 def test_prefill_full_size_T8192_H32():
     """Chunked prefill workload: T = 8192, H = 32, dk = dv = 128, bf16, zero initial state.
-    Oracle on 3 sampled heads (full 8192-token chains); every output must be finite."""
+    Every head against the oracle (32 full 8192-token chains): whole tensor, worst head and
+    worst (64-token chunk, head) for o, whole and worst head for the final state."""
     dev = need_gpu()
     announce("prefill T8192 H32 d128")
     y = W.prefill(seed=0, seqlens=(8192,), H=32, dk=128, dv=128, num_slots=1)
     o, pool = run_prefill(y, dev, h0_from_pool=False)
-    assert torch.isfinite(o).all()
-    heads = [0, 13, 31]
-    o_ref, h_ref, _ = oracle_prefill(y, h0_from_pool=False, heads=heads)
-    assert rel_l2(f64(o[:, heads]), o_ref) <= 1e-2
-    assert worst_rel_l2(f64(o[:, heads]), o_ref, axis=1) <= 1e-2
-    assert rel_l2(f64(pool.cpu()[0, heads]), h_ref[0]) <= 1e-2
+    o_ref, h_ref, _ = oracle_prefill(y, h0_from_pool=False)
+    oc, hc = f64(o), f64(pool.cpu()[y["slot_idx"].long()])
+    check_prefill_parity(oc, o_ref, hc, h_ref, y["cu_seqlens"], 1e-2, "T8192 H32")
+    wc = worst_chunk_head(oc, o_ref, y["cu_seqlens"])
+    announce("T8192 H32: worst (chunk, head) rel-L2 %.3g" % wc)
+    assert wc <= 2e-2
 
 
 def test_prefill_full_size_varlen_long_context():
     """Long-context varlen workload: 4 sequences (100000, 16384, 8192, 3500) packed with
-    cu_seqlens, H = 16, initial states from 4 pool slots.  Oracle on 2 sampled heads over
-    all four sequences (the 100,000-token chain included)."""
+    cu_seqlens, H = 16, initial states from 4 pool slots.  Every head of every sequence
+    against the oracle (the 100,000-token chains included): whole tensor, worst (sequence,
+    head), worst (64-token chunk, head) for o; whole and worst for the final states."""
     dev = need_gpu()
     announce("prefill varlen 128076 tokens H16")
     y = W.prefill_long(seed=0)
     o, pool = run_prefill(y, dev)
-    assert torch.isfinite(o).all()
-    heads = [2, 11]
-    o_ref, h_ref, _ = oracle_prefill(y, heads=heads)
-    assert rel_l2(f64(o[:, heads]), o_ref) <= 1e-2
-    sl = y["slot_idx"].long()
-    assert rel_l2(f64(pool.cpu()[sl][:, heads]), h_ref) <= 1e-2
-    # per-sequence outputs
-    cu = y["cu_seqlens"].tolist()
-    for i in range(4):
-        assert rel_l2(f64(o[cu[i]:cu[i + 1], heads]), o_ref[cu[i]:cu[i + 1]]) <= 1e-2, i
+    o_ref, h_ref, _ = oracle_prefill(y)
+    oc, hc = f64(o), f64(pool.cpu()[y["slot_idx"].long()])
+    check_prefill_parity(oc, o_ref, hc, h_ref, y["cu_seqlens"], 1e-2, "varlen 128076 H16")
+    wc = worst_chunk_head(oc, o_ref, y["cu_seqlens"])
+    announce("varlen 128076 H16: worst (chunk, head) rel-L2 %.3g" % wc)
+    assert wc <= 2e-2
