@@ -16,7 +16,8 @@
  *
  * Conventions shared by every entry point:
  *  - Ownership: the caller owns every buffer.  No entry point allocates or frees
- *    memory or keeps state between calls; calls are thread-safe.
+ *    memory or keeps state between calls; calls are thread-safe.  (Exception:
+ *    kda_chunk_prefill_noalloc uses a library-owned static device array per GPU.)
  *  - All pointers are device pointers to contiguous row-major arrays, 16-byte
  *    aligned.  Index arrays (slot_idx, accepted_len, cu_seqlens) live on the device
  *    and are read by the kernels, not by the host.
@@ -185,6 +186,30 @@ int kda_chunk_prefill_snapshots(const void* q, const void* k, const void* v, int
                                 int H, int dk, int dv, float scale, int use_qk_l2norm, void* o,
                                 void* workspace, size_t workspace_bytes, int snap_every,
                                 const int32_t* snap_slots, int max_snaps, hipStream_t stream);
+
+/*
+ * kda_chunk_prefill_noalloc -- kda_chunk_prefill without a caller workspace, for callers that
+ * cannot allocate device memory: code under HIP graph capture, serving loops that must not
+ * allocate, harnesses that forbid hipMalloc.  The call itself allocates nothing.
+ *
+ * Arguments, results and errors are those of kda_chunk_prefill minus workspace and
+ * workspace_bytes.  The workspace is a library-owned static device array of
+ * KDA_NOALLOC_SCRATCH_BYTES per GPU (held from the library's first use of the GPU until the
+ * process ends); its address is looked up on the first call on each device.  A call whose
+ * kda_chunk_prefill_workspace_size(...) exceeds KDA_NOALLOC_SCRATCH_BYTES returns
+ * KDA_ERR_WORKSPACE before any HIP call (about 3,000 (64-token chunk, head) items at
+ * dk = dv = 128: e.g. 4,096 tokens x 32 heads, or 8,192 x 16).  Every call on one GPU uses
+ * the same array: calls that overlap in time on one GPU (on different streams or from
+ * different host threads) race and give undefined results; calls ordered on one stream are
+ * safe.  The array's contents between calls do not matter (nothing needs clearing).
+ */
+#define KDA_NOALLOC_SCRATCH_BYTES ((size_t)256 << 20)
+int kda_chunk_prefill_noalloc(const void* q, const void* k, const void* v, int dtype,
+                              const float* g, const float* beta, const int32_t* cu_seqlens,
+                              int num_seqs, int64_t total_tokens, float* state_pool,
+                              int64_t num_slots, const int32_t* slot_idx, int h0_from_pool, int H,
+                              int dk, int dv, float scale, int use_qk_l2norm, void* o,
+                              hipStream_t stream);
 
 /* Human-readable name of a kda_status value (static string, never NULL). */
 const char* kda_status_string(int status);

@@ -17,6 +17,7 @@ KDA_ERR_WORKSPACE = -3
 KDA_ERR_HIP = -4
 KDA_F32 = 0
 KDA_BF16 = 1
+KDA_NOALLOC_SCRATCH_BYTES = 256 << 20  # include/kda.h
 
 _c_p = ctypes.c_void_p
 _c_i = ctypes.c_int
@@ -37,6 +38,9 @@ SIGNATURES = {
     "kda_chunk_prefill_snapshots": (_c_i, [_c_p, _c_p, _c_p, _c_i, _c_p, _c_p, _c_p, _c_i, _c_i64,
                                            _c_p, _c_i64, _c_p, _c_i, _c_i, _c_i, _c_i, _c_f, _c_i,
                                            _c_p, _c_p, _c_sz, _c_i, _c_p, _c_i, _c_p]),
+    "kda_chunk_prefill_noalloc": (_c_i, [_c_p, _c_p, _c_p, _c_i, _c_p, _c_p, _c_p, _c_i, _c_i64,
+                                         _c_p, _c_i64, _c_p, _c_i, _c_i, _c_i, _c_i, _c_f, _c_i,
+                                         _c_p, _c_p]),
     "kda_status_string": (ctypes.c_char_p, [_c_i]),
 }
 

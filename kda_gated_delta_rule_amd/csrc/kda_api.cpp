@@ -90,7 +90,7 @@ int chunk_prefill_impl(const void* q, const void* k, const void* v, int dtype, c
                        const int32_t* slot_idx, int h0_from_pool, int H, int dk, int dv,
                        float scale, int use_qk_l2norm, void* o, void* workspace,
                        size_t workspace_bytes, int snap_every, const int32_t* snap_slots,
-                       int max_snaps, hipStream_t stream) {
+                       int max_snaps, bool use_static, hipStream_t stream) {
     if (!valid_dtype(dtype)) return KDA_ERR_INVALID_ARG;
     if (num_seqs < 0 || total_tokens < 0 || H < 1 || num_slots < 1) return KDA_ERR_INVALID_ARG;
     if (num_seqs == 0 && total_tokens != 0) return KDA_ERR_INVALID_ARG;
@@ -119,6 +119,13 @@ int chunk_prefill_impl(const void* q, const void* k, const void* v, int dtype, c
     }
     const size_t need =
         kda::prefill_workspace_bytes(num_seqs, total_tokens, H, dk, dv, dtype == KDA_BF16);
+    if (use_static) {
+        // the library's static array: sizes beyond it are rejected before any HIP call
+        if (need > KDA_NOALLOC_SCRATCH_BYTES) return KDA_ERR_WORKSPACE;
+        workspace = kda::prefill_noalloc_scratch();
+        if (!workspace) return KDA_ERR_HIP;
+        workspace_bytes = KDA_NOALLOC_SCRATCH_BYTES;
+    }
     if (!workspace || !aligned16(workspace) || workspace_bytes < need) return KDA_ERR_WORKSPACE;
 
     kda::PrefillArgs a{q, k, v, g, beta, cu_seqlens, num_seqs, total_tokens, state_pool,
@@ -138,7 +145,20 @@ KDA_EXPORT int kda_chunk_prefill(const void* q, const void* k, const void* v, in
                                  void* workspace, size_t workspace_bytes, hipStream_t stream) {
     return chunk_prefill_impl(q, k, v, dtype, g, beta, cu_seqlens, num_seqs, total_tokens,
                               state_pool, num_slots, slot_idx, h0_from_pool, H, dk, dv, scale,
-                              use_qk_l2norm, o, workspace, workspace_bytes, 0, nullptr, 0, stream);
+                              use_qk_l2norm, o, workspace, workspace_bytes, 0, nullptr, 0, false,
+                              stream);
+}
+
+KDA_EXPORT int kda_chunk_prefill_noalloc(const void* q, const void* k, const void* v, int dtype,
+                                         const float* g, const float* beta,
+                                         const int32_t* cu_seqlens, int num_seqs,
+                                         int64_t total_tokens, float* state_pool,
+                                         int64_t num_slots, const int32_t* slot_idx,
+                                         int h0_from_pool, int H, int dk, int dv, float scale,
+                                         int use_qk_l2norm, void* o, hipStream_t stream) {
+    return chunk_prefill_impl(q, k, v, dtype, g, beta, cu_seqlens, num_seqs, total_tokens,
+                              state_pool, num_slots, slot_idx, h0_from_pool, H, dk, dv, scale,
+                              use_qk_l2norm, o, nullptr, 0, 0, nullptr, 0, true, stream);
 }
 
 KDA_EXPORT int kda_chunk_prefill_snapshots(
@@ -153,7 +173,7 @@ KDA_EXPORT int kda_chunk_prefill_snapshots(
     return chunk_prefill_impl(q, k, v, dtype, g, beta, cu_seqlens, num_seqs, total_tokens,
                               state_pool, num_slots, slot_idx, h0_from_pool, H, dk, dv, scale,
                               use_qk_l2norm, o, workspace, workspace_bytes, snap_every,
-                              snap_slots, max_snaps, stream);
+                              snap_slots, max_snaps, false, stream);
 }
 
 KDA_EXPORT const char* kda_status_string(int status) {

@@ -63,5 +63,9 @@ size_t prefill_workspace_bytes(int num_seqs, int64_t total_tokens, int H, int dk
 // False where the prefill LDS plan does not fit (fp32 inputs need dk = 64).
 bool prefill_supported(int bf16, int dk, int dv);
 hipError_t launch_prefill(const PrefillArgs& a, int bf16, int dk, int dv, hipStream_t stream);
+// The static prefill workspace of kda_chunk_prefill_noalloc (KDA_NOALLOC_SCRATCH_BYTES per
+// GPU): its device address on the current device, looked up once per device; nullptr if the
+// lookup fails.
+void* prefill_noalloc_scratch();
 
 }  // namespace kda

@@ -53,6 +53,10 @@
 // inputs the A and P operands are each carried as a high and a low bf16 part
 // (three MFMAs per product), so every A and P entry is accurate to about 2^-16 of
 // its terms.  Every accumulation, the cumsum and the triangular solve are fp32.
+#include <atomic>
+#include <mutex>
+
+#include "kda.h"
 #include "kda_device.hpp"
 #include "kda_internal.hpp"
 
@@ -1365,17 +1369,20 @@ __global__ __launch_bounds__(64 * (DK / 16)) void seg_scan_kernel(PrefillArgs a)
     }
 }
 
-// Compute units of the current device (cached per device).
+constexpr int kMaxDevices = 64;
+
+// Compute units of the current device (looked up once per device; the cache entries are
+// atomics, so concurrent first calls only repeat the lookup).
 int device_cu_count() {
-    static int cached[64] = {0};
+    static std::atomic<int> cached[kMaxDevices];
     int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (cached[dev] == 0) {
-        int n = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+    int n = cached[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
         if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-        cached[dev] = n;
+        cached[dev].store(n, std::memory_order_relaxed);
     }
-    return cached[dev];
+    return n;
 }
 
 template <int DK, int DV, class TIn>
@@ -1421,6 +1428,28 @@ hipError_t launch_prefill_dt(const PrefillArgs& a, int dk, int dv, hipStream_t s
 }
 
 }  // namespace
+
+// The workspace of kda_chunk_prefill_noalloc: one array per GPU, in the code object's
+// device memory.  In host code `scratch` names a host-side stand-in, not the device array:
+// kernels get the address hipGetSymbolAddress returns on each device, never the name.
+static __device__ __attribute__((aligned(256))) char scratch[KDA_NOALLOC_SCRATCH_BYTES];
+
+void* prefill_noalloc_scratch() {
+    static std::atomic<void*> addr[kMaxDevices];
+    static std::mutex mu;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    void* p = addr[dev].load(std::memory_order_acquire);
+    if (p) return p;
+    std::lock_guard<std::mutex> lock(mu);
+    p = addr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+        // with device `dev` current: its own copy of the array
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+        addr[dev].store(p, std::memory_order_release);
+    }
+    return p;
+}
 
 size_t prefill_workspace_bytes(int num_seqs, int64_t total_tokens, int H, int dk, int dv, int bf16) {
     return WsLayout(num_seqs, total_tokens, H, dk, dv, bf16 ? 2 : 4).total;

@@ -127,3 +127,34 @@ def chunk_prefill(q, k, v, g, beta, cu_seqlens, state_pool, slot_idx, *, h0_from
                                                      snapshot_slots.shape[1], _stream(q))
         _lib.check("kda_chunk_prefill_snapshots", st)
     return o
+
+
+def chunk_prefill_noalloc(q, k, v, g, beta, cu_seqlens, state_pool, slot_idx, *, h0_from_pool=True,
+                          o=None, scale=None, use_qk_l2norm=True):
+    """Varlen chunked prefill on the library's static workspace (kda_chunk_prefill_noalloc):
+    no device allocation inside the call (pass o to avoid the output allocation here too).
+    Arguments and result as chunk_prefill; sizes whose workspace exceeds
+    KDA_NOALLOC_SCRATCH_BYTES raise KdaError(KDA_ERR_WORKSPACE).  Calls that overlap in time on
+    one GPU share the workspace and race."""
+    Tt, H, dk = q.shape
+    dv = v.shape[-1]
+    ns = cu_seqlens.shape[0] - 1
+    _need(q.dtype in _DTYPES and k.dtype == q.dtype and v.dtype == q.dtype, "q/k/v dtype")
+    _need(g.dtype == torch.float32 and beta.dtype == torch.float32, "g and beta must be fp32")
+    _need(k.shape == q.shape and g.shape == q.shape and v.shape == (Tt, H, dv), "q/k/v/g shape")
+    _need(beta.shape == (Tt, H), "beta shape")
+    _need(cu_seqlens.dtype == torch.int32 and slot_idx.dtype == torch.int32, "index dtype")
+    _need(slot_idx.shape == (ns,), "slot_idx shape")
+    _need(state_pool.dim() == 4 and state_pool.shape[1:] == (H, dk, dv), "state_pool shape")
+    if o is None:
+        o = torch.empty(Tt, H, dv, dtype=q.dtype, device=q.device)
+    _need(o.shape == (Tt, H, dv) and o.dtype == q.dtype, "o shape/dtype")
+    _contig(q, k, v, g, beta, cu_seqlens, state_pool, slot_idx, o)
+    if scale is None:
+        scale = dk ** -0.5
+    st = _lib.load().kda_chunk_prefill_noalloc(
+        _ptr(q), _ptr(k), _ptr(v), _DTYPES[q.dtype], _ptr(g), _ptr(beta), _ptr(cu_seqlens), ns, Tt,
+        _ptr(state_pool), state_pool.shape[0], _ptr(slot_idx), int(bool(h0_from_pool)), H, dk, dv,
+        float(scale), int(bool(use_qk_l2norm)), _ptr(o), _stream(q))
+    _lib.check("kda_chunk_prefill_noalloc", st)
+    return o

@@ -148,6 +148,37 @@ def test_prefill_valid_arguments_reach_workspace_check(lib):
     assert lib.kda_chunk_prefill(*prefill_args().values()) == _lib.KDA_ERR_WORKSPACE
 
 
+def noalloc_args(**over):
+    args = prefill_args(**over)
+    del args["ws"], args["ws_bytes"]
+    return list(args.values())
+
+
+def test_noalloc_rejects_sizes_beyond_the_static_workspace(lib):
+    # T = 8192 x H = 32 needs about 350 MB of workspace, more than the 256 MiB array: the
+    # call stops at the size check, before any HIP call
+    f = lib.kda_chunk_prefill_workspace_size
+    assert f(1, 8192, 32, 128, 128, 1) > _lib.KDA_NOALLOC_SCRATCH_BYTES
+    assert f(1, 4096, 32, 128, 128, 1) <= _lib.KDA_NOALLOC_SCRATCH_BYTES
+    assert lib.kda_chunk_prefill_noalloc(*noalloc_args(ns=1, T=8192, H=32)) == _lib.KDA_ERR_WORKSPACE
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(q=None), _lib.KDA_ERR_INVALID_ARG),
+    (dict(h0=3), _lib.KDA_ERR_INVALID_ARG),
+    (dict(ns=0, T=0), _lib.KDA_OK),
+    (dict(dk=100), _lib.KDA_ERR_UNSUPPORTED),
+])
+def test_noalloc_validation(lib, over, code):
+    assert lib.kda_chunk_prefill_noalloc(*noalloc_args(**over)) == code
+
+
+def test_noalloc_limit_matches_the_header():
+    text = open(os.path.join(ROOT, "include", "kda.h")).read()
+    m = re.search(r"#define KDA_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == _lib.KDA_NOALLOC_SCRATCH_BYTES
+
+
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(_lib, "_LIB", None)
     monkeypatch.setattr(_lib, "lib_path", lambda: str(tmp_path / "missing.so"))
