@@ -1,4 +1,11 @@
-"""Thin wrappers: torch tensors -> C ABI calls of libkda.so (marshalling only)."""
+"""Thin wrappers: torch tensors -> C ABI calls of libkda.so (marshalling only).
+
+The C ABI does not read the device-resident index arrays on the host (out-of-range or duplicate
+slots, accepted lengths outside 0..T and inconsistent cu_seqlens are undefined behaviour there).
+With the environment variable KDA_DEBUG_VALIDATE=1, every wrapper here first copies those arrays
+to the host and checks them, raising ValueError before any launch (a synchronising debug aid)."""
+import os
+
 import torch
 
 from . import _lib
@@ -25,6 +32,45 @@ def _contig(*ts):
             _need(t.is_contiguous(), "tensors must be contiguous")
 
 
+def debug_validate_enabled():
+    """True when KDA_DEBUG_VALIDATE is set to a non-empty value other than 0."""
+    return os.environ.get("KDA_DEBUG_VALIDATE", "0") not in ("", "0")
+
+
+def _host(t):
+    return [int(x) for x in t.detach().to("cpu").reshape(-1).tolist()]
+
+
+def validate_slots(slot_idx, num_slots, allow_skip):
+    """Slots in range and distinct; negative entries (skipped) only where allowed."""
+    s = _host(slot_idx)
+    live = [x for x in s if x >= 0]
+    _need(allow_skip or len(live) == len(s), "KDA_DEBUG_VALIDATE: negative slot index")
+    _need(all(x < num_slots for x in live), "KDA_DEBUG_VALIDATE: slot index >= num_slots")
+    _need(len(set(live)) == len(live), "KDA_DEBUG_VALIDATE: duplicate slot index")
+    return live
+
+
+def validate_accepted(accepted_len, T):
+    a = _host(accepted_len)
+    _need(all(0 <= x <= T for x in a), "KDA_DEBUG_VALIDATE: accepted_len outside 0..T")
+
+
+def validate_cu_seqlens(cu_seqlens, total_tokens):
+    cu = _host(cu_seqlens)
+    _need(len(cu) >= 1 and cu[0] == 0, "KDA_DEBUG_VALIDATE: cu_seqlens[0] != 0")
+    _need(all(b >= a for a, b in zip(cu[:-1], cu[1:])), "KDA_DEBUG_VALIDATE: cu_seqlens decreases")
+    _need(cu[-1] == total_tokens, "KDA_DEBUG_VALIDATE: cu_seqlens[-1] != total_tokens")
+
+
+def validate_snapshots(snapshot_slots, slot_idx, num_slots):
+    snaps = [x for x in _host(snapshot_slots) if x >= 0]
+    fin = set(_host(slot_idx))
+    _need(all(x < num_slots for x in snaps), "KDA_DEBUG_VALIDATE: snapshot slot >= num_slots")
+    _need(len(set(snaps)) == len(snaps), "KDA_DEBUG_VALIDATE: duplicate snapshot slot")
+    _need(not (set(snaps) & fin), "KDA_DEBUG_VALIDATE: snapshot slot equals a final-state slot")
+
+
 def decode_step(q, k, v, g, beta, state_pool, slot_idx, *, o=None, records=None, scale=None,
                 use_qk_l2norm=True):
     """Decode / MTP step (kda_decode_step).
@@ -49,6 +95,8 @@ def decode_step(q, k, v, g, beta, state_pool, slot_idx, *, o=None, records=None,
         _need(records.shape == (N, T, H, 2 * dk + dv) and records.dtype == torch.float32,
               "records shape/dtype")
     _contig(q, k, v, g, beta, state_pool, slot_idx, o, records)
+    if debug_validate_enabled():
+        validate_slots(slot_idx, state_pool.shape[0], allow_skip=True)
     if scale is None:
         scale = dk ** -0.5
     st = _lib.load().kda_decode_step(
@@ -68,6 +116,9 @@ def replay_commit(state_pool, slot_idx, records, accepted_len):
     _need(slot_idx.shape == (N,) and accepted_len.shape == (N,), "slot_idx/accepted_len shape")
     _need(accepted_len.dtype == torch.int32 and slot_idx.dtype == torch.int32, "index dtype")
     _contig(state_pool, slot_idx, records, accepted_len)
+    if debug_validate_enabled():
+        validate_slots(slot_idx, state_pool.shape[0], allow_skip=True)
+        validate_accepted(accepted_len, T)
     st = _lib.load().kda_replay_commit(_ptr(state_pool), state_pool.shape[0], _ptr(slot_idx),
                                        _ptr(records), _ptr(accepted_len), N, T, H, dk, dv,
                                        _stream(state_pool))
@@ -105,6 +156,11 @@ def chunk_prefill(q, k, v, g, beta, cu_seqlens, state_pool, slot_idx, *, h0_from
     _need(state_pool.dim() == 4 and state_pool.shape[1:] == (H, dk, dv), "state_pool shape")
     if o is None:
         o = torch.empty(Tt, H, dv, dtype=q.dtype, device=q.device)
+    if debug_validate_enabled():
+        validate_cu_seqlens(cu_seqlens, Tt)
+        validate_slots(slot_idx, state_pool.shape[0], allow_skip=False)
+        if snapshot_slots is not None:
+            validate_snapshots(snapshot_slots, slot_idx, state_pool.shape[0])
     need = chunk_prefill_workspace_size(ns, Tt, H, dk, dv, q.dtype)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
@@ -150,6 +206,9 @@ def chunk_prefill_noalloc(q, k, v, g, beta, cu_seqlens, state_pool, slot_idx, *,
         o = torch.empty(Tt, H, dv, dtype=q.dtype, device=q.device)
     _need(o.shape == (Tt, H, dv) and o.dtype == q.dtype, "o shape/dtype")
     _contig(q, k, v, g, beta, cu_seqlens, state_pool, slot_idx, o)
+    if debug_validate_enabled():
+        validate_cu_seqlens(cu_seqlens, Tt)
+        validate_slots(slot_idx, state_pool.shape[0], allow_skip=False)
     if scale is None:
         scale = dk ** -0.5
     st = _lib.load().kda_chunk_prefill_noalloc(

@@ -26,7 +26,8 @@ EPS = 1e-6  # L2-norm epsilon inside the square root (the pages give none)
 def _lib():
     global _LIB
     if _LIB is None:
-        path = _build.LIB
+        # KDA_ORACLE_LIB selects another build of the same source (the sanitizer build)
+        path = os.environ.get("KDA_ORACLE_LIB") or _build.LIB
         if not os.path.exists(path):
             _build.build(force=True)
         lib = ctypes.CDLL(path)
