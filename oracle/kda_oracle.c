@@ -341,6 +341,254 @@ int kda_oracle_chunked(const double *q, const double *k, const double *v, const 
     return run_all(&J);
 }
 
+/* ---------------------------------------------------------------------------
+ * Backward of the token recurrence (gradients of L = sum(do * o) + sum(dht * ht)),
+ * one (sequence, head) chain per call.  The page's training section (the item on
+ * linear-attention kernels built with Triton-Ascend, "基于昇腾实现Kimi K3训练基础功能适配
+ * 与深度优化") names backward kernels but prints no formula; this is the chain rule
+ * through the steps of run_chain_recurrent in reverse token order, with
+ * D = dL/dS_t carried backwards (the same steps as oracle/kda_backward.py):
+ *
+ *   dqh_t = scale S_t do_t ;  D += scale qh_t do_t^T
+ *   du_t = D^T kh_t ;  dkh_t = D u_t
+ *   dbeta_t = du_t . (v_t - p_t) ;  dv_t = beta_t du_t ;  dp_t = -beta_t du_t
+ *   D' = D + kh_t dp_t^T ;  dkh_t += S'_t dp_t
+ *   dg_t = alpha_t * rowsum(D' * S_{t-1}) ;  D <- diag(alpha_t) D'
+ *   dq_t = (dqh_t - qh_t (qh_t . dqh_t)) / sqrt(|q_t|^2 + eps)  (k likewise; identity
+ *                                                                 without the norm)
+ *   dh0 = D after the first token.
+ *
+ * The forward states are needed in reverse order: the forward pass keeps the state at
+ * every 64-token boundary, and the backward recomputes the states of one 64-token span
+ * at a time from its kept state with the same forward steps.
+ * ------------------------------------------------------------------------- */
+typedef struct {
+    const double *q, *k, *v, *g, *beta, *h0, *dout, *dht;
+    const int64_t *cu_seqlens;
+    int num_seqs, H, dk, dv, use_qk_l2norm;
+    double scale, eps;
+    double *dq, *dk_, *dv_, *dg, *dbeta, *dh0;
+    int nthreads, tid, status;
+} bwd_job_t;
+
+#define BWD_SPAN 64
+
+/* One forward token step from S (dk x dv) into Sn, keeping S' = diag(alpha) S, p, u and
+ * the normalised q and k. */
+static void fwd_token(const bwd_job_t *J, int64_t t, int h, const double *S, double *Sp,
+                      double *Sn, double *qh, double *kh, double *nq, double *nk, double *al,
+                      double *p, double *u)
+{
+    const int H = J->H, dk = J->dk, dv = J->dv;
+    const size_t rk = ((size_t)t * H + h) * dk, rv = ((size_t)t * H + h) * dv;
+    double sq = 0.0, sk = 0.0;
+    for (int c = 0; c < dk; ++c) {
+        sq += J->q[rk + c] * J->q[rk + c];
+        sk += J->k[rk + c] * J->k[rk + c];
+    }
+    *nq = J->use_qk_l2norm ? sqrt(sq + J->eps) : 1.0;
+    *nk = J->use_qk_l2norm ? sqrt(sk + J->eps) : 1.0;
+    for (int c = 0; c < dk; ++c) {
+        qh[c] = J->q[rk + c] / *nq;
+        kh[c] = J->k[rk + c] / *nk;
+        al[c] = exp(J->g[rk + c]);
+    }
+    for (int c = 0; c < dk; ++c)
+        for (int j = 0; j < dv; ++j) Sp[(size_t)c * dv + j] = al[c] * S[(size_t)c * dv + j];
+    const double b = J->beta[(size_t)t * H + h];
+    for (int j = 0; j < dv; ++j) {
+        double x = 0.0;
+        for (int c = 0; c < dk; ++c) x += Sp[(size_t)c * dv + j] * kh[c];
+        p[j] = x;
+        u[j] = b * (J->v[rv + j] - x);
+    }
+    for (int c = 0; c < dk; ++c)
+        for (int j = 0; j < dv; ++j) Sn[(size_t)c * dv + j] = Sp[(size_t)c * dv + j] + kh[c] * u[j];
+}
+
+static int run_chain_backward(const bwd_job_t *J, int n, int h)
+{
+    const int H = J->H, dk = J->dk, dv = J->dv;
+    const size_t SZ = (size_t)dk * dv;
+    const int64_t bos = J->cu_seqlens[n], eos = J->cu_seqlens[n + 1];
+    const int64_t nspan = (eos - bos + BWD_SPAN - 1) / BWD_SPAN;
+    double *ck = (double *)malloc(sizeof(double) * SZ * (size_t)(nspan > 0 ? nspan : 1));
+    double *Sprev = (double *)malloc(sizeof(double) * SZ * BWD_SPAN);
+    double *Spv = (double *)malloc(sizeof(double) * SZ * BWD_SPAN);
+    double *Snew = (double *)malloc(sizeof(double) * SZ * BWD_SPAN);
+    double *D = (double *)malloc(sizeof(double) * SZ);
+    double *Dp = (double *)malloc(sizeof(double) * SZ);
+    double *QH = (double *)malloc(sizeof(double) * (size_t)dk * BWD_SPAN);
+    double *KH = (double *)malloc(sizeof(double) * (size_t)dk * BWD_SPAN);
+    double *AL = (double *)malloc(sizeof(double) * (size_t)dk * BWD_SPAN);
+    double *PP = (double *)malloc(sizeof(double) * (size_t)dv * BWD_SPAN);
+    double *UU = (double *)malloc(sizeof(double) * (size_t)dv * BWD_SPAN);
+    double *NQ = (double *)malloc(sizeof(double) * BWD_SPAN);
+    double *NK = (double *)malloc(sizeof(double) * BWD_SPAN);
+    double *dqh = (double *)malloc(sizeof(double) * dk);
+    double *dkh = (double *)malloc(sizeof(double) * dk);
+    double *du = (double *)malloc(sizeof(double) * dv);
+    int st = KDA_ORACLE_OK;
+    if (!ck || !Sprev || !Spv || !Snew || !D || !Dp || !QH || !KH || !AL || !PP || !UU || !NQ ||
+        !NK || !dqh || !dkh || !du) {
+        st = KDA_ORACLE_ENOMEM;
+        goto done;
+    }
+    /* forward: the state entering every 64-token span */
+    {
+        double *S = Sprev, *Sn = Snew;
+        if (J->h0) memcpy(S, J->h0 + ((size_t)n * H + h) * SZ, sizeof(double) * SZ);
+        else memset(S, 0, sizeof(double) * SZ);
+        for (int64_t m = 0; m < nspan; ++m) {
+            memcpy(ck + (size_t)m * SZ, S, sizeof(double) * SZ);
+            const int64_t t1 = bos + (m + 1) * BWD_SPAN < eos ? bos + (m + 1) * BWD_SPAN : eos;
+            for (int64_t t = bos + m * BWD_SPAN; t < t1; ++t) {
+                fwd_token(J, t, h, S, Spv, Sn, QH, KH, NQ, NK, AL, PP, UU);
+                double *x = S; S = Sn; Sn = x;
+            }
+        }
+    }
+    /* backward, one span at a time from the last */
+    if (J->dht) memcpy(D, J->dht + ((size_t)n * H + h) * SZ, sizeof(double) * SZ);
+    else memset(D, 0, sizeof(double) * SZ);
+    for (int64_t m = nspan - 1; m >= 0; --m) {
+        const int64_t t0 = bos + m * BWD_SPAN;
+        const int L = (int)((t0 + BWD_SPAN < eos ? t0 + BWD_SPAN : eos) - t0);
+        memcpy(Sprev, ck + (size_t)m * SZ, sizeof(double) * SZ);
+        for (int i = 0; i < L; ++i) {
+            if (i > 0) memcpy(Sprev + (size_t)i * SZ, Snew + (size_t)(i - 1) * SZ, sizeof(double) * SZ);
+            fwd_token(J, t0 + i, h, Sprev + (size_t)i * SZ, Spv + (size_t)i * SZ, Snew + (size_t)i * SZ,
+                      QH + (size_t)i * dk, KH + (size_t)i * dk, NQ + i, NK + i, AL + (size_t)i * dk,
+                      PP + (size_t)i * dv, UU + (size_t)i * dv);
+        }
+        for (int i = L - 1; i >= 0; --i) {
+            const int64_t t = t0 + i;
+            const size_t rk = ((size_t)t * H + h) * dk, rv = ((size_t)t * H + h) * dv;
+            const double *S1 = Snew + (size_t)i * SZ, *S0 = Sprev + (size_t)i * SZ;
+            const double *Sp = Spv + (size_t)i * SZ;
+            const double *qh = QH + (size_t)i * dk, *kh = KH + (size_t)i * dk, *al = AL + (size_t)i * dk;
+            const double *p = PP + (size_t)i * dv, *u = UU + (size_t)i * dv;
+            const double *dout = J->dout + rv;
+            const double b = J->beta[(size_t)t * H + h];
+            /* output: o = scale S_t^T qh */
+            for (int c = 0; c < dk; ++c) {
+                double x = 0.0;
+                for (int j = 0; j < dv; ++j) x += S1[(size_t)c * dv + j] * dout[j];
+                dqh[c] = J->scale * x;
+            }
+            for (int c = 0; c < dk; ++c)
+                for (int j = 0; j < dv; ++j) D[(size_t)c * dv + j] += J->scale * qh[c] * dout[j];
+            /* update S_t = S'_t + kh u^T */
+            double db = 0.0;
+            for (int j = 0; j < dv; ++j) {
+                double x = 0.0;
+                for (int c = 0; c < dk; ++c) x += D[(size_t)c * dv + j] * kh[c];
+                du[j] = x;
+                db += x * (J->v[rv + j] - p[j]);
+            }
+            for (int c = 0; c < dk; ++c) {
+                double x = 0.0;
+                for (int j = 0; j < dv; ++j) x += D[(size_t)c * dv + j] * u[j];
+                dkh[c] = x;
+            }
+            /* u = beta (v - p), p = S'^T kh */
+            J->dbeta[(size_t)t * H + h] = db;
+            for (int j = 0; j < dv; ++j) J->dv_[rv + j] = b * du[j];
+            for (int c = 0; c < dk; ++c) {
+                double x = 0.0;
+                for (int j = 0; j < dv; ++j) {
+                    const double dp = -b * du[j];
+                    Dp[(size_t)c * dv + j] = D[(size_t)c * dv + j] + kh[c] * dp;
+                    x += Sp[(size_t)c * dv + j] * dp;
+                }
+                dkh[c] += x;
+            }
+            /* S' = diag(alpha) S_{t-1}, alpha = exp(g) */
+            for (int c = 0; c < dk; ++c) {
+                double x = 0.0;
+                for (int j = 0; j < dv; ++j) x += Dp[(size_t)c * dv + j] * S0[(size_t)c * dv + j];
+                J->dg[rk + c] = al[c] * x;
+                for (int j = 0; j < dv; ++j) D[(size_t)c * dv + j] = al[c] * Dp[(size_t)c * dv + j];
+            }
+            /* L2 norms */
+            double pq = 0.0, pk = 0.0;
+            for (int c = 0; c < dk; ++c) {
+                pq += qh[c] * dqh[c];
+                pk += kh[c] * dkh[c];
+            }
+            for (int c = 0; c < dk; ++c) {
+                if (J->use_qk_l2norm) {
+                    J->dq[rk + c] = (dqh[c] - qh[c] * pq) / NQ[i];
+                    J->dk_[rk + c] = (dkh[c] - kh[c] * pk) / NK[i];
+                } else {
+                    J->dq[rk + c] = dqh[c];
+                    J->dk_[rk + c] = dkh[c];
+                }
+            }
+        }
+    }
+    if (J->dh0) memcpy(J->dh0 + ((size_t)n * H + h) * SZ, D, sizeof(double) * SZ);
+done:
+    free(ck); free(Sprev); free(Spv); free(Snew); free(D); free(Dp); free(QH); free(KH);
+    free(AL); free(PP); free(UU); free(NQ); free(NK); free(dqh); free(dkh); free(du);
+    return st;
+}
+
+static void *bwd_worker(void *arg)
+{
+    bwd_job_t *J = (bwd_job_t *)arg;
+    const int nchains = J->num_seqs * J->H;
+    for (int i = J->tid; i < nchains; i += J->nthreads) {
+        int st = run_chain_backward(J, i / J->H, i % J->H);
+        if (st != KDA_ORACLE_OK) J->status = st;
+    }
+    return NULL;
+}
+
+/* Gradients of sum(do * o) + sum(dht * ht) of the varlen token recurrence with respect to
+ * q, k, v, g, beta and h0.  h0 and dht may be NULL (zero); dh0 may be NULL.  Layouts as the
+ * forward; do [T_total, H, dv]; dq, dk, dg [T_total, H, dk]; dv [T_total, H, dv]; dbeta
+ * [T_total, H]; dh0 [num_seqs, H, dk, dv].  Returns 0 on success. */
+int kda_oracle_backward(const double *q, const double *k, const double *v, const double *g,
+                        const double *beta, const int64_t *cu_seqlens, int num_seqs, int H,
+                        int dk, int dv, double scale, int use_qk_l2norm, double eps,
+                        const double *h0, const double *dout, const double *dht, double *dq,
+                        double *dk_, double *dv_, double *dg, double *dbeta, double *dh0,
+                        int nthreads)
+{
+    int st = check_common(q, k, v, g, beta, cu_seqlens, num_seqs, H, dk, dv, dout);
+    if (st) return st;
+    if (!dq || !dk_ || !dv_ || !dg || !dbeta) return KDA_ORACLE_EINVAL;
+    bwd_job_t proto = {q, k, v, g, beta, h0, dout, dht, cu_seqlens, num_seqs, H, dk, dv,
+                       use_qk_l2norm, scale, eps, dq, dk_, dv_, dg, dbeta, dh0, 0, 0, 0};
+    int nt = nthreads < 1 ? 1 : nthreads;
+    const int nchains = num_seqs * H;
+    if (nt > nchains) nt = nchains > 0 ? nchains : 1;
+    bwd_job_t *jobs = (bwd_job_t *)calloc((size_t)nt, sizeof(bwd_job_t));
+    pthread_t *th = (pthread_t *)calloc((size_t)nt, sizeof(pthread_t));
+    if (!jobs || !th) {
+        free(jobs); free(th);
+        return KDA_ORACLE_ENOMEM;
+    }
+    for (int i = 0; i < nt; ++i) {
+        jobs[i] = proto;
+        jobs[i].nthreads = nt;
+        jobs[i].tid = i;
+    }
+    for (int i = 1; i < nt; ++i)
+        if (pthread_create(&th[i], NULL, bwd_worker, &jobs[i]) != 0) {
+            bwd_worker(&jobs[i]);
+            th[i] = 0;
+        }
+    bwd_worker(&jobs[0]);
+    for (int i = 1; i < nt; ++i)
+        if (th[i]) pthread_join(th[i], NULL);
+    for (int i = 0; i < nt; ++i)
+        if (jobs[i].status != KDA_ORACLE_OK) st = jobs[i].status;
+    free(jobs); free(th);
+    return st;
+}
+
 /* ReplaySSM commit (section 04): for each sequence n, starting from the committed
  * state[n] ([H, dk, dv]), apply the records of tokens 0 .. accepted[n]-1 in order:
  * S <- diag(alpha) S + kh u^T.  records [N, T, H, 2*dk + dv]. */

@@ -38,6 +38,9 @@ def _lib():
         lib.kda_oracle_chunked.argtypes = [_DP] * 5 + [_I64P] + [ctypes.c_int] * 4 + [
             ctypes.c_double, ctypes.c_int, ctypes.c_double, _DP, _DP, _DP, ctypes.c_int,
             ctypes.c_int]
+        lib.kda_oracle_backward.restype = ctypes.c_int
+        lib.kda_oracle_backward.argtypes = [_DP] * 5 + [_I64P] + [ctypes.c_int] * 4 + [
+            ctypes.c_double, ctypes.c_int, ctypes.c_double] + [_DP] * 9 + [ctypes.c_int]
         lib.kda_oracle_replay.restype = ctypes.c_int
         lib.kda_oracle_replay.argtypes = [_DP, _DP, _I64P] + [ctypes.c_int] * 5
         _LIB = lib
@@ -115,6 +118,33 @@ def chunked(q, k, v, g, beta, cu_seqlens, h0=None, scale=None, use_qk_l2norm=Tru
     if st != 0:
         raise RuntimeError("kda_oracle_chunked failed with status %d" % st)
     return o, ht
+
+
+def backward(q, k, v, g, beta, cu_seqlens, do, dht=None, h0=None, scale=None, use_qk_l2norm=True,
+             eps=EPS, nthreads=None):
+    """fp64 gradients of sum(do * o) + sum(dht * ht) of the token recurrence (kda_oracle.c,
+    run_chain_backward).  Returns (dq, dk, dv, dg, dbeta, dh0)."""
+    q, k, v, g, beta, cu, h0, T, H, dk, dv, ns = _prep(q, k, v, g, beta, cu_seqlens, h0)
+    do = _f64(do)
+    if do.shape != (T, H, dv):
+        raise ValueError("do must be [T_total, H, dv]")
+    if dht is not None:
+        dht = _f64(dht)
+        if dht.shape != (ns, H, dk, dv):
+            raise ValueError("dht must be [num_seqs, H, dk, dv]")
+    if scale is None:
+        scale = dk ** -0.5
+    dq, dk_, dg = np.zeros((T, H, dk)), np.zeros((T, H, dk)), np.zeros((T, H, dk))
+    dvv, dbeta = np.zeros((T, H, dv)), np.zeros((T, H))
+    dh0 = np.zeros((ns, H, dk, dv))
+    st = _lib().kda_oracle_backward(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), cu.ctypes.data_as(_I64P), ns, H, dk, dv,
+        float(scale), int(bool(use_qk_l2norm)), float(eps), _ptr(h0), _ptr(do), _ptr(dht),
+        _ptr(dq), _ptr(dk_), _ptr(dvv), _ptr(dg), _ptr(dbeta), _ptr(dh0),
+        int(nthreads or default_threads()))
+    if st != 0:
+        raise RuntimeError("kda_oracle_backward failed with status %d" % st)
+    return dq, dk_, dvv, dg, dbeta, dh0
 
 
 def replay(state, records, accepted):

@@ -73,3 +73,47 @@ def test_constant_state_readout_closed_form():
             want = dht[n, h] + scale * sum(np.outer(x["q"][t, h], do[t, h]) for t in range(b, e))
             assert np.allclose(dh0[n, h], want, rtol=0, atol=1e-12)
     assert np.all(dv == 0) and np.allclose(dk, 0, atol=1e-15)
+
+
+def test_c_backward_equals_the_numpy_backward():
+    """The C backward (kda_oracle.c: forward kept every 64 tokens, spans recomputed) and the
+    numpy backward are two implementations of the same reverse recurrence: equal to 1e-12
+    over sequences that cross several 64-token spans, with and without the norm, h0 and dht."""
+    r = np.random.default_rng(7)
+    lens = (1, 64, 65, 130, 0, 7)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    T, H, dk, dv = int(cu[-1]), 2, 5, 4
+    for l2, with_state in ((True, True), (False, True), (True, False)):
+        x = dict(q=r.normal(size=(T, H, dk)), k=r.normal(size=(T, H, dk)) * (1 if l2 else 0.4),
+                 v=r.normal(size=(T, H, dv)), g=-0.2 * np.log1p(np.exp(r.normal(size=(T, H, dk)))),
+                 beta=1.0 / (1.0 + np.exp(-r.normal(size=(T, H)))))
+        h0 = 0.3 * r.normal(size=(len(lens), H, dk, dv)) if with_state else None
+        dht = r.normal(size=(len(lens), H, dk, dv)) if with_state else None
+        do = r.normal(size=(T, H, dv))
+        a = O.backward(x["q"], x["k"], x["v"], x["g"], x["beta"], cu, do, dht=dht, h0=h0,
+                       use_qk_l2norm=l2, nthreads=3)
+        b = recurrent_backward(x["q"], x["k"], x["v"], x["g"], x["beta"], cu, do, dht=dht, h0=h0,
+                               use_qk_l2norm=l2)
+        for name, ga, gb in zip(("dq", "dk", "dv", "dg", "dbeta", "dh0"), a, b):
+            assert np.abs(ga - gb).max() <= 1e-12 * max(1.0, np.abs(gb).max()), (name, l2)
+
+
+def test_c_backward_matches_central_differences_across_spans():
+    """The C backward against central finite differences of the C forward oracle on a sequence
+    of 70 tokens (two 64-token spans of the recomputation) plus a 3-token one."""
+    x, cu, do, dht = _case(11, T_lens=(70, 3), H=1, dk=3, dv=2)
+    dq, dk, dv, dg, dbeta, dh0 = O.backward(x["q"], x["k"], x["v"], x["g"], x["beta"], cu, do,
+                                            dht=dht, h0=x["h0"], nthreads=1)
+    grads = dict(q=dq, k=dk, v=dv, g=dg, beta=dbeta, h0=dh0)
+    eps = 1e-6
+    for name, grad in grads.items():
+        base = x[name]
+        for idx in list(np.ndindex(base.shape))[::7]:
+            keep = base[idx]
+            base[idx] = keep + eps
+            lp = _loss(x, cu, do, dht, True)
+            base[idx] = keep - eps
+            lm = _loss(x, cu, do, dht, True)
+            base[idx] = keep
+            num = (lp - lm) / (2 * eps)
+            assert abs(num - grad[idx]) <= 1e-6 * max(1.0, abs(num)), (name, idx, num, grad[idx])
