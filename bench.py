@@ -12,8 +12,9 @@ value = state updates per second = (sequences x heads) x steps / elapsed.
 Also measured in the same run (reported under "extra", not part of the timed
 step): chunked prefill (T = 8192, H = 32) and the long-context varlen prefill
 (4 sequences, 128,076 tokens, H = 16) as tokens/s with their MFMA and HBM
-fractions; speculative verify + ReplaySSM commit (32 x 8 tokens, H = 32); a
-device copy of 1 GiB as a bandwidth reference; and the fp64 CPU oracle on a
+fractions; speculative verify + ReplaySSM commit (32 x 8 tokens, H = 32); the
+chunked backward on the T = 8192, H = 32 shape; a device copy of 1 GiB as a
+bandwidth reference; and the fp64 CPU oracle on a
 bounded sample of the decode workload (cpu_baseline).
 
 Prints ONE JSON line.
@@ -30,6 +31,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, vendor figure
+FP32_PEAK_TFLOPS = 157.3       # MI355X fp32 (matrix and vector), vendor figure
 METRIC = ("KDA decode state-updates/s (HBM GB/s % peak); "
           "chunked-prefill tokens/s (MFMA %)")
 
@@ -52,13 +54,36 @@ def prefill_bytes_per_token_head(dk, dv, io_bytes):
 
 
 def prefill_flops_per_token_head(dk, dv, C=64):
-    """Algorithmic flops per (token, head) of the 64-token chunk form, counting every
-    intra-chunk product as a dense C x C tile: A and P (2 C^2 dk each), the W and Ut
-    triangular solves (2 C^2 dk and 2 C^2 dv), Q' = QG - P W and Ot = P Ut (2 C^2 dk and
-    2 C^2 dv) -- together 2 C^2 (3 dk + 2 dv) -- plus the three state products W S, Q' S and
-    Kt U (2 C dk dv each); divided by the C tokens of a chunk."""
+    """Algorithmic flops per (token, head) of the 64-token chunk form as the kernels compute it,
+    counting every intra-chunk product as a dense C x C tile: A and P (2 C^2 dk each), W = T KG
+    (2 C^2 dk), Ut = T V (2 C^2 dv) and P U (2 C^2 dv) -- together 2 C^2 (3 dk + 2 dv) -- plus
+    the three state products W S, QG S and Kt^T U (2 C dk dv each); divided by the C tokens of
+    a chunk."""
     per_chunk = 2 * C * C * (3 * dk + 2 * dv) + 3 * 2 * C * dk * dv
     return per_chunk / C
+
+
+def backward_flops_per_token_head(dk, dv, C=64):
+    """Algorithmic flops per (token, head) of the chunked backward as the kernels compute it
+    (dense C x C tiles), divided by the C tokens of a chunk: the forward pass it runs again
+    (prefill_flops_per_token_head), the recomputed A, P, W, Ut (2 C^2 (3 dk + dv)), the reverse
+    recurrence's Mt = W^T Kt, P W and b = Q'^T dO (2 C dk^2 + 2 C^2 dk + 2 C dk dv) and its
+    step Mt dS (2 dk^2 dv), the products with the state and its gradient (W S, Kt dH, dO S^T,
+    dU S^T, U dH^T: 5 x 2 C dk dv; P^T dO and dO U^T: 2 x 2 C^2 dv), the UT backward (dT, dBK,
+    dBV: 2 C^2 (2 dk + 2 dv); T^T dT and its product with T^T: 2 x 2 C^3) and the four decayed
+    token products (4 x 2 C^2 dk)."""
+    per_chunk = (2 * C * C * (3 * dk + dv)
+                 + 2 * C * dk * dk + 2 * C * C * dk + 2 * C * dk * dv + 2 * dk * dk * dv
+                 + 5 * 2 * C * dk * dv + 2 * 2 * C * C * dv
+                 + 2 * C * C * (2 * dk + 2 * dv) + 2 * 2 * C ** 3
+                 + 4 * 2 * C * C * dk)
+    return per_chunk / C + prefill_flops_per_token_head(dk, dv, C)
+
+
+def backward_bytes_per_token_head(dk, dv, io_bytes):
+    """q, k, v and the output gradient read (io dtype), g and beta read; dq, dk, dv written (io
+    dtype), dg and dbeta written (fp32), once each."""
+    return (4 * dk + 3 * dv) * io_bytes + 8 * dk + 8
 
 
 def counted_traffic(path):
@@ -392,6 +417,51 @@ def bench_prefill(args, dev, log, which):
                                                name, per * 1e6, byts)}
 
 
+def bench_backward(args, dev, log):
+    """The chunked backward (kda_chunk_backward) on the prefill workload's shape (T = 8192,
+    H = 32, dk = dv = 128, bf16, zero initial state, random output and final-state gradients):
+    eager time per call over alternating input copies; every product runs on fp32 MFMA, so the
+    compute roofline is the fp32 matrix peak."""
+    import torch
+
+    import kda_gated_delta_rule_amd as kda
+    import kda_workloads as W
+
+    y = W.prefill(seed=0)
+    Tt, H, dk = y["q"].shape
+    dv = y["v"].shape[-1]
+    gen = torch.Generator().manual_seed(1)
+    do = torch.randn(Tt, H, dv, generator=gen).to(torch.bfloat16).to(dev)
+    dht = torch.randn(1, H, dk, dv, generator=gen).to(dev)
+    ins = two_input_copies(y, dev)
+    cu = y["cu_seqlens"].to(dev)
+    ws = torch.empty(kda.chunk_backward_workspace_size(1, Tt, H, dk, dv), dtype=torch.uint8, device=dev)
+
+    def step(i):
+        q, k, v, g, beta = ins[i % 2]
+        kda.chunk_backward(q, k, v, g, beta, cu, do, dht=dht, workspace=ws)
+
+    iters = max(4, args.steps // 20)
+    for i in range(2):
+        step(i)
+    _, per = time_loop(step, iters, torch.cuda.synchronize)
+    th = Tt * H
+    flops = th * backward_flops_per_token_head(dk, dv)
+    byts = th * backward_bytes_per_token_head(dk, dv, 2)
+    tflops = flops / per / 1e12
+    gbs = byts / per / 1e9
+    log("%s backward: %.1f us/call (eager), %.3g tokens/s, %.1f TFLOP/s (%.1f%% of fp32 MFMA), "
+        "%.0f GB/s (%.1f%% HBM)" % (W.PREFILL["name"], per * 1e6, Tt / per, tflops,
+                                    100 * tflops / FP32_PEAK_TFLOPS, gbs, 100 * gbs / HBM_PEAK_GBS))
+    return {"workload": W.PREFILL["name"], "us_per_call": per * 1e6,
+            "timing": "eager, %d calls, two input copies in turn" % iters,
+            "tokens_per_s": Tt / per, "token_heads_per_s": th / per,
+            "algorithmic_flops": flops, "algorithmic_bytes": byts, "achieved_TFLOPs": tflops,
+            "fp32_mfma_frac": tflops / FP32_PEAK_TFLOPS, "achieved_GBs": gbs,
+            "hbm_frac": gbs / HBM_PEAK_GBS,
+            "binding_roofline_frac": max(tflops / FP32_PEAK_TFLOPS, gbs / HBM_PEAK_GBS)}
+
+
 def bench_prefill_snapshots(args, dev, log, plain_us):
     """The T = 8192 x H = 32 prefill with prefix-cache snapshots every 1,024 tokens (8 states
     per head written to extra pool slots); reports the eager time per call and the cost over
@@ -528,6 +598,8 @@ def main():
     ap.add_argument("--verify-only", action="store_true",
                     help="measure only the copy reference and verify + replay (for counter runs); "
                          "prints their figures without the headline metric")
+    ap.add_argument("--backward-only", action="store_true",
+                    help="measure only the chunked backward (for counter and trace runs)")
     ap.add_argument("--quiet", action="store_true")
     args = ap.parse_args()
 
@@ -561,6 +633,10 @@ def main():
         print(json.dumps({"mode": "prefill-only", "extra": extra}))
         return
 
+    if args.backward_only:
+        print(json.dumps({"mode": "backward-only", "extra": {"backward": bench_backward(args, dev, log)}}))
+        return
+
     if args.verify_only:
         extra = {"copy_reference": bench_copy(dev, log),
                  "verify_replay": bench_verify_replay(args, dev, log)}
@@ -578,6 +654,7 @@ def main():
         extra["prefill_varlen"] = bench_prefill(args, dev, log, "varlen")
         extra["prefill_snapshots"] = bench_prefill_snapshots(args, dev, log,
                                                              extra["prefill"]["us_per_call_eager"])
+        extra["backward"] = bench_backward(args, dev, log)
     cpu = None if args.decode_only else cpu_baseline(dec["inputs"], log)
 
     import kda_workloads as W

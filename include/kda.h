@@ -188,6 +188,43 @@ int kda_chunk_prefill_snapshots(const void* q, const void* k, const void* v, int
                                 const int32_t* snap_slots, int max_snaps, hipStream_t stream);
 
 /*
+ * kda_chunk_backward_workspace_size -- bytes of device workspace kda_chunk_backward needs for
+ * these sizes (an upper bound that depends only on the arguments; 0 for invalid arguments).
+ */
+size_t kda_chunk_backward_workspace_size(int num_seqs, int64_t total_tokens, int H, int dk,
+                                         int dv, int dtype);
+
+/*
+ * kda_chunk_backward -- gradients of the varlen chunked prefill, for training (the Kimi K3
+ * day-0 adaptation page, section "基于昇腾实现Kimi K3训练基础功能适配与深度优化": the item on
+ * forward and backward linear-attention kernels; the page gives no backward formula, so this
+ * is the chain rule through the forward defined above).
+ *
+ * For o and the final states ht of kda_chunk_prefill on the same inputs (initial states h0),
+ * returns the gradients of L = sum(dout * o) + sum(dht * ht):
+ *   q, k, v, g, beta, cu_seqlens, num_seqs, total_tokens, H, dk, dv, scale, use_qk_l2norm
+ *               as kda_chunk_prefill (same layouts and dtype)
+ *   h0          [num_seqs, H, dk, dv] fp32 dense initial states, or NULL (zero)
+ *   dout        [total_tokens, H, dv] dtype
+ *   dht         [num_seqs, H, dk, dv] fp32, or NULL (zero)
+ *   dq, dk_out  [total_tokens, H, dk] dtype;  dv_out [total_tokens, H, dv] dtype
+ *   dg          [total_tokens, H, dk] fp32;   dbeta [total_tokens, H] fp32
+ *   dh0         [num_seqs, H, dk, dv] fp32, or NULL (not written)
+ *   workspace   at least kda_chunk_backward_workspace_size(...) bytes; contents on entry do not
+ *               matter
+ * The call runs the forward again (the state entering every 64-token chunk is kept in the
+ * workspace), then the reverse chunk recurrence of the state gradient and the per-chunk input
+ * gradients, all in fp32 arithmetic.  Supported shapes, limits and errors as kda_chunk_prefill
+ * (the same numerical range; fp32 inputs need dk = 64).
+ */
+int kda_chunk_backward(const void* q, const void* k, const void* v, int dtype, const float* g,
+                       const float* beta, const int32_t* cu_seqlens, int num_seqs,
+                       int64_t total_tokens, const float* h0, const void* dout, const float* dht,
+                       int H, int dk, int dv, float scale, int use_qk_l2norm, void* dq,
+                       void* dk_out, void* dv_out, float* dg, float* dbeta, float* dh0,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * kda_chunk_prefill_noalloc -- kda_chunk_prefill without a caller workspace, for callers that
  * cannot allocate device memory: code under HIP graph capture, serving loops that must not
  * allocate, harnesses that forbid hipMalloc.  The call itself allocates nothing.

@@ -7,13 +7,14 @@ the GPU; they provide device memory and the stream, nothing else:
   replay_commit  ReplaySSM commit of accepted update records
   chunk_prefill  varlen 64-token chunked prefill with initial / final states
   chunk_prefill_noalloc  the same on the library's static workspace (no allocation)
+  chunk_backward gradients of the chunked prefill (training)
 
 All arithmetic runs in the HIP kernels of libkda.so.
 """
 from ._lib import KdaError, load, status_string  # noqa: F401
-from .ops import (chunk_prefill, chunk_prefill_noalloc, chunk_prefill_workspace_size,  # noqa: F401
-                  decode_step, replay_commit)
+from .ops import (chunk_backward, chunk_backward_workspace_size, chunk_prefill,  # noqa: F401
+                  chunk_prefill_noalloc, chunk_prefill_workspace_size, decode_step, replay_commit)
 
 __all__ = ["decode_step", "replay_commit", "chunk_prefill", "chunk_prefill_noalloc",
-           "chunk_prefill_workspace_size",
+           "chunk_prefill_workspace_size", "chunk_backward", "chunk_backward_workspace_size",
            "KdaError", "load", "status_string"]

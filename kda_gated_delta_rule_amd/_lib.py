@@ -41,6 +41,10 @@ SIGNATURES = {
     "kda_chunk_prefill_noalloc": (_c_i, [_c_p, _c_p, _c_p, _c_i, _c_p, _c_p, _c_p, _c_i, _c_i64,
                                          _c_p, _c_i64, _c_p, _c_i, _c_i, _c_i, _c_i, _c_f, _c_i,
                                          _c_p, _c_p]),
+    "kda_chunk_backward_workspace_size": (_c_sz, [_c_i, _c_i64, _c_i, _c_i, _c_i, _c_i]),
+    "kda_chunk_backward": (_c_i, [_c_p, _c_p, _c_p, _c_i, _c_p, _c_p, _c_p, _c_i, _c_i64, _c_p, _c_p,
+                                  _c_p, _c_i, _c_i, _c_i, _c_f, _c_i, _c_p, _c_p, _c_p, _c_p, _c_p,
+                                  _c_p, _c_p, _c_sz, _c_p]),
     "kda_status_string": (ctypes.c_char_p, [_c_i]),
 }
 

@@ -176,6 +176,64 @@ KDA_EXPORT int kda_chunk_prefill_snapshots(
                               snap_slots, max_snaps, false, stream);
 }
 
+KDA_EXPORT size_t kda_chunk_backward_workspace_size(int num_seqs, int64_t total_tokens, int H,
+                                                    int dk, int dv, int dtype) {
+    if (num_seqs < 0 || total_tokens < 0 || H < 1 || !supported_dim(dk) || !supported_dim(dv) ||
+        !valid_dtype(dtype))
+        return 0;
+    return kda::backward_workspace_bytes(num_seqs, total_tokens, H, dk, dv, dtype == KDA_BF16);
+}
+
+KDA_EXPORT int kda_chunk_backward(const void* q, const void* k, const void* v, int dtype,
+                                  const float* g, const float* beta, const int32_t* cu_seqlens,
+                                  int num_seqs, int64_t total_tokens, const float* h0,
+                                  const void* dout, const float* dht, int H, int dk, int dv,
+                                  float scale, int use_qk_l2norm, void* dq, void* dk_out,
+                                  void* dv_out, float* dg, float* dbeta, float* dh0,
+                                  void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (!valid_dtype(dtype)) return KDA_ERR_INVALID_ARG;
+    if (num_seqs < 0 || total_tokens < 0 || H < 1) return KDA_ERR_INVALID_ARG;
+    if (num_seqs == 0 && total_tokens != 0) return KDA_ERR_INVALID_ARG;
+    if (!isfinite(scale)) return KDA_ERR_INVALID_ARG;
+    if (use_qk_l2norm != 0 && use_qk_l2norm != 1) return KDA_ERR_INVALID_ARG;
+    if (!supported_dim(dk) || !supported_dim(dv)) return KDA_ERR_UNSUPPORTED;
+    if (!kda::prefill_supported(dtype == KDA_BF16, dk, dv)) return KDA_ERR_UNSUPPORTED;
+    if (total_tokens > (1ll << 31) - 1) return KDA_ERR_INVALID_ARG;
+    if (H > 65535) return KDA_ERR_INVALID_ARG;
+    if (checked_mul(total_tokens / 64 + num_seqs, H) > (1ll << 22)) return KDA_ERR_INVALID_ARG;
+    if (checked_mul(checked_mul(total_tokens, H), 2 * dk + dv) < 0) return KDA_ERR_INVALID_ARG;
+    if (checked_mul(checked_mul(num_seqs, H), static_cast<int64_t>(dk) * dv) < 0)
+        return KDA_ERR_INVALID_ARG;
+    if (num_seqs == 0) return KDA_OK;
+    if (!cu_seqlens || !aligned16(cu_seqlens)) return KDA_ERR_INVALID_ARG;
+    const void* opt[] = {h0, dht, dh0};
+    for (const void* p : opt)
+        if (p && !aligned16(p)) return KDA_ERR_INVALID_ARG;
+    if (total_tokens > 0) {
+        const void* tp[] = {q, k, v, g, beta, dout, dq, dk_out, dv_out, dg, dbeta};
+        for (const void* p : tp)
+            if (!p || !aligned16(p)) return KDA_ERR_INVALID_ARG;
+    }
+    const size_t need =
+        kda::backward_workspace_bytes(num_seqs, total_tokens, H, dk, dv, dtype == KDA_BF16);
+    if (!workspace || !aligned16(workspace) || workspace_bytes < need) return KDA_ERR_WORKSPACE;
+
+    kda::BackwardArgs b{};
+    b.fwd = kda::PrefillArgs{q, k, v, g, beta, cu_seqlens, num_seqs, total_tokens, nullptr,
+                             nullptr, 1, H, scale, use_qk_l2norm, nullptr, workspace};
+    b.h0 = h0;
+    b.dout = dout;
+    b.dht = dht;
+    b.dq = dq;
+    b.dk = dk_out;
+    b.dv = dv_out;
+    b.dg = dg;
+    b.dbeta = dbeta;
+    b.dh0 = dh0;
+    kda::backward_setup(b, dk, dv, dtype == KDA_BF16);
+    return to_status(kda::launch_backward(b, dtype == KDA_BF16, dk, dv, stream));
+}
+
 KDA_EXPORT const char* kda_status_string(int status) {
     switch (status) {
         case KDA_OK: return "KDA_OK";

@@ -1,0 +1,900 @@
+// kda_backward.hip -- chunked backward of the KDA recurrence for gfx950 (training).
+//
+// The Kimi K3 day-0 adaptation page names forward and backward linear-attention kernels for
+// training (section "基于昇腾实现Kimi K3训练基础功能适配与深度优化", the Triton-Ascend item) but
+// prints no formula.  The gradients here are the chain rule through the 64-token chunk form of
+// the forward (the chunk algebra of kda_prefill.hip), for a chunk entering with state S:
+//
+//   forward  A = beta (.) Ag,  Ag_ts = sum_c kh_tc kh_sc e^(G_tc - G_sc)  (s < t)
+//            P_ts = sum_c qh_tc kh_sc e^(G_tc - G_sc)  (s <= t),  T = (I + A)^-1
+//            BK = beta kh e^G,  BV = beta v,  W = T BK,  Ut = T BV,  U = Ut - W S
+//            O = scale (QG S + P U),  QG = qh e^G;  S' = e^(G_L) S + Kt^T U,  Kt = kh e^(G_L - G)
+//   backward (dH = dL/dS', dO = dL/dO)
+//            dU = scale P^T dO + Kt dH;  dS = e^(G_L) dH - W^T dU + scale QG^T dO
+//                                          = Mt dH + b,  Mt = e^(G_L) - W^T Kt,  b = scale (QG - P W)^T dO
+//            dQG = scale dO S^T,  dP = scale dO U^T (s <= t),  dW = -dU S^T,  dKt = U dH^T
+//            dT = dW BK^T + dU BV^T,  dBK = T^T dW,  dBV = T^T dU,  dA = -(T^T dT T^T) (s < t)
+//            dv = beta dBV,  dbeta = sum(v dBV) + sum(kh e^G dBK) + sum_s dA Ag,  dAg = beta dA
+//            dkh = beta e^G dBK + e^(G_L - G) dKt + X1 + X2 + X3,   dqh = e^G dQG + X4
+//              X1_t = sum_s dAg_ts kh_s e^(G_t - G_s),  X2_s = sum_t dAg_ts kh_t e^(G_t - G_s)
+//              X3_s = sum_t dP_ts qh_t e^(G_t - G_s),   X4_t = sum_s dP_ts kh_s e^(G_t - G_s)
+//            dG = QG dQG + BK dBK - Kt dKt + kh X1 - kh X2 + qh X4 - kh X3   (per token, channel)
+//            dG_L = e^(G_L) sum_j S dH + sum_t Kt dKt;  dg_t = sum_(t' >= t) dG_t' + dG_L
+//            dq = (dqh - qh (qh . dqh)) / |q|,  dk likewise (identity without the L2 norm)
+//
+// Launches on the caller's stream (all arithmetic fp32; bf16 inputs are widened):
+//   0. bwd_init        identity slot map and the initial states for the forward pass
+//   1. the forward prefill (kda_prefill.hip) with its carry storing every chunk's entering state
+//   2. bwd_intra       per (chunk, head): Ag, P, T (forward substitution), W, Ut, exp(G_L)
+//   3. bwd_prep        per (chunk, head): Mt and b of the reverse state recurrence
+//   4. bwd_scan        per (sequence, head, 16 columns): dS_c = Mt_c dS_(c+1) + b_c from the
+//                      last chunk back, keeping each chunk's exit-state gradient; dh0
+//   5. bwd_state       per (chunk, head): the products with S and dH (U, dU, dQG, dW, dKt, dP,
+//                      the e^(G_L) part of dG_L), over 32-column blocks of the state
+//   6. bwd_ut          per (chunk, head): dT, dBK, dBV, dA; writes dv and dbeta
+//   7. bwd_final       per (chunk, head): X1..X4, dkh, dqh, dG, the reverse cumsum and the
+//                      norm backward; writes dq, dk and dg
+// Every e^(G_t - G_s) is split at a reference inside its 16-token block pair, as in the
+// forward: off-diagonal block pairs at a block end (both factors at most 1), diagonal blocks
+// at the block's 8th token.
+#include "kda.h"
+#include "kda_device.hpp"
+#include "kda_internal.hpp"
+#include "kda_layout.hpp"
+
+namespace kda {
+
+namespace {
+
+constexpr int kC = 64;
+constexpr int kT = 256;  // threads of every per-chunk kernel (4 waves)
+constexpr float kL2e = 1.4426950408889634f;
+constexpr float kEps = 1e-6f;
+
+__host__ __device__ constexpr size_t al256(size_t x) { return (x + 255) / 256 * 256; }
+
+// ---------------------------------------------------------------------------
+// Workspace: the forward prefill's workspace first (its chunk table is read here), then
+//   pool [ns][H][dk][dv] f32, slots [ns] i32, o_fwd [T][H][dv] (input dtype),
+//   per (chunk, head) item (fp32, row-major):
+//     S [dk][dv]   state entering the chunk (forward carry)
+//     dX [dk][dv]  gradient of the chunk's exit state (scan)
+//     Mt [dk][dk], b [dk][dv]
+//     T, Ag, P [64][64];  W [64][dk], Ut [64][dv];  gl [dk] = e^(G_L)
+//     dU [64][dv], dQG, dW, dKt [64][dk], dP [64][64], dgl [dk];  dBK [64][dk], dAg [64][64]
+// ---------------------------------------------------------------------------
+struct BwLayout {
+    size_t fwd, off_pool, off_slots, off_o, off_items, item, total;
+    size_t S, dX, Mt, b, T, Ag, P, W, Ut, gl, dU, dQG, dW, dKt, dP, dgl, dBK, dAg;
+    int64_t max_items;
+    __host__ __device__ BwLayout(int ns, int64_t T_tot, int H, int dk, int dv, int e) {
+        fwd = al256(WsLayout(ns, T_tot, H, dk, dv, e).total);
+        off_pool = fwd;
+        off_slots = off_pool + al256(sizeof(float) * ns * H * dk * dv);
+        off_o = off_slots + al256(sizeof(int32_t) * ns);
+        off_items = off_o + al256(static_cast<size_t>(T_tot) * H * dv * e);
+        size_t o = 0;
+        auto take = [&](size_t n) {
+            const size_t at = o;
+            o += al256(sizeof(float) * n);
+            return at;
+        };
+        S = take(dk * dv), dX = take(dk * dv), Mt = take(dk * dk), b = take(dk * dv);
+        T = take(kC * kC), Ag = take(kC * kC), P = take(kC * kC), W = take(kC * dk), Ut = take(kC * dv);
+        gl = take(dk), dU = take(kC * dv), dQG = take(kC * dk), dW = take(kC * dk), dKt = take(kC * dk);
+        dP = take(kC * kC), dgl = take(dk), dBK = take(kC * dk), dAg = take(kC * kC);
+        item = o;
+        max_items = (T_tot / kC + ns) * H;
+        total = off_items + item * static_cast<size_t>(max_items);
+    }
+};
+
+// The forward's chunk offsets (at 0 of its workspace) and chunk table (kda_layout.hpp).
+struct FwdTables {
+    const int32_t* chunk_off;
+    const int4* table;
+};
+
+// fp32 MFMA 16x16 tile: C(m, n) += sum_k A(m, k) B(k, n), k in [0, K) (K a multiple of 4);
+// A(m, k) = A[m * am + k * ak], B(k, n) = B[k * bk + n * bn].  Lane l holds C(4 (l / 16) + i,
+// l % 16), i = 0..3.
+__device__ __forceinline__ f32x4 mm16(const float* A, int am, int ak, const float* B, int bk, int bn, int K,
+                                      int lane, f32x4 c) {
+    const int r = lane & 15, q = lane >> 4;
+    for (int k0 = 0; k0 < K; k0 += 4)
+        c = __builtin_amdgcn_mfma_f32_16x16x4f32(A[r * am + (k0 + q) * ak], B[(k0 + q) * bk + r * bn], c, 0, 0, 0);
+    return c;
+}
+
+template <class TIn>
+__device__ __forceinline__ float ld_in(const void* p, int64_t i) {
+    return load1<TIn>(p, i);
+}
+__device__ __forceinline__ void st_out(void* p, int64_t i, float x, F32) { static_cast<float*>(p)[i] = x; }
+__device__ __forceinline__ void st_out(void* p, int64_t i, float x, BF16) {
+    static_cast<uint16_t*>(p)[i] = f32_to_bf16(x);
+}
+
+struct Item {
+    int seq, t0, L, h, chunk;
+};
+
+__device__ __forceinline__ bool item_of(const PrefillArgs& a, const char* ws, const FwdTables& ft, int item,
+                                        Item& it) {
+    const int nch = ft.chunk_off[a.num_seqs];
+    if (item >= nch * a.H) return false;
+    it.chunk = item / a.H;
+    it.h = item % a.H;
+    const int4 e = ft.table[it.chunk];
+    it.seq = e.x;
+    it.t0 = e.y;
+    it.L = e.z;
+    return true;
+}
+
+// Rows t0 .. t0 + L - 1 of head h of a [T][H][D] input into LDS dst [64][ld] (fp32, rows from
+// L on are zero).
+template <class TIn>
+__device__ void load_rows(const void* src, int D, float* dst, int ld, const Item& it, int H) {
+    for (int i = threadIdx.x; i < kC * D; i += kT) {
+        const int t = i / D, c = i % D;
+        dst[t * ld + c] = t < it.L ? ld_in<TIn>(src, (static_cast<int64_t>(it.t0 + t) * H + it.h) * D + c) : 0.f;
+    }
+}
+
+// In place x_t <- x_t / sqrt(|x_t|^2 + eps) (when use_l2); inv[t] gets the factor.
+__device__ void normalize_rows(float* x, int ld, int D, float* inv, int use_l2) {
+    if (threadIdx.x < kC) {
+        const int t = threadIdx.x;
+        float s = 0.f;
+        for (int c = 0; c < D; ++c) s = fmaf(x[t * ld + c], x[t * ld + c], s);
+        inv[t] = use_l2 ? 1.f / sqrtf(s + kEps) : 1.f;
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < kC * D; i += kT) x[(i / D) * ld + i % D] *= inv[i / D];
+    __syncthreads();
+}
+
+// G [64][ld] = in-chunk inclusive cumsum of g, in log2 units (rows from L on repeat G_L).
+// The chunk's gates are first copied into G by all threads (coalesced), then one thread per
+// channel scans its column in LDS.  The caller synchronises before reading G.
+__device__ void gate_cumsum(const float* g, float* G, int ld, int DK, const Item& it, int H) {
+    for (int i = threadIdx.x; i < kC * DK; i += kT) {
+        const int t = i / DK, c = i % DK;
+        G[t * ld + c] = t < it.L ? g[(static_cast<int64_t>(it.t0 + t) * H + it.h) * DK + c] * kL2e : 0.f;
+    }
+    __syncthreads();
+    if (threadIdx.x < DK) {
+        const int c = threadIdx.x;
+        float x = 0.f;
+        for (int t = 0; t < kC; ++t) {
+            x += G[t * ld + c];
+            G[t * ld + c] = x;
+        }
+    }
+}
+
+__device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Decayed Gram tile (t block i, s block j <= i): C(t, s) = sum_c X_tc Y_sc 2^(G_tc - G_sc), the
+// factor split at row R = 16 i - 1 (j < i) or 16 i + 7 (j = i).  Lane holds (t = 16 i + 4q + ii,
+// s = 16 j + r).
+__device__ f32x4 dgram_tile(const float* X, const float* Y, const float* G, int ld, int DK, int i, int j, int lane) {
+    const int r = lane & 15, q = lane >> 4;
+    const int R = j < i ? 16 * i - 1 : 16 * i + 7;
+    f32x4 c = {0.f, 0.f, 0.f, 0.f};
+    for (int k0 = 0; k0 < DK; k0 += 4) {
+        const int ch = k0 + q;
+        const float ref = G[R * ld + ch];
+        const float av = X[(16 * i + r) * ld + ch] * ex2(G[(16 * i + r) * ld + ch] - ref);
+        const float bv = Y[(16 * j + r) * ld + ch] * ex2(ref - G[(16 * j + r) * ld + ch]);
+        c = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, c, 0, 0, 0);
+    }
+    return c;
+}
+
+// Decayed token products over a 16 x 16 (rows, channels) output tile.
+//  t mode: Y(t, c) = sum_(s <= t) X(t, s) Z(s, c) 2^(G_tc - G_sc), t in block i
+//  s mode: Y(s, c) = sum_(t >= s) X(t, s) Z(t, c) 2^(G_tc - G_sc), s in block i
+// X [64][ldx] is stored lower triangular (zero above the diagonal).  Block pairs off the
+// diagonal split the factor at a block end (t mode: the end of block i - 1; s mode: the end
+// of block i), the diagonal block at its 8th token.  Lane holds (row 16 i + 4q + ii, channel
+// 16 cb + r).
+template <bool TMODE>
+__device__ f32x4 dtok_tile(const float* X, int ldx, const float* Z, const float* G, int ld, int i, int cb, int lane) {
+    const int r = lane & 15, q = lane >> 4, ch = 16 * cb + r;
+    const int Roff = TMODE ? 16 * i - 1 : 16 * i + 15, M = 16 * i + 7;
+    f32x4 off = {0.f, 0.f, 0.f, 0.f}, dg = off;
+    // off-diagonal blocks: t mode the s blocks before i, s mode the t blocks after i
+    const int kb = TMODE ? 0 : 16 * (i + 1), ke = TMODE ? 16 * i : kC;
+    if (ke > kb) {
+        const float ref = G[Roff * ld + ch];
+        for (int k0 = kb; k0 < ke; k0 += 4) {
+            const int k = k0 + q;  // s (t mode) or t (s mode)
+            const float av = TMODE ? X[(16 * i + r) * ldx + k] : X[k * ldx + 16 * i + r];
+            const float zf = TMODE ? ex2(ref - G[k * ld + ch]) : ex2(G[k * ld + ch] - ref);
+            off = __builtin_amdgcn_mfma_f32_16x16x4f32(av, Z[k * ld + ch] * zf, off, 0, 0, 0);
+        }
+    }
+    {
+        const float ref = G[M * ld + ch];
+        for (int k0 = 16 * i; k0 < 16 * i + 16; k0 += 4) {
+            const int k = k0 + q;
+            const float av = TMODE ? X[(16 * i + r) * ldx + k] : X[k * ldx + 16 * i + r];
+            const float zf = TMODE ? ex2(ref - G[k * ld + ch]) : ex2(G[k * ld + ch] - ref);
+            dg = __builtin_amdgcn_mfma_f32_16x16x4f32(av, Z[k * ld + ch] * zf, dg, 0, 0, 0);
+        }
+    }
+    f32x4 y;
+    const float ro = ke > kb ? G[Roff * ld + ch] : 0.f, rm = G[M * ld + ch];
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) {
+        const float gr = G[(16 * i + 4 * q + ii) * ld + ch];
+        const float fo = ke > kb ? (TMODE ? ex2(gr - ro) : ex2(ro - gr)) : 0.f;
+        const float fm = TMODE ? ex2(gr - rm) : ex2(rm - gr);
+        y[ii] = off[ii] * fo + dg[ii] * fm;
+    }
+    return y;
+}
+
+// Stores a 16 x 16 accumulator tile (rows 16 rb + 4q + ii, columns 16 cb + r) to a row-major
+// fp32 matrix of leading dimension ld.
+__device__ __forceinline__ void put_tile(float* M, int ld, int rb, int cb, f32x4 v, int lane) {
+    const int r = lane & 15, q = lane >> 4;
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) M[(16 * rb + 4 * q + ii) * ld + 16 * cb + r] = v[ii];
+}
+__device__ __forceinline__ f32x4 get_tile(const float* M, int ld, int rb, int cb, int lane) {
+    const int r = lane & 15, q = lane >> 4;
+    f32x4 v;
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) v[ii] = M[(16 * rb + 4 * q + ii) * ld + 16 * cb + r];
+    return v;
+}
+
+// T = (I + A)^-1 for A = diag(beta) Ag (Ag [64][68] strictly lower, fp32), into T [64][68],
+// by 16 x 16 blocks: wave w inverts diagonal block w by forward substitution (one lane per
+// column, the block's rows read as vectors, the column in registers); then for d = 1, 2, 3
+// the waves w >= d form T_(w, w-d) = -T_ww sum_(k = w-d .. w-1) A_wk T_(k, w-d) on fp32 MFMA.
+// Y is a per-wave 16 x 20 scratch.  Ends with a barrier.
+__device__ void unit_lower_inverse(const float* Ag, const float* beta, float* T, float* Y, int lane, int wave) {
+    constexpr int LC = kC + 4, LY = 20;
+    const int r = lane & 15, q = lane >> 4;
+    // zero the blocks above the diagonal of this wave's rows
+    for (int i = lane; i < 16 * kC; i += 64) {
+        const int row = 16 * wave + i / kC, c = i % kC;
+        if (c >= 16 * (wave + 1)) T[row * LC + c] = 0.f;
+    }
+    {
+        const int col = r, b0 = 16 * wave;
+        float x[16];
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) {
+            const float bt = beta[b0 + rr];
+            f32x4 row[4];
+#pragma unroll
+            for (int m = 0; m < 4; ++m) row[m] = *reinterpret_cast<const f32x4*>(Ag + (b0 + rr) * LC + b0 + 4 * m);
+            float acc = rr == col ? 1.f : 0.f;
+#pragma unroll
+            for (int s = 0; s < rr; ++s) acc = fmaf(-bt * row[s >> 2][s & 3], x[s], acc);
+            x[rr] = acc;
+        }
+        if (q == 0) {
+#pragma unroll
+            for (int rr = 0; rr < 16; ++rr) T[(b0 + rr) * LC + b0 + col] = x[rr];
+        }
+    }
+    __syncthreads();
+    float* y = Y + wave * 16 * LY;
+    for (int d = 1; d < 4; ++d) {
+        if (wave >= d) {
+            const int jb = wave - d;
+            // y = A_(wave, jb .. wave-1) T_(jb .. wave-1, jb): k over 16 d rows of T
+            f32x4 acc = mm16(Ag + 16 * wave * LC + 16 * jb, LC, 1, T + 16 * jb * LC + 16 * jb, LC, 1, 16 * d, lane,
+                             f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) acc[ii] *= beta[16 * wave + 4 * q + ii];
+            put_tile(y, LY, 0, 0, acc, lane);
+            // z = T_(wave, wave) y (this wave's own scratch, so no workgroup barrier is needed)
+            const f32x4 z = mm16(T + 16 * wave * LC + 16 * wave, LC, 1, y, LY, 1, 16, lane, f32x4{0.f, 0.f, 0.f, 0.f});
+            put_tile(T + 16 * wave * LC + 16 * jb, LC, 0, 0, -z, lane);
+        }
+        __syncthreads();
+    }
+}
+
+// Global <-> LDS copies of a row-major fp32 [rows][cols] matrix.
+__device__ void g2s(const float* g, int gld, float* s, int sld, int rows, int cols) {
+    for (int i = threadIdx.x; i < rows * cols; i += kT) s[(i / cols) * sld + i % cols] = g[(i / cols) * gld + i % cols];
+}
+__device__ void s2g(const float* s, int sld, float* g, int gld, int rows, int cols) {
+    for (int i = threadIdx.x; i < rows * cols; i += kT) g[(i / cols) * gld + i % cols] = s[(i / cols) * sld + i % cols];
+}
+
+struct BwCtx {
+    BwLayout bw;
+    FwdTables ft;
+    char* items;
+    __device__ BwCtx(const PrefillArgs& a, int dk, int dv, int e)
+        : bw(a.num_seqs, a.total_tokens, a.H, dk, dv, e) {
+        const char* base = static_cast<const char*>(a.workspace);
+        ft.chunk_off = reinterpret_cast<const int32_t*>(base);
+        ft.table = reinterpret_cast<const int4*>(base + WsLayout(a.num_seqs, a.total_tokens, a.H, dk, dv, e).off_table);
+        items = static_cast<char*>(a.workspace) + bw.off_items;
+    }
+    __device__ float* blk(int item, size_t off) const {
+        return reinterpret_cast<float*>(items + bw.item * static_cast<size_t>(item) + off);
+    }
+};
+
+// ---------------------------------------------------------------------------
+// 0. initial states and the identity slot map for the forward pass
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kT) void bwd_init_kernel(BackwardArgs b, int dk, int dv, int e) {
+    const BwLayout bw(b.fwd.num_seqs, b.fwd.total_tokens, b.fwd.H, dk, dv, e);
+    char* base = static_cast<char*>(b.fwd.workspace);
+    float* pool = reinterpret_cast<float*>(base + bw.off_pool);
+    int32_t* slots = reinterpret_cast<int32_t*>(base + bw.off_slots);
+    const int64_t n = static_cast<int64_t>(b.fwd.num_seqs) * b.fwd.H * dk * dv;
+    for (int64_t i = blockIdx.x * static_cast<int64_t>(kT) + threadIdx.x; i < n; i += static_cast<int64_t>(gridDim.x) * kT)
+        pool[i] = b.h0 ? b.h0[i] : 0.f;
+    for (int64_t i = blockIdx.x * static_cast<int64_t>(kT) + threadIdx.x; i < b.fwd.num_seqs;
+         i += static_cast<int64_t>(gridDim.x) * kT)
+        slots[i] = static_cast<int32_t>(i);
+}
+
+// ---------------------------------------------------------------------------
+// 2. bwd_intra: Ag, P, T, W, Ut, exp(G_L) of one (chunk, head)
+// ---------------------------------------------------------------------------
+template <int DK, int DV, class TIn>
+__global__ __launch_bounds__(kT) void bwd_intra_kernel(BackwardArgs b) {
+    const PrefillArgs& a = b.fwd;
+    constexpr int LK = DK + 4, LV = DV + 4, LC = kC + 4, LM = LK > LV ? LK : LV;
+    __shared__ float sK[kC * LM], sQ[kC * LK], sG[kC * LK], sA[kC * LC], sT[kC * LC], sY[4 * 16 * 20], inv[kC],
+        sB[kC];
+    const BwCtx X(a, DK, DV, TIn::bytes);
+    Item it;
+    if (!item_of(a, static_cast<const char*>(a.workspace), X.ft, blockIdx.x, it)) return;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, H = a.H;
+    const int item = blockIdx.x;
+    load_rows<TIn>(a.k, DK, sK, LK, it, H);
+    load_rows<TIn>(a.q, DK, sQ, LK, it, H);
+    gate_cumsum(a.g, sG, LK, DK, it, H);
+    if (threadIdx.x < kC) sB[threadIdx.x] = threadIdx.x < it.L ? a.beta[static_cast<int64_t>(it.t0 + threadIdx.x) * H + it.h] : 0.f;
+    __syncthreads();
+    normalize_rows(sK, LK, DK, inv, a.use_l2);
+    normalize_rows(sQ, LK, DK, inv, a.use_l2);
+    // Ag (strictly lower) and P (lower with the diagonal), tile (i, j <= i) by the wave owning
+    // block i's rows; upper tiles are zero
+    float* Pg = X.blk(item, X.bw.P);
+    float* Ag = X.blk(item, X.bw.Ag);
+    for (int j = 0; j < 4; ++j) {
+        const int i = wave;
+        // tiles above the diagonal (j > i) are computed too (straight-line) and discarded by
+        // the masks below
+        f32x4 ta = dgram_tile(sK, sK, sG, LK, DK, i, j < i ? j : i, lane);
+        f32x4 tp = dgram_tile(sQ, sK, sG, LK, DK, i, j < i ? j : i, lane);
+        const int r = lane & 15, q = lane >> 4;
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+            const int t = 16 * i + 4 * q + ii, s = 16 * j + r;
+            ta[ii] = j <= i && s < t ? ta[ii] : 0.f;
+            tp[ii] = j <= i && s <= t ? tp[ii] : 0.f;
+        }
+        put_tile(sA, LC, i, j, ta, lane);
+        put_tile(Pg, kC, i, j, tp, lane);
+        put_tile(Ag, kC, i, j, ta, lane);
+    }
+    __syncthreads();
+    unit_lower_inverse(sA, sB, sT, sY, lane, wave);
+    s2g(sT, LC, X.blk(item, X.bw.T), kC, kC, kC);
+    // BK = beta kh 2^G into sQ (P is done), then W = T BK
+    for (int i = threadIdx.x; i < kC * DK; i += kT) {
+        const int t = i / DK, c = i % DK;
+        sQ[t * LK + c] = sB[t] * sK[t * LK + c] * ex2(sG[t * LK + c]);
+    }
+    if (threadIdx.x < DK) X.blk(item, X.bw.gl)[threadIdx.x] = ex2(sG[(kC - 1) * LK + threadIdx.x]);
+    __syncthreads();
+    float* Wg = X.blk(item, X.bw.W);
+    for (int cb = 0; cb < DK / 16; ++cb) {
+        const f32x4 w = mm16(sT + 16 * wave * LC, LC, 1, sQ + 16 * cb, LK, 1, kC, lane, f32x4{0.f, 0.f, 0.f, 0.f});
+        put_tile(Wg, DK, wave, cb, w, lane);
+    }
+    __syncthreads();
+    // BV = beta v into sK, then Ut = T BV
+    load_rows<TIn>(a.v, DV, sK, LV, it, H);
+    __syncthreads();
+    for (int i = threadIdx.x; i < kC * DV; i += kT) sK[(i / DV) * LV + i % DV] *= sB[i / DV];
+    __syncthreads();
+    float* Ug = X.blk(item, X.bw.Ut);
+    for (int cb = 0; cb < DV / 16; ++cb) {
+        const f32x4 u = mm16(sT + 16 * wave * LC, LC, 1, sK + 16 * cb, LV, 1, kC, lane, f32x4{0.f, 0.f, 0.f, 0.f});
+        put_tile(Ug, DV, wave, cb, u, lane);
+    }
+}
+
+// Kt = kh 2^(G_L - G) and QG = qh 2^G in place (the raw normalised rows on entry).
+__device__ void to_kt(float* K, const float* G, int ld, int DK) {
+    for (int i = threadIdx.x; i < kC * DK; i += kT) {
+        const int t = i / DK, c = i % DK;
+        K[t * ld + c] *= ex2(G[(kC - 1) * ld + c] - G[t * ld + c]);
+    }
+}
+__device__ void to_qg(float* Q, const float* G, int ld, int DK) {
+    for (int i = threadIdx.x; i < kC * DK; i += kT) {
+        const int t = i / DK, c = i % DK;
+        Q[t * ld + c] *= ex2(G[t * ld + c]);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// 3. bwd_prep: Mt = diag(e^(G_L)) - W^T Kt,  b = scale (QG - P W)^T dO
+// ---------------------------------------------------------------------------
+template <int DK, int DV, class TIn>
+__global__ __launch_bounds__(kT) void bwd_prep_kernel(BackwardArgs b) {
+    const PrefillArgs& a = b.fwd;
+    constexpr int LK = DK + 4, LV = DV + 4, LC = kC + 4;
+    __shared__ float sK[kC * LK], sQ[kC * LK], sW[kC * LK], sO[kC * LV], sP[kC * LC], inv[kC];
+    float* sG = sW;  // the gate cumsum lives where W goes once Kt and QG are formed
+    const BwCtx X(a, DK, DV, TIn::bytes);
+    Item it;
+    if (!item_of(a, static_cast<const char*>(a.workspace), X.ft, blockIdx.x, it)) return;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, H = a.H, item = blockIdx.x;
+    load_rows<TIn>(a.k, DK, sK, LK, it, H);
+    load_rows<TIn>(a.q, DK, sQ, LK, it, H);
+    load_rows<TIn>(b.dout, DV, sO, LV, it, H);
+    gate_cumsum(a.g, sG, LK, DK, it, H);
+    g2s(X.blk(item, X.bw.P), kC, sP, LC, kC, kC);
+    __syncthreads();
+    normalize_rows(sK, LK, DK, inv, a.use_l2);
+    normalize_rows(sQ, LK, DK, inv, a.use_l2);
+    to_kt(sK, sG, LK, DK);
+    to_qg(sQ, sG, LK, DK);
+    __syncthreads();
+    g2s(X.blk(item, X.bw.W), DK, sW, LK, kC, DK);
+    const float* gl = X.blk(item, X.bw.gl);
+    __syncthreads();
+    // Mt (dk x dk): tile (rb, cb), rows c = W's columns, k over tokens
+    float* Mt = X.blk(item, X.bw.Mt);
+    for (int tI = wave; tI < (DK / 16) * (DK / 16); tI += 4) {
+        const int rb = tI / (DK / 16), cb = tI % (DK / 16);
+        f32x4 m = mm16(sW + 16 * rb, 1, LK, sK + 16 * cb, LK, 1, kC, lane, f32x4{0.f, 0.f, 0.f, 0.f});
+        const int r = lane & 15, q = lane >> 4;
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+            const int row = 16 * rb + 4 * q + ii, col = 16 * cb + r;
+            m[ii] = (row == col ? gl[row] : 0.f) - m[ii];
+        }
+        put_tile(Mt, DK, rb, cb, m, lane);
+    }
+    // Q' = QG - P W (wave: its token block, all channel tiles), in place over QG
+    __syncthreads();
+    f32x4 qp[DK / 16];
+    for (int cb = 0; cb < DK / 16; ++cb)
+        qp[cb] = mm16(sP + 16 * wave * LC, LC, 1, sW + 16 * cb, LK, 1, kC, lane, f32x4{0.f, 0.f, 0.f, 0.f});
+    __syncthreads();
+    for (int cb = 0; cb < DK / 16; ++cb) put_tile(sQ, LK, wave, cb, get_tile(sQ, LK, wave, cb, lane) - qp[cb], lane);
+    __syncthreads();
+    // b = scale Q'^T dO (dk x dv)
+    float* bb = X.blk(item, X.bw.b);
+    for (int tI = wave; tI < (DK / 16) * (DV / 16); tI += 4) {
+        const int rb = tI / (DV / 16), cb = tI % (DV / 16);
+        const f32x4 v = mm16(sQ + 16 * rb, 1, LK, sO + 16 * cb, LV, 1, kC, lane, f32x4{0.f, 0.f, 0.f, 0.f});
+        put_tile(bb, DV, rb, cb, v * a.scale, lane);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// 4. bwd_scan: per (sequence, head, 16-column tile), from the last chunk back:
+//    dX_c = X (the gradient of chunk c's exit state), X <- Mt_c X + b_c; dh0 = X.
+//    DK / 16 waves, wave w owns rows 16 w .. 16 w + 15.
+// ---------------------------------------------------------------------------
+template <int DK, int DV>
+__global__ __launch_bounds__(64 * (DK / 16)) void bwd_scan_kernel(BackwardArgs b, int e) {
+    const PrefillArgs& a = b.fwd;
+    constexpr int NTS = DV / 16, LX = DK + 4;
+    __shared__ float xs[16 * LX];  // X^T [16 columns][DK]
+    const BwCtx X(a, DK, DV, e);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int r = lane & 15, q4 = 4 * (lane >> 4);
+    const int H = a.H, grp = blockIdx.x / NTS, tile = blockIdx.x % NTS;
+    const int seq = grp / H, h = grp % H;
+    if (seq >= a.num_seqs) return;
+    const int c0 = X.ft.chunk_off[seq], nch = X.ft.chunk_off[seq + 1] - c0;
+    const int col = 16 * tile + r;
+    const size_t SZ = static_cast<size_t>(DK) * DV;
+    f32x4 x;
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr)
+        x[rr] = b.dht ? b.dht[(static_cast<size_t>(seq) * H + h) * SZ + (16 * wave + q4 + rr) * DV + col] : 0.f;
+    for (int c = nch - 1; c >= 0; --c) {
+        const int item = (c0 + c) * H + h;
+        float* dX = X.blk(item, X.bw.dX);
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) dX[(16 * wave + q4 + rr) * DV + col] = x[rr];
+        const float* Mt = X.blk(item, X.bw.Mt);
+        const float* bb = X.blk(item, X.bw.b);
+        f32x4 acc;
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) acc[rr] = bb[(16 * wave + q4 + rr) * DV + col];
+        *reinterpret_cast<f32x4*>(xs + r * LX + 16 * wave + q4) = x;
+        __syncthreads();
+        // lane (r, q) supplies k = 16 kb + 4q + ks of Mt row 16 wave + r and of X column r
+        for (int kb = 0; kb < DK / 16; ++kb) {
+            const f32x4 mt = *reinterpret_cast<const f32x4*>(Mt + (16 * wave + r) * DK + 16 * kb + q4);
+            const f32x4 xb = *reinterpret_cast<const f32x4*>(xs + r * LX + 16 * kb + q4);
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(mt[ks], xb[ks], acc, 0, 0, 0);
+        }
+        __syncthreads();
+        x = acc;
+    }
+    if (b.dh0) {
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr)
+            b.dh0[(static_cast<size_t>(seq) * H + h) * SZ + (16 * wave + q4 + rr) * DV + col] = x[rr];
+    }
+}
+
+// ---------------------------------------------------------------------------
+// 5. bwd_state: U = Ut - W S, dU = scale P^T dO + Kt dX; dQG = scale dO S^T, dW = -dU S^T,
+//    dKt = U dX^T, dP = scale dO U^T (s <= t); dgl = e^(G_L) sum_j S dX.  Over 32-column
+//    blocks of S and dX; wave w owns token block w of every output.
+// ---------------------------------------------------------------------------
+constexpr int kVB = 32;
+template <int DK, int DV, class TIn>
+__global__ __launch_bounds__(kT) void bwd_state_kernel(BackwardArgs b) {
+    const PrefillArgs& a = b.fwd;
+    constexpr int LK = DK + 4, LC = kC + 4, LB = kVB + 4;
+    constexpr int NKB = DK / 16;
+    __shared__ float sW[kC * LK], sK[kC * LK], sP[kC * LC], sS[DK * LB], sX[DK * LB], sO[kC * LB],
+        sU[kC * LB], sdU[kC * LB], inv[kC], sgl[DK];
+    float* sG = sW;
+    const BwCtx X(a, DK, DV, TIn::bytes);
+    Item it;
+    if (!item_of(a, static_cast<const char*>(a.workspace), X.ft, blockIdx.x, it)) return;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, H = a.H, item = blockIdx.x;
+    const int r = lane & 15, q = lane >> 4;
+    load_rows<TIn>(a.k, DK, sK, LK, it, H);
+    gate_cumsum(a.g, sG, LK, DK, it, H);
+    g2s(X.blk(item, X.bw.P), kC, sP, LC, kC, kC);
+    __syncthreads();
+    normalize_rows(sK, LK, DK, inv, a.use_l2);
+    to_kt(sK, sG, LK, DK);
+    __syncthreads();
+    g2s(X.blk(item, X.bw.W), DK, sW, LK, kC, DK);
+    if (threadIdx.x < DK) sgl[threadIdx.x] = 0.f;
+    const float* S = X.blk(item, X.bw.S);
+    const float* dX = X.blk(item, X.bw.dX);
+    const float* Ut = X.blk(item, X.bw.Ut);
+    float* dUg = X.blk(item, X.bw.dU);
+    f32x4 dqg[NKB], dw[NKB], dkt[NKB], dp[4];
+    for (int i = 0; i < NKB; ++i) dqg[i] = dw[i] = dkt[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < 4; ++i) dp[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int jb = 0; jb < DV / kVB; ++jb) {
+        __syncthreads();
+        g2s(S + kVB * jb, DV, sS, LB, DK, kVB);
+        g2s(dX + kVB * jb, DV, sX, LB, DK, kVB);
+        for (int i = threadIdx.x; i < kC * kVB; i += kT) {
+            const int t = i / kVB, j = i % kVB;
+            sO[t * LB + j] = t < it.L ? ld_in<TIn>(b.dout, (static_cast<int64_t>(it.t0 + t) * H + it.h) * DV + kVB * jb + j) : 0.f;
+            sU[t * LB + j] = Ut[t * DV + kVB * jb + j];
+        }
+        __syncthreads();
+        // U and dU of this wave's token block
+        for (int cb = 0; cb < kVB / 16; ++cb) {
+            const f32x4 ws = mm16(sW + 16 * wave * LK, LK, 1, sS + 16 * cb, LB, 1, DK, lane, f32x4{0.f, 0.f, 0.f, 0.f});
+            const f32x4 u = get_tile(sU, LB, wave, cb, lane) - ws;
+            f32x4 du = mm16(sP + 16 * wave, 1, LC, sO + 16 * cb, LB, 1, kC, lane, f32x4{0.f, 0.f, 0.f, 0.f}) * a.scale;
+            du = mm16(sK + 16 * wave * LK, LK, 1, sX + 16 * cb, LB, 1, DK, lane, du);
+            __syncthreads();
+            put_tile(sU, LB, wave, cb, u, lane);
+            put_tile(sdU, LB, wave, cb, du, lane);
+            __syncthreads();
+        }
+        __syncthreads();
+        for (int i = threadIdx.x; i < kC * kVB; i += kT)
+            dUg[(i / kVB) * DV + kVB * jb + i % kVB] = sdU[(i / kVB) * LB + i % kVB];
+        if (threadIdx.x < DK) {
+            float s = 0.f;
+            for (int j = 0; j < kVB; ++j) s = fmaf(sS[threadIdx.x * LB + j], sX[threadIdx.x * LB + j], s);
+            sgl[threadIdx.x] += s;
+        }
+        // contractions over this block's columns (k = the block's 32 value columns)
+        for (int cb = 0; cb < NKB; ++cb) {
+            dqg[cb] = mm16(sO + 16 * wave * LB, LB, 1, sS + 16 * cb * LB, 1, LB, kVB, lane, dqg[cb]);
+            dw[cb] = mm16(sdU + 16 * wave * LB, LB, 1, sS + 16 * cb * LB, 1, LB, kVB, lane, dw[cb]);
+            dkt[cb] = mm16(sU + 16 * wave * LB, LB, 1, sX + 16 * cb * LB, 1, LB, kVB, lane, dkt[cb]);
+        }
+        for (int sb = 0; sb < 4; ++sb)
+            dp[sb] = mm16(sO + 16 * wave * LB, LB, 1, sU + 16 * sb * LB, 1, LB, kVB, lane, dp[sb]);
+    }
+    float* dQG = X.blk(item, X.bw.dQG);
+    float* dW = X.blk(item, X.bw.dW);
+    float* dKt = X.blk(item, X.bw.dKt);
+    float* dP = X.blk(item, X.bw.dP);
+    for (int cb = 0; cb < NKB; ++cb) {
+        put_tile(dQG, DK, wave, cb, dqg[cb] * a.scale, lane);
+        put_tile(dW, DK, wave, cb, -dw[cb], lane);
+        put_tile(dKt, DK, wave, cb, dkt[cb], lane);
+    }
+    for (int sb = 0; sb < 4; ++sb) {
+        f32x4 v = dp[sb] * a.scale;
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) v[ii] = 16 * sb + r <= 16 * wave + 4 * q + ii ? v[ii] : 0.f;
+        put_tile(dP, kC, wave, sb, v, lane);
+    }
+    __syncthreads();
+    if (threadIdx.x < DK) X.blk(item, X.bw.dgl)[threadIdx.x] = X.blk(item, X.bw.gl)[threadIdx.x] * sgl[threadIdx.x];
+}
+
+// ---------------------------------------------------------------------------
+// 6. bwd_ut: dT = dW BK^T + dU BV^T, dBK = T^T dW, dBV = T^T dU, dA = -(T^T dT T^T) (s < t);
+//    dv = beta dBV, dbeta = sum v dBV + sum kh 2^G dBK + sum_s dA Ag, dAg = beta dA.
+// ---------------------------------------------------------------------------
+template <int DK, int DV, class TIn>
+__global__ __launch_bounds__(kT) void bwd_ut_kernel(BackwardArgs b) {
+    const PrefillArgs& a = b.fwd;
+    constexpr int LK = DK + 4, LV = DV + 4, LC = kC + 4;
+    constexpr int LM = LK > LV ? LK : LV;
+    __shared__ float sT[kC * LC], sM1[kC * LM], sM2[kC * LM], sDE[2 * kC * LC], inv[kC], sB[kC];
+    float* sD = sDE;
+    float* sE = sDE + kC * LC;
+    float* sG = sDE;  // the gate cumsum (DK wide) spans sD and sE while KG is formed
+    const BwCtx X(a, DK, DV, TIn::bytes);
+    Item it;
+    if (!item_of(a, static_cast<const char*>(a.workspace), X.ft, blockIdx.x, it)) return;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, H = a.H, item = blockIdx.x;
+    const int r = lane & 15, q = lane >> 4;
+    static_assert(2 * kC * LC >= kC * LK, "gate cumsum fits sD + sE");
+    // KG = kh 2^G (sM2) and dW (sM1)
+    load_rows<TIn>(a.k, DK, sM2, LK, it, H);
+    gate_cumsum(a.g, sG, LK, DK, it, H);
+    if (threadIdx.x < kC) {
+        sB[threadIdx.x] = threadIdx.x < it.L ? a.beta[static_cast<int64_t>(it.t0 + threadIdx.x) * H + it.h] : 0.f;
+    }
+    g2s(X.blk(item, X.bw.T), kC, sT, LC, kC, kC);
+    __syncthreads();
+    normalize_rows(sM2, LK, DK, inv, a.use_l2);
+    to_qg(sM2, sG, LK, DK);  // kh 2^G
+    g2s(X.blk(item, X.bw.dW), DK, sM1, LK, kC, DK);
+    __syncthreads();
+    // dT (part 1: dW BK^T, BK = beta KG, so column s takes beta_s) and dBK of this wave's
+    // rows; dbeta part sum_c KG dBK
+    f32x4 dT[4];
+    for (int sb = 0; sb < 4; ++sb)
+        dT[sb] = mm16(sM1 + 16 * wave * LK, LK, 1, sM2 + 16 * sb * LK, 1, LK, DK, lane, f32x4{0.f, 0.f, 0.f, 0.f}) *
+                 sB[16 * sb + r];
+    float* dBK = X.blk(item, X.bw.dBK);
+    float part[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int cb = 0; cb < DK / 16; ++cb) {
+        const f32x4 v = mm16(sT + 16 * wave, 1, LC, sM1 + 16 * cb, LK, 1, kC, lane, f32x4{0.f, 0.f, 0.f, 0.f});
+        put_tile(dBK, DK, wave, cb, v, lane);
+        const f32x4 kg = get_tile(sM2, LK, wave, cb, lane);
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) part[ii] = fmaf(kg[ii], v[ii], part[ii]);
+    }
+    __syncthreads();
+    // BV = beta v (sM2) and dU (sM1)
+    load_rows<TIn>(a.v, DV, sM2, LV, it, H);
+    g2s(X.blk(item, X.bw.dU), DV, sM1, LV, kC, DV);
+    __syncthreads();
+    for (int i = threadIdx.x; i < kC * DV; i += kT) sM2[(i / DV) * LV + i % DV] *= sB[i / DV];
+    __syncthreads();
+    for (int sb = 0; sb < 4; ++sb)
+        dT[sb] = mm16(sM1 + 16 * wave * LV, LV, 1, sM2 + 16 * sb * LV, 1, LV, DV, lane, dT[sb]);
+    // dBV = T^T dU: dv = beta dBV, dbeta part sum_j v dBV = sum_j BV dBV / beta (v from BV)
+    for (int cb = 0; cb < DV / 16; ++cb) {
+        const f32x4 v = mm16(sT + 16 * wave, 1, LC, sM1 + 16 * cb, LV, 1, kC, lane, f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+            const int t = 16 * wave + 4 * q + ii, j = 16 * cb + r;
+            if (t < it.L) {
+                const float raw = ld_in<TIn>(a.v, (static_cast<int64_t>(it.t0 + t) * H + it.h) * DV + j);
+                part[ii] = fmaf(raw, v[ii], part[ii]);
+                st_out(b.dv, (static_cast<int64_t>(it.t0 + t) * H + it.h) * DV + j, sB[t] * v[ii], TIn{});
+            }
+        }
+    }
+    // dT to LDS; E = T^T dT; dA = -(E T^T) (s < t)
+    for (int sb = 0; sb < 4; ++sb) put_tile(sD, LC, wave, sb, dT[sb], lane);
+    __syncthreads();
+    for (int sb = 0; sb < 4; ++sb)
+        put_tile(sE, LC, wave, sb, mm16(sT + 16 * wave, 1, LC, sD + 16 * sb, LC, 1, kC, lane, f32x4{0.f, 0.f, 0.f, 0.f}), lane);
+    __syncthreads();
+    const float* Ag = X.blk(item, X.bw.Ag);
+    float* dAg = X.blk(item, X.bw.dAg);
+    for (int sb = 0; sb < 4; ++sb) {
+        f32x4 v = mm16(sE + 16 * wave * LC, LC, 1, sT + 16 * sb * LC, 1, LC, kC, lane, f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+            const int t = 16 * wave + 4 * q + ii, s = 16 * sb + r;
+            const float da = s < t ? -v[ii] : 0.f;
+            part[ii] = fmaf(da, Ag[t * kC + s], part[ii]);
+            v[ii] = sB[t] * da;
+        }
+        put_tile(dAg, kC, wave, sb, v, lane);
+    }
+    // dbeta: reduce the partial sums over the 16 lanes of each row group
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) {
+        float x = part[ii];
+        x += __shfl_xor(x, 1, 64);
+        x += __shfl_xor(x, 2, 64);
+        x += __shfl_xor(x, 4, 64);
+        x += __shfl_xor(x, 8, 64);
+        const int t = 16 * wave + 4 * q + ii;
+        if (r == 0 && t < it.L) b.dbeta[static_cast<int64_t>(it.t0 + t) * H + it.h] = x;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// 7. bwd_final: X1..X4, dkh, dqh, dG, reverse cumsum, norm backward; dq, dk, dg.
+//    Wave w owns token block w (rows of every output tile).
+// ---------------------------------------------------------------------------
+template <int DK, int DV, class TIn>
+__global__ __launch_bounds__(kT) void bwd_final_kernel(BackwardArgs b) {
+    const PrefillArgs& a = b.fwd;
+    constexpr int LK = DK + 4, LC = kC + 4, NKB = DK / 16;
+    __shared__ float sK[kC * LK], sQ[kC * LK], sG[kC * LK], sA[kC * LC], sP[kC * LC], iq[kC], ik[kC], sB[kC],
+        sGL[DK];
+    const BwCtx X(a, DK, DV, TIn::bytes);
+    Item it;
+    if (!item_of(a, static_cast<const char*>(a.workspace), X.ft, blockIdx.x, it)) return;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, H = a.H, item = blockIdx.x;
+    const int r = lane & 15, q = lane >> 4;
+    load_rows<TIn>(a.k, DK, sK, LK, it, H);
+    load_rows<TIn>(a.q, DK, sQ, LK, it, H);
+    gate_cumsum(a.g, sG, LK, DK, it, H);
+    g2s(X.blk(item, X.bw.dAg), kC, sA, LC, kC, kC);
+    g2s(X.blk(item, X.bw.dP), kC, sP, LC, kC, kC);
+    if (threadIdx.x < kC) sB[threadIdx.x] = threadIdx.x < it.L ? a.beta[static_cast<int64_t>(it.t0 + threadIdx.x) * H + it.h] : 0.f;
+    __syncthreads();
+    normalize_rows(sK, LK, DK, ik, a.use_l2);
+    normalize_rows(sQ, LK, DK, iq, a.use_l2);
+    const float* dBK = X.blk(item, X.bw.dBK);
+    const float* dQG = X.blk(item, X.bw.dQG);
+    const float* dKt = X.blk(item, X.bw.dKt);
+    // per channel tile: dkh, dqh and dG of this wave's 16 rows
+    f32x4 dkh[NKB], dqh[NKB], dG[NKB];
+    float ktdkt[NKB];  // sum over this lane's rows of Kt dKt (for dG_L)
+    for (int cb = 0; cb < NKB; ++cb) {
+        const f32x4 x1 = dtok_tile<true>(sA, LC, sK, sG, LK, wave, cb, lane);
+        const f32x4 x2 = dtok_tile<false>(sA, LC, sK, sG, LK, wave, cb, lane);
+        const f32x4 x3 = dtok_tile<false>(sP, LC, sQ, sG, LK, wave, cb, lane);
+        const f32x4 x4 = dtok_tile<true>(sP, LC, sK, sG, LK, wave, cb, lane);
+        const f32x4 dbk = get_tile(dBK, DK, wave, cb, lane), dqg = get_tile(dQG, DK, wave, cb, lane);
+        const f32x4 dkt = get_tile(dKt, DK, wave, cb, lane);
+        const int c = 16 * cb + r;
+        const float gL = sG[(kC - 1) * LK + c];
+        ktdkt[cb] = 0.f;
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+            const int t = 16 * wave + 4 * q + ii;
+            const float kh = sK[t * LK + c], qh = sQ[t * LK + c], Gt = sG[t * LK + c];
+            const float eg = ex2(Gt), el = ex2(gL - Gt);
+            const float bk = sB[t] * kh * eg, kt = kh * el, qg = qh * eg;
+            dkh[cb][ii] = sB[t] * eg * dbk[ii] + el * dkt[ii] + x1[ii] + x2[ii] + x3[ii];
+            dqh[cb][ii] = eg * dqg[ii] + x4[ii];
+            dG[cb][ii] = qg * dqg[ii] + bk * dbk[ii] - kt * dkt[ii] + kh * (x1[ii] - x2[ii] - x3[ii]) + qh * x4[ii];
+            ktdkt[cb] = fmaf(kt, dkt[ii], ktdkt[cb]);
+        }
+    }
+    // norm backward: row dot products over the channel tiles and the 16 lanes of a row group
+    float pq[4], pk[4];
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) {
+        float x = 0.f, y = 0.f;
+        for (int cb = 0; cb < NKB; ++cb) {
+            const int t = 16 * wave + 4 * q + ii, c = 16 * cb + r;
+            x = fmaf(sQ[t * LK + c], dqh[cb][ii], x);
+            y = fmaf(sK[t * LK + c], dkh[cb][ii], y);
+        }
+        for (int m = 1; m < 16; m <<= 1) {
+            x += __shfl_xor(x, m, 64);
+            y += __shfl_xor(y, m, 64);
+        }
+        pq[ii] = x;
+        pk[ii] = y;
+    }
+    for (int cb = 0; cb < NKB; ++cb) {
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+            const int t = 16 * wave + 4 * q + ii, c = 16 * cb + r;
+            if (t < it.L) {
+                const int64_t o = (static_cast<int64_t>(it.t0 + t) * H + it.h) * DK + c;
+                const float vq = a.use_l2 ? iq[t] * (dqh[cb][ii] - sQ[t * LK + c] * pq[ii]) : dqh[cb][ii];
+                const float vk = a.use_l2 ? ik[t] * (dkh[cb][ii] - sK[t * LK + c] * pk[ii]) : dkh[cb][ii];
+                st_out(b.dq, o, vq, TIn{});
+                st_out(b.dk, o, vk, TIn{});
+            }
+        }
+    }
+    // dG_L = dgl + sum_t Kt dKt: the per-lane sums reduced over q (the 4 row groups of a wave)
+    // and over the waves through LDS
+    __syncthreads();  // sG's values are no longer read below this point
+    if (threadIdx.x < DK) sGL[threadIdx.x] = X.blk(item, X.bw.dgl)[threadIdx.x];
+    __syncthreads();
+    for (int cb = 0; cb < NKB; ++cb) {
+        float x = ktdkt[cb];
+        x += __shfl_xor(x, 16, 64);
+        x += __shfl_xor(x, 32, 64);
+        if (q == 0) atomicAdd(&sGL[16 * cb + r], x);
+    }
+    // dG into sG (rows of this wave), then the reverse cumsum per channel plus dG_L
+    for (int cb = 0; cb < NKB; ++cb) put_tile(sG, LK, wave, cb, dG[cb], lane);
+    __syncthreads();
+    if (threadIdx.x < DK) {
+        const int c = threadIdx.x;
+        float x = sGL[c];
+        for (int t = kC - 1; t >= 0; --t) {
+            if (t < it.L) x += sG[t * LK + c];
+            sG[t * LK + c] = x;
+        }
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < it.L * DK; i += kT) {
+        const int t = i / DK, c = i % DK;
+        b.dg[(static_cast<int64_t>(it.t0 + t) * H + it.h) * DK + c] = sG[t * LK + c];
+    }
+}
+
+template <int DK, int DV, class TIn>
+hipError_t launch_backward_t(const BackwardArgs& b, hipStream_t stream) {
+    constexpr int E = TIn::bytes;
+    const PrefillArgs& a = b.fwd;
+    const BwLayout bw(a.num_seqs, a.total_tokens, a.H, DK, DV, E);
+    // 0: initial states and slots for the forward pass
+    const int64_t n0 = static_cast<int64_t>(a.num_seqs) * a.H * DK * DV;
+    const int g0 = static_cast<int>(n0 / kT + 1 < 4096 ? n0 / kT + 1 : 4096);
+    hipLaunchKernelGGL(bwd_init_kernel, dim3(g0), dim3(kT), 0, stream, b, DK, DV, E);
+    // 1: the forward with chunk states
+    hipError_t err = launch_prefill(a, E == 2, DK, DV, stream);
+    if (err != hipSuccess) return err;
+    const dim3 grid(static_cast<unsigned>(bw.max_items));
+    if (bw.max_items > 0) {
+        hipLaunchKernelGGL((bwd_intra_kernel<DK, DV, TIn>), grid, dim3(kT), 0, stream, b);
+        hipLaunchKernelGGL((bwd_prep_kernel<DK, DV, TIn>), grid, dim3(kT), 0, stream, b);
+    }
+    hipLaunchKernelGGL((bwd_scan_kernel<DK, DV>), dim3(static_cast<unsigned>(a.num_seqs * a.H * (DV / 16))),
+                       dim3(64 * (DK / 16)), 0, stream, b, E);
+    if (bw.max_items > 0) {
+        hipLaunchKernelGGL((bwd_state_kernel<DK, DV, TIn>), grid, dim3(kT), 0, stream, b);
+        hipLaunchKernelGGL((bwd_ut_kernel<DK, DV, TIn>), grid, dim3(kT), 0, stream, b);
+        hipLaunchKernelGGL((bwd_final_kernel<DK, DV, TIn>), grid, dim3(kT), 0, stream, b);
+    }
+    return hipGetLastError();
+}
+
+template <class TIn>
+hipError_t launch_backward_dt(const BackwardArgs& b, int dk, int dv, hipStream_t stream) {
+    if (dk == 128 && dv == 128) return launch_backward_t<128, 128, TIn>(b, stream);
+    if (dk == 128 && dv == 64) return launch_backward_t<128, 64, TIn>(b, stream);
+    if (dk == 64 && dv == 128) return launch_backward_t<64, 128, TIn>(b, stream);
+    if (dk == 64 && dv == 64) return launch_backward_t<64, 64, TIn>(b, stream);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+size_t backward_workspace_bytes(int num_seqs, int64_t total_tokens, int H, int dk, int dv, int bf16) {
+    return BwLayout(num_seqs, total_tokens, H, dk, dv, bf16 ? 2 : 4).total;
+}
+
+// Points the forward pass of a backward call at its part of the workspace.
+void backward_setup(BackwardArgs& b, int dk, int dv, int bf16) {
+    const BwLayout bw(b.fwd.num_seqs, b.fwd.total_tokens, b.fwd.H, dk, dv, bf16 ? 2 : 4);
+    char* base = static_cast<char*>(b.fwd.workspace);
+    b.fwd.pool = reinterpret_cast<float*>(base + bw.off_pool);
+    b.fwd.slot_idx = reinterpret_cast<const int32_t*>(base + bw.off_slots);
+    b.fwd.h0_from_pool = 1;
+    b.fwd.o = base + bw.off_o;
+    b.fwd.chunk_states = reinterpret_cast<float*>(base + bw.off_items + bw.S);
+    b.fwd.chunk_state_stride = bw.item / sizeof(float);
+}
+
+hipError_t launch_backward(const BackwardArgs& b, int bf16, int dk, int dv, hipStream_t stream) {
+    return bf16 ? launch_backward_dt<BF16>(b, dk, dv, stream) : launch_backward_dt<F32>(b, dk, dv, stream);
+}
+
+}  // namespace kda

@@ -53,6 +53,24 @@ struct PrefillArgs {
     int snap_every = 0;
     const int32_t* snap_slots = nullptr;
     int max_snaps = 0;
+    // chunk states (nullptr: none): the fp32 [dk][dv] state entering chunk c of the batch
+    // (global chunk index, head h) goes to chunk_states + (c * H + h) * chunk_state_stride
+    float* chunk_states = nullptr;
+    size_t chunk_state_stride = 0;  // floats
+};
+
+struct BackwardArgs {
+    PrefillArgs fwd;   // the forward's inputs; its pool, slots, o and chunk states are set by
+                       // backward_setup to parts of the backward workspace
+    const float* h0;   // [num_seqs, H, dk, dv] or nullptr (zero)
+    const void* dout;  // [T, H, dv] dtype
+    const float* dht;  // [num_seqs, H, dk, dv] or nullptr (zero)
+    void* dq;          // [T, H, dk] dtype
+    void* dk;          // [T, H, dk] dtype
+    void* dv;          // [T, H, dv] dtype
+    float* dg;         // [T, H, dk]
+    float* dbeta;      // [T, H]
+    float* dh0;        // [num_seqs, H, dk, dv] or nullptr
 };
 
 // Each launcher returns hipSuccess or the launch error.
@@ -67,5 +85,8 @@ hipError_t launch_prefill(const PrefillArgs& a, int bf16, int dk, int dv, hipStr
 // GPU): its device address on the current device, looked up once per device; nullptr if the
 // lookup fails.
 void* prefill_noalloc_scratch();
+size_t backward_workspace_bytes(int num_seqs, int64_t total_tokens, int H, int dk, int dv, int bf16);
+void backward_setup(BackwardArgs& b, int dk, int dv, int bf16);
+hipError_t launch_backward(const BackwardArgs& b, int bf16, int dk, int dv, hipStream_t stream);
 
 }  // namespace kda

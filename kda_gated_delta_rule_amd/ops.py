@@ -217,3 +217,49 @@ def chunk_prefill_noalloc(q, k, v, g, beta, cu_seqlens, state_pool, slot_idx, *,
         float(scale), int(bool(use_qk_l2norm)), _ptr(o), _stream(q))
     _lib.check("kda_chunk_prefill_noalloc", st)
     return o
+
+
+def chunk_backward_workspace_size(num_seqs, total_tokens, H, dk, dv, dtype=torch.bfloat16):
+    return int(_lib.load().kda_chunk_backward_workspace_size(num_seqs, total_tokens, H, dk, dv,
+                                                             _DTYPES[dtype]))
+
+
+def chunk_backward(q, k, v, g, beta, cu_seqlens, do, *, h0=None, dht=None, workspace=None,
+                   scale=None, use_qk_l2norm=True, want_dh0=True):
+    """Gradients of sum(do * o) + sum(dht * ht) of chunk_prefill (kda_chunk_backward).
+
+    q, k [T, H, dk], v [T, H, dv] (bf16 or fp32); g [T, H, dk] fp32; beta [T, H] fp32;
+    cu_seqlens [num_seqs + 1] int32; do [T, H, dv] (dtype of q); h0, dht [num_seqs, H, dk, dv]
+    fp32 or None (zero).  Returns (dq, dk, dv, dg, dbeta, dh0): dq, dk, dv in the dtype of q,
+    dg, dbeta and dh0 fp32 (dh0 None when want_dh0 is False)."""
+    Tt, H, dk = q.shape
+    dv = v.shape[-1]
+    ns = cu_seqlens.shape[0] - 1
+    _need(q.dtype in _DTYPES and k.dtype == q.dtype and v.dtype == q.dtype and do.dtype == q.dtype,
+          "q/k/v/do dtype")
+    _need(g.dtype == torch.float32 and beta.dtype == torch.float32, "g and beta must be fp32")
+    _need(k.shape == q.shape and g.shape == q.shape and v.shape == (Tt, H, dv) and do.shape == v.shape,
+          "q/k/v/g/do shape")
+    _need(beta.shape == (Tt, H) and cu_seqlens.dtype == torch.int32, "beta shape / cu_seqlens dtype")
+    for st in (h0, dht):
+        if st is not None:
+            _need(st.dtype == torch.float32 and st.shape == (ns, H, dk, dv), "h0/dht [num_seqs, H, dk, dv] fp32")
+    if debug_validate_enabled():
+        validate_cu_seqlens(cu_seqlens, Tt)
+    dq, dk_, dv_ = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    dg = torch.empty_like(g)
+    dbeta = torch.empty_like(beta)
+    dh0 = torch.empty(ns, H, dk, dv, dtype=torch.float32, device=q.device) if want_dh0 else None
+    need = chunk_backward_workspace_size(ns, Tt, H, dk, dv, q.dtype)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _contig(q, k, v, g, beta, cu_seqlens, do, h0, dht, workspace)
+    if scale is None:
+        scale = dk ** -0.5
+    st = _lib.load().kda_chunk_backward(
+        _ptr(q), _ptr(k), _ptr(v), _DTYPES[q.dtype], _ptr(g), _ptr(beta), _ptr(cu_seqlens), ns, Tt,
+        _ptr(h0), _ptr(do), _ptr(dht), H, dk, dv, float(scale), int(bool(use_qk_l2norm)), _ptr(dq),
+        _ptr(dk_), _ptr(dv_), _ptr(dg), _ptr(dbeta), _ptr(dh0), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(q))
+    _lib.check("kda_chunk_backward", st)
+    return dq, dk_, dv_, dg, dbeta, dh0

@@ -179,6 +179,38 @@ def test_noalloc_limit_matches_the_header():
     assert m and int(m.group(1)) << int(m.group(2)) == _lib.KDA_NOALLOC_SCRATCH_BYTES
 
 
+def backward_args(**over):
+    args = dict(q=A, k=A, v=A, dtype=1, g=A, beta=A, cu=A, ns=2, T=200, h0=None, do=A, dht=None,
+                H=2, dk=128, dv=128, scale=0.1, l2=1, dq=A, dk_=A, dv_=A, dg=A, dbeta=A, dh0=None,
+                ws=A, ws_bytes=0, stream=None)
+    args.update(over)
+    return list(args.values())
+
+
+def test_backward_workspace_size(lib):
+    f = lib.kda_chunk_backward_workspace_size
+    small = f(1, 64, 1, 128, 128, 1)
+    assert small > lib.kda_chunk_prefill_workspace_size(1, 64, 1, 128, 128, 1)
+    assert f(1, 128, 1, 128, 128, 1) > small
+    assert f(1, 64, 1, 96, 128, 1) == 0
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(q=None), _lib.KDA_ERR_INVALID_ARG),
+    (dict(do=None), _lib.KDA_ERR_INVALID_ARG),
+    (dict(dg=A + 4), _lib.KDA_ERR_INVALID_ARG),
+    (dict(h0=A + 8), _lib.KDA_ERR_INVALID_ARG),
+    (dict(l2=2), _lib.KDA_ERR_INVALID_ARG),
+    (dict(ns=0, T=0), _lib.KDA_OK),
+    (dict(dv=32), _lib.KDA_ERR_UNSUPPORTED),
+    (dict(dtype=0, dk=128), _lib.KDA_ERR_UNSUPPORTED),
+    (dict(), _lib.KDA_ERR_WORKSPACE),  # valid: stops at the workspace check
+    (dict(ws=None, ws_bytes=1 << 40), _lib.KDA_ERR_WORKSPACE),
+])
+def test_backward_validation(lib, over, code):
+    assert lib.kda_chunk_backward(*backward_args(**over)) == code
+
+
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(_lib, "_LIB", None)
     monkeypatch.setattr(_lib, "lib_path", lambda: str(tmp_path / "missing.so"))
