@@ -21,9 +21,8 @@
  *  - All pointers are device pointers to contiguous row-major arrays, 16-byte
  *    aligned.  Index arrays (slot_idx, accepted_len, cu_seqlens) live on the device
  *    and are read by the kernels, not by the host.
- *  - Supported head dims: dk, dv in {64, 128}.  Other values: KDA_ERR_UNSUPPORTED.
- *    kda_chunk_prefill with fp32 q/k/v additionally needs dk = 64 (its fp32 MFMA
- *    operand tiles for dk = 128 do not fit the 160 KiB LDS of a CU).
+ *  - Supported head dims: dk, dv in {64, 128}, for both dtypes and every entry point.
+ *    Other values: KDA_ERR_UNSUPPORTED.
  *  - Every argument check runs on the host before any HIP call; on failure nothing
  *    is launched and the error code is returned.  Device-resident indices are not
  *    checked: a slot index >= num_slots, duplicate slots within one call, or
@@ -48,7 +47,7 @@ extern "C" {
 typedef enum {
     KDA_OK = 0,
     KDA_ERR_INVALID_ARG = -1, /* null/misaligned pointer, bad size or dtype      */
-    KDA_ERR_UNSUPPORTED = -2, /* dk or dv outside {64, 128}; fp32 prefill, dk 128 */
+    KDA_ERR_UNSUPPORTED = -2, /* dk or dv outside {64, 128} */
     KDA_ERR_WORKSPACE = -3,   /* prefill workspace null or too small             */
     KDA_ERR_HIP = -4          /* a HIP launch failed                             */
 } kda_status;
@@ -215,7 +214,7 @@ size_t kda_chunk_backward_workspace_size(int num_seqs, int64_t total_tokens, int
  * The call runs the forward again (the state entering every 64-token chunk is kept in the
  * workspace), then the reverse chunk recurrence of the state gradient and the per-chunk input
  * gradients, all in fp32 arithmetic.  Supported shapes, limits and errors as kda_chunk_prefill
- * (the same numerical range; fp32 inputs need dk = 64).
+ * (the same numerical range).
  */
 int kda_chunk_backward(const void* q, const void* k, const void* v, int dtype, const float* g,
                        const float* beta, const int32_t* cu_seqlens, int num_seqs,

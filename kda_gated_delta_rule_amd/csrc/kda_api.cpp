@@ -238,7 +238,7 @@ KDA_EXPORT const char* kda_status_string(int status) {
     switch (status) {
         case KDA_OK: return "KDA_OK";
         case KDA_ERR_INVALID_ARG: return "KDA_ERR_INVALID_ARG: invalid argument";
-        case KDA_ERR_UNSUPPORTED: return "KDA_ERR_UNSUPPORTED: dk and dv must be 64 or 128 (fp32 prefill: dk = 64)";
+        case KDA_ERR_UNSUPPORTED: return "KDA_ERR_UNSUPPORTED: dk and dv must be 64 or 128";
         case KDA_ERR_WORKSPACE: return "KDA_ERR_WORKSPACE: prefill workspace missing or too small";
         case KDA_ERR_HIP: return "KDA_ERR_HIP: a HIP launch failed";
         default: return "unknown kda_status";

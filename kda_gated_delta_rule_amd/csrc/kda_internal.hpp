@@ -78,7 +78,7 @@ hipError_t launch_decode(const DecodeArgs& a, int bf16, int dk, int dv, hipStrea
 hipError_t launch_replay(const ReplayArgs& a, int dk, int dv, hipStream_t stream);
 size_t prefill_workspace_bytes(int num_seqs, int64_t total_tokens, int H, int dk, int dv,
                                int bf16);
-// False where the prefill LDS plan does not fit (fp32 inputs need dk = 64).
+// False where the prefill LDS plan does not fit a CU (every dk, dv in {64, 128} fits).
 bool prefill_supported(int bf16, int dk, int dv);
 hipError_t launch_prefill(const PrefillArgs& a, int bf16, int dk, int dv, hipStream_t stream);
 // The static prefill workspace of kda_chunk_prefill_noalloc (KDA_NOALLOC_SCRATCH_BYTES per

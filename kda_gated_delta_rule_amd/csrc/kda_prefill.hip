@@ -898,7 +898,11 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_intra_kernel(PrefillArgs a)
 //                        final state to its slot.
 //    A seg_carry workgroup has 8 waves and owns all state columns: wave w computes
 //    token block w & 3 of U (w < 4) or of O [OUT] / of the Phi columns' U [LOCAL]
-//    (w >= 4), and the state rows of dk block w % (DK/16) for its column blocks.  Its
+//    (w >= 4), and the state rows of dk block w % (DK/16) for its column blocks.
+//    Where [S | Phi] does not fit one CU's LDS (fp32 inputs, dk = 128), the local pass
+//    splits the columns over two workgroups (SPLIT = 2; the columns are independent
+//    through a chunk step): each takes half of the column blocks, and wave w computes
+//    token block w & 3 of U for half of its workgroup's blocks.  Its
 //    record granules go from the workspace into registers NB chunks ahead of their
 //    use (issued unconditionally, clamped to the segment's last chunk); ragged output
 //    rows are dropped by the buffer range check.  S and U cross between waves
@@ -907,25 +911,37 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_intra_kernel(PrefillArgs a)
 constexpr int kSegThreads = 512;
 constexpr int kLocal = 0, kOut = 1;
 
-template <int DK, int DV, class TIn, int MODE>
+template <int DK, int DV, class TIn, int MODE, int SPLIT_ = 1>
 struct SegPlan {
     using RG = RecGeo<DK, DV, TIn>;
     static constexpr int E = RG::E, CT = RG::CT, GK = RG::GK, GT = RG::GT, NT = RG::NT, TB = RG::NCB;
     static constexpr int NUB = RG::UB / 16;
     static constexpr int VB = DV / 16, KB = DK / 16;
+    static constexpr int SPLIT = SPLIT_;
     static constexpr int NCB = MODE == kOut ? VB : VB + KB;  // 16-column blocks of the state
+    static constexpr int NCW = NCB / SPLIT;                  // ... held by one workgroup
+    static constexpr int HB = NCW / 2;                       // U blocks per wave (SPLIT = 2)
     static constexpr int WPC = 8 / KB;                       // waves per dk block (1 or 2)
-    static constexpr int SJB = NCB / WPC;                    // state column blocks per wave
-    static constexpr size_t O_SX = 0, O_UX = 16ull * GK * NCB * 64;
-    static constexpr size_t BYTES = O_UX + 16ull * GT * NCB * 64;
+    static constexpr int SJB = NCW / WPC;                    // state column blocks per wave
+    static constexpr size_t O_SX = 0, O_UX = 16ull * GK * NCW * 64;
+    static constexpr size_t BYTES = O_UX + 16ull * GT * NCW * 64;
     static constexpr bool fits = BYTES <= 160 * 1024;
-    static_assert(8 % KB == 0 && NCB % WPC == 0, "segment plan");
+    static_assert(8 % KB == 0 && NCB % SPLIT == 0 && NCW % WPC == 0, "segment plan");
+    static_assert(SPLIT == 1 || (SPLIT == 2 && MODE == kLocal && E == 4 && NCW % 2 == 0),
+                  "the column split serves the fp32 local pass");
 };
 
-// The prefill supports a shape when every kernel's LDS plan fits a CU (fp32 inputs: dk = 64).
+// Column split of the local pass: 1 where [S | Phi] fits one workgroup, else 2.
+template <int DK, int DV, class TIn>
+constexpr int local_split() {
+    return SegPlan<DK, DV, TIn, kLocal>::fits || Geo<TIn>::E != 4 ? 1 : 2;
+}
+
+// The prefill supports a shape when every kernel's LDS plan fits a CU.
 template <int DK, int DV, class TIn>
 constexpr bool prefill_fits() {
-    return IntraPlan<DK, DV, TIn>::fits && SegPlan<DK, DV, TIn, kLocal>::fits && SegPlan<DK, DV, TIn, kOut>::fits;
+    return IntraPlan<DK, DV, TIn>::fits && SegPlan<DK, DV, TIn, kLocal, local_split<DK, DV, TIn>()>::fits &&
+           SegPlan<DK, DV, TIn, kOut>::fits;
 }
 
 // One chunk's operands for one wave.
@@ -936,19 +952,33 @@ struct SegOps {
     u32x4 p[SP::GT];             // P granules of the token block (O task)
     u32x4 kt[SP::GT];            // Kt granules of the wave's dk block
     f32x4 gl;                    // exp(G_L) of the wave's rows
+    f32x4 us[SP::SPLIT == 2 ? SP::HB : 1];  // SPLIT = 2: Ut of the wave's U blocks (0: Phi)
 };
 
 template <class SP>
 __device__ __forceinline__ void seg_fetch(SegOps<SP>& F, const char* rec, const WsLayout& ws, int tb, int task,
-                                          int cb, int lane) {
-    // task (wave-uniform): 0 = U (W, Ut), 1 = O (QG, P), 2 = W alone (the Phi columns' U)
+                                          int cb, int lane, int ub0 = 0) {
+    // task (wave-uniform): 0 = U (W, Ut), 1 = O (QG, P), 2 = W alone (the Phi columns' U);
+    // SPLIT = 2: W, and Ut of the global column blocks ub0 .. ub0 + HB - 1 that are state
+    // columns (zero for Phi columns)
+    if constexpr (SP::SPLIT == 2) {
+#pragma unroll
+        for (int i = 0; i < SP::HB; ++i) {
+            const int g = ub0 + i;  // wave-uniform
+            F.us[i] = g < SP::VB ? *reinterpret_cast<const f32x4*>(
+                                       rec + ws.o_u +
+                                       (static_cast<size_t>((g / SP::TB) * 4 + tb) * 64 + lane) * (SP::NUB * 16) +
+                                       16 * (g % SP::TB))
+                                 : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+    }
     {
         const char* ab = rec + (task == 1 ? ws.o_q : ws.o_w);
 #pragma unroll
         for (int g = 0; g < SP::GK; ++g)
             F.a[g] = *reinterpret_cast<const u32x4*>(ab + ((static_cast<size_t>(tb) * SP::GK + g) * 64 + lane) * 16);
     }
-    if (task == 0) {
+    if (SP::SPLIT == 1 && task == 0) {
 #pragma unroll
         for (int t = 0; t < SP::NT; ++t)
 #pragma unroll
@@ -1010,19 +1040,18 @@ __device__ __forceinline__ void store_o4(__amdgpu_buffer_rsrc_t orsrc, int trow,
 }
 
 // One chunk on the segment state.
-template <int DK, int DV, class TIn, int MODE>
-__device__ __forceinline__ void seg_step(const SegOps<SegPlan<DK, DV, TIn, MODE>>& F,
-                                         f32x4 (&S)[SegPlan<DK, DV, TIn, MODE>::SJB], char* sx, char* ux,
+template <class SP, class TIn, int MODE>
+__device__ __forceinline__ void seg_step(const SegOps<SP>& F, f32x4 (&S)[SP::SJB], char* sx, char* ux,
                                          __amdgpu_buffer_rsrc_t orsrc, int orow, int ocol, float scale, int tb,
                                          int part, int cb, int jb0, int lane) {
-    using SP = SegPlan<DK, DV, TIn, MODE>;
     constexpr TIn tag{};
+    constexpr int NCW = SP::NCW;  // column blocks of this workgroup (block indices below are its own)
     const int r = lane & 15, q4 = 4 * (lane >> 4);
 
     // (1) this wave's state tiles -> S granules (k over dk) in LDS
 #pragma unroll
     for (int j = 0; j < SP::SJB; ++j)
-        lds_tile_to_gran(sx, ((cb / SP::CT) * SP::NCB + jb0 + j) * 64 + lane, cb % SP::CT, S[j], tag);
+        lds_tile_to_gran(sx, ((cb / SP::CT) * NCW + jb0 + j) * 64 + lane, cb % SP::CT, S[j], tag);
     lds_barrier();
 
     // (2) the token block's U (part 0), and QG S [OUT] or the Phi columns' U [LOCAL] (part 1)
@@ -1030,11 +1059,18 @@ __device__ __forceinline__ void seg_step(const SegOps<SegPlan<DK, DV, TIn, MODE>
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int g = 0; g < SP::GK; ++g)
-            acc = gmma(F.a[g], *reinterpret_cast<const u32x4*>(sx + ((g * SP::NCB + jb) * 64 + lane) * 16), acc, tag);
+            acc = gmma(F.a[g], *reinterpret_cast<const u32x4*>(sx + ((g * NCW + jb) * 64 + lane) * 16), acc, tag);
         return acc;
     };
-    const int ug = ((tb / SP::CT) * SP::NCB) * 64 + lane, uh = tb % SP::CT;
-    if (part == 0) {
+    const int ug = ((tb / SP::CT) * NCW) * 64 + lane, uh = tb % SP::CT;
+    if constexpr (SP::SPLIT == 2) {
+        // blocks part * HB .. of this workgroup: U = Ut - W S (Ut zero for Phi columns)
+#pragma unroll
+        for (int i = 0; i < SP::HB; ++i) {
+            const int jb = part * SP::HB + i;
+            lds_tile_to_gran(ux, ug + jb * 64, uh, F.us[i] - prod(jb), tag);
+        }
+    } else if (part == 0) {
 #pragma unroll
         for (int jb = 0; jb < SP::VB; ++jb) {
             const f32x4 acc = prod(jb);
@@ -1044,7 +1080,7 @@ __device__ __forceinline__ void seg_step(const SegOps<SegPlan<DK, DV, TIn, MODE>
             lds_tile_to_gran(ux, ug + jb * 64, uh, uv, tag);
         }
     }
-    if constexpr (MODE == kLocal) {
+    if constexpr (MODE == kLocal && SP::SPLIT == 1) {
         // the Phi columns' U (no Ut term)
         if (part == 1) {
 #pragma unroll
@@ -1067,7 +1103,7 @@ __device__ __forceinline__ void seg_step(const SegOps<SegPlan<DK, DV, TIn, MODE>
         f32x4 acc = S[j] * F.gl;
 #pragma unroll
         for (int g = 0; g < SP::GT; ++g)
-            acc = gmma(F.kt[g], *reinterpret_cast<const u32x4*>(ux + ((g * SP::NCB + jb0 + j) * 64 + lane) * 16),
+            acc = gmma(F.kt[g], *reinterpret_cast<const u32x4*>(ux + ((g * NCW + jb0 + j) * 64 + lane) * 16),
                        acc, tag);
         S[j] = acc;
     }
@@ -1079,7 +1115,7 @@ __device__ __forceinline__ void seg_step(const SegOps<SegPlan<DK, DV, TIn, MODE>
                 f32x4 acc = oacc[jb];
 #pragma unroll
                 for (int g = 0; g < SP::GT; ++g)
-                    acc = gmma(F.p[g], *reinterpret_cast<const u32x4*>(ux + ((g * SP::NCB + jb) * 64 + lane) * 16),
+                    acc = gmma(F.p[g], *reinterpret_cast<const u32x4*>(ux + ((g * NCW + jb) * 64 + lane) * 16),
                                acc, tag);
                 store_o4(orsrc, trow, orow, ocol + 16 * jb + r, acc * scale, r, tag);
             }
@@ -1087,9 +1123,9 @@ __device__ __forceinline__ void seg_step(const SegOps<SegPlan<DK, DV, TIn, MODE>
     }
 }
 
-template <int DK, int DV, class TIn, int MODE, int NB>
+template <int DK, int DV, class TIn, int MODE, int NB, int SPLIT>
 __global__ __launch_bounds__(kSegThreads) void seg_carry_kernel(PrefillArgs a) {
-    using SP = SegPlan<DK, DV, TIn, MODE>;
+    using SP = SegPlan<DK, DV, TIn, MODE, SPLIT>;
     constexpr int E = SP::E;
     __shared__ __attribute__((aligned(16))) char smem[SP::BYTES];
     char* sx = smem + SP::O_SX;
@@ -1098,7 +1134,16 @@ __global__ __launch_bounds__(kSegThreads) void seg_carry_kernel(PrefillArgs a) {
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int tb = wave & 3, part = wave >> 2;
     const int cb = wave % SP::KB, jb0 = (wave / SP::KB) * SP::SJB;
-    const int H = a.H, s = blockIdx.x / H, h = blockIdx.x % H;
+    // SPLIT = 2: the two workgroups of a (segment, head) have block ids congruent mod
+    // kNumXcd (so they run on one XCD and read each record from its L2); half 0 holds the
+    // column blocks 0 .. NCW - 1, half 1 the rest
+    int pair = blockIdx.x, half = 0;
+    if constexpr (SPLIT == 2) {
+        pair = (blockIdx.x / (2 * kNumXcd)) * kNumXcd + blockIdx.x % kNumXcd;
+        half = (blockIdx.x / kNumXcd) & 1;
+    }
+    const int cw0 = half * SP::NCW;  // first global column block of this workgroup
+    const int H = a.H, s = pair / H, h = pair % H;
     const WsLayout ws(a.num_seqs, a.total_tokens, H, DK, DV, E);
     const char* base = static_cast<const char*>(a.workspace);
     const int32_t* chunk_off = reinterpret_cast<const int32_t*>(base);
@@ -1123,12 +1168,14 @@ __global__ __launch_bounds__(kSegThreads) void seg_carry_kernel(PrefillArgs a) {
         for (int j = 0; j < SP::SJB; ++j)
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr)
-                S[j][rr] = (jb0 + j >= SP::VB && 16 * cb + q4 + rr == 16 * (jb0 + j - SP::VB) + r) ? 1.f : 0.f;
+                S[j][rr] = (cw0 + jb0 + j >= SP::VB && 16 * cb + q4 + rr == 16 * (cw0 + jb0 + j - SP::VB) + r) ? 1.f
+                                                                                                            : 0.f;
     }
 
     const char* recs = base + ws.off_rec;
     auto rec_of = [&](int c) { return recs + ws.rec_bytes * (static_cast<size_t>(c) * H + h); };
-    const int task = part == 0 ? 0 : (MODE == kOut ? 1 : 2);
+    const int task = SPLIT == 2 || part == 0 ? 0 : (MODE == kOut ? 1 : 2);
+    const int ub0 = cw0 + part * SP::HB;  // SPLIT = 2: the wave's first U column block
     const int c_last = c_first + nc - 1;
     const int bos = a.cu_seqlens[seq], eos = a.cu_seqlens[seq + 1], cs0 = chunk_off[seq];
     const int orow = H * DV, ocol = h * DV;
@@ -1149,7 +1196,7 @@ __global__ __launch_bounds__(kSegThreads) void seg_carry_kernel(PrefillArgs a) {
     SegOps<SP> F[NB];
 #pragma unroll
     for (int k = 0; k < NB; ++k)
-        seg_fetch(F[k], rec_of(min(c_first + k, c_last)), ws, tb, task, cb, lane);
+        seg_fetch(F[k], rec_of(min(c_first + k, c_last)), ws, tb, task, cb, lane, ub0);
     for (int c = c_first; c <= c_last; c += NB) {
 #pragma unroll
         for (int k = 0; k < NB; ++k) {
@@ -1168,9 +1215,9 @@ __global__ __launch_bounds__(kSegThreads) void seg_carry_kernel(PrefillArgs a) {
 #pragma unroll
                         for (int rr = 0; rr < 4; ++rr) Sc[(16 * cb + q4 + rr) * DV + 16 * (jb0 + j2) + r] = S[j2][rr];
                 }
-                seg_step<DK, DV, TIn, MODE>(F[k], S, sx, ux, orsrc, orow, ocol, a.scale, tb, part, cb, jb0, lane);
+                seg_step<SP, TIn, MODE>(F[k], S, sx, ux, orsrc, orow, ocol, a.scale, tb, part, cb, jb0, lane);
             }
-            seg_fetch(F[k], rec_of(min(cc + NB, c_last)), ws, tb, task, cb, lane);
+            seg_fetch(F[k], rec_of(min(cc + NB, c_last)), ws, tb, task, cb, lane, ub0);
         }
     }
 
@@ -1189,7 +1236,7 @@ __global__ __launch_bounds__(kSegThreads) void seg_carry_kernel(PrefillArgs a) {
         float* Ph = reinterpret_cast<float*>(blk + ws.s_phi);
 #pragma unroll
         for (int j = 0; j < SP::SJB; ++j) {
-            const int jb = jb0 + j;
+            const int jb = cw0 + jb0 + j;
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) {
                 const int row = 16 * cb + q4 + rr;
@@ -1349,8 +1396,11 @@ hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t stream) {
             const int slots = 2 * device_cu_count();
             const int grid = static_cast<int>(items < slots ? items : slots);
             hipLaunchKernelGGL((chunk_intra_kernel<DK, DV, TIn>), dim3(grid), dim3(kThreads), 0, stream, a);
-            const dim3 sgrid(static_cast<unsigned>(ws.max_segs * a.H));
-            hipLaunchKernelGGL((seg_carry_kernel<DK, DV, TIn, kLocal, kCarryNB>), sgrid, dim3(kSegThreads), 0,
+            constexpr int LS = local_split<DK, DV, TIn>();
+            const int64_t pairs = ws.max_segs * a.H;
+            const dim3 lgrid(static_cast<unsigned>(
+                LS == 1 ? pairs : (pairs + kNumXcd - 1) / kNumXcd * kNumXcd * LS));
+            hipLaunchKernelGGL((seg_carry_kernel<DK, DV, TIn, kLocal, kCarryNB, LS>), lgrid, dim3(kSegThreads), 0,
                                stream, a);
         }
         // one block per (sequence, head, 16-column tile), padded to whole XCD groups;
@@ -1359,7 +1409,7 @@ hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t stream) {
         const int sblocks = (groups < 4096 ? groups : 4096) * kNumXcd * (DV / 16);
         hipLaunchKernelGGL((seg_scan_kernel<DK, DV, E>), dim3(sblocks), dim3(64 * (DK / 16)), 0, stream, a);
         if (items > 0)
-            hipLaunchKernelGGL((seg_carry_kernel<DK, DV, TIn, kOut, kCarryNB>),
+            hipLaunchKernelGGL((seg_carry_kernel<DK, DV, TIn, kOut, kCarryNB, 1>),
                                dim3(static_cast<unsigned>(ws.max_segs * a.H)), dim3(kSegThreads), 0, stream, a);
         return hipGetLastError();
     }

@@ -118,7 +118,7 @@ def test_prefill_workspace_size(lib):
     (dict(ns=0, T=0), _lib.KDA_OK),
     (dict(T=-5), _lib.KDA_ERR_INVALID_ARG),
     (dict(dk=100), _lib.KDA_ERR_UNSUPPORTED),
-    (dict(dtype=0, dk=128), _lib.KDA_ERR_UNSUPPORTED),  # fp32 prefill needs dk = 64
+    (dict(dtype=0, dk=128), _lib.KDA_ERR_WORKSPACE),  # fp32 at dk = 128 is supported
     (dict(ws=None), _lib.KDA_ERR_WORKSPACE),
     (dict(ws_bytes=1024), _lib.KDA_ERR_WORKSPACE),
 ])
@@ -203,7 +203,7 @@ def test_backward_workspace_size(lib):
     (dict(l2=2), _lib.KDA_ERR_INVALID_ARG),
     (dict(ns=0, T=0), _lib.KDA_OK),
     (dict(dv=32), _lib.KDA_ERR_UNSUPPORTED),
-    (dict(dtype=0, dk=128), _lib.KDA_ERR_UNSUPPORTED),
+    (dict(dtype=0, dk=128), _lib.KDA_ERR_WORKSPACE),  # fp32 at dk = 128 is supported
     (dict(), _lib.KDA_ERR_WORKSPACE),  # valid: stops at the workspace check
     (dict(ws=None, ws_bytes=1 << 40), _lib.KDA_ERR_WORKSPACE),
 ])

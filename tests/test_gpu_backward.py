@@ -56,13 +56,22 @@ def run_and_compare(y, do, dht, h0, tol, label, use_l2=True, heads_check=True):
     announce("%s: rel-L2 whole/worst %s" % (label, ", ".join(msg)))
 
 
-@pytest.mark.parametrize("dv", [64, 128])
-def test_fp32_varlen(dv):
-    """fp32 (dk = 64): ragged varlen batch (1, 63, 64, 65, 0, 200, 130 tokens), h0 and dht."""
-    y = W.prefill(seed=41, seqlens=(1, 63, 64, 65, 0, 200, 130), H=2, dk=64, dv=dv, num_slots=7,
+@pytest.mark.parametrize("dk,dv", [(64, 64), (64, 128), (128, 64), (128, 128)])
+def test_fp32_varlen(dk, dv):
+    """fp32: ragged varlen batch (1, 63, 64, 65, 0, 200, 130 tokens), h0 and dht."""
+    y = W.prefill(seed=41, seqlens=(1, 63, 64, 65, 0, 200, 130), H=2, dk=dk, dv=dv, num_slots=7,
                   h0_std=0.05, dtype=torch.float32)
     do, dht, h0 = grads_case(y, 1)
-    run_and_compare(y, do, dht, h0, 1e-4, "backward fp32 dv=%d" % dv)
+    run_and_compare(y, do, dht, h0, 1e-4, "backward fp32 dk=%d dv=%d" % (dk, dv))
+
+
+def test_fp32_multi_segment_dk128():
+    """fp32, dk = dv = 128, sequences of several segments: the forward's local pass splits
+    [S | Phi] over two workgroups by columns."""
+    y = W.prefill(seed=45, seqlens=(2100, 1030), H=1, dk=128, dv=128, num_slots=2, h0_std=0.05,
+                  dtype=torch.float32)
+    do, dht, h0 = grads_case(y, 6)
+    run_and_compare(y, do, dht, h0, 1e-4, "backward fp32 multi-segment dk=128")
 
 
 @pytest.mark.parametrize("dk,dv", [(128, 128), (64, 64), (128, 64), (64, 128)])

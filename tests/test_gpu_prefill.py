@@ -49,12 +49,12 @@ def test_tiny_fp32_through_prefill():
     check_prefill_parity(f64(o), o_ref, f64(pool.cpu()), h_ref, y["cu_seqlens"], 1e-4, "tiny fp32")
 
 
-@pytest.mark.parametrize("dv", [64, 128])
-def test_fp32_varlen_ragged(dv):
-    """fp32 (dk = 64): ragged varlen batch with tails, an empty sequence and h0 from slots."""
+@pytest.mark.parametrize("dk,dv", [(64, 64), (64, 128), (128, 64), (128, 128)])
+def test_fp32_varlen_ragged(dk, dv):
+    """fp32: ragged varlen batch with tails, an empty sequence and h0 from slots."""
     dev = need_gpu()
-    announce("prefill fp32 varlen dk=64 dv=%d" % dv)
-    y = W.prefill(seed=1, seqlens=(1, 63, 64, 65, 0, 200, 130), H=3, dk=64, dv=dv, num_slots=10,
+    announce("prefill fp32 varlen dk=%d dv=%d" % (dk, dv))
+    y = W.prefill(seed=1, seqlens=(1, 63, 64, 65, 0, 200, 130), H=3, dk=dk, dv=dv, num_slots=10,
                   h0_std=0.05, dtype=torch.float32)
     o, pool = run_prefill(y, dev)
     o_ref, h_ref, _ = oracle_prefill(y)
@@ -85,12 +85,13 @@ def test_bf16_varlen_ragged(dk, dv):
 MULTI_SEG = (4200, 2049, 64, 0, 4097, 2048)
 
 
-@pytest.mark.parametrize("dv", [64, 128])
-def test_fp32_multi_segment(dv):
-    """fp32 (dk = 64) through several segments per sequence with h0 from slots; <= 1e-4."""
+@pytest.mark.parametrize("dk,dv", [(64, 64), (64, 128), (128, 64), (128, 128)])
+def test_fp32_multi_segment(dk, dv):
+    """fp32 through several segments per sequence with h0 from slots; <= 1e-4.  At dk = dv =
+    128 the local pass splits [S | Phi] over two workgroups by columns."""
     dev = need_gpu()
-    announce("prefill fp32 multi-segment dk=64 dv=%d" % dv)
-    y = W.prefill(seed=7, seqlens=MULTI_SEG, H=2, dk=64, dv=dv, num_slots=8, h0_std=0.05,
+    announce("prefill fp32 multi-segment dk=%d dv=%d" % (dk, dv))
+    y = W.prefill(seed=7, seqlens=MULTI_SEG, H=2, dk=dk, dv=dv, num_slots=8, h0_std=0.05,
                   dtype=torch.float32)
     o, pool = run_prefill(y, dev)
     o_ref, h_ref, _ = oracle_prefill(y)
@@ -126,7 +127,7 @@ def test_many_short_sequences_scan_grid_loops():
                          1e-2, "520 short sequences")
 
 
-@pytest.mark.parametrize("dtype,d", [(torch.bfloat16, 128), (torch.float32, 64)])
+@pytest.mark.parametrize("dtype,d", [(torch.bfloat16, 128), (torch.float32, 64), (torch.float32, 128)])
 def test_beta0_g0_keeps_the_state_exactly(dtype, d):
     """beta = 0 and g = 0: every chunk leaves the state unchanged (W = 0, Ut = 0, exp(G_L) = 1),
     the local pass keeps Phi = I and S_loc = 0, and the scan multiplies by I, all exactly, so
@@ -279,14 +280,6 @@ def test_zero_initial_state_ignores_pool_contents():
     o_ref, h_ref, _ = oracle_prefill(y, h0_from_pool=False)
     check_prefill_parity(f64(o), o_ref, f64(pool.cpu()[y["slot_idx"].long()]), h_ref, y["cu_seqlens"],
                          1e-2, "h0 zero")
-
-
-def test_fp32_prefill_with_dk128_is_rejected():
-    dev = need_gpu()
-    y = W.prefill(seed=6, seqlens=(10,), H=1, dk=128, dv=128, num_slots=1, dtype=torch.float32)
-    with pytest.raises(kda.KdaError) as e:
-        run_prefill(y, dev)
-    assert e.value.status == -2
 
 
 def test_empty_sequence_passes_state_through():
