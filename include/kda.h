@@ -247,6 +247,62 @@ int kda_chunk_prefill_noalloc(const void* q, const void* k, const void* v, int d
                               int dk, int dv, float scale, int use_qk_l2norm, void* o,
                               hipStream_t stream);
 
+/*
+ * kda_front -- the input front of the recurrence, for the fused entry points below.  The
+ * CANN Kimi K3 inference page (section 03, MegaKDA) moves the steps in front of KDA -- the
+ * input projections, ShortConv, and the gate and beta processing -- into the same operator,
+ * without giving their formulas.  The front here takes the gate and beta processing and
+ * ShortConv, read as:
+ *   q, k, v    each convolved along the tokens of its sequence, channel by channel (causal
+ *              depthwise, width W = conv_width in 1..4):
+ *                  y_t[c] = sum_{j < W} w[h][c][j] x_{t-(W-1)+j}[c]
+ *              the W - 1 inputs before the call's first token taken from the slot's
+ *              convolution state; with conv_silu = 1, y <- y / (1 + e^-y) (SiLU).  The
+ *              convolved q, k, v then enter the recurrence (L2 norm included).
+ *   g          the log-decay is -gate_scale[h] * softplus(z) for the raw gate z passed in g's
+ *              place (softplus(z) = log(1 + e^z)); the workloads' g = -0.1 softplus(N(0, 1))
+ *              is gate_scale = 0.1.
+ *   beta       1 / (1 + e^-b) for the raw value b passed in beta's place.
+ * The input projections are not included (the pages give no weight shapes).
+ *
+ *   gate_scale  [H] fp32, >= 0
+ *   conv_q      [H, dk, conv_width] fp32;  conv_k [H, dk, conv_width] fp32;
+ *   conv_v      [H, dv, conv_width] fp32   (w[h][c][j] above; j = W - 1 is the current token)
+ *   conv_state  [num_slots, H, conv_width - 1, 2*dk + dv] in the io dtype (channels q | k | v,
+ *               row 0 the oldest input): read for the slot's sequence and replaced by its last
+ *               W - 1 inputs (earlier rows kept where the call has fewer tokens).  May be NULL
+ *               when conv_width = 1.
+ *   conv_width  1..4;  conv_silu 0 or 1
+ * The struct is read on the host during the call; the arrays it points to are device memory,
+ * 16-byte aligned.
+ */
+typedef struct {
+    const float* gate_scale;
+    const float* conv_q;
+    const float* conv_k;
+    const float* conv_v;
+    void* conv_state;
+    int conv_width;
+    int conv_silu;
+} kda_front;
+
+/*
+ * kda_decode_step_front -- kda_decode_step in commit mode with the input front fused in: the
+ * convolution, the gate and beta processing, the convolution state's update and the decode
+ * step run in one kernel per (sequence, head).  q, k, v [N, T, H, *] are the raw inputs of the
+ * convolution, g [N, T, H, dk] the raw gates z, beta [N, T, H] the raw b (see kda_front);
+ * the other arguments and the results are those of kda_decode_step with records = NULL (the
+ * front has no verify mode).  T >= 1 tokens are applied in order.  A skipped sequence
+ * (negative slot) keeps its convolution state.
+ * Errors: as kda_decode_step; front NULL, a null or misaligned gate_scale or conv weight,
+ * conv_width outside 1..4, conv_silu not 0 or 1, or (conv_width > 1) a null or misaligned
+ * conv_state give KDA_ERR_INVALID_ARG.
+ */
+int kda_decode_step_front(const void* q, const void* k, const void* v, int dtype, const float* g,
+                          const float* beta, const kda_front* front, float* state_pool,
+                          int64_t num_slots, const int32_t* slot_idx, int N, int T, int H, int dk,
+                          int dv, float scale, int use_qk_l2norm, void* o, hipStream_t stream);
+
 /* Human-readable name of a kda_status value (static string, never NULL). */
 const char* kda_status_string(int status);
 

@@ -25,6 +25,15 @@ _c_i64 = ctypes.c_int64
 _c_f = ctypes.c_float
 _c_sz = ctypes.c_size_t
 
+
+class KdaFront(ctypes.Structure):
+    """struct kda_front (include/kda.h)."""
+    _fields_ = [("gate_scale", _c_p), ("conv_q", _c_p), ("conv_k", _c_p), ("conv_v", _c_p),
+                ("conv_state", _c_p), ("conv_width", _c_i), ("conv_silu", _c_i)]
+
+
+_FRONT_P = ctypes.POINTER(KdaFront)
+
 # name -> (restype, argtypes); mirrors include/kda.h
 SIGNATURES = {
     "kda_decode_step": (_c_i, [_c_p, _c_p, _c_p, _c_i, _c_p, _c_p, _c_p, _c_i64, _c_p, _c_i, _c_i,
@@ -45,6 +54,8 @@ SIGNATURES = {
     "kda_chunk_backward": (_c_i, [_c_p, _c_p, _c_p, _c_i, _c_p, _c_p, _c_p, _c_i, _c_i64, _c_p, _c_p,
                                   _c_p, _c_i, _c_i, _c_i, _c_f, _c_i, _c_p, _c_p, _c_p, _c_p, _c_p,
                                   _c_p, _c_p, _c_sz, _c_p]),
+    "kda_decode_step_front": (_c_i, [_c_p, _c_p, _c_p, _c_i, _c_p, _c_p, _FRONT_P, _c_p, _c_i64, _c_p,
+                                     _c_i, _c_i, _c_i, _c_i, _c_i, _c_f, _c_i, _c_p, _c_p]),
     "kda_status_string": (ctypes.c_char_p, [_c_i]),
 }
 

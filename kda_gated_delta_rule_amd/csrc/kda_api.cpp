@@ -55,6 +55,53 @@ KDA_EXPORT int kda_decode_step(const void* q, const void* k, const void* v, int 
     return to_status(kda::launch_decode(a, dtype == KDA_BF16, dk, dv, stream));
 }
 
+namespace {
+
+// Checks a kda_front and copies it into the launcher's arguments; KDA_OK or the error.
+int front_args(const kda_front* f, kda::FrontArgs& out) {
+    if (!f) return KDA_ERR_INVALID_ARG;
+    if (f->conv_width < 1 || f->conv_width > 4) return KDA_ERR_INVALID_ARG;
+    if (f->conv_silu != 0 && f->conv_silu != 1) return KDA_ERR_INVALID_ARG;
+    const void* ptrs[] = {f->gate_scale, f->conv_q, f->conv_k, f->conv_v};
+    for (const void* p : ptrs)
+        if (!p || !aligned16(p)) return KDA_ERR_INVALID_ARG;
+    if (f->conv_width > 1 && (!f->conv_state || !aligned16(f->conv_state))) return KDA_ERR_INVALID_ARG;
+    out = kda::FrontArgs{f->gate_scale, f->conv_q,     f->conv_k,    f->conv_v,
+                         f->conv_state, f->conv_width, f->conv_silu};
+    return KDA_OK;
+}
+
+}  // namespace
+
+KDA_EXPORT int kda_decode_step_front(const void* q, const void* k, const void* v, int dtype,
+                                     const float* g, const float* beta, const kda_front* front,
+                                     float* state_pool, int64_t num_slots, const int32_t* slot_idx,
+                                     int N, int T, int H, int dk, int dv, float scale,
+                                     int use_qk_l2norm, void* o, hipStream_t stream) {
+    if (!valid_dtype(dtype)) return KDA_ERR_INVALID_ARG;
+    if (N < 0 || T < 1 || H < 1 || num_slots < 1) return KDA_ERR_INVALID_ARG;
+    if (!isfinite(scale)) return KDA_ERR_INVALID_ARG;
+    if (use_qk_l2norm != 0 && use_qk_l2norm != 1) return KDA_ERR_INVALID_ARG;
+    if (!supported_dim(dk) || !supported_dim(dv)) return KDA_ERR_UNSUPPORTED;
+    const void* ptrs[] = {q, k, v, g, beta, state_pool, slot_idx, o};
+    for (const void* p : ptrs)
+        if (!p || !aligned16(p)) return KDA_ERR_INVALID_ARG;
+    kda::FrontArgs fa;
+    if (const int st = front_args(front, fa); st != KDA_OK) return st;
+    const int64_t tokens = checked_mul(checked_mul(N, T), H);
+    if (tokens < 0 || checked_mul(tokens, 2 * dk + dv) < 0) return KDA_ERR_INVALID_ARG;
+    if (checked_mul(checked_mul(num_slots, H), static_cast<int64_t>(dk) * dv) < 0)
+        return KDA_ERR_INVALID_ARG;
+    if (checked_mul(checked_mul(checked_mul(num_slots, H), 3), 2 * dk + dv) < 0)
+        return KDA_ERR_INVALID_ARG;
+    if (checked_mul(N, H) > (1ll << 22)) return KDA_ERR_INVALID_ARG;
+    if (N == 0) return KDA_OK;
+
+    kda::DecodeArgs a{q, k, v, g, beta, state_pool, slot_idx, o, nullptr,
+                      N, T, H, scale, use_qk_l2norm, fa};
+    return to_status(kda::launch_decode(a, dtype == KDA_BF16, dk, dv, stream));
+}
+
 KDA_EXPORT int kda_replay_commit(float* state_pool, int64_t num_slots, const int32_t* slot_idx,
                                  const float* records, const int32_t* accepted_len, int N, int T,
                                  int H, int dk, int dv, hipStream_t stream) {

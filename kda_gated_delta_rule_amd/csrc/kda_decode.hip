@@ -40,6 +40,7 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
+constexpr int kFrontTB = kWaves;  // tokens per LDS block with the input front
 constexpr float kNormEps = 1e-6f;
 constexpr int kBufFlags = 0x00020000;  // raw buffer resource word 3 (gfx9 family)
 constexpr int kNonTemporal = 2;        // buffer access cache policy: streaming (nt)
@@ -87,6 +88,17 @@ __device__ __forceinline__ float4 quad_sum(float4 x) {
     x = make_float4(pair_sum16(x.x), pair_sum16(x.y), pair_sum16(x.z), pair_sum16(x.w));
     return make_float4(pair_sum32(x.x), pair_sum32(x.y), pair_sum32(x.z), pair_sum32(x.w));
 }
+// Sum over the lane positions of a wave that hold the same column quad: 4 (lanes 16 apart)
+// for 16 column quads per tile, 2 (lanes 32 apart) for 32.
+template <int NC4>
+__device__ __forceinline__ float4 lane_pos_sum(float4 x) {
+    if constexpr (NC4 == 16) {
+        return quad_sum(x);
+    } else {
+        static_assert(NC4 == 32, "16 or 32 column quads per tile");
+        return make_float4(pair_sum32(x.x), pair_sum32(x.y), pair_sum32(x.z), pair_sum32(x.w));
+    }
+}
 
 // Per-token vectors prepared in LDS.
 template <int DK, int BV, int TB>
@@ -99,15 +111,49 @@ struct TokenLds {
     float kq[TB];
 };
 
-// Prepares token t (local slot j) by one wave: L2 norms, alpha = exp(g), k.q.
-template <int DK, int DV, int BV, int TB, class TIn, bool VERIFY>
+// Prepares token t (local slot j) by one wave: L2 norms, alpha = exp(g), k.q.  With the
+// input front (FRONT), q, k and v are first convolved along the tokens (the inputs before
+// the call come from the slot's convolution state), g = -a_h softplus(z), beta = sigmoid(b).
+template <int DK, int DV, int BV, int TB, class TIn, bool VERIFY, bool FRONT>
 __device__ __forceinline__ void prep_token(const DecodeArgs& a, TokenLds<DK, BV, TB>& L, int j,
-                                           int n, int t, int h, int tile, int lane) {
+                                           int n, int t, int h, int tile, int lane, int slot) {
     using C = Tile<DK, DV, BV>;
     const int64_t tok = (static_cast<int64_t>(n) * a.T + t) * a.H + h;
     const int64_t rowk = tok * DK;
     float qv[C::EPL], kv[C::EPL], gv[C::EPL];
-    if constexpr (C::EPL == 2) {
+    float vv[C::VPL];
+    float b;
+    if constexpr (FRONT) {
+        const FrontArgs& f = a.front;
+        const int W = f.conv_width;
+        constexpr int CW = 2 * DK + DV;
+        // channel c of input u of the call (u >= 0), or of row u + W - 1 of the state
+        auto raw = [&](const void* x, int D, int off, int u, int c) -> float {
+            return u >= 0 ? load1<TIn>(x, ((static_cast<int64_t>(n) * a.T + u) * a.H + h) * D + c)
+                          : load1<TIn>(f.conv_state,
+                                       ((static_cast<int64_t>(slot) * a.H + h) * (W - 1) + u + W - 1) * CW + off + c);
+        };
+        auto conv = [&](const void* x, const float* w, int D, int off, int c) -> float {
+            const float* wc = w + (static_cast<int64_t>(h) * D + c) * W;
+            float acc = 0.f;
+            for (int i = 0; i < W; ++i) acc = fmaf(wc[i], raw(x, D, off, t - (W - 1) + i, c), acc);
+            return f.conv_silu ? front_silu(acc) : acc;
+        };
+        const float gs = f.gate_scale[h];
+#pragma unroll
+        for (int e = 0; e < C::EPL; ++e) {
+            const int c = lane * C::EPL + e;
+            qv[e] = conv(a.q, f.conv_q, DK, 0, c);
+            kv[e] = conv(a.k, f.conv_k, DK, DK, c);
+            gv[e] = -gs * front_softplus(a.g[rowk + c]);
+        }
+#pragma unroll
+        for (int e = 0; e < C::VPL; ++e) {
+            const int col = lane + e * kWave;
+            vv[e] = col < BV ? conv(a.v, f.conv_v, DV, 2 * DK, tile * BV + col) : 0.f;
+        }
+        b = front_sigmoid(a.beta[tok]);
+    } else if constexpr (C::EPL == 2) {
         const int c = lane * 2;
         const float2 x = load2<TIn>(a.q, rowk + c);
         const float2 y = load2<TIn>(a.k, rowk + c);
@@ -121,17 +167,18 @@ __device__ __forceinline__ void prep_token(const DecodeArgs& a, TokenLds<DK, BV,
         kv[0] = load1<TIn>(a.k, rowk + lane);
         gv[0] = a.g[rowk + lane];
     }
-    float vv[C::VPL];
+    if constexpr (!FRONT) {
 #pragma unroll
-    for (int e = 0; e < C::VPL; ++e) {
-        const int col = lane + e * kWave;
-        vv[e] = 0.f;
-        if (col < BV) {
-            const int64_t idx = tok * DV + tile * BV + col;
-            vv[e] = load1<TIn>(a.v, idx);
+        for (int e = 0; e < C::VPL; ++e) {
+            const int col = lane + e * kWave;
+            vv[e] = 0.f;
+            if (col < BV) {
+                const int64_t idx = tok * DV + tile * BV + col;
+                vv[e] = load1<TIn>(a.v, idx);
+            }
         }
+        b = a.beta[tok];
     }
-    const float b = a.beta[tok];
 
     float iq = 1.f, ik = 1.f;
     if (a.use_l2) {
@@ -173,8 +220,8 @@ __device__ __forceinline__ void prep_token(const DecodeArgs& a, TokenLds<DK, BV,
     }
 }
 
-template <int DK, int DV, int BV, int TB, class TIn, bool VERIFY>
-__global__ __launch_bounds__(kThreads, 5) void decode_kernel(DecodeArgs a) {
+template <int DK, int DV, int BV, int TB, class TIn, bool VERIFY, bool FRONT = false>
+__global__ __launch_bounds__(kThreads, FRONT ? 2 : 5) void decode_kernel(DecodeArgs a) {
     using C = Tile<DK, DV, BV>;
     __shared__ __attribute__((aligned(16))) TokenLds<DK, BV, TB> L;  // read as float4
     __shared__ float4 red[2][kWaves][kWave][2];
@@ -201,7 +248,7 @@ __global__ __launch_bounds__(kThreads, 5) void decode_kernel(DecodeArgs a) {
     for (int tb = 0; tb < a.T; tb += TB) {
         const int nb = min(TB, a.T - tb);
         for (int j = wave; j < nb; j += kWaves)
-            prep_token<DK, DV, BV, TB, TIn, VERIFY>(a, L, j, n, tb + j, h, tile, lane);
+            prep_token<DK, DV, BV, TB, TIn, VERIFY, FRONT>(a, L, j, n, tb + j, h, tile, lane, slot);
         if (tb == 0) {
 #pragma unroll
             for (int i = 0; i < C::RPT; ++i)
@@ -242,8 +289,8 @@ __global__ __launch_bounds__(kThreads, 5) void decode_kernel(DecodeArgs a) {
                 pk = f4_add(pk, red[buf][w][lane][0]);
                 pq = f4_add(pq, red[buf][w][lane][1]);
             }
-            pk = quad_sum(pk);
-            pq = quad_sum(pq);
+            pk = lane_pos_sum<C::NC4>(pk);
+            pq = lane_pos_sum<C::NC4>(pq);
             const float4 vv = *reinterpret_cast<const float4*>(&L.v[j][4 * c4]);
             const float b = L.beta[j], kq = L.kq[j];
             const float4 u = f4_mul(f4_sub(vv, pk), b);                 // beta * delta
@@ -267,6 +314,39 @@ __global__ __launch_bounds__(kThreads, 5) void decode_kernel(DecodeArgs a) {
     if (!VERIFY) {
 #pragma unroll
         for (int i = 0; i < C::RPT; ++i) store_stream4(S + (rg + C::RG * i) * DV + col0, s[i]);
+    }
+    if constexpr (FRONT) {
+        // the convolution state after the call: its last W - 1 inputs, earlier state rows
+        // where the call has fewer tokens.  The workgroup owns the whole head (one tile), so
+        // its prep reads of the state (done before the first barrier) precede these writes.
+        const FrontArgs& f = a.front;
+        const int W = f.conv_width;
+        if (W > 1) {
+            static_assert(C::NT == 1, "the front runs one workgroup per head");
+            constexpr int CW = 2 * DK + DV, NV = (3 * CW + kThreads - 1) / kThreads;
+            const int nv = (W - 1) * CW;
+            const int64_t st0 = (static_cast<int64_t>(slot) * a.H + h) * (W - 1) * CW;
+            float keep[NV];
+#pragma unroll
+            for (int i = 0; i < NV; ++i) {
+                const int idx = tid + i * kThreads;
+                keep[i] = 0.f;
+                if (idx < nv) {
+                    const int r = idx / CW, c = idx % CW, u = a.T - (W - 1) + r;
+                    const int64_t tk = (static_cast<int64_t>(n) * a.T + u) * a.H + h;
+                    keep[i] = u < 0 ? load1<TIn>(f.conv_state, st0 + static_cast<int64_t>(u + W - 1) * CW + c)
+                              : c < DK ? load1<TIn>(a.q, tk * DK + c)
+                              : c < 2 * DK ? load1<TIn>(a.k, tk * DK + c - DK)
+                              : load1<TIn>(a.v, tk * DV + c - 2 * DK);
+                }
+            }
+            __syncthreads();
+#pragma unroll
+            for (int i = 0; i < NV; ++i) {
+                const int idx = tid + i * kThreads;
+                if (idx < nv) store1<TIn>(f.conv_state, st0 + idx, keep[i]);
+            }
+        }
     }
 }
 
@@ -316,17 +396,6 @@ struct WyLds {
 // the diagonal qk_aa at 28 + a (a < 4) and 56 + a (a >= 4).
 __host__ __device__ constexpr int wy_pair(int a, int b) { return a * (a - 1) / 2 + b; }
 __host__ __device__ constexpr int wy_diag(int a) { return a < 4 ? 28 + a : 56 + a; }
-
-template <class TIn>
-__device__ __forceinline__ void store1(void* p, int64_t i, float x);
-template <>
-__device__ __forceinline__ void store1<F32>(void* p, int64_t i, float x) {
-    static_cast<float*>(p)[i] = x;
-}
-template <>
-__device__ __forceinline__ void store1<BF16>(void* p, int64_t i, float x) {
-    static_cast<uint16_t*>(p)[i] = f32_to_bf16(x);
-}
 
 // Orders this wave's LDS accesses in the compiler's schedule (the hardware completes one
 // wave's LDS operations in issue order, so a single-wave workgroup needs no s_barrier).
@@ -743,7 +812,12 @@ template <int DK, int DV, class TIn>
 hipError_t launch_decode_d(const DecodeArgs& a, hipStream_t stream) {
     constexpr int BV = DV < 64 ? DV : 64;
     const dim3 grid(static_cast<unsigned>(a.N) * a.H * (DV / BV));
-    if (a.T == 1) {
+    if (a.front.gate_scale) {
+        // the input front: one workgroup per (sequence, head) owns the head's convolution
+        // state; tokens in blocks of kFrontTB, one token per wave, commit mode only
+        hipLaunchKernelGGL((decode_kernel<DK, DV, DV, kFrontTB, TIn, false, true>),
+                           dim3(static_cast<unsigned>(a.N) * a.H), dim3(kThreads), 0, stream, a);
+    } else if (a.T == 1) {
         if (a.records)
             hipLaunchKernelGGL((decode_kernel<DK, DV, BV, 1, TIn, true>), grid, dim3(kThreads), 0, stream, a);
         else

@@ -79,6 +79,25 @@ __device__ __forceinline__ float4 load4<BF16>(const void* p, int64_t i) {
                        __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xffff0000u));
 }
 
+// Stores one element (fp32 in, rounded for bf16).
+template <class T>
+__device__ __forceinline__ void store1(void* p, int64_t i, float x);
+template <>
+__device__ __forceinline__ void store1<F32>(void* p, int64_t i, float x) {
+    static_cast<float*>(p)[i] = x;
+}
+template <>
+__device__ __forceinline__ void store1<BF16>(void* p, int64_t i, float x) {
+    static_cast<uint16_t*>(p)[i] = f32_to_bf16(x);
+}
+
+// Activations of the input front, in fp32: softplus(x) = max(x, 0) + log1p(e^-|x|) (no
+// overflow for large |x|), the logistic function 1 / (1 + e^-x), and SiLU x / (1 + e^-x)
+// (both 0 in the limit x -> -inf, where e^-x overflows to inf).
+__device__ __forceinline__ float front_softplus(float x) { return fmaxf(x, 0.f) + log1pf(expf(-fabsf(x))); }
+__device__ __forceinline__ float front_sigmoid(float x) { return 1.f / (1.f + expf(-x)); }
+__device__ __forceinline__ float front_silu(float x) { return x / (1.f + expf(-x)); }
+
 // Stores 4 consecutive elements (fp32 in, rounded for bf16).
 template <class T>
 __device__ __forceinline__ void store4(void* p, int64_t i, float4 x);

@@ -8,6 +8,19 @@
 
 namespace kda {
 
+// The input front (kda_front in include/kda.h): gate_scale == nullptr means none.  With a
+// front, the g argument holds raw gates z (g = -gate_scale[h] softplus(z)), beta raw values
+// (beta = sigmoid), and q, k, v the inputs of the causal depthwise convolution.
+struct FrontArgs {
+    const float* gate_scale = nullptr;  // [H]
+    const float* conv_q = nullptr;      // [H, dk, conv_width]
+    const float* conv_k = nullptr;      // [H, dk, conv_width]
+    const float* conv_v = nullptr;      // [H, dv, conv_width]
+    void* conv_state = nullptr;         // [num_slots, H, conv_width - 1, 2 dk + dv], io dtype
+    int conv_width = 1;
+    int conv_silu = 0;
+};
+
 struct DecodeArgs {
     const void* q;
     const void* k;
@@ -21,6 +34,7 @@ struct DecodeArgs {
     int N, T, H;
     float scale;
     int use_l2;
+    FrontArgs front = {};
 };
 
 struct ReplayArgs {
@@ -57,6 +71,7 @@ struct PrefillArgs {
     // (global chunk index, head h) goes to chunk_states + (c * H + h) * chunk_state_stride
     float* chunk_states = nullptr;
     size_t chunk_state_stride = 0;  // floats
+    FrontArgs front = {};
 };
 
 struct BackwardArgs {

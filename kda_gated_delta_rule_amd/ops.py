@@ -4,6 +4,7 @@ The C ABI does not read the device-resident index arrays on the host (out-of-ran
 slots, accepted lengths outside 0..T and inconsistent cu_seqlens are undefined behaviour there).
 With the environment variable KDA_DEBUG_VALIDATE=1, every wrapper here first copies those arrays
 to the host and checks them, raising ValueError before any launch (a synchronising debug aid)."""
+import ctypes
 import os
 
 import torch
@@ -104,6 +105,59 @@ def decode_step(q, k, v, g, beta, state_pool, slot_idx, *, o=None, records=None,
         state_pool.shape[0], _ptr(slot_idx), N, T, H, dk, dv, float(scale), int(bool(use_qk_l2norm)),
         _ptr(o), _ptr(records), _stream(q))
     _lib.check("kda_decode_step", st)
+    return o
+
+
+def _front(gate_scale, conv_q, conv_k, conv_v, conv_state, conv_silu, H, dk, dv, num_slots, dtype):
+    """Checks the front's tensors and returns the kda_front struct (a reference to it)."""
+    W = conv_q.shape[-1]
+    _need(1 <= W <= 4, "conv width must be 1..4")
+    _need(gate_scale.dtype == torch.float32 and gate_scale.shape == (H,), "gate_scale [H] fp32")
+    for w, d in ((conv_q, dk), (conv_k, dk), (conv_v, dv)):
+        _need(w.dtype == torch.float32 and w.shape == (H, d, W), "conv weights [H, d, W] fp32")
+    if W > 1:
+        _need(conv_state is not None and conv_state.dtype == dtype and
+              conv_state.shape == (num_slots, H, W - 1, 2 * dk + dv),
+              "conv_state [num_slots, H, W - 1, 2 dk + dv] in the dtype of q")
+    _contig(gate_scale, conv_q, conv_k, conv_v, conv_state if W > 1 else None)
+    return _lib.KdaFront(_ptr(gate_scale), _ptr(conv_q), _ptr(conv_k), _ptr(conv_v),
+                         _ptr(conv_state) if W > 1 else None, W, int(bool(conv_silu)))
+
+
+def decode_step_front(q, k, v, gate, beta, state_pool, slot_idx, *, gate_scale, conv_q, conv_k,
+                      conv_v, conv_state=None, conv_silu=False, o=None, scale=None,
+                      use_qk_l2norm=True):
+    """Decode / MTP commit step with the input front fused in (kda_decode_step_front).
+
+    q, k [N, T, H, dk], v [N, T, H, dv]: raw convolution inputs (bf16 or fp32); gate
+    [N, T, H, dk] fp32 raw gates z (g = -gate_scale softplus(z)); beta [N, T, H] fp32 raw
+    values (sigmoid applied); gate_scale [H] fp32; conv_q/conv_k [H, dk, W], conv_v [H, dv, W]
+    fp32; conv_state [num_slots, H, W - 1, 2 dk + dv] in the dtype of q (updated in place;
+    may be None for W = 1); state_pool and slot_idx as decode_step.  Returns o.
+    """
+    N, T, H, dk = q.shape
+    dv = v.shape[-1]
+    _need(q.dtype in _DTYPES and k.dtype == q.dtype and v.dtype == q.dtype, "q/k/v dtype")
+    _need(gate.dtype == torch.float32 and beta.dtype == torch.float32, "gate and beta must be fp32")
+    _need(state_pool.dtype == torch.float32 and slot_idx.dtype == torch.int32, "pool/slot dtype")
+    _need(k.shape == q.shape and gate.shape == q.shape and v.shape == (N, T, H, dv), "q/k/v/gate shape")
+    _need(beta.shape == (N, T, H) and slot_idx.shape == (N,), "beta/slot_idx shape")
+    _need(state_pool.dim() == 4 and state_pool.shape[1:] == (H, dk, dv), "state_pool shape")
+    front = _front(gate_scale, conv_q, conv_k, conv_v, conv_state, conv_silu, H, dk, dv,
+                   state_pool.shape[0], q.dtype)
+    if o is None:
+        o = torch.empty(N, T, H, dv, dtype=q.dtype, device=q.device)
+    _need(o.shape == (N, T, H, dv) and o.dtype == q.dtype, "o shape/dtype")
+    _contig(q, k, v, gate, beta, state_pool, slot_idx, o)
+    if debug_validate_enabled():
+        validate_slots(slot_idx, state_pool.shape[0], allow_skip=True)
+    if scale is None:
+        scale = dk ** -0.5
+    st = _lib.load().kda_decode_step_front(
+        _ptr(q), _ptr(k), _ptr(v), _DTYPES[q.dtype], _ptr(gate), _ptr(beta), ctypes.byref(front),
+        _ptr(state_pool), state_pool.shape[0], _ptr(slot_idx), N, T, H, dk, dv, float(scale),
+        int(bool(use_qk_l2norm)), _ptr(o), _stream(q))
+    _lib.check("kda_decode_step_front", st)
     return o
 
 

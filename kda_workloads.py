@@ -131,6 +131,36 @@ def prefill(seed=0, seqlens=(8192,), H=None, dk=None, dv=None, num_slots=None, h
     return dict(q=q, k=k, v=v, g=g, beta=beta, cu_seqlens=cu, pool=pool, slot_idx=slot_idx)
 
 
+def front_params(seed, H, dk, dv, num_slots, width=4, dtype=torch.bfloat16):
+    """Parameters and state of the input front (ShortConv, gate and beta processing).
+
+    Returns dict(gate_scale [H] fp32 = 0.1 (the workloads' gate g = -0.1 softplus(N(0, 1))),
+    conv_q, conv_k [H, dk, width] and conv_v [H, dv, width] fp32 ~ N(0, 1 / width) (so a
+    convolution of unit-variance inputs keeps unit variance), conv_state
+    [num_slots, H, width - 1, 2 dk + dv] in dtype ~ N(0, 1) (the raw inputs' distribution)).
+    """
+    gen = _gen(seed)
+    std = width ** -0.5
+    return dict(gate_scale=torch.full((H,), 0.1, dtype=torch.float32),
+                conv_q=_normal(gen, (H, dk, width), std=std), conv_k=_normal(gen, (H, dk, width), std=std),
+                conv_v=_normal(gen, (H, dv, width), std=std),
+                conv_state=_normal(gen, (num_slots, H, width - 1, 2 * dk + dv)).to(dtype))
+
+
+def decode_front(seed=0, N=None, T=None, H=None, dk=None, dv=None, num_slots=None, width=4,
+                 dtype=torch.bfloat16):
+    """Decode inputs for the front: raw q, k, v ~ N(0, 1) (the convolution's inputs), raw gates
+    z ~ N(0, 1) in g's place and raw beta values b ~ N(0, 1) (the draws the workloads pass
+    through -0.1 softplus and sigmoid), the pool and slots as decode(), plus front_params()."""
+    x = decode(seed, N=N, T=T, H=H, dk=dk, dv=dv, num_slots=num_slots, dtype=dtype)
+    gen = _gen(seed + 1)
+    N, T, H, dk = x["q"].shape
+    x["g"] = _normal(gen, (N, T, H, dk))
+    x["beta"] = _normal(gen, (N, T, H))
+    x.update(front_params(seed + 2, H, dk, x["v"].shape[-1], x["pool"].shape[0], width, dtype))
+    return x
+
+
 def prefill_long(seed=0, **kw):
     """Long-context varlen prefill: 4 sequences (100000, 16384, 8192, 3500), H=16,
     initial states from 4 distinct slots of a 512-slot pool ~ N(0, 0.05^2)."""
