@@ -303,6 +303,26 @@ int kda_decode_step_front(const void* q, const void* k, const void* v, int dtype
                           int64_t num_slots, const int32_t* slot_idx, int N, int T, int H, int dk,
                           int dv, float scale, int use_qk_l2norm, void* o, hipStream_t stream);
 
+/*
+ * kda_chunk_prefill_front -- kda_chunk_prefill with the input front fused in: the chunk kernel
+ * convolves each 64-token chunk's raw q, k, v in its registers (the three inputs before the
+ * chunk from the previous chunk or, at a sequence start, from the slot's convolution state)
+ * and processes the raw gates and beta values there, and the output pass writes each
+ * sequence's convolution state back to its slot.  q, k, v [total_tokens, H, *] are the raw
+ * inputs of the convolution, g [total_tokens, H, dk] the raw gates z, beta [total_tokens, H]
+ * the raw b (see kda_front); the other arguments and the results are those of
+ * kda_chunk_prefill.  h0_from_pool = 1 reads both the recurrent and the convolution state
+ * from the slot; 0 starts both from zero.  With bf16 inputs the convolved q, k, v are rounded
+ * to bf16 before the chunk products (the decode front keeps them in fp32).
+ * Errors: as kda_chunk_prefill, plus the kda_front checks of kda_decode_step_front.
+ */
+int kda_chunk_prefill_front(const void* q, const void* k, const void* v, int dtype, const float* g,
+                            const float* beta, const kda_front* front, const int32_t* cu_seqlens,
+                            int num_seqs, int64_t total_tokens, float* state_pool,
+                            int64_t num_slots, const int32_t* slot_idx, int h0_from_pool, int H,
+                            int dk, int dv, float scale, int use_qk_l2norm, void* o,
+                            void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Human-readable name of a kda_status value (static string, never NULL). */
 const char* kda_status_string(int status);
 

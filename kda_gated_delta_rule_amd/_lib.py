@@ -56,6 +56,9 @@ SIGNATURES = {
                                   _c_p, _c_p, _c_sz, _c_p]),
     "kda_decode_step_front": (_c_i, [_c_p, _c_p, _c_p, _c_i, _c_p, _c_p, _FRONT_P, _c_p, _c_i64, _c_p,
                                      _c_i, _c_i, _c_i, _c_i, _c_i, _c_f, _c_i, _c_p, _c_p]),
+    "kda_chunk_prefill_front": (_c_i, [_c_p, _c_p, _c_p, _c_i, _c_p, _c_p, _FRONT_P, _c_p, _c_i, _c_i64,
+                                       _c_p, _c_i64, _c_p, _c_i, _c_i, _c_i, _c_i, _c_f, _c_i, _c_p,
+                                       _c_p, _c_sz, _c_p]),
     "kda_status_string": (ctypes.c_char_p, [_c_i]),
 }
 

@@ -137,7 +137,8 @@ int chunk_prefill_impl(const void* q, const void* k, const void* v, int dtype, c
                        const int32_t* slot_idx, int h0_from_pool, int H, int dk, int dv,
                        float scale, int use_qk_l2norm, void* o, void* workspace,
                        size_t workspace_bytes, int snap_every, const int32_t* snap_slots,
-                       int max_snaps, bool use_static, hipStream_t stream) {
+                       int max_snaps, bool use_static, hipStream_t stream,
+                       const kda::FrontArgs* front = nullptr) {
     if (!valid_dtype(dtype)) return KDA_ERR_INVALID_ARG;
     if (num_seqs < 0 || total_tokens < 0 || H < 1 || num_slots < 1) return KDA_ERR_INVALID_ARG;
     if (num_seqs == 0 && total_tokens != 0) return KDA_ERR_INVALID_ARG;
@@ -178,6 +179,7 @@ int chunk_prefill_impl(const void* q, const void* k, const void* v, int dtype, c
     kda::PrefillArgs a{q, k, v, g, beta, cu_seqlens, num_seqs, total_tokens, state_pool,
                        slot_idx, h0_from_pool, H, scale, use_qk_l2norm, o, workspace,
                        snap_every, snap_slots, max_snaps};
+    if (front) a.front = *front;
     return to_status(kda::launch_prefill(a, dtype == KDA_BF16, dk, dv, stream));
 }
 
@@ -206,6 +208,23 @@ KDA_EXPORT int kda_chunk_prefill_noalloc(const void* q, const void* k, const voi
     return chunk_prefill_impl(q, k, v, dtype, g, beta, cu_seqlens, num_seqs, total_tokens,
                               state_pool, num_slots, slot_idx, h0_from_pool, H, dk, dv, scale,
                               use_qk_l2norm, o, nullptr, 0, 0, nullptr, 0, true, stream);
+}
+
+KDA_EXPORT int kda_chunk_prefill_front(const void* q, const void* k, const void* v, int dtype,
+                                       const float* g, const float* beta, const kda_front* front,
+                                       const int32_t* cu_seqlens, int num_seqs, int64_t total_tokens,
+                                       float* state_pool, int64_t num_slots, const int32_t* slot_idx,
+                                       int h0_from_pool, int H, int dk, int dv, float scale,
+                                       int use_qk_l2norm, void* o, void* workspace,
+                                       size_t workspace_bytes, hipStream_t stream) {
+    kda::FrontArgs fa;
+    if (const int st = front_args(front, fa); st != KDA_OK) return st;
+    if (checked_mul(checked_mul(checked_mul(num_slots, H), 3), 2 * dk + dv) < 0)
+        return KDA_ERR_INVALID_ARG;
+    return chunk_prefill_impl(q, k, v, dtype, g, beta, cu_seqlens, num_seqs, total_tokens,
+                              state_pool, num_slots, slot_idx, h0_from_pool, H, dk, dv, scale,
+                              use_qk_l2norm, o, workspace, workspace_bytes, 0, nullptr, 0, false,
+                              stream, &fa);
 }
 
 KDA_EXPORT int kda_chunk_prefill_snapshots(

@@ -55,6 +55,7 @@
 // its terms.  Every accumulation, the cumsum and the triangular solve are fp32.
 #include <atomic>
 #include <mutex>
+#include <type_traits>
 
 #include "kda.h"
 #include "kda_device.hpp"
@@ -375,6 +376,137 @@ __device__ __forceinline__ void intra_fetch(IntraIn<DK, DV, TIn>& X, const Prefi
             X.g[j][m] = __builtin_bit_cast(
                 f32x4, __builtin_amdgcn_raw_buffer_load_b128(rg, (t * H * DK + GW * (4 * j + q) + 4 * m) * 4, 0, 0));
     X.beta = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rb, t * H * 4, 0, 0));
+}
+
+// ---------------------------------------------------------------------------
+// Input front (kda_chunk_prefill_front): before phase 1, the item's raw q, k, v are convolved
+// along the tokens of their sequence (causal depthwise, width W <= 4:
+// y_t[c] = sum_j w[c][j] x_{t-(W-1)+j}[c]), optionally passed through SiLU, and the raw
+// gates and beta values processed (g = -a_h softplus(z), beta = sigmoid(b)), all in the
+// item's registers.  Lane (r, q) of wave w holds token 16 w + r, so the input d tokens back
+// is lane r - d of the same wave (a DPP row shift keeps the channels) or, for the wave's
+// first d tokens, one of the previous wave's last three tokens, which each wave leaves in
+// LDS; wave 0 fetches the three tokens before the chunk (the previous chunk's, or at the
+// sequence start the slot's convolution state, or zeros).  Rows past the chunk's end are
+// zeroed, gates included, as the plain prefill reads them.  With bf16 inputs the convolved
+// q, k, v are rounded to bf16 (the granules the phases read).
+// ---------------------------------------------------------------------------
+template <int DK, int DV, class TIn>
+struct FrontTails {
+    static constexpr int CW = 2 * DK + DV;                        // channels q | k | v
+    static constexpr size_t BYTES = 5ull * 3 * CW * Geo<TIn>::E;  // [slot 5][row 3][CW]
+    static_assert(BYTES <= IntraPlan<DK, DV, TIn>::R1, "front tails exceed region R1");
+};
+
+template <int D>
+__device__ __forceinline__ u32x4 row_shift_gran(u32x4 x) {
+    u32x4 y;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) y[i] = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x[i]), 0x110 + D, 0xf, 0xf, false));
+    return y;
+}
+
+template <int DK, int DV, class TIn>
+__device__ __forceinline__ void intra_front(IntraIn<DK, DV, TIn>& X, char* smem, const PrefillArgs& a, int t0, int L,
+                                            int bos, int seq, int h, int wave, int lane) {
+    using P = IntraPlan<DK, DV, TIn>;
+    using FT = FrontTails<DK, DV, TIn>;
+    constexpr int E = P::E, GW = P::GW, NGK = P::NGK, NGV = P::NGV, CW = FT::CW;
+    constexpr TIn tag{};
+    const FrontArgs& f = a.front;
+    const int W = f.conv_width, H = a.H;
+    const int r = lane & 15, q = lane >> 4, t = 16 * wave + r;
+    char* tails = smem + P::O1;
+    auto tail_at = [&](int slot, int row, int chan) { return tails + ((slot * 3 + row) * CW + chan) * E; };
+
+    if (W > 1) {
+        // this wave's last three tokens -> tail slot wave + 1
+        if (r >= 13) {
+#pragma unroll
+            for (int j = 0; j < NGK; ++j) {
+                *reinterpret_cast<u32x4*>(tail_at(wave + 1, r - 13, GW * (4 * j + q))) = X.q[j];
+                *reinterpret_cast<u32x4*>(tail_at(wave + 1, r - 13, DK + GW * (4 * j + q))) = X.k[j];
+            }
+#pragma unroll
+            for (int j = 0; j < NGV; ++j)
+                *reinterpret_cast<u32x4*>(tail_at(wave + 1, r - 13, 2 * DK + GW * (4 * j + q))) = X.v[j];
+        }
+        // the three tokens before the chunk -> slot 0
+        if (wave == 0 && r >= 13) {
+            const int u = t0 - 16 + r;  // its token index
+            const bool in_seq = u >= bos;
+            const int crow = u - bos + W - 1;  // its row of the convolution state (if >= 0)
+            const bool from_state = !in_seq && a.h0_from_pool && crow >= 0;
+            const char* src = nullptr;
+            if (from_state)
+                src = static_cast<const char*>(f.conv_state) +
+                      ((static_cast<int64_t>(a.slot_idx[seq]) * H + h) * (W - 1) + crow) * CW * E;
+            auto fetch = [&](const void* x, int D, int off, int chan) -> u32x4 {
+                if (in_seq)
+                    return *reinterpret_cast<const u32x4*>(static_cast<const char*>(x) +
+                                                           ((static_cast<int64_t>(u) * H + h) * D + chan) * E);
+                if (from_state) return *reinterpret_cast<const u32x4*>(src + (off + chan) * E);
+                return u32x4{0u, 0u, 0u, 0u};
+            };
+#pragma unroll
+            for (int j = 0; j < NGK; ++j) {
+                const int c = GW * (4 * j + q);
+                *reinterpret_cast<u32x4*>(tail_at(0, r - 13, c)) = fetch(a.q, DK, 0, c);
+                *reinterpret_cast<u32x4*>(tail_at(0, r - 13, DK + c)) = fetch(a.k, DK, DK, c);
+            }
+#pragma unroll
+            for (int j = 0; j < NGV; ++j) {
+                const int c = GW * (4 * j + q);
+                *reinterpret_cast<u32x4*>(tail_at(0, r - 13, 2 * DK + c)) = fetch(a.v, DV, 2 * DK, c);
+            }
+        }
+        lds_barrier();
+    }
+    // one granule: channels c0 .. c0 + GW - 1 of the block at channel offset off (q | k | v)
+    auto conv = [&](u32x4& G, const float* w, int D, int off, int c0) {
+        const float* wc = w + (static_cast<int64_t>(h) * D + c0) * W;
+        float x[GW], acc[GW];
+        gran_to_f32(G, x, tag);
+#pragma unroll
+        for (int e = 0; e < GW; ++e) acc[e] = wc[e * W + W - 1] * x[e];
+        auto tap = [&](auto dtag) {
+            constexpr int d = decltype(dtag)::value;
+            if (d < W) {
+                const u32x4 sh = row_shift_gran<d>(G);
+                // lanes r < d: token 16 wave + r - d, row 3 + r - d of the previous wave's tail
+                const u32x4 tv = *reinterpret_cast<const u32x4*>(tail_at(wave, 3 + min(r, d - 1) - d, off + c0));
+                const u32x4 xv = r >= d ? sh : tv;
+                float xd[GW];
+                gran_to_f32(xv, xd, tag);
+#pragma unroll
+                for (int e = 0; e < GW; ++e) acc[e] = fmaf(wc[e * W + W - 1 - d], xd[e], acc[e]);
+            }
+        };
+        tap(std::integral_constant<int, 1>{});
+        tap(std::integral_constant<int, 2>{});
+        tap(std::integral_constant<int, 3>{});
+#pragma unroll
+        for (int e = 0; e < GW; ++e) {
+            const float y = f.conv_silu ? front_silu(acc[e]) : acc[e];
+            acc[e] = t < L ? y : 0.f;
+        }
+        G = f32_to_gran(acc, tag);
+    };
+#pragma unroll
+    for (int j = 0; j < NGK; ++j) {
+        conv(X.q[j], f.conv_q, DK, 0, GW * (4 * j + q));
+        conv(X.k[j], f.conv_k, DK, DK, GW * (4 * j + q));
+    }
+#pragma unroll
+    for (int j = 0; j < NGV; ++j) conv(X.v[j], f.conv_v, DV, 2 * DK, GW * (4 * j + q));
+    const float gs = f.gate_scale[h];
+#pragma unroll
+    for (int j = 0; j < NGK; ++j)
+#pragma unroll
+        for (int m = 0; m < GW / 4; ++m)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) X.g[j][m][e] = t < L ? -gs * front_softplus(X.g[j][m][e]) : 0.f;
+    X.beta = t < L ? front_sigmoid(X.beta) : 0.f;
 }
 
 template <int DK, int DV, class TIn>
@@ -810,7 +942,7 @@ __device__ __forceinline__ void intra_compute(const IntraIn<DK, DV, TIn>& X, cha
 // workgroups share a CU (bf16), so one computes while the other waits for its inputs.
 // The table entry of the next item is read with a vector load one item ahead, so the
 // LDS barriers (which wait for scalar loads) never wait for it.
-template <int DK, int DV, class TIn>
+template <int DK, int DV, class TIn, bool FRONT>
 __global__ __launch_bounds__(kThreads, 2) void chunk_intra_kernel(PrefillArgs a) {
     using P = IntraPlan<DK, DV, TIn>;
     static_assert(P::fits, "LDS plan exceeds 160 KiB");
@@ -853,7 +985,7 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_intra_kernel(PrefillArgs a)
     const int total = (inl ? m_coff[ns] : chunk_off[ns]) * H;
     for (int item = blockIdx.x; item < total; item += stride) {
         const int c = item / H;
-        int t0, L;
+        int t0, L, seq;
         if (inl) {
             // the sequence lo with m_coff[lo] <= c < m_coff[lo + 1] (it has chunks)
             int lo = 0, hi = ns;
@@ -866,8 +998,10 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_intra_kernel(PrefillArgs a)
             }
             t0 = __builtin_amdgcn_readfirstlane(m_cu[lo] + kChunk * (c - m_coff[lo]));
             L = __builtin_amdgcn_readfirstlane(min(kChunk, m_cu[lo + 1] - t0));
+            seq = lo;
         } else {
             const int4 e = table[c];
+            seq = e.x;
             t0 = e.y;
             L = e.z;
         }
@@ -879,6 +1013,8 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_intra_kernel(PrefillArgs a)
         asm volatile("" : "+s"(wv));
         IntraIn<DK, DV, TIn> X;
         intra_fetch(X, a, t0, L, item % H, wv, ln);
+        if constexpr (FRONT)
+            intra_front(X, smem, a, t0, L, inl ? m_cu[seq] : a.cu_seqlens[seq], seq, item % H, wv, ln);
         intra_compute(X, smem, a, recs + ws.rec_bytes * static_cast<size_t>(item), ws, wv, ln, tid);
     }
 }
@@ -1037,6 +1173,39 @@ __device__ __forceinline__ void store_o4(__amdgpu_buffer_rsrc_t orsrc, int trow,
                                          F32) {
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) store_out(orsrc, (trow + rr) * orow + col, ov[rr], F32{});
+}
+
+// Input front: the slot's convolution state after sequence seq (tokens bos .. eos - 1): its
+// last W - 1 inputs, earlier state rows (or zeros without h0_from_pool) where the sequence is
+// shorter.  Every read precedes every write (a barrier between), since the rows move.
+template <int DK, int DV, class TIn>
+__device__ void front_state_out(const PrefillArgs& a, int seq, int h, int bos, int eos, int tid) {
+    using elem = typename Geo<TIn>::elem;
+    constexpr int CW = 2 * DK + DV, NV = (3 * CW + kSegThreads - 1) / kSegThreads;
+    const int W = a.front.conv_width, H = a.H;
+    elem* cs = static_cast<elem*>(a.front.conv_state) + (static_cast<int64_t>(a.slot_idx[seq]) * H + h) * (W - 1) * CW;
+    elem keep[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        const int idx = tid + i * kSegThreads;
+        keep[i] = 0;
+        if (idx < (W - 1) * CW) {
+            const int r = idx / CW, c = idx % CW, u = eos - (W - 1) + r;
+            const int64_t tk = static_cast<int64_t>(u) * H + h;
+            if (u >= bos)
+                keep[i] = c < DK       ? static_cast<const elem*>(a.q)[tk * DK + c]
+                          : c < 2 * DK ? static_cast<const elem*>(a.k)[tk * DK + c - DK]
+                                       : static_cast<const elem*>(a.v)[tk * DV + c - 2 * DK];
+            else if (a.h0_from_pool)
+                keep[i] = cs[(u - bos + W - 1) * CW + c];
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        const int idx = tid + i * kSegThreads;
+        if (idx < (W - 1) * CW) cs[idx] = keep[i];
+    }
 }
 
 // One chunk on the segment state.
@@ -1230,6 +1399,7 @@ __global__ __launch_bounds__(kSegThreads) void seg_carry_kernel(PrefillArgs a) {
 #pragma unroll
                 for (int rr = 0; rr < 4; ++rr) Sg[(16 * cb + q4 + rr) * DV + 16 * (jb0 + j) + r] = S[j][rr];
             if (a.snap_every > 0) snapshot(eos - bos);  // a snapshot at the full length
+            if (a.front.gate_scale && a.front.conv_width > 1) front_state_out<DK, DV, TIn>(a, seq, h, bos, eos, tid);
         }
     } else {
         float* Sl = reinterpret_cast<float*>(blk + ws.s_loc);
@@ -1275,12 +1445,20 @@ __device__ __forceinline__ void scan_group(const PrefillArgs& a, int group, int 
         for (int rr = 0; rr < 4; ++rr)
             X[i][rr] = a.h0_from_pool ? Sg[(16 * (RW * wave + i) + q4 + rr) * DV + r] : 0.f;
     if (nseg == 0) {
-        // no tokens: the final state is the initial state (zero unless read from the slot)
-        if (!a.h0_from_pool)
+        // no tokens: the final state is the initial state (zero unless read from the slot),
+        // and so is the input front's convolution state
+        if (!a.h0_from_pool) {
 #pragma unroll
             for (int i = 0; i < RW; ++i)
 #pragma unroll
                 for (int rr = 0; rr < 4; ++rr) Sg[(16 * (RW * wave + i) + q4 + rr) * DV + r] = 0.f;
+            if (a.front.gate_scale && a.front.conv_width > 1 && tile == 0) {
+                const int n = (a.front.conv_width - 1) * (2 * DK + DV) * E;  // bytes
+                char* cs = static_cast<char*>(a.front.conv_state) +
+                           (static_cast<int64_t>(a.slot_idx[seq]) * H + h) * n;
+                for (int i = 64 * wave + lane; i < n / 4; i += 64 * (DK / 16)) reinterpret_cast<uint32_t*>(cs)[i] = 0u;
+            }
+        }
         return;
     }
     // Phi_k and S_loc(k) rows of this wave, loaded one segment ahead of their use
@@ -1395,7 +1573,10 @@ hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t stream) {
         if (items > 0) {
             const int slots = 2 * device_cu_count();
             const int grid = static_cast<int>(items < slots ? items : slots);
-            hipLaunchKernelGGL((chunk_intra_kernel<DK, DV, TIn>), dim3(grid), dim3(kThreads), 0, stream, a);
+            if (a.front.gate_scale)
+                hipLaunchKernelGGL((chunk_intra_kernel<DK, DV, TIn, true>), dim3(grid), dim3(kThreads), 0, stream, a);
+            else
+                hipLaunchKernelGGL((chunk_intra_kernel<DK, DV, TIn, false>), dim3(grid), dim3(kThreads), 0, stream, a);
             constexpr int LS = local_split<DK, DV, TIn>();
             const int64_t pairs = ws.max_segs * a.H;
             const dim3 lgrid(static_cast<unsigned>(

@@ -239,6 +239,48 @@ def chunk_prefill(q, k, v, g, beta, cu_seqlens, state_pool, slot_idx, *, h0_from
     return o
 
 
+def chunk_prefill_front(q, k, v, gate, beta, cu_seqlens, state_pool, slot_idx, *, gate_scale, conv_q,
+                        conv_k, conv_v, conv_state=None, conv_silu=False, h0_from_pool=True, o=None,
+                        workspace=None, scale=None, use_qk_l2norm=True):
+    """Varlen chunked prefill with the input front fused in (kda_chunk_prefill_front).
+
+    q, k [T_total, H, dk], v [T_total, H, dv]: raw convolution inputs; gate [T_total, H, dk]
+    fp32 raw gates z; beta [T_total, H] fp32 raw values; the front's tensors as
+    decode_step_front (conv_state [num_slots, H, W - 1, 2 dk + dv] read when h0_from_pool and
+    written back per sequence); the rest as chunk_prefill.  Returns o.
+    """
+    Tt, H, dk = q.shape
+    dv = v.shape[-1]
+    ns = cu_seqlens.shape[0] - 1
+    _need(q.dtype in _DTYPES and k.dtype == q.dtype and v.dtype == q.dtype, "q/k/v dtype")
+    _need(gate.dtype == torch.float32 and beta.dtype == torch.float32, "gate and beta must be fp32")
+    _need(k.shape == q.shape and gate.shape == q.shape and v.shape == (Tt, H, dv), "q/k/v/gate shape")
+    _need(beta.shape == (Tt, H), "beta shape")
+    _need(cu_seqlens.dtype == torch.int32 and slot_idx.dtype == torch.int32, "index dtype")
+    _need(slot_idx.shape == (ns,), "slot_idx shape")
+    _need(state_pool.dim() == 4 and state_pool.shape[1:] == (H, dk, dv), "state_pool shape")
+    front = _front(gate_scale, conv_q, conv_k, conv_v, conv_state, conv_silu, H, dk, dv,
+                   state_pool.shape[0], q.dtype)
+    if o is None:
+        o = torch.empty(Tt, H, dv, dtype=q.dtype, device=q.device)
+    if debug_validate_enabled():
+        validate_cu_seqlens(cu_seqlens, Tt)
+        validate_slots(slot_idx, state_pool.shape[0], allow_skip=False)
+    need = chunk_prefill_workspace_size(ns, Tt, H, dk, dv, q.dtype)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _contig(q, k, v, gate, beta, cu_seqlens, state_pool, slot_idx, o, workspace)
+    if scale is None:
+        scale = dk ** -0.5
+    st = _lib.load().kda_chunk_prefill_front(
+        _ptr(q), _ptr(k), _ptr(v), _DTYPES[q.dtype], _ptr(gate), _ptr(beta), ctypes.byref(front),
+        _ptr(cu_seqlens), ns, Tt, _ptr(state_pool), state_pool.shape[0], _ptr(slot_idx),
+        int(bool(h0_from_pool)), H, dk, dv, float(scale), int(bool(use_qk_l2norm)), _ptr(o),
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(q))
+    _lib.check("kda_chunk_prefill_front", st)
+    return o
+
+
 def chunk_prefill_noalloc(q, k, v, g, beta, cu_seqlens, state_pool, slot_idx, *, h0_from_pool=True,
                           o=None, scale=None, use_qk_l2norm=True):
     """Varlen chunked prefill on the library's static workspace (kda_chunk_prefill_noalloc):

@@ -161,6 +161,20 @@ def decode_front(seed=0, N=None, T=None, H=None, dk=None, dv=None, num_slots=Non
     return x
 
 
+def prefill_front(seed=0, seqlens=(8192,), H=None, dk=None, dv=None, num_slots=None, h0_std=None,
+                  width=4, dtype=torch.bfloat16):
+    """Prefill inputs for the front: prefill() with raw gates z ~ N(0, 1) in g's place and raw
+    beta values b ~ N(0, 1) (the draws the workloads pass through -0.1 softplus and sigmoid),
+    plus front_params() for the pool's slots."""
+    x = prefill(seed, seqlens=seqlens, H=H, dk=dk, dv=dv, num_slots=num_slots, h0_std=h0_std, dtype=dtype)
+    gen = _gen(seed + 1)
+    T, H, dk = x["q"].shape
+    x["g"] = _normal(gen, (T, H, dk))
+    x["beta"] = _normal(gen, (T, H))
+    x.update(front_params(seed + 2, H, dk, x["v"].shape[-1], x["pool"].shape[0], width, dtype))
+    return x
+
+
 def prefill_long(seed=0, **kw):
     """Long-context varlen prefill: 4 sequences (100000, 16384, 8192, 3500), H=16,
     initial states from 4 distinct slots of a 512-slot pool ~ N(0, 0.05^2)."""

@@ -125,3 +125,105 @@ def test_two_calls_equal_one():
     assert rel_l2(f64(o2), f64(o_all)) <= 1e-6
     assert rel_l2(f64(pool), f64(pool_all)) <= 1e-6
     assert torch.equal(cs.cpu(), cs_all.cpu())
+
+
+# ---- prefill -------------------------------------------------------------------------------
+
+def run_prefill_front(y, dev, h0_from_pool=True, silu=True):
+    pool = y["pool"].to(dev)
+    cs = y["conv_state"].to(dev) if y["conv_q"].shape[-1] > 1 else None
+    o = kda.chunk_prefill_front(*(y[n].to(dev) for n in ("q", "k", "v", "g", "beta")),
+                                y["cu_seqlens"].to(dev), pool, y["slot_idx"].to(dev), conv_state=cs,
+                                conv_silu=silu, h0_from_pool=h0_from_pool,
+                                **{n: y[n].to(dev) for n in FRONT})
+    torch.cuda.synchronize()
+    return o, pool, cs
+
+
+def oracle_prefill_front(y, h0_from_pool=True, silu=True):
+    sl = y["slot_idx"].long()
+    W_ = y["conv_q"].shape[-1]
+    st0 = f64(y["conv_state"][sl]) if (W_ > 1 and h0_from_pool) else None
+    q, k, v, g, beta, st = F.front(*(f64(y[n]) for n in ("q", "k", "v", "g", "beta")),
+                                   y["cu_seqlens"].numpy(), f64(y["gate_scale"]), f64(y["conv_q"]),
+                                   f64(y["conv_k"]), f64(y["conv_v"]), st0, use_silu=silu)
+    h0 = f64(y["pool"][sl]) if h0_from_pool else None
+    o, h, _ = O.recurrent(q, k, v, g, beta, y["cu_seqlens"].numpy(), h0=h0)
+    return o, h, st
+
+
+def check_prefill(y, dev, tol, label, h0_from_pool=True, silu=True):
+    announce(label)
+    o, pool, cs = run_prefill_front(y, dev, h0_from_pool, silu)
+    o_ref, h_ref, st_ref = oracle_prefill_front(y, h0_from_pool, silu)
+    sl = y["slot_idx"].long()
+    cu = y["cu_seqlens"]
+    from tests._util import worst_seq_head
+    h = f64(pool.cpu()[sl])
+    e = dict(o=rel_l2(f64(o), o_ref), o_worst=worst_seq_head(f64(o), o_ref, cu), h=rel_l2(h, h_ref),
+             h_worst=worst_state(h, h_ref))
+    announce("%s rel-L2 o %.3g (worst seq/head %.3g), state %.3g (worst %.3g)"
+             % (label, e["o"], e["o_worst"], e["h"], e["h_worst"]))
+    for name, val in e.items():
+        assert val <= tol, (name, val, tol)
+    if cs is not None:
+        got = cs.cpu()
+        want = y["conv_state"].clone()
+        want[sl] = torch.as_tensor(st_ref).to(want.dtype)
+        assert torch.equal(got, want), "convolution state"
+
+
+@pytest.mark.parametrize("dk,dv", [(128, 128), (64, 64), (128, 64), (64, 128)])
+def test_prefill_bf16_varlen(dk, dv):
+    """Ragged varlen batch: sequences of 1, 2, 3 and 4 tokens (shorter than and equal to the
+    width), chunk tails, an empty sequence, h0 and convolution states from the slots."""
+    dev = need_gpu()
+    y = W.prefill_front(seed=50, seqlens=(1, 2, 3, 4, 63, 64, 65, 0, 200, 777), H=3, dk=dk, dv=dv,
+                        num_slots=12, h0_std=0.05)
+    check_prefill(y, dev, 1e-2, "front prefill bf16 varlen dk=%d dv=%d" % (dk, dv))
+
+
+@pytest.mark.parametrize("dk,dv", [(64, 64), (128, 128)])
+@pytest.mark.parametrize("width,silu,h0", [(4, True, True), (2, False, True), (1, True, True), (3, True, False)])
+def test_prefill_fp32(dk, dv, width, silu, h0):
+    """fp32 through several segments (sequences longer than 1,024 tokens), every width, with and
+    without the slots' initial states; <= 1e-4."""
+    dev = need_gpu()
+    y = W.prefill_front(seed=51 + width, seqlens=(2100, 3, 0, 130), H=2, dk=dk, dv=dv, num_slots=5,
+                        h0_std=0.05, width=width, dtype=torch.float32)
+    check_prefill(y, dev, 1e-4, "front prefill fp32 dk=%d dv=%d W=%d silu=%d h0=%d" % (dk, dv, width, silu, h0),
+                  h0_from_pool=h0, silu=silu)
+
+
+def test_prefill_workload_shape():
+    """The chunked prefill workload's shape (T = 8192, H = 32, d = 128, bf16, zero initial
+    states), width 4 with SiLU, every head against the oracle."""
+    dev = need_gpu()
+    y = W.prefill_front(seed=52, seqlens=(8192,), H=32, dk=128, dv=128)
+    check_prefill(y, dev, 1e-2, "front prefill bf16 T8192 H32", h0_from_pool=False)
+
+
+def test_prefill_then_decode_continues_the_sequence():
+    """A prefill of 70 tokens then a 3-token decode step on the same slots equals one prefill
+    of 73 tokens (outputs of the last 3 tokens, recurrent and convolution states), fp32."""
+    dev = need_gpu()
+    y = W.prefill_front(seed=53, seqlens=(73, 73), H=2, dk=64, dv=64, num_slots=3, h0_std=0.05,
+                        dtype=torch.float32)
+    o_all, pool_all, cs_all = run_prefill_front(y, dev)
+    # first 70 tokens of each sequence through the prefill, the last 3 through the decode
+    idx = torch.cat([torch.arange(0, 70), torch.arange(73, 143)])
+    tail = torch.cat([torch.arange(70, 73), torch.arange(143, 146)])
+    y1 = dict(y)
+    for n in ("q", "k", "v", "g", "beta"):
+        y1[n] = y[n][idx].contiguous()
+    y1["cu_seqlens"] = torch.tensor([0, 70, 140], dtype=torch.int32)
+    _, pool, cs = run_prefill_front(y1, dev)
+    shp = lambda t: t[tail].reshape((2, 3) + tuple(t.shape[1:])).contiguous().to(dev)
+    o_dec = kda.decode_step_front(*(shp(y[n]) for n in ("q", "k", "v", "g", "beta")), pool,
+                                  y["slot_idx"].to(dev), conv_state=cs, conv_silu=True,
+                                  **{n: y[n].to(dev) for n in FRONT})
+    torch.cuda.synchronize()
+    o_ref = o_all[tail.to(dev)].reshape(2, 3, *o_all.shape[1:])
+    assert rel_l2(f64(o_dec), f64(o_ref)) <= 1e-5
+    assert rel_l2(f64(pool), f64(pool_all)) <= 1e-5
+    assert torch.equal(cs.cpu(), cs_all.cpu())
