@@ -53,6 +53,15 @@ def prefill_bytes_per_token_head(dk, dv, io_bytes):
     return (2 * dk + dv) * io_bytes + dk * 4 + 4 + dv * io_bytes
 
 
+def front_decode_bytes_per_update(dk, dv, width, io_bytes, sequences):
+    """A decode update with the input front: decode_bytes_per_update (the raw q, k, v, gate and
+    beta in place of the processed ones, same sizes), the slot's convolution state read and
+    written ((width - 1) rows of 2 dk + dv channels, io dtype), and the head's fp32 convolution
+    weights (width taps per channel) read once per launch, shared by its `sequences` updates."""
+    return (decode_bytes_per_update(dk, dv, io_bytes) + 2 * (width - 1) * (2 * dk + dv) * io_bytes
+            + (2 * dk + dv) * width * 4 / sequences)
+
+
 def prefill_flops_per_token_head(dk, dv, C=64):
     """Algorithmic flops per (token, head) of the 64-token chunk form as the kernels compute it,
     counting every intra-chunk product as a dense C x C tile: A and P (2 C^2 dk each), W = T KG
@@ -341,6 +350,115 @@ def bench_verify_replay(args, dev, log):
             "hbm_frac": gbs / HBM_PEAK_GBS}
 
 
+def bench_front(args, dev, log, prefill_us):
+    """The input front fused into the kernels (kda_decode_step_front, kda_chunk_prefill_front:
+    width-4 convolution with SiLU, gate and beta processing, the convolution state kept in the
+    slots).  Decode on the decode workload's pool and sequences (8 disjoint slot sets in turn,
+    graph replay), beside the same front run as separate torch operators followed by
+    kda_decode_step (the unfused pipeline); prefill on the T = 8192 x H = 32 workload beside the
+    plain prefill's graph time."""
+    import torch
+    import torch.nn.functional as Fn
+
+    import kda_gated_delta_rule_amd as kda
+    import kda_workloads as W
+
+    cfg = W.DECODE
+    x = W.decode_front(seed=0)
+    N, H, dk, dv, ns = cfg["N"], cfg["H"], cfg["dk"], cfg["dv"], cfg["num_slots"]
+    width = x["conv_q"].shape[-1]
+    pool = x["pool"].to(dev)
+    cs = x["conv_state"].to(dev)
+    q, k, v, z, b = (x[n].to(dev) for n in ("q", "k", "v", "g", "beta"))
+    fr = {n: x[n].to(dev) for n in ("gate_scale", "conv_q", "conv_k", "conv_v")}
+    o = torch.empty_like(q)
+    rest = [s for s in torch.randperm(ns, generator=torch.Generator().manual_seed(1)).tolist()
+            if s not in set(x["slot_idx"].tolist())]
+    sets = [x["slot_idx"]] + [torch.tensor(rest[i * N:(i + 1) * N], dtype=torch.int32)
+                              for i in range(ns // N - 1)]
+    sets = [st.to(dev) for st in sets]
+    wcat = torch.cat([fr["conv_q"], fr["conv_k"], fr["conv_v"]], dim=1).permute(0, 2, 1).contiguous()
+
+    def fused(i):
+        kda.decode_step_front(q, k, v, z, b, pool, sets[i % len(sets)], conv_state=cs, conv_silu=True,
+                              o=o, **fr)
+
+    def unfused(i):
+        sl = sets[i % len(sets)]
+        sll = sl.long()
+        X = torch.cat([cs[sll], torch.cat([q, k, v], dim=-1).permute(0, 2, 1, 3)], dim=2)  # [N, H, W, C]
+        y = Fn.silu((X.float() * wcat[None]).sum(2)).to(q.dtype)  # [N, H, C]
+        cs[sll] = X[:, :, 1:]
+        y = y[:, None]
+        g = -fr["gate_scale"][None, None, :, None] * Fn.softplus(z)
+        kda.decode_step(y[..., :dk].contiguous(), y[..., dk:2 * dk].contiguous(), y[..., 2 * dk:].contiguous(),
+                        g, torch.sigmoid(b), pool, sl, o=o)
+
+    iters = max(len(sets), args.steps // 4)
+
+    def graph_time(step):
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step(0)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr):
+            for i in range(iters):
+                step(i)
+        gr.replay()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        ev0.record()
+        gr.replay()
+        ev1.record()
+        torch.cuda.synchronize()
+        return ev0.elapsed_time(ev1) / 1e3 / iters
+
+    per = graph_time(fused)
+    per_unfused = graph_time(unfused)
+    bpu = front_decode_bytes_per_update(dk, dv, width, 2, N)
+    gbs = N * H * bpu / per / 1e9
+    log("front decode: %.2f us/call fused, %.2f us unfused (torch front + decode_step), %.1f GB/s (%.1f%% HBM)"
+        % (per * 1e6, per_unfused * 1e6, gbs, 100 * gbs / HBM_PEAK_GBS))
+    dec = {"workload": cfg["name"] + "_front_w%d_silu" % width, "us_per_call": per * 1e6,
+           "timing": "graph replay of %d calls, %d disjoint slot sets in turn" % (iters, len(sets)),
+           "unfused_us_per_call": per_unfused * 1e6,
+           "unfused": "the front as torch operators (gather, convolution, SiLU, softplus, sigmoid, "
+                      "state scatter) then kda_decode_step",
+           "updates_per_s": N * H / per, "bytes_per_update": bpu, "achieved_GBs": gbs,
+           "hbm_frac": gbs / HBM_PEAK_GBS}
+    del pool, cs
+
+    y = W.prefill_front(seed=0)
+    Tt, H, dk = y["q"].shape
+    dv = y["v"].shape[-1]
+    ins = two_input_copies(y, dev)
+    cu = y["cu_seqlens"].to(dev)
+    pool, slots = y["pool"].to(dev), y["slot_idx"].to(dev)
+    cs = y["conv_state"].to(dev)
+    fr = {n: y[n].to(dev) for n in ("gate_scale", "conv_q", "conv_k", "conv_v")}
+    o = torch.empty_like(ins[0][2])
+    ws = torch.empty(kda.chunk_prefill_workspace_size(1, Tt, H, dk, dv), dtype=torch.uint8, device=dev)
+
+    def pstep(i):
+        qq, kk, vv, zz, bb = ins[i % 2]
+        kda.chunk_prefill_front(qq, kk, vv, zz, bb, cu, pool, slots, conv_state=cs, conv_silu=True,
+                                h0_from_pool=False, o=o, workspace=ws, **fr)
+
+    iters = max(5, args.steps // 10)
+    pper = graph_time(pstep)
+    th = Tt * H
+    byts = th * prefill_bytes_per_token_head(dk, dv, 2)
+    log("front prefill %s: %.1f us/call (graph), plain prefill %.1f us" % (W.PREFILL["name"], pper * 1e6, prefill_us))
+    pre = {"workload": W.PREFILL["name"] + "_front_w%d_silu" % width, "us_per_call": pper * 1e6,
+           "timing": "graph replay of %d calls, two input copies in turn" % iters,
+           "plain_us_per_call": prefill_us, "overhead": pper * 1e6 / prefill_us - 1.0,
+           "tokens_per_s": Tt / pper, "hbm_frac": byts / pper / 1e9 / HBM_PEAK_GBS}
+    return {"decode": dec, "prefill": pre}
+
+
 def two_input_copies(y, dev):
     """The prefill inputs (q, k, v, g, beta) twice on the device: consecutive calls alternate
     between the copies, so no call finds its inputs in the Infinity Cache from the call before."""
@@ -600,6 +718,8 @@ def main():
                          "prints their figures without the headline metric")
     ap.add_argument("--backward-only", action="store_true",
                     help="measure only the chunked backward (for counter and trace runs)")
+    ap.add_argument("--front-only", action="store_true",
+                    help="measure only the fused input front (decode and prefill)")
     ap.add_argument("--quiet", action="store_true")
     args = ap.parse_args()
 
@@ -633,6 +753,12 @@ def main():
         print(json.dumps({"mode": "prefill-only", "extra": extra}))
         return
 
+    if args.front_only:
+        pre = bench_prefill(args, dev, log, "prefill")
+        print(json.dumps({"mode": "front-only", "extra": {"prefill": pre,
+                                                          "front": bench_front(args, dev, log, pre["us_per_call"])}}))
+        return
+
     if args.backward_only:
         print(json.dumps({"mode": "backward-only", "extra": {"backward": bench_backward(args, dev, log)}}))
         return
@@ -655,6 +781,7 @@ def main():
         extra["prefill_snapshots"] = bench_prefill_snapshots(args, dev, log,
                                                              extra["prefill"]["us_per_call_eager"])
         extra["backward"] = bench_backward(args, dev, log)
+        extra["front"] = bench_front(args, dev, log, extra["prefill"]["us_per_call"])
     cpu = None if args.decode_only else cpu_baseline(dec["inputs"], log)
 
     import kda_workloads as W

@@ -292,11 +292,12 @@ typedef struct {
  * step run in one kernel per (sequence, head).  q, k, v [N, T, H, *] are the raw inputs of the
  * convolution, g [N, T, H, dk] the raw gates z, beta [N, T, H] the raw b (see kda_front);
  * the other arguments and the results are those of kda_decode_step with records = NULL (the
- * front has no verify mode).  T >= 1 tokens are applied in order.  A skipped sequence
+ * front has no verify mode).  1 <= T <= 8 tokens are applied in order (longer inputs take the
+ * prefill).  A skipped sequence
  * (negative slot) keeps its convolution state.
  * Errors: as kda_decode_step; front NULL, a null or misaligned gate_scale or conv weight,
- * conv_width outside 1..4, conv_silu not 0 or 1, or (conv_width > 1) a null or misaligned
- * conv_state give KDA_ERR_INVALID_ARG.
+ * conv_width outside 1..4, conv_silu not 0 or 1, (conv_width > 1) a null or misaligned
+ * conv_state, or T > 8 give KDA_ERR_INVALID_ARG.
  */
 int kda_decode_step_front(const void* q, const void* k, const void* v, int dtype, const float* g,
                           const float* beta, const kda_front* front, float* state_pool,

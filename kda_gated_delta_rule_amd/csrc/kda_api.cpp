@@ -86,6 +86,7 @@ KDA_EXPORT int kda_decode_step_front(const void* q, const void* k, const void* v
     const void* ptrs[] = {q, k, v, g, beta, state_pool, slot_idx, o};
     for (const void* p : ptrs)
         if (!p || !aligned16(p)) return KDA_ERR_INVALID_ARG;
+    if (T > 8) return KDA_ERR_INVALID_ARG;  // the front's tokens form one block of at most 8
     kda::FrontArgs fa;
     if (const int st = front_args(front, fa); st != KDA_OK) return st;
     const int64_t tokens = checked_mul(checked_mul(N, T), H);

@@ -40,7 +40,7 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
-constexpr int kFrontTB = kWaves;  // tokens per LDS block with the input front
+constexpr int kFrontTB = 8;  // with the input front: at most 8 tokens, prepared as one block
 constexpr float kNormEps = 1e-6f;
 constexpr int kBufFlags = 0x00020000;  // raw buffer resource word 3 (gfx9 family)
 constexpr int kNonTemporal = 2;        // buffer access cache policy: streaming (nt)
@@ -221,7 +221,7 @@ __device__ __forceinline__ void prep_token(const DecodeArgs& a, TokenLds<DK, BV,
 }
 
 template <int DK, int DV, int BV, int TB, class TIn, bool VERIFY, bool FRONT = false>
-__global__ __launch_bounds__(kThreads, FRONT ? 2 : 5) void decode_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(kThreads, FRONT ? 4 : 5) void decode_kernel(DecodeArgs a) {
     using C = Tile<DK, DV, BV>;
     __shared__ __attribute__((aligned(16))) TokenLds<DK, BV, TB> L;  // read as float4
     __shared__ float4 red[2][kWaves][kWave][2];
@@ -245,7 +245,10 @@ __global__ __launch_bounds__(kThreads, FRONT ? 2 : 5) void decode_kernel(DecodeA
     float* S = a.pool + (static_cast<int64_t>(slot) * a.H + h) * (DK * DV);
 
     float4 s[C::RPT];
-    for (int tb = 0; tb < a.T; tb += TB) {
+    // With the front (T <= TB) the tokens form one block: every token is prepared before the
+    // (whole-head) state tile is loaded, so the preparation's temporaries and the tile are
+    // never live together.
+    for (int tb = 0; tb < (FRONT ? 1 : a.T); tb += TB) {
         const int nb = min(TB, a.T - tb);
         for (int j = wave; j < nb; j += kWaves)
             prep_token<DK, DV, BV, TB, TIn, VERIFY, FRONT>(a, L, j, n, tb + j, h, tile, lane, slot);
@@ -814,7 +817,7 @@ hipError_t launch_decode_d(const DecodeArgs& a, hipStream_t stream) {
     const dim3 grid(static_cast<unsigned>(a.N) * a.H * (DV / BV));
     if (a.front.gate_scale) {
         // the input front: one workgroup per (sequence, head) owns the head's convolution
-        // state; tokens in blocks of kFrontTB, one token per wave, commit mode only
+        // state; up to kFrontTB tokens as one block, commit mode only
         hipLaunchKernelGGL((decode_kernel<DK, DV, DV, kFrontTB, TIn, false, true>),
                            dim3(static_cast<unsigned>(a.N) * a.H), dim3(kThreads), 0, stream, a);
     } else if (a.T == 1) {

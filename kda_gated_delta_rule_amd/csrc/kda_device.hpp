@@ -91,12 +91,25 @@ __device__ __forceinline__ void store1<BF16>(void* p, int64_t i, float x) {
     static_cast<uint16_t*>(p)[i] = f32_to_bf16(x);
 }
 
-// Activations of the input front, in fp32: softplus(x) = max(x, 0) + log1p(e^-|x|) (no
-// overflow for large |x|), the logistic function 1 / (1 + e^-x), and SiLU x / (1 + e^-x)
-// (both 0 in the limit x -> -inf, where e^-x overflows to inf).
-__device__ __forceinline__ float front_softplus(float x) { return fmaxf(x, 0.f) + log1pf(expf(-fabsf(x))); }
-__device__ __forceinline__ float front_sigmoid(float x) { return 1.f / (1.f + expf(-x)); }
-__device__ __forceinline__ float front_silu(float x) { return x / (1.f + expf(-x)); }
+// Activations of the input front, in fp32, on the hardware exp2 / log2 / reciprocal
+// (v_exp_f32, v_log_f32, v_rcp_f32, each about 1 ulp):
+//   e^x = 2^(x log2(e));
+//   the logistic function 1 / (1 + e^-x) (0 in the limit x -> -inf, where e^-x is inf);
+//   SiLU x / (1 + e^-x);
+//   softplus(x) = max(x, 0) + log1p(e^-|x|), with log1p(y) for y in [0, 1] by Goldberg's
+//   method (u = 1 + y rounded; log1p(y) = y if u = 1, else log(u) y / (u - 1)), which keeps
+//   the relative accuracy of log for small y where log(1 + y) alone would lose it.
+constexpr float kFrontLog2e = 1.4426950408889634f;
+constexpr float kFrontLn2 = 0.6931471805599453f;
+__device__ __forceinline__ float front_exp(float x) { return __builtin_amdgcn_exp2f(x * kFrontLog2e); }
+__device__ __forceinline__ float front_sigmoid(float x) { return __builtin_amdgcn_rcpf(1.f + front_exp(-x)); }
+__device__ __forceinline__ float front_silu(float x) { return x * front_sigmoid(x); }
+__device__ __forceinline__ float front_softplus(float x) {
+    const float y = front_exp(-fabsf(x));
+    const float u = 1.f + y;
+    const float l1p = u == 1.f ? y : __builtin_amdgcn_logf(u) * kFrontLn2 * y * __builtin_amdgcn_rcpf(u - 1.f);
+    return fmaxf(x, 0.f) + l1p;
+}
 
 // Stores 4 consecutive elements (fp32 in, rounded for bf16).
 template <class T>

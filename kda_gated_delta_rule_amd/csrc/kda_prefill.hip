@@ -465,10 +465,26 @@ __device__ __forceinline__ void intra_front(IntraIn<DK, DV, TIn>& X, char* smem,
     // one granule: channels c0 .. c0 + GW - 1 of the block at channel offset off (q | k | v)
     auto conv = [&](u32x4& G, const float* w, int D, int off, int c0) {
         const float* wc = w + (static_cast<int64_t>(h) * D + c0) * W;
+        // wt[e][d]: the weight of the input d tokens back (zero beyond the width); width 4
+        // reads each channel's taps as one 16-byte load
+        float wt[GW][4];
+        if (W == 4) {
+#pragma unroll
+            for (int e = 0; e < GW; ++e) {
+                const f32x4 w4 = *reinterpret_cast<const f32x4*>(wc + 4 * e);
+#pragma unroll
+                for (int d = 0; d < 4; ++d) wt[e][d] = w4[3 - d];
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < GW; ++e)
+#pragma unroll
+                for (int d = 0; d < 4; ++d) wt[e][d] = d < W ? wc[e * W + W - 1 - d] : 0.f;
+        }
         float x[GW], acc[GW];
         gran_to_f32(G, x, tag);
 #pragma unroll
-        for (int e = 0; e < GW; ++e) acc[e] = wc[e * W + W - 1] * x[e];
+        for (int e = 0; e < GW; ++e) acc[e] = wt[e][0] * x[e];
         auto tap = [&](auto dtag) {
             constexpr int d = decltype(dtag)::value;
             if (d < W) {
@@ -479,7 +495,7 @@ __device__ __forceinline__ void intra_front(IntraIn<DK, DV, TIn>& X, char* smem,
                 float xd[GW];
                 gran_to_f32(xv, xd, tag);
 #pragma unroll
-                for (int e = 0; e < GW; ++e) acc[e] = fmaf(wc[e * W + W - 1 - d], xd[e], acc[e]);
+                for (int e = 0; e < GW; ++e) acc[e] = fmaf(wt[e][d], xd[e], acc[e]);
             }
         };
         tap(std::integral_constant<int, 1>{});

@@ -226,3 +226,49 @@ def test_isa_has_no_mfma_result_read_through_short_branch_path():
 
     findings = isa_lint.lint()
     assert not findings, findings[:3]
+
+
+def front(**over):
+    f = dict(gate_scale=A, conv_q=A, conv_k=A, conv_v=A, conv_state=A, conv_width=4, conv_silu=1)
+    f.update(over)
+    return _lib.KdaFront(*f.values())
+
+
+def decode_front_args(fr, **over):
+    args = dict(q=A, k=A, v=A, dtype=1, g=A, beta=A, front=ctypes.byref(fr), pool=A, num_slots=8,
+                slot=A, N=0, T=1, H=2, dk=128, dv=128, scale=0.1, l2=1, o=A, stream=None)
+    args.update(over)
+    return list(args.values())
+
+
+@pytest.mark.parametrize("fover,over,code", [
+    (dict(), dict(), _lib.KDA_OK),  # valid, N = 0: returns before any launch
+    (dict(conv_width=1, conv_state=None), dict(), _lib.KDA_OK),  # width 1 needs no state
+    (dict(conv_width=0), dict(), _lib.KDA_ERR_INVALID_ARG),
+    (dict(conv_width=5), dict(), _lib.KDA_ERR_INVALID_ARG),
+    (dict(conv_silu=2), dict(), _lib.KDA_ERR_INVALID_ARG),
+    (dict(conv_state=None), dict(), _lib.KDA_ERR_INVALID_ARG),
+    (dict(conv_state=A + 4), dict(), _lib.KDA_ERR_INVALID_ARG),
+    (dict(gate_scale=None), dict(), _lib.KDA_ERR_INVALID_ARG),
+    (dict(conv_v=A + 8), dict(), _lib.KDA_ERR_INVALID_ARG),
+    (dict(), dict(T=9), _lib.KDA_ERR_INVALID_ARG),  # at most 8 tokens with the front
+    (dict(), dict(front=None), _lib.KDA_ERR_INVALID_ARG),
+    (dict(), dict(dk=96), _lib.KDA_ERR_UNSUPPORTED),
+])
+def test_decode_front_validation(lib, fover, over, code):
+    fr = front(**fover)
+    assert lib.kda_decode_step_front(*decode_front_args(fr, **over)) == code
+
+
+@pytest.mark.parametrize("fover,code", [
+    (dict(), _lib.KDA_ERR_WORKSPACE),  # valid: stops at the workspace check
+    (dict(conv_width=7), _lib.KDA_ERR_INVALID_ARG),
+    (dict(conv_q=None), _lib.KDA_ERR_INVALID_ARG),
+])
+def test_prefill_front_validation(lib, fover, code):
+    fr = front(**fover)
+    p = prefill_args()
+    args = list(p.values())
+    # kda_chunk_prefill_front takes the front after beta (position 6)
+    args = args[:6] + [ctypes.byref(fr)] + args[6:]
+    assert lib.kda_chunk_prefill_front(*args) == code
