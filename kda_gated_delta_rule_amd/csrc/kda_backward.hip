@@ -46,6 +46,8 @@ namespace kda {
 
 namespace {
 
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
 constexpr int kC = 64;
 constexpr int kT = 256;  // threads of every per-chunk kernel (4 waves)
 constexpr float kL2e = 1.4426950408889634f;
@@ -98,12 +100,36 @@ struct FwdTables {
 // fp32 MFMA 16x16 tile: C(m, n) += sum_k A(m, k) B(k, n), k in [0, K) (K a multiple of 4);
 // A(m, k) = A[m * am + k * ak], B(k, n) = B[k * bk + n * bn].  Lane l holds C(4 (l / 16) + i,
 // l % 16), i = 0..3.
+// The k steps go round four independent accumulators (K a multiple of 16), so consecutive
+// MFMAs do not wait for each other's results.
 __device__ __forceinline__ f32x4 mm16(const float* A, int am, int ak, const float* B, int bk, int bn, int K,
                                       int lane, f32x4 c) {
     const int r = lane & 15, q = lane >> 4;
-    for (int k0 = 0; k0 < K; k0 += 4)
+    f32x4 c1 = {0.f, 0.f, 0.f, 0.f}, c2 = c1, c3 = c1;
+    for (int k0 = 0; k0 < K; k0 += 16) {
         c = __builtin_amdgcn_mfma_f32_16x16x4f32(A[r * am + (k0 + q) * ak], B[(k0 + q) * bk + r * bn], c, 0, 0, 0);
-    return c;
+        c1 = __builtin_amdgcn_mfma_f32_16x16x4f32(A[r * am + (k0 + 4 + q) * ak], B[(k0 + 4 + q) * bk + r * bn], c1, 0,
+                                                  0, 0);
+        c2 = __builtin_amdgcn_mfma_f32_16x16x4f32(A[r * am + (k0 + 8 + q) * ak], B[(k0 + 8 + q) * bk + r * bn], c2, 0,
+                                                  0, 0);
+        c3 = __builtin_amdgcn_mfma_f32_16x16x4f32(A[r * am + (k0 + 12 + q) * ak], B[(k0 + 12 + q) * bk + r * bn], c3,
+                                                  0, 0, 0);
+    }
+    return (c + c1) + (c2 + c3);
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave (lane i gets x_0 + ... + x_i): a scan in
+// each 16-lane row by DPP row shifts (lanes shifted in from outside the row add 0), then the
+// totals of the rows before carried in with row_bcast:15 (into rows 1 and 3) and
+// row_bcast:31 (into rows 2 and 3).
+__device__ __forceinline__ float wave_prefix64(float x) {
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x111, 0xf, 0xf, false));
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x112, 0xf, 0xf, false));
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x114, 0xf, 0xf, false));
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x118, 0xf, 0xf, false));
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x142, 0xa, 0xf, false));
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x143, 0xc, 0xf, false));
+    return x;
 }
 
 template <class TIn>
@@ -132,13 +158,38 @@ __device__ __forceinline__ bool item_of(const PrefillArgs& a, const char* ws, co
     return true;
 }
 
-// Rows t0 .. t0 + L - 1 of head h of a [T][H][D] input into LDS dst [64][ld] (fp32, rows from
-// L on are zero).
-template <class TIn>
-__device__ void load_rows(const void* src, int D, float* dst, int ld, const Item& it, int H) {
-    for (int i = threadIdx.x; i < kC * D; i += kT) {
-        const int t = i / D, c = i % D;
-        dst[t * ld + c] = t < it.L ? ld_in<TIn>(src, (static_cast<int64_t>(it.t0 + t) * H + it.h) * D + c) : 0.f;
+// The copies below issue every load of a thread before any of its stores (16-byte accesses,
+// compile-time counts), so the loads are in flight together instead of each waiting in turn.
+
+// Columns c0 .. c0 + W - 1 of rows t0 .. t0 + L - 1 of head h of a [T][H][D] input into LDS
+// dst [64][ld] (fp32; rows from L on are zero).
+template <class TIn, int D, int W = D>
+__device__ void load_rows(const void* src, float* dst, int ld, const Item& it, int H, int c0 = 0) {
+    constexpr int EPG = 16 / TIn::bytes;  // elements per 16-byte access
+    constexpr int GPR = W / EPG, N = kC * GPR / kT;
+    static_assert(W % EPG == 0 && (kC * GPR) % kT == 0, "row copy shape");
+    u32x4 v[N];
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        const int idx = threadIdx.x + i * kT, t = idx / GPR, c = c0 + EPG * (idx % GPR);
+        v[i] = u32x4{0u, 0u, 0u, 0u};
+        if (t < it.L)
+            v[i] = *reinterpret_cast<const u32x4*>(static_cast<const char*>(src) +
+                                                   ((static_cast<int64_t>(it.t0 + t) * H + it.h) * D + c) * TIn::bytes);
+    }
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        const int idx = threadIdx.x + i * kT, t = idx / GPR, c = EPG * (idx % GPR);
+        float* d = dst + t * ld + c;
+        if constexpr (TIn::bytes == 2) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                d[2 * e] = __uint_as_float(v[i][e] << 16);
+                d[2 * e + 1] = __uint_as_float(v[i][e] & 0xffff0000u);
+            }
+        } else {
+            *reinterpret_cast<f32x4*>(d) = __builtin_bit_cast(f32x4, v[i]);
+        }
     }
 }
 
@@ -156,22 +207,14 @@ __device__ void normalize_rows(float* x, int ld, int D, float* inv, int use_l2) 
 }
 
 // G [64][ld] = in-chunk inclusive cumsum of g, in log2 units (rows from L on repeat G_L).
-// The chunk's gates are first copied into G by all threads (coalesced), then one thread per
-// channel scans its column in LDS.  The caller synchronises before reading G.
-__device__ void gate_cumsum(const float* g, float* G, int ld, int DK, const Item& it, int H) {
-    for (int i = threadIdx.x; i < kC * DK; i += kT) {
-        const int t = i / DK, c = i % DK;
-        G[t * ld + c] = t < it.L ? g[(static_cast<int64_t>(it.t0 + t) * H + it.h) * DK + c] * kL2e : 0.f;
-    }
+// The chunk's gates are first copied into G by all threads (coalesced), then each wave scans
+// columns across its 64 lanes (lane = token).  The caller synchronises before reading G.
+template <int DK>
+__device__ void gate_cumsum(const float* g, float* G, int ld, const Item& it, int H) {
+    load_rows<F32, DK>(g, G, ld, it, H);
     __syncthreads();
-    if (threadIdx.x < DK) {
-        const int c = threadIdx.x;
-        float x = 0.f;
-        for (int t = 0; t < kC; ++t) {
-            x += G[t * ld + c];
-            G[t * ld + c] = x;
-        }
-    }
+    const int lane = threadIdx.x & 63;
+    for (int c = threadIdx.x >> 6; c < DK; c += kT / 64) G[lane * ld + c] = wave_prefix64(G[lane * ld + c] * kL2e);
 }
 
 __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -182,15 +225,18 @@ __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x)
 __device__ f32x4 dgram_tile(const float* X, const float* Y, const float* G, int ld, int DK, int i, int j, int lane) {
     const int r = lane & 15, q = lane >> 4;
     const int R = j < i ? 16 * i - 1 : 16 * i + 7;
-    f32x4 c = {0.f, 0.f, 0.f, 0.f};
-    for (int k0 = 0; k0 < DK; k0 += 4) {
-        const int ch = k0 + q;
-        const float ref = G[R * ld + ch];
-        const float av = X[(16 * i + r) * ld + ch] * ex2(G[(16 * i + r) * ld + ch] - ref);
-        const float bv = Y[(16 * j + r) * ld + ch] * ex2(ref - G[(16 * j + r) * ld + ch]);
-        c = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, c, 0, 0, 0);
+    f32x4 c[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};  // two independent chains
+    for (int k0 = 0; k0 < DK; k0 += 8) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int ch = k0 + 4 * h + q;
+            const float ref = G[R * ld + ch];
+            const float av = X[(16 * i + r) * ld + ch] * ex2(G[(16 * i + r) * ld + ch] - ref);
+            const float bv = Y[(16 * j + r) * ld + ch] * ex2(ref - G[(16 * j + r) * ld + ch]);
+            c[h] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, c[h], 0, 0, 0);
+        }
     }
-    return c;
+    return c[0] + c[1];
 }
 
 // Decayed token products over a 16 x 16 (rows, channels) output tile.
@@ -204,27 +250,35 @@ template <bool TMODE>
 __device__ f32x4 dtok_tile(const float* X, int ldx, const float* Z, const float* G, int ld, int i, int cb, int lane) {
     const int r = lane & 15, q = lane >> 4, ch = 16 * cb + r;
     const int Roff = TMODE ? 16 * i - 1 : 16 * i + 15, M = 16 * i + 7;
-    f32x4 off = {0.f, 0.f, 0.f, 0.f}, dg = off;
+    // two independent accumulator chains each for the off-diagonal and the diagonal part
+    f32x4 off2[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}}, dg2[2] = {off2[0], off2[1]};
     // off-diagonal blocks: t mode the s blocks before i, s mode the t blocks after i
     const int kb = TMODE ? 0 : 16 * (i + 1), ke = TMODE ? 16 * i : kC;
     if (ke > kb) {
         const float ref = G[Roff * ld + ch];
-        for (int k0 = kb; k0 < ke; k0 += 4) {
-            const int k = k0 + q;  // s (t mode) or t (s mode)
-            const float av = TMODE ? X[(16 * i + r) * ldx + k] : X[k * ldx + 16 * i + r];
-            const float zf = TMODE ? ex2(ref - G[k * ld + ch]) : ex2(G[k * ld + ch] - ref);
-            off = __builtin_amdgcn_mfma_f32_16x16x4f32(av, Z[k * ld + ch] * zf, off, 0, 0, 0);
+        for (int k0 = kb; k0 < ke; k0 += 8) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int k = k0 + 4 * h + q;  // s (t mode) or t (s mode)
+                const float av = TMODE ? X[(16 * i + r) * ldx + k] : X[k * ldx + 16 * i + r];
+                const float zf = TMODE ? ex2(ref - G[k * ld + ch]) : ex2(G[k * ld + ch] - ref);
+                off2[h] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, Z[k * ld + ch] * zf, off2[h], 0, 0, 0);
+            }
         }
     }
     {
         const float ref = G[M * ld + ch];
-        for (int k0 = 16 * i; k0 < 16 * i + 16; k0 += 4) {
-            const int k = k0 + q;
-            const float av = TMODE ? X[(16 * i + r) * ldx + k] : X[k * ldx + 16 * i + r];
-            const float zf = TMODE ? ex2(ref - G[k * ld + ch]) : ex2(G[k * ld + ch] - ref);
-            dg = __builtin_amdgcn_mfma_f32_16x16x4f32(av, Z[k * ld + ch] * zf, dg, 0, 0, 0);
+        for (int k0 = 16 * i; k0 < 16 * i + 16; k0 += 8) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int k = k0 + 4 * h + q;
+                const float av = TMODE ? X[(16 * i + r) * ldx + k] : X[k * ldx + 16 * i + r];
+                const float zf = TMODE ? ex2(ref - G[k * ld + ch]) : ex2(G[k * ld + ch] - ref);
+                dg2[h] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, Z[k * ld + ch] * zf, dg2[h], 0, 0, 0);
+            }
         }
     }
+    const f32x4 off = off2[0] + off2[1], dg = dg2[0] + dg2[1];
     f32x4 y;
     const float ro = ke > kb ? G[Roff * ld + ch] : 0.f, rm = G[M * ld + ch];
 #pragma unroll
@@ -303,12 +357,34 @@ __device__ void unit_lower_inverse(const float* Ag, const float* beta, float* T,
     }
 }
 
-// Global <-> LDS copies of a row-major fp32 [rows][cols] matrix.
-__device__ void g2s(const float* g, int gld, float* s, int sld, int rows, int cols) {
-    for (int i = threadIdx.x; i < rows * cols; i += kT) s[(i / cols) * sld + i % cols] = g[(i / cols) * gld + i % cols];
+// Global <-> LDS copies of a row-major fp32 [ROWS][COLS] matrix (leading dimensions and base
+// addresses multiples of 4 floats).
+template <int ROWS, int COLS>
+__device__ void g2s(const float* g, int gld, float* s, int sld) {
+    constexpr int C4 = COLS / 4, N = ROWS * C4 / kT;
+    static_assert(COLS % 4 == 0 && (ROWS * C4) % kT == 0, "copy shape");
+    f32x4 v[N];
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        const int idx = threadIdx.x + i * kT;
+        v[i] = *reinterpret_cast<const f32x4*>(g + (idx / C4) * gld + 4 * (idx % C4));
+    }
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        const int idx = threadIdx.x + i * kT;
+        *reinterpret_cast<f32x4*>(s + (idx / C4) * sld + 4 * (idx % C4)) = v[i];
+    }
 }
-__device__ void s2g(const float* s, int sld, float* g, int gld, int rows, int cols) {
-    for (int i = threadIdx.x; i < rows * cols; i += kT) g[(i / cols) * gld + i % cols] = s[(i / cols) * sld + i % cols];
+template <int ROWS, int COLS>
+__device__ void s2g(const float* s, int sld, float* g, int gld) {
+    constexpr int C4 = COLS / 4, N = ROWS * C4 / kT;
+    static_assert(COLS % 4 == 0 && (ROWS * C4) % kT == 0, "copy shape");
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        const int idx = threadIdx.x + i * kT;
+        *reinterpret_cast<f32x4*>(g + (idx / C4) * gld + 4 * (idx % C4)) =
+            *reinterpret_cast<const f32x4*>(s + (idx / C4) * sld + 4 * (idx % C4));
+    }
 }
 
 struct BwCtx {
@@ -350,16 +426,16 @@ template <int DK, int DV, class TIn>
 __global__ __launch_bounds__(kT) void bwd_intra_kernel(BackwardArgs b) {
     const PrefillArgs& a = b.fwd;
     constexpr int LK = DK + 4, LV = DV + 4, LC = kC + 4, LM = LK > LV ? LK : LV;
-    __shared__ float sK[kC * LM], sQ[kC * LK], sG[kC * LK], sA[kC * LC], sT[kC * LC], sY[4 * 16 * 20], inv[kC],
+    __shared__ __attribute__((aligned(16))) float sK[kC * LM], sQ[kC * LK], sG[kC * LK], sA[kC * LC], sT[kC * LC], sY[4 * 16 * 20], inv[kC],
         sB[kC];
     const BwCtx X(a, DK, DV, TIn::bytes);
     Item it;
     if (!item_of(a, static_cast<const char*>(a.workspace), X.ft, blockIdx.x, it)) return;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, H = a.H;
     const int item = blockIdx.x;
-    load_rows<TIn>(a.k, DK, sK, LK, it, H);
-    load_rows<TIn>(a.q, DK, sQ, LK, it, H);
-    gate_cumsum(a.g, sG, LK, DK, it, H);
+    load_rows<TIn, DK>(a.k, sK, LK, it, H);
+    load_rows<TIn, DK>(a.q, sQ, LK, it, H);
+    gate_cumsum<DK>(a.g, sG, LK, it, H);
     if (threadIdx.x < kC) sB[threadIdx.x] = threadIdx.x < it.L ? a.beta[static_cast<int64_t>(it.t0 + threadIdx.x) * H + it.h] : 0.f;
     __syncthreads();
     normalize_rows(sK, LK, DK, inv, a.use_l2);
@@ -387,7 +463,7 @@ __global__ __launch_bounds__(kT) void bwd_intra_kernel(BackwardArgs b) {
     }
     __syncthreads();
     unit_lower_inverse(sA, sB, sT, sY, lane, wave);
-    s2g(sT, LC, X.blk(item, X.bw.T), kC, kC, kC);
+    s2g<kC, kC>(sT, LC, X.blk(item, X.bw.T), kC);
     // BK = beta kh 2^G into sQ (P is done), then W = T BK
     for (int i = threadIdx.x; i < kC * DK; i += kT) {
         const int t = i / DK, c = i % DK;
@@ -402,7 +478,7 @@ __global__ __launch_bounds__(kT) void bwd_intra_kernel(BackwardArgs b) {
     }
     __syncthreads();
     // BV = beta v into sK, then Ut = T BV
-    load_rows<TIn>(a.v, DV, sK, LV, it, H);
+    load_rows<TIn, DV>(a.v, sK, LV, it, H);
     __syncthreads();
     for (int i = threadIdx.x; i < kC * DV; i += kT) sK[(i / DV) * LV + i % DV] *= sB[i / DV];
     __syncthreads();
@@ -434,24 +510,24 @@ template <int DK, int DV, class TIn>
 __global__ __launch_bounds__(kT) void bwd_prep_kernel(BackwardArgs b) {
     const PrefillArgs& a = b.fwd;
     constexpr int LK = DK + 4, LV = DV + 4, LC = kC + 4;
-    __shared__ float sK[kC * LK], sQ[kC * LK], sW[kC * LK], sO[kC * LV], sP[kC * LC], inv[kC];
+    __shared__ __attribute__((aligned(16))) float sK[kC * LK], sQ[kC * LK], sW[kC * LK], sO[kC * LV], sP[kC * LC], inv[kC];
     float* sG = sW;  // the gate cumsum lives where W goes once Kt and QG are formed
     const BwCtx X(a, DK, DV, TIn::bytes);
     Item it;
     if (!item_of(a, static_cast<const char*>(a.workspace), X.ft, blockIdx.x, it)) return;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, H = a.H, item = blockIdx.x;
-    load_rows<TIn>(a.k, DK, sK, LK, it, H);
-    load_rows<TIn>(a.q, DK, sQ, LK, it, H);
-    load_rows<TIn>(b.dout, DV, sO, LV, it, H);
-    gate_cumsum(a.g, sG, LK, DK, it, H);
-    g2s(X.blk(item, X.bw.P), kC, sP, LC, kC, kC);
+    load_rows<TIn, DK>(a.k, sK, LK, it, H);
+    load_rows<TIn, DK>(a.q, sQ, LK, it, H);
+    load_rows<TIn, DV>(b.dout, sO, LV, it, H);
+    gate_cumsum<DK>(a.g, sG, LK, it, H);
+    g2s<kC, kC>(X.blk(item, X.bw.P), kC, sP, LC);
     __syncthreads();
     normalize_rows(sK, LK, DK, inv, a.use_l2);
     normalize_rows(sQ, LK, DK, inv, a.use_l2);
     to_kt(sK, sG, LK, DK);
     to_qg(sQ, sG, LK, DK);
     __syncthreads();
-    g2s(X.blk(item, X.bw.W), DK, sW, LK, kC, DK);
+    g2s<kC, DK>(X.blk(item, X.bw.W), DK, sW, LK);
     const float* gl = X.blk(item, X.bw.gl);
     __syncthreads();
     // Mt (dk x dk): tile (rb, cb), rows c = W's columns, k over tokens
@@ -493,7 +569,7 @@ template <int DK, int DV>
 __global__ __launch_bounds__(64 * (DK / 16)) void bwd_scan_kernel(BackwardArgs b, int e) {
     const PrefillArgs& a = b.fwd;
     constexpr int NTS = DV / 16, LX = DK + 4;
-    __shared__ float xs[16 * LX];  // X^T [16 columns][DK]
+    __shared__ __attribute__((aligned(16))) float xs[16 * LX];  // X^T [16 columns][DK]
     const BwCtx X(a, DK, DV, e);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int r = lane & 15, q4 = 4 * (lane >> 4);
@@ -547,7 +623,7 @@ __global__ __launch_bounds__(kT) void bwd_state_kernel(BackwardArgs b) {
     const PrefillArgs& a = b.fwd;
     constexpr int LK = DK + 4, LC = kC + 4, LB = kVB + 4;
     constexpr int NKB = DK / 16;
-    __shared__ float sW[kC * LK], sK[kC * LK], sP[kC * LC], sS[DK * LB], sX[DK * LB], sO[kC * LB],
+    __shared__ __attribute__((aligned(16))) float sW[kC * LK], sK[kC * LK], sP[kC * LC], sS[DK * LB], sX[DK * LB], sO[kC * LB],
         sU[kC * LB], sdU[kC * LB], inv[kC], sgl[DK];
     float* sG = sW;
     const BwCtx X(a, DK, DV, TIn::bytes);
@@ -555,14 +631,14 @@ __global__ __launch_bounds__(kT) void bwd_state_kernel(BackwardArgs b) {
     if (!item_of(a, static_cast<const char*>(a.workspace), X.ft, blockIdx.x, it)) return;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, H = a.H, item = blockIdx.x;
     const int r = lane & 15, q = lane >> 4;
-    load_rows<TIn>(a.k, DK, sK, LK, it, H);
-    gate_cumsum(a.g, sG, LK, DK, it, H);
-    g2s(X.blk(item, X.bw.P), kC, sP, LC, kC, kC);
+    load_rows<TIn, DK>(a.k, sK, LK, it, H);
+    gate_cumsum<DK>(a.g, sG, LK, it, H);
+    g2s<kC, kC>(X.blk(item, X.bw.P), kC, sP, LC);
     __syncthreads();
     normalize_rows(sK, LK, DK, inv, a.use_l2);
     to_kt(sK, sG, LK, DK);
     __syncthreads();
-    g2s(X.blk(item, X.bw.W), DK, sW, LK, kC, DK);
+    g2s<kC, DK>(X.blk(item, X.bw.W), DK, sW, LK);
     if (threadIdx.x < DK) sgl[threadIdx.x] = 0.f;
     const float* S = X.blk(item, X.bw.S);
     const float* dX = X.blk(item, X.bw.dX);
@@ -573,13 +649,10 @@ __global__ __launch_bounds__(kT) void bwd_state_kernel(BackwardArgs b) {
     for (int i = 0; i < 4; ++i) dp[i] = f32x4{0.f, 0.f, 0.f, 0.f};
     for (int jb = 0; jb < DV / kVB; ++jb) {
         __syncthreads();
-        g2s(S + kVB * jb, DV, sS, LB, DK, kVB);
-        g2s(dX + kVB * jb, DV, sX, LB, DK, kVB);
-        for (int i = threadIdx.x; i < kC * kVB; i += kT) {
-            const int t = i / kVB, j = i % kVB;
-            sO[t * LB + j] = t < it.L ? ld_in<TIn>(b.dout, (static_cast<int64_t>(it.t0 + t) * H + it.h) * DV + kVB * jb + j) : 0.f;
-            sU[t * LB + j] = Ut[t * DV + kVB * jb + j];
-        }
+        g2s<DK, kVB>(S + kVB * jb, DV, sS, LB);
+        g2s<DK, kVB>(dX + kVB * jb, DV, sX, LB);
+        load_rows<TIn, DV, kVB>(b.dout, sO, LB, it, H, kVB * jb);
+        g2s<kC, kVB>(Ut + kVB * jb, DV, sU, LB);
         __syncthreads();
         // U and dU of this wave's token block
         for (int cb = 0; cb < kVB / 16; ++cb) {
@@ -637,7 +710,7 @@ __global__ __launch_bounds__(kT) void bwd_ut_kernel(BackwardArgs b) {
     const PrefillArgs& a = b.fwd;
     constexpr int LK = DK + 4, LV = DV + 4, LC = kC + 4;
     constexpr int LM = LK > LV ? LK : LV;
-    __shared__ float sT[kC * LC], sM1[kC * LM], sM2[kC * LM], sDE[2 * kC * LC], inv[kC], sB[kC];
+    __shared__ __attribute__((aligned(16))) float sT[kC * LC], sM1[kC * LM], sM2[kC * LM], sDE[2 * kC * LC], inv[kC], sB[kC];
     float* sD = sDE;
     float* sE = sDE + kC * LC;
     float* sG = sDE;  // the gate cumsum (DK wide) spans sD and sE while KG is formed
@@ -648,16 +721,16 @@ __global__ __launch_bounds__(kT) void bwd_ut_kernel(BackwardArgs b) {
     const int r = lane & 15, q = lane >> 4;
     static_assert(2 * kC * LC >= kC * LK, "gate cumsum fits sD + sE");
     // KG = kh 2^G (sM2) and dW (sM1)
-    load_rows<TIn>(a.k, DK, sM2, LK, it, H);
-    gate_cumsum(a.g, sG, LK, DK, it, H);
+    load_rows<TIn, DK>(a.k, sM2, LK, it, H);
+    gate_cumsum<DK>(a.g, sG, LK, it, H);
     if (threadIdx.x < kC) {
         sB[threadIdx.x] = threadIdx.x < it.L ? a.beta[static_cast<int64_t>(it.t0 + threadIdx.x) * H + it.h] : 0.f;
     }
-    g2s(X.blk(item, X.bw.T), kC, sT, LC, kC, kC);
+    g2s<kC, kC>(X.blk(item, X.bw.T), kC, sT, LC);
     __syncthreads();
     normalize_rows(sM2, LK, DK, inv, a.use_l2);
     to_qg(sM2, sG, LK, DK);  // kh 2^G
-    g2s(X.blk(item, X.bw.dW), DK, sM1, LK, kC, DK);
+    g2s<kC, DK>(X.blk(item, X.bw.dW), DK, sM1, LK);
     __syncthreads();
     // dT (part 1: dW BK^T, BK = beta KG, so column s takes beta_s) and dBK of this wave's
     // rows; dbeta part sum_c KG dBK
@@ -676,8 +749,8 @@ __global__ __launch_bounds__(kT) void bwd_ut_kernel(BackwardArgs b) {
     }
     __syncthreads();
     // BV = beta v (sM2) and dU (sM1)
-    load_rows<TIn>(a.v, DV, sM2, LV, it, H);
-    g2s(X.blk(item, X.bw.dU), DV, sM1, LV, kC, DV);
+    load_rows<TIn, DV>(a.v, sM2, LV, it, H);
+    g2s<kC, DV>(X.blk(item, X.bw.dU), DV, sM1, LV);
     __syncthreads();
     for (int i = threadIdx.x; i < kC * DV; i += kT) sM2[(i / DV) * LV + i % DV] *= sB[i / DV];
     __syncthreads();
@@ -736,18 +809,18 @@ template <int DK, int DV, class TIn>
 __global__ __launch_bounds__(kT) void bwd_final_kernel(BackwardArgs b) {
     const PrefillArgs& a = b.fwd;
     constexpr int LK = DK + 4, LC = kC + 4, NKB = DK / 16;
-    __shared__ float sK[kC * LK], sQ[kC * LK], sG[kC * LK], sA[kC * LC], sP[kC * LC], iq[kC], ik[kC], sB[kC],
+    __shared__ __attribute__((aligned(16))) float sK[kC * LK], sQ[kC * LK], sG[kC * LK], sA[kC * LC], sP[kC * LC], iq[kC], ik[kC], sB[kC],
         sGL[DK];
     const BwCtx X(a, DK, DV, TIn::bytes);
     Item it;
     if (!item_of(a, static_cast<const char*>(a.workspace), X.ft, blockIdx.x, it)) return;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, H = a.H, item = blockIdx.x;
     const int r = lane & 15, q = lane >> 4;
-    load_rows<TIn>(a.k, DK, sK, LK, it, H);
-    load_rows<TIn>(a.q, DK, sQ, LK, it, H);
-    gate_cumsum(a.g, sG, LK, DK, it, H);
-    g2s(X.blk(item, X.bw.dAg), kC, sA, LC, kC, kC);
-    g2s(X.blk(item, X.bw.dP), kC, sP, LC, kC, kC);
+    load_rows<TIn, DK>(a.k, sK, LK, it, H);
+    load_rows<TIn, DK>(a.q, sQ, LK, it, H);
+    gate_cumsum<DK>(a.g, sG, LK, it, H);
+    g2s<kC, kC>(X.blk(item, X.bw.dAg), kC, sA, LC);
+    g2s<kC, kC>(X.blk(item, X.bw.dP), kC, sP, LC);
     if (threadIdx.x < kC) sB[threadIdx.x] = threadIdx.x < it.L ? a.beta[static_cast<int64_t>(it.t0 + threadIdx.x) * H + it.h] : 0.f;
     __syncthreads();
     normalize_rows(sK, LK, DK, ik, a.use_l2);
@@ -824,13 +897,12 @@ __global__ __launch_bounds__(kT) void bwd_final_kernel(BackwardArgs b) {
     // dG into sG (rows of this wave), then the reverse cumsum per channel plus dG_L
     for (int cb = 0; cb < NKB; ++cb) put_tile(sG, LK, wave, cb, dG[cb], lane);
     __syncthreads();
-    if (threadIdx.x < DK) {
-        const int c = threadIdx.x;
-        float x = sGL[c];
-        for (int t = kC - 1; t >= 0; --t) {
-            if (t < it.L) x += sG[t * LK + c];
-            sG[t * LK + c] = x;
-        }
+    // suffix sums over the live rows (lane = token): total - inclusive prefix + own value
+    for (int c = wave; c < DK; c += kT / 64) {
+        const float v = lane < it.L ? sG[lane * LK + c] : 0.f;
+        const float incl = wave_prefix64(v);
+        const float tot = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(incl), 63));
+        sG[lane * LK + c] = (tot - incl + v) + sGL[c];
     }
     __syncthreads();
     for (int i = threadIdx.x; i < it.L * DK; i += kT) {
