@@ -583,27 +583,53 @@ __global__ __launch_bounds__(64 * (DK / 16)) void bwd_scan_kernel(BackwardArgs b
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr)
         x[rr] = b.dht ? b.dht[(static_cast<size_t>(seq) * H + h) * SZ + (16 * wave + q4 + rr) * DV + col] : 0.f;
-    for (int c = nch - 1; c >= 0; --c) {
+    // Mt rows and b of a chunk for this wave, loaded two chunks ahead of their use (the three
+    // operand sets rotate by name, the loop unrolled three times, so no copy waits for loads
+    // still in flight)
+    struct Ops {
+        f32x4 mt[DK / 16], bb;
+    };
+    auto load = [&](Ops& o, int c) {
         const int item = (c0 + c) * H + h;
-        float* dX = X.blk(item, X.bw.dX);
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) dX[(16 * wave + q4 + rr) * DV + col] = x[rr];
         const float* Mt = X.blk(item, X.bw.Mt);
         const float* bb = X.blk(item, X.bw.b);
-        f32x4 acc;
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) acc[rr] = bb[(16 * wave + q4 + rr) * DV + col];
+        for (int kb = 0; kb < DK / 16; ++kb)
+            o.mt[kb] = *reinterpret_cast<const f32x4*>(Mt + (16 * wave + r) * DK + 16 * kb + q4);
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) o.bb[rr] = bb[(16 * wave + q4 + rr) * DV + col];
+    };
+    auto step = [&](int c, const Ops& cur, Ops& fill) {
+        if (c < 0) return false;
+        float* dX = X.blk((c0 + c) * H + h, X.bw.dX);
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) dX[(16 * wave + q4 + rr) * DV + col] = x[rr];
+        load(fill, c >= 2 ? c - 2 : 0);  // (a valid chunk when none is left)
         *reinterpret_cast<f32x4*>(xs + r * LX + 16 * wave + q4) = x;
         __syncthreads();
-        // lane (r, q) supplies k = 16 kb + 4q + ks of Mt row 16 wave + r and of X column r
+        // lane (r, q) supplies k = 16 kb + 4q + ks of Mt row 16 wave + r and of X column r;
+        // four independent accumulator chains (one per ks)
+        f32x4 acc[4] = {cur.bb, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
         for (int kb = 0; kb < DK / 16; ++kb) {
-            const f32x4 mt = *reinterpret_cast<const f32x4*>(Mt + (16 * wave + r) * DK + 16 * kb + q4);
             const f32x4 xb = *reinterpret_cast<const f32x4*>(xs + r * LX + 16 * kb + q4);
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(mt[ks], xb[ks], acc, 0, 0, 0);
+            for (int ks = 0; ks < 4; ++ks)
+                acc[ks] = __builtin_amdgcn_mfma_f32_16x16x4f32(cur.mt[kb][ks], xb[ks], acc[ks], 0, 0, 0);
         }
         __syncthreads();
-        x = acc;
+        x = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+        return true;
+    };
+    if (nch > 0) {
+        Ops o0, o1, o2;
+        load(o0, nch - 1);
+        load(o1, nch >= 2 ? nch - 2 : 0);
+        for (int c = nch - 1;; c -= 3) {
+            if (!step(c, o0, o2)) break;
+            if (!step(c - 1, o1, o0)) break;
+            if (!step(c - 2, o2, o1)) break;
+        }
     }
     if (b.dh0) {
 #pragma unroll
@@ -673,14 +699,23 @@ __global__ __launch_bounds__(kT) void bwd_state_kernel(BackwardArgs b) {
             for (int j = 0; j < kVB; ++j) s = fmaf(sS[threadIdx.x * LB + j], sX[threadIdx.x * LB + j], s);
             sgl[threadIdx.x] += s;
         }
-        // contractions over this block's columns (k = the block's 32 value columns)
-        for (int cb = 0; cb < NKB; ++cb) {
-            dqg[cb] = mm16(sO + 16 * wave * LB, LB, 1, sS + 16 * cb * LB, 1, LB, kVB, lane, dqg[cb]);
-            dw[cb] = mm16(sdU + 16 * wave * LB, LB, 1, sS + 16 * cb * LB, 1, LB, kVB, lane, dw[cb]);
-            dkt[cb] = mm16(sU + 16 * wave * LB, LB, 1, sX + 16 * cb * LB, 1, LB, kVB, lane, dkt[cb]);
+        // contractions over this block's columns (k = the block's 32 value columns): per k step
+        // the wave's rows of dO, dU and U are read once and serve every output tile
+        for (int k0 = 0; k0 < kVB; k0 += 4) {
+            const int kk = k0 + q;
+            const float ao = sO[(16 * wave + r) * LB + kk], adu = sdU[(16 * wave + r) * LB + kk];
+            const float au = sU[(16 * wave + r) * LB + kk];
+#pragma unroll
+            for (int cb = 0; cb < NKB; ++cb) {
+                const float bs = sS[(16 * cb + r) * LB + kk], bx = sX[(16 * cb + r) * LB + kk];
+                dqg[cb] = __builtin_amdgcn_mfma_f32_16x16x4f32(ao, bs, dqg[cb], 0, 0, 0);
+                dw[cb] = __builtin_amdgcn_mfma_f32_16x16x4f32(adu, bs, dw[cb], 0, 0, 0);
+                dkt[cb] = __builtin_amdgcn_mfma_f32_16x16x4f32(au, bx, dkt[cb], 0, 0, 0);
+            }
+#pragma unroll
+            for (int sb = 0; sb < 4; ++sb)
+                dp[sb] = __builtin_amdgcn_mfma_f32_16x16x4f32(ao, sU[(16 * sb + r) * LB + kk], dp[sb], 0, 0, 0);
         }
-        for (int sb = 0; sb < 4; ++sb)
-            dp[sb] = mm16(sO + 16 * wave * LB, LB, 1, sU + 16 * sb * LB, 1, LB, kVB, lane, dp[sb]);
     }
     float* dQG = X.blk(item, X.bw.dQG);
     float* dW = X.blk(item, X.bw.dW);
