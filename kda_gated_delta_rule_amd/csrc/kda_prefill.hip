@@ -759,13 +759,14 @@ __device__ __forceinline__ void intra_compute(const IntraIn<DK, DV, TIn>& X, cha
             }
             *reinterpret_cast<u32x4*>(rec + ws.o_q + ((static_cast<size_t>(wave) * RG::GK + j) * 64 + lane) * 16) =
                 tiles_to_gran(qt[0], qt[RG::CT - 1], tag);
-            // the diagonal tiles from this lane's own rows (s and t both in this block)
-            u32x4 SDh, SDl, KDh, KDl, QDh, QDl;
-            split_gran(sd, SDh, SDl, tag);
-            split_gran(kd, KDh, KDl, tag);
-            split_gran(qd, QDh, QDl, tag);
-            Adg = smma(SDh, SDl, KDh, KDl, Adg, tag);
-            Pdg = smma(SDh, SDl, QDh, QDl, Pdg, tag);
+            // the diagonal tiles from this lane's own rows (s and t both in this block) on fp32
+            // MFMA (no operand split): step e takes channel GW (4 j + q) + e of lane (r, q) as
+            // its k index q
+#pragma unroll
+            for (int e = 0; e < GW; ++e) {
+                Adg = __builtin_amdgcn_mfma_f32_16x16x4f32(sd[e], kd[e], Adg, 0, 0, 0);
+                Pdg = __builtin_amdgcn_mfma_f32_16x16x4f32(sd[e], qd[e], Pdg, 0, 0, 0);
+            }
             // one granule at a time: interleaving the unrolled iterations runs out of registers
             __builtin_amdgcn_sched_barrier(0);
         }
