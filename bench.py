@@ -180,6 +180,7 @@ def bench_decode(args, dev, log):
 
     import kda_gated_delta_rule_amd as kda
     import kda_workloads as W
+    from kda_gated_delta_rule_amd import ops
 
     cfg = W.DECODE
     x = W.decode(seed=0)
@@ -228,8 +229,27 @@ def bench_decode(args, dev, log):
     achieved = updates * bpu / per / 1e9
     log("decode (graph): %.2f us/step wall, %.2f us/launch (events), %.3f GB/s algorithmic"
         % (total / args.steps * 1e6, per * 1e6, achieved))
+    # the floor of the same state traffic: kda_diag_state_stream over the same slot sets, the
+    # decode kernel's access pattern with no token inputs or arithmetic, timed the same way
+    gd = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gd):
+        for i in range(args.steps):
+            ops.diag_state_stream(pool, sets[i % len(sets)])
+    gd.replay()
+    torch.cuda.synchronize()
+    ev0.record()
+    gd.replay()
+    ev1.record()
+    torch.cuda.synchronize()
+    per_pat = ev0.elapsed_time(ev1) / 1e3 / args.steps
+    state_bytes = updates * 2 * dk * dv * 4
+    log("state traffic floor (same pattern, no compute): %.2f us/launch, %.0f GB/s; decode at %.1f%% of it"
+        % (per_pat * 1e6, state_bytes / per_pat / 1e9, 100 * per_pat / per))
+    pattern = {"kernel": "kda_diag_state_stream (the decode kernel's state loads and stores, no inputs or arithmetic)",
+               "us_per_launch": per_pat * 1e6, "state_bytes": state_bytes,
+               "GBs": state_bytes / per_pat / 1e9, "decode_speed_vs_floor": per_pat / per}
     return dict(total=total, per=per, updates=updates, bytes_per_update=bpu, achieved=achieved,
-                inputs=x)
+                inputs=x, pattern=pattern)
 
 
 def bench_mtp(args, dev, log, T):
@@ -771,7 +791,7 @@ def main():
 
     dec = bench_decode(args, dev, log)
     value = dec["updates"] * args.steps / dec["total"]
-    extra = {"copy_reference": bench_copy(dev, log)}
+    extra = {"copy_reference": bench_copy(dev, log), "decode_state_traffic_floor": dec["pattern"]}
     if not args.decode_only:
         extra["verify_replay"] = bench_verify_replay(args, dev, log)
         extra["mtp_commit_T2"] = bench_mtp(args, dev, log, 2)

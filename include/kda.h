@@ -324,6 +324,17 @@ int kda_chunk_prefill_front(const void* q, const void* k, const void* v, int dty
                             int dk, int dv, float scale, int use_qk_l2norm, void* o,
                             void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * kda_diag_state_stream -- a diagnostic, not part of the method: reads the fp32 state of each
+ * sequence's slot (slot_idx [N] int32 on the device, negative skips) with the access pattern of
+ * kda_decode_step's T = 1 kernel (a workgroup per (sequence, head, 64-column tile), the whole tile
+ * held in registers, 16-byte non-temporal accesses) and writes it back unchanged.  Its time is
+ * the floor that the decode step's state traffic sets on the GPU; the benchmark reports it beside
+ * the decode kernel.  Errors and limits as kda_decode_step.
+ */
+int kda_diag_state_stream(float* state_pool, int64_t num_slots, const int32_t* slot_idx, int N, int H,
+                          int dk, int dv, hipStream_t stream);
+
 /* Human-readable name of a kda_status value (static string, never NULL). */
 const char* kda_status_string(int status);
 

@@ -7,7 +7,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libkda.so")
-SOURCES = ["kda_decode.hip", "kda_prefill.hip", "kda_backward.hip", "kda_api.cpp"]
+SOURCES = ["kda_decode.hip", "kda_prefill.hip", "kda_backward.hip", "kda_diag.hip", "kda_api.cpp"]
 ARCH = "gfx950"
 
 FLAGS = [

@@ -59,6 +59,7 @@ SIGNATURES = {
     "kda_chunk_prefill_front": (_c_i, [_c_p, _c_p, _c_p, _c_i, _c_p, _c_p, _FRONT_P, _c_p, _c_i, _c_i64,
                                        _c_p, _c_i64, _c_p, _c_i, _c_i, _c_i, _c_i, _c_f, _c_i, _c_p,
                                        _c_p, _c_sz, _c_p]),
+    "kda_diag_state_stream": (_c_i, [_c_p, _c_i64, _c_p, _c_i, _c_i, _c_i, _c_i, _c_p]),
     "kda_status_string": (ctypes.c_char_p, [_c_i]),
 }
 

@@ -103,6 +103,18 @@ KDA_EXPORT int kda_decode_step_front(const void* q, const void* k, const void* v
     return to_status(kda::launch_decode(a, dtype == KDA_BF16, dk, dv, stream));
 }
 
+KDA_EXPORT int kda_diag_state_stream(float* state_pool, int64_t num_slots, const int32_t* slot_idx,
+                                     int N, int H, int dk, int dv, hipStream_t stream) {
+    if (N < 0 || H < 1 || num_slots < 1) return KDA_ERR_INVALID_ARG;
+    if (!supported_dim(dk) || !supported_dim(dv)) return KDA_ERR_UNSUPPORTED;
+    if (!state_pool || !aligned16(state_pool) || !slot_idx || !aligned16(slot_idx)) return KDA_ERR_INVALID_ARG;
+    if (checked_mul(checked_mul(num_slots, H), static_cast<int64_t>(dk) * dv) < 0)
+        return KDA_ERR_INVALID_ARG;
+    if (checked_mul(N, H) > (1ll << 22)) return KDA_ERR_INVALID_ARG;
+    if (N == 0) return KDA_OK;
+    return to_status(kda::launch_state_stream(state_pool, slot_idx, N, H, dk, dv, stream));
+}
+
 KDA_EXPORT int kda_replay_commit(float* state_pool, int64_t num_slots, const int32_t* slot_idx,
                                  const float* records, const int32_t* accepted_len, int N, int T,
                                  int H, int dk, int dv, hipStream_t stream) {

@@ -91,6 +91,8 @@ struct BackwardArgs {
 // Each launcher returns hipSuccess or the launch error.
 hipError_t launch_decode(const DecodeArgs& a, int bf16, int dk, int dv, hipStream_t stream);
 hipError_t launch_replay(const ReplayArgs& a, int dk, int dv, hipStream_t stream);
+hipError_t launch_state_stream(float* pool, const int32_t* slot_idx, int N, int H, int dk, int dv,
+                               hipStream_t stream);
 size_t prefill_workspace_bytes(int num_seqs, int64_t total_tokens, int H, int dk, int dv,
                                int bf16);
 // False where the prefill LDS plan does not fit a CU (every dk, dv in {64, 128} fits).

@@ -161,6 +161,19 @@ def decode_step_front(q, k, v, gate, beta, state_pool, slot_idx, *, gate_scale, 
     return o
 
 
+def diag_state_stream(state_pool, slot_idx):
+    """Diagnostic (kda_diag_state_stream): reads and rewrites, unchanged, the state of each
+    slot in slot_idx with the T = 1 decode kernel's access pattern; its time is the floor the
+    decode step's state traffic sets."""
+    _need(state_pool.dtype == torch.float32 and state_pool.dim() == 4, "state_pool")
+    _need(slot_idx.dtype == torch.int32 and slot_idx.dim() == 1, "slot_idx")
+    _contig(state_pool, slot_idx)
+    ns, H, dk, dv = state_pool.shape
+    st = _lib.load().kda_diag_state_stream(_ptr(state_pool), ns, _ptr(slot_idx), slot_idx.shape[0], H, dk,
+                                           dv, _stream(state_pool))
+    _lib.check("kda_diag_state_stream", st)
+
+
 def replay_commit(state_pool, slot_idx, records, accepted_len):
     """ReplaySSM commit (kda_replay_commit): applies records[n, :accepted_len[n]] to the slots."""
     N, T, H, R = records.shape

@@ -365,3 +365,19 @@ def test_pool_offsets_beyond_32_bits():
     assert rel_l2(f64(big[far2.long()].cpu()), h_ref) <= 1e-2
     del big
     torch.cuda.empty_cache()
+
+
+def test_diag_state_stream_leaves_the_pool_unchanged():
+    """The diagnostic memory pass (the decode kernel's state access pattern, no arithmetic) reads
+    and rewrites the slots bit for bit, skips negative slots, and touches nothing else."""
+    dev = need_gpu()
+    announce("diag state stream")
+    from kda_gated_delta_rule_amd import ops
+    for dk, dv in ((128, 128), (64, 128), (128, 64), (64, 64)):
+        x = W.decode(seed=70, N=6, H=3, dk=dk, dv=dv, num_slots=10)
+        pool = x["pool"].to(dev)
+        sl = x["slot_idx"].clone()
+        sl[1] = -1
+        ops.diag_state_stream(pool, sl.to(dev))
+        torch.cuda.synchronize()
+        assert torch.equal(pool.cpu(), x["pool"])
