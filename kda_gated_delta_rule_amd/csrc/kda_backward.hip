@@ -163,23 +163,24 @@ __device__ __forceinline__ bool item_of(const PrefillArgs& a, const char* ws, co
 
 // Columns c0 .. c0 + W - 1 of rows t0 .. t0 + L - 1 of head h of a [T][H][D] input into LDS
 // dst [64][ld] (fp32; rows from L on are zero).
-template <class TIn, int D, int W = D>
+template <class TIn, int D, int W = D, int NT = kT>
 __device__ void load_rows(const void* src, float* dst, int ld, const Item& it, int H, int c0 = 0) {
     constexpr int EPG = 16 / TIn::bytes;  // elements per 16-byte access
-    constexpr int GPR = W / EPG, N = kC * GPR / kT;
-    static_assert(W % EPG == 0 && (kC * GPR) % kT == 0, "row copy shape");
+    constexpr int GPR = W / EPG, N = (kC * GPR + NT - 1) / NT;
+    static_assert(W % EPG == 0, "row copy shape");
     u32x4 v[N];
 #pragma unroll
     for (int i = 0; i < N; ++i) {
-        const int idx = threadIdx.x + i * kT, t = idx / GPR, c = c0 + EPG * (idx % GPR);
+        const int idx = threadIdx.x + i * NT, t = idx / GPR, c = c0 + EPG * (idx % GPR);
         v[i] = u32x4{0u, 0u, 0u, 0u};
-        if (t < it.L)
+        if (idx < kC * GPR && t < it.L)
             v[i] = *reinterpret_cast<const u32x4*>(static_cast<const char*>(src) +
                                                    ((static_cast<int64_t>(it.t0 + t) * H + it.h) * D + c) * TIn::bytes);
     }
 #pragma unroll
     for (int i = 0; i < N; ++i) {
-        const int idx = threadIdx.x + i * kT, t = idx / GPR, c = EPG * (idx % GPR);
+        const int idx = threadIdx.x + i * NT, t = idx / GPR, c = EPG * (idx % GPR);
+        if (idx >= kC * GPR) break;
         float* d = dst + t * ld + c;
         if constexpr (TIn::bytes == 2) {
 #pragma unroll
@@ -194,6 +195,7 @@ __device__ void load_rows(const void* src, float* dst, int ld, const Item& it, i
 }
 
 // In place x_t <- x_t / sqrt(|x_t|^2 + eps) (when use_l2); inv[t] gets the factor.
+template <int NT = kT>
 __device__ void normalize_rows(float* x, int ld, int D, float* inv, int use_l2) {
     if (threadIdx.x < kC) {
         const int t = threadIdx.x;
@@ -202,19 +204,19 @@ __device__ void normalize_rows(float* x, int ld, int D, float* inv, int use_l2) 
         inv[t] = use_l2 ? 1.f / sqrtf(s + kEps) : 1.f;
     }
     __syncthreads();
-    for (int i = threadIdx.x; i < kC * D; i += kT) x[(i / D) * ld + i % D] *= inv[i / D];
+    for (int i = threadIdx.x; i < kC * D; i += NT) x[(i / D) * ld + i % D] *= inv[i / D];
     __syncthreads();
 }
 
 // G [64][ld] = in-chunk inclusive cumsum of g, in log2 units (rows from L on repeat G_L).
 // The chunk's gates are first copied into G by all threads (coalesced), then each wave scans
 // columns across its 64 lanes (lane = token).  The caller synchronises before reading G.
-template <int DK>
+template <int DK, int NT = kT>
 __device__ void gate_cumsum(const float* g, float* G, int ld, const Item& it, int H) {
-    load_rows<F32, DK>(g, G, ld, it, H);
+    load_rows<F32, DK, DK, NT>(g, G, ld, it, H);
     __syncthreads();
     const int lane = threadIdx.x & 63;
-    for (int c = threadIdx.x >> 6; c < DK; c += kT / 64) G[lane * ld + c] = wave_prefix64(G[lane * ld + c] * kL2e);
+    for (int c = threadIdx.x >> 6; c < DK; c += NT / 64) G[lane * ld + c] = wave_prefix64(G[lane * ld + c] * kL2e);
 }
 
 __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -359,19 +361,19 @@ __device__ void unit_lower_inverse(const float* Ag, const float* beta, float* T,
 
 // Global <-> LDS copies of a row-major fp32 [ROWS][COLS] matrix (leading dimensions and base
 // addresses multiples of 4 floats).
-template <int ROWS, int COLS>
+template <int ROWS, int COLS, int NT = kT>
 __device__ void g2s(const float* g, int gld, float* s, int sld) {
-    constexpr int C4 = COLS / 4, N = ROWS * C4 / kT;
-    static_assert(COLS % 4 == 0 && (ROWS * C4) % kT == 0, "copy shape");
+    constexpr int C4 = COLS / 4, N = ROWS * C4 / NT;
+    static_assert(COLS % 4 == 0 && (ROWS * C4) % NT == 0, "copy shape");
     f32x4 v[N];
 #pragma unroll
     for (int i = 0; i < N; ++i) {
-        const int idx = threadIdx.x + i * kT;
+        const int idx = threadIdx.x + i * NT;
         v[i] = *reinterpret_cast<const f32x4*>(g + (idx / C4) * gld + 4 * (idx % C4));
     }
 #pragma unroll
     for (int i = 0; i < N; ++i) {
-        const int idx = threadIdx.x + i * kT;
+        const int idx = threadIdx.x + i * NT;
         *reinterpret_cast<f32x4*>(s + (idx / C4) * sld + 4 * (idx % C4)) = v[i];
     }
 }
@@ -490,8 +492,9 @@ __global__ __launch_bounds__(kT) void bwd_intra_kernel(BackwardArgs b) {
 }
 
 // Kt = kh 2^(G_L - G) and QG = qh 2^G in place (the raw normalised rows on entry).
+template <int NT = kT>
 __device__ void to_kt(float* K, const float* G, int ld, int DK) {
-    for (int i = threadIdx.x; i < kC * DK; i += kT) {
+    for (int i = threadIdx.x; i < kC * DK; i += NT) {
         const int t = i / DK, c = i % DK;
         K[t * ld + c] *= ex2(G[(kC - 1) * ld + c] - G[t * ld + c]);
     }
@@ -641,14 +644,16 @@ __global__ __launch_bounds__(64 * (DK / 16)) void bwd_scan_kernel(BackwardArgs b
 // ---------------------------------------------------------------------------
 // 5. bwd_state: U = Ut - W S, dU = scale P^T dO + Kt dX; dQG = scale dO S^T, dW = -dU S^T,
 //    dKt = U dX^T, dP = scale dO U^T (s <= t); dgl = e^(G_L) sum_j S dX.  Over 32-column
-//    blocks of S and dX; wave w owns token block w of every output.
+//    blocks of S and dX.  Eight waves (two per SIMD): wave w owns token block w & 3 of every
+//    output, and half w >> 2 of its column tiles.
 // ---------------------------------------------------------------------------
 constexpr int kVB = 32;
+constexpr int kTS = 512;  // threads of bwd_state
 template <int DK, int DV, class TIn>
-__global__ __launch_bounds__(kT) void bwd_state_kernel(BackwardArgs b) {
+__global__ __launch_bounds__(kTS) void bwd_state_kernel(BackwardArgs b) {
     const PrefillArgs& a = b.fwd;
     constexpr int LK = DK + 4, LC = kC + 4, LB = kVB + 4;
-    constexpr int NKB = DK / 16;
+    constexpr int NKB = DK / 16, HK = NKB / 2;  // dk tiles, per half
     __shared__ __attribute__((aligned(16))) float sW[kC * LK], sK[kC * LK], sP[kC * LC], sS[DK * LB], sX[DK * LB], sO[kC * LB],
         sU[kC * LB], sdU[kC * LB], inv[kC], sgl[DK];
     float* sG = sW;
@@ -656,43 +661,44 @@ __global__ __launch_bounds__(kT) void bwd_state_kernel(BackwardArgs b) {
     Item it;
     if (!item_of(a, static_cast<const char*>(a.workspace), X.ft, blockIdx.x, it)) return;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, H = a.H, item = blockIdx.x;
+    const int tb = wave & 3, half = wave >> 2;
     const int r = lane & 15, q = lane >> 4;
-    load_rows<TIn, DK>(a.k, sK, LK, it, H);
-    gate_cumsum<DK>(a.g, sG, LK, it, H);
-    g2s<kC, kC>(X.blk(item, X.bw.P), kC, sP, LC);
+    load_rows<TIn, DK, DK, kTS>(a.k, sK, LK, it, H);
+    gate_cumsum<DK, kTS>(a.g, sG, LK, it, H);
+    g2s<kC, kC, kTS>(X.blk(item, X.bw.P), kC, sP, LC);
     __syncthreads();
-    normalize_rows(sK, LK, DK, inv, a.use_l2);
-    to_kt(sK, sG, LK, DK);
+    normalize_rows<kTS>(sK, LK, DK, inv, a.use_l2);
+    to_kt<kTS>(sK, sG, LK, DK);
     __syncthreads();
-    g2s<kC, DK>(X.blk(item, X.bw.W), DK, sW, LK);
+    g2s<kC, DK, kTS>(X.blk(item, X.bw.W), DK, sW, LK);
     if (threadIdx.x < DK) sgl[threadIdx.x] = 0.f;
     const float* S = X.blk(item, X.bw.S);
     const float* dX = X.blk(item, X.bw.dX);
     const float* Ut = X.blk(item, X.bw.Ut);
     float* dUg = X.blk(item, X.bw.dU);
-    f32x4 dqg[NKB], dw[NKB], dkt[NKB], dp[4];
-    for (int i = 0; i < NKB; ++i) dqg[i] = dw[i] = dkt[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int i = 0; i < 4; ++i) dp[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    f32x4 dqg[HK], dw[HK], dkt[HK], dp[2];
+    for (int i = 0; i < HK; ++i) dqg[i] = dw[i] = dkt[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < 2; ++i) dp[i] = f32x4{0.f, 0.f, 0.f, 0.f};
     for (int jb = 0; jb < DV / kVB; ++jb) {
         __syncthreads();
-        g2s<DK, kVB>(S + kVB * jb, DV, sS, LB);
-        g2s<DK, kVB>(dX + kVB * jb, DV, sX, LB);
-        load_rows<TIn, DV, kVB>(b.dout, sO, LB, it, H, kVB * jb);
-        g2s<kC, kVB>(Ut + kVB * jb, DV, sU, LB);
+        g2s<DK, kVB, kTS>(S + kVB * jb, DV, sS, LB);
+        g2s<DK, kVB, kTS>(dX + kVB * jb, DV, sX, LB);
+        load_rows<TIn, DV, kVB, kTS>(b.dout, sO, LB, it, H, kVB * jb);
+        g2s<kC, kVB, kTS>(Ut + kVB * jb, DV, sU, LB);
         __syncthreads();
-        // U and dU of this wave's token block
-        for (int cb = 0; cb < kVB / 16; ++cb) {
-            const f32x4 ws = mm16(sW + 16 * wave * LK, LK, 1, sS + 16 * cb, LB, 1, DK, lane, f32x4{0.f, 0.f, 0.f, 0.f});
-            const f32x4 u = get_tile(sU, LB, wave, cb, lane) - ws;
-            f32x4 du = mm16(sP + 16 * wave, 1, LC, sO + 16 * cb, LB, 1, kC, lane, f32x4{0.f, 0.f, 0.f, 0.f}) * a.scale;
-            du = mm16(sK + 16 * wave * LK, LK, 1, sX + 16 * cb, LB, 1, DK, lane, du);
-            __syncthreads();
-            put_tile(sU, LB, wave, cb, u, lane);
-            put_tile(sdU, LB, wave, cb, du, lane);
-            __syncthreads();
+        // U and dU of this wave's token block and column tile (one of the block's two); each
+        // wave reads and writes only its own tile of sU and sdU here
+        {
+            const int cb = half;
+            const f32x4 ws = mm16(sW + 16 * tb * LK, LK, 1, sS + 16 * cb, LB, 1, DK, lane, f32x4{0.f, 0.f, 0.f, 0.f});
+            const f32x4 u = get_tile(sU, LB, tb, cb, lane) - ws;
+            f32x4 du = mm16(sP + 16 * tb, 1, LC, sO + 16 * cb, LB, 1, kC, lane, f32x4{0.f, 0.f, 0.f, 0.f}) * a.scale;
+            du = mm16(sK + 16 * tb * LK, LK, 1, sX + 16 * cb, LB, 1, DK, lane, du);
+            put_tile(sU, LB, tb, cb, u, lane);
+            put_tile(sdU, LB, tb, cb, du, lane);
         }
         __syncthreads();
-        for (int i = threadIdx.x; i < kC * kVB; i += kT)
+        for (int i = threadIdx.x; i < kC * kVB; i += kTS)
             dUg[(i / kVB) * DV + kVB * jb + i % kVB] = sdU[(i / kVB) * LB + i % kVB];
         if (threadIdx.x < DK) {
             float s = 0.f;
@@ -700,37 +706,40 @@ __global__ __launch_bounds__(kT) void bwd_state_kernel(BackwardArgs b) {
             sgl[threadIdx.x] += s;
         }
         // contractions over this block's columns (k = the block's 32 value columns): per k step
-        // the wave's rows of dO, dU and U are read once and serve every output tile
+        // the wave's rows of dO, dU and U are read once and serve its half of the output tiles
         for (int k0 = 0; k0 < kVB; k0 += 4) {
             const int kk = k0 + q;
-            const float ao = sO[(16 * wave + r) * LB + kk], adu = sdU[(16 * wave + r) * LB + kk];
-            const float au = sU[(16 * wave + r) * LB + kk];
+            const float ao = sO[(16 * tb + r) * LB + kk], adu = sdU[(16 * tb + r) * LB + kk];
+            const float au = sU[(16 * tb + r) * LB + kk];
 #pragma unroll
-            for (int cb = 0; cb < NKB; ++cb) {
+            for (int i = 0; i < HK; ++i) {
+                const int cb = HK * half + i;
                 const float bs = sS[(16 * cb + r) * LB + kk], bx = sX[(16 * cb + r) * LB + kk];
-                dqg[cb] = __builtin_amdgcn_mfma_f32_16x16x4f32(ao, bs, dqg[cb], 0, 0, 0);
-                dw[cb] = __builtin_amdgcn_mfma_f32_16x16x4f32(adu, bs, dw[cb], 0, 0, 0);
-                dkt[cb] = __builtin_amdgcn_mfma_f32_16x16x4f32(au, bx, dkt[cb], 0, 0, 0);
+                dqg[i] = __builtin_amdgcn_mfma_f32_16x16x4f32(ao, bs, dqg[i], 0, 0, 0);
+                dw[i] = __builtin_amdgcn_mfma_f32_16x16x4f32(adu, bs, dw[i], 0, 0, 0);
+                dkt[i] = __builtin_amdgcn_mfma_f32_16x16x4f32(au, bx, dkt[i], 0, 0, 0);
             }
 #pragma unroll
-            for (int sb = 0; sb < 4; ++sb)
-                dp[sb] = __builtin_amdgcn_mfma_f32_16x16x4f32(ao, sU[(16 * sb + r) * LB + kk], dp[sb], 0, 0, 0);
+            for (int i = 0; i < 2; ++i)
+                dp[i] = __builtin_amdgcn_mfma_f32_16x16x4f32(ao, sU[(16 * (2 * half + i) + r) * LB + kk], dp[i], 0, 0, 0);
         }
     }
     float* dQG = X.blk(item, X.bw.dQG);
     float* dW = X.blk(item, X.bw.dW);
     float* dKt = X.blk(item, X.bw.dKt);
     float* dP = X.blk(item, X.bw.dP);
-    for (int cb = 0; cb < NKB; ++cb) {
-        put_tile(dQG, DK, wave, cb, dqg[cb] * a.scale, lane);
-        put_tile(dW, DK, wave, cb, -dw[cb], lane);
-        put_tile(dKt, DK, wave, cb, dkt[cb], lane);
+    for (int i = 0; i < HK; ++i) {
+        const int cb = HK * half + i;
+        put_tile(dQG, DK, tb, cb, dqg[i] * a.scale, lane);
+        put_tile(dW, DK, tb, cb, -dw[i], lane);
+        put_tile(dKt, DK, tb, cb, dkt[i], lane);
     }
-    for (int sb = 0; sb < 4; ++sb) {
-        f32x4 v = dp[sb] * a.scale;
+    for (int i = 0; i < 2; ++i) {
+        const int sb = 2 * half + i;
+        f32x4 v = dp[i] * a.scale;
 #pragma unroll
-        for (int ii = 0; ii < 4; ++ii) v[ii] = 16 * sb + r <= 16 * wave + 4 * q + ii ? v[ii] : 0.f;
-        put_tile(dP, kC, wave, sb, v, lane);
+        for (int ii = 0; ii < 4; ++ii) v[ii] = 16 * sb + r <= 16 * tb + 4 * q + ii ? v[ii] : 0.f;
+        put_tile(dP, kC, tb, sb, v, lane);
     }
     __syncthreads();
     if (threadIdx.x < DK) X.blk(item, X.bw.dgl)[threadIdx.x] = X.blk(item, X.bw.gl)[threadIdx.x] * sgl[threadIdx.x];
@@ -966,7 +975,7 @@ hipError_t launch_backward_t(const BackwardArgs& b, hipStream_t stream) {
     hipLaunchKernelGGL((bwd_scan_kernel<DK, DV>), dim3(static_cast<unsigned>(a.num_seqs * a.H * (DV / 16))),
                        dim3(64 * (DK / 16)), 0, stream, b, E);
     if (bw.max_items > 0) {
-        hipLaunchKernelGGL((bwd_state_kernel<DK, DV, TIn>), grid, dim3(kT), 0, stream, b);
+        hipLaunchKernelGGL((bwd_state_kernel<DK, DV, TIn>), grid, dim3(kTS), 0, stream, b);
         hipLaunchKernelGGL((bwd_ut_kernel<DK, DV, TIn>), grid, dim3(kT), 0, stream, b);
         hipLaunchKernelGGL((bwd_final_kernel<DK, DV, TIn>), grid, dim3(kT), 0, stream, b);
     }
