@@ -91,3 +91,25 @@ def test_prefill_snapshot_slots(on):
                        ([[2, 8], [3, -1]], ">= num_slots")):
         with pytest.raises(ValueError, match=msg):
             ops.chunk_prefill(*args, snapshot_every=64, snapshot_slots=torch.tensor(snaps, dtype=torch.int32))
+
+
+def front_tensors(H=2, d=64, num_slots=5, W=4):
+    z = lambda *s: torch.zeros(*s)
+    return dict(gate_scale=z(H), conv_q=z(H, d, W), conv_k=z(H, d, W), conv_v=z(H, d, W),
+                conv_state=z(num_slots, H, W - 1, 3 * d))
+
+
+@pytest.mark.parametrize("slots,msg", [((0, 7, 1), "num_slots"), ((2, 2, 1), "duplicate")])
+def test_decode_front_slots(on, slots, msg):
+    x = decode_inputs()
+    with pytest.raises(ValueError, match=msg):
+        ops.decode_step_front(x["q"], x["k"], x["v"], x["g"], x["beta"], x["state_pool"], i32(*slots),
+                              **front_tensors())
+
+
+@pytest.mark.parametrize("cu,msg", [((0, 4, 11), "total_tokens"), ((1, 4, 10), r"\[0\]")])
+def test_prefill_front_cu_seqlens(on, cu, msg):
+    x = prefill_inputs()
+    with pytest.raises(ValueError, match=msg):
+        ops.chunk_prefill_front(x["q"], x["k"], x["v"], x["g"], x["beta"], i32(*cu), x["state_pool"], i32(0, 1),
+                                **front_tensors(num_slots=4))
