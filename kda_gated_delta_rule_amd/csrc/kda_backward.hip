@@ -499,43 +499,47 @@ __device__ void to_kt(float* K, const float* G, int ld, int DK) {
         K[t * ld + c] *= ex2(G[(kC - 1) * ld + c] - G[t * ld + c]);
     }
 }
+template <int NT = kT>
 __device__ void to_qg(float* Q, const float* G, int ld, int DK) {
-    for (int i = threadIdx.x; i < kC * DK; i += kT) {
+    for (int i = threadIdx.x; i < kC * DK; i += NT) {
         const int t = i / DK, c = i % DK;
         Q[t * ld + c] *= ex2(G[t * ld + c]);
     }
 }
 
 // ---------------------------------------------------------------------------
-// 3. bwd_prep: Mt = diag(e^(G_L)) - W^T Kt,  b = scale (QG - P W)^T dO
+// 3. bwd_prep: Mt = diag(e^(G_L)) - W^T Kt,  b = scale (QG - P W)^T dO.  Eight waves (two
+//    per SIMD) share the output tiles.
 // ---------------------------------------------------------------------------
+constexpr int kTP = 512;  // threads of bwd_prep
 template <int DK, int DV, class TIn>
-__global__ __launch_bounds__(kT) void bwd_prep_kernel(BackwardArgs b) {
+__global__ __launch_bounds__(kTP) void bwd_prep_kernel(BackwardArgs b) {
     const PrefillArgs& a = b.fwd;
-    constexpr int LK = DK + 4, LV = DV + 4, LC = kC + 4;
+    constexpr int LK = DK + 4, LV = DV + 4, LC = kC + 4, NW = kTP / 64, HK = DK / 32;
     __shared__ __attribute__((aligned(16))) float sK[kC * LK], sQ[kC * LK], sW[kC * LK], sO[kC * LV], sP[kC * LC], inv[kC];
     float* sG = sW;  // the gate cumsum lives where W goes once Kt and QG are formed
     const BwCtx X(a, DK, DV, TIn::bytes);
     Item it;
     if (!item_of(a, static_cast<const char*>(a.workspace), X.ft, blockIdx.x, it)) return;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, H = a.H, item = blockIdx.x;
-    load_rows<TIn, DK>(a.k, sK, LK, it, H);
-    load_rows<TIn, DK>(a.q, sQ, LK, it, H);
-    load_rows<TIn, DV>(b.dout, sO, LV, it, H);
-    gate_cumsum<DK>(a.g, sG, LK, it, H);
-    g2s<kC, kC>(X.blk(item, X.bw.P), kC, sP, LC);
+    const int tb = wave & 3, half = wave >> 2;
+    load_rows<TIn, DK, DK, kTP>(a.k, sK, LK, it, H);
+    load_rows<TIn, DK, DK, kTP>(a.q, sQ, LK, it, H);
+    load_rows<TIn, DV, DV, kTP>(b.dout, sO, LV, it, H);
+    gate_cumsum<DK, kTP>(a.g, sG, LK, it, H);
+    g2s<kC, kC, kTP>(X.blk(item, X.bw.P), kC, sP, LC);
     __syncthreads();
-    normalize_rows(sK, LK, DK, inv, a.use_l2);
-    normalize_rows(sQ, LK, DK, inv, a.use_l2);
-    to_kt(sK, sG, LK, DK);
-    to_qg(sQ, sG, LK, DK);
+    normalize_rows<kTP>(sK, LK, DK, inv, a.use_l2);
+    normalize_rows<kTP>(sQ, LK, DK, inv, a.use_l2);
+    to_kt<kTP>(sK, sG, LK, DK);
+    to_qg<kTP>(sQ, sG, LK, DK);
     __syncthreads();
-    g2s<kC, DK>(X.blk(item, X.bw.W), DK, sW, LK);
+    g2s<kC, DK, kTP>(X.blk(item, X.bw.W), DK, sW, LK);
     const float* gl = X.blk(item, X.bw.gl);
     __syncthreads();
     // Mt (dk x dk): tile (rb, cb), rows c = W's columns, k over tokens
     float* Mt = X.blk(item, X.bw.Mt);
-    for (int tI = wave; tI < (DK / 16) * (DK / 16); tI += 4) {
+    for (int tI = wave; tI < (DK / 16) * (DK / 16); tI += NW) {
         const int rb = tI / (DK / 16), cb = tI % (DK / 16);
         f32x4 m = mm16(sW + 16 * rb, 1, LK, sK + 16 * cb, LK, 1, kC, lane, f32x4{0.f, 0.f, 0.f, 0.f});
         const int r = lane & 15, q = lane >> 4;
@@ -546,17 +550,17 @@ __global__ __launch_bounds__(kT) void bwd_prep_kernel(BackwardArgs b) {
         }
         put_tile(Mt, DK, rb, cb, m, lane);
     }
-    // Q' = QG - P W (wave: its token block, all channel tiles), in place over QG
-    __syncthreads();
-    f32x4 qp[DK / 16];
-    for (int cb = 0; cb < DK / 16; ++cb)
-        qp[cb] = mm16(sP + 16 * wave * LC, LC, 1, sW + 16 * cb, LK, 1, kC, lane, f32x4{0.f, 0.f, 0.f, 0.f});
-    __syncthreads();
-    for (int cb = 0; cb < DK / 16; ++cb) put_tile(sQ, LK, wave, cb, get_tile(sQ, LK, wave, cb, lane) - qp[cb], lane);
+    // Q' = QG - P W in place over QG: wave (tb, half) takes token block tb and half of the
+    // channel tiles (only it reads or writes those tiles of sQ here)
+    for (int i = 0; i < HK; ++i) {
+        const int cb = HK * half + i;
+        const f32x4 pw = mm16(sP + 16 * tb * LC, LC, 1, sW + 16 * cb, LK, 1, kC, lane, f32x4{0.f, 0.f, 0.f, 0.f});
+        put_tile(sQ, LK, tb, cb, get_tile(sQ, LK, tb, cb, lane) - pw, lane);
+    }
     __syncthreads();
     // b = scale Q'^T dO (dk x dv)
     float* bb = X.blk(item, X.bw.b);
-    for (int tI = wave; tI < (DK / 16) * (DV / 16); tI += 4) {
+    for (int tI = wave; tI < (DK / 16) * (DV / 16); tI += NW) {
         const int rb = tI / (DV / 16), cb = tI % (DV / 16);
         const f32x4 v = mm16(sQ + 16 * rb, 1, LK, sO + 16 * cb, LV, 1, kC, lane, f32x4{0.f, 0.f, 0.f, 0.f});
         put_tile(bb, DV, rb, cb, v * a.scale, lane);
@@ -970,7 +974,7 @@ hipError_t launch_backward_t(const BackwardArgs& b, hipStream_t stream) {
     const dim3 grid(static_cast<unsigned>(bw.max_items));
     if (bw.max_items > 0) {
         hipLaunchKernelGGL((bwd_intra_kernel<DK, DV, TIn>), grid, dim3(kT), 0, stream, b);
-        hipLaunchKernelGGL((bwd_prep_kernel<DK, DV, TIn>), grid, dim3(kT), 0, stream, b);
+        hipLaunchKernelGGL((bwd_prep_kernel<DK, DV, TIn>), grid, dim3(kTP), 0, stream, b);
     }
     hipLaunchKernelGGL((bwd_scan_kernel<DK, DV>), dim3(static_cast<unsigned>(a.num_seqs * a.H * (DV / 16))),
                        dim3(64 * (DK / 16)), 0, stream, b, E);
