@@ -49,6 +49,7 @@ namespace {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kC = 64;
+constexpr int kXcd = 8;  // XCDs of the GPU (workgroups are dispatched to them round-robin)
 constexpr int kT = 256;  // threads of every per-chunk kernel (4 waves)
 constexpr float kL2e = 1.4426950408889634f;
 constexpr float kEps = 1e-6f;
@@ -203,9 +204,9 @@ __device__ void normalize_rows(float* x, int ld, int D, float* inv, int use_l2) 
         for (int c = 0; c < D; ++c) s = fmaf(x[t * ld + c], x[t * ld + c], s);
         inv[t] = use_l2 ? 1.f / sqrtf(s + kEps) : 1.f;
     }
-    __syncthreads();
+    lds_barrier();
     for (int i = threadIdx.x; i < kC * D; i += NT) x[(i / D) * ld + i % D] *= inv[i / D];
-    __syncthreads();
+    lds_barrier();
 }
 
 // G [64][ld] = in-chunk inclusive cumsum of g, in log2 units (rows from L on repeat G_L).
@@ -214,7 +215,7 @@ __device__ void normalize_rows(float* x, int ld, int D, float* inv, int use_l2) 
 template <int DK, int NT = kT>
 __device__ void gate_cumsum(const float* g, float* G, int ld, const Item& it, int H) {
     load_rows<F32, DK, DK, NT>(g, G, ld, it, H);
-    __syncthreads();
+    lds_barrier();
     const int lane = threadIdx.x & 63;
     for (int c = threadIdx.x >> 6; c < DK; c += NT / 64) G[lane * ld + c] = wave_prefix64(G[lane * ld + c] * kL2e);
 }
@@ -340,7 +341,7 @@ __device__ void unit_lower_inverse(const float* Ag, const float* beta, float* T,
             for (int rr = 0; rr < 16; ++rr) T[(b0 + rr) * LC + b0 + col] = x[rr];
         }
     }
-    __syncthreads();
+    lds_barrier();
     float* y = Y + wave * 16 * LY;
     for (int d = 1; d < 4; ++d) {
         if (wave >= d) {
@@ -355,7 +356,7 @@ __device__ void unit_lower_inverse(const float* Ag, const float* beta, float* T,
             const f32x4 z = mm16(T + 16 * wave * LC + 16 * wave, LC, 1, y, LY, 1, 16, lane, f32x4{0.f, 0.f, 0.f, 0.f});
             put_tile(T + 16 * wave * LC + 16 * jb, LC, 0, 0, -z, lane);
         }
-        __syncthreads();
+        lds_barrier();
     }
 }
 
@@ -439,7 +440,7 @@ __global__ __launch_bounds__(kT) void bwd_intra_kernel(BackwardArgs b) {
     load_rows<TIn, DK>(a.q, sQ, LK, it, H);
     gate_cumsum<DK>(a.g, sG, LK, it, H);
     if (threadIdx.x < kC) sB[threadIdx.x] = threadIdx.x < it.L ? a.beta[static_cast<int64_t>(it.t0 + threadIdx.x) * H + it.h] : 0.f;
-    __syncthreads();
+    lds_barrier();
     normalize_rows(sK, LK, DK, inv, a.use_l2);
     normalize_rows(sQ, LK, DK, inv, a.use_l2);
     // Ag (strictly lower) and P (lower with the diagonal), tile (i, j <= i) by the wave owning
@@ -463,7 +464,7 @@ __global__ __launch_bounds__(kT) void bwd_intra_kernel(BackwardArgs b) {
         put_tile(Pg, kC, i, j, tp, lane);
         put_tile(Ag, kC, i, j, ta, lane);
     }
-    __syncthreads();
+    lds_barrier();
     unit_lower_inverse(sA, sB, sT, sY, lane, wave);
     s2g<kC, kC>(sT, LC, X.blk(item, X.bw.T), kC);
     // BK = beta kh 2^G into sQ (P is done), then W = T BK
@@ -472,18 +473,18 @@ __global__ __launch_bounds__(kT) void bwd_intra_kernel(BackwardArgs b) {
         sQ[t * LK + c] = sB[t] * sK[t * LK + c] * ex2(sG[t * LK + c]);
     }
     if (threadIdx.x < DK) X.blk(item, X.bw.gl)[threadIdx.x] = ex2(sG[(kC - 1) * LK + threadIdx.x]);
-    __syncthreads();
+    lds_barrier();
     float* Wg = X.blk(item, X.bw.W);
     for (int cb = 0; cb < DK / 16; ++cb) {
         const f32x4 w = mm16(sT + 16 * wave * LC, LC, 1, sQ + 16 * cb, LK, 1, kC, lane, f32x4{0.f, 0.f, 0.f, 0.f});
         put_tile(Wg, DK, wave, cb, w, lane);
     }
-    __syncthreads();
+    lds_barrier();
     // BV = beta v into sK, then Ut = T BV
     load_rows<TIn, DV>(a.v, sK, LV, it, H);
-    __syncthreads();
+    lds_barrier();
     for (int i = threadIdx.x; i < kC * DV; i += kT) sK[(i / DV) * LV + i % DV] *= sB[i / DV];
-    __syncthreads();
+    lds_barrier();
     float* Ug = X.blk(item, X.bw.Ut);
     for (int cb = 0; cb < DV / 16; ++cb) {
         const f32x4 u = mm16(sT + 16 * wave * LC, LC, 1, sK + 16 * cb, LV, 1, kC, lane, f32x4{0.f, 0.f, 0.f, 0.f});
@@ -528,15 +529,15 @@ __global__ __launch_bounds__(kTP) void bwd_prep_kernel(BackwardArgs b) {
     load_rows<TIn, DV, DV, kTP>(b.dout, sO, LV, it, H);
     gate_cumsum<DK, kTP>(a.g, sG, LK, it, H);
     g2s<kC, kC, kTP>(X.blk(item, X.bw.P), kC, sP, LC);
-    __syncthreads();
+    lds_barrier();
     normalize_rows<kTP>(sK, LK, DK, inv, a.use_l2);
     normalize_rows<kTP>(sQ, LK, DK, inv, a.use_l2);
     to_kt<kTP>(sK, sG, LK, DK);
     to_qg<kTP>(sQ, sG, LK, DK);
-    __syncthreads();
+    lds_barrier();
     g2s<kC, DK, kTP>(X.blk(item, X.bw.W), DK, sW, LK);
     const float* gl = X.blk(item, X.bw.gl);
-    __syncthreads();
+    lds_barrier();
     // Mt (dk x dk): tile (rb, cb), rows c = W's columns, k over tokens
     float* Mt = X.blk(item, X.bw.Mt);
     for (int tI = wave; tI < (DK / 16) * (DK / 16); tI += NW) {
@@ -557,7 +558,7 @@ __global__ __launch_bounds__(kTP) void bwd_prep_kernel(BackwardArgs b) {
         const f32x4 pw = mm16(sP + 16 * tb * LC, LC, 1, sW + 16 * cb, LK, 1, kC, lane, f32x4{0.f, 0.f, 0.f, 0.f});
         put_tile(sQ, LK, tb, cb, get_tile(sQ, LK, tb, cb, lane) - pw, lane);
     }
-    __syncthreads();
+    lds_barrier();
     // b = scale Q'^T dO (dk x dv)
     float* bb = X.blk(item, X.bw.b);
     for (int tI = wave; tI < (DK / 16) * (DV / 16); tI += NW) {
@@ -580,7 +581,10 @@ __global__ __launch_bounds__(64 * (DK / 16)) void bwd_scan_kernel(BackwardArgs b
     const BwCtx X(a, DK, DV, e);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int r = lane & 15, q4 = 4 * (lane >> 4);
-    const int H = a.H, grp = blockIdx.x / NTS, tile = blockIdx.x % NTS;
+    // The NTS column tiles of one (sequence, head) read the same Mt: their block ids are
+    // congruent mod kXcd, so they run on one XCD and read each Mt from its L2 (round-robin
+    // dispatch over the XCDs by block id); the grid is padded to whole groups of kXcd.
+    const int H = a.H, j = blockIdx.x / kXcd, tile = j % NTS, grp = (j / NTS) * kXcd + blockIdx.x % kXcd;
     const int seq = grp / H, h = grp % H;
     if (seq >= a.num_seqs) return;
     const int c0 = X.ft.chunk_off[seq], nch = X.ft.chunk_off[seq + 1] - c0;
@@ -613,7 +617,8 @@ __global__ __launch_bounds__(64 * (DK / 16)) void bwd_scan_kernel(BackwardArgs b
         for (int rr = 0; rr < 4; ++rr) dX[(16 * wave + q4 + rr) * DV + col] = x[rr];
         load(fill, c >= 2 ? c - 2 : 0);  // (a valid chunk when none is left)
         *reinterpret_cast<f32x4*>(xs + r * LX + 16 * wave + q4) = x;
-        __syncthreads();
+        // LDS-only barriers: a __syncthreads() would also wait for the loads just issued
+        lds_barrier();
         // lane (r, q) supplies k = 16 kb + 4q + ks of Mt row 16 wave + r and of X column r;
         // four independent accumulator chains (one per ks)
         f32x4 acc[4] = {cur.bb, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
@@ -624,7 +629,7 @@ __global__ __launch_bounds__(64 * (DK / 16)) void bwd_scan_kernel(BackwardArgs b
             for (int ks = 0; ks < 4; ++ks)
                 acc[ks] = __builtin_amdgcn_mfma_f32_16x16x4f32(cur.mt[kb][ks], xb[ks], acc[ks], 0, 0, 0);
         }
-        __syncthreads();
+        lds_barrier();
         x = (acc[0] + acc[1]) + (acc[2] + acc[3]);
         return true;
     };
@@ -670,10 +675,10 @@ __global__ __launch_bounds__(kTS) void bwd_state_kernel(BackwardArgs b) {
     load_rows<TIn, DK, DK, kTS>(a.k, sK, LK, it, H);
     gate_cumsum<DK, kTS>(a.g, sG, LK, it, H);
     g2s<kC, kC, kTS>(X.blk(item, X.bw.P), kC, sP, LC);
-    __syncthreads();
+    lds_barrier();
     normalize_rows<kTS>(sK, LK, DK, inv, a.use_l2);
     to_kt<kTS>(sK, sG, LK, DK);
-    __syncthreads();
+    lds_barrier();
     g2s<kC, DK, kTS>(X.blk(item, X.bw.W), DK, sW, LK);
     if (threadIdx.x < DK) sgl[threadIdx.x] = 0.f;
     const float* S = X.blk(item, X.bw.S);
@@ -684,12 +689,12 @@ __global__ __launch_bounds__(kTS) void bwd_state_kernel(BackwardArgs b) {
     for (int i = 0; i < HK; ++i) dqg[i] = dw[i] = dkt[i] = f32x4{0.f, 0.f, 0.f, 0.f};
     for (int i = 0; i < 2; ++i) dp[i] = f32x4{0.f, 0.f, 0.f, 0.f};
     for (int jb = 0; jb < DV / kVB; ++jb) {
-        __syncthreads();
+        lds_barrier();
         g2s<DK, kVB, kTS>(S + kVB * jb, DV, sS, LB);
         g2s<DK, kVB, kTS>(dX + kVB * jb, DV, sX, LB);
         load_rows<TIn, DV, kVB, kTS>(b.dout, sO, LB, it, H, kVB * jb);
         g2s<kC, kVB, kTS>(Ut + kVB * jb, DV, sU, LB);
-        __syncthreads();
+        lds_barrier();
         // U and dU of this wave's token block and column tile (one of the block's two); each
         // wave reads and writes only its own tile of sU and sdU here
         {
@@ -701,7 +706,7 @@ __global__ __launch_bounds__(kTS) void bwd_state_kernel(BackwardArgs b) {
             put_tile(sU, LB, tb, cb, u, lane);
             put_tile(sdU, LB, tb, cb, du, lane);
         }
-        __syncthreads();
+        lds_barrier();
         for (int i = threadIdx.x; i < kC * kVB; i += kTS)
             dUg[(i / kVB) * DV + kVB * jb + i % kVB] = sdU[(i / kVB) * LB + i % kVB];
         if (threadIdx.x < DK) {
@@ -745,7 +750,7 @@ __global__ __launch_bounds__(kTS) void bwd_state_kernel(BackwardArgs b) {
         for (int ii = 0; ii < 4; ++ii) v[ii] = 16 * sb + r <= 16 * tb + 4 * q + ii ? v[ii] : 0.f;
         put_tile(dP, kC, tb, sb, v, lane);
     }
-    __syncthreads();
+    lds_barrier();
     if (threadIdx.x < DK) X.blk(item, X.bw.dgl)[threadIdx.x] = X.blk(item, X.bw.gl)[threadIdx.x] * sgl[threadIdx.x];
 }
 
@@ -775,11 +780,11 @@ __global__ __launch_bounds__(kT) void bwd_ut_kernel(BackwardArgs b) {
         sB[threadIdx.x] = threadIdx.x < it.L ? a.beta[static_cast<int64_t>(it.t0 + threadIdx.x) * H + it.h] : 0.f;
     }
     g2s<kC, kC>(X.blk(item, X.bw.T), kC, sT, LC);
-    __syncthreads();
+    lds_barrier();
     normalize_rows(sM2, LK, DK, inv, a.use_l2);
     to_qg(sM2, sG, LK, DK);  // kh 2^G
     g2s<kC, DK>(X.blk(item, X.bw.dW), DK, sM1, LK);
-    __syncthreads();
+    lds_barrier();
     // dT (part 1: dW BK^T, BK = beta KG, so column s takes beta_s) and dBK of this wave's
     // rows; dbeta part sum_c KG dBK
     f32x4 dT[4];
@@ -795,13 +800,13 @@ __global__ __launch_bounds__(kT) void bwd_ut_kernel(BackwardArgs b) {
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) part[ii] = fmaf(kg[ii], v[ii], part[ii]);
     }
-    __syncthreads();
+    lds_barrier();
     // BV = beta v (sM2) and dU (sM1)
     load_rows<TIn, DV>(a.v, sM2, LV, it, H);
     g2s<kC, DV>(X.blk(item, X.bw.dU), DV, sM1, LV);
-    __syncthreads();
+    lds_barrier();
     for (int i = threadIdx.x; i < kC * DV; i += kT) sM2[(i / DV) * LV + i % DV] *= sB[i / DV];
-    __syncthreads();
+    lds_barrier();
     for (int sb = 0; sb < 4; ++sb)
         dT[sb] = mm16(sM1 + 16 * wave * LV, LV, 1, sM2 + 16 * sb * LV, 1, LV, DV, lane, dT[sb]);
     // dBV = T^T dU: dv = beta dBV, dbeta part sum_j v dBV = sum_j BV dBV / beta (v from BV)
@@ -819,10 +824,10 @@ __global__ __launch_bounds__(kT) void bwd_ut_kernel(BackwardArgs b) {
     }
     // dT to LDS; E = T^T dT; dA = -(E T^T) (s < t)
     for (int sb = 0; sb < 4; ++sb) put_tile(sD, LC, wave, sb, dT[sb], lane);
-    __syncthreads();
+    lds_barrier();
     for (int sb = 0; sb < 4; ++sb)
         put_tile(sE, LC, wave, sb, mm16(sT + 16 * wave, 1, LC, sD + 16 * sb, LC, 1, kC, lane, f32x4{0.f, 0.f, 0.f, 0.f}), lane);
-    __syncthreads();
+    lds_barrier();
     const float* Ag = X.blk(item, X.bw.Ag);
     float* dAg = X.blk(item, X.bw.dAg);
     for (int sb = 0; sb < 4; ++sb) {
@@ -870,7 +875,7 @@ __global__ __launch_bounds__(kT) void bwd_final_kernel(BackwardArgs b) {
     g2s<kC, kC>(X.blk(item, X.bw.dAg), kC, sA, LC);
     g2s<kC, kC>(X.blk(item, X.bw.dP), kC, sP, LC);
     if (threadIdx.x < kC) sB[threadIdx.x] = threadIdx.x < it.L ? a.beta[static_cast<int64_t>(it.t0 + threadIdx.x) * H + it.h] : 0.f;
-    __syncthreads();
+    lds_barrier();
     normalize_rows(sK, LK, DK, ik, a.use_l2);
     normalize_rows(sQ, LK, DK, iq, a.use_l2);
     const float* dBK = X.blk(item, X.bw.dBK);
@@ -933,9 +938,9 @@ __global__ __launch_bounds__(kT) void bwd_final_kernel(BackwardArgs b) {
     }
     // dG_L = dgl + sum_t Kt dKt: the per-lane sums reduced over q (the 4 row groups of a wave)
     // and over the waves through LDS
-    __syncthreads();  // sG's values are no longer read below this point
+    lds_barrier();  // sG's values are no longer read below this point
     if (threadIdx.x < DK) sGL[threadIdx.x] = X.blk(item, X.bw.dgl)[threadIdx.x];
-    __syncthreads();
+    lds_barrier();
     for (int cb = 0; cb < NKB; ++cb) {
         float x = ktdkt[cb];
         x += __shfl_xor(x, 16, 64);
@@ -944,7 +949,7 @@ __global__ __launch_bounds__(kT) void bwd_final_kernel(BackwardArgs b) {
     }
     // dG into sG (rows of this wave), then the reverse cumsum per channel plus dG_L
     for (int cb = 0; cb < NKB; ++cb) put_tile(sG, LK, wave, cb, dG[cb], lane);
-    __syncthreads();
+    lds_barrier();
     // suffix sums over the live rows (lane = token): total - inclusive prefix + own value
     for (int c = wave; c < DK; c += kT / 64) {
         const float v = lane < it.L ? sG[lane * LK + c] : 0.f;
@@ -952,7 +957,7 @@ __global__ __launch_bounds__(kT) void bwd_final_kernel(BackwardArgs b) {
         const float tot = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(incl), 63));
         sG[lane * LK + c] = (tot - incl + v) + sGL[c];
     }
-    __syncthreads();
+    lds_barrier();
     for (int i = threadIdx.x; i < it.L * DK; i += kT) {
         const int t = i / DK, c = i % DK;
         b.dg[(static_cast<int64_t>(it.t0 + t) * H + it.h) * DK + c] = sG[t * LK + c];
@@ -976,7 +981,8 @@ hipError_t launch_backward_t(const BackwardArgs& b, hipStream_t stream) {
         hipLaunchKernelGGL((bwd_intra_kernel<DK, DV, TIn>), grid, dim3(kT), 0, stream, b);
         hipLaunchKernelGGL((bwd_prep_kernel<DK, DV, TIn>), grid, dim3(kTP), 0, stream, b);
     }
-    hipLaunchKernelGGL((bwd_scan_kernel<DK, DV>), dim3(static_cast<unsigned>(a.num_seqs * a.H * (DV / 16))),
+    const int sgroups = (a.num_seqs * a.H + kXcd - 1) / kXcd;
+    hipLaunchKernelGGL((bwd_scan_kernel<DK, DV>), dim3(static_cast<unsigned>(sgroups) * kXcd * (DV / 16)),
                        dim3(64 * (DK / 16)), 0, stream, b, E);
     if (bw.max_items > 0) {
         hipLaunchKernelGGL((bwd_state_kernel<DK, DV, TIn>), grid, dim3(kTS), 0, stream, b);
