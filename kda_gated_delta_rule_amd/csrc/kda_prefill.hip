@@ -68,7 +68,10 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kCarryBV = 32;  // dv columns per Ut record tile
-constexpr int kCarryNB = 2;   // chunks whose operands the carry has in flight
+// chunks of record granules a carry wave holds in registers: with 1, a chunk's granules load
+// right after the previous step (measured faster than 2, whose extra registers cost the
+// step its batching of LDS operand reads)
+constexpr int kCarryNB = 1;
 constexpr int kNumXcd = 8;    // MI355X: 8 XCDs, workgroups dispatched round-robin
 constexpr float kNormEps = 1e-6f;
 constexpr int kBufFlags = 0x00020000;  // raw buffer resource word 3 (gfx9 family)
@@ -304,7 +307,7 @@ __global__ __launch_bounds__(kThreads) void chunk_map_kernel(const int32_t* __re
 //     R2  KG^T [DK][LDT]
 //   R3  V^T [DV][LDT]
 //   RM  beta [64], key norm factors [64], per-wave gate totals, in-wave gate cumsums at
-//       token 7, and 2^totals [4][DK] each
+//       token 7, 2^totals [4][DK] each, and per wave 2^(G at its start) [4][DK]
 // (bf16, dk = dv = 128: 72.5 KiB, so two workgroups share a CU.)  The rest of A stays in
 // the registers of the wave that owns its rows; the QG and Kt record granules are built
 // in registers by MFMA products with a 0/1 selector (exact), without an LDS transpose.
@@ -325,7 +328,7 @@ struct IntraPlan {
     static constexpr int LDD = 20;  // fp32 diagonal-block rows (16 + 4, 16-byte aligned)
     static constexpr size_t RD = align_up(4ull * 16 * LDD * 4, 16);
     static constexpr size_t RT = align_up(64ull * LDT * E, 16);
-    static constexpr size_t RM = align_up(4ull * (2 * 64 + 13 * DK), 16);
+    static constexpr size_t RM = align_up(4ull * (2 * 64 + 17 * DK), 16);
     static constexpr size_t O1 = 0, OD = O1 + R1, OT = OD + RD, O2 = OT + RT, O3 = O2 + R2;
     static constexpr size_t OM = O3 + R3;
     static constexpr size_t BYTES = OM + RM;
@@ -550,6 +553,7 @@ __device__ __forceinline__ void intra_compute(const IntraIn<DK, DV, TIn>& X, cha
     float* sTot = sIk + 64;       // [wave][DK] the wave's gate total (log2 units)
     float* sMid = sTot + 4 * DK;  // [wave][DK] the in-wave gate cumsum at the wave's token 7
     float* sT2 = sMid + 4 * DK;   // [1 + wave][DK] 2^(the wave's gate total); row 0 = 1
+    float* sPW = sT2 + 5 * DK + wave * DK;  // [wave][DK] 2^(G_end(wave - 1) - chunk start)
 
     const int r = lane & 15, q = lane >> 4, t = 16 * wave + r;
 
@@ -673,6 +677,10 @@ __device__ __forceinline__ void intra_compute(const IntraIn<DK, DV, TIn>& X, cha
     const int c1 = 8 * (wave + 1) * wave + t, c2 = 8 * (wave + 2) * (wave + 1) + t, c3 = 48 + t;
     u32x4 KBh[NGK], KBl[NGK], QBh[NGK], QBl[NGK];
     f32x4 Adg = {0.f, 0.f, 0.f, 0.f}, Pdg = Adg;
+    // this wave's chunk-start factors per channel, formed once (not by each of the 16 lanes
+    // holding a channel); only this wave reads them, after its own writes
+    for (int c = lane; c < DK; c += kWave) sPW[c] = sT2[p1 + c] * sT2[p2 + c] * sT2[p3 + c];
+    asm volatile("" ::: "memory");
     {
         float* gl_out = reinterpret_cast<float*>(rec + ws.o_gl);
 #pragma unroll
@@ -684,9 +692,7 @@ __device__ __forceinline__ void intra_compute(const IntraIn<DK, DV, TIn>& X, cha
 #pragma unroll
             for (int m = 0; m < GW / 4; ++m) {
                 const int c = GW * (4 * j + q) + 4 * m;
-                const f32x4 P1 = *reinterpret_cast<const f32x4*>(sT2 + p1 + c);
-                const f32x4 P2 = *reinterpret_cast<const f32x4*>(sT2 + p2 + c);
-                const f32x4 P3 = *reinterpret_cast<const f32x4*>(sT2 + p3 + c);
+                const f32x4 PW = *reinterpret_cast<const f32x4*>(sPW + c);
                 const f32x4 N1 = *reinterpret_cast<const f32x4*>(sT2 + n1 + c);
                 const f32x4 N2 = *reinterpret_cast<const f32x4*>(sT2 + n2 + c);
                 const f32x4 N3 = *reinterpret_cast<const f32x4*>(sT2 + n3 + c);
@@ -697,7 +703,7 @@ __device__ __forceinline__ void intra_compute(const IntraIn<DK, DV, TIn>& X, cha
                     const int i = 4 * m + e;
                     const float G = gf[j][i];
                     // 2^(G_t - chunk start) and 2^(G_L - G_t) from the block factors
-                    const float pw = P1[e] * P2[e] * P3[e];
+                    const float pw = PW[e];
                     const float kw = N1[e] * N2[e] * N3[e];
                     const float et = __builtin_amdgcn_exp2f(G);           // 2^(G_t - G_end(i-1))
                     const float kif = __builtin_amdgcn_exp2f(tw[e] - G);  // 2^(G_end(i) - G_t)
@@ -827,13 +833,11 @@ __device__ __forceinline__ void intra_compute(const IntraIn<DK, DV, TIn>& X, cha
 #pragma unroll
         for (int m = 0; m < GW / 4; ++m) {
             const int c = GW * (4 * j + q) + 4 * m;
-            const f32x4 P1 = *reinterpret_cast<const f32x4*>(sT2 + p1 + c);
-            const f32x4 P2 = *reinterpret_cast<const f32x4*>(sT2 + p2 + c);
-            const f32x4 P3 = *reinterpret_cast<const f32x4*>(sT2 + p3 + c);
+            const f32x4 PW = *reinterpret_cast<const f32x4*>(sPW + c);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int i = 4 * m + e;
-                kg[i] = (E == 2 ? kg[i] + lo[i] : kg[i]) * (ik * (P1[e] * P2[e] * P3[e]));
+                kg[i] = (E == 2 ? kg[i] + lo[i] : kg[i]) * (ik * PW[e]);
             }
         }
         const u32x4 KG = f32_to_gran(kg, tag);
@@ -976,8 +980,12 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_intra_kernel(PrefillArgs a)
     // cu_seqlens, copied once), and workgroup 0 also writes the workspace tables the segment
     // kernels read.  Larger batches: chunk_map_kernel ran first and each item reads its entry
     // of the chunk table.
-    __shared__ int32_t m_cu[kThreads + 1], m_coff[kThreads + 1], m_soff[kThreads + 1], m_part[kThreads];
+    __shared__ int32_t m_cu[kThreads + 1], m_coff[kThreads + 1];
     __shared__ int32_t m_carry;
+    // used only before the item loop: over the phase regions
+    int32_t* m_soff = reinterpret_cast<int32_t*>(smem);
+    int32_t* m_part = m_soff + kThreads + 1;
+    static_assert(sizeof(int32_t) * (2 * kThreads + 1) <= P::BYTES, "scan arrays exceed the phase regions");
     const bool inl = map_inline(ns);
     if (inl) {
         for (int i = tid; i <= ns; i += kThreads) m_cu[i] = a.cu_seqlens[i];
@@ -998,6 +1006,7 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_intra_kernel(PrefillArgs a)
             write_chunk_tables(m_cu, ns, seg, m_coff, m_soff, table,
                                reinterpret_cast<int4*>(static_cast<char*>(a.workspace) + ws.off_segtab));
         }
+        __syncthreads();  // m_soff and m_part are dead before any phase writes their LDS
     }
     const int total = (inl ? m_coff[ns] : chunk_off[ns]) * H;
     for (int item = blockIdx.x; item < total; item += stride) {
@@ -1055,10 +1064,10 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_intra_kernel(PrefillArgs a)
 //    Where [S | Phi] does not fit one CU's LDS (fp32 inputs, dk = 128), the local pass
 //    splits the columns over two workgroups (SPLIT = 2; the columns are independent
 //    through a chunk step): each takes half of the column blocks, and wave w computes
-//    token block w & 3 of U for half of its workgroup's blocks.  Its
-//    record granules go from the workspace into registers NB chunks ahead of their
-//    use (issued unconditionally, clamped to the segment's last chunk); ragged output
-//    rows are dropped by the buffer range check.  S and U cross between waves
+//    token block w & 3 of U for half of its workgroup's blocks.  A wave's record
+//    granules go from the workspace into registers for the next NB chunks (issued
+//    unconditionally, clamped to the segment's last chunk); ragged output rows are
+//    dropped by the buffer range check.  S and U cross between waves
 //    through LDS as whole granules.
 // ---------------------------------------------------------------------------
 constexpr int kSegThreads = 512;
