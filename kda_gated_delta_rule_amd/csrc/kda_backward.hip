@@ -249,49 +249,53 @@ __device__ f32x4 dgram_tile(const float* X, const float* Y, const float* G, int 
 // diagonal split the factor at a block end (t mode: the end of block i - 1; s mode: the end
 // of block i), the diagonal block at its 8th token.  Lane holds (row 16 i + 4q + ii, channel
 // 16 cb + r).
-template <bool TMODE>
-__device__ f32x4 dtok_tile(const float* X, int ldx, const float* Z, const float* G, int ld, int i, int cb, int lane) {
+// Two such products of one mode are formed together, sharing their exponentials: ya from
+// (Xa, Za), yb from (Xb, Zb); with SAMEZ (Zb = Za) they also share the B operand.
+template <bool TMODE, bool SAMEZ>
+__device__ void dtok_pair(const float* Xa, const float* Xb, int ldx, const float* Za, const float* Zb,
+                          const float* G, int ld, int i, int cb, int lane, f32x4& ya, f32x4& yb) {
     const int r = lane & 15, q = lane >> 4, ch = 16 * cb + r;
     const int Roff = TMODE ? 16 * i - 1 : 16 * i + 15, M = 16 * i + 7;
-    // two independent accumulator chains each for the off-diagonal and the diagonal part
-    f32x4 off2[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}}, dg2[2] = {off2[0], off2[1]};
+    const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
+    // per product two independent accumulator chains each for the off-diagonal and the
+    // diagonal part
+    f32x4 oa[2] = {z4, z4}, ob[2] = {z4, z4}, da[2] = {z4, z4}, db[2] = {z4, z4};
+    auto kstep = [&](int k, float ref, f32x4& ca, f32x4& cb2) {
+        const float xa = TMODE ? Xa[(16 * i + r) * ldx + k] : Xa[k * ldx + 16 * i + r];
+        const float xb = TMODE ? Xb[(16 * i + r) * ldx + k] : Xb[k * ldx + 16 * i + r];
+        const float g = G[k * ld + ch];
+        const float zf = TMODE ? ex2(ref - g) : ex2(g - ref);
+        const float za = Za[k * ld + ch] * zf;
+        const float zb = SAMEZ ? za : Zb[k * ld + ch] * zf;
+        ca = __builtin_amdgcn_mfma_f32_16x16x4f32(xa, za, ca, 0, 0, 0);
+        cb2 = __builtin_amdgcn_mfma_f32_16x16x4f32(xb, zb, cb2, 0, 0, 0);
+    };
     // off-diagonal blocks: t mode the s blocks before i, s mode the t blocks after i
     const int kb = TMODE ? 0 : 16 * (i + 1), ke = TMODE ? 16 * i : kC;
     if (ke > kb) {
         const float ref = G[Roff * ld + ch];
         for (int k0 = kb; k0 < ke; k0 += 8) {
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const int k = k0 + 4 * h + q;  // s (t mode) or t (s mode)
-                const float av = TMODE ? X[(16 * i + r) * ldx + k] : X[k * ldx + 16 * i + r];
-                const float zf = TMODE ? ex2(ref - G[k * ld + ch]) : ex2(G[k * ld + ch] - ref);
-                off2[h] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, Z[k * ld + ch] * zf, off2[h], 0, 0, 0);
-            }
+            for (int h = 0; h < 2; ++h) kstep(k0 + 4 * h + q, ref, oa[h], ob[h]);
         }
     }
     {
         const float ref = G[M * ld + ch];
         for (int k0 = 16 * i; k0 < 16 * i + 16; k0 += 8) {
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const int k = k0 + 4 * h + q;
-                const float av = TMODE ? X[(16 * i + r) * ldx + k] : X[k * ldx + 16 * i + r];
-                const float zf = TMODE ? ex2(ref - G[k * ld + ch]) : ex2(G[k * ld + ch] - ref);
-                dg2[h] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, Z[k * ld + ch] * zf, dg2[h], 0, 0, 0);
-            }
+            for (int h = 0; h < 2; ++h) kstep(k0 + 4 * h + q, ref, da[h], db[h]);
         }
     }
-    const f32x4 off = off2[0] + off2[1], dg = dg2[0] + dg2[1];
-    f32x4 y;
+    const f32x4 offa = oa[0] + oa[1], offb = ob[0] + ob[1], dga = da[0] + da[1], dgb = db[0] + db[1];
     const float ro = ke > kb ? G[Roff * ld + ch] : 0.f, rm = G[M * ld + ch];
 #pragma unroll
     for (int ii = 0; ii < 4; ++ii) {
         const float gr = G[(16 * i + 4 * q + ii) * ld + ch];
         const float fo = ke > kb ? (TMODE ? ex2(gr - ro) : ex2(ro - gr)) : 0.f;
         const float fm = TMODE ? ex2(gr - rm) : ex2(rm - gr);
-        y[ii] = off[ii] * fo + dg[ii] * fm;
+        ya[ii] = offa[ii] * fo + dga[ii] * fm;
+        yb[ii] = offb[ii] * fo + dgb[ii] * fm;
     }
-    return y;
 }
 
 // Stores a 16 x 16 accumulator tile (rows 16 rb + 4q + ii, columns 16 cb + r) to a row-major
@@ -885,10 +889,9 @@ __global__ __launch_bounds__(kT) void bwd_final_kernel(BackwardArgs b) {
     f32x4 dkh[NKB], dqh[NKB], dG[NKB];
     float ktdkt[NKB];  // sum over this lane's rows of Kt dKt (for dG_L)
     for (int cb = 0; cb < NKB; ++cb) {
-        const f32x4 x1 = dtok_tile<true>(sA, LC, sK, sG, LK, wave, cb, lane);
-        const f32x4 x2 = dtok_tile<false>(sA, LC, sK, sG, LK, wave, cb, lane);
-        const f32x4 x3 = dtok_tile<false>(sP, LC, sQ, sG, LK, wave, cb, lane);
-        const f32x4 x4 = dtok_tile<true>(sP, LC, sK, sG, LK, wave, cb, lane);
+        f32x4 x1, x2, x3, x4;
+        dtok_pair<true, true>(sA, sP, LC, sK, sK, sG, LK, wave, cb, lane, x1, x4);
+        dtok_pair<false, false>(sA, sP, LC, sK, sQ, sG, LK, wave, cb, lane, x2, x3);
         const f32x4 dbk = get_tile(dBK, DK, wave, cb, lane), dqg = get_tile(dQG, DK, wave, cb, lane);
         const f32x4 dkt = get_tile(dKt, DK, wave, cb, lane);
         const int c = 16 * cb + r;

@@ -176,13 +176,6 @@ __device__ __forceinline__ void lds_store4(uint16_t* p, float x0, float x1, floa
 __device__ __forceinline__ void lds_store4(float* p, float x0, float x1, float x2, float x3) {
     *reinterpret_cast<f32x4*>(p) = f32x4{x0, x1, x2, x3};
 }
-// Four consecutive LDS elements as fp32.
-__device__ __forceinline__ f32x4 lds_load4(const uint16_t* p) {
-    const u32x2 w = *reinterpret_cast<const u32x2*>(p);
-    return f32x4{__uint_as_float(w[0] << 16), __uint_as_float(w[0] & 0xffff0000u), __uint_as_float(w[1] << 16),
-                 __uint_as_float(w[1] & 0xffff0000u)};
-}
-__device__ __forceinline__ f32x4 lds_load4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
 
 // One MFMA k-step with both operands read from LDS in the natural order
 // (row r = lane % 16, k contiguous): bf16 16 bytes per lane, fp32 4 bytes.
@@ -194,10 +187,6 @@ __device__ __forceinline__ f32x4 lmma(const float* A, const float* B, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(*A, *B, c, 0, 0, 0);
 }
 
-// Value of the neighbouring lane (lane ^ 1, same 16-lane row).
-__device__ __forceinline__ float swap_adjacent(float x) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xf, 0xf, false));
-}
 // Inclusive prefix sum over the 16 lanes of each row (DPP row_shr 1, 2, 4, 8; lanes
 // shifted in from outside the row contribute 0).
 __device__ __forceinline__ float row_scan16(float x) {
@@ -535,7 +524,7 @@ __device__ __forceinline__ void intra_compute(const IntraIn<DK, DV, TIn>& X, cha
     using RG = RecGeo<DK, DV, TIn>;
     using elem = typename P::elem;
     constexpr int E = P::E, GW = P::GW, NGK = P::NGK, NGV = P::NGV;
-    constexpr int LDK = P::LDK, LDT = P::LDT, LDA = P::LDA;
+    constexpr int LDT = P::LDT, LDA = P::LDA;
     constexpr int KS = Mma<TIn>::KS, KST = kChunk / KS;  // natural k-steps over tokens
     constexpr TIn tag{};
     // phases 2-3: s-operand copies, rows of DK elements without padding; the 16-byte
