@@ -752,8 +752,11 @@ __device__ __forceinline__ void intra_compute(const IntraIn<DK, DV, TIn>& X, cha
                 // QG^T tile (rows c, columns t): lane holds channels 16 cb + 4q + rr of token t
                 qt[h] = gmma(sel[h], qgg, f32x4{0.f, 0.f, 0.f, 0.f}, tag);
             }
-            *reinterpret_cast<u32x4*>(rec + ws.o_q + ((static_cast<size_t>(wave) * RG::GK + j) * 64 + lane) * 16) =
-                tiles_to_gran(qt[0], qt[RG::CT - 1], tag);
+            // QG and P are read once, by the output pass: streaming stores, so the Infinity
+            // Cache keeps more of the W, Kt, Ut granules that both carries read
+            __builtin_nontemporal_store(
+                tiles_to_gran(qt[0], qt[RG::CT - 1], tag),
+                reinterpret_cast<u32x4*>(rec + ws.o_q + ((static_cast<size_t>(wave) * RG::GK + j) * 64 + lane) * 16));
             // the diagonal tiles from this lane's own rows (s and t both in this block) on fp32
             // MFMA (no operand split): step e takes channel GW (4 j + q) + e of lane (r, q) as
             // its k index q
@@ -806,8 +809,9 @@ __device__ __forceinline__ void intra_compute(const IntraIn<DK, DV, TIn>& X, cha
     // P granules (rows t of this token block, k over tokens) to the record
 #pragma unroll
     for (int g = 0; g < RG::GT; ++g)
-        *reinterpret_cast<u32x4*>(rec + ws.o_p + ((static_cast<size_t>(wave) * RG::GT + g) * 64 + lane) * 16) =
-            tiles_to_gran(Preg[RG::CT * g], Preg[RG::CT * g + RG::CT - 1], tag);
+        __builtin_nontemporal_store(
+            tiles_to_gran(Preg[RG::CT * g], Preg[RG::CT * g + RG::CT - 1], tag),
+            reinterpret_cast<u32x4*>(rec + ws.o_p + ((static_cast<size_t>(wave) * RG::GT + g) * 64 + lane) * 16));
     lds_barrier();
 
     // ---- 4. (the s-operand copies are dead) KG^T for phase 6, KG = 2^G kh from KB =
@@ -1069,6 +1073,7 @@ struct SegPlan {
     static constexpr int NUB = RG::UB / 16;
     static constexpr int VB = DV / 16, KB = DK / 16;
     static constexpr int SPLIT = SPLIT_;
+    static constexpr bool OUT = MODE == kOut;
     static constexpr int NCB = MODE == kOut ? VB : VB + KB;  // 16-column blocks of the state
     static constexpr int NCW = NCB / SPLIT;                  // ... held by one workgroup
     static constexpr int HB = NCW / 2;                       // U blocks per wave (SPLIT = 2)
@@ -1106,6 +1111,17 @@ struct SegOps {
     f32x4 us[SP::SPLIT == 2 ? SP::HB : 1];  // SPLIT = 2: Ut of the wave's U blocks (0: Phi)
 };
 
+// A record granule: a streaming load in the output pass (the record's last read), so the
+// records the output pass has not reached yet stay in the Infinity Cache; a plain load in
+// the local pass (the output pass reads the same granules again).
+template <bool NTL, class T>
+__device__ __forceinline__ T rec_load(const char* p) {
+    if constexpr (NTL)
+        return __builtin_nontemporal_load(reinterpret_cast<const T*>(p));
+    else
+        return *reinterpret_cast<const T*>(p);
+}
+
 template <class SP>
 __device__ __forceinline__ void seg_fetch(SegOps<SP>& F, const char* rec, const WsLayout& ws, int tb, int task,
                                           int cb, int lane, int ub0 = 0) {
@@ -1126,25 +1142,27 @@ __device__ __forceinline__ void seg_fetch(SegOps<SP>& F, const char* rec, const 
     {
         const char* ab = rec + (task == 1 ? ws.o_q : ws.o_w);
 #pragma unroll
-        for (int g = 0; g < SP::GK; ++g)
-            F.a[g] = *reinterpret_cast<const u32x4*>(ab + ((static_cast<size_t>(tb) * SP::GK + g) * 64 + lane) * 16);
+        for (int g = 0; g < SP::GK; ++g) {
+            const char* pa = ab + ((static_cast<size_t>(tb) * SP::GK + g) * 64 + lane) * 16;
+            F.a[g] = rec_load<SP::OUT, u32x4>(pa);
+        }
     }
     if (SP::SPLIT == 1 && task == 0) {
 #pragma unroll
         for (int t = 0; t < SP::NT; ++t)
 #pragma unroll
             for (int n = 0; n < SP::NUB; ++n)
-                F.uo[t][n] = *reinterpret_cast<const u32x4*>(
+                F.uo[t][n] = rec_load<SP::OUT, u32x4>(
                     rec + ws.o_u + (static_cast<size_t>(t * 4 + tb) * 64 + lane) * (SP::NUB * 16) + 16 * n);
     } else if (task == 1) {
 #pragma unroll
         for (int g = 0; g < SP::GT; ++g)
-            F.p[g] = *reinterpret_cast<const u32x4*>(rec + ws.o_p + ((static_cast<size_t>(tb) * SP::GT + g) * 64 + lane) * 16);
+            F.p[g] = rec_load<SP::OUT, u32x4>(rec + ws.o_p + ((static_cast<size_t>(tb) * SP::GT + g) * 64 + lane) * 16);
     }
 #pragma unroll
     for (int g = 0; g < SP::GT; ++g)
-        F.kt[g] = *reinterpret_cast<const u32x4*>(rec + ws.o_kt + ((static_cast<size_t>(cb) * SP::GT + g) * 64 + lane) * 16);
-    F.gl = *reinterpret_cast<const f32x4*>(rec + ws.o_gl + (16 * cb + 4 * (lane >> 4)) * 4);
+        F.kt[g] = rec_load<SP::OUT, u32x4>(rec + ws.o_kt + ((static_cast<size_t>(cb) * SP::GT + g) * 64 + lane) * 16);
+    F.gl = rec_load<SP::OUT, f32x4>(rec + ws.o_gl + (16 * cb + 4 * (lane >> 4)) * 4);
 }
 
 // Value (column block jb, row rr) of a U/O part held as granules, one tile of
