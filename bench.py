@@ -830,7 +830,7 @@ def main():
                          ROOT, "profiles", "decode_pool512_N64_H32_d128_traffic.json")),
                      "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, "
                                      "scaled by a 1 GiB copy)",
-                     "kernel": "decode_kernel<dk=128,dv=128,BV=64,T=1,bf16,commit>",
+                     "kernel": "decode_kernel<dk=128,dv=128,BV=128,T=1,bf16,commit,512 threads>",
                      "bytes_per_update": dec["bytes_per_update"],
                      "updates_per_launch": dec["updates"],
                      "avg_launch_us": dec["per"] * 1e6},

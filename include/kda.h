@@ -327,8 +327,8 @@ int kda_chunk_prefill_front(const void* q, const void* k, const void* v, int dty
 /*
  * kda_diag_state_stream -- a diagnostic, not part of the method: reads the fp32 state of each
  * sequence's slot (slot_idx [N] int32 on the device, negative skips) with the access pattern of
- * kda_decode_step's T = 1 kernel (a workgroup per (sequence, head, 64-column tile), the whole tile
- * held in registers, 16-byte non-temporal accesses) and writes it back unchanged.  Its time is
+ * kda_decode_step's T = 1 kernel (a workgroup per (sequence, head), 512 threads at dv = 128, the
+ * whole state held in registers, 16-byte non-temporal accesses) and writes it back unchanged.  Its time is
  * the floor that the decode step's state traffic sets on the GPU; the benchmark reports it beside
  * the decode kernel.  Errors and limits as kda_decode_step.
  */

@@ -8,19 +8,23 @@
 // Replay follows section 04 (ReplaySSM) of the CANN Kimi K3 inference page.
 //
 // Design (MI355X-first, not the NPU's Unified-Buffer scheme):
-//  * The fp32 state tile (dk x BV, BV = 64 columns) of a (sequence, head, dv tile) is
-//    streamed once from HBM into VGPRs with 16-byte non-temporal loads (each wave load
-//    instruction covers whole 256-byte tile rows), kept there for all T tokens, and
-//    written back once with non-temporal stores.  A one-token step is about 0.9 flop
+//  * The fp32 state tile (dk x BV) of a (sequence, head, dv tile) is streamed once from HBM
+//    into VGPRs with 16-byte non-temporal loads (each wave load instruction covers whole
+//    tile rows), kept there for all T tokens, and written back once with non-temporal
+//    stores.  A one-token step is about 0.9 flop
 //    per byte and runs on the VALU; only the multi-token blocks use MFMA.
 //  * T = 1 (decode_kernel, HBM-bound): both reductions over dk (S'^T k and S'^T q) come
 //    from one pass over the decayed state, using o = scale * (S'^T q + (k.q) u): the
-//    output needs no second pass.  256 threads (4 waves) per tile; thread (w, rq, c4) owns
-//    columns 4 c4 .. 4 c4 + 3 of row group 4w + rq (group g = rows g, g + 16, ...); each
-//    group's sum runs down its rows, the four waves' sums meet through one LDS exchange
-//    (one barrier per token), and the four lane positions are combined pairwise with the
-//    gfx950 row-swap instructions (v_permlane16_swap, v_permlane32_swap).  Per-token
-//    vectors (qh, kh, alpha, v, beta, k.q) are prepared by one wave per token into LDS.
+//    output needs no second pass.  One workgroup per (sequence, head) holds the whole head:
+//    at dv = 128, 512 threads (8 waves), thread (w, rq, c4) owning columns 4 c4 .. 4 c4 + 3
+//    of row group 2w + rq (group g = rows g, g + 16, ...), so each wave instruction covers
+//    two whole 512-byte rows (a bare memory pass measured 5.6% faster in this shape than
+//    with 64-column tiles of 4 waves); at dv = 64, 256 threads and four lane positions per
+//    column quad.  Each group's sum runs down its rows, the waves' sums meet through one LDS
+//    exchange (one barrier per token), and the lane positions of a column quad are combined
+//    pairwise with the gfx950 row-swap instructions (v_permlane16_swap, v_permlane32_swap).
+//    Per-token vectors (qh, kh, alpha, v, beta, k.q) are prepared by one wave per token
+//    into LDS.
 //  * T > 1 (wy_multi_kernel, MTP / verify): the WY form of 8-token blocks (see the
 //    kernel), one workgroup per head with a wave per 64-column tile (the waves split the
 //    block's preparation): one fp32 MFMA pass over the register-resident tile gives the 16 products
@@ -58,15 +62,15 @@ __device__ __forceinline__ void state_store4(__amdgpu_buffer_rsrc_t r, int voff,
     __builtin_amdgcn_raw_buffer_store_b128(v, r, voff, soff, kNonTemporal);
 }
 
-template <int DK, int DV, int BV>
+template <int DK, int DV, int BV, int NTHR = kThreads>
 struct Tile {
     static constexpr int NC4 = BV / 4;          // float4 column groups per tile
-    static constexpr int RG = kThreads / NC4;   // row groups
+    static constexpr int RG = NTHR / NC4;       // row groups
     static constexpr int RPT = DK / RG;         // rows per thread
     static constexpr int NT = DV / BV;          // tiles per head
     static constexpr int EPL = DK / kWave;      // key channels per lane in the prep
     static constexpr int VPL = (BV + kWave - 1) / kWave;  // v columns per lane in the prep
-    static_assert(kThreads % NC4 == 0 && DK % RG == 0 && RPT % 4 == 0, "tile shape");
+    static_assert(NTHR % NC4 == 0 && DK % RG == 0 && RPT % 4 == 0, "tile shape");
     static_assert(EPL >= 1 && BV % 4 == 0 && DV % BV == 0, "tile shape");
     // LDS slot of key channel c: rows of one thread are contiguous.
     __device__ static constexpr int pos(int c) { return (c % RG) * RPT + c / RG; }
@@ -114,10 +118,10 @@ struct TokenLds {
 // Prepares token t (local slot j) by one wave: L2 norms, alpha = exp(g), k.q.  With the
 // input front (FRONT), q, k and v are first convolved along the tokens (the inputs before
 // the call come from the slot's convolution state), g = -a_h softplus(z), beta = sigmoid(b).
-template <int DK, int DV, int BV, int TB, class TIn, bool VERIFY, bool FRONT>
+template <int DK, int DV, int BV, int TB, class TIn, bool VERIFY, bool FRONT, int NTHR>
 __device__ __forceinline__ void prep_token(const DecodeArgs& a, TokenLds<DK, BV, TB>& L, int j,
                                            int n, int t, int h, int tile, int lane, int slot) {
-    using C = Tile<DK, DV, BV>;
+    using C = Tile<DK, DV, BV, NTHR>;
     const int64_t tok = (static_cast<int64_t>(n) * a.T + t) * a.H + h;
     const int64_t rowk = tok * DK;
     float qv[C::EPL], kv[C::EPL], gv[C::EPL];
@@ -220,11 +224,12 @@ __device__ __forceinline__ void prep_token(const DecodeArgs& a, TokenLds<DK, BV,
     }
 }
 
-template <int DK, int DV, int BV, int TB, class TIn, bool VERIFY, bool FRONT = false>
-__global__ __launch_bounds__(kThreads, FRONT ? 4 : 5) void decode_kernel(DecodeArgs a) {
-    using C = Tile<DK, DV, BV>;
+template <int DK, int DV, int BV, int TB, class TIn, bool VERIFY, bool FRONT = false, int NTHR = kThreads>
+__global__ __launch_bounds__(NTHR, FRONT ? 4 : 5 * kThreads / NTHR) void decode_kernel(DecodeArgs a) {
+    using C = Tile<DK, DV, BV, NTHR>;
+    constexpr int NW = NTHR / kWave;
     __shared__ __attribute__((aligned(16))) TokenLds<DK, BV, TB> L;  // read as float4
-    __shared__ float4 red[2][kWaves][kWave][2];
+    __shared__ float4 red[2][NW][kWave][2];
 
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
     const int tile = blockIdx.x % C::NT;
@@ -235,7 +240,7 @@ __global__ __launch_bounds__(kThreads, FRONT ? 4 : 5) void decode_kernel(DecodeA
     const int slot = a.slot_idx[n];
 
     if (slot < 0) {  // skipped sequence: zero outputs, no state access
-        for (int idx = tid; idx < a.T * C::NC4; idx += kThreads) {
+        for (int idx = tid; idx < a.T * C::NC4; idx += NTHR) {
             const int t = idx / C::NC4, c = idx % C::NC4;
             const int64_t tok = (static_cast<int64_t>(n) * a.T + t) * a.H + h;
             store4<TIn>(a.o, tok * DV + tile * BV + 4 * c, make_float4(0.f, 0.f, 0.f, 0.f));
@@ -250,8 +255,8 @@ __global__ __launch_bounds__(kThreads, FRONT ? 4 : 5) void decode_kernel(DecodeA
     // never live together.
     for (int tb = 0; tb < (FRONT ? 1 : a.T); tb += TB) {
         const int nb = min(TB, a.T - tb);
-        for (int j = wave; j < nb; j += kWaves)
-            prep_token<DK, DV, BV, TB, TIn, VERIFY, FRONT>(a, L, j, n, tb + j, h, tile, lane, slot);
+        for (int j = wave; j < nb; j += NW)
+            prep_token<DK, DV, BV, TB, TIn, VERIFY, FRONT, NTHR>(a, L, j, n, tb + j, h, tile, lane, slot);
         if (tb == 0) {
 #pragma unroll
             for (int i = 0; i < C::RPT; ++i)
@@ -288,7 +293,7 @@ __global__ __launch_bounds__(kThreads, FRONT ? 4 : 5) void decode_kernel(DecodeA
             pk = red[buf][0][lane][0];
             pq = red[buf][0][lane][1];
 #pragma unroll
-            for (int w = 1; w < kWaves; ++w) {
+            for (int w = 1; w < NW; ++w) {
                 pk = f4_add(pk, red[buf][w][lane][0]);
                 pq = f4_add(pq, red[buf][w][lane][1]);
             }
@@ -326,13 +331,13 @@ __global__ __launch_bounds__(kThreads, FRONT ? 4 : 5) void decode_kernel(DecodeA
         const int W = f.conv_width;
         if (W > 1) {
             static_assert(C::NT == 1, "the front runs one workgroup per head");
-            constexpr int CW = 2 * DK + DV, NV = (3 * CW + kThreads - 1) / kThreads;
+            constexpr int CW = 2 * DK + DV, NV = (3 * CW + NTHR - 1) / NTHR;
             const int nv = (W - 1) * CW;
             const int64_t st0 = (static_cast<int64_t>(slot) * a.H + h) * (W - 1) * CW;
             float keep[NV];
 #pragma unroll
             for (int i = 0; i < NV; ++i) {
-                const int idx = tid + i * kThreads;
+                const int idx = tid + i * NTHR;
                 keep[i] = 0.f;
                 if (idx < nv) {
                     const int r = idx / CW, c = idx % CW, u = a.T - (W - 1) + r;
@@ -346,7 +351,7 @@ __global__ __launch_bounds__(kThreads, FRONT ? 4 : 5) void decode_kernel(DecodeA
             __syncthreads();
 #pragma unroll
             for (int i = 0; i < NV; ++i) {
-                const int idx = tid + i * kThreads;
+                const int idx = tid + i * NTHR;
                 if (idx < nv) store1<TIn>(f.conv_state, st0 + idx, keep[i]);
             }
         }
@@ -808,25 +813,27 @@ __global__ __launch_bounds__(kThreads) void replay_kernel(ReplayArgs a) {
     for (int i = 0; i < C::RPT; ++i) store_stream4(S + (rg + C::RG * i) * DV + col0, s[i]);
 }
 
-// T = 1: four-wave workgroups per 64-column tile (HBM-bound, decode_kernel).  T > 1: one
-// workgroup per head, a wave per 64-column tile, the WY form of 8-token blocks
+// T = 1: a workgroup per (sequence, head) holding the whole state (HBM-bound, decode_kernel).
+// T > 1: one workgroup per head, a wave per 64-column tile, the WY form of 8-token blocks
 // (wy_multi_kernel).
 template <int DK, int DV, class TIn>
 hipError_t launch_decode_d(const DecodeArgs& a, hipStream_t stream) {
-    constexpr int BV = DV < 64 ? DV : 64;
-    const dim3 grid(static_cast<unsigned>(a.N) * a.H * (DV / BV));
+    const dim3 hgrid(static_cast<unsigned>(a.N) * a.H);  // one workgroup per (sequence, head)
     if (a.front.gate_scale) {
-        // the input front: one workgroup per (sequence, head) owns the head's convolution
-        // state; up to kFrontTB tokens as one block, commit mode only
-        hipLaunchKernelGGL((decode_kernel<DK, DV, DV, kFrontTB, TIn, false, true>),
-                           dim3(static_cast<unsigned>(a.N) * a.H), dim3(kThreads), 0, stream, a);
+        // the input front: the workgroup owns the head's convolution state; up to kFrontTB
+        // tokens as one block, commit mode only
+        hipLaunchKernelGGL((decode_kernel<DK, DV, DV, kFrontTB, TIn, false, true>), hgrid, dim3(kThreads), 0,
+                           stream, a);
     } else if (a.T == 1) {
+        // the whole head's state per workgroup: eight waves for dv = 128 (each row group's
+        // 128 columns are one 512-byte access), four for dv = 64
+        constexpr int NT1 = DV == 128 ? 2 * kThreads : kThreads;
         if (a.records)
-            hipLaunchKernelGGL((decode_kernel<DK, DV, BV, 1, TIn, true>), grid, dim3(kThreads), 0, stream, a);
+            hipLaunchKernelGGL((decode_kernel<DK, DV, DV, 1, TIn, true, false, NT1>), hgrid, dim3(NT1), 0, stream, a);
         else
-            hipLaunchKernelGGL((decode_kernel<DK, DV, BV, 1, TIn, false>), grid, dim3(kThreads), 0, stream, a);
+            hipLaunchKernelGGL((decode_kernel<DK, DV, DV, 1, TIn, false, false, NT1>), hgrid, dim3(NT1), 0, stream, a);
     } else {
-        const dim3 hgrid(static_cast<unsigned>(a.N) * a.H), hblock(kWave * (DV / 64));
+        const dim3 hblock(kWave * (DV / 64));
         if (a.records && a.T <= kWyTB)
             hipLaunchKernelGGL((wy_multi_kernel<DK, DV, TIn, true, true>), hgrid, hblock, 0, stream, a);
         else if (a.records)

@@ -1,9 +1,9 @@
 // kda_diag.hip -- a diagnostic memory pass with the decode kernel's state access pattern.
 //
-// For each (sequence, head, 64-column dv tile) of a decode call, 256 threads load the fp32 state
-// tile of the sequence's slot exactly as decode_kernel does (16-byte non-temporal loads, thread
-// (row group, column quad) owning rows rg, rg + RG, ...), hold the whole tile in registers, and
-// store it back unchanged.  No token inputs, no arithmetic, no outputs: its time is the floor
+// For each (sequence, head) of a one-token decode call, a workgroup of the decode kernel's shape
+// (512 threads for dv = 128, 256 for dv = 64) loads the head's fp32 state from the sequence's
+// slot exactly as decode_kernel does (16-byte non-temporal loads, thread (row group, column
+// quad) owning rows rg, rg + RG, ...), holds it in registers, and stores it back unchanged.  No token inputs, no arithmetic, no outputs: its time is the floor
 // the decode step's state traffic sets with this access pattern on this GPU, which the
 // benchmark reports beside the decode kernel.  The pool's contents are left as they were.
 #include "kda_device.hpp"
@@ -13,17 +13,15 @@ namespace kda {
 
 namespace {
 
-constexpr int kDiagThreads = 256;
-
-template <int DK, int DV, int BV>
-__global__ __launch_bounds__(kDiagThreads) void state_stream_kernel(float* pool, const int32_t* slot_idx, int H) {
-    constexpr int NC4 = BV / 4, RG = kDiagThreads / NC4, RPT = DK / RG, NT = DV / BV;
-    const int tid = threadIdx.x, tile = blockIdx.x % NT, nh = blockIdx.x / NT;
+template <int DK, int DV, int NTHR>
+__global__ __launch_bounds__(NTHR) void state_stream_kernel(float* pool, const int32_t* slot_idx, int H) {
+    constexpr int NC4 = DV / 4, RG = NTHR / NC4, RPT = DK / RG;
+    const int tid = threadIdx.x, nh = blockIdx.x;
     const int h = nh % H, n = nh / H;
     const int slot = slot_idx[n];
     if (slot < 0) return;
     float* S = pool + (static_cast<int64_t>(slot) * H + h) * (DK * DV);
-    const int c4 = tid % NC4, rg = tid / NC4, col0 = tile * BV + 4 * c4;
+    const int c4 = tid % NC4, rg = tid / NC4, col0 = 4 * c4;
     float4 s[RPT];
 #pragma unroll
     for (int i = 0; i < RPT; ++i) s[i] = load_stream4(S + (rg + RG * i) * DV + col0);
@@ -37,9 +35,9 @@ __global__ __launch_bounds__(kDiagThreads) void state_stream_kernel(float* pool,
 
 template <int DK, int DV>
 hipError_t launch_d(float* pool, const int32_t* slot_idx, int N, int H, hipStream_t stream) {
-    constexpr int BV = DV < 64 ? DV : 64;
-    hipLaunchKernelGGL((state_stream_kernel<DK, DV, BV>), dim3(static_cast<unsigned>(N) * H * (DV / BV)),
-                       dim3(kDiagThreads), 0, stream, pool, slot_idx, H);
+    constexpr int NTHR = DV == 128 ? 512 : 256;  // as decode_kernel at T = 1
+    hipLaunchKernelGGL((state_stream_kernel<DK, DV, NTHR>), dim3(static_cast<unsigned>(N) * H), dim3(NTHR), 0,
+                       stream, pool, slot_idx, H);
     return hipGetLastError();
 }
 
