@@ -98,25 +98,37 @@ struct FwdTables {
     const int4* table;
 };
 
-// fp32 MFMA 16x16 tile: C(m, n) += sum_k A(m, k) B(k, n), k in [0, K) (K a multiple of 4);
+// fp32 MFMA 16x16 tile: C(m, n) += sum_k A(m, k) B(k, n), k in [0, K) (K a multiple of 16);
 // A(m, k) = A[m * am + k * ak], B(k, n) = B[k * bk + n * bn].  Lane l holds C(4 (l / 16) + i,
 // l % 16), i = 0..3.
-// The k steps go round four independent accumulators (K a multiple of 16), so consecutive
-// MFMAs do not wait for each other's results.
+// Of every 16 k values, lane (r, q) supplies k = 16 s + 4 q + j to step j of four
+// independent accumulator chains (consecutive MFMAs do not wait for each other's results),
+// so an operand whose k index is contiguous (ak = 1 or bk = 1: every call passes these as
+// constants) is read as one 16-byte LDS load per four steps.  Every base, stride and offset
+// here is a multiple of 4 floats of a 16-byte aligned array.
 __device__ __forceinline__ f32x4 mm16(const float* A, int am, int ak, const float* B, int bk, int bn, int K,
                                       int lane, f32x4 c) {
     const int r = lane & 15, q = lane >> 4;
-    f32x4 c1 = {0.f, 0.f, 0.f, 0.f}, c2 = c1, c3 = c1;
+    f32x4 acc[4] = {c, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
     for (int k0 = 0; k0 < K; k0 += 16) {
-        c = __builtin_amdgcn_mfma_f32_16x16x4f32(A[r * am + (k0 + q) * ak], B[(k0 + q) * bk + r * bn], c, 0, 0, 0);
-        c1 = __builtin_amdgcn_mfma_f32_16x16x4f32(A[r * am + (k0 + 4 + q) * ak], B[(k0 + 4 + q) * bk + r * bn], c1, 0,
-                                                  0, 0);
-        c2 = __builtin_amdgcn_mfma_f32_16x16x4f32(A[r * am + (k0 + 8 + q) * ak], B[(k0 + 8 + q) * bk + r * bn], c2, 0,
-                                                  0, 0);
-        c3 = __builtin_amdgcn_mfma_f32_16x16x4f32(A[r * am + (k0 + 12 + q) * ak], B[(k0 + 12 + q) * bk + r * bn], c3,
-                                                  0, 0, 0);
+        const int kb = k0 + 4 * q;
+        f32x4 av, bv;
+        if (ak == 1) {
+            av = *reinterpret_cast<const f32x4*>(A + r * am + kb);
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) av[j] = A[r * am + (kb + j) * ak];
+        }
+        if (bk == 1) {
+            bv = *reinterpret_cast<const f32x4*>(B + r * bn + kb);
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) bv[j] = B[(kb + j) * bk + r * bn];
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[j], bv[j], acc[j], 0, 0, 0);
     }
-    return (c + c1) + (c2 + c3);
+    return (acc[0] + acc[1]) + (acc[2] + acc[3]);
 }
 
 // Inclusive prefix sum over the 64 lanes of a wave (lane i gets x_0 + ... + x_i): a scan in
@@ -228,18 +240,25 @@ __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x)
 __device__ f32x4 dgram_tile(const float* X, const float* Y, const float* G, int ld, int DK, int i, int j, int lane) {
     const int r = lane & 15, q = lane >> 4;
     const int R = j < i ? 16 * i - 1 : 16 * i + 7;
-    f32x4 c[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};  // two independent chains
-    for (int k0 = 0; k0 < DK; k0 += 8) {
+    // of every 16 channels, lane (r, q) supplies channels 16 s + 4 q + e to step e of four
+    // chains, so each operand row is read as 16-byte LDS loads (ld and every offset are
+    // multiples of 4 floats)
+    f32x4 c[4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+    for (int k0 = 0; k0 < DK; k0 += 16) {
+        const int ch = k0 + 4 * q;
+        const f32x4 ref = *reinterpret_cast<const f32x4*>(G + R * ld + ch);
+        const f32x4 xt = *reinterpret_cast<const f32x4*>(X + (16 * i + r) * ld + ch);
+        const f32x4 gt = *reinterpret_cast<const f32x4*>(G + (16 * i + r) * ld + ch);
+        const f32x4 ys = *reinterpret_cast<const f32x4*>(Y + (16 * j + r) * ld + ch);
+        const f32x4 gs = *reinterpret_cast<const f32x4*>(G + (16 * j + r) * ld + ch);
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int ch = k0 + 4 * h + q;
-            const float ref = G[R * ld + ch];
-            const float av = X[(16 * i + r) * ld + ch] * ex2(G[(16 * i + r) * ld + ch] - ref);
-            const float bv = Y[(16 * j + r) * ld + ch] * ex2(ref - G[(16 * j + r) * ld + ch]);
-            c[h] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, c[h], 0, 0, 0);
+        for (int e = 0; e < 4; ++e) {
+            const float av = xt[e] * ex2(gt[e] - ref[e]);
+            const float bv = ys[e] * ex2(ref[e] - gs[e]);
+            c[e] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, c[e], 0, 0, 0);
         }
     }
-    return c[0] + c[1];
+    return (c[0] + c[1]) + (c[2] + c[3]);
 }
 
 // Decayed token products over a 16 x 16 (rows, channels) output tile.
