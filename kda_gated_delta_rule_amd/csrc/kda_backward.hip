@@ -207,17 +207,30 @@ __device__ void load_rows(const void* src, float* dst, int ld, const Item& it, i
     }
 }
 
-// In place x_t <- x_t / sqrt(|x_t|^2 + eps) (when use_l2); inv[t] gets the factor.
+// In place x_t <- x_t / sqrt(|x_t|^2 + eps) (when use_l2); inv[t] gets the factor.  NT / 64
+// adjacent lanes share a row: each sums and then scales its own D / (NT / 64) channels (16-byte
+// LDS accesses; ld and the offsets are multiples of 4 floats), the partial sums meet by lane
+// shuffles, so only the final barrier is needed.
 template <int NT = kT>
 __device__ void normalize_rows(float* x, int ld, int D, float* inv, int use_l2) {
-    if (threadIdx.x < kC) {
-        const int t = threadIdx.x;
-        float s = 0.f;
-        for (int c = 0; c < D; ++c) s = fmaf(x[t * ld + c], x[t * ld + c], s);
-        inv[t] = use_l2 ? 1.f / sqrtf(s + kEps) : 1.f;
+    constexpr int TPR = NT / kC;  // threads per row
+    const int t = threadIdx.x / TPR, p = threadIdx.x % TPR, w = D / TPR;
+    float* row = x + t * ld + p * w;
+    float s = 0.f;
+    for (int c = 0; c < w; c += 4) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(row + c);
+        s = fmaf(v[0], v[0], fmaf(v[1], v[1], fmaf(v[2], v[2], fmaf(v[3], v[3], s))));
     }
-    lds_barrier();
-    for (int i = threadIdx.x; i < kC * D; i += NT) x[(i / D) * ld + i % D] *= inv[i / D];
+#pragma unroll
+    for (int m = 1; m < TPR; m <<= 1) s += __shfl_xor(s, m, 64);
+    const float f = use_l2 ? 1.f / sqrtf(s + kEps) : 1.f;
+    if (p == 0) inv[t] = f;
+    if (use_l2) {
+        for (int c = 0; c < w; c += 4) {
+            f32x4 v = *reinterpret_cast<const f32x4*>(row + c);
+            *reinterpret_cast<f32x4*>(row + c) = v * f;
+        }
+    }
     lds_barrier();
 }
 
