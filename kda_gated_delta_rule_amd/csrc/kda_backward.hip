@@ -207,6 +207,14 @@ __device__ void load_rows(const void* src, float* dst, int ld, const Item& it, i
     }
 }
 
+// f(t, c) for every 4-column group (t < 64, c = 0, 4, .., D - 4) of a 64 x D block, the
+// workgroup's threads taking consecutive groups (16-byte LDS accesses in f).
+template <int D, int NT = kT, class F>
+__device__ __forceinline__ void for_groups(F f) {
+    constexpr int GPR = D / 4;
+    for (int i = threadIdx.x; i < kC * GPR; i += NT) f(i / GPR, 4 * (i % GPR));
+}
+
 // In place x_t <- x_t / sqrt(|x_t|^2 + eps) (when use_l2); inv[t] gets the factor.  NT / 64
 // adjacent lanes share a row: each sums and then scales its own D / (NT / 64) channels (16-byte
 // LDS accesses; ld and the offsets are multiples of 4 floats), the partial sums meet by lane
@@ -241,8 +249,15 @@ template <int DK, int NT = kT>
 __device__ void gate_cumsum(const float* g, float* G, int ld, const Item& it, int H) {
     load_rows<F32, DK, DK, NT>(g, G, ld, it, H);
     lds_barrier();
+    // a wave scans four adjacent columns per pass (one 16-byte LDS access per lane)
     const int lane = threadIdx.x & 63;
-    for (int c = threadIdx.x >> 6; c < DK; c += NT / 64) G[lane * ld + c] = wave_prefix64(G[lane * ld + c] * kL2e);
+    for (int c = 4 * (threadIdx.x >> 6); c < DK; c += 4 * (NT / 64)) {
+        f32x4* p = reinterpret_cast<f32x4*>(G + lane * ld + c);
+        f32x4 v = *p;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = wave_prefix64(v[e] * kL2e);
+        *p = v;
+    }
 }
 
 __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -504,10 +519,14 @@ __global__ __launch_bounds__(kT) void bwd_intra_kernel(BackwardArgs b) {
     unit_lower_inverse(sA, sB, sT, sY, lane, wave);
     s2g<kC, kC>(sT, LC, X.blk(item, X.bw.T), kC);
     // BK = beta kh 2^G into sQ (P is done), then W = T BK
-    for (int i = threadIdx.x; i < kC * DK; i += kT) {
-        const int t = i / DK, c = i % DK;
-        sQ[t * LK + c] = sB[t] * sK[t * LK + c] * ex2(sG[t * LK + c]);
-    }
+    for_groups<DK>([&](int t, int c) {
+        const f32x4 k4 = *reinterpret_cast<const f32x4*>(sK + t * LK + c);
+        const f32x4 g4 = *reinterpret_cast<const f32x4*>(sG + t * LK + c);
+        f32x4 b4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) b4[e] = sB[t] * k4[e] * ex2(g4[e]);
+        *reinterpret_cast<f32x4*>(sQ + t * LK + c) = b4;
+    });
     if (threadIdx.x < DK) X.blk(item, X.bw.gl)[threadIdx.x] = ex2(sG[(kC - 1) * LK + threadIdx.x]);
     lds_barrier();
     float* Wg = X.blk(item, X.bw.W);
@@ -519,7 +538,10 @@ __global__ __launch_bounds__(kT) void bwd_intra_kernel(BackwardArgs b) {
     // BV = beta v into sK, then Ut = T BV
     load_rows<TIn, DV>(a.v, sK, LV, it, H);
     lds_barrier();
-    for (int i = threadIdx.x; i < kC * DV; i += kT) sK[(i / DV) * LV + i % DV] *= sB[i / DV];
+    for_groups<DV>([&](int t, int c) {
+        f32x4* x = reinterpret_cast<f32x4*>(sK + t * LV + c);
+        *x = *x * sB[t];
+    });
     lds_barrier();
     float* Ug = X.blk(item, X.bw.Ut);
     for (int cb = 0; cb < DV / 16; ++cb) {
@@ -529,19 +551,28 @@ __global__ __launch_bounds__(kT) void bwd_intra_kernel(BackwardArgs b) {
 }
 
 // Kt = kh 2^(G_L - G) and QG = qh 2^G in place (the raw normalised rows on entry).
-template <int NT = kT>
-__device__ void to_kt(float* K, const float* G, int ld, int DK) {
-    for (int i = threadIdx.x; i < kC * DK; i += NT) {
-        const int t = i / DK, c = i % DK;
-        K[t * ld + c] *= ex2(G[(kC - 1) * ld + c] - G[t * ld + c]);
-    }
+template <int DK, int NT = kT>
+__device__ void to_kt(float* K, const float* G, int ld) {
+    for_groups<DK, NT>([&](int t, int c) {
+        const f32x4 gl = *reinterpret_cast<const f32x4*>(G + (kC - 1) * ld + c);
+        const f32x4 g = *reinterpret_cast<const f32x4*>(G + t * ld + c);
+        f32x4* x = reinterpret_cast<f32x4*>(K + t * ld + c);
+        f32x4 v = *x;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] *= ex2(gl[e] - g[e]);
+        *x = v;
+    });
 }
-template <int NT = kT>
-__device__ void to_qg(float* Q, const float* G, int ld, int DK) {
-    for (int i = threadIdx.x; i < kC * DK; i += NT) {
-        const int t = i / DK, c = i % DK;
-        Q[t * ld + c] *= ex2(G[t * ld + c]);
-    }
+template <int DK, int NT = kT>
+__device__ void to_qg(float* Q, const float* G, int ld) {
+    for_groups<DK, NT>([&](int t, int c) {
+        const f32x4 g = *reinterpret_cast<const f32x4*>(G + t * ld + c);
+        f32x4* x = reinterpret_cast<f32x4*>(Q + t * ld + c);
+        f32x4 v = *x;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] *= ex2(g[e]);
+        *x = v;
+    });
 }
 
 // ---------------------------------------------------------------------------
@@ -568,8 +599,8 @@ __global__ __launch_bounds__(kTP) void bwd_prep_kernel(BackwardArgs b) {
     lds_barrier();
     normalize_rows<kTP>(sK, LK, DK, inv, a.use_l2);
     normalize_rows<kTP>(sQ, LK, DK, inv, a.use_l2);
-    to_kt<kTP>(sK, sG, LK, DK);
-    to_qg<kTP>(sQ, sG, LK, DK);
+    to_kt<DK, kTP>(sK, sG, LK);
+    to_qg<DK, kTP>(sQ, sG, LK);
     lds_barrier();
     g2s<kC, DK, kTP>(X.blk(item, X.bw.W), DK, sW, LK);
     const float* gl = X.blk(item, X.bw.gl);
@@ -713,7 +744,7 @@ __global__ __launch_bounds__(kTS) void bwd_state_kernel(BackwardArgs b) {
     g2s<kC, kC, kTS>(X.blk(item, X.bw.P), kC, sP, LC);
     lds_barrier();
     normalize_rows<kTS>(sK, LK, DK, inv, a.use_l2);
-    to_kt<kTS>(sK, sG, LK, DK);
+    to_kt<DK, kTS>(sK, sG, LK);
     lds_barrier();
     g2s<kC, DK, kTS>(X.blk(item, X.bw.W), DK, sW, LK);
     if (threadIdx.x < DK) sgl[threadIdx.x] = 0.f;
@@ -743,11 +774,17 @@ __global__ __launch_bounds__(kTS) void bwd_state_kernel(BackwardArgs b) {
             put_tile(sdU, LB, tb, cb, du, lane);
         }
         lds_barrier();
-        for (int i = threadIdx.x; i < kC * kVB; i += kTS)
-            dUg[(i / kVB) * DV + kVB * jb + i % kVB] = sdU[(i / kVB) * LB + i % kVB];
+        for_groups<kVB, kTS>([&](int t, int c) {
+            *reinterpret_cast<f32x4*>(dUg + t * DV + kVB * jb + c) = *reinterpret_cast<const f32x4*>(sdU + t * LB + c);
+        });
         if (threadIdx.x < DK) {
             float s = 0.f;
-            for (int j = 0; j < kVB; ++j) s = fmaf(sS[threadIdx.x * LB + j], sX[threadIdx.x * LB + j], s);
+            for (int j = 0; j < kVB; j += 4) {
+                const f32x4 sv = *reinterpret_cast<const f32x4*>(sS + threadIdx.x * LB + j);
+                const f32x4 xv = *reinterpret_cast<const f32x4*>(sX + threadIdx.x * LB + j);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) s = fmaf(sv[e], xv[e], s);
+            }
             sgl[threadIdx.x] += s;
         }
         // contractions over this block's columns (k = the block's 32 value columns): per k step
@@ -818,7 +855,7 @@ __global__ __launch_bounds__(kT) void bwd_ut_kernel(BackwardArgs b) {
     g2s<kC, kC>(X.blk(item, X.bw.T), kC, sT, LC);
     lds_barrier();
     normalize_rows(sM2, LK, DK, inv, a.use_l2);
-    to_qg(sM2, sG, LK, DK);  // kh 2^G
+    to_qg<DK>(sM2, sG, LK);  // kh 2^G
     g2s<kC, DK>(X.blk(item, X.bw.dW), DK, sM1, LK);
     lds_barrier();
     // dT (part 1: dW BK^T, BK = beta KG, so column s takes beta_s) and dBK of this wave's
@@ -841,7 +878,10 @@ __global__ __launch_bounds__(kT) void bwd_ut_kernel(BackwardArgs b) {
     load_rows<TIn, DV>(a.v, sM2, LV, it, H);
     g2s<kC, DV>(X.blk(item, X.bw.dU), DV, sM1, LV);
     lds_barrier();
-    for (int i = threadIdx.x; i < kC * DV; i += kT) sM2[(i / DV) * LV + i % DV] *= sB[i / DV];
+    for_groups<DV>([&](int t, int c) {
+        f32x4* x = reinterpret_cast<f32x4*>(sM2 + t * LV + c);
+        *x = *x * sB[t];
+    });
     lds_barrier();
     for (int sb = 0; sb < 4; ++sb)
         dT[sb] = mm16(sM1 + 16 * wave * LV, LV, 1, sM2 + 16 * sb * LV, 1, LV, DV, lane, dT[sb]);
@@ -993,10 +1033,11 @@ __global__ __launch_bounds__(kT) void bwd_final_kernel(BackwardArgs b) {
         sG[lane * LK + c] = (tot - incl + v) + sGL[c];
     }
     lds_barrier();
-    for (int i = threadIdx.x; i < it.L * DK; i += kT) {
-        const int t = i / DK, c = i % DK;
-        b.dg[(static_cast<int64_t>(it.t0 + t) * H + it.h) * DK + c] = sG[t * LK + c];
-    }
+    for_groups<DK>([&](int t, int c) {
+        if (t < it.L)
+            *reinterpret_cast<f32x4*>(b.dg + (static_cast<int64_t>(it.t0 + t) * H + it.h) * DK + c) =
+                *reinterpret_cast<const f32x4*>(sG + t * LK + c);
+    });
 }
 
 template <int DK, int DV, class TIn>
