@@ -368,10 +368,10 @@ __device__ __forceinline__ f32x4 get_tile(const float* M, int ld, int rb, int cb
 __device__ void unit_lower_inverse(const float* Ag, const float* beta, float* T, float* Y, int lane, int wave) {
     constexpr int LC = kC + 4, LY = 20;
     const int r = lane & 15, q = lane >> 4;
-    // zero the blocks above the diagonal of this wave's rows
-    for (int i = lane; i < 16 * kC; i += 64) {
-        const int row = 16 * wave + i / kC, c = i % kC;
-        if (c >= 16 * (wave + 1)) T[row * LC + c] = 0.f;
+    // zero the blocks above the diagonal of this wave's rows (4 columns per store)
+    for (int i = lane; i < 16 * (kC / 4); i += 64) {
+        const int row = 16 * wave + i / (kC / 4), c = 4 * (i % (kC / 4));
+        if (c >= 16 * (wave + 1)) *reinterpret_cast<f32x4*>(T + row * LC + c) = f32x4{0.f, 0.f, 0.f, 0.f};
     }
     {
         const int col = r, b0 = 16 * wave;
@@ -787,23 +787,33 @@ __global__ __launch_bounds__(kTS) void bwd_state_kernel(BackwardArgs b) {
             }
             sgl[threadIdx.x] += s;
         }
-        // contractions over this block's columns (k = the block's 32 value columns): per k step
-        // the wave's rows of dO, dU and U are read once and serve its half of the output tiles
-        for (int k0 = 0; k0 < kVB; k0 += 4) {
-            const int kk = k0 + q;
-            const float ao = sO[(16 * tb + r) * LB + kk], adu = sdU[(16 * tb + r) * LB + kk];
-            const float au = sU[(16 * tb + r) * LB + kk];
+        // contractions over this block's columns (k = the block's 32 value columns): the wave's
+        // rows of dO, dU and U are read once per 16 k values and serve its half of the output
+        // tiles; of every 16 k values lane (r, q) supplies k = 16 s + 4 q + e to step e, so every
+        // operand row is read as 16-byte LDS loads
+        for (int k0 = 0; k0 < kVB; k0 += 16) {
+            const int kb = k0 + 4 * q;
+            const f32x4 ao = *reinterpret_cast<const f32x4*>(sO + (16 * tb + r) * LB + kb);
+            const f32x4 adu = *reinterpret_cast<const f32x4*>(sdU + (16 * tb + r) * LB + kb);
+            const f32x4 au = *reinterpret_cast<const f32x4*>(sU + (16 * tb + r) * LB + kb);
 #pragma unroll
             for (int i = 0; i < HK; ++i) {
                 const int cb = HK * half + i;
-                const float bs = sS[(16 * cb + r) * LB + kk], bx = sX[(16 * cb + r) * LB + kk];
-                dqg[i] = __builtin_amdgcn_mfma_f32_16x16x4f32(ao, bs, dqg[i], 0, 0, 0);
-                dw[i] = __builtin_amdgcn_mfma_f32_16x16x4f32(adu, bs, dw[i], 0, 0, 0);
-                dkt[i] = __builtin_amdgcn_mfma_f32_16x16x4f32(au, bx, dkt[i], 0, 0, 0);
+                const f32x4 bs = *reinterpret_cast<const f32x4*>(sS + (16 * cb + r) * LB + kb);
+                const f32x4 bx = *reinterpret_cast<const f32x4*>(sX + (16 * cb + r) * LB + kb);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    dqg[i] = __builtin_amdgcn_mfma_f32_16x16x4f32(ao[e], bs[e], dqg[i], 0, 0, 0);
+                    dw[i] = __builtin_amdgcn_mfma_f32_16x16x4f32(adu[e], bs[e], dw[i], 0, 0, 0);
+                    dkt[i] = __builtin_amdgcn_mfma_f32_16x16x4f32(au[e], bx[e], dkt[i], 0, 0, 0);
+                }
             }
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
-                dp[i] = __builtin_amdgcn_mfma_f32_16x16x4f32(ao, sU[(16 * (2 * half + i) + r) * LB + kk], dp[i], 0, 0, 0);
+            for (int i = 0; i < 2; ++i) {
+                const f32x4 bu = *reinterpret_cast<const f32x4*>(sU + (16 * (2 * half + i) + r) * LB + kb);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) dp[i] = __builtin_amdgcn_mfma_f32_16x16x4f32(ao[e], bu[e], dp[i], 0, 0, 0);
+            }
         }
     }
     float* dQG = X.blk(item, X.bw.dQG);
@@ -1025,12 +1035,20 @@ __global__ __launch_bounds__(kT) void bwd_final_kernel(BackwardArgs b) {
     // dG into sG (rows of this wave), then the reverse cumsum per channel plus dG_L
     for (int cb = 0; cb < NKB; ++cb) put_tile(sG, LK, wave, cb, dG[cb], lane);
     lds_barrier();
-    // suffix sums over the live rows (lane = token): total - inclusive prefix + own value
-    for (int c = wave; c < DK; c += kT / 64) {
-        const float v = lane < it.L ? sG[lane * LK + c] : 0.f;
-        const float incl = wave_prefix64(v);
-        const float tot = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(incl), 63));
-        sG[lane * LK + c] = (tot - incl + v) + sGL[c];
+    // suffix sums over the live rows (lane = token): total - inclusive prefix + own value; a
+    // wave takes four adjacent columns per pass (one 16-byte LDS access per lane)
+    for (int c = 4 * wave; c < DK; c += 4 * (kT / 64)) {
+        f32x4* p = reinterpret_cast<f32x4*>(sG + lane * LK + c);
+        const f32x4 v4 = *p;
+        f32x4 o4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float v = lane < it.L ? v4[e] : 0.f;
+            const float incl = wave_prefix64(v);
+            const float tot = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(incl), 63));
+            o4[e] = (tot - incl + v) + sGL[c + e];
+        }
+        *p = o4;
     }
     lds_barrier();
     for_groups<DK>([&](int t, int c) {
