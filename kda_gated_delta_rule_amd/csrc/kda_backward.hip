@@ -175,25 +175,34 @@ __device__ __forceinline__ bool item_of(const PrefillArgs& a, const char* ws, co
 // compile-time counts), so the loads are in flight together instead of each waiting in turn.
 
 // Columns c0 .. c0 + W - 1 of rows t0 .. t0 + L - 1 of head h of a [T][H][D] input into LDS
-// dst [64][ld] (fp32; rows from L on are zero).
-template <class TIn, int D, int W = D, int NT = kT>
-__device__ void load_rows(const void* src, float* dst, int ld, const Item& it, int H, int c0 = 0) {
-    constexpr int EPG = 16 / TIn::bytes;  // elements per 16-byte access
-    constexpr int GPR = W / EPG, N = (kC * GPR + NT - 1) / NT;
+// dst [64][ld] (fp32; rows from L on are zero): rows_fetch issues the loads into registers,
+// rows_store writes them (so a caller can keep the loads in flight across other work).
+template <class TIn, int W, int NT = kT>
+struct RowCopy {
+    static constexpr int EPG = 16 / TIn::bytes;  // elements per 16-byte access
+    static constexpr int GPR = W / EPG, N = (kC * GPR + NT - 1) / NT;
     static_assert(W % EPG == 0, "row copy shape");
-    u32x4 v[N];
+};
+template <class TIn, int D, int W = D, int NT = kT>
+__device__ __forceinline__ void rows_fetch(const void* src, u32x4 (&v)[RowCopy<TIn, W, NT>::N], const Item& it, int H,
+                                           int c0 = 0) {
+    using RC = RowCopy<TIn, W, NT>;
 #pragma unroll
-    for (int i = 0; i < N; ++i) {
-        const int idx = threadIdx.x + i * NT, t = idx / GPR, c = c0 + EPG * (idx % GPR);
+    for (int i = 0; i < RC::N; ++i) {
+        const int idx = threadIdx.x + i * NT, t = idx / RC::GPR, c = c0 + RC::EPG * (idx % RC::GPR);
         v[i] = u32x4{0u, 0u, 0u, 0u};
-        if (idx < kC * GPR && t < it.L)
+        if (idx < kC * RC::GPR && t < it.L)
             v[i] = *reinterpret_cast<const u32x4*>(static_cast<const char*>(src) +
                                                    ((static_cast<int64_t>(it.t0 + t) * H + it.h) * D + c) * TIn::bytes);
     }
+}
+template <class TIn, int W, int NT = kT>
+__device__ __forceinline__ void rows_store(const u32x4 (&v)[RowCopy<TIn, W, NT>::N], float* dst, int ld) {
+    using RC = RowCopy<TIn, W, NT>;
 #pragma unroll
-    for (int i = 0; i < N; ++i) {
-        const int idx = threadIdx.x + i * NT, t = idx / GPR, c = EPG * (idx % GPR);
-        if (idx >= kC * GPR) break;
+    for (int i = 0; i < RC::N; ++i) {
+        const int idx = threadIdx.x + i * NT, t = idx / RC::GPR, c = RC::EPG * (idx % RC::GPR);
+        if (idx >= kC * RC::GPR) break;
         float* d = dst + t * ld + c;
         if constexpr (TIn::bytes == 2) {
 #pragma unroll
@@ -205,6 +214,12 @@ __device__ void load_rows(const void* src, float* dst, int ld, const Item& it, i
             *reinterpret_cast<f32x4*>(d) = __builtin_bit_cast(f32x4, v[i]);
         }
     }
+}
+template <class TIn, int D, int W = D, int NT = kT>
+__device__ void load_rows(const void* src, float* dst, int ld, const Item& it, int H, int c0 = 0) {
+    u32x4 v[RowCopy<TIn, W, NT>::N];
+    rows_fetch<TIn, D, W, NT>(src, v, it, H, c0);
+    rows_store<TIn, W, NT>(v, dst, ld);
 }
 
 // f(t, c) for every 4-column group (t < 64, c = 0, 4, .., D - 4) of a 64 x D block, the
@@ -414,20 +429,33 @@ __device__ void unit_lower_inverse(const float* Ag, const float* beta, float* T,
 // Global <-> LDS copies of a row-major fp32 [ROWS][COLS] matrix (leading dimensions and base
 // addresses multiples of 4 floats).
 template <int ROWS, int COLS, int NT = kT>
-__device__ void g2s(const float* g, int gld, float* s, int sld) {
-    constexpr int C4 = COLS / 4, N = ROWS * C4 / NT;
+struct MatCopy {
+    static constexpr int C4 = COLS / 4, N = ROWS * C4 / NT;
     static_assert(COLS % 4 == 0 && (ROWS * C4) % NT == 0, "copy shape");
-    f32x4 v[N];
+};
+template <int ROWS, int COLS, int NT = kT>
+__device__ __forceinline__ void g2r(const float* g, int gld, f32x4 (&v)[MatCopy<ROWS, COLS, NT>::N]) {
+    using MC = MatCopy<ROWS, COLS, NT>;
 #pragma unroll
-    for (int i = 0; i < N; ++i) {
+    for (int i = 0; i < MC::N; ++i) {
         const int idx = threadIdx.x + i * NT;
-        v[i] = *reinterpret_cast<const f32x4*>(g + (idx / C4) * gld + 4 * (idx % C4));
+        v[i] = *reinterpret_cast<const f32x4*>(g + (idx / MC::C4) * gld + 4 * (idx % MC::C4));
     }
+}
+template <int ROWS, int COLS, int NT = kT>
+__device__ __forceinline__ void r2s(const f32x4 (&v)[MatCopy<ROWS, COLS, NT>::N], float* s, int sld) {
+    using MC = MatCopy<ROWS, COLS, NT>;
 #pragma unroll
-    for (int i = 0; i < N; ++i) {
+    for (int i = 0; i < MC::N; ++i) {
         const int idx = threadIdx.x + i * NT;
-        *reinterpret_cast<f32x4*>(s + (idx / C4) * sld + 4 * (idx % C4)) = v[i];
+        *reinterpret_cast<f32x4*>(s + (idx / MC::C4) * sld + 4 * (idx % MC::C4)) = v[i];
     }
+}
+template <int ROWS, int COLS, int NT = kT>
+__device__ void g2s(const float* g, int gld, float* s, int sld) {
+    f32x4 v[MatCopy<ROWS, COLS, NT>::N];
+    g2r<ROWS, COLS, NT>(g, gld, v);
+    r2s<ROWS, COLS, NT>(v, s, sld);
 }
 template <int ROWS, int COLS>
 __device__ void s2g(const float* s, int sld, float* g, int gld) {
@@ -492,6 +520,10 @@ __global__ __launch_bounds__(kT) void bwd_intra_kernel(BackwardArgs b) {
     gate_cumsum<DK>(a.g, sG, LK, it, H);
     if (threadIdx.x < kC) sB[threadIdx.x] = threadIdx.x < it.L ? a.beta[static_cast<int64_t>(it.t0 + threadIdx.x) * H + it.h] : 0.f;
     lds_barrier();
+    // v is first needed after T and W: its loads, issued once the first operands are in,
+    // stay in flight (registers) until then
+    u32x4 rV[RowCopy<TIn, DV>::N];
+    rows_fetch<TIn, DV>(a.v, rV, it, H);
     normalize_rows(sK, LK, DK, inv, a.use_l2);
     normalize_rows(sQ, LK, DK, inv, a.use_l2);
     // Ag (strictly lower) and P (lower with the diagonal), tile (i, j <= i) by the wave owning
@@ -536,7 +568,7 @@ __global__ __launch_bounds__(kT) void bwd_intra_kernel(BackwardArgs b) {
     }
     lds_barrier();
     // BV = beta v into sK, then Ut = T BV
-    load_rows<TIn, DV>(a.v, sK, LV, it, H);
+    rows_store<TIn, DV>(rV, sK, LV);
     lds_barrier();
     for_groups<DV>([&](int t, int c) {
         f32x4* x = reinterpret_cast<f32x4*>(sK + t * LV + c);
@@ -597,12 +629,16 @@ __global__ __launch_bounds__(kTP) void bwd_prep_kernel(BackwardArgs b) {
     gate_cumsum<DK, kTP>(a.g, sG, LK, it, H);
     g2s<kC, kC, kTP>(X.blk(item, X.bw.P), kC, sP, LC);
     lds_barrier();
+    // W goes where the gate cumsum is until Kt and QG are formed: its loads stay in flight
+    // (registers) until then
+    f32x4 rW[MatCopy<kC, DK, kTP>::N];
+    g2r<kC, DK, kTP>(X.blk(item, X.bw.W), DK, rW);
     normalize_rows<kTP>(sK, LK, DK, inv, a.use_l2);
     normalize_rows<kTP>(sQ, LK, DK, inv, a.use_l2);
     to_kt<DK, kTP>(sK, sG, LK);
     to_qg<DK, kTP>(sQ, sG, LK);
     lds_barrier();
-    g2s<kC, DK, kTP>(X.blk(item, X.bw.W), DK, sW, LK);
+    r2s<kC, DK, kTP>(rW, sW, LK);
     const float* gl = X.blk(item, X.bw.gl);
     lds_barrier();
     // Mt (dk x dk): tile (rb, cb), rows c = W's columns, k over tokens
@@ -755,12 +791,24 @@ __global__ __launch_bounds__(kTS) void bwd_state_kernel(BackwardArgs b) {
     f32x4 dqg[HK], dw[HK], dkt[HK], dp[2];
     for (int i = 0; i < HK; ++i) dqg[i] = dw[i] = dkt[i] = f32x4{0.f, 0.f, 0.f, 0.f};
     for (int i = 0; i < 2; ++i) dp[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // a column block's S, dX, Ut and dO: loaded into registers one block ahead (during the
+    // previous block's contractions), stored to LDS at the block's start
+    f32x4 rS[MatCopy<DK, kVB, kTS>::N], rX[MatCopy<DK, kVB, kTS>::N], rU[MatCopy<kC, kVB, kTS>::N];
+    u32x4 rO[RowCopy<TIn, kVB, kTS>::N];
+    auto fetch = [&](int jb) {
+        g2r<DK, kVB, kTS>(S + kVB * jb, DV, rS);
+        g2r<DK, kVB, kTS>(dX + kVB * jb, DV, rX);
+        rows_fetch<TIn, DV, kVB, kTS>(b.dout, rO, it, H, kVB * jb);
+        g2r<kC, kVB, kTS>(Ut + kVB * jb, DV, rU);
+    };
+    fetch(0);
     for (int jb = 0; jb < DV / kVB; ++jb) {
         lds_barrier();
-        g2s<DK, kVB, kTS>(S + kVB * jb, DV, sS, LB);
-        g2s<DK, kVB, kTS>(dX + kVB * jb, DV, sX, LB);
-        load_rows<TIn, DV, kVB, kTS>(b.dout, sO, LB, it, H, kVB * jb);
-        g2s<kC, kVB, kTS>(Ut + kVB * jb, DV, sU, LB);
+        r2s<DK, kVB, kTS>(rS, sS, LB);
+        r2s<DK, kVB, kTS>(rX, sX, LB);
+        rows_store<TIn, kVB, kTS>(rO, sO, LB);
+        r2s<kC, kVB, kTS>(rU, sU, LB);
+        if (jb + 1 < DV / kVB) fetch(jb + 1);
         lds_barrier();
         // U and dU of this wave's token block and column tile (one of the block's two); each
         // wave reads and writes only its own tile of sU and sdU here
@@ -856,7 +904,9 @@ __global__ __launch_bounds__(kT) void bwd_ut_kernel(BackwardArgs b) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, H = a.H, item = blockIdx.x;
     const int r = lane & 15, q = lane >> 4;
     static_assert(2 * kC * LC >= kC * LK, "gate cumsum fits sD + sE");
-    // KG = kh 2^G (sM2) and dW (sM1)
+    // KG = kh 2^G (sM2) and dW (sM1); dW's loads stay in flight (registers) until sM1 is free
+    f32x4 rW[MatCopy<kC, DK>::N];
+    g2r<kC, DK>(X.blk(item, X.bw.dW), DK, rW);
     load_rows<TIn, DK>(a.k, sM2, LK, it, H);
     gate_cumsum<DK>(a.g, sG, LK, it, H);
     if (threadIdx.x < kC) {
@@ -866,8 +916,13 @@ __global__ __launch_bounds__(kT) void bwd_ut_kernel(BackwardArgs b) {
     lds_barrier();
     normalize_rows(sM2, LK, DK, inv, a.use_l2);
     to_qg<DK>(sM2, sG, LK);  // kh 2^G
-    g2s<kC, DK>(X.blk(item, X.bw.dW), DK, sM1, LK);
+    r2s<kC, DK>(rW, sM1, LK);
     lds_barrier();
+    // v and dU load during the dT and dBK products
+    u32x4 rV[RowCopy<TIn, DV>::N];
+    f32x4 rU[MatCopy<kC, DV>::N];
+    rows_fetch<TIn, DV>(a.v, rV, it, H);
+    g2r<kC, DV>(X.blk(item, X.bw.dU), DV, rU);
     // dT (part 1: dW BK^T, BK = beta KG, so column s takes beta_s) and dBK of this wave's
     // rows; dbeta part sum_c KG dBK
     f32x4 dT[4];
@@ -885,8 +940,8 @@ __global__ __launch_bounds__(kT) void bwd_ut_kernel(BackwardArgs b) {
     }
     lds_barrier();
     // BV = beta v (sM2) and dU (sM1)
-    load_rows<TIn, DV>(a.v, sM2, LV, it, H);
-    g2s<kC, DV>(X.blk(item, X.bw.dU), DV, sM1, LV);
+    rows_store<TIn, DV>(rV, sM2, LV);
+    r2s<kC, DV>(rU, sM1, LV);
     lds_barrier();
     for_groups<DV>([&](int t, int c) {
         f32x4* x = reinterpret_cast<f32x4*>(sM2 + t * LV + c);
