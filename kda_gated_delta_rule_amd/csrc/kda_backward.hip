@@ -1025,12 +1025,19 @@ __global__ __launch_bounds__(kT) void bwd_final_kernel(BackwardArgs b) {
     // per channel tile: dkh, dqh and dG of this wave's 16 rows
     f32x4 dkh[NKB], dqh[NKB], dG[NKB];
     float ktdkt[NKB];  // sum over this lane's rows of Kt dKt (for dG_L)
+    // the channel tile's dBK, dQG and dKt (global) are loaded one tile ahead
+    f32x4 nbk = get_tile(dBK, DK, wave, 0, lane), nqg = get_tile(dQG, DK, wave, 0, lane);
+    f32x4 nkt = get_tile(dKt, DK, wave, 0, lane);
     for (int cb = 0; cb < NKB; ++cb) {
+        const f32x4 dbk = nbk, dqg = nqg, dkt = nkt;
+        if (cb + 1 < NKB) {
+            nbk = get_tile(dBK, DK, wave, cb + 1, lane);
+            nqg = get_tile(dQG, DK, wave, cb + 1, lane);
+            nkt = get_tile(dKt, DK, wave, cb + 1, lane);
+        }
         f32x4 x1, x2, x3, x4;
         dtok_pair<true, true>(sA, sP, LC, sK, sK, sG, LK, wave, cb, lane, x1, x4);
         dtok_pair<false, false>(sA, sP, LC, sK, sQ, sG, LK, wave, cb, lane, x2, x3);
-        const f32x4 dbk = get_tile(dBK, DK, wave, cb, lane), dqg = get_tile(dQG, DK, wave, cb, lane);
-        const f32x4 dkt = get_tile(dKt, DK, wave, cb, lane);
         const int c = 16 * cb + r;
         const float gL = sG[(kC - 1) * LK + c];
         ktdkt[cb] = 0.f;
