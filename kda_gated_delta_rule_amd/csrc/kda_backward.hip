@@ -25,6 +25,7 @@
 // Launches on the caller's stream (all arithmetic fp32; bf16 inputs are widened):
 //   0. bwd_init        identity slot map and the initial states for the forward pass
 //   1. the forward prefill (kda_prefill.hip) with its carry storing every chunk's entering state
+//      (and no output O: its intra-chunk records skip QG and P)
 //   2. bwd_intra       per (chunk, head): Ag, P, T (forward substitution), W, Ut, exp(G_L)
 //   3. bwd_prep        per (chunk, head): Mt and b of the reverse state recurrence
 //   4. bwd_scan        per (sequence, head, 16 columns): dS_c = Mt_c dS_(c+1) + b_c from the
@@ -58,7 +59,7 @@ __host__ __device__ constexpr size_t al256(size_t x) { return (x + 255) / 256 * 
 
 // ---------------------------------------------------------------------------
 // Workspace: the forward prefill's workspace first (its chunk table is read here), then
-//   pool [ns][H][dk][dv] f32, slots [ns] i32, o_fwd [T][H][dv] (input dtype),
+//   pool [ns][H][dk][dv] f32, slots [ns] i32,
 //   per (chunk, head) item (fp32, row-major):
 //     S [dk][dv]   state entering the chunk (forward carry)
 //     dX [dk][dv]  gradient of the chunk's exit state (scan)
@@ -67,15 +68,14 @@ __host__ __device__ constexpr size_t al256(size_t x) { return (x + 255) / 256 * 
 //     dU [64][dv], dQG, dW, dKt [64][dk], dP [64][64], dgl [dk];  dBK [64][dk], dAg [64][64]
 // ---------------------------------------------------------------------------
 struct BwLayout {
-    size_t fwd, off_pool, off_slots, off_o, off_items, item, total;
+    size_t fwd, off_pool, off_slots, off_items, item, total;
     size_t S, dX, Mt, b, T, Ag, P, W, Ut, gl, dU, dQG, dW, dKt, dP, dgl, dBK, dAg;
     int64_t max_items;
     __host__ __device__ BwLayout(int ns, int64_t T_tot, int H, int dk, int dv, int e) {
         fwd = al256(WsLayout(ns, T_tot, H, dk, dv, e).total);
         off_pool = fwd;
         off_slots = off_pool + al256(sizeof(float) * ns * H * dk * dv);
-        off_o = off_slots + al256(sizeof(int32_t) * ns);
-        off_items = off_o + al256(static_cast<size_t>(T_tot) * H * dv * e);
+        off_items = off_slots + al256(sizeof(int32_t) * ns);
         size_t o = 0;
         auto take = [&](size_t n) {
             const size_t at = o;
@@ -1170,7 +1170,7 @@ void backward_setup(BackwardArgs& b, int dk, int dv, int bf16) {
     b.fwd.pool = reinterpret_cast<float*>(base + bw.off_pool);
     b.fwd.slot_idx = reinterpret_cast<const int32_t*>(base + bw.off_slots);
     b.fwd.h0_from_pool = 1;
-    b.fwd.o = base + bw.off_o;
+    b.fwd.o = nullptr;  // the forward pass keeps only the chunk states
     b.fwd.chunk_states = reinterpret_cast<float*>(base + bw.off_items + bw.S);
     b.fwd.chunk_state_stride = bw.item / sizeof(float);
 }

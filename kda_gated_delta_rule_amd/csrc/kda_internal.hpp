@@ -60,6 +60,8 @@ struct PrefillArgs {
     int H;
     float scale;
     int use_l2;
+    // output [T][H][dv]; nullptr (internal: the backward's forward pass, which keeps only the
+    // chunk states) computes no O, and the intra-chunk records then skip QG and P
     void* o;
     void* workspace;
     // prefix snapshots (0 / nullptr / 0: none): the state after (j + 1) * snap_every tokens of

@@ -545,6 +545,8 @@ __device__ __forceinline__ void intra_compute(const IntraIn<DK, DV, TIn>& X, cha
     float* sPW = sT2 + 5 * DK + wave * DK;  // [wave][DK] 2^(G_end(wave - 1) - chunk start)
 
     const int r = lane & 15, q = lane >> 4, t = 16 * wave + r;
+    // no output (the backward's forward pass): the QG and P records are never read
+    const bool with_o = a.o != nullptr;
 
     // ---- 1. norms, gate cumsum inside the wave, per-wave gate tables ------------------
     // The gates are scaled by log2(e) before the scan, so each exponential below is a
@@ -736,7 +738,7 @@ __device__ __forceinline__ void intra_compute(const IntraIn<DK, DV, TIn>& X, cha
             // records: granule j spans the dk blocks CT j .. CT j + CT - 1
             const u32x4 ktg = f32_to_gran(kt, tag);
             const u32x4 qgg = f32_to_gran(qg, tag);
-            f32x4 qt[RG::CT];
+            f32x4 qt[RG::CT] = {};
 #pragma unroll
             for (int h = 0; h < RG::CT; ++h) {
                 const int cb = RG::CT * j + h;
@@ -750,13 +752,14 @@ __device__ __forceinline__ void intra_compute(const IntraIn<DK, DV, TIn>& X, cha
                 else
                     *reinterpret_cast<f32x4*>(dk) = kt4;
                 // QG^T tile (rows c, columns t): lane holds channels 16 cb + 4q + rr of token t
-                qt[h] = gmma(sel[h], qgg, f32x4{0.f, 0.f, 0.f, 0.f}, tag);
+                if (with_o) qt[h] = gmma(sel[h], qgg, f32x4{0.f, 0.f, 0.f, 0.f}, tag);
             }
             // QG and P are read once, by the output pass: streaming stores, so the Infinity
             // Cache keeps more of the W, Kt, Ut granules that both carries read
-            __builtin_nontemporal_store(
-                tiles_to_gran(qt[0], qt[RG::CT - 1], tag),
-                reinterpret_cast<u32x4*>(rec + ws.o_q + ((static_cast<size_t>(wave) * RG::GK + j) * 64 + lane) * 16));
+            if (with_o)
+                __builtin_nontemporal_store(
+                    tiles_to_gran(qt[0], qt[RG::CT - 1], tag),
+                    reinterpret_cast<u32x4*>(rec + ws.o_q + ((static_cast<size_t>(wave) * RG::GK + j) * 64 + lane) * 16));
             // the diagonal tiles from this lane's own rows (s and t both in this block) on fp32
             // MFMA (no operand split): step e takes channel GW (4 j + q) + e of lane (r, q) as
             // its k index q
@@ -809,9 +812,10 @@ __device__ __forceinline__ void intra_compute(const IntraIn<DK, DV, TIn>& X, cha
     // P granules (rows t of this token block, k over tokens) to the record
 #pragma unroll
     for (int g = 0; g < RG::GT; ++g)
-        __builtin_nontemporal_store(
-            tiles_to_gran(Preg[RG::CT * g], Preg[RG::CT * g + RG::CT - 1], tag),
-            reinterpret_cast<u32x4*>(rec + ws.o_p + ((static_cast<size_t>(wave) * RG::GT + g) * 64 + lane) * 16));
+        if (with_o)
+            __builtin_nontemporal_store(
+                tiles_to_gran(Preg[RG::CT * g], Preg[RG::CT * g + RG::CT - 1], tag),
+                reinterpret_cast<u32x4*>(rec + ws.o_p + ((static_cast<size_t>(wave) * RG::GT + g) * 64 + lane) * 16));
     lds_barrier();
 
     // ---- 4. (the s-operand copies are dead) KG^T for phase 6, KG = 2^G kh from KB =
@@ -1125,7 +1129,8 @@ __device__ __forceinline__ T rec_load(const char* p) {
 template <class SP>
 __device__ __forceinline__ void seg_fetch(SegOps<SP>& F, const char* rec, const WsLayout& ws, int tb, int task,
                                           int cb, int lane, int ub0 = 0) {
-    // task (wave-uniform): 0 = U (W, Ut), 1 = O (QG, P), 2 = W alone (the Phi columns' U);
+    // task (wave-uniform): 0 = U (W, Ut), 1 = O (QG, P), 2 = W alone (the Phi columns' U),
+    // 3 = none (the O waves of an output pass without output);
     // SPLIT = 2: W, and Ut of the global column blocks ub0 .. ub0 + HB - 1 that are state
     // columns (zero for Phi columns)
     if constexpr (SP::SPLIT == 2) {
@@ -1139,7 +1144,7 @@ __device__ __forceinline__ void seg_fetch(SegOps<SP>& F, const char* rec, const 
                                  : f32x4{0.f, 0.f, 0.f, 0.f};
         }
     }
-    {
+    if (task != 3) {
         const char* ab = rec + (task == 1 ? ws.o_q : ws.o_w);
 #pragma unroll
         for (int g = 0; g < SP::GK; ++g) {
@@ -1245,7 +1250,7 @@ __device__ void front_state_out(const PrefillArgs& a, int seq, int h, int bos, i
 template <class SP, class TIn, int MODE>
 __device__ __forceinline__ void seg_step(const SegOps<SP>& F, f32x4 (&S)[SP::SJB], char* sx, char* ux,
                                          __amdgpu_buffer_rsrc_t orsrc, int orow, int ocol, float scale, int tb,
-                                         int part, int cb, int jb0, int lane) {
+                                         int part, bool with_o, int cb, int jb0, int lane) {
     constexpr TIn tag{};
     constexpr int NCW = SP::NCW;  // column blocks of this workgroup (block indices below are its own)
     const int r = lane & 15, q4 = 4 * (lane >> 4);
@@ -1292,7 +1297,7 @@ __device__ __forceinline__ void seg_step(const SegOps<SP>& F, f32x4 (&S)[SP::SJB
     // O task, first half: QG S (the P U half needs this chunk's U)
     f32x4 oacc[MODE == kOut ? SP::VB : 1];
     if constexpr (MODE == kOut) {
-        if (part == 1) {
+        if (part == 1 && with_o) {
 #pragma unroll
             for (int jb = 0; jb < SP::VB; ++jb) oacc[jb] = prod(jb);
         }
@@ -1310,7 +1315,7 @@ __device__ __forceinline__ void seg_step(const SegOps<SP>& F, f32x4 (&S)[SP::SJB
         S[j] = acc;
     }
     if constexpr (MODE == kOut) {
-        if (part == 1) {
+        if (part == 1 && with_o) {
             const int trow = 16 * tb + q4;
 #pragma unroll
             for (int jb = 0; jb < SP::VB; ++jb) {
@@ -1376,7 +1381,8 @@ __global__ __launch_bounds__(kSegThreads) void seg_carry_kernel(PrefillArgs a) {
 
     const char* recs = base + ws.off_rec;
     auto rec_of = [&](int c) { return recs + ws.rec_bytes * (static_cast<size_t>(c) * H + h); };
-    const int task = SPLIT == 2 || part == 0 ? 0 : (MODE == kOut ? 1 : 2);
+    const bool with_o = a.o != nullptr;  // nullptr: chunk states only (the backward's forward pass)
+    const int task = SPLIT == 2 || part == 0 ? 0 : (MODE == kOut ? (with_o ? 1 : 3) : 2);
     const int ub0 = cw0 + part * SP::HB;  // SPLIT = 2: the wave's first U column block
     const int c_last = c_first + nc - 1;
     const int bos = a.cu_seqlens[seq], eos = a.cu_seqlens[seq + 1], cs0 = chunk_off[seq];
@@ -1407,8 +1413,8 @@ __global__ __launch_bounds__(kSegThreads) void seg_carry_kernel(PrefillArgs a) {
                 // output rows of this chunk (an empty range in LOCAL mode, which stores nothing)
                 const int t0 = bos + kChunk * (cc - cs0), L = min(kChunk, eos - t0);
                 const __amdgpu_buffer_rsrc_t orsrc =
-                    buf_rsrc(static_cast<char*>(a.o) + static_cast<int64_t>(t0) * orow * E,
-                             MODE == kOut ? static_cast<int64_t>(L) * orow * E : 0);
+                    buf_rsrc(with_o ? static_cast<char*>(a.o) + static_cast<int64_t>(t0) * orow * E : nullptr,
+                             MODE == kOut && with_o ? static_cast<int64_t>(L) * orow * E : 0);
                 if (MODE == kOut && a.snap_every > 0) snapshot(t0 - bos);  // S = state before this chunk
                 if (MODE == kOut && a.chunk_states) {
                     float* Sc = a.chunk_states + (static_cast<size_t>(cc) * H + h) * a.chunk_state_stride;
@@ -1417,7 +1423,7 @@ __global__ __launch_bounds__(kSegThreads) void seg_carry_kernel(PrefillArgs a) {
 #pragma unroll
                         for (int rr = 0; rr < 4; ++rr) Sc[(16 * cb + q4 + rr) * DV + 16 * (jb0 + j2) + r] = S[j2][rr];
                 }
-                seg_step<SP, TIn, MODE>(F[k], S, sx, ux, orsrc, orow, ocol, a.scale, tb, part, cb, jb0, lane);
+                seg_step<SP, TIn, MODE>(F[k], S, sx, ux, orsrc, orow, ocol, a.scale, tb, part, with_o, cb, jb0, lane);
             }
             seg_fetch(F[k], rec_of(min(cc + NB, c_last)), ws, tb, task, cb, lane, ub0);
         }
