@@ -319,9 +319,9 @@ __device__ void dtok_pair(const float* Xa, const float* Xb, int ldx, const float
     const int r = lane & 15, q = lane >> 4, ch = 16 * cb + r;
     const int Roff = TMODE ? 16 * i - 1 : 16 * i + 15, M = 16 * i + 7;
     const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
-    // per product two independent accumulator chains each for the off-diagonal and the
-    // diagonal part
-    f32x4 oa[2] = {z4, z4}, ob[2] = {z4, z4}, da[2] = {z4, z4}, db[2] = {z4, z4};
+    // one accumulator per product for the off-diagonal and one for the diagonal part (the two
+    // products' chains alternate, so consecutive MFMAs do not wait for each other)
+    f32x4 oa = z4, ob = z4, da = z4, db = z4;
     auto kstep = [&](int k, float ref, f32x4& ca, f32x4& cb2) {
         const float xa = TMODE ? Xa[(16 * i + r) * ldx + k] : Xa[k * ldx + 16 * i + r];
         const float xb = TMODE ? Xb[(16 * i + r) * ldx + k] : Xb[k * ldx + 16 * i + r];
@@ -338,17 +338,17 @@ __device__ void dtok_pair(const float* Xa, const float* Xb, int ldx, const float
         const float ref = G[Roff * ld + ch];
         for (int k0 = kb; k0 < ke; k0 += 8) {
 #pragma unroll
-            for (int h = 0; h < 2; ++h) kstep(k0 + 4 * h + q, ref, oa[h], ob[h]);
+            for (int h = 0; h < 2; ++h) kstep(k0 + 4 * h + q, ref, oa, ob);
         }
     }
     {
         const float ref = G[M * ld + ch];
         for (int k0 = 16 * i; k0 < 16 * i + 16; k0 += 8) {
 #pragma unroll
-            for (int h = 0; h < 2; ++h) kstep(k0 + 4 * h + q, ref, da[h], db[h]);
+            for (int h = 0; h < 2; ++h) kstep(k0 + 4 * h + q, ref, da, db);
         }
     }
-    const f32x4 offa = oa[0] + oa[1], offb = ob[0] + ob[1], dga = da[0] + da[1], dgb = db[0] + db[1];
+    const f32x4 offa = oa, offb = ob, dga = da, dgb = db;
     const float ro = ke > kb ? G[Roff * ld + ch] : 0.f, rm = G[M * ld + ch];
 #pragma unroll
     for (int ii = 0; ii < 4; ++ii) {
