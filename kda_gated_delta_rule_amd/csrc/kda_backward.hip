@@ -101,15 +101,16 @@ struct FwdTables {
 // fp32 MFMA 16x16 tile: C(m, n) += sum_k A(m, k) B(k, n), k in [0, K) (K a multiple of 16);
 // A(m, k) = A[m * am + k * ak], B(k, n) = B[k * bk + n * bn].  Lane l holds C(4 (l / 16) + i,
 // l % 16), i = 0..3.
-// Of every 16 k values, lane (r, q) supplies k = 16 s + 4 q + j to step j of four
-// independent accumulator chains (consecutive MFMAs do not wait for each other's results),
-// so an operand whose k index is contiguous (ak = 1 or bk = 1: every call passes these as
-// constants) is read as one 16-byte LDS load per four steps.  Every base, stride and offset
+// Of every 16 k values, lane (r, q) supplies k = 16 s + 4 q + j to step j (the order of the
+// k sum is free), so an operand whose k index is contiguous (ak = 1 or bk = 1: every call
+// passes these as constants) is read as one 16-byte LDS load per four steps.  One
+// accumulator: the matrix core takes back-to-back accumulation into the same registers, and
+// more chains only add initialisation and combining instructions.  Every base, stride and offset
 // here is a multiple of 4 floats of a 16-byte aligned array.
 __device__ __forceinline__ f32x4 mm16(const float* A, int am, int ak, const float* B, int bk, int bn, int K,
                                       int lane, f32x4 c) {
     const int r = lane & 15, q = lane >> 4;
-    f32x4 acc[4] = {c, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+    f32x4 acc = c;
     for (int k0 = 0; k0 < K; k0 += 16) {
         const int kb = k0 + 4 * q;
         f32x4 av, bv;
@@ -126,9 +127,9 @@ __device__ __forceinline__ f32x4 mm16(const float* A, int am, int ak, const floa
             for (int j = 0; j < 4; ++j) bv[j] = B[(kb + j) * bk + r * bn];
         }
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[j], bv[j], acc[j], 0, 0, 0);
+        for (int j = 0; j < 4; ++j) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[j], bv[j], acc, 0, 0, 0);
     }
-    return (acc[0] + acc[1]) + (acc[2] + acc[3]);
+    return acc;
 }
 
 // Inclusive prefix sum over the 64 lanes of a wave (lane i gets x_0 + ... + x_i): a scan in
@@ -283,10 +284,9 @@ __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x)
 __device__ f32x4 dgram_tile(const float* X, const float* Y, const float* G, int ld, int DK, int i, int j, int lane) {
     const int r = lane & 15, q = lane >> 4;
     const int R = j < i ? 16 * i - 1 : 16 * i + 7;
-    // of every 16 channels, lane (r, q) supplies channels 16 s + 4 q + e to step e of four
-    // chains, so each operand row is read as 16-byte LDS loads (ld and every offset are
-    // multiples of 4 floats)
-    f32x4 c[4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+    // of every 16 channels, lane (r, q) supplies channels 16 s + 4 q + e to step e, so each
+    // operand row is read as 16-byte LDS loads (ld and every offset are multiples of 4 floats)
+    f32x4 c = {0.f, 0.f, 0.f, 0.f};
     for (int k0 = 0; k0 < DK; k0 += 16) {
         const int ch = k0 + 4 * q;
         const f32x4 ref = *reinterpret_cast<const f32x4*>(G + R * ld + ch);
@@ -298,10 +298,10 @@ __device__ f32x4 dgram_tile(const float* X, const float* Y, const float* G, int 
         for (int e = 0; e < 4; ++e) {
             const float av = xt[e] * ex2(gt[e] - ref[e]);
             const float bv = ys[e] * ex2(ref[e] - gs[e]);
-            c[e] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, c[e], 0, 0, 0);
+            c = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, c, 0, 0, 0);
         }
     }
-    return (c[0] + c[1]) + (c[2] + c[3]);
+    return c;
 }
 
 // Decayed token products over a 16 x 16 (rows, channels) output tile.
