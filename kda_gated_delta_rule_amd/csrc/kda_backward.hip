@@ -723,17 +723,17 @@ __global__ __launch_bounds__(64 * (DK / 16)) void bwd_scan_kernel(BackwardArgs b
         // LDS-only barriers: a __syncthreads() would also wait for the loads just issued
         lds_barrier();
         // lane (r, q) supplies k = 16 kb + 4q + ks of Mt row 16 wave + r and of X column r;
-        // four independent accumulator chains (one per ks)
-        f32x4 acc[4] = {cur.bb, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+        // one accumulator (the matrix core accumulates back to back into the same registers)
+        f32x4 acc = cur.bb;
 #pragma unroll
         for (int kb = 0; kb < DK / 16; ++kb) {
             const f32x4 xb = *reinterpret_cast<const f32x4*>(xs + r * LX + 16 * kb + q4);
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks)
-                acc[ks] = __builtin_amdgcn_mfma_f32_16x16x4f32(cur.mt[kb][ks], xb[ks], acc[ks], 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(cur.mt[kb][ks], xb[ks], acc, 0, 0, 0);
         }
         lds_barrier();
-        x = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+        x = acc;
         return true;
     };
     if (nch > 0) {
