@@ -206,11 +206,12 @@ __device__ __forceinline__ void rows_store(const u32x4 (&v)[RowCopy<TIn, W, NT>:
         if (idx >= kC * RC::GPR) break;
         float* d = dst + t * ld + c;
         if constexpr (TIn::bytes == 2) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                d[2 * e] = __uint_as_float(v[i][e] << 16);
-                d[2 * e + 1] = __uint_as_float(v[i][e] & 0xffff0000u);
-            }
+            auto wide = [](uint32_t a, uint32_t b) {
+                return f32x4{__uint_as_float(a << 16), __uint_as_float(a & 0xffff0000u), __uint_as_float(b << 16),
+                             __uint_as_float(b & 0xffff0000u)};
+            };
+            reinterpret_cast<f32x4*>(d)[0] = wide(v[i][0], v[i][1]);
+            reinterpret_cast<f32x4*>(d)[1] = wide(v[i][2], v[i][3]);
         } else {
             *reinterpret_cast<f32x4*>(d) = __builtin_bit_cast(f32x4, v[i]);
         }
@@ -943,26 +944,29 @@ __global__ __launch_bounds__(kT) void bwd_ut_kernel(BackwardArgs b) {
     rows_store<TIn, DV>(rV, sM2, LV);
     r2s<kC, DV>(rU, sM1, LV);
     lds_barrier();
+    // the raw v stays in sV (over sD and sE, free until dT goes there) for the dbeta part
+    float* sV = sDE;
+    static_assert(kC * LV <= 2 * kC * LC, "v fits sD + sE");
     for_groups<DV>([&](int t, int c) {
         f32x4* x = reinterpret_cast<f32x4*>(sM2 + t * LV + c);
-        *x = *x * sB[t];
+        const f32x4 raw = *x;
+        *reinterpret_cast<f32x4*>(sV + t * LV + c) = raw;
+        *x = raw * sB[t];
     });
     lds_barrier();
     for (int sb = 0; sb < 4; ++sb)
         dT[sb] = mm16(sM1 + 16 * wave * LV, LV, 1, sM2 + 16 * sb * LV, 1, LV, DV, lane, dT[sb]);
-    // dBV = T^T dU: dv = beta dBV, dbeta part sum_j v dBV = sum_j BV dBV / beta (v from BV)
+    // dBV = T^T dU: dv = beta dBV, dbeta part sum_j v dBV
     for (int cb = 0; cb < DV / 16; ++cb) {
         const f32x4 v = mm16(sT + 16 * wave, 1, LC, sM1 + 16 * cb, LV, 1, kC, lane, f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) {
             const int t = 16 * wave + 4 * q + ii, j = 16 * cb + r;
-            if (t < it.L) {
-                const float raw = ld_in<TIn>(a.v, (static_cast<int64_t>(it.t0 + t) * H + it.h) * DV + j);
-                part[ii] = fmaf(raw, v[ii], part[ii]);
-                st_out(b.dv, (static_cast<int64_t>(it.t0 + t) * H + it.h) * DV + j, sB[t] * v[ii], TIn{});
-            }
+            part[ii] = fmaf(sV[t * LV + j], v[ii], part[ii]);  // rows past the end: v = 0
+            if (t < it.L) st_out(b.dv, (static_cast<int64_t>(it.t0 + t) * H + it.h) * DV + j, sB[t] * v[ii], TIn{});
         }
     }
+    lds_barrier();  // every wave's reads of sV precede the dT stores over it
     // dT to LDS; E = T^T dT; dA = -(E T^T) (s < t)
     for (int sb = 0; sb < 4; ++sb) put_tile(sD, LC, wave, sb, dT[sb], lane);
     lds_barrier();
