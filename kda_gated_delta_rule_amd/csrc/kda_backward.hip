@@ -617,7 +617,8 @@ template <int DK, int DV, class TIn>
 __global__ __launch_bounds__(kTP) void bwd_prep_kernel(BackwardArgs b) {
     const PrefillArgs& a = b.fwd;
     constexpr int LK = DK + 4, LV = DV + 4, LC = kC + 4, NW = kTP / 64, HK = DK / 32;
-    __shared__ __attribute__((aligned(16))) float sK[kC * LK], sQ[kC * LK], sW[kC * LK], sO[kC * LV], sP[kC * LC], inv[kC];
+    __shared__ __attribute__((aligned(16))) float sK[kC * LK], sQ[kC * LK], sW[kC * LK], sO[kC * LV], sP[kC * LC], inv[kC],
+        sgl[DK];
     float* sG = sW;  // the gate cumsum lives where W goes once Kt and QG are formed
     const BwCtx X(a, DK, DV, TIn::bytes);
     Item it;
@@ -629,6 +630,7 @@ __global__ __launch_bounds__(kTP) void bwd_prep_kernel(BackwardArgs b) {
     load_rows<TIn, DV, DV, kTP>(b.dout, sO, LV, it, H);
     gate_cumsum<DK, kTP>(a.g, sG, LK, it, H);
     g2s<kC, kC, kTP>(X.blk(item, X.bw.P), kC, sP, LC);
+    if (threadIdx.x < DK) sgl[threadIdx.x] = X.blk(item, X.bw.gl)[threadIdx.x];
     lds_barrier();
     // W goes where the gate cumsum is until Kt and QG are formed: its loads stay in flight
     // (registers) until then
@@ -640,7 +642,6 @@ __global__ __launch_bounds__(kTP) void bwd_prep_kernel(BackwardArgs b) {
     to_qg<DK, kTP>(sQ, sG, LK);
     lds_barrier();
     r2s<kC, DK, kTP>(rW, sW, LK);
-    const float* gl = X.blk(item, X.bw.gl);
     lds_barrier();
     // Mt (dk x dk): tile (rb, cb), rows c = W's columns, k over tokens
     float* Mt = X.blk(item, X.bw.Mt);
@@ -651,7 +652,7 @@ __global__ __launch_bounds__(kTP) void bwd_prep_kernel(BackwardArgs b) {
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) {
             const int row = 16 * rb + 4 * q + ii, col = 16 * cb + r;
-            m[ii] = (row == col ? gl[row] : 0.f) - m[ii];
+            m[ii] = (row == col ? sgl[row] : 0.f) - m[ii];
         }
         put_tile(Mt, DK, rb, cb, m, lane);
     }
@@ -966,6 +967,11 @@ __global__ __launch_bounds__(kT) void bwd_ut_kernel(BackwardArgs b) {
             if (t < it.L) st_out(b.dv, (static_cast<int64_t>(it.t0 + t) * H + it.h) * DV + j, sB[t] * v[ii], TIn{});
         }
     }
+    // this wave's rows of Ag for the dbeta part of dA (global), loaded during E
+    const float* Ag = X.blk(item, X.bw.Ag);
+    f32x4 agt[4];
+#pragma unroll
+    for (int sb = 0; sb < 4; ++sb) agt[sb] = get_tile(Ag, kC, wave, sb, lane);
     lds_barrier();  // every wave's reads of sV precede the dT stores over it
     // dT to LDS; E = T^T dT; dA = -(E T^T) (s < t)
     for (int sb = 0; sb < 4; ++sb) put_tile(sD, LC, wave, sb, dT[sb], lane);
@@ -973,15 +979,15 @@ __global__ __launch_bounds__(kT) void bwd_ut_kernel(BackwardArgs b) {
     for (int sb = 0; sb < 4; ++sb)
         put_tile(sE, LC, wave, sb, mm16(sT + 16 * wave, 1, LC, sD + 16 * sb, LC, 1, kC, lane, f32x4{0.f, 0.f, 0.f, 0.f}), lane);
     lds_barrier();
-    const float* Ag = X.blk(item, X.bw.Ag);
     float* dAg = X.blk(item, X.bw.dAg);
+#pragma unroll
     for (int sb = 0; sb < 4; ++sb) {
         f32x4 v = mm16(sE + 16 * wave * LC, LC, 1, sT + 16 * sb * LC, 1, LC, kC, lane, f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) {
             const int t = 16 * wave + 4 * q + ii, s = 16 * sb + r;
             const float da = s < t ? -v[ii] : 0.f;
-            part[ii] = fmaf(da, Ag[t * kC + s], part[ii]);
+            part[ii] = fmaf(da, agt[sb][ii], part[ii]);
             v[ii] = sB[t] * da;
         }
         put_tile(dAg, kC, wave, sb, v, lane);
