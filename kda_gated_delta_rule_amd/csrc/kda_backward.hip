@@ -279,30 +279,35 @@ __device__ void gate_cumsum(const float* g, float* G, int ld, const Item& it, in
 
 __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Decayed Gram tile (t block i, s block j <= i): C(t, s) = sum_c X_tc Y_sc 2^(G_tc - G_sc), the
-// factor split at row R = 16 i - 1 (j < i) or 16 i + 7 (j = i).  Lane holds (t = 16 i + 4q + ii,
-// s = 16 j + r).
-__device__ f32x4 dgram_tile(const float* X, const float* Y, const float* G, int ld, int DK, int i, int j, int lane) {
+// Decayed Gram tiles (t block i, s block j <= i) of the key and the query rows against the key
+// rows: ta(t, s) = sum_c K_tc K_sc 2^(G_tc - G_sc), tp(t, s) = sum_c Q_tc K_sc 2^(G_tc - G_sc),
+// the factor split at row R = 16 i - 1 (j < i) or 16 i + 7 (j = i).  The two share every
+// exponential and the s-side operand.  Lane holds (t = 16 i + 4q + ii, s = 16 j + r).
+__device__ void dgram_pair(const float* K, const float* Q, const float* G, int ld, int DK, int i, int j, int lane,
+                           f32x4& ta, f32x4& tp) {
     const int r = lane & 15, q = lane >> 4;
     const int R = j < i ? 16 * i - 1 : 16 * i + 7;
     // of every 16 channels, lane (r, q) supplies channels 16 s + 4 q + e to step e, so each
     // operand row is read as 16-byte LDS loads (ld and every offset are multiples of 4 floats)
-    f32x4 c = {0.f, 0.f, 0.f, 0.f};
+    f32x4 ca = {0.f, 0.f, 0.f, 0.f}, cp = ca;
     for (int k0 = 0; k0 < DK; k0 += 16) {
         const int ch = k0 + 4 * q;
         const f32x4 ref = *reinterpret_cast<const f32x4*>(G + R * ld + ch);
-        const f32x4 xt = *reinterpret_cast<const f32x4*>(X + (16 * i + r) * ld + ch);
+        const f32x4 kt = *reinterpret_cast<const f32x4*>(K + (16 * i + r) * ld + ch);
+        const f32x4 qt = *reinterpret_cast<const f32x4*>(Q + (16 * i + r) * ld + ch);
         const f32x4 gt = *reinterpret_cast<const f32x4*>(G + (16 * i + r) * ld + ch);
-        const f32x4 ys = *reinterpret_cast<const f32x4*>(Y + (16 * j + r) * ld + ch);
+        const f32x4 ks = *reinterpret_cast<const f32x4*>(K + (16 * j + r) * ld + ch);
         const f32x4 gs = *reinterpret_cast<const f32x4*>(G + (16 * j + r) * ld + ch);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const float av = xt[e] * ex2(gt[e] - ref[e]);
-            const float bv = ys[e] * ex2(ref[e] - gs[e]);
-            c = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, c, 0, 0, 0);
+            const float ft = ex2(gt[e] - ref[e]);
+            const float bv = ks[e] * ex2(ref[e] - gs[e]);
+            ca = __builtin_amdgcn_mfma_f32_16x16x4f32(kt[e] * ft, bv, ca, 0, 0, 0);
+            cp = __builtin_amdgcn_mfma_f32_16x16x4f32(qt[e] * ft, bv, cp, 0, 0, 0);
         }
     }
-    return c;
+    ta = ca;
+    tp = cp;
 }
 
 // Decayed token products over a 16 x 16 (rows, channels) output tile.
@@ -527,26 +532,46 @@ __global__ __launch_bounds__(kT) void bwd_intra_kernel(BackwardArgs b) {
     rows_fetch<TIn, DV>(a.v, rV, it, H);
     normalize_rows(sK, LK, DK, inv, a.use_l2);
     normalize_rows(sQ, LK, DK, inv, a.use_l2);
-    // Ag (strictly lower) and P (lower with the diagonal), tile (i, j <= i) by the wave owning
-    // block i's rows; upper tiles are zero
+    // Ag (strictly lower) and P (lower with the diagonal): the ten tiles (i, j <= i), at most
+    // three per wave (wave 0: (0,0) (3,0) (3,1); wave 1: (1,0) (1,1) (3,2); wave 2: (2,0) (2,1)
+    // (2,2); wave 3: (3,3) and the six zero tiles above the diagonal)
     float* Pg = X.blk(item, X.bw.P);
     float* Ag = X.blk(item, X.bw.Ag);
-    for (int j = 0; j < 4; ++j) {
-        const int i = wave;
-        // tiles above the diagonal (j > i) are computed too (straight-line) and discarded by
-        // the masks below
-        f32x4 ta = dgram_tile(sK, sK, sG, LK, DK, i, j < i ? j : i, lane);
-        f32x4 tp = dgram_tile(sQ, sK, sG, LK, DK, i, j < i ? j : i, lane);
+    {
+        const int w = __builtin_amdgcn_readfirstlane(wave);
         const int r = lane & 15, q = lane >> 4;
 #pragma unroll
-        for (int ii = 0; ii < 4; ++ii) {
-            const int t = 16 * i + 4 * q + ii, s = 16 * j + r;
-            ta[ii] = j <= i && s < t ? ta[ii] : 0.f;
-            tp[ii] = j <= i && s <= t ? tp[ii] : 0.f;
+        for (int n = 0; n < 3; ++n) {
+            // tile index 4 i + j of this wave's slot n (-1: none)
+            const int ij = w == 0 ? (n == 0 ? 0 : n == 1 ? 12 : 13)
+                         : w == 1 ? (n == 0 ? 4 : n == 1 ? 5 : 14)
+                         : w == 2 ? (n == 0 ? 8 : n == 1 ? 9 : 10)
+                                  : (n == 0 ? 15 : -1);
+            if (ij < 0) break;
+            const int i = ij >> 2, j = ij & 3;
+            f32x4 ta, tp;
+            dgram_pair(sK, sQ, sG, LK, DK, i, j, lane, ta, tp);
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) {
+                const int t = 16 * i + 4 * q + ii, s = 16 * j + r;
+                ta[ii] = s < t ? ta[ii] : 0.f;
+                tp[ii] = s <= t ? tp[ii] : 0.f;
+            }
+            put_tile(sA, LC, i, j, ta, lane);
+            put_tile(Pg, kC, i, j, tp, lane);
+            put_tile(Ag, kC, i, j, ta, lane);
         }
-        put_tile(sA, LC, i, j, ta, lane);
-        put_tile(Pg, kC, i, j, tp, lane);
-        put_tile(Ag, kC, i, j, ta, lane);
+        if (w == 3) {
+            const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int i = 0; i < 3; ++i)
+#pragma unroll
+                for (int j = i + 1; j < 4; ++j) {
+                    put_tile(sA, LC, i, j, z, lane);
+                    put_tile(Pg, kC, i, j, z, lane);
+                    put_tile(Ag, kC, i, j, z, lane);
+                }
+        }
     }
     lds_barrier();
     unit_lower_inverse(sA, sB, sT, sY, lane, wave);
