@@ -263,8 +263,7 @@ __device__ void normalize_rows(float* x, int ld, int D, float* inv, int use_l2) 
 // The chunk's gates are first copied into G by all threads (coalesced), then each wave scans
 // columns across its 64 lanes (lane = token).  The caller synchronises before reading G.
 template <int DK, int NT = kT>
-__device__ void gate_cumsum(const float* g, float* G, int ld, const Item& it, int H) {
-    load_rows<F32, DK, DK, NT>(g, G, ld, it, H);
+__device__ void gate_scan(float* G, int ld) {
     lds_barrier();
     // a wave scans four adjacent columns per pass (one 16-byte LDS access per lane)
     const int lane = threadIdx.x & 63;
@@ -275,6 +274,11 @@ __device__ void gate_cumsum(const float* g, float* G, int ld, const Item& it, in
         for (int e = 0; e < 4; ++e) v[e] = wave_prefix64(v[e] * kL2e);
         *p = v;
     }
+}
+template <int DK, int NT = kT>
+__device__ void gate_cumsum(const float* g, float* G, int ld, const Item& it, int H) {
+    load_rows<F32, DK, DK, NT>(g, G, ld, it, H);
+    gate_scan<DK, NT>(G, ld);
 }
 
 __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -475,6 +479,22 @@ __device__ void s2g(const float* s, int sld, float* g, int gld) {
     }
 }
 
+// The opening operands of a per-chunk kernel: every global load is issued before the first
+// LDS store (load_rows and g2s each wait for their own loads before storing, so a sequence of
+// them pays one memory latency per call).
+template <class TIn, int D, int NT = kT>
+struct Rows {
+    u32x4 v[RowCopy<TIn, D, NT>::N];
+    __device__ void fetch(const void* src, const Item& it, int H) { rows_fetch<TIn, D, D, NT>(src, v, it, H); }
+    __device__ void store(float* dst, int ld) const { rows_store<TIn, D, NT>(v, dst, ld); }
+};
+template <int ROWS, int COLS, int NT = kT>
+struct Mat {
+    f32x4 v[MatCopy<ROWS, COLS, NT>::N];
+    __device__ void fetch(const float* g, int gld) { g2r<ROWS, COLS, NT>(g, gld, v); }
+    __device__ void store(float* s, int sld) const { r2s<ROWS, COLS, NT>(v, s, sld); }
+};
+
 struct BwCtx {
     BwLayout bw;
     FwdTables ft;
@@ -521,10 +541,19 @@ __global__ __launch_bounds__(kT) void bwd_intra_kernel(BackwardArgs b) {
     if (!item_of(a, static_cast<const char*>(a.workspace), X.ft, blockIdx.x, it)) return;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, H = a.H;
     const int item = blockIdx.x;
-    load_rows<TIn, DK>(a.k, sK, LK, it, H);
-    load_rows<TIn, DK>(a.q, sQ, LK, it, H);
-    gate_cumsum<DK>(a.g, sG, LK, it, H);
-    if (threadIdx.x < kC) sB[threadIdx.x] = threadIdx.x < it.L ? a.beta[static_cast<int64_t>(it.t0 + threadIdx.x) * H + it.h] : 0.f;
+    {
+        Rows<TIn, DK> rk, rq;
+        Rows<F32, DK> rg;
+        rk.fetch(a.k, it, H);
+        rq.fetch(a.q, it, H);
+        rg.fetch(a.g, it, H);
+        const float bt = threadIdx.x < it.L ? a.beta[static_cast<int64_t>(it.t0 + threadIdx.x) * H + it.h] : 0.f;
+        rk.store(sK, LK);
+        rq.store(sQ, LK);
+        rg.store(sG, LK);
+        if (threadIdx.x < kC) sB[threadIdx.x] = bt;
+    }
+    gate_scan<DK>(sG, LK);
     lds_barrier();
     // v is first needed after T and W: its loads, issued once the first operands are in,
     // stay in flight (registers) until then
@@ -650,12 +679,25 @@ __global__ __launch_bounds__(kTP) void bwd_prep_kernel(BackwardArgs b) {
     if (!item_of(a, static_cast<const char*>(a.workspace), X.ft, blockIdx.x, it)) return;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, H = a.H, item = blockIdx.x;
     const int tb = wave & 3, half = wave >> 2;
-    load_rows<TIn, DK, DK, kTP>(a.k, sK, LK, it, H);
-    load_rows<TIn, DK, DK, kTP>(a.q, sQ, LK, it, H);
-    load_rows<TIn, DV, DV, kTP>(b.dout, sO, LV, it, H);
-    gate_cumsum<DK, kTP>(a.g, sG, LK, it, H);
-    g2s<kC, kC, kTP>(X.blk(item, X.bw.P), kC, sP, LC);
-    if (threadIdx.x < DK) sgl[threadIdx.x] = X.blk(item, X.bw.gl)[threadIdx.x];
+    {
+        Rows<TIn, DK, kTP> rk, rq;
+        Rows<TIn, DV, kTP> ro;
+        Rows<F32, DK, kTP> rg;
+        Mat<kC, kC, kTP> rp;
+        rk.fetch(a.k, it, H);
+        rq.fetch(a.q, it, H);
+        ro.fetch(b.dout, it, H);
+        rg.fetch(a.g, it, H);
+        rp.fetch(X.blk(item, X.bw.P), kC);
+        const float gv = threadIdx.x < DK ? X.blk(item, X.bw.gl)[threadIdx.x] : 0.f;
+        rk.store(sK, LK);
+        rq.store(sQ, LK);
+        ro.store(sO, LV);
+        rg.store(sG, LK);
+        rp.store(sP, LC);
+        if (threadIdx.x < DK) sgl[threadIdx.x] = gv;
+    }
+    gate_scan<DK, kTP>(sG, LK);
     lds_barrier();
     // W goes where the gate cumsum is until Kt and QG are formed: its loads stay in flight
     // (registers) until then
@@ -802,9 +844,18 @@ __global__ __launch_bounds__(kTS) void bwd_state_kernel(BackwardArgs b) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, H = a.H, item = blockIdx.x;
     const int tb = wave & 3, half = wave >> 2;
     const int r = lane & 15, q = lane >> 4;
-    load_rows<TIn, DK, DK, kTS>(a.k, sK, LK, it, H);
-    gate_cumsum<DK, kTS>(a.g, sG, LK, it, H);
-    g2s<kC, kC, kTS>(X.blk(item, X.bw.P), kC, sP, LC);
+    {
+        Rows<TIn, DK, kTS> rk;
+        Rows<F32, DK, kTS> rg;
+        Mat<kC, kC, kTS> rp;
+        rk.fetch(a.k, it, H);
+        rg.fetch(a.g, it, H);
+        rp.fetch(X.blk(item, X.bw.P), kC);
+        rk.store(sK, LK);
+        rg.store(sG, LK);
+        rp.store(sP, LC);
+    }
+    gate_scan<DK, kTS>(sG, LK);
     lds_barrier();
     normalize_rows<kTS>(sK, LK, DK, inv, a.use_l2);
     to_kt<DK, kTS>(sK, sG, LK);
@@ -933,13 +984,21 @@ __global__ __launch_bounds__(kT) void bwd_ut_kernel(BackwardArgs b) {
     static_assert(2 * kC * LC >= kC * LK, "gate cumsum fits sD + sE");
     // KG = kh 2^G (sM2) and dW (sM1); dW's loads stay in flight (registers) until sM1 is free
     f32x4 rW[MatCopy<kC, DK>::N];
-    g2r<kC, DK>(X.blk(item, X.bw.dW), DK, rW);
-    load_rows<TIn, DK>(a.k, sM2, LK, it, H);
-    gate_cumsum<DK>(a.g, sG, LK, it, H);
-    if (threadIdx.x < kC) {
-        sB[threadIdx.x] = threadIdx.x < it.L ? a.beta[static_cast<int64_t>(it.t0 + threadIdx.x) * H + it.h] : 0.f;
+    {
+        Rows<TIn, DK> rk;
+        Rows<F32, DK> rg;
+        Mat<kC, kC> rt;
+        rk.fetch(a.k, it, H);
+        rg.fetch(a.g, it, H);
+        rt.fetch(X.blk(item, X.bw.T), kC);
+        g2r<kC, DK>(X.blk(item, X.bw.dW), DK, rW);
+        const float bt = threadIdx.x < it.L ? a.beta[static_cast<int64_t>(it.t0 + threadIdx.x) * H + it.h] : 0.f;
+        rk.store(sM2, LK);
+        rg.store(sG, LK);
+        rt.store(sT, LC);
+        if (threadIdx.x < kC) sB[threadIdx.x] = bt;
     }
-    g2s<kC, kC>(X.blk(item, X.bw.T), kC, sT, LC);
+    gate_scan<DK>(sG, LK);
     lds_barrier();
     normalize_rows(sM2, LK, DK, inv, a.use_l2);
     to_qg<DK>(sM2, sG, LK);  // kh 2^G
@@ -1045,12 +1104,24 @@ __global__ __launch_bounds__(kT) void bwd_final_kernel(BackwardArgs b) {
     if (!item_of(a, static_cast<const char*>(a.workspace), X.ft, blockIdx.x, it)) return;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, H = a.H, item = blockIdx.x;
     const int r = lane & 15, q = lane >> 4;
-    load_rows<TIn, DK>(a.k, sK, LK, it, H);
-    load_rows<TIn, DK>(a.q, sQ, LK, it, H);
-    gate_cumsum<DK>(a.g, sG, LK, it, H);
-    g2s<kC, kC>(X.blk(item, X.bw.dAg), kC, sA, LC);
-    g2s<kC, kC>(X.blk(item, X.bw.dP), kC, sP, LC);
-    if (threadIdx.x < kC) sB[threadIdx.x] = threadIdx.x < it.L ? a.beta[static_cast<int64_t>(it.t0 + threadIdx.x) * H + it.h] : 0.f;
+    {
+        Rows<TIn, DK> rk, rq;
+        Rows<F32, DK> rg;
+        Mat<kC, kC> ra, rp;
+        rk.fetch(a.k, it, H);
+        rq.fetch(a.q, it, H);
+        rg.fetch(a.g, it, H);
+        ra.fetch(X.blk(item, X.bw.dAg), kC);
+        rp.fetch(X.blk(item, X.bw.dP), kC);
+        const float bt = threadIdx.x < it.L ? a.beta[static_cast<int64_t>(it.t0 + threadIdx.x) * H + it.h] : 0.f;
+        rk.store(sK, LK);
+        rq.store(sQ, LK);
+        rg.store(sG, LK);
+        ra.store(sA, LC);
+        rp.store(sP, LC);
+        if (threadIdx.x < kC) sB[threadIdx.x] = bt;
+    }
+    gate_scan<DK>(sG, LK);
     lds_barrier();
     normalize_rows(sK, LK, DK, ik, a.use_l2);
     normalize_rows(sQ, LK, DK, iq, a.use_l2);
