@@ -332,32 +332,38 @@ __device__ void dtok_pair(const float* Xa, const float* Xb, int ldx, const float
     // one accumulator per product for the off-diagonal and one for the diagonal part (the two
     // products' chains alternate, so consecutive MFMAs do not wait for each other)
     f32x4 oa = z4, ob = z4, da = z4, db = z4;
-    auto kstep = [&](int k, float ref, f32x4& ca, f32x4& cb2) {
-        const float xa = TMODE ? Xa[(16 * i + r) * ldx + k] : Xa[k * ldx + 16 * i + r];
-        const float xb = TMODE ? Xb[(16 * i + r) * ldx + k] : Xb[k * ldx + 16 * i + r];
-        const float g = G[k * ld + ch];
-        const float zf = TMODE ? ex2(ref - g) : ex2(g - ref);
-        const float za = Za[k * ld + ch] * zf;
-        const float zb = SAMEZ ? za : Zb[k * ld + ch] * zf;
-        ca = __builtin_amdgcn_mfma_f32_16x16x4f32(xa, za, ca, 0, 0, 0);
-        cb2 = __builtin_amdgcn_mfma_f32_16x16x4f32(xb, zb, cb2, 0, 0, 0);
+    // a 16-token block: lane (r, q) supplies token k0 + 4q + e to step e (the order of the sum
+    // is free), so in t mode its X row segment is one 16-byte LDS read
+    auto kblock = [&](int k0, float ref, f32x4& ca, f32x4& cb2) {
+        f32x4 xa, xb;
+        if constexpr (TMODE) {
+            xa = *reinterpret_cast<const f32x4*>(Xa + (16 * i + r) * ldx + k0 + 4 * q);
+            xb = *reinterpret_cast<const f32x4*>(Xb + (16 * i + r) * ldx + k0 + 4 * q);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                xa[e] = Xa[(k0 + 4 * q + e) * ldx + 16 * i + r];
+                xb[e] = Xb[(k0 + 4 * q + e) * ldx + 16 * i + r];
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int k = k0 + 4 * q + e;
+            const float g = G[k * ld + ch];
+            const float zf = TMODE ? ex2(ref - g) : ex2(g - ref);
+            const float za = Za[k * ld + ch] * zf;
+            const float zb = SAMEZ ? za : Zb[k * ld + ch] * zf;
+            ca = __builtin_amdgcn_mfma_f32_16x16x4f32(xa[e], za, ca, 0, 0, 0);
+            cb2 = __builtin_amdgcn_mfma_f32_16x16x4f32(xb[e], zb, cb2, 0, 0, 0);
+        }
     };
     // off-diagonal blocks: t mode the s blocks before i, s mode the t blocks after i
     const int kb = TMODE ? 0 : 16 * (i + 1), ke = TMODE ? 16 * i : kC;
     if (ke > kb) {
         const float ref = G[Roff * ld + ch];
-        for (int k0 = kb; k0 < ke; k0 += 8) {
-#pragma unroll
-            for (int h = 0; h < 2; ++h) kstep(k0 + 4 * h + q, ref, oa, ob);
-        }
+        for (int k0 = kb; k0 < ke; k0 += 16) kblock(k0, ref, oa, ob);
     }
-    {
-        const float ref = G[M * ld + ch];
-        for (int k0 = 16 * i; k0 < 16 * i + 16; k0 += 8) {
-#pragma unroll
-            for (int h = 0; h < 2; ++h) kstep(k0 + 4 * h + q, ref, da, db);
-        }
-    }
+    kblock(16 * i, G[M * ld + ch], da, db);
     const f32x4 offa = oa, offb = ob, dga = da, dgb = db;
     const float ro = ke > kb ? G[Roff * ld + ch] : 0.f, rm = G[M * ld + ch];
 #pragma unroll
