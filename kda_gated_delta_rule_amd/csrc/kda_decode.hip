@@ -132,16 +132,25 @@ __device__ __forceinline__ void prep_token(const DecodeArgs& a, TokenLds<DK, BV,
         const FrontArgs& f = a.front;
         const int W = f.conv_width;
         constexpr int CW = 2 * DK + DV;
-        // channel c of input u of the call (u >= 0), or of row u + W - 1 of the state
+        // channel c of input u of the call (u >= 0), or of row u + W - 1 of the state: the
+        // source and index are selected, so each tap is one load
         auto raw = [&](const void* x, int D, int off, int u, int c) -> float {
-            return u >= 0 ? load1<TIn>(x, ((static_cast<int64_t>(n) * a.T + u) * a.H + h) * D + c)
-                          : load1<TIn>(f.conv_state,
-                                       ((static_cast<int64_t>(slot) * a.H + h) * (W - 1) + u + W - 1) * CW + off + c);
+            const bool in = u >= 0;
+            const int64_t idx = in ? ((static_cast<int64_t>(n) * a.T + u) * a.H + h) * D + c
+                                   : ((static_cast<int64_t>(slot) * a.H + h) * (W - 1) + u + W - 1) * CW + off + c;
+            return load1<TIn>(in ? x : f.conv_state, idx);
         };
+        // unrolled to the largest width with every tap's loads unconditional (taps past the
+        // width re-read the last one and are not added), so they are all in flight together
         auto conv = [&](const void* x, const float* w, int D, int off, int c) -> float {
             const float* wc = w + (static_cast<int64_t>(h) * D + c) * W;
             float acc = 0.f;
-            for (int i = 0; i < W; ++i) acc = fmaf(wc[i], raw(x, D, off, t - (W - 1) + i, c), acc);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int ii = i < W ? i : W - 1;
+                const float xv = raw(x, D, off, t - (W - 1) + ii, c), wv = wc[ii];
+                acc = i < W ? fmaf(wv, xv, acc) : acc;
+            }
             return f.conv_silu ? front_silu(acc) : acc;
         };
         const float gs = f.gate_scale[h];
@@ -822,7 +831,7 @@ hipError_t launch_decode_d(const DecodeArgs& a, hipStream_t stream) {
     const dim3 hgrid(static_cast<unsigned>(a.N) * a.H);  // one workgroup per (sequence, head)
     if (a.front.gate_scale) {
         // the input front: the workgroup owns the head's convolution state; up to kFrontTB
-        // tokens as one block, commit mode only
+        // tokens as one block, commit mode only (four waves: eight measured slower)
         hipLaunchKernelGGL((decode_kernel<DK, DV, DV, kFrontTB, TIn, false, true>), hgrid, dim3(kThreads), 0,
                            stream, a);
     } else if (a.T == 1) {
