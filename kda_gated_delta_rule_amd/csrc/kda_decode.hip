@@ -783,22 +783,47 @@ __global__ __launch_bounds__(NTHR) void replay_kernel(ReplayArgs a) {
     if (slot < 0 || acc <= 0) return;
     float* S = a.pool + (static_cast<int64_t>(slot) * a.H + h) * (DK * DV);
 
+    // a block's records as 16-byte loads, all in flight before the first LDS store (records
+    // are 16-byte aligned: 2 dk + dv floats per token, a multiple of 4)
+    constexpr int RV = (2 * DK + BV) / 4, MV = (TB * RV + NTHR - 1) / NTHR;
+    float4 rv[MV];
+    auto fetch = [&](int tb, int nb) {
+#pragma unroll
+        for (int m = 0; m < MV; ++m) {
+            const int idx = tid + m * NTHR, j = idx / RV, e = 4 * (idx % RV);
+            rv[m] = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (j < nb) {
+                const int64_t tok = (static_cast<int64_t>(n) * a.T + tb + j) * a.H + h;
+                const float* rec = a.records + tok * (2 * DK + DV);
+                rv[m] = *reinterpret_cast<const float4*>(e < 2 * DK ? rec + e : rec + 2 * DK + tile * BV + (e - 2 * DK));
+            }
+        }
+    };
+    // the first block's records go out ahead of the state tile (loads complete in issue
+    // order, so they are in LDS while the tile streams in)
+    fetch(0, min(TB, acc));
     float4 s[C::RPT];
 #pragma unroll
     for (int i = 0; i < C::RPT; ++i) s[i] = load_stream4(S + (rg + C::RG * i) * DV + col0);
 
     for (int tb = 0; tb < acc; tb += TB) {
         const int nb = min(TB, acc - tb);
-        for (int idx = tid; idx < nb * (2 * DK + BV); idx += NTHR) {
-            const int j = idx / (2 * DK + BV), e = idx % (2 * DK + BV);
-            const int64_t tok = (static_cast<int64_t>(n) * a.T + tb + j) * a.H + h;
-            const float* rec = a.records + tok * (2 * DK + DV);
-            if (e < DK)
-                Lk[j][C::pos(e)] = rec[e];
-            else if (e < 2 * DK)
-                La[j][C::pos(e - DK)] = rec[e];
-            else
-                Lu[j][e - 2 * DK] = rec[2 * DK + tile * BV + (e - 2 * DK)];
+        if (tb > 0) fetch(tb, nb);
+#pragma unroll
+        for (int m = 0; m < MV; ++m) {
+            const int idx = tid + m * NTHR, j = idx / RV, e = 4 * (idx % RV);
+            if (j < nb) {
+                const float x[4] = {rv[m].x, rv[m].y, rv[m].z, rv[m].w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    if (e < DK)
+                        Lk[j][C::pos(e + i)] = x[i];
+                    else if (e < 2 * DK)
+                        La[j][C::pos(e - DK + i)] = x[i];
+                    else
+                        Lu[j][e - 2 * DK + i] = x[i];
+                }
+            }
         }
         __syncthreads();
         for (int j = 0; j < nb; ++j) {
