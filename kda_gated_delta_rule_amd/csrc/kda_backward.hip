@@ -1099,21 +1099,25 @@ __global__ __launch_bounds__(kT) void bwd_ut_kernel(BackwardArgs b) {
 // 7. bwd_final: X1..X4, dkh, dqh, dG, reverse cumsum, norm backward; dq, dk, dg.
 //    Wave w owns token block w (rows of every output tile).
 // ---------------------------------------------------------------------------
+constexpr int kTF = 512;  // threads of bwd_final
 template <int DK, int DV, class TIn>
-__global__ __launch_bounds__(kT) void bwd_final_kernel(BackwardArgs b) {
+__global__ __launch_bounds__(kTF) void bwd_final_kernel(BackwardArgs b) {
     const PrefillArgs& a = b.fwd;
-    constexpr int LK = DK + 4, LC = kC + 4, NKB = DK / 16;
+    constexpr int LK = DK + 4, LC = kC + 4, NKB = DK / 16, NH = NKB / 2;
     __shared__ __attribute__((aligned(16))) float sK[kC * LK], sQ[kC * LK], sG[kC * LK], sA[kC * LC], sP[kC * LC], iq[kC], ik[kC], sB[kC],
-        sGL[DK];
+        sGL[DK], sNB[2][2][kC];
     const BwCtx X(a, DK, DV, TIn::bytes);
     Item it;
     if (!item_of(a, static_cast<const char*>(a.workspace), X.ft, blockIdx.x, it)) return;
+    // eight waves (two per SIMD): wave (tb, half) takes token block tb and half of the channel
+    // tiles of every per-row result
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, H = a.H, item = blockIdx.x;
+    const int tb = wave & 3, half = wave >> 2, cb0 = NH * half;
     const int r = lane & 15, q = lane >> 4;
     {
-        Rows<TIn, DK> rk, rq;
-        Rows<F32, DK> rg;
-        Mat<kC, kC> ra, rp;
+        Rows<TIn, DK, kTF> rk, rq;
+        Rows<F32, DK, kTF> rg;
+        Mat<kC, kC, kTF> ra, rp;
         rk.fetch(a.k, it, H);
         rq.fetch(a.q, it, H);
         rg.fetch(a.g, it, H);
@@ -1127,69 +1131,81 @@ __global__ __launch_bounds__(kT) void bwd_final_kernel(BackwardArgs b) {
         rp.store(sP, LC);
         if (threadIdx.x < kC) sB[threadIdx.x] = bt;
     }
-    gate_scan<DK>(sG, LK);
+    gate_scan<DK, kTF>(sG, LK);
     lds_barrier();
-    normalize_rows(sK, LK, DK, ik, a.use_l2);
-    normalize_rows(sQ, LK, DK, iq, a.use_l2);
+    normalize_rows<kTF>(sK, LK, DK, ik, a.use_l2);
+    normalize_rows<kTF>(sQ, LK, DK, iq, a.use_l2);
     const float* dBK = X.blk(item, X.bw.dBK);
     const float* dQG = X.blk(item, X.bw.dQG);
     const float* dKt = X.blk(item, X.bw.dKt);
-    // per channel tile: dkh, dqh and dG of this wave's 16 rows
-    f32x4 dkh[NKB], dqh[NKB], dG[NKB];
-    float ktdkt[NKB];  // sum over this lane's rows of Kt dKt (for dG_L)
+    // per channel tile of this wave: dkh, dqh and dG of its 16 rows
+    f32x4 dkh[NH], dqh[NH], dG[NH];
+    float ktdkt[NH];  // sum over this lane's rows of Kt dKt (for dG_L)
     // the channel tile's dBK, dQG and dKt (global) are loaded one tile ahead
-    f32x4 nbk = get_tile(dBK, DK, wave, 0, lane), nqg = get_tile(dQG, DK, wave, 0, lane);
-    f32x4 nkt = get_tile(dKt, DK, wave, 0, lane);
-    for (int cb = 0; cb < NKB; ++cb) {
+    f32x4 nbk = get_tile(dBK, DK, tb, cb0, lane), nqg = get_tile(dQG, DK, tb, cb0, lane);
+    f32x4 nkt = get_tile(dKt, DK, tb, cb0, lane);
+#pragma unroll 1
+    for (int i = 0; i < NH; ++i) {
+        const int cb = cb0 + i;
         const f32x4 dbk = nbk, dqg = nqg, dkt = nkt;
-        if (cb + 1 < NKB) {
-            nbk = get_tile(dBK, DK, wave, cb + 1, lane);
-            nqg = get_tile(dQG, DK, wave, cb + 1, lane);
-            nkt = get_tile(dKt, DK, wave, cb + 1, lane);
+        if (i + 1 < NH) {
+            nbk = get_tile(dBK, DK, tb, cb + 1, lane);
+            nqg = get_tile(dQG, DK, tb, cb + 1, lane);
+            nkt = get_tile(dKt, DK, tb, cb + 1, lane);
         }
         f32x4 x1, x2, x3, x4;
-        dtok_pair<true, true>(sA, sP, LC, sK, sK, sG, LK, wave, cb, lane, x1, x4);
-        dtok_pair<false, false>(sA, sP, LC, sK, sQ, sG, LK, wave, cb, lane, x2, x3);
+        dtok_pair<true, true>(sA, sP, LC, sK, sK, sG, LK, tb, cb, lane, x1, x4);
+        dtok_pair<false, false>(sA, sP, LC, sK, sQ, sG, LK, tb, cb, lane, x2, x3);
         const int c = 16 * cb + r;
         const float gL = sG[(kC - 1) * LK + c];
-        ktdkt[cb] = 0.f;
+        ktdkt[i] = 0.f;
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) {
-            const int t = 16 * wave + 4 * q + ii;
+            const int t = 16 * tb + 4 * q + ii;
             const float kh = sK[t * LK + c], qh = sQ[t * LK + c], Gt = sG[t * LK + c];
             const float eg = ex2(Gt), el = ex2(gL - Gt);
             const float bk = sB[t] * kh * eg, kt = kh * el, qg = qh * eg;
-            dkh[cb][ii] = sB[t] * eg * dbk[ii] + el * dkt[ii] + x1[ii] + x2[ii] + x3[ii];
-            dqh[cb][ii] = eg * dqg[ii] + x4[ii];
-            dG[cb][ii] = qg * dqg[ii] + bk * dbk[ii] - kt * dkt[ii] + kh * (x1[ii] - x2[ii] - x3[ii]) + qh * x4[ii];
-            ktdkt[cb] = fmaf(kt, dkt[ii], ktdkt[cb]);
+            dkh[i][ii] = sB[t] * eg * dbk[ii] + el * dkt[ii] + x1[ii] + x2[ii] + x3[ii];
+            dqh[i][ii] = eg * dqg[ii] + x4[ii];
+            dG[i][ii] = qg * dqg[ii] + bk * dbk[ii] - kt * dkt[ii] + kh * (x1[ii] - x2[ii] - x3[ii]) + qh * x4[ii];
+            ktdkt[i] = fmaf(kt, dkt[ii], ktdkt[i]);
         }
     }
-    // norm backward: row dot products over the channel tiles and the 16 lanes of a row group
+    // norm backward: row dot products over this wave's channel tiles and the 16 lanes of a row
+    // group, then the two halves' sums added through LDS (in the same order by both)
     float pq[4], pk[4];
 #pragma unroll
     for (int ii = 0; ii < 4; ++ii) {
         float x = 0.f, y = 0.f;
-        for (int cb = 0; cb < NKB; ++cb) {
-            const int t = 16 * wave + 4 * q + ii, c = 16 * cb + r;
-            x = fmaf(sQ[t * LK + c], dqh[cb][ii], x);
-            y = fmaf(sK[t * LK + c], dkh[cb][ii], y);
+        for (int i = 0; i < NH; ++i) {
+            const int t = 16 * tb + 4 * q + ii, c = 16 * (cb0 + i) + r;
+            x = fmaf(sQ[t * LK + c], dqh[i][ii], x);
+            y = fmaf(sK[t * LK + c], dkh[i][ii], y);
         }
         for (int m = 1; m < 16; m <<= 1) {
             x += __shfl_xor(x, m, 64);
             y += __shfl_xor(y, m, 64);
         }
-        pq[ii] = x;
-        pk[ii] = y;
+        if (r == 0) {
+            sNB[half][0][16 * tb + 4 * q + ii] = x;
+            sNB[half][1][16 * tb + 4 * q + ii] = y;
+        }
     }
-    for (int cb = 0; cb < NKB; ++cb) {
+    lds_barrier();
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) {
+        const int t = 16 * tb + 4 * q + ii;
+        pq[ii] = sNB[0][0][t] + sNB[1][0][t];
+        pk[ii] = sNB[0][1][t] + sNB[1][1][t];
+    }
+    for (int i = 0; i < NH; ++i) {
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) {
-            const int t = 16 * wave + 4 * q + ii, c = 16 * cb + r;
+            const int t = 16 * tb + 4 * q + ii, c = 16 * (cb0 + i) + r;
             if (t < it.L) {
                 const int64_t o = (static_cast<int64_t>(it.t0 + t) * H + it.h) * DK + c;
-                const float vq = a.use_l2 ? iq[t] * (dqh[cb][ii] - sQ[t * LK + c] * pq[ii]) : dqh[cb][ii];
-                const float vk = a.use_l2 ? ik[t] * (dkh[cb][ii] - sK[t * LK + c] * pk[ii]) : dkh[cb][ii];
+                const float vq = a.use_l2 ? iq[t] * (dqh[i][ii] - sQ[t * LK + c] * pq[ii]) : dqh[i][ii];
+                const float vk = a.use_l2 ? ik[t] * (dkh[i][ii] - sK[t * LK + c] * pk[ii]) : dkh[i][ii];
                 st_out(b.dq, o, vq, TIn{});
                 st_out(b.dk, o, vk, TIn{});
             }
@@ -1200,18 +1216,18 @@ __global__ __launch_bounds__(kT) void bwd_final_kernel(BackwardArgs b) {
     lds_barrier();  // sG's values are no longer read below this point
     if (threadIdx.x < DK) sGL[threadIdx.x] = X.blk(item, X.bw.dgl)[threadIdx.x];
     lds_barrier();
-    for (int cb = 0; cb < NKB; ++cb) {
-        float x = ktdkt[cb];
+    for (int i = 0; i < NH; ++i) {
+        float x = ktdkt[i];
         x += __shfl_xor(x, 16, 64);
         x += __shfl_xor(x, 32, 64);
-        if (q == 0) atomicAdd(&sGL[16 * cb + r], x);
+        if (q == 0) atomicAdd(&sGL[16 * (cb0 + i) + r], x);
     }
-    // dG into sG (rows of this wave), then the reverse cumsum per channel plus dG_L
-    for (int cb = 0; cb < NKB; ++cb) put_tile(sG, LK, wave, cb, dG[cb], lane);
+    // dG into sG (rows of this wave's token block), then the reverse cumsum per channel plus dG_L
+    for (int i = 0; i < NH; ++i) put_tile(sG, LK, tb, cb0 + i, dG[i], lane);
     lds_barrier();
     // suffix sums over the live rows (lane = token): total - inclusive prefix + own value; a
     // wave takes four adjacent columns per pass (one 16-byte LDS access per lane)
-    for (int c = 4 * wave; c < DK; c += 4 * (kT / 64)) {
+    for (int c = 4 * wave; c < DK; c += 4 * (kTF / 64)) {
         f32x4* p = reinterpret_cast<f32x4*>(sG + lane * LK + c);
         const f32x4 v4 = *p;
         f32x4 o4;
@@ -1225,7 +1241,7 @@ __global__ __launch_bounds__(kT) void bwd_final_kernel(BackwardArgs b) {
         *p = o4;
     }
     lds_barrier();
-    for_groups<DK>([&](int t, int c) {
+    for_groups<DK, kTF>([&](int t, int c) {
         if (t < it.L)
             *reinterpret_cast<f32x4*>(b.dg + (static_cast<int64_t>(it.t0 + t) * H + it.h) * DK + c) =
                 *reinterpret_cast<const f32x4*>(sG + t * LK + c);
@@ -1255,7 +1271,7 @@ hipError_t launch_backward_t(const BackwardArgs& b, hipStream_t stream) {
     if (bw.max_items > 0) {
         hipLaunchKernelGGL((bwd_state_kernel<DK, DV, TIn>), grid, dim3(kTS), 0, stream, b);
         hipLaunchKernelGGL((bwd_ut_kernel<DK, DV, TIn>), grid, dim3(kT), 0, stream, b);
-        hipLaunchKernelGGL((bwd_final_kernel<DK, DV, TIn>), grid, dim3(kT), 0, stream, b);
+        hipLaunchKernelGGL((bwd_final_kernel<DK, DV, TIn>), grid, dim3(kTF), 0, stream, b);
     }
     return hipGetLastError();
 }
