@@ -399,12 +399,14 @@ __device__ __forceinline__ f32x4 get_tile(const float* M, int ld, int rb, int cb
 __device__ void unit_lower_inverse(const float* Ag, const float* beta, float* T, float* Y, int lane, int wave) {
     constexpr int LC = kC + 4, LY = 20;
     const int r = lane & 15, q = lane >> 4;
+    // waves 0..3 own the four row blocks; further waves of the caller only join the barriers
+    const bool on = wave < 4;
     // zero the blocks above the diagonal of this wave's rows (4 columns per store)
-    for (int i = lane; i < 16 * (kC / 4); i += 64) {
+    for (int i = lane; on && i < 16 * (kC / 4); i += 64) {
         const int row = 16 * wave + i / (kC / 4), c = 4 * (i % (kC / 4));
         if (c >= 16 * (wave + 1)) *reinterpret_cast<f32x4*>(T + row * LC + c) = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    {
+    if (on) {
         const int col = r, b0 = 16 * wave;
         float x[16];
 #pragma unroll
@@ -424,9 +426,9 @@ __device__ void unit_lower_inverse(const float* Ag, const float* beta, float* T,
         }
     }
     lds_barrier();
-    float* y = Y + wave * 16 * LY;
+    float* y = Y + (on ? wave : 0) * 16 * LY;
     for (int d = 1; d < 4; ++d) {
-        if (wave >= d) {
+        if (on && wave >= d) {
             const int jb = wave - d;
             // y = A_(wave, jb .. wave-1) T_(jb .. wave-1, jb): k over 16 d rows of T
             f32x4 acc = mm16(Ag + 16 * wave * LC + 16 * jb, LC, 1, T + 16 * jb * LC + 16 * jb, LC, 1, 16 * d, lane,
@@ -473,13 +475,13 @@ __device__ void g2s(const float* g, int gld, float* s, int sld) {
     g2r<ROWS, COLS, NT>(g, gld, v);
     r2s<ROWS, COLS, NT>(v, s, sld);
 }
-template <int ROWS, int COLS>
+template <int ROWS, int COLS, int NT = kT>
 __device__ void s2g(const float* s, int sld, float* g, int gld) {
-    constexpr int C4 = COLS / 4, N = ROWS * C4 / kT;
-    static_assert(COLS % 4 == 0 && (ROWS * C4) % kT == 0, "copy shape");
+    constexpr int C4 = COLS / 4, N = ROWS * C4 / NT;
+    static_assert(COLS % 4 == 0 && (ROWS * C4) % NT == 0, "copy shape");
 #pragma unroll
     for (int i = 0; i < N; ++i) {
-        const int idx = threadIdx.x + i * kT;
+        const int idx = threadIdx.x + i * NT;
         *reinterpret_cast<f32x4*>(g + (idx / C4) * gld + 4 * (idx % C4)) =
             *reinterpret_cast<const f32x4*>(s + (idx / C4) * sld + 4 * (idx % C4));
     }
@@ -536,8 +538,9 @@ __global__ __launch_bounds__(kT) void bwd_init_kernel(BackwardArgs b, int dk, in
 // ---------------------------------------------------------------------------
 // 2. bwd_intra: Ag, P, T, W, Ut, exp(G_L) of one (chunk, head)
 // ---------------------------------------------------------------------------
+constexpr int kTI = 512;  // threads of bwd_intra
 template <int DK, int DV, class TIn>
-__global__ __launch_bounds__(kT) void bwd_intra_kernel(BackwardArgs b) {
+__global__ __launch_bounds__(kTI) void bwd_intra_kernel(BackwardArgs b) {
     const PrefillArgs& a = b.fwd;
     constexpr int LK = DK + 4, LV = DV + 4, LC = kC + 4, LM = LK > LV ? LK : LV;
     __shared__ __attribute__((aligned(16))) float sK[kC * LM], sQ[kC * LK], sG[kC * LK], sA[kC * LC], sT[kC * LC], sY[4 * 16 * 20], inv[kC],
@@ -545,11 +548,14 @@ __global__ __launch_bounds__(kT) void bwd_intra_kernel(BackwardArgs b) {
     const BwCtx X(a, DK, DV, TIn::bytes);
     Item it;
     if (!item_of(a, static_cast<const char*>(a.workspace), X.ft, blockIdx.x, it)) return;
+    // eight waves (two per SIMD): the Gram tiles spread over all of them; wave (tb, half) takes
+    // token block tb and half of the column tiles of W and Ut; the UT inverse runs on waves 0..3
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, H = a.H;
+    const int tb = wave & 3, half = wave >> 2;
     const int item = blockIdx.x;
     {
-        Rows<TIn, DK> rk, rq;
-        Rows<F32, DK> rg;
+        Rows<TIn, DK, kTI> rk, rq;
+        Rows<F32, DK, kTI> rg;
         rk.fetch(a.k, it, H);
         rq.fetch(a.q, it, H);
         rg.fetch(a.g, it, H);
@@ -559,29 +565,32 @@ __global__ __launch_bounds__(kT) void bwd_intra_kernel(BackwardArgs b) {
         rg.store(sG, LK);
         if (threadIdx.x < kC) sB[threadIdx.x] = bt;
     }
-    gate_scan<DK>(sG, LK);
+    gate_scan<DK, kTI>(sG, LK);
     lds_barrier();
     // v is first needed after T and W: its loads, issued once the first operands are in,
     // stay in flight (registers) until then
-    u32x4 rV[RowCopy<TIn, DV>::N];
-    rows_fetch<TIn, DV>(a.v, rV, it, H);
-    normalize_rows(sK, LK, DK, inv, a.use_l2);
-    normalize_rows(sQ, LK, DK, inv, a.use_l2);
+    u32x4 rV[RowCopy<TIn, DV, kTI>::N];
+    rows_fetch<TIn, DV, DV, kTI>(a.v, rV, it, H);
+    normalize_rows<kTI>(sK, LK, DK, inv, a.use_l2);
+    normalize_rows<kTI>(sQ, LK, DK, inv, a.use_l2);
     // Ag (strictly lower) and P (lower with the diagonal): the ten tiles (i, j <= i), at most
-    // three per wave (wave 0: (0,0) (3,0) (3,1); wave 1: (1,0) (1,1) (3,2); wave 2: (2,0) (2,1)
-    // (2,2); wave 3: (3,3) and the six zero tiles above the diagonal)
+    // two per wave (wave 0: (0,0) (3,0); 1: (1,0) (3,1); 2: (1,1) (3,2); 3: (2,0) (3,3);
+    // 4: (2,1); 5: (2,2); wave 6 the six zero tiles above the diagonal)
     float* Pg = X.blk(item, X.bw.P);
     float* Ag = X.blk(item, X.bw.Ag);
     {
         const int w = __builtin_amdgcn_readfirstlane(wave);
         const int r = lane & 15, q = lane >> 4;
 #pragma unroll
-        for (int n = 0; n < 3; ++n) {
+        for (int n = 0; n < 2; ++n) {
             // tile index 4 i + j of this wave's slot n (-1: none)
-            const int ij = w == 0 ? (n == 0 ? 0 : n == 1 ? 12 : 13)
-                         : w == 1 ? (n == 0 ? 4 : n == 1 ? 5 : 14)
-                         : w == 2 ? (n == 0 ? 8 : n == 1 ? 9 : 10)
-                                  : (n == 0 ? 15 : -1);
+            const int ij = w == 0 ? (n == 0 ? 0 : 12)
+                         : w == 1 ? (n == 0 ? 4 : 13)
+                         : w == 2 ? (n == 0 ? 5 : 14)
+                         : w == 3 ? (n == 0 ? 8 : 15)
+                         : w == 4 ? (n == 0 ? 9 : -1)
+                         : w == 5 ? (n == 0 ? 10 : -1)
+                                  : -1;
             if (ij < 0) break;
             const int i = ij >> 2, j = ij & 3;
             f32x4 ta, tp;
@@ -596,7 +605,7 @@ __global__ __launch_bounds__(kT) void bwd_intra_kernel(BackwardArgs b) {
             put_tile(Pg, kC, i, j, tp, lane);
             put_tile(Ag, kC, i, j, ta, lane);
         }
-        if (w == 3) {
+        if (w == 6) {
             const f32x4 z = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int i = 0; i < 3; ++i)
@@ -610,9 +619,9 @@ __global__ __launch_bounds__(kT) void bwd_intra_kernel(BackwardArgs b) {
     }
     lds_barrier();
     unit_lower_inverse(sA, sB, sT, sY, lane, wave);
-    s2g<kC, kC>(sT, LC, X.blk(item, X.bw.T), kC);
+    s2g<kC, kC, kTI>(sT, LC, X.blk(item, X.bw.T), kC);
     // BK = beta kh 2^G into sQ (P is done), then W = T BK
-    for_groups<DK>([&](int t, int c) {
+    for_groups<DK, kTI>([&](int t, int c) {
         const f32x4 k4 = *reinterpret_cast<const f32x4*>(sK + t * LK + c);
         const f32x4 g4 = *reinterpret_cast<const f32x4*>(sG + t * LK + c);
         f32x4 b4;
@@ -623,23 +632,23 @@ __global__ __launch_bounds__(kT) void bwd_intra_kernel(BackwardArgs b) {
     if (threadIdx.x < DK) X.blk(item, X.bw.gl)[threadIdx.x] = ex2(sG[(kC - 1) * LK + threadIdx.x]);
     lds_barrier();
     float* Wg = X.blk(item, X.bw.W);
-    for (int cb = 0; cb < DK / 16; ++cb) {
-        const f32x4 w = mm16(sT + 16 * wave * LC, LC, 1, sQ + 16 * cb, LK, 1, kC, lane, f32x4{0.f, 0.f, 0.f, 0.f});
-        put_tile(Wg, DK, wave, cb, w, lane);
+    for (int cb = half * (DK / 32); cb < (half + 1) * (DK / 32); ++cb) {
+        const f32x4 w = mm16(sT + 16 * tb * LC, LC, 1, sQ + 16 * cb, LK, 1, kC, lane, f32x4{0.f, 0.f, 0.f, 0.f});
+        put_tile(Wg, DK, tb, cb, w, lane);
     }
     lds_barrier();
     // BV = beta v into sK, then Ut = T BV
-    rows_store<TIn, DV>(rV, sK, LV);
+    rows_store<TIn, DV, kTI>(rV, sK, LV);
     lds_barrier();
-    for_groups<DV>([&](int t, int c) {
+    for_groups<DV, kTI>([&](int t, int c) {
         f32x4* x = reinterpret_cast<f32x4*>(sK + t * LV + c);
         *x = *x * sB[t];
     });
     lds_barrier();
     float* Ug = X.blk(item, X.bw.Ut);
-    for (int cb = 0; cb < DV / 16; ++cb) {
-        const f32x4 u = mm16(sT + 16 * wave * LC, LC, 1, sK + 16 * cb, LV, 1, kC, lane, f32x4{0.f, 0.f, 0.f, 0.f});
-        put_tile(Ug, DV, wave, cb, u, lane);
+    for (int cb = half * (DV / 32); cb < (half + 1) * (DV / 32); ++cb) {
+        const f32x4 u = mm16(sT + 16 * tb * LC, LC, 1, sK + 16 * cb, LV, 1, kC, lane, f32x4{0.f, 0.f, 0.f, 0.f});
+        put_tile(Ug, DV, tb, cb, u, lane);
     }
 }
 
@@ -1262,7 +1271,7 @@ hipError_t launch_backward_t(const BackwardArgs& b, hipStream_t stream) {
     if (err != hipSuccess) return err;
     const dim3 grid(static_cast<unsigned>(bw.max_items));
     if (bw.max_items > 0) {
-        hipLaunchKernelGGL((bwd_intra_kernel<DK, DV, TIn>), grid, dim3(kT), 0, stream, b);
+        hipLaunchKernelGGL((bwd_intra_kernel<DK, DV, TIn>), grid, dim3(kTI), 0, stream, b);
         hipLaunchKernelGGL((bwd_prep_kernel<DK, DV, TIn>), grid, dim3(kTP), 0, stream, b);
     }
     const int sgroups = (a.num_seqs * a.H + kXcd - 1) / kXcd;
