@@ -982,116 +982,127 @@ __global__ __launch_bounds__(kTS) void bwd_state_kernel(BackwardArgs b) {
 // 6. bwd_ut: dT = dW BK^T + dU BV^T, dBK = T^T dW, dBV = T^T dU, dA = -(T^T dT T^T) (s < t);
 //    dv = beta dBV, dbeta = sum v dBV + sum kh 2^G dBK + sum_s dA Ag, dAg = beta dA.
 // ---------------------------------------------------------------------------
+constexpr int kTU = 512;  // threads of bwd_ut
 template <int DK, int DV, class TIn>
-__global__ __launch_bounds__(kT) void bwd_ut_kernel(BackwardArgs b) {
+__global__ __launch_bounds__(kTU) void bwd_ut_kernel(BackwardArgs b) {
     const PrefillArgs& a = b.fwd;
     constexpr int LK = DK + 4, LV = DV + 4, LC = kC + 4;
     constexpr int LM = LK > LV ? LK : LV;
-    __shared__ __attribute__((aligned(16))) float sT[kC * LC], sM1[kC * LM], sM2[kC * LM], sDE[2 * kC * LC], inv[kC], sB[kC];
+    __shared__ __attribute__((aligned(16))) float sT[kC * LC], sM1[kC * LM], sM2[kC * LM], sDE[2 * kC * LC], inv[kC], sB[kC],
+        sDB[2][kC];
     float* sD = sDE;
     float* sE = sDE + kC * LC;
     float* sG = sDE;  // the gate cumsum (DK wide) spans sD and sE while KG is formed
     const BwCtx X(a, DK, DV, TIn::bytes);
     Item it;
     if (!item_of(a, static_cast<const char*>(a.workspace), X.ft, blockIdx.x, it)) return;
+    // eight waves (two per SIMD): wave (tb, half) takes token block tb (the rows of every
+    // output tile) and half of its column tiles; dbeta adds the two halves through LDS
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, H = a.H, item = blockIdx.x;
+    const int tb = wave & 3, half = wave >> 2;
     const int r = lane & 15, q = lane >> 4;
     static_assert(2 * kC * LC >= kC * LK, "gate cumsum fits sD + sE");
     // KG = kh 2^G (sM2) and dW (sM1); dW's loads stay in flight (registers) until sM1 is free
-    f32x4 rW[MatCopy<kC, DK>::N];
+    f32x4 rW[MatCopy<kC, DK, kTU>::N];
     {
-        Rows<TIn, DK> rk;
-        Rows<F32, DK> rg;
-        Mat<kC, kC> rt;
+        Rows<TIn, DK, kTU> rk;
+        Rows<F32, DK, kTU> rg;
+        Mat<kC, kC, kTU> rt;
         rk.fetch(a.k, it, H);
         rg.fetch(a.g, it, H);
         rt.fetch(X.blk(item, X.bw.T), kC);
-        g2r<kC, DK>(X.blk(item, X.bw.dW), DK, rW);
+        g2r<kC, DK, kTU>(X.blk(item, X.bw.dW), DK, rW);
         const float bt = threadIdx.x < it.L ? a.beta[static_cast<int64_t>(it.t0 + threadIdx.x) * H + it.h] : 0.f;
         rk.store(sM2, LK);
         rg.store(sG, LK);
         rt.store(sT, LC);
         if (threadIdx.x < kC) sB[threadIdx.x] = bt;
     }
-    gate_scan<DK>(sG, LK);
+    gate_scan<DK, kTU>(sG, LK);
     lds_barrier();
-    normalize_rows(sM2, LK, DK, inv, a.use_l2);
-    to_qg<DK>(sM2, sG, LK);  // kh 2^G
-    r2s<kC, DK>(rW, sM1, LK);
+    normalize_rows<kTU>(sM2, LK, DK, inv, a.use_l2);
+    to_qg<DK, kTU>(sM2, sG, LK);  // kh 2^G
+    r2s<kC, DK, kTU>(rW, sM1, LK);
     lds_barrier();
     // v and dU load during the dT and dBK products
-    u32x4 rV[RowCopy<TIn, DV>::N];
-    f32x4 rU[MatCopy<kC, DV>::N];
-    rows_fetch<TIn, DV>(a.v, rV, it, H);
-    g2r<kC, DV>(X.blk(item, X.bw.dU), DV, rU);
-    // dT (part 1: dW BK^T, BK = beta KG, so column s takes beta_s) and dBK of this wave's
-    // rows; dbeta part sum_c KG dBK
-    f32x4 dT[4];
-    for (int sb = 0; sb < 4; ++sb)
-        dT[sb] = mm16(sM1 + 16 * wave * LK, LK, 1, sM2 + 16 * sb * LK, 1, LK, DK, lane, f32x4{0.f, 0.f, 0.f, 0.f}) *
-                 sB[16 * sb + r];
+    u32x4 rV[RowCopy<TIn, DV, kTU>::N];
+    f32x4 rU[MatCopy<kC, DV, kTU>::N];
+    rows_fetch<TIn, DV, DV, kTU>(a.v, rV, it, H);
+    g2r<kC, DV, kTU>(X.blk(item, X.bw.dU), DV, rU);
+    // dT (part 1: dW BK^T, BK = beta KG, so column s takes beta_s; this wave's tiles (tb, sb),
+    // sb = 2 half, 2 half + 1) and dBK of its rows; dbeta part sum_c KG dBK
+    f32x4 dT[2];
+    for (int i = 0; i < 2; ++i) {
+        const int sb = 2 * half + i;
+        dT[i] = mm16(sM1 + 16 * tb * LK, LK, 1, sM2 + 16 * sb * LK, 1, LK, DK, lane, f32x4{0.f, 0.f, 0.f, 0.f}) *
+                sB[16 * sb + r];
+    }
     float* dBK = X.blk(item, X.bw.dBK);
     float part[4] = {0.f, 0.f, 0.f, 0.f};
-    for (int cb = 0; cb < DK / 16; ++cb) {
-        const f32x4 v = mm16(sT + 16 * wave, 1, LC, sM1 + 16 * cb, LK, 1, kC, lane, f32x4{0.f, 0.f, 0.f, 0.f});
-        put_tile(dBK, DK, wave, cb, v, lane);
-        const f32x4 kg = get_tile(sM2, LK, wave, cb, lane);
+    for (int cb = half * (DK / 32); cb < (half + 1) * (DK / 32); ++cb) {
+        const f32x4 v = mm16(sT + 16 * tb, 1, LC, sM1 + 16 * cb, LK, 1, kC, lane, f32x4{0.f, 0.f, 0.f, 0.f});
+        put_tile(dBK, DK, tb, cb, v, lane);
+        const f32x4 kg = get_tile(sM2, LK, tb, cb, lane);
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) part[ii] = fmaf(kg[ii], v[ii], part[ii]);
     }
     lds_barrier();
     // BV = beta v (sM2) and dU (sM1)
-    rows_store<TIn, DV>(rV, sM2, LV);
-    r2s<kC, DV>(rU, sM1, LV);
+    rows_store<TIn, DV, kTU>(rV, sM2, LV);
+    r2s<kC, DV, kTU>(rU, sM1, LV);
     lds_barrier();
     // the raw v stays in sV (over sD and sE, free until dT goes there) for the dbeta part
     float* sV = sDE;
     static_assert(kC * LV <= 2 * kC * LC, "v fits sD + sE");
-    for_groups<DV>([&](int t, int c) {
+    for_groups<DV, kTU>([&](int t, int c) {
         f32x4* x = reinterpret_cast<f32x4*>(sM2 + t * LV + c);
         const f32x4 raw = *x;
         *reinterpret_cast<f32x4*>(sV + t * LV + c) = raw;
         *x = raw * sB[t];
     });
     lds_barrier();
-    for (int sb = 0; sb < 4; ++sb)
-        dT[sb] = mm16(sM1 + 16 * wave * LV, LV, 1, sM2 + 16 * sb * LV, 1, LV, DV, lane, dT[sb]);
+    for (int i = 0; i < 2; ++i)
+        dT[i] = mm16(sM1 + 16 * tb * LV, LV, 1, sM2 + 16 * (2 * half + i) * LV, 1, LV, DV, lane, dT[i]);
     // dBV = T^T dU: dv = beta dBV, dbeta part sum_j v dBV
-    for (int cb = 0; cb < DV / 16; ++cb) {
-        const f32x4 v = mm16(sT + 16 * wave, 1, LC, sM1 + 16 * cb, LV, 1, kC, lane, f32x4{0.f, 0.f, 0.f, 0.f});
+    for (int cb = half * (DV / 32); cb < (half + 1) * (DV / 32); ++cb) {
+        const f32x4 v = mm16(sT + 16 * tb, 1, LC, sM1 + 16 * cb, LV, 1, kC, lane, f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) {
-            const int t = 16 * wave + 4 * q + ii, j = 16 * cb + r;
+            const int t = 16 * tb + 4 * q + ii, j = 16 * cb + r;
             part[ii] = fmaf(sV[t * LV + j], v[ii], part[ii]);  // rows past the end: v = 0
             if (t < it.L) st_out(b.dv, (static_cast<int64_t>(it.t0 + t) * H + it.h) * DV + j, sB[t] * v[ii], TIn{});
         }
     }
     // this wave's rows of Ag for the dbeta part of dA (global), loaded during E
     const float* Ag = X.blk(item, X.bw.Ag);
-    f32x4 agt[4];
+    f32x4 agt[2];
 #pragma unroll
-    for (int sb = 0; sb < 4; ++sb) agt[sb] = get_tile(Ag, kC, wave, sb, lane);
+    for (int i = 0; i < 2; ++i) agt[i] = get_tile(Ag, kC, tb, 2 * half + i, lane);
     lds_barrier();  // every wave's reads of sV precede the dT stores over it
     // dT to LDS; E = T^T dT; dA = -(E T^T) (s < t)
-    for (int sb = 0; sb < 4; ++sb) put_tile(sD, LC, wave, sb, dT[sb], lane);
+    for (int i = 0; i < 2; ++i) put_tile(sD, LC, tb, 2 * half + i, dT[i], lane);
     lds_barrier();
-    for (int sb = 0; sb < 4; ++sb)
-        put_tile(sE, LC, wave, sb, mm16(sT + 16 * wave, 1, LC, sD + 16 * sb, LC, 1, kC, lane, f32x4{0.f, 0.f, 0.f, 0.f}), lane);
+    for (int i = 0; i < 2; ++i) {
+        const int sb = 2 * half + i;
+        put_tile(sE, LC, tb, sb, mm16(sT + 16 * tb, 1, LC, sD + 16 * sb, LC, 1, kC, lane, f32x4{0.f, 0.f, 0.f, 0.f}), lane);
+    }
     lds_barrier();
     float* dAg = X.blk(item, X.bw.dAg);
 #pragma unroll
-    for (int sb = 0; sb < 4; ++sb) {
-        f32x4 v = mm16(sE + 16 * wave * LC, LC, 1, sT + 16 * sb * LC, 1, LC, kC, lane, f32x4{0.f, 0.f, 0.f, 0.f});
+    for (int i = 0; i < 2; ++i) {
+        const int sb = 2 * half + i;
+        f32x4 v = mm16(sE + 16 * tb * LC, LC, 1, sT + 16 * sb * LC, 1, LC, kC, lane, f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) {
-            const int t = 16 * wave + 4 * q + ii, s = 16 * sb + r;
+            const int t = 16 * tb + 4 * q + ii, s = 16 * sb + r;
             const float da = s < t ? -v[ii] : 0.f;
-            part[ii] = fmaf(da, agt[sb][ii], part[ii]);
+            part[ii] = fmaf(da, agt[i][ii], part[ii]);
             v[ii] = sB[t] * da;
         }
-        put_tile(dAg, kC, wave, sb, v, lane);
+        put_tile(dAg, kC, tb, sb, v, lane);
     }
-    // dbeta: reduce the partial sums over the 16 lanes of each row group
+    // dbeta: reduce the partial sums over the 16 lanes of each row group, then add the two
+    // halves (in the same order for every row)
 #pragma unroll
     for (int ii = 0; ii < 4; ++ii) {
         float x = part[ii];
@@ -1099,9 +1110,11 @@ __global__ __launch_bounds__(kT) void bwd_ut_kernel(BackwardArgs b) {
         x += __shfl_xor(x, 2, 64);
         x += __shfl_xor(x, 4, 64);
         x += __shfl_xor(x, 8, 64);
-        const int t = 16 * wave + 4 * q + ii;
-        if (r == 0 && t < it.L) b.dbeta[static_cast<int64_t>(it.t0 + t) * H + it.h] = x;
+        if (r == 0) sDB[half][16 * tb + 4 * q + ii] = x;
     }
+    lds_barrier();
+    if (threadIdx.x < it.L)
+        b.dbeta[static_cast<int64_t>(it.t0 + threadIdx.x) * H + it.h] = sDB[0][threadIdx.x] + sDB[1][threadIdx.x];
 }
 
 // ---------------------------------------------------------------------------
@@ -1279,7 +1292,7 @@ hipError_t launch_backward_t(const BackwardArgs& b, hipStream_t stream) {
                        dim3(64 * (DK / 16)), 0, stream, b, E);
     if (bw.max_items > 0) {
         hipLaunchKernelGGL((bwd_state_kernel<DK, DV, TIn>), grid, dim3(kTS), 0, stream, b);
-        hipLaunchKernelGGL((bwd_ut_kernel<DK, DV, TIn>), grid, dim3(kT), 0, stream, b);
+        hipLaunchKernelGGL((bwd_ut_kernel<DK, DV, TIn>), grid, dim3(kTU), 0, stream, b);
         hipLaunchKernelGGL((bwd_final_kernel<DK, DV, TIn>), grid, dim3(kTF), 0, stream, b);
     }
     return hipGetLastError();
