@@ -678,14 +678,14 @@ __device__ void to_qg(float* Q, const float* G, int ld) {
 }
 
 // ---------------------------------------------------------------------------
-// 3. bwd_prep: Mt = diag(e^(G_L)) - W^T Kt,  b = scale (QG - P W)^T dO.  Eight waves (two
+// 3. bwd_prep: Mt = diag(e^(G_L)) - W^T Kt,  b = scale (QG - P W)^T dO.  Sixteen waves (four
 //    per SIMD) share the output tiles.
 // ---------------------------------------------------------------------------
-constexpr int kTP = 512;  // threads of bwd_prep
+constexpr int kTP = 1024;  // threads of bwd_prep
 template <int DK, int DV, class TIn>
 __global__ __launch_bounds__(kTP) void bwd_prep_kernel(BackwardArgs b) {
     const PrefillArgs& a = b.fwd;
-    constexpr int LK = DK + 4, LV = DV + 4, LC = kC + 4, NW = kTP / 64, HK = DK / 32;
+    constexpr int LK = DK + 4, LV = DV + 4, LC = kC + 4, NW = kTP / 64, NQ = (DK / 16) / (NW / 4);
     __shared__ __attribute__((aligned(16))) float sK[kC * LK], sQ[kC * LK], sW[kC * LK], sO[kC * LV], sP[kC * LC], inv[kC],
         sgl[DK];
     float* sG = sW;  // the gate cumsum lives where W goes once Kt and QG are formed
@@ -693,7 +693,7 @@ __global__ __launch_bounds__(kTP) void bwd_prep_kernel(BackwardArgs b) {
     Item it;
     if (!item_of(a, static_cast<const char*>(a.workspace), X.ft, blockIdx.x, it)) return;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, H = a.H, item = blockIdx.x;
-    const int tb = wave & 3, half = wave >> 2;
+    const int tb = wave & 3, part = wave >> 2;
     {
         Rows<TIn, DK, kTP> rk, rq;
         Rows<TIn, DV, kTP> ro;
@@ -738,10 +738,10 @@ __global__ __launch_bounds__(kTP) void bwd_prep_kernel(BackwardArgs b) {
         }
         put_tile(Mt, DK, rb, cb, m, lane);
     }
-    // Q' = QG - P W in place over QG: wave (tb, half) takes token block tb and half of the
+    // Q' = QG - P W in place over QG: wave (tb, part) takes token block tb and a quarter of the
     // channel tiles (only it reads or writes those tiles of sQ here)
-    for (int i = 0; i < HK; ++i) {
-        const int cb = HK * half + i;
+    for (int i = 0; i < NQ; ++i) {
+        const int cb = NQ * part + i;
         const f32x4 pw = mm16(sP + 16 * tb * LC, LC, 1, sW + 16 * cb, LK, 1, kC, lane, f32x4{0.f, 0.f, 0.f, 0.f});
         put_tile(sQ, LK, tb, cb, get_tile(sQ, LK, tb, cb, lane) - pw, lane);
     }
