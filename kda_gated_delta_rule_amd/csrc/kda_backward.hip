@@ -982,24 +982,26 @@ __global__ __launch_bounds__(kTS) void bwd_state_kernel(BackwardArgs b) {
 // 6. bwd_ut: dT = dW BK^T + dU BV^T, dBK = T^T dW, dBV = T^T dU, dA = -(T^T dT T^T) (s < t);
 //    dv = beta dBV, dbeta = sum v dBV + sum kh 2^G dBK + sum_s dA Ag, dAg = beta dA.
 // ---------------------------------------------------------------------------
-constexpr int kTU = 512;  // threads of bwd_ut
+constexpr int kTU = 1024;  // threads of bwd_ut
 template <int DK, int DV, class TIn>
 __global__ __launch_bounds__(kTU) void bwd_ut_kernel(BackwardArgs b) {
     const PrefillArgs& a = b.fwd;
     constexpr int LK = DK + 4, LV = DV + 4, LC = kC + 4;
     constexpr int LM = LK > LV ? LK : LV;
     __shared__ __attribute__((aligned(16))) float sT[kC * LC], sM1[kC * LM], sM2[kC * LM], sDE[2 * kC * LC], inv[kC], sB[kC],
-        sDB[2][kC];
+        sDB[kTU / 256][kC];
     float* sD = sDE;
     float* sE = sDE + kC * LC;
     float* sG = sDE;  // the gate cumsum (DK wide) spans sD and sE while KG is formed
     const BwCtx X(a, DK, DV, TIn::bytes);
     Item it;
     if (!item_of(a, static_cast<const char*>(a.workspace), X.ft, blockIdx.x, it)) return;
-    // eight waves (two per SIMD): wave (tb, half) takes token block tb (the rows of every
-    // output tile) and half of its column tiles; dbeta adds the two halves through LDS
+    // NP = kTU / 256 waves per token block: wave (tb, pw) takes token block tb (the rows of
+    // every output tile) and part pw of its column tiles; dbeta adds the parts' row
+    // sums through LDS
+    constexpr int NP = kTU / 256, NS = 4 / NP;  // parts, s tiles of a part
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, H = a.H, item = blockIdx.x;
-    const int tb = wave & 3, half = wave >> 2;
+    const int tb = wave & 3, pw = wave >> 2;
     const int r = lane & 15, q = lane >> 4;
     static_assert(2 * kC * LC >= kC * LK, "gate cumsum fits sD + sE");
     // KG = kh 2^G (sM2) and dW (sM1); dW's loads stay in flight (registers) until sM1 is free
@@ -1030,16 +1032,16 @@ __global__ __launch_bounds__(kTU) void bwd_ut_kernel(BackwardArgs b) {
     rows_fetch<TIn, DV, DV, kTU>(a.v, rV, it, H);
     g2r<kC, DV, kTU>(X.blk(item, X.bw.dU), DV, rU);
     // dT (part 1: dW BK^T, BK = beta KG, so column s takes beta_s; this wave's tiles (tb, sb),
-    // sb = 2 half, 2 half + 1) and dBK of its rows; dbeta part sum_c KG dBK
-    f32x4 dT[2];
-    for (int i = 0; i < 2; ++i) {
-        const int sb = 2 * half + i;
+    // sb = NS pw .. NS pw + NS - 1) and dBK of its rows; dbeta part sum_c KG dBK
+    f32x4 dT[NS];
+    for (int i = 0; i < NS; ++i) {
+        const int sb = NS * pw + i;
         dT[i] = mm16(sM1 + 16 * tb * LK, LK, 1, sM2 + 16 * sb * LK, 1, LK, DK, lane, f32x4{0.f, 0.f, 0.f, 0.f}) *
                 sB[16 * sb + r];
     }
     float* dBK = X.blk(item, X.bw.dBK);
     float part[4] = {0.f, 0.f, 0.f, 0.f};
-    for (int cb = half * (DK / 32); cb < (half + 1) * (DK / 32); ++cb) {
+    for (int cb = pw * (DK / 16 / NP); cb < (pw + 1) * (DK / 16 / NP); ++cb) {
         const f32x4 v = mm16(sT + 16 * tb, 1, LC, sM1 + 16 * cb, LK, 1, kC, lane, f32x4{0.f, 0.f, 0.f, 0.f});
         put_tile(dBK, DK, tb, cb, v, lane);
         const f32x4 kg = get_tile(sM2, LK, tb, cb, lane);
@@ -1061,10 +1063,10 @@ __global__ __launch_bounds__(kTU) void bwd_ut_kernel(BackwardArgs b) {
         *x = raw * sB[t];
     });
     lds_barrier();
-    for (int i = 0; i < 2; ++i)
-        dT[i] = mm16(sM1 + 16 * tb * LV, LV, 1, sM2 + 16 * (2 * half + i) * LV, 1, LV, DV, lane, dT[i]);
+    for (int i = 0; i < NS; ++i)
+        dT[i] = mm16(sM1 + 16 * tb * LV, LV, 1, sM2 + 16 * (NS * pw + i) * LV, 1, LV, DV, lane, dT[i]);
     // dBV = T^T dU: dv = beta dBV, dbeta part sum_j v dBV
-    for (int cb = half * (DV / 32); cb < (half + 1) * (DV / 32); ++cb) {
+    for (int cb = pw * (DV / 16 / NP); cb < (pw + 1) * (DV / 16 / NP); ++cb) {
         const f32x4 v = mm16(sT + 16 * tb, 1, LC, sM1 + 16 * cb, LV, 1, kC, lane, f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) {
@@ -1075,22 +1077,22 @@ __global__ __launch_bounds__(kTU) void bwd_ut_kernel(BackwardArgs b) {
     }
     // this wave's rows of Ag for the dbeta part of dA (global), loaded during E
     const float* Ag = X.blk(item, X.bw.Ag);
-    f32x4 agt[2];
+    f32x4 agt[NS];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) agt[i] = get_tile(Ag, kC, tb, 2 * half + i, lane);
+    for (int i = 0; i < NS; ++i) agt[i] = get_tile(Ag, kC, tb, NS * pw + i, lane);
     lds_barrier();  // every wave's reads of sV precede the dT stores over it
     // dT to LDS; E = T^T dT; dA = -(E T^T) (s < t)
-    for (int i = 0; i < 2; ++i) put_tile(sD, LC, tb, 2 * half + i, dT[i], lane);
+    for (int i = 0; i < NS; ++i) put_tile(sD, LC, tb, NS * pw + i, dT[i], lane);
     lds_barrier();
-    for (int i = 0; i < 2; ++i) {
-        const int sb = 2 * half + i;
+    for (int i = 0; i < NS; ++i) {
+        const int sb = NS * pw + i;
         put_tile(sE, LC, tb, sb, mm16(sT + 16 * tb, 1, LC, sD + 16 * sb, LC, 1, kC, lane, f32x4{0.f, 0.f, 0.f, 0.f}), lane);
     }
     lds_barrier();
     float* dAg = X.blk(item, X.bw.dAg);
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int sb = 2 * half + i;
+    for (int i = 0; i < NS; ++i) {
+        const int sb = NS * pw + i;
         f32x4 v = mm16(sE + 16 * tb * LC, LC, 1, sT + 16 * sb * LC, 1, LC, kC, lane, f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) {
@@ -1101,8 +1103,8 @@ __global__ __launch_bounds__(kTU) void bwd_ut_kernel(BackwardArgs b) {
         }
         put_tile(dAg, kC, tb, sb, v, lane);
     }
-    // dbeta: reduce the partial sums over the 16 lanes of each row group, then add the two
-    // halves (in the same order for every row)
+    // dbeta: reduce the partial sums over the 16 lanes of each row group, then add the parts
+    // (in the same order for every row)
 #pragma unroll
     for (int ii = 0; ii < 4; ++ii) {
         float x = part[ii];
@@ -1110,11 +1112,15 @@ __global__ __launch_bounds__(kTU) void bwd_ut_kernel(BackwardArgs b) {
         x += __shfl_xor(x, 2, 64);
         x += __shfl_xor(x, 4, 64);
         x += __shfl_xor(x, 8, 64);
-        if (r == 0) sDB[half][16 * tb + 4 * q + ii] = x;
+        if (r == 0) sDB[pw][16 * tb + 4 * q + ii] = x;
     }
     lds_barrier();
-    if (threadIdx.x < it.L)
-        b.dbeta[static_cast<int64_t>(it.t0 + threadIdx.x) * H + it.h] = sDB[0][threadIdx.x] + sDB[1][threadIdx.x];
+    if (threadIdx.x < it.L) {
+        float x = sDB[0][threadIdx.x];
+#pragma unroll
+        for (int pp = 1; pp < NP; ++pp) x += sDB[pp][threadIdx.x];
+        b.dbeta[static_cast<int64_t>(it.t0 + threadIdx.x) * H + it.h] = x;
+    }
 }
 
 // ---------------------------------------------------------------------------
