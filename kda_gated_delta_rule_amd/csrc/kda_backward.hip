@@ -1125,7 +1125,8 @@ __global__ __launch_bounds__(kTU) void bwd_ut_kernel(BackwardArgs b) {
 
 // ---------------------------------------------------------------------------
 // 7. bwd_final: X1..X4, dkh, dqh, dG, reverse cumsum, norm backward; dq, dk, dg.
-//    Wave w owns token block w (rows of every output tile).
+//    Eight waves: wave (tb, half) owns token block tb (rows of every output tile) and half of
+//    the channel tiles.
 // ---------------------------------------------------------------------------
 constexpr int kTF = 512;  // threads of bwd_final
 template <int DK, int DV, class TIn>
