@@ -764,7 +764,10 @@ template <int DK, int DV>
 __global__ __launch_bounds__(64 * (DK / 16)) void bwd_scan_kernel(BackwardArgs b, int e) {
     const PrefillArgs& a = b.fwd;
     constexpr int NTS = DV / 16, LX = DK + 4;
-    __shared__ __attribute__((aligned(16))) float xs[16 * LX];  // X^T [16 columns][DK]
+    // X^T [16 columns][DK], double-buffered by step parity: a step writes one buffer while no
+    // wave can still be reading it (its last reads were before the previous step's barrier),
+    // so each step needs one barrier
+    __shared__ __attribute__((aligned(16))) float xs2[2][16 * LX];
     const BwCtx X(a, DK, DV, e);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int r = lane & 15, q4 = 4 * (lane >> 4);
@@ -803,8 +806,9 @@ __global__ __launch_bounds__(64 * (DK / 16)) void bwd_scan_kernel(BackwardArgs b
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) dX[(16 * wave + q4 + rr) * DV + col] = x[rr];
         load(fill, c >= 2 ? c - 2 : 0);  // (a valid chunk when none is left)
+        float* xs = xs2[c & 1];
         *reinterpret_cast<f32x4*>(xs + r * LX + 16 * wave + q4) = x;
-        // LDS-only barriers: a __syncthreads() would also wait for the loads just issued
+        // LDS-only barrier: a __syncthreads() would also wait for the loads just issued
         lds_barrier();
         // lane (r, q) supplies k = 16 kb + 4q + ks of Mt row 16 wave + r and of X column r;
         // one accumulator (the matrix core accumulates back to back into the same registers)
@@ -816,7 +820,6 @@ __global__ __launch_bounds__(64 * (DK / 16)) void bwd_scan_kernel(BackwardArgs b
             for (int ks = 0; ks < 4; ++ks)
                 acc = __builtin_amdgcn_mfma_f32_16x16x4f32(cur.mt[kb][ks], xb[ks], acc, 0, 0, 0);
         }
-        lds_barrier();
         x = acc;
         return true;
     };
