@@ -873,12 +873,16 @@ __global__ __launch_bounds__(kTS) void bwd_state_kernel(BackwardArgs b) {
         rg.store(sG, LK);
         rp.store(sP, LC);
     }
+    // W goes where the gate cumsum is once Kt is formed: its loads go out once the opening
+    // operands are stored and stay in flight (registers) through the scan and the norms
+    Mat<kC, DK, kTS> rw;
+    rw.fetch(X.blk(item, X.bw.W), DK);
     gate_scan<DK, kTS>(sG, LK);
     lds_barrier();
     normalize_rows<kTS>(sK, LK, DK, inv, a.use_l2);
     to_kt<DK, kTS>(sK, sG, LK);
     lds_barrier();
-    g2s<kC, DK, kTS>(X.blk(item, X.bw.W), DK, sW, LK);
+    rw.store(sW, LK);
     if (threadIdx.x < DK) sgl[threadIdx.x] = 0.f;
     const float* S = X.blk(item, X.bw.S);
     const float* dX = X.blk(item, X.bw.dX);
