@@ -618,19 +618,23 @@ __global__ __launch_bounds__(kTI) void bwd_intra_kernel(BackwardArgs b) {
         }
     }
     lds_barrier();
+    // BK = beta kh 2^G into sQ (P is done) by waves 4..7 while waves 0..3 invert (I + A); the
+    // inverse's barriers order these writes before W = T BK
+    if (wave >= 4) {
+        constexpr int GPR = DK / 4, NB = kTI - 256;
+        for (int i = threadIdx.x - 256; i < kC * GPR; i += NB) {
+            const int t = i / GPR, c = 4 * (i % GPR);
+            const f32x4 k4 = *reinterpret_cast<const f32x4*>(sK + t * LK + c);
+            const f32x4 g4 = *reinterpret_cast<const f32x4*>(sG + t * LK + c);
+            f32x4 b4;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) b4[e] = sB[t] * k4[e] * ex2(g4[e]);
+            *reinterpret_cast<f32x4*>(sQ + t * LK + c) = b4;
+        }
+        if (threadIdx.x - 256 < DK) X.blk(item, X.bw.gl)[threadIdx.x - 256] = ex2(sG[(kC - 1) * LK + threadIdx.x - 256]);
+    }
     unit_lower_inverse(sA, sB, sT, sY, lane, wave);
     s2g<kC, kC, kTI>(sT, LC, X.blk(item, X.bw.T), kC);
-    // BK = beta kh 2^G into sQ (P is done), then W = T BK
-    for_groups<DK, kTI>([&](int t, int c) {
-        const f32x4 k4 = *reinterpret_cast<const f32x4*>(sK + t * LK + c);
-        const f32x4 g4 = *reinterpret_cast<const f32x4*>(sG + t * LK + c);
-        f32x4 b4;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) b4[e] = sB[t] * k4[e] * ex2(g4[e]);
-        *reinterpret_cast<f32x4*>(sQ + t * LK + c) = b4;
-    });
-    if (threadIdx.x < DK) X.blk(item, X.bw.gl)[threadIdx.x] = ex2(sG[(kC - 1) * LK + threadIdx.x]);
-    lds_barrier();
     float* Wg = X.blk(item, X.bw.W);
     for (int cb = half * (DK / 32); cb < (half + 1) * (DK / 32); ++cb) {
         const f32x4 w = mm16(sT + 16 * tb * LC, LC, 1, sQ + 16 * cb, LK, 1, kC, lane, f32x4{0.f, 0.f, 0.f, 0.f});
