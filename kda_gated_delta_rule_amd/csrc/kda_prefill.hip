@@ -545,7 +545,8 @@ __device__ __forceinline__ void intra_compute(const IntraIn<DK, DV, TIn>& X, cha
     float* sPW = sT2 + 5 * DK + wave * DK;  // [wave][DK] 2^(G_end(wave - 1) - chunk start)
 
     const int r = lane & 15, q = lane >> 4, t = 16 * wave + r;
-    // no output (the backward's forward pass): the QG and P records are never read
+    // no output (the backward's forward pass): the QG and P records are never read, so
+    // neither they nor the P tiles are formed
     const bool with_o = a.o != nullptr;
 
     // ---- 1. norms, gate cumsum inside the wave, per-wave gate tables ------------------
@@ -723,7 +724,7 @@ __device__ __forceinline__ void intra_compute(const IntraIn<DK, DV, TIn>& X, cha
                 }
             }
             split_gran(kb, KBh[j], KBl[j], tag);
-            split_gran(qb, QBh[j], QBl[j], tag);
+            if (with_o) split_gran(qb, QBh[j], QBl[j], tag);
             // s-operand copies of this wave's rows for every later block i (copy i holds
             // rows 0 .. 16 i - 1 from KS row 8 i (i - 1); the low parts 96 rows further)
             auto put = [&](int row, const float* x) {
@@ -766,7 +767,7 @@ __device__ __forceinline__ void intra_compute(const IntraIn<DK, DV, TIn>& X, cha
 #pragma unroll
             for (int e = 0; e < GW; ++e) {
                 Adg = __builtin_amdgcn_mfma_f32_16x16x4f32(sd[e], kd[e], Adg, 0, 0, 0);
-                Pdg = __builtin_amdgcn_mfma_f32_16x16x4f32(sd[e], qd[e], Pdg, 0, 0, 0);
+                if (with_o) Pdg = __builtin_amdgcn_mfma_f32_16x16x4f32(sd[e], qd[e], Pdg, 0, 0, 0);
             }
             // one granule at a time: interleaving the unrolled iterations runs out of registers
             __builtin_amdgcn_sched_barrier(0);
@@ -791,7 +792,7 @@ __device__ __forceinline__ void intra_compute(const IntraIn<DK, DV, TIn>& X, cha
                     const u32x4 bl =
                         E == 2 ? *reinterpret_cast<const u32x4*>(sKS + ks_at(96 + row, 4 * j + q)) : bh;
                     accA = smma(bh, bl, KBh[j], KBl[j], accA, tag);
-                    accP = smma(bh, bl, QBh[j], QBl[j], accP, tag);
+                    if (with_o) accP = smma(bh, bl, QBh[j], QBl[j], accP, tag);
                 }
             }
             const f32x4 iks = *reinterpret_cast<const f32x4*>(sIk + 16 * jj + 4 * q);
