@@ -831,11 +831,17 @@ __global__ __launch_bounds__(64 * (DK / 16)) void bwd_scan_kernel(BackwardArgs b
         Ops o0, o1, o2;
         load(o0, nch - 1);
         load(o1, nch >= 2 ? nch - 2 : 0);
-        for (int c = nch - 1;; c -= 3) {
-            if (!step(c, o0, o2)) break;
-            if (!step(c - 1, o1, o0)) break;
-            if (!step(c - 2, o2, o1)) break;
+        // whole groups of three steps with no exit inside the loop body, the last zero to two
+        // chunks after it: with exits between the steps the compiler's load-wait placement
+        // gave up on the two-ahead distance and waited for every load in flight
+        int c = nch - 1;
+        for (; c >= 2; c -= 3) {
+            step(c, o0, o2);
+            step(c - 1, o1, o0);
+            step(c - 2, o2, o1);
         }
+        if (c >= 0) step(c, o0, o2);
+        if (c >= 1) step(c - 1, o1, o0);
     }
     if (b.dh0) {
 #pragma unroll
