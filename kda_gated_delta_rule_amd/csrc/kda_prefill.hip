@@ -1484,6 +1484,9 @@ __device__ __forceinline__ void scan_group(const PrefillArgs& a, int group, int 
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr)
             X[i][rr] = a.h0_from_pool ? Sg[(16 * (RW * wave + i) + q4 + rr) * DV + r] : 0.f;
+    // the initial state has arrived before the loop: otherwise the compiler, merging this
+    // path with the loop's back edge, waits for every load in flight at each loop entry
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), the other counters unconstrained
     if (nseg == 0) {
         // no tokens: the final state is the initial state (zero unless read from the slot),
         // and so is the input front's convolution state
@@ -1524,18 +1527,21 @@ __device__ __forceinline__ void scan_group(const PrefillArgs& a, int group, int 
     };
     // Two segments in flight: step k uses the operands loaded two steps earlier and issues
     // the loads of step k + 2.  The three operand sets rotate by name (the loop is unrolled
-    // three times), so no register copy forces a wait for loads still in flight.
-    auto step = [&](int k, const Ops& cur, Ops& fill) {
+    // three times), so no register copy forces a wait for loads still in flight.  X^T goes
+    // through LDS buffer k & 1: a step writes the buffer whose last reads (two steps back)
+    // ended before the previous step's barrier, so one barrier per step suffices.
+    auto step = [&](int k, const Ops& cur, Ops& fill, bool may_end) {
         float* Ss = reinterpret_cast<float*>(blk_of(k) + ws.s_start);
 #pragma unroll
         for (int i = 0; i < RW; ++i)
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) Ss[(16 * (RW * wave + i) + q4 + rr) * DV + col] = X[i][rr];
-        if (k == nseg - 1) return false;
+        if (may_end && k == nseg - 1) return false;
         load(fill, min(k + 2, nseg - 2));  // the last segment has no transition; repeat a valid one
+        float* xb = xs + (k & 1) * 16 * LDX;
 #pragma unroll
         for (int i = 0; i < RW; ++i)
-            *reinterpret_cast<f32x4*>(xs + r * LDX + 16 * (RW * wave + i) + q4) = X[i];
+            *reinterpret_cast<f32x4*>(xb + r * LDX + 16 * (RW * wave + i) + q4) = X[i];
         lds_barrier();
         // lane (r, q) supplies k = 16 kb + 4q + ks of Phi row 16 rb + r and of X column r
 #pragma unroll
@@ -1543,14 +1549,13 @@ __device__ __forceinline__ void scan_group(const PrefillArgs& a, int group, int 
             f32x4 acc = cur.sl[i];
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb) {
-                const f32x4 pb = *reinterpret_cast<const f32x4*>(xs + r * LDX + 16 * kb + q4);
+                const f32x4 pb = *reinterpret_cast<const f32x4*>(xb + r * LDX + 16 * kb + q4);
 #pragma unroll
                 for (int ks = 0; ks < 4; ++ks)
                     acc = __builtin_amdgcn_mfma_f32_16x16x4f32(cur.ph[i][kb][ks], pb[ks], acc, 0, 0, 0);
             }
             X[i] = acc;
         }
-        lds_barrier();
         return true;
     };
     Ops o0, o1, o2;
@@ -1558,17 +1563,23 @@ __device__ __forceinline__ void scan_group(const PrefillArgs& a, int group, int 
         load(o0, 0);
         load(o1, min(1, nseg - 2));
     }
-    for (int k = 0;; k += 3) {
-        if (!step(k, o0, o2)) break;
-        if (!step(k + 1, o1, o0)) break;
-        if (!step(k + 2, o2, o1)) break;
+    // whole groups of three steps that are not the last (no exit inside the loop body, which
+    // lets the compiler keep the loads two steps ahead), then the last one to three steps
+    int k = 0;
+    for (; k + 3 <= nseg - 1; k += 3) {
+        step(k, o0, o2, false);
+        step(k + 1, o1, o0, false);
+        step(k + 2, o2, o1, false);
     }
+    if (step(k, o0, o2, true) && step(k + 1, o1, o0, true)) step(k + 2, o2, o1, true);
+    // the next group's first step writes buffer 0: every wave's reads of this group end here
+    lds_barrier();
 }
 
 template <int DK, int DV, int E>
 __global__ __launch_bounds__(64 * (DK / 16)) void seg_scan_kernel(PrefillArgs a) {
     constexpr int NTS = DV / 16, LDX = DK + 4;
-    __shared__ __attribute__((aligned(16))) float xs[16 * LDX];  // X^T [16 columns][DK]
+    __shared__ __attribute__((aligned(16))) float xs[2 * 16 * LDX];  // X^T [16 columns][DK], two buffers
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     // The NTS column tiles of one (sequence, head) all read the same Phi blocks: they get
     // virtual block ids congruent mod kNumXcd, so they run on one XCD and share its L2
